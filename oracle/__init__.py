@@ -1,0 +1,269 @@
+"""CPU oracle for one 3D Gaussian Splatting training step -- TEST INFRASTRUCTURE.
+
+Only the test-suite, the smoke check and the bench's CPU-baseline leg import this package.
+The product path (the HIP library and its binding) never imports, links or runs it.
+
+The arithmetic lives in ``oracle.c`` (plain C, IEEE double); this module compiles it with
+gcc into ``liboracle.so`` next to the source and wraps each function with numpy arrays.
+Function-by-function citations of the pages are in ``oracle.c``.
+
+Parity status: every function is pinned by tests under ``tests/`` (closed forms,
+invariants, brute force, finite differences, a library Adam); the absolute images are not
+pinned by the pages, which print no rendered values.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+PROJ_FIELDS = ("u", "v", "depth", "opacity", "A", "B", "C", "r", "g", "b")
+GRAD2D_FIELDS = ("u", "v", "A", "B", "C", "opacity", "r", "g", "b")
+DEC_SKIP, DEC_BLEND, DEC_BLEND_CLAMPED, DEC_STOP, DEC_NONE = 0, 1, 2, 3, 4
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c with gcc (no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + f".tmp{os.getpid()}"
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+                               "-D_GNU_SOURCE", "-ffp-contract=off", "-fno-fast-math",
+                               "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i64, i32, dbl = ctypes.c_int64, ctypes.c_int, ctypes.c_double
+        L.or_rows_for_degree.argtypes = [i32]
+        L.or_sh_basis.argtypes = [i32, dbl, dbl, dbl, P]
+        L.or_quat_to_rot.argtypes = [P, P]
+        L.or_preprocess.argtypes = [i64, i32, P, P, i32, i32, P, P, P]
+        L.or_preprocess_margins.argtypes = [i64, i32, P, P, i32, i32, P]
+        L.or_count_intersections.argtypes = [i64, P, P, i32, i32]
+        L.or_count_intersections.restype = i64
+        L.or_bin_sort.argtypes = [i64, P, P, i32, i32, P, P]
+        L.or_bin_sort.restype = i64
+        L.or_ranges.argtypes = [i64, P, i32, P]
+        L.or_render_forward.argtypes = [i32, i32, P, i64, P, P, P, P, P, P, P, P, P, P, i64, i32]
+        L.or_render_bruteforce.argtypes = [i32, i32, P, i64, P, P, P, P, P, P]
+        L.or_loss_l1.argtypes = [i64, P, P, P]
+        L.or_loss_l1.restype = dbl
+        L.or_render_backward.argtypes = [i32, i32, P, i64, P, P, P, P, P, P, i64]
+        L.or_preprocess_backward.argtypes = [i64, i32, P, P, i32, i32, P, P]
+        L.or_adam.argtypes = [i64, P, P, P, P, i32, dbl, dbl, dbl, dbl]
+        L.or_debug_gaussian.argtypes = [i32, P, P, i32, i32, P]
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return ctypes.c_void_p(a.ctypes.data) if a is not None else None
+
+
+def _f64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def rows_for_degree(d):
+    return lib().or_rows_for_degree(d)
+
+
+def sh_basis(deg, x, y, z):
+    out = np.zeros(16)
+    lib().or_sh_basis(deg, x, y, z, _p(out))
+    return out
+
+
+def quat_to_rot(q):
+    q = _f64(q)
+    out = np.zeros(9)
+    lib().or_quat_to_rot(_p(q), _p(out))
+    return out.reshape(3, 3)
+
+
+def debug_gaussian(param_col, sh_degree, cam_flat, W, H):
+    """Intermediates of the preprocess for one Gaussian (its R parameters)."""
+    p = _f64(param_col).reshape(-1)
+    out = np.zeros(63)
+    lib().or_debug_gaussian(sh_degree, _p(p), _p(_f64(cam_flat)), W, H, _p(out))
+    return dict(visible=bool(out[0]), s=out[1:4], o=out[4], R=out[5:14].reshape(3, 3),
+                Sigma=out[14:23].reshape(3, 3), p_cam=out[23:26], J=out[26:32].reshape(2, 3),
+                V=out[32:41].reshape(3, 3), S2=out[41:45].reshape(2, 2), Q=out[45:49].reshape(2, 2),
+                u=out[49], v=out[50], rx=int(out[51]), ry=int(out[52]), tiles=int(out[53]),
+                dir=out[54:57], raw=out[57:60], rgb=out[60:63])
+
+
+def preprocess(params, sh_degree, cam_flat, W, H):
+    """params [R][n] -> (proj [10][n] float64, radii [2][n] int32, tiles [n] uint32)."""
+    params = _f64(params)
+    n = params.shape[1]
+    cam = _f64(cam_flat)
+    proj = np.zeros((10, n))
+    radii = np.zeros((2, n), np.int32)
+    tiles = np.zeros(n, np.uint32)
+    lib().or_preprocess(n, sh_degree, _p(params), _p(cam), W, H, _p(proj), _p(radii), _p(tiles))
+    return proj, radii, tiles
+
+
+def preprocess_margins(params, sh_degree, cam_flat, W, H):
+    """[3][n]: 3 sqrt(S2_00), 3 sqrt(S2_11), min |raw colour| (0 for culled)."""
+    params = _f64(params)
+    n = params.shape[1]
+    out = np.zeros((3, n))
+    lib().or_preprocess_margins(n, sh_degree, _p(params), _p(_f64(cam_flat)), W, H, _p(out))
+    return out
+
+
+def bin_sort(proj, radii, W, H):
+    """-> (keys uint64 [K], vals uint32 [K]).  u, v, depth are read as float32."""
+    proj = _f64(proj)
+    radii = np.ascontiguousarray(radii, np.int32)
+    n = proj.shape[1]
+    K = lib().or_count_intersections(n, _p(proj), _p(radii), W, H)
+    keys = np.zeros(max(K, 1), np.uint64)
+    vals = np.zeros(max(K, 1), np.uint32)
+    K2 = lib().or_bin_sort(n, _p(proj), _p(radii), W, H, _p(keys), _p(vals))
+    assert K2 == K
+    return keys[:K], vals[:K]
+
+
+def ranges(keys, n_tiles):
+    keys = np.ascontiguousarray(keys, np.uint64)
+    out = np.zeros(2 * n_tiles, np.uint32)
+    lib().or_ranges(keys.size, _p(keys), n_tiles, _p(out))
+    return out.reshape(n_tiles, 2)
+
+
+def render_forward(proj, vals, rng, W, H, bg=(0.0, 0.0, 0.0), margins=None,
+                   record_decisions=False, decisions=None):
+    """Tiled forward.  Returns dict(image [H][W][3], T_final, last_contrib, n_examined,
+    borderline) and, with record_decisions, 'decisions' (int8 [H*W][maxlen])."""
+    proj = _f64(proj)
+    n = proj.shape[1]
+    vals = np.ascontiguousarray(vals, np.uint32)
+    rng = np.ascontiguousarray(rng, np.uint32).reshape(-1)
+    bgv = _f64(bg)
+    img = np.zeros((H, W, 3))
+    Tf = np.zeros((H, W))
+    last = np.zeros((H, W), np.uint32)
+    ex = np.zeros((H, W), np.uint32)
+    bl = np.zeros((H, W), np.uint8)
+    mg = _f64(margins) if margins is not None else None
+    lens = rng[1::2].astype(np.int64) - rng[0::2].astype(np.int64)
+    stride = int(max(1, lens.max() if lens.size else 1))
+    dec, mode = None, 0
+    if record_decisions:
+        dec = np.full((H * W, stride), DEC_NONE, np.int8)
+        mode = 1
+    elif decisions is not None:
+        dec = np.ascontiguousarray(decisions, np.int8)
+        stride = dec.shape[1]
+        mode = 2
+    vals_arg = vals if vals.size else np.zeros(1, np.uint32)
+    lib().or_render_forward(W, H, _p(bgv), n, _p(proj), _p(vals_arg), _p(rng), _p(img), _p(Tf),
+                            _p(last), _p(ex), _p(bl), _p(mg), _p(dec), stride, mode)
+    out = dict(image=img, T_final=Tf, last_contrib=last, n_examined=ex, borderline=bl.astype(bool))
+    if record_decisions:
+        out["decisions"] = dec
+    return out
+
+
+def render_bruteforce(proj, radii, W, H, bg=(0.0, 0.0, 0.0)):
+    proj = _f64(proj)
+    n = proj.shape[1]
+    radii = np.ascontiguousarray(radii, np.int32)
+    img = np.zeros((H, W, 3))
+    Tf = np.zeros((H, W))
+    last = np.zeros((H, W), np.uint32)
+    ex = np.zeros((H, W), np.uint32)
+    lib().or_render_bruteforce(W, H, _p(_f64(bg)), n, _p(proj), _p(radii), _p(img), _p(Tf),
+                               _p(last), _p(ex))
+    return dict(image=img, T_final=Tf, last_contrib=last, n_examined=ex)
+
+
+def loss_l1(image, target):
+    image = _f64(image)
+    target = _f64(target)
+    g = np.zeros_like(image)
+    L = lib().or_loss_l1(image.size, _p(image), _p(target), _p(g))
+    return L, g
+
+
+def render_backward(proj, vals, rng, W, H, dLdI, bg=(0.0, 0.0, 0.0), decisions=None):
+    """-> grad2d [9][n] float64 (u, v, A, B, C, opacity, r, g, b)."""
+    proj = _f64(proj)
+    n = proj.shape[1]
+    vals = np.ascontiguousarray(vals, np.uint32)
+    rng = np.ascontiguousarray(rng, np.uint32).reshape(-1)
+    g = _f64(dLdI)
+    out = np.zeros((9, n))
+    dec, stride = None, 0
+    if decisions is not None:
+        dec = np.ascontiguousarray(decisions, np.int8)
+        stride = dec.shape[1]
+    vals_arg = vals if vals.size else np.zeros(1, np.uint32)
+    lib().or_render_backward(W, H, _p(_f64(bg)), n, _p(proj), _p(vals_arg), _p(rng), _p(g),
+                             _p(out), _p(dec), stride)
+    return out
+
+
+def preprocess_backward(params, sh_degree, cam_flat, W, H, grad2d):
+    params = _f64(params)
+    n = params.shape[1]
+    out = np.zeros_like(params)
+    lib().or_preprocess_backward(n, sh_degree, _p(params), _p(_f64(cam_flat)), W, H,
+                                 _p(_f64(grad2d)), _p(out))
+    return out
+
+
+def adam(theta, grad, m, v, t, lr=1e-3, b1=0.9, b2=0.999, eps=1e-8):
+    """In-place on float64 arrays (copies are returned for convenience)."""
+    theta = _f64(theta).copy()
+    m = _f64(m).copy()
+    v = _f64(v).copy()
+    g = _f64(grad)
+    lib().or_adam(theta.size, _p(theta), _p(g), _p(m), _p(v), t, lr, b1, b2, eps)
+    return theta, m, v
+
+
+def n_tiles(W, H):
+    return ((W + 15) // 16) * ((H + 15) // 16)
+
+
+def train_step_reference(params, sh_degree, cam_flat, W, H, target=None, upstream=None,
+                         m=None, v=None, t=1, lr=1e-3, bg=(0.0, 0.0, 0.0)):
+    """The whole step in the oracle: preprocess -> bin/sort -> ranges -> forward -> loss
+    (L1 against `target`, or the given upstream dL/dI) -> backward -> preprocess backward
+    -> Adam.  Returns a dict with every intermediate."""
+    proj, radii, tiles = preprocess(params, sh_degree, cam_flat, W, H)
+    keys, vals = bin_sort(proj, radii, W, H)
+    rg = ranges(keys, n_tiles(W, H))
+    fwd = render_forward(proj, vals, rg, W, H, bg)
+    if upstream is not None:
+        dLdI = _f64(upstream)
+        loss = float((dLdI * fwd["image"]).sum())
+    else:
+        loss, dLdI = loss_l1(fwd["image"], target)
+    g2 = render_backward(proj, vals, rg, W, H, dLdI, bg)
+    grads = preprocess_backward(params, sh_degree, cam_flat, W, H, g2)
+    out = dict(proj=proj, radii=radii, tiles=tiles, keys=keys, vals=vals, ranges=rg, loss=loss,
+               dLdI=dLdI, grad2d=g2, grads=grads, **fwd)
+    if m is not None:
+        out["params_new"], out["m_new"], out["v_new"] = adam(params, grads, m, v, t, lr)
+    return out

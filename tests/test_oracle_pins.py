@@ -1,0 +1,498 @@
+"""Pins for the CPU oracle: each test checks the oracle against something other than
+itself -- a figure the pages print, a closed form, an invariant, a library routine or a
+brute-force enumeration -- chosen so that a dropped term, a wrong sign or index or a
+transposed operand in the oracle fails at least one of them."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from gaussian_splatting_differentiable_preprocess_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_figures.json")
+
+
+def golden(key):
+    with open(GOLDEN) as f:
+        return json.load(f)[key]["value"]
+
+
+def cam_at(pos, W, H=None):
+    return inputs.lookat_camera(pos, W, W if H is None else H)
+
+
+# ------------------------------------------------------------------------------------
+# figures printed on the pages
+# ------------------------------------------------------------------------------------
+
+def test_parameter_rows_and_bytes_match_pages():
+    assert (3 + 1) ** 2 == golden("sh3_coefficients_per_channel")
+    assert (2 + 1) ** 2 == golden("sh2_coefficients_per_channel")
+    assert oracle.rows_for_degree(3) == golden("sh3_learnable_scalars")
+    assert oracle.rows_for_degree(2) == golden("sh2_learnable_scalars")
+    # parameters + two Adam moments, float32
+    assert oracle.rows_for_degree(3) * 4 * 3 == golden("sh3_bytes_with_adam")
+    assert abs(192e9 / (oracle.rows_for_degree(3) * 12) - golden("max_gaussians_192GB_sh3")) < 0.5e6
+    assert abs(192e9 / (oracle.rows_for_degree(2) * 12) - golden("max_gaussians_192GB_sh2")) < 0.5e6
+    assert abs(8 * 192e9 / (oracle.rows_for_degree(3) * 12) - golden("max_gaussians_8x192GB_sh3")) < 0.01e9
+    assert 3 * 16 * 4 == golden("sh3_sh_bytes") and 3 * 4 == golden("rgb_bytes")
+    # projected record: radii 2 + means 2 + depth 1 + conic 3 + opacity 1 + colour 3
+    assert len(oracle.PROJ_FIELDS) + 2 == golden("record_scalars")
+    assert 4 * golden("record_scalars") == golden("record_bytes")
+
+
+# ------------------------------------------------------------------------------------
+# rotation, covariance, projection
+# ------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("theta", [0.0, 0.3, 1.0, 2.5, -1.2])
+def test_quaternion_about_z_is_planar_rotation(theta):
+    R = oracle.quat_to_rot([math.cos(theta / 2), 0, 0, math.sin(theta / 2)])
+    c, s = math.cos(theta), math.sin(theta)
+    np.testing.assert_allclose(R, [[c, -s, 0], [s, c, 0], [0, 0, 1]], atol=1e-15)
+
+
+def test_quaternion_about_x_and_y():
+    t = 0.7
+    Rx = oracle.quat_to_rot([math.cos(t / 2), math.sin(t / 2), 0, 0])
+    np.testing.assert_allclose(Rx, [[1, 0, 0], [0, math.cos(t), -math.sin(t)], [0, math.sin(t), math.cos(t)]], atol=1e-15)
+    Ry = oracle.quat_to_rot([math.cos(t / 2), 0, math.sin(t / 2), 0])
+    np.testing.assert_allclose(Ry, [[math.cos(t), 0, math.sin(t)], [0, 1, 0], [-math.sin(t), 0, math.cos(t)]], atol=1e-15)
+
+
+def test_rotation_orthonormal_and_composes():
+    rng = np.random.default_rng(1)
+    for _ in range(20):
+        q1 = rng.normal(size=4); q1 /= np.linalg.norm(q1)
+        q2 = rng.normal(size=4); q2 /= np.linalg.norm(q2)
+        R1, R2 = oracle.quat_to_rot(q1), oracle.quat_to_rot(q2)
+        np.testing.assert_allclose(R1 @ R1.T, np.eye(3), atol=1e-14)
+        assert abs(np.linalg.det(R1) - 1) < 1e-14
+        # Hamilton product q1 q2 rotates like R1 R2
+        w1, x1, y1, z1 = q1; w2, x2, y2, z2 = q2
+        q12 = [w1 * w2 - x1 * x2 - y1 * y2 - z1 * z2, w1 * x2 + x1 * w2 + y1 * z2 - z1 * y2,
+               w1 * y2 - x1 * z2 + y1 * w2 + z1 * x2, w1 * z2 + x1 * y2 - y1 * x2 + z1 * w2]
+        np.testing.assert_allclose(oracle.quat_to_rot(q12), R1 @ R2, atol=1e-14)
+
+
+def _one(mu, logs, q, a, dc, deg=0, rest=None):
+    R = oracle.rows_for_degree(deg)
+    p = np.zeros(R)
+    p[0:3], p[3:6], p[6:10], p[10] = mu, logs, q, a
+    p[11:14] = dc
+    if rest is not None:
+        p[14:R] = rest
+    return p
+
+
+def test_covariance_eigen_decomposition():
+    cam = cam_at((3, 0, 0), 64)
+    rng = np.random.default_rng(2)
+    for _ in range(10):
+        q = rng.normal(size=4)
+        logs = rng.normal(-2, 0.5, 3)
+        d = oracle.debug_gaussian(_one([0.1, 0.2, -0.1], logs, q, 0.0, [0.5] * 3), 0, cam.flat(), 64, 64)
+        ev, evec = np.linalg.eigh(d["Sigma"])
+        np.testing.assert_allclose(np.sort(ev), np.sort(np.exp(2 * logs)), rtol=1e-12)
+        # the columns of R(q/|q|) are the principal axes with variances s^2
+        Rq = oracle.quat_to_rot(q / np.linalg.norm(q))
+        np.testing.assert_allclose(Rq.T @ d["Sigma"] @ Rq, np.diag(np.exp(2 * logs)), atol=1e-14)
+
+
+def test_projection_axis_and_field_of_view_edge():
+    W = 64
+    cam = cam_at((3, 0, 0), W)
+    # the look-at target maps to the principal point
+    d0 = oracle.debug_gaussian(_one([0, 0, 0], [-3] * 3, [1, 0, 0, 0], 0, [0.5] * 3), 0, cam.flat(), W, W)
+    assert abs(d0["u"] - W / 2) < 1e-5 and abs(d0["v"] - W / 2) < 1e-5
+    # a point seen at exactly half the 50 degree field of view lands on the image border;
+    # the camera's right axis is +y, its down axis is -z for this pose.
+    t25 = math.tan(math.radians(25.0))
+    d1 = oracle.debug_gaussian(_one([0, 3 * t25, 0], [-3] * 3, [1, 0, 0, 0], 0, [0.5] * 3), 0, cam.flat(), W, W)
+    assert abs(d1["u"] - W) < 1e-4 and abs(d1["v"] - W / 2) < 1e-4
+    d2 = oracle.debug_gaussian(_one([0, 0, -3 * t25], [-3] * 3, [1, 0, 0, 0], 0, [0.5] * 3), 0, cam.flat(), W, W)
+    assert abs(d2["v"] - W) < 1e-4 and abs(d2["u"] - W / 2) < 1e-4
+    # depth is the view-space z, here the distance along the axis
+    assert abs(d0["p_cam"][2] - 3.0) < 1e-6
+
+
+def test_ewa_jacobian_is_derivative_of_pinhole_map():
+    W = 96
+    cam = cam_at((2.5, 1.0, 0.7), W)
+    c = cam.flat()
+    Rc = c[:12].reshape(3, 4)[:, :3]
+    t = c[:12].reshape(3, 4)[:, 3]
+    fx, fy, cx, cy = c[12:16]
+
+    def pinhole(p):
+        return np.array([fx * p[0] / p[2] + cx, fy * p[1] / p[2] + cy])
+
+    rng = np.random.default_rng(3)
+    for _ in range(8):
+        mu = rng.normal(0, 0.4, 3)
+        d = oracle.debug_gaussian(_one(mu, rng.normal(-2.5, 0.3, 3), rng.normal(size=4), 0, [0.5] * 3),
+                                  0, c, W, W)
+        p = Rc @ mu + t
+        np.testing.assert_allclose(d["p_cam"], p, atol=1e-12)
+        Jfd = np.zeros((2, 3))
+        for j in range(3):
+            e = np.zeros(3); e[j] = 1e-6
+            Jfd[:, j] = (pinhole(p + e) - pinhole(p - e)) / 2e-6
+        np.testing.assert_allclose(d["J"], Jfd, rtol=1e-7, atol=1e-7)
+        # Sigma_2 = J (Rc Sigma Rc^T) J^T + 0.3 I
+        V = Rc @ d["Sigma"] @ Rc.T
+        np.testing.assert_allclose(d["V"], V, atol=1e-14)
+        np.testing.assert_allclose(d["S2"], Jfd @ V @ Jfd.T + 0.3 * np.eye(2), rtol=1e-6)
+        np.testing.assert_allclose(d["Q"] @ d["S2"], np.eye(2), atol=1e-12)
+
+
+# ------------------------------------------------------------------------------------
+# spherical harmonics
+# ------------------------------------------------------------------------------------
+
+def _sh_scipy(l, m, x, y, z):
+    """Real SH from scipy's complex Y_l^m (Condon-Shortley phase): sqrt(2) Im Y_l^|m| for
+    m < 0, Y_l^0, sqrt(2) Re Y_l^m for m > 0."""
+    from scipy.special import sph_harm_y
+    theta = math.acos(max(-1.0, min(1.0, z)))
+    phi = math.atan2(y, x)
+    Y = complex(sph_harm_y(l, abs(m), theta, phi))
+    if m < 0:
+        return math.sqrt(2) * Y.imag
+    if m == 0:
+        return Y.real
+    return math.sqrt(2) * Y.real
+
+
+def test_sh_basis_matches_scipy_complex_harmonics():
+    rng = np.random.default_rng(4)
+    for _ in range(25):
+        v = rng.normal(size=3); v /= np.linalg.norm(v)
+        Y = oracle.sh_basis(3, *v)
+        k = 0
+        for l in range(4):
+            for m in range(-l, l + 1):
+                assert abs(Y[k] - _sh_scipy(l, m, *v)) < 1e-12, (l, m)
+                k += 1
+
+
+def test_sh_gram_matrix_is_identity():
+    # Gauss-Legendre in cos(theta) x uniform phi integrates degree <= 6 products exactly
+    xs, ws = np.polynomial.legendre.leggauss(12)
+    nphi = 16
+    G = np.zeros((16, 16))
+    for ct, w in zip(xs, ws):
+        st = math.sqrt(1 - ct * ct)
+        for j in range(nphi):
+            ph = 2 * math.pi * j / nphi
+            Y = oracle.sh_basis(3, st * math.cos(ph), st * math.sin(ph), ct)
+            G += w * (2 * math.pi / nphi) * np.outer(Y, Y)
+    np.testing.assert_allclose(G, np.eye(16), atol=1e-12)
+
+
+def test_sh_degree_zero_colour():
+    cam = cam_at((3, 0, 0), 64)
+    dc = [0.2, 0.7, -0.4]
+    d = oracle.debug_gaussian(_one([0, 0, 0], [-3] * 3, [1, 0, 0, 0], 0, dc), 0, cam.flat(), 64, 64)
+    for ch in range(3):
+        assert abs(d["raw"][ch] - (0.5 + dc[ch] / (2 * math.sqrt(math.pi)))) < 1e-15
+    assert d["rgb"][2] == pytest.approx(0.5 - 0.4 / (2 * math.sqrt(math.pi)))
+
+
+def test_sh_view_direction_from_camera_centre():
+    cam = cam_at((3, 0, 0), 64)
+    # coefficient of Y_3 = -c1 x only: colour changes sign with the x component of the
+    # direction from the camera centre (3,0,0) to the Gaussian
+    rest = np.zeros(45)
+    rest[3 * 2 + 0] = 1.0  # k = 3, channel 0
+    d = oracle.debug_gaussian(_one([0, 0, 0], [-3] * 3, [1, 0, 0, 0], 0, [0, 0, 0], deg=3, rest=rest),
+                              3, cam.flat(), 64, 64)
+    np.testing.assert_allclose(d["dir"], [-1, 0, 0], atol=1e-15)
+    c1 = math.sqrt(3 / (4 * math.pi))
+    assert abs(d["raw"][0] - (0.5 + c1)) < 1e-14
+
+
+# ------------------------------------------------------------------------------------
+# single Gaussian closed form
+# ------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("logs,a", [(-3.0, 0.5), (-2.5, 3.0), (-3.5, -1.0), (-2.0, 6.0)])
+def test_single_isotropic_gaussian_closed_form(logs, a):
+    W = 64
+    cam = cam_at((3, 0, 0), W)
+    p = _one([0, 0, 0], [logs] * 3, [1, 0, 0, 0], a, [0.3, 0.6, 0.9])[:, None]
+    proj, radii, tiles = oracle.preprocess(p, 0, cam.flat(), W, W)
+    f = cam.fx
+    sigma2 = (f * math.exp(logs) / 3.0) ** 2 + 0.3
+    d = oracle.debug_gaussian(p[:, 0], 0, cam.flat(), W, W)
+    np.testing.assert_allclose(d["S2"], sigma2 * np.eye(2), rtol=1e-12, atol=1e-15)
+    out = oracle.train_step_reference(p, 0, cam.flat(), W, W, upstream=np.zeros((W, W, 3)))
+    o = 1 / (1 + math.exp(-a))
+    rgb = 0.5 + np.array([0.3, 0.6, 0.9]) / (2 * math.sqrt(math.pi))
+    r = int(radii[0, 0])
+    assert r == math.ceil(3 * math.sqrt(sigma2))
+    tx0, tx1 = int((W / 2 - r) // 16), int((W / 2 + r) // 16) + 1
+    for py in range(W):
+        for px in range(W):
+            inside = tx0 <= px // 16 < tx1 and tx0 <= py // 16 < tx1
+            r2 = (px + 0.5 - W / 2) ** 2 + (py + 0.5 - W / 2) ** 2
+            alpha = min(0.99, o * math.exp(-r2 / (2 * sigma2)))
+            want = rgb * alpha if (inside and np.float32(o * math.exp(-r2 / (2 * sigma2))) >= np.float32(1 / 255)) else 0 * rgb
+            np.testing.assert_allclose(out["image"][py, px], want, atol=1e-12)
+
+
+# ------------------------------------------------------------------------------------
+# binning, sort, ranges
+# ------------------------------------------------------------------------------------
+
+def _random_proj(rng, n, W, H, rmax=20):
+    proj = np.zeros((10, n))
+    proj[0] = rng.uniform(-30, W + 30, n)
+    proj[1] = rng.uniform(-30, H + 30, n)
+    proj[2] = rng.uniform(1, 5, n)
+    proj[2, : n // 4] = proj[2, n // 4: 2 * (n // 4)]  # equal depths exercise the tie-break
+    radii = rng.integers(1, rmax, (2, n)).astype(np.int32)
+    radii[:, rng.random(n) < 0.1] = 0  # culled
+    return proj, radii
+
+
+def test_binning_is_tile_interval_overlap():
+    rng = np.random.default_rng(5)
+    W, H = 100, 70
+    TX, TY = (W + 15) // 16, (H + 15) // 16
+    proj, radii = _random_proj(rng, 300, W, H)
+    keys, vals = oracle.bin_sort(proj, radii, W, H)
+    got = set((int(k >> 32), int(v)) for k, v in zip(keys, vals))
+    want = set()
+    for i in range(proj.shape[1]):
+        if radii[0, i] == 0:
+            continue
+        u, v = np.float32(proj[0, i]), np.float32(proj[1, i])
+        lo_x, hi_x = np.float32(u - np.float32(radii[0, i])), np.float32(u + np.float32(radii[0, i]))
+        lo_y, hi_y = np.float32(v - np.float32(radii[1, i])), np.float32(v + np.float32(radii[1, i]))
+        for ty in range(TY):
+            for tx in range(TX):
+                # tile [16 tx, 16 tx + 16) intersects the closed box [lo, hi]
+                if 16 * tx <= hi_x and lo_x < 16 * tx + 16 and 16 * ty <= hi_y and lo_y < 16 * ty + 16:
+                    want.add((ty * TX + tx, i))
+    assert got == want
+
+
+def test_sort_is_numpy_stable_argsort_and_ranges_searchsorted():
+    rng = np.random.default_rng(6)
+    W, H = 128, 96
+    proj, radii = _random_proj(rng, 500, W, H)
+    keys, vals = oracle.bin_sort(proj, radii, W, H)
+    # rebuild the unsorted emission order and sort it with numpy's stable sort
+    TX, TY = W // 16, H // 16
+    ek, ev = [], []
+    for i in range(proj.shape[1]):
+        if radii[0, i] == 0:
+            continue
+        m = set()
+        for k_, v_ in zip(keys, vals):
+            if v_ == i:
+                m.add(int(k_ >> 32))
+        for t in sorted(m):  # row-major = increasing tile id
+            ek.append((t << 32) | int(np.float32(proj[2, i]).view(np.uint32)))
+            ev.append(i)
+    ek = np.array(ek, np.uint64)
+    ev = np.array(ev, np.uint32)
+    order = np.argsort(ek, kind="stable")
+    np.testing.assert_array_equal(keys, ek[order])
+    np.testing.assert_array_equal(vals, ev[order])
+    rg = oracle.ranges(keys, TX * TY)
+    tiles = (keys >> np.uint64(32)).astype(np.int64)
+    for t in range(TX * TY):
+        lo, hi = np.searchsorted(tiles, t, "left"), np.searchsorted(tiles, t, "right")
+        if lo == hi:
+            assert tuple(rg[t]) == (0, 0)
+        else:
+            assert tuple(rg[t]) == (lo, hi)
+
+
+# ------------------------------------------------------------------------------------
+# forward blend
+# ------------------------------------------------------------------------------------
+
+def _proj_manual(entries):
+    """entries: list of dict(u, v, depth, o, A, B, C, rgb) -> proj [10][n], radii."""
+    n = len(entries)
+    proj = np.zeros((10, n))
+    radii = np.zeros((2, n), np.int32)
+    for i, e in enumerate(entries):
+        proj[:, i] = [e["u"], e["v"], e["depth"], e["o"], e["A"], e.get("B", 0.0), e["C"], *e["rgb"]]
+        radii[:, i] = e.get("r", 8)
+    return proj, radii
+
+
+def _render(proj, radii, W, H, bg=(0, 0, 0)):
+    keys, vals = oracle.bin_sort(proj, radii, W, H)
+    rg = oracle.ranges(keys, oracle.n_tiles(W, H))
+    return oracle.render_forward(proj, vals, rg, W, H, bg)
+
+
+def test_two_layer_closed_form_and_depth_swap():
+    W = 32
+    c1, c2, bg = np.array([0.9, 0.1, 0.2]), np.array([0.1, 0.8, 0.3]), np.array([0.05, 0.1, 0.15])
+    a1, a2 = 0.6, 0.7
+    # broad flat Gaussians centred on pixel (8, 8): G = 1 there
+    e1 = dict(u=8.5, v=8.5, depth=1.0, o=a1, A=1e-3, C=1e-3, rgb=c1)
+    e2 = dict(u=8.5, v=8.5, depth=2.0, o=a2, A=1e-3, C=1e-3, rgb=c2)
+    proj, radii = _proj_manual([e1, e2])
+    out = _render(proj, radii, W, W, bg)
+    want = c1 * a1 + c2 * a2 * (1 - a1) + bg * (1 - a1) * (1 - a2)
+    np.testing.assert_allclose(out["image"][8, 8], want, rtol=1e-15)
+    assert out["T_final"][8, 8] == pytest.approx((1 - a1) * (1 - a2), rel=1e-15)
+    # swapping the depths swaps the roles
+    e1["depth"], e2["depth"] = 2.0, 1.0
+    proj, radii = _proj_manual([e1, e2])
+    out = _render(proj, radii, W, W, bg)
+    want = c2 * a2 + c1 * a1 * (1 - a2) + bg * (1 - a1) * (1 - a2)
+    np.testing.assert_allclose(out["image"][8, 8], want, rtol=1e-15)
+
+
+def test_stacked_layers_stop_before_blending():
+    W = 16
+    col = np.array([0.2, 0.4, 0.6])
+    ents = [dict(u=8.5, v=8.5, depth=1.0 + i, o=0.95, A=1e-3, C=1e-3, rgb=col) for i in range(6)]
+    proj, radii = _proj_manual(ents)
+    out = _render(proj, radii, W, W)
+    # weights 0.95, 0.0475, 0.002375; T after 3 layers = 1.25e-4; the 4th would take T to
+    # 6.25e-6 < 1e-4, so it is examined but not blended
+    np.testing.assert_allclose(out["image"][8, 8], col * (0.95 + 0.0475 + 0.002375), rtol=1e-14)
+    assert out["T_final"][8, 8] == pytest.approx(1.25e-4, rel=1e-12)
+    assert out["last_contrib"][8, 8] == 3
+    assert out["n_examined"][8, 8] == 4
+
+
+def _tiny_scene(seed, n, deg, W, logs=-2.0, dist=3.0):
+    params = inputs.small_scene(seed, n, deg, logscale_mean=logs, logscale_std=0.3)
+    cam = cam_at((dist, 0.4, 0.3), W)
+    return params, cam
+
+
+@pytest.mark.parametrize("seed,n,deg,W,H", [(10, 200, 0, 64, 48), (11, 256, 3, 48, 64), (12, 60, 3, 33, 17)])
+def test_tiled_renderer_equals_bruteforce_bitwise(seed, n, deg, W, H):
+    params = inputs.small_scene(seed, n, deg, logscale_mean=-2.5, logscale_std=0.5)
+    cam = inputs.lookat_camera((3.0, 0.4, 0.3), W, H)
+    proj, radii, tiles = oracle.preprocess(params, deg, cam.flat(), W, H)
+    keys, vals = oracle.bin_sort(proj, radii, W, H)
+    assert keys.size == tiles.sum()
+    rg = oracle.ranges(keys, oracle.n_tiles(W, H))
+    bg = (0.1, 0.2, 0.3)
+    a = oracle.render_forward(proj, vals, rg, W, H, bg)
+    b = oracle.render_bruteforce(proj, radii, W, H, bg)
+    for k in ("image", "T_final", "last_contrib", "n_examined"):
+        np.testing.assert_array_equal(a[k], b[k])
+    assert (a["last_contrib"] > 0).mean() > 0.3
+
+
+def test_partition_of_unity_and_transmittance_invariants():
+    W = 48
+    params, cam = _tiny_scene(20, 300, 0, W)
+    params = params.astype(np.float64)
+    c = 0.37
+    # all colours = background = c  =>  image = c everywhere
+    params[11:14] = (c - 0.5) * 2 * math.sqrt(math.pi)
+    proj, radii, _ = oracle.preprocess(params, 0, cam.flat(), W, W)
+    keys, vals = oracle.bin_sort(proj, radii, W, W)
+    rg = oracle.ranges(keys, oracle.n_tiles(W, W))
+    out = oracle.render_forward(proj, vals, rg, W, W, (c, c, c))
+    np.testing.assert_allclose(out["image"], c, rtol=1e-13)
+    assert (out["T_final"] >= 1e-4 * (1 - 1e-7)).all() and (out["T_final"] <= 1).all()
+    assert (out["n_examined"] >= out["last_contrib"]).all()
+    # T_final is the product of (1 - alpha) over the blended entries
+    dec = oracle.render_forward(proj, vals, rg, W, W, record_decisions=True)["decisions"]
+    for p in range(0, W * W, 37):
+        py, px = divmod(p, W)
+        t = (py // 16) * ((W + 15) // 16) + px // 16
+        T = 1.0
+        for j, code in enumerate(dec[p][: rg[t, 1] - rg[t, 0]]):
+            if code in (oracle.DEC_BLEND, oracle.DEC_BLEND_CLAMPED):
+                i = vals[rg[t, 0] + j]
+                dx, dy = px + 0.5 - proj[0, i], py + 0.5 - proj[1, i]
+                pw = -0.5 * (proj[4, i] * dx * dx + proj[6, i] * dy * dy) - proj[5, i] * dx * dy
+                T *= 1 - min(0.99, proj[3, i] * math.exp(pw))
+        assert T == pytest.approx(out["T_final"][py, px], rel=1e-12)
+
+
+def test_index_permutation_leaves_image_unchanged():
+    W = 40
+    params, cam = _tiny_scene(21, 150, 3, W)
+    perm = np.random.default_rng(0).permutation(params.shape[1])
+    a = oracle.train_step_reference(params, 3, cam.flat(), W, W, upstream=np.zeros((W, W, 3)))
+    b = oracle.train_step_reference(params[:, perm], 3, cam.flat(), W, W, upstream=np.zeros((W, W, 3)))
+    np.testing.assert_array_equal(a["image"], b["image"])
+    np.testing.assert_array_equal(a["T_final"], b["T_final"])
+
+
+# ------------------------------------------------------------------------------------
+# loss and Adam against library routines
+# ------------------------------------------------------------------------------------
+
+def test_l1_loss_matches_torch():
+    import torch
+    rng = np.random.default_rng(7)
+    img = rng.uniform(0, 1, (9, 11, 3))
+    tgt = rng.uniform(0, 1, (9, 11, 3))
+    tgt[0, 0, :] = img[0, 0, :]  # zero differences: sign(0) = 0
+    L, g = oracle.loss_l1(img, tgt)
+    ti = torch.tensor(img, requires_grad=True)
+    tl = torch.nn.functional.l1_loss(ti, torch.tensor(tgt))
+    tl.backward()
+    assert L == pytest.approx(float(tl), rel=1e-15)
+    np.testing.assert_allclose(g, ti.grad.numpy(), rtol=1e-15, atol=0)
+
+
+def test_adam_first_step_closed_form_and_zero_gradient():
+    rng = np.random.default_rng(8)
+    th = rng.normal(size=50)
+    g = rng.normal(size=50)
+    g[:5] = 0.0
+    lr, eps = 1e-3, 1e-8
+    t1, m1, v1 = oracle.adam(th, g, np.zeros(50), np.zeros(50), 1, lr=lr, eps=eps)
+    np.testing.assert_allclose(t1, th - lr * g / (np.abs(g) + eps), rtol=1e-14, atol=1e-17)
+    np.testing.assert_array_equal(t1[:5], th[:5])
+
+
+def test_adam_matches_torch_optim_over_ten_steps():
+    import torch
+    rng = np.random.default_rng(9)
+    th = rng.normal(size=64)
+    grads = rng.normal(size=(10, 64))
+    p = torch.tensor(th, requires_grad=True)
+    opt = torch.optim.Adam([p], lr=1e-3, betas=(0.9, 0.999), eps=1e-8)
+    m = np.zeros(64); v = np.zeros(64); cur = th.copy()
+    for t in range(10):
+        opt.zero_grad()
+        p.grad = torch.tensor(grads[t])
+        opt.step()
+        cur, m, v = oracle.adam(cur, grads[t], m, v, t + 1)
+    np.testing.assert_allclose(cur, p.detach().numpy(), rtol=1e-12, atol=1e-15)
+
+
+# ------------------------------------------------------------------------------------
+# culling
+# ------------------------------------------------------------------------------------
+
+def test_culled_gaussians_write_zeros_and_get_zero_gradients():
+    W = 32
+    cam = cam_at((3, 0, 0), W)
+    good = _one([0, 0, 0], [-2.5] * 3, [1, 0, 0, 0], 1.0, [0.5] * 3)
+    behind = _one([5, 0, 0], [-2.5] * 3, [1, 0, 0, 0], 1.0, [0.5] * 3)   # behind the camera
+    nan = good.copy(); nan[0] = np.nan
+    inf = good.copy(); inf[3] = np.inf
+    zq = good.copy(); zq[6:10] = 0.0
+    off = _one([0, 10, 0], [-2.5] * 3, [1, 0, 0, 0], 1.0, [0.5] * 3)     # far outside the image
+    P = np.stack([good, behind, nan, inf, zq, off], axis=1)
+    proj, radii, tiles = oracle.preprocess(P, 0, cam.flat(), W, W)
+    assert tiles[0] > 0 and (tiles[1:] == 0).all()
+    assert (proj[:, 1:] == 0).all() and (radii[:, 1:] == 0).all()
+    out = oracle.train_step_reference(P, 0, cam.flat(), W, W,
+                                      upstream=np.random.default_rng(0).uniform(-1, 1, (W, W, 3)))
+    assert np.abs(out["grads"][:, 0]).sum() > 0
+    assert (out["grads"][:, 1:] == 0).all()
