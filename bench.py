@@ -1,0 +1,289 @@
+#!/usr/bin/env python3
+"""Benchmark of one 3D Gaussian Splatting training step on one MI355X.
+
+A step is one pass of the whole hot path for one orbit view: preprocess -> bin/sort -> forward
+blend -> L1 loss -> backward blend -> preprocess backward fused with Adam, over the scene's
+Gaussians, with every input already resident in HBM.  Default workload: the 4M-Gaussian gyroid
+isosurface at 2048x2048 over the 448-view orbit (views taken in orbit order; targets rendered
+beforehand from a second seeded Gaussian set, untimed).
+
+Prints ONE JSON line on stdout (progress goes to stderr):
+  value        Gaussian-pixel blends per second over the timed steps (sum of n_examined, the
+               list entries each pixel's forward walk examines, / wall time)
+  ms_per_step  wall time per step
+  roofline     the dominant single-kernel phase against its roof (HBM bytes the method must
+               move / measured kernel time, from HIP events on the launch stream)
+  cpu_baseline the CPU oracle on a bounded sample of the same step (see cpu_baseline())
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "ms per fwd+bwd+Adam step and Gaussian-pixel blends/s, 4M Gaussians @2048^2"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def alg_bytes(phase, N, R, K, P, T, n_vis):
+    """Bytes the method itself must move per launch (reads + writes), by phase."""
+    if phase == "preprocess":          # params in; 48-B record + tiles + depth key out
+        return N * (4 * R + 56)
+    if phase == "forward":             # per entry: index + 36 B of record; per pixel: RGB, T, last
+        return K * 40 + P * 20 + T * 8
+    if phase == "loss":                # image + target in, dL/dI out
+        return P * 36
+    if phase == "backward_blend":      # entries + pixels (dL/dI, T, last) + grad2d zero + accumulate
+        return K * 40 + P * 20 + T * 8 + 36 * N + 36 * n_vis
+    if phase == "prebwd_adam":         # params, m, v, grad2d in; params, m, v out
+        return N * (24 * R + 36)
+    return 0
+
+
+def render_targets(gsmi, torch, cfg, cams, tparams_np, targets, log_every=64):
+    """Renders each view of the target Gaussian set into targets[v] (GPU forward; untimed)."""
+    R, n = tparams_np.shape
+    W = H = cfg.res
+    tp = torch.from_numpy(tparams_np).cuda()
+    buf = gsmi.StepBuffers(n, n, cfg.sh_degree, W, H, k_capacity=3 * n)
+    ks = []
+    for vi, cam in enumerate(cams):
+        c = gsmi.make_camera(cam)
+        gsmi.preprocess(buf.scene, tp, c, buf.proj)
+        while True:
+            try:
+                K = gsmi.bin_and_sort(buf.scene, c, buf.proj, buf.ws, buf.k_capacity, buf.vals, buf.ranges)
+                break
+            except gsmi.GsCapacityError as e:
+                buf.grow(int(e.required * 1.25) + 1024)
+        gsmi.render_forward(c, n, buf.proj.splat, buf.vals, buf.ranges, (0.0, 0.0, 0.0), targets[vi], buf.T_final,
+                            buf.last)
+        ks.append(K)
+        if vi % log_every == 0:
+            log(f"  target view {vi}: K = {K}")
+    torch.cuda.synchronize()
+    del tp, buf
+    return ks
+
+
+def tile_histogram(ranges_np):
+    lens = (ranges_np[:, 1].astype(np.int64) - ranges_np[:, 0].astype(np.int64))
+    q = np.percentile(lens, [0, 50, 90, 99, 100]).tolist()
+    edges = [0] + [2 ** k for k in range(0, 16)]
+    hist = np.histogram(lens, bins=edges + [1 << 40])[0].tolist()
+    return {"min": q[0], "median": q[1], "p90": q[2], "p99": q[3], "max": q[4],
+            "log2_bins": {f"<{e}": h for e, h in zip(edges[1:] + ["inf"], hist)}}
+
+
+def cpu_baseline(cfg, params_np, cam, blends_full, crop=512):
+    """The CPU oracle (test infrastructure, untouched) on a bounded sample of one step:
+    every per-Gaussian stage over all N Gaussians (preprocess, preprocess backward, Adam) and
+    the per-pixel stages (bin/sort, ranges, forward, L1, backward blend) on a crop x crop
+    window at the image centre; the window's time is scaled by full-image blends / window
+    blends to one full step."""
+    import oracle
+
+    oracle.build()
+    threads = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+    deg, W = cfg.sh_degree, cfg.res
+    p64 = params_np.astype(np.float64)
+    c = cam.flat()
+    t0 = time.perf_counter()
+    oracle.preprocess(p64, deg, c, W, W)
+    t_pre = time.perf_counter() - t0
+    # the crop camera: same pose and focal length, principal point shifted to the window
+    off = (W - crop) / 2.0
+    cc = c.copy()
+    cc[14] -= off
+    cc[15] -= off
+    proj, radii, _ = oracle.preprocess(p64, deg, cc, crop, crop)
+    target = np.zeros((crop, crop, 3))
+    t0 = time.perf_counter()
+    keys, vals = oracle.bin_sort(proj, radii, crop, crop)
+    rg = oracle.ranges(keys, oracle.n_tiles(crop, crop))
+    fwd = oracle.render_forward(proj, vals, rg, crop, crop)
+    _, dLdI = oracle.loss_l1(fwd["image"], target)
+    g2 = oracle.render_backward(proj, vals, rg, crop, crop, dLdI)
+    t_pix = time.perf_counter() - t0
+    blends_crop = int(fwd["n_examined"].astype(np.int64).sum())
+    t0 = time.perf_counter()
+    grads = oracle.preprocess_backward(p64, deg, c, W, W, np.zeros((9, p64.shape[1])))
+    t_pb = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.adam(p64, grads, np.zeros_like(p64), np.zeros_like(p64), 1)
+    t_adam = time.perf_counter() - t0
+    scale = blends_full / max(blends_crop, 1)
+    sec = t_pre + t_pb + t_adam + t_pix * scale
+    sample = (f"all {p64.shape[1]} Gaussians for preprocess ({t_pre:.2f} s), preprocess backward "
+              f"({t_pb:.2f} s) and Adam ({t_adam:.2f} s); bin/sort/forward/L1/backward blend on the "
+              f"central {crop}x{crop} window of view 0 ({t_pix:.2f} s, {blends_crop} blends) scaled by "
+              f"{scale:.1f} to the full image's {blends_full} blends")
+    return {"value": blends_full / sec, "unit": "Gaussian-pixel blends/s", "cores": threads, "kind": "oracle",
+            "sample": sample, "ms_per_step": sec * 1e3}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=448)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="gyroid_4m_2048")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--unfused-adam", action="store_true", help="separate Adam kernel instead of the fused one")
+    ap.add_argument("--detail", default=None, help="write a detailed JSON record to this path")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs the single-GPU hot path only: one MI355X holds the whole scene "
+              "(4M or 18.18M Gaussians); the multi-GPU exchange is design only. Use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from gaussian_splatting_differentiable_preprocess_amd import gsmi, inputs
+
+    gsmi.load()
+    torch.cuda.set_device(0)
+    cfg = inputs.CONFIGS[args.config]
+    W = H = cfg.res
+    P = W * H
+    T = gsmi.n_tiles(W, H)
+    log(f"[bench] {cfg.name}: generating {cfg.n} Gaussians (scene) ...")
+    t0 = time.time()
+    params_np = inputs.gaussian_params(cfg)
+    log(f"[bench]   {time.time() - t0:.1f} s; target set ...")
+    tparams_np = inputs.gaussian_params(cfg, inputs.STREAM_TARGET)
+    cams = inputs.cameras_for(cfg)
+    V = len(cams)
+    R, N = params_np.shape
+    log(f"[bench] rendering {V} target views at {W}x{H} ...")
+    targets = torch.empty((V, H, W, 3), dtype=torch.float32, device="cuda")
+    tks = render_targets(gsmi, torch, cfg, cams, tparams_np, targets)
+    del tparams_np
+
+    p = torch.from_numpy(params_np).cuda()
+    m = torch.zeros_like(p)
+    v = torch.zeros_like(p)
+    kcap = int(1.5 * max(tks)) + 4096
+    buf = gsmi.StepBuffers(N, N, cfg.sh_degree, W, H, k_capacity=kcap)
+    grads = torch.empty_like(p) if args.unfused_adam else None
+    gcams = [gsmi.make_camera(c) for c in cams]
+    blends = torch.zeros(1, dtype=torch.int64, device="cuda")
+    bg = (0.0, 0.0, 0.0)
+    phases = ["preprocess", "bin_and_sort", "forward", "loss", "backward_blend", "prebwd_adam"]
+
+    def step(t, view, ev=None):
+        cam = gcams[view]
+        if ev is not None:
+            ev[0].record()
+        gsmi.preprocess(buf.scene, p, cam, buf.proj)
+        if ev is not None:
+            ev[1].record()
+        K = gsmi.bin_and_sort(buf.scene, cam, buf.proj, buf.ws, buf.k_capacity, buf.vals, buf.ranges)
+        if ev is not None:
+            ev[2].record()
+        gsmi.render_forward(cam, N, buf.proj.splat, buf.vals, buf.ranges, bg, buf.image, buf.T_final, buf.last,
+                            blend_count=blends)
+        if ev is not None:
+            ev[3].record()
+        gsmi.loss_l1(3 * P, buf.image, targets[view], buf.loss, buf.dLdI, buf.loss_ws)
+        if ev is not None:
+            ev[4].record()
+        gsmi.render_backward(buf.scene, None, cam, buf.proj, buf.vals, buf.ranges, bg, buf.T_final, buf.last,
+                             buf.dLdI, buf.grad2d)
+        if ev is not None:
+            ev[5].record()
+        adam = gsmi.make_adam(m, v, t, 1e-3)
+        if args.unfused_adam:
+            gsmi.preprocess_backward(buf.scene, p, cam, buf.grad2d, grads)
+            gsmi.adam_step(R * N, p, grads, adam)
+        else:
+            gsmi.preprocess_backward(buf.scene, p, cam, buf.grad2d, None, adam)
+        if ev is not None:
+            ev[6].record()
+        return K
+
+    log(f"[bench] warmup {args.warmup} steps ...")
+    t = 0
+    for w in range(args.warmup):
+        t += 1
+        step(t, w % V)
+    torch.cuda.synchronize()
+    blends.zero_()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    ks = []
+    log(f"[bench] timing {args.steps} steps ...")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        t += 1
+        ks.append(step(t, (args.warmup + k) % V, evs[k]))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_blends = int(blends.item())
+    ms_per_step = wall * 1e3 / args.steps
+    ph_ms = {ph: float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)]))
+             for i, ph in enumerate(phases)}
+    log("[bench] per-phase ms: " + ", ".join(f"{k} {v:.3f}" for k, v in ph_ms.items()))
+    log(f"[bench] {ms_per_step:.3f} ms/step, {total_blends / wall:.4g} blends/s, K mean {np.mean(ks):.0f}")
+
+    # roofline of the dominant single-kernel phase (bin_and_sort is a multi-kernel phase)
+    Kmean = float(np.mean(ks))
+    n_vis = N
+    single = {ph: ph_ms[ph] for ph in ("preprocess", "forward", "backward_blend", "prebwd_adam")}
+    dom = max(single, key=single.get)
+    bytes_dom = alg_bytes(dom, N, R, Kmean, P, T, n_vis)
+    achieved = bytes_dom / (ph_ms[dom] * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom,
+            "alg_bytes_per_launch": int(bytes_dom), "ms_per_launch": round(ph_ms[dom], 4)}
+    per_phase = {ph: {"ms": round(ph_ms[ph], 4),
+                      "alg_GBps": round(alg_bytes(ph, N, R, Kmean, P, T, n_vis) / (ph_ms[ph] * 1e-3) / 1e9, 1)}
+                 for ph in phases}
+
+    # K and tile-load statistics for the last view (untimed)
+    rng_np = buf.ranges.cpu().numpy()
+    hist = tile_histogram(rng_np)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle baseline on a bounded sample ...")
+        view = 0
+        blends.zero_()
+        step(t + 1, view)  # one untimed step to count view 0's blends at full resolution
+        torch.cuda.synchronize()
+        cpu = cpu_baseline(cfg, params_np, cams[view], int(blends.item()))
+        log(f"[bench] CPU oracle: {cpu['ms_per_step']:.0f} ms/step-equivalent on {cpu['cores']} threads")
+
+    out = {
+        "metric": METRIC, "value": total_blends / wall, "unit": "Gaussian-pixel blends/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": cfg.name, "gaussians": N, "sh_degree": cfg.sh_degree, "resolution": [W, H],
+                   "views": V, "loss": "l1", "adam": "fused" if not args.unfused_adam else "separate",
+                   "intersections_mean": round(Kmean), "intersections_min": int(min(ks)),
+                   "intersections_max": int(max(ks))},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    if args.detail:
+        with open(args.detail, "w") as f:
+            json.dump(dict(out, per_phase=per_phase, tile_list_lengths=hist, target_K=tks), f, indent=1)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,547 @@
+// Tile binning, stable (tile, depth) sort and per-tile ranges, for gfx950.
+//
+// What is computed ("Scaling 3D Gaussian Splatting with Distributed Compute": the memory
+// accounting passage on per-tile sorted intersection lists, and the trace section on
+// intersect_offset_kernel, which finds each tile's offsets in the sorted list): every visible
+// Gaussian i emits one intersection per tile of its 3-sigma box with key
+// (tile << 32) | bits(depth_i) and value i; the intersections are sorted ascending by key,
+// ties in emission order (Gaussian index), and ranges[t] is tile t's [start, end).
+//
+// How.  An LSD radix sort of the 64-bit key visits the depth bits before the tile bits.  All
+// intersections of one Gaussian share its depth, so the depth passes run over the N Gaussians
+// instead of the K >= N intersections: stable depth passes give the Gaussians in (depth,
+// index) order, the intersections are then emitted in that order (scan + key generation), and
+// stable passes over the tile bits finish the sort.  The result is exactly the stable sort of
+// the 64-bit keys.  Only the depth bits that vary are sorted: the passes run over
+// clamp(key, dmin, dmax) - dmin, which keeps the order of every visible Gaussian.
+//
+// Radix passes are reduce-then-scan with 8-bit digits: a histogram kernel (LDS atomics), a
+// per-digit scan over blocks, and a scatter kernel that ranks each 4096-item block stably
+// (wave64 ballot match of the digit per round of 256 items), sorts the block in LDS and writes
+// runs of equal digits contiguously.  All kernels are HBM-bound.
+#include "gsmi_internal.h"
+
+namespace gsmi {
+
+namespace {
+
+constexpr int kItems = 16;                   // items per thread in a radix block
+constexpr int kRadixTile = kBlock * kItems;  // 4096 items per radix block
+constexpr int kGatherItems = 8;              // items per thread in gather/keygen
+constexpr int kGatherTile = kBlock * kGatherItems;
+constexpr int kReduceTile = kBlock * 16;
+
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+// Block-wide exclusive scan of one uint32 per thread (256 threads); returns the prefix and
+// writes the total to *total.  Uses `tmp` (>= 4 entries of LDS).
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, uint32_t* tmp, uint32_t* total) {
+  const int lane = threadIdx.x & 63, w = wave_id();
+  uint32_t incl = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) tmp[w] = incl;
+  __syncthreads();
+  uint32_t wpre = 0, tot = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t t = tmp[k];
+    wpre += (k < w) ? t : 0u;
+    tot += t;
+  }
+  __syncthreads();
+  *total = tot;
+  return wpre + incl - x;
+}
+
+// ---- reduction: K and the depth-key range over visible Gaussians -----------------------
+struct Partial {
+  unsigned long long sum;
+  uint32_t mn, mx;
+};
+
+__global__ __launch_bounds__(kBlock) void k_bin_reduce(int64_t n, const uint32_t* __restrict__ tiles,
+                                                        const uint32_t* __restrict__ dkey,
+                                                        Partial* __restrict__ part) {
+  __shared__ unsigned long long ssum[kBlock / 64];
+  __shared__ uint32_t smn[kBlock / 64], smx[kBlock / 64];
+  const int64_t base = (int64_t)blockIdx.x * kReduceTile;
+  unsigned long long s = 0;
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+  for (int j = 0; j < kReduceTile / kBlock; ++j) {
+    const int64_t i = base + j * kBlock + threadIdx.x;
+    if (i < n) {
+      const uint32_t t = tiles[i];
+      s += t;
+      if (t > 0) {
+        const uint32_t k = dkey[i];
+        mn = min(mn, k);
+        mx = max(mx, k);
+      }
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    s += __shfl_xor(s, o, 64);
+    mn = min(mn, (uint32_t)__shfl_xor(mn, o, 64));
+    mx = max(mx, (uint32_t)__shfl_xor(mx, o, 64));
+  }
+  if ((threadIdx.x & 63) == 0) {
+    ssum[wave_id()] = s;
+    smn[wave_id()] = mn;
+    smx[wave_id()] = mx;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    Partial p{0ull, 0xFFFFFFFFu, 0u};
+    for (int k = 0; k < kBlock / 64; ++k) {
+      p.sum += ssum[k];
+      p.mn = min(p.mn, smn[k]);
+      p.mx = max(p.mx, smx[k]);
+    }
+    part[blockIdx.x] = p;
+  }
+}
+
+__global__ __launch_bounds__(1024) void k_bin_reduce_final(int64_t nblk, const Partial* __restrict__ part,
+                                                            BinInfo* __restrict__ info) {
+  __shared__ unsigned long long ssum[16];
+  __shared__ uint32_t smn[16], smx[16];
+  unsigned long long s = 0;
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+  for (int64_t b = threadIdx.x; b < nblk; b += 1024) {
+    const Partial p = part[b];
+    s += p.sum;
+    mn = min(mn, p.mn);
+    mx = max(mx, p.mx);
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    s += __shfl_xor(s, o, 64);
+    mn = min(mn, (uint32_t)__shfl_xor(mn, o, 64));
+    mx = max(mx, (uint32_t)__shfl_xor(mx, o, 64));
+  }
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    ssum[w] = s;
+    smn[w] = mn;
+    smx[w] = mx;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    BinInfo r{0ull, 0xFFFFFFFFu, 0u};
+    for (int k = 0; k < 16; ++k) {
+      r.K += ssum[k];
+      r.dmin = min(r.dmin, smn[k]);
+      r.dmax = max(r.dmax, smx[k]);
+    }
+    *info = r;
+  }
+}
+
+// ---- radix sort passes --------------------------------------------------------------------
+// Key transform of the first depth pass: clamp(k, lo, hi) - lo.
+__device__ __forceinline__ uint32_t xform_key(uint32_t k, bool xform, uint32_t lo, uint32_t hi) {
+  return xform ? (min(max(k, lo), hi) - lo) : k;
+}
+
+__global__ __launch_bounds__(kBlock) void k_radix_hist(const uint32_t* __restrict__ keys, int64_t n,
+                                                        int shift, int xform, uint32_t lo, uint32_t hi,
+                                                        uint32_t* __restrict__ counts, int64_t nblk) {
+  __shared__ uint32_t hist[4][256];
+  for (int e = threadIdx.x; e < 4 * 256; e += kBlock) (&hist[0][0])[e] = 0;
+  __syncthreads();
+  const int64_t base = (int64_t)blockIdx.x * kRadixTile;
+  const int w = wave_id();
+#pragma unroll 4
+  for (int j = 0; j < kItems; ++j) {
+    const int64_t idx = base + j * kBlock + threadIdx.x;
+    if (idx < n) {
+      const uint32_t k = xform_key(keys[idx], xform != 0, lo, hi);
+      atomicAdd(&hist[w][(k >> shift) & 255u], 1u);
+    }
+  }
+  __syncthreads();
+  const int d = threadIdx.x;
+  counts[(int64_t)d * nblk + blockIdx.x] = hist[0][d] + hist[1][d] + hist[2][d] + hist[3][d];
+}
+
+// One workgroup per digit: exclusive scan of counts[d][0..nblk) in place; totals[d] = sum.
+__global__ __launch_bounds__(kBlock) void k_radix_scan(uint32_t* __restrict__ counts, int64_t nblk,
+                                                        uint32_t* __restrict__ totals) {
+  __shared__ uint32_t tmp[4];
+  uint32_t* c = counts + (int64_t)blockIdx.x * nblk;
+  const int64_t per = ceil_div(nblk, kBlock);
+  const int64_t lo = threadIdx.x * per, hi = min(lo + per, nblk);
+  uint32_t s = 0;
+  for (int64_t b = lo; b < hi; ++b) s += c[b];
+  uint32_t tot;
+  uint32_t run = block_excl_scan(s, tmp, &tot);
+  for (int64_t b = lo; b < hi; ++b) {
+    const uint32_t x = c[b];
+    c[b] = run;
+    run += x;
+  }
+  if (threadIdx.x == 0) totals[blockIdx.x] = tot;
+}
+
+__global__ __launch_bounds__(kBlock) void k_radix_scatter(
+    const uint32_t* __restrict__ keys_in, const uint32_t* __restrict__ vals_in, int64_t n, int shift,
+    int xform, uint32_t lo, uint32_t hi, const uint32_t* __restrict__ counts,
+    const uint32_t* __restrict__ totals, int64_t nblk, uint32_t* __restrict__ keys_out,
+    uint32_t* __restrict__ vals_out) {
+  __shared__ uint32_t s_keys[kRadixTile];
+  __shared__ uint32_t s_vals[kRadixTile];
+  __shared__ uint32_t wcnt[4][256];
+  __shared__ uint32_t woff[4][256];
+  __shared__ uint32_t running[256];
+  __shared__ uint32_t gbase[256];
+  __shared__ uint32_t lstart[256];
+  __shared__ uint32_t tmp[4];
+
+  const int tid = threadIdx.x, w = wave_id(), lane = tid & 63;
+  const int64_t base = (int64_t)blockIdx.x * kRadixTile;
+
+  // global start of each digit's run for this block
+  {
+    uint32_t tot;
+    const uint32_t dbase = block_excl_scan(totals[tid], tmp, &tot);
+    gbase[tid] = dbase + counts[(int64_t)tid * nblk + blockIdx.x];
+    running[tid] = 0;
+    for (int k = 0; k < 4; ++k) wcnt[k][tid] = 0;
+  }
+  __syncthreads();
+
+  uint32_t mk[kItems], mv[kItems], mr[kItems];
+  const unsigned long long lt = __lanemask_lt();
+#pragma unroll
+  for (int r = 0; r < kItems; ++r) {
+    const int64_t idx = base + r * kBlock + tid;
+    const bool valid = idx < n;
+    uint32_t k = 0, v = 0;
+    if (valid) {
+      k = xform_key(keys_in[idx], xform != 0, lo, hi);
+      v = vals_in ? vals_in[idx] : (uint32_t)idx;
+    }
+    const uint32_t d = (k >> shift) & 255u;
+    // lanes of this wave holding the same digit
+    unsigned long long peers = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const bool bit = (d >> b) & 1u;
+      const unsigned long long bb = __ballot(bit);
+      peers &= bit ? bb : ~bb;
+    }
+    const uint32_t rank = (uint32_t)__popcll(peers & lt);
+    if (valid && rank == 0) wcnt[w][d] = (uint32_t)__popcll(peers);
+    __syncthreads();
+    {
+      const uint32_t c0 = wcnt[0][tid], c1 = wcnt[1][tid], c2 = wcnt[2][tid], c3 = wcnt[3][tid];
+      const uint32_t run = running[tid];
+      woff[0][tid] = run;
+      woff[1][tid] = run + c0;
+      woff[2][tid] = run + c0 + c1;
+      woff[3][tid] = run + c0 + c1 + c2;
+      running[tid] = run + c0 + c1 + c2 + c3;
+      wcnt[0][tid] = wcnt[1][tid] = wcnt[2][tid] = wcnt[3][tid] = 0;
+    }
+    __syncthreads();
+    mk[r] = k;
+    mv[r] = v;
+    mr[r] = valid ? woff[w][d] + rank : 0xFFFFFFFFu;
+  }
+  (void)lane;
+  // local start of each digit inside the block
+  {
+    uint32_t tot;
+    lstart[tid] = block_excl_scan(running[tid], tmp, &tot);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < kItems; ++r) {
+    if (mr[r] != 0xFFFFFFFFu) {
+      const uint32_t d = (mk[r] >> shift) & 255u;
+      const uint32_t pos = lstart[d] + mr[r];
+      s_keys[pos] = mk[r];
+      s_vals[pos] = mv[r];
+    }
+  }
+  __syncthreads();
+  const int64_t cnt = min((int64_t)kRadixTile, n - base);
+  for (int j = tid; j < cnt; j += kBlock) {
+    const uint32_t k = s_keys[j];
+    const uint32_t d = (k >> shift) & 255u;
+    const uint32_t g = gbase[d] + ((uint32_t)j - lstart[d]);
+    if ((int64_t)g < n) {  // always true for a consistent histogram; keeps writes in bounds
+      if (keys_out) keys_out[g] = k;
+      vals_out[g] = s_vals[j];
+    }
+  }
+}
+
+// ---- emission of intersections in depth order ---------------------------------------------
+__device__ __forceinline__ uint32_t rect_count(uint2 r) {
+  const uint32_t x0 = r.x & 0xFFFFu, y0 = r.x >> 16, x1 = r.y & 0xFFFFu, y1 = r.y >> 16;
+  return (x1 > x0 && y1 > y0) ? (x1 - x0) * (y1 - y0) : 0u;
+}
+
+// rect_sorted[k] = tile rect of Gaussian order[k] (packed 16-bit x0|y0, x1|y1); bsum[block] =
+// intersections of the block's items.
+__global__ __launch_bounds__(kBlock) void k_gather_rect(const uint32_t* __restrict__ order, int64_t n,
+                                                         const float4* __restrict__ splat, int TX,
+                                                         int TY, uint2* __restrict__ rect_sorted,
+                                                         uint32_t* __restrict__ bsum) {
+  __shared__ uint32_t tmp[4];
+  const int64_t base = (int64_t)blockIdx.x * kGatherTile + (int64_t)threadIdx.x * kGatherItems;
+  uint32_t s = 0;
+#pragma unroll
+  for (int j = 0; j < kGatherItems; ++j) {
+    const int64_t k = base + j;
+    if (k < n) {
+      const uint32_t i = order[k];
+      const float4 q0 = splat[3 * (int64_t)i];  // u, v, radius_x, radius_y
+      const int rx = __float_as_int(q0.z), ry = __float_as_int(q0.w);
+      uint2 r = make_uint2(0u, 0u);
+      if (rx > 0 && ry > 0) {
+        int x0, y0, x1, y1;
+        tile_rect(q0.x, q0.y, rx, ry, TX, TY, x0, y0, x1, y1);
+        r = make_uint2((uint32_t)x0 | ((uint32_t)y0 << 16), (uint32_t)x1 | ((uint32_t)y1 << 16));
+      }
+      rect_sorted[k] = r;
+      s += rect_count(r);
+    }
+  }
+  uint32_t tot;
+  block_excl_scan(s, tmp, &tot);
+  if (threadIdx.x == 0) bsum[blockIdx.x] = tot;
+}
+
+// Exclusive scan of bsum[0..nblk) in place by one 1024-thread workgroup.
+__global__ __launch_bounds__(1024) void k_scan_blocks(uint32_t* __restrict__ bsum, int64_t nblk) {
+  __shared__ uint32_t part[1024];
+  const int64_t per = ceil_div(nblk, 1024);
+  const int64_t lo = threadIdx.x * per, hi = min(lo + per, nblk);
+  uint32_t s = 0;
+  for (int64_t b = lo; b < hi; ++b) s += bsum[b];
+  part[threadIdx.x] = s;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const uint32_t y = threadIdx.x >= (unsigned)o ? part[threadIdx.x - o] : 0u;
+    __syncthreads();
+    part[threadIdx.x] += y;
+    __syncthreads();
+  }
+  uint32_t run = part[threadIdx.x] - s;
+  for (int64_t b = lo; b < hi; ++b) {
+    const uint32_t x = bsum[b];
+    bsum[b] = run;
+    run += x;
+  }
+}
+
+// Writes the intersections of Gaussians order[k] (in depth order) at their scanned slots:
+// tile id (row-major over the rect) and Gaussian index.  Writes past kcap are dropped.
+__global__ __launch_bounds__(kBlock) void k_keygen(const uint2* __restrict__ rect_sorted,
+                                                    const uint32_t* __restrict__ order, int64_t n,
+                                                    const uint32_t* __restrict__ bsum, int TX,
+                                                    int64_t kcap, uint32_t* __restrict__ tkeys,
+                                                    uint32_t* __restrict__ tvals) {
+  __shared__ uint32_t tmp[4];
+  const int64_t base = (int64_t)blockIdx.x * kGatherTile + (int64_t)threadIdx.x * kGatherItems;
+  uint2 r[kGatherItems];
+  uint32_t s = 0;
+#pragma unroll
+  for (int j = 0; j < kGatherItems; ++j) {
+    r[j] = (base + j < n) ? rect_sorted[base + j] : make_uint2(0u, 0u);
+    s += rect_count(r[j]);
+  }
+  uint32_t tot;
+  const uint32_t pre = block_excl_scan(s, tmp, &tot);
+  int64_t slot = (int64_t)bsum[blockIdx.x] + pre;
+#pragma unroll
+  for (int j = 0; j < kGatherItems; ++j) {
+    const uint32_t c = rect_count(r[j]);
+    if (c == 0) continue;
+    const uint32_t i = order[base + j];
+    const uint32_t x0 = r[j].x & 0xFFFFu, y0 = r[j].x >> 16, x1 = r[j].y & 0xFFFFu, y1 = r[j].y >> 16;
+    for (uint32_t ty = y0; ty < y1; ++ty)
+      for (uint32_t tx = x0; tx < x1; ++tx) {
+        if (slot < kcap) {
+          tkeys[slot] = ty * (uint32_t)TX + tx;
+          tvals[slot] = i;
+        }
+        ++slot;
+      }
+  }
+}
+
+// ranges[2t], ranges[2t+1] = first and one-past-last position of tile t (ranges pre-zeroed).
+__global__ __launch_bounds__(kBlock) void k_ranges(const uint32_t* __restrict__ tk, int64_t K,
+                                                    uint32_t T, uint32_t* __restrict__ ranges) {
+  const int64_t j = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (j >= K) return;
+  const uint32_t t = tk[j];
+  if (t >= T) return;
+  if (j == 0 || tk[j - 1] != t) ranges[2 * (int64_t)t] = (uint32_t)j;
+  if (j == K - 1 || tk[j + 1] != t) ranges[2 * (int64_t)t + 1] = (uint32_t)(j + 1);
+}
+
+__global__ __launch_bounds__(kBlock) void k_iota(uint32_t* __restrict__ out, int64_t n) {
+  const int64_t j = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (j < n) out[j] = (uint32_t)j;
+}
+
+__global__ __launch_bounds__(kBlock) void k_keys64(const uint32_t* __restrict__ tk,
+                                                    const uint32_t* __restrict__ vals,
+                                                    const uint32_t* __restrict__ dkey, int64_t K,
+                                                    int64_t n, uint64_t* __restrict__ keys) {
+  const int64_t j = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (j >= K) return;
+  const uint32_t i = vals[j];
+  keys[j] = ((uint64_t)tk[j] << 32) | (uint64_t)((int64_t)i < n ? dkey[i] : 0xFFFFFFFFu);
+}
+
+// One stable radix pass over bits [shift, shift+8) of n items.
+hipError_t radix_pass(const uint32_t* kin, const uint32_t* vin, int64_t n, int shift, bool xform,
+                      uint32_t lo, uint32_t hi, uint32_t* counts, uint32_t* totals, uint32_t* kout,
+                      uint32_t* vout, hipStream_t s) {
+  const int64_t nblk = ceil_div(n, kRadixTile);
+  hipLaunchKernelGGL(k_radix_hist, dim3((unsigned)nblk), dim3(kBlock), 0, s, kin, n, shift,
+                     (int)xform, lo, hi, counts, nblk);
+  hipLaunchKernelGGL(k_radix_scan, dim3(256), dim3(kBlock), 0, s, counts, nblk, totals);
+  hipLaunchKernelGGL(k_radix_scatter, dim3((unsigned)nblk), dim3(kBlock), 0, s, kin, vin, n, shift,
+                     (int)xform, lo, hi, counts, totals, nblk, kout, vout);
+  return hipGetLastError();
+}
+
+size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+BinLayout bin_layout(int64_t n, int64_t kcap, int32_t W, int32_t H) {
+  (void)W;
+  (void)H;
+  BinLayout L{};
+  const int64_t nr = ceil_div(n > 0 ? n : 1, kReduceTile);
+  L.nblk_n = ceil_div(n > 0 ? n : 1, kRadixTile);
+  L.nblk_k = ceil_div(kcap > 0 ? kcap : 1, kRadixTile);
+  L.nblk_rect = ceil_div(n > 0 ? n : 1, kGatherTile);
+  const int64_t nn = n > 0 ? n : 1, kk = kcap > 0 ? kcap : 1;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  L.partials = take(sizeof(Partial) * nr);
+  L.info = take(sizeof(BinInfo));
+  L.dkA = take(4 * nn);
+  L.dvA = take(4 * nn);
+  L.dkB = take(4 * nn);
+  L.dvB = take(4 * nn);
+  L.counts = take(4 * 256 * (L.nblk_n > L.nblk_k ? L.nblk_n : L.nblk_k));
+  L.totals = take(4 * 256);
+  L.rect = take(8 * nn);
+  L.bsum = take(4 * (L.nblk_rect + 1));
+  L.tkA = take(4 * kk);
+  L.tvA = take(4 * kk);
+  L.tkB = take(4 * kk);
+  L.tvB = take(4 * kk);
+  L.total = off;
+  return L;
+}
+
+hipError_t launch_bin_reduce(int64_t n, const uint32_t* tiles, const uint32_t* dkey, char* ws,
+                             const BinLayout& L, hipStream_t s) {
+  const int64_t nr = ceil_div(n > 0 ? n : 1, kReduceTile);
+  Partial* part = reinterpret_cast<Partial*>(ws + L.partials);
+  if (n > 0)
+    hipLaunchKernelGGL(k_bin_reduce, dim3((unsigned)nr), dim3(kBlock), 0, s, n, tiles, dkey, part);
+  hipLaunchKernelGGL(k_bin_reduce_final, dim3(1), dim3(1024), 0, s, n > 0 ? nr : 0, part,
+                     reinterpret_cast<BinInfo*>(ws + L.info));
+  return hipGetLastError();
+}
+
+hipError_t launch_bin_sort_rest(int64_t n, int64_t K, const BinInfo& info, const CamK& cam,
+                                gs_proj proj, char* ws, const BinLayout& L, uint32_t* vals,
+                                uint32_t* ranges, uint64_t* keys, hipStream_t s) {
+  hipError_t e;
+  const int64_t T = (int64_t)cam.TX * cam.TY;
+  if ((e = launch_fill_u32(ranges, 2 * T, 0u, s)) != hipSuccess) return e;
+  if (K == 0) return hipSuccess;
+  uint32_t* counts = reinterpret_cast<uint32_t*>(ws + L.counts);
+  uint32_t* totals = reinterpret_cast<uint32_t*>(ws + L.totals);
+
+  // 1. stable depth passes over the N Gaussians (only the bits of dmax - dmin)
+  const uint32_t span = info.dmax - info.dmin;
+  const int dbits = span == 0 ? 0 : 32 - __builtin_clz(span);
+  const int dpasses = (dbits + 7) / 8;
+  uint32_t* kA = reinterpret_cast<uint32_t*>(ws + L.dkA);
+  uint32_t* vA = reinterpret_cast<uint32_t*>(ws + L.dvA);
+  uint32_t* kB = reinterpret_cast<uint32_t*>(ws + L.dkB);
+  uint32_t* vB = reinterpret_cast<uint32_t*>(ws + L.dvB);
+  const uint32_t* order = nullptr;  // Gaussian indices in (depth, index) order; null = identity
+  {
+    const uint32_t* kin = proj.depth_key;
+    const uint32_t* vin = nullptr;
+    for (int p = 0; p < dpasses; ++p) {
+      const bool last = p == dpasses - 1;
+      uint32_t* ko = (p & 1) ? kA : kB;
+      uint32_t* vo = (p & 1) ? vA : vB;
+      if ((e = radix_pass(kin, vin, n, 8 * p, p == 0, info.dmin, info.dmax, counts, totals,
+                          last ? nullptr : ko, vo, s)) != hipSuccess)
+        return e;
+      kin = ko;
+      vin = vo;
+    }
+    order = vin;
+  }
+  if (order == nullptr) {
+    // no depth bits vary: (depth, index) order is the index order
+    hipLaunchKernelGGL(k_iota, dim3((unsigned)ceil_div(n, kBlock)), dim3(kBlock), 0, s, vA, n);
+    order = vA;
+  }
+
+  // 2. emission in depth order: rects, block sums, scan, keys
+  uint2* rect = reinterpret_cast<uint2*>(ws + L.rect);
+  uint32_t* bsum = reinterpret_cast<uint32_t*>(ws + L.bsum);
+  const int64_t nb = ceil_div(n, kGatherTile);
+  const float4* sp = reinterpret_cast<const float4*>(proj.splat);
+  hipLaunchKernelGGL(k_gather_rect, dim3((unsigned)nb), dim3(kBlock), 0, s, order, n, sp, cam.TX,
+                     cam.TY, rect, bsum);
+  hipLaunchKernelGGL(k_scan_blocks, dim3(1), dim3(1024), 0, s, bsum, nb);
+  uint32_t* tkA = reinterpret_cast<uint32_t*>(ws + L.tkA);
+  uint32_t* tvA = reinterpret_cast<uint32_t*>(ws + L.tvA);
+  uint32_t* tkB = reinterpret_cast<uint32_t*>(ws + L.tkB);
+  uint32_t* tvB = reinterpret_cast<uint32_t*>(ws + L.tvB);
+  hipLaunchKernelGGL(k_keygen, dim3((unsigned)nb), dim3(kBlock), 0, s, rect, order, n, bsum, cam.TX,
+                     K, tkA, tvA);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+
+  // 3. stable tile passes over the K intersections; the last pass writes `vals`
+  const uint32_t tmax = (uint32_t)(T - 1);
+  const int tbits = tmax == 0 ? 1 : 32 - __builtin_clz(tmax);
+  const int tpasses = (tbits + 7) / 8;
+  const uint32_t* kin = tkA;
+  const uint32_t* vin = tvA;
+  for (int p = 0; p < tpasses; ++p) {
+    const bool last = p == tpasses - 1;
+    uint32_t* ko = (p & 1) ? tkA : tkB;
+    uint32_t* vo = last ? vals : ((p & 1) ? tvA : tvB);
+    if ((e = radix_pass(kin, vin, K, 8 * p, false, 0u, 0u, counts, totals, ko, vo, s)) != hipSuccess)
+      return e;
+    kin = ko;
+    vin = vo;
+  }
+  const uint32_t* tsorted = kin;
+
+  // 4. per-tile ranges and the optional 64-bit keys
+  const unsigned gk = (unsigned)ceil_div(K, kBlock);
+  hipLaunchKernelGGL(k_ranges, dim3(gk), dim3(kBlock), 0, s, tsorted, K, (uint32_t)T, ranges);
+  if (keys)
+    hipLaunchKernelGGL(k_keys64, dim3(gk), dim3(kBlock), 0, s, tsorted, vals, proj.depth_key, K, n, keys);
+  return hipGetLastError();
+}
+
+}  // namespace gsmi

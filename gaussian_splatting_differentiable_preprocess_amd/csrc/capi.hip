@@ -1,0 +1,276 @@
+// C ABI of libgsmi.so: argument validation, launch geometry and error reporting around the
+// kernels.  Every function checks its arguments before touching HIP, enqueues on the
+// caller's stream and returns a gs_status; no exception crosses the boundary.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "gsmi_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  return fail(GS_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return GS_OK;
+}
+
+bool finite(float x) { return std::isfinite(x); }
+
+int check_camera(const gs_camera* c) {
+  if (!c) return fail(GS_ERR_INVALID_ARGUMENT, "camera is null");
+  for (int k = 0; k < 12; ++k)
+    if (!finite(c->viewmat[k])) return fail(GS_ERR_INVALID_ARGUMENT, "camera viewmat[%d] not finite", k);
+  if (!(finite(c->fx) && c->fx > 0.f && finite(c->fy) && c->fy > 0.f))
+    return fail(GS_ERR_INVALID_ARGUMENT, "camera focal lengths must be finite and > 0");
+  if (!(finite(c->cx) && finite(c->cy))) return fail(GS_ERR_INVALID_ARGUMENT, "camera principal point not finite");
+  if (!(finite(c->near_plane) && c->near_plane > 0.f))
+    return fail(GS_ERR_INVALID_ARGUMENT, "camera near_plane must be finite and > 0");
+  if (c->width < 1 || c->height < 1 || c->width > 32768 || c->height > 32768)
+    return fail(GS_ERR_INVALID_ARGUMENT, "camera size %dx%d outside [1, 32768]", c->width, c->height);
+  return GS_OK;
+}
+
+int check_scene(const gs_scene* s) {
+  if (!s) return fail(GS_ERR_INVALID_ARGUMENT, "scene is null");
+  if (s->n < 0 || s->n > 2147483647LL) return fail(GS_ERR_INVALID_ARGUMENT, "scene n = %lld out of range", (long long)s->n);
+  if (s->ld < s->n || s->ld < 0) return fail(GS_ERR_INVALID_ARGUMENT, "scene ld = %lld < n", (long long)s->ld);
+  if (s->sh_degree < 0 || s->sh_degree > 3)
+    return fail(GS_ERR_INVALID_ARGUMENT, "sh_degree = %d not in [0, 3]", s->sh_degree);
+  return GS_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_proj(const gs_proj& p, bool need_aux, int64_t n) {
+  if (n == 0) return GS_OK;
+  if (!p.splat) return fail(GS_ERR_INVALID_ARGUMENT, "proj.splat is null");
+  if (!aligned16(p.splat)) return fail(GS_ERR_INVALID_ARGUMENT, "proj.splat must be 16-byte aligned");
+  if (need_aux && (!p.tiles || !p.depth_key)) return fail(GS_ERR_INVALID_ARGUMENT, "proj.tiles / proj.depth_key is null");
+  return GS_OK;
+}
+
+int check_adam(const gs_adam* a) {
+  if (!a) return GS_OK;
+  if (!a->m || !a->v) return fail(GS_ERR_INVALID_ARGUMENT, "adam m / v is null");
+  if (a->step < 1) return fail(GS_ERR_INVALID_ARGUMENT, "adam step must be >= 1");
+  if (!(std::isfinite(a->lr) && std::isfinite(a->eps) && a->beta1 >= 0.0 && a->beta1 < 1.0 && a->beta2 >= 0.0 &&
+        a->beta2 < 1.0))
+    return fail(GS_ERR_INVALID_ARGUMENT, "adam hyper-parameters out of range");
+  return GS_OK;
+}
+
+gsmi::AdamCoef adam_coef(const gs_adam& a) {
+  gsmi::AdamCoef c;
+  c.lr = (float)a.lr;
+  c.b1 = (float)a.beta1;
+  c.omb1 = (float)(1.0 - a.beta1);
+  c.b2 = (float)a.beta2;
+  c.omb2 = (float)(1.0 - a.beta2);
+  c.eps = (float)a.eps;
+  c.inv_bc1 = (float)(1.0 / (1.0 - std::pow(a.beta1, (double)a.step)));
+  c.inv_bc2 = (float)(1.0 / (1.0 - std::pow(a.beta2, (double)a.step)));
+  return c;
+}
+
+int64_t n_tiles(const gs_camera& c) {
+  return (int64_t)((c.width + GS_TILE - 1) / GS_TILE) * ((c.height + GS_TILE - 1) / GS_TILE);
+}
+
+}  // namespace
+
+namespace gsmi {
+
+CamK make_cam(const gs_camera& c) {
+  CamK k{};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 3; ++j) k.R[3 * i + j] = c.viewmat[4 * i + j];
+    k.t[i] = c.viewmat[4 * i + 3];
+  }
+  k.fx = c.fx;
+  k.fy = c.fy;
+  k.cx = c.cx;
+  k.cy = c.cy;
+  k.near_plane = c.near_plane;
+  k.limx = (float)(1.3 * (0.5 * c.width) / c.fx);
+  k.limy = (float)(1.3 * (0.5 * c.height) / c.fy);
+  for (int j = 0; j < 3; ++j) {
+    double acc = 0.0;
+    for (int i = 0; i < 3; ++i) acc -= (double)k.R[3 * i + j] * (double)k.t[i];
+    k.pos[j] = (float)acc;
+  }
+  k.W = c.width;
+  k.H = c.height;
+  k.TX = (c.width + kTile - 1) / kTile;
+  k.TY = (c.height + kTile - 1) / kTile;
+  return k;
+}
+
+}  // namespace gsmi
+
+using namespace gsmi;
+
+extern "C" {
+
+int gs_version(void) { return GSMI_VERSION; }
+
+const char* gs_last_error(void) { return g_err; }
+
+int gs_preprocess(const gs_scene* scene, const float* params, const gs_camera* cam, gs_proj out,
+                  hipStream_t stream) {
+  int st;
+  if ((st = check_scene(scene)) || (st = check_camera(cam)) || (st = check_proj(out, true, scene->n))) return st;
+  if (!params && scene->n > 0) return fail(GS_ERR_INVALID_ARGUMENT, "params is null");
+  const hipError_t e = launch_preprocess(*scene, params, make_cam(*cam), out, stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "gs_preprocess");
+}
+
+int gs_bin_and_sort_workspace(int64_t n, int64_t k_capacity, int32_t width, int32_t height, size_t* bytes) {
+  if (!bytes) return fail(GS_ERR_INVALID_ARGUMENT, "bytes is null");
+  if (n < 0 || k_capacity < 0 || width < 1 || height < 1 || k_capacity > 4294967295LL)
+    return fail(GS_ERR_INVALID_ARGUMENT, "invalid sizes");
+  *bytes = bin_layout(n, k_capacity, width, height).total;
+  return ok();
+}
+
+int gs_bin_and_sort(const gs_scene* scene, const gs_camera* cam, gs_proj proj, void* workspace,
+                    size_t workspace_bytes, int64_t k_capacity, uint32_t* vals, uint32_t* ranges,
+                    uint64_t* keys, int64_t* k_out, hipStream_t stream) {
+  int st;
+  if ((st = check_scene(scene)) || (st = check_camera(cam)) || (st = check_proj(proj, true, scene->n))) return st;
+  if (!workspace || !vals || !ranges || !k_out)
+    return fail(GS_ERR_INVALID_ARGUMENT, "workspace / vals / ranges / k_out is null");
+  if (k_capacity < 0 || k_capacity > 4294967295LL) return fail(GS_ERR_INVALID_ARGUMENT, "k_capacity out of range");
+  const BinLayout L = bin_layout(scene->n, k_capacity, cam->width, cam->height);
+  if (workspace_bytes < L.total)
+    return fail(GS_ERR_INVALID_ARGUMENT, "workspace has %zu bytes, needs %zu", workspace_bytes, L.total);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(GS_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  const CamK ck = make_cam(*cam);
+  hipError_t e = launch_bin_reduce(scene->n, proj.tiles, proj.depth_key, ws, L, stream);
+  if (e != hipSuccess) return hip_fail(e, "gs_bin_and_sort (reduce)");
+  BinInfo info{};
+  e = hipMemcpyAsync(&info, ws + L.info, sizeof(BinInfo), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "gs_bin_and_sort (count readback)");
+  *k_out = (int64_t)info.K;
+  if ((int64_t)info.K > k_capacity)
+    return fail(GS_ERR_CAPACITY, "%llu intersections exceed k_capacity %lld", info.K, (long long)k_capacity);
+  e = launch_bin_sort_rest(scene->n, (int64_t)info.K, info, ck, proj, ws, L, vals, ranges, keys, stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "gs_bin_and_sort");
+}
+
+int gs_render_forward(const gs_camera* cam, int64_t n, const gs_splat* splat, const uint32_t* vals,
+                      const uint32_t* ranges, const float* bg, float* image, float* T_final,
+                      uint32_t* last_contrib, uint32_t* n_examined, uint64_t* blend_count,
+                      hipStream_t stream) {
+  int st;
+  if ((st = check_camera(cam))) return st;
+  if (n < 0) return fail(GS_ERR_INVALID_ARGUMENT, "n < 0");
+  if ((!splat && n > 0) || !vals || !ranges || !bg || !image || !T_final || !last_contrib)
+    return fail(GS_ERR_INVALID_ARGUMENT, "a required pointer is null");
+  if (!aligned16(splat)) return fail(GS_ERR_INVALID_ARGUMENT, "splat must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(ranges) & 7u) return fail(GS_ERR_INVALID_ARGUMENT, "ranges must be 8-byte aligned");
+  if (!(finite(bg[0]) && finite(bg[1]) && finite(bg[2]))) return fail(GS_ERR_INVALID_ARGUMENT, "bg not finite");
+  const hipError_t e = launch_blend_forward(make_cam(*cam), n, splat, vals, ranges, bg[0], bg[1], bg[2], image,
+                                            T_final, last_contrib, n_examined, blend_count, stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "gs_render_forward");
+}
+
+int gs_loss_l1_workspace(int64_t count, size_t* bytes) {
+  if (!bytes || count < 0) return fail(GS_ERR_INVALID_ARGUMENT, "invalid arguments");
+  *bytes = loss_workspace_bytes(count);
+  return ok();
+}
+
+int gs_loss_l1(int64_t count, const float* image, const float* target, float* loss, float* dL_dimage,
+               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (count < 0) return fail(GS_ERR_INVALID_ARGUMENT, "count < 0");
+  if (!loss || !workspace || (count > 0 && (!image || !target || !dL_dimage)))
+    return fail(GS_ERR_INVALID_ARGUMENT, "a required pointer is null");
+  if (workspace_bytes < loss_workspace_bytes(count))
+    return fail(GS_ERR_INVALID_ARGUMENT, "loss workspace too small");
+  const hipError_t e = launch_loss_l1(count, image, target, loss, dL_dimage, workspace, stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "gs_loss_l1");
+}
+
+int gs_preprocess_backward(const gs_scene* scene, float* params, const gs_camera* cam,
+                           const float* grad2d, float* grads, const gs_adam* adam, hipStream_t stream) {
+  int st;
+  if ((st = check_scene(scene)) || (st = check_camera(cam)) || (st = check_adam(adam))) return st;
+  if (scene->n > 0 && (!params || !grad2d)) return fail(GS_ERR_INVALID_ARGUMENT, "params / grad2d is null");
+  if (scene->n > 0 && !grads && !adam)
+    return fail(GS_ERR_INVALID_ARGUMENT, "grads is null and no adam update requested");
+  PrebwdArgs a{};
+  a.n = scene->n;
+  a.ld = scene->ld;
+  a.deg = scene->sh_degree;
+  a.params = params;
+  a.grad2d = grad2d;
+  a.grads = grads;
+  if (adam) {
+    a.m = adam->m;
+    a.v = adam->v;
+    const AdamCoef c = adam_coef(*adam);
+    a.lr = c.lr;
+    a.b1 = c.b1;
+    a.omb1 = c.omb1;
+    a.b2 = c.b2;
+    a.omb2 = c.omb2;
+    a.eps = c.eps;
+    a.inv_bc1 = c.inv_bc1;
+    a.inv_bc2 = c.inv_bc2;
+  }
+  const hipError_t e = launch_preprocess_backward(a, make_cam(*cam), stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "gs_preprocess_backward");
+}
+
+int gs_render_backward(const gs_scene* scene, float* params, const gs_camera* cam, gs_proj proj,
+                       const uint32_t* vals, const uint32_t* ranges, const float* bg,
+                       const float* T_final, const uint32_t* last_contrib, const float* dL_dimage,
+                       float* grad2d, float* grads, const gs_adam* adam, hipStream_t stream) {
+  int st;
+  if ((st = check_scene(scene)) || (st = check_camera(cam)) || (st = check_proj(proj, false, scene->n)) ||
+      (st = check_adam(adam)))
+    return st;
+  if (!vals || !ranges || !bg || !T_final || !last_contrib || !dL_dimage)
+    return fail(GS_ERR_INVALID_ARGUMENT, "a required pointer is null");
+  if (scene->n > 0 && !grad2d) return fail(GS_ERR_INVALID_ARGUMENT, "grad2d is null");
+  if (scene->n > 0 && (grads || adam) && !params) return fail(GS_ERR_INVALID_ARGUMENT, "params is null");
+  if (reinterpret_cast<uintptr_t>(ranges) & 7u) return fail(GS_ERR_INVALID_ARGUMENT, "ranges must be 8-byte aligned");
+  if (!(finite(bg[0]) && finite(bg[1]) && finite(bg[2]))) return fail(GS_ERR_INVALID_ARGUMENT, "bg not finite");
+  const CamK ck = make_cam(*cam);
+  hipError_t e = launch_fill_f32(grad2d, 9 * scene->ld, 0.f, stream);
+  if (e == hipSuccess)
+    e = launch_blend_backward(ck, scene->n, scene->ld, proj.splat, vals, ranges, bg[0], bg[1], bg[2], T_final,
+                              last_contrib, dL_dimage, grad2d, stream);
+  if (e != hipSuccess) return hip_fail(e, "gs_render_backward (blend)");
+  if (!grads && !adam) return ok();  // backward blend only
+  return gs_preprocess_backward(scene, params, cam, grad2d, grads, adam, stream);
+}
+
+int gs_adam_step(int64_t count, float* params, const float* grads, const gs_adam* adam, hipStream_t stream) {
+  int st;
+  if (!adam) return fail(GS_ERR_INVALID_ARGUMENT, "adam is null");
+  if ((st = check_adam(adam))) return st;
+  if (count < 0) return fail(GS_ERR_INVALID_ARGUMENT, "count < 0");
+  if (count > 0 && (!params || !grads)) return fail(GS_ERR_INVALID_ARGUMENT, "params / grads is null");
+  const hipError_t e = launch_adam(count, params, grads, adam->m, adam->v, adam_coef(*adam), stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "gs_adam_step");
+}
+
+}  // extern "C"

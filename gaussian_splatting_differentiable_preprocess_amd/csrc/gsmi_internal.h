@@ -1,0 +1,108 @@
+// Internal declarations shared by the HIP translation units of libgsmi.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gsmi.h"
+
+namespace gsmi {
+
+constexpr int kTile = GS_TILE;
+constexpr int kBlock = 256;  // threads per workgroup (4 wave64)
+
+// Camera as the kernels use it (float32, passed by value as a kernel argument).
+struct CamK {
+  float R[9];        // world->camera rotation, row-major
+  float t[3];
+  float fx, fy, cx, cy;
+  float near_plane;
+  float limx, limy;  // guard band for x/z, y/z inside the EWA Jacobian: 1.3 x half-extent / f
+  float pos[3];      // camera centre in world space, -R^T t
+  int W, H, TX, TY;
+};
+
+CamK make_cam(const gs_camera& c);
+
+inline int rows_for_degree(int d) { return 11 + 3 * (d + 1) * (d + 1); }
+
+// Tile rect [x0,x1) x [y0,y1) of the box (u +- rx, v +- ry): x0 = clamp(floor((u-rx)/16), 0,
+// TX), x1 = clamp(floor((u+rx)/16) + 1, 0, TX), the same in y.  u +- rx is a single float32
+// add and the scale by 1/16 is exact, so every caller that passes the same stored (u, v, rx,
+// ry) gets the same rect.  Contraction is off so no caller can fuse these adds.
+__device__ __forceinline__ int clamp_tile(float f, int hi) {
+  return !(f > 0.0f) ? 0 : (f > (float)hi ? hi : (int)f);
+}
+__device__ __forceinline__ void tile_rect(float u, float v, int rx, int ry, int TX, int TY,
+                                          int& x0, int& y0, int& x1, int& y1) {
+#pragma clang fp contract(off)
+  const float frx = (float)rx, fry = (float)ry;
+  const float ulo = u - frx, uhi = u + frx, vlo = v - fry, vhi = v + fry;
+  x0 = clamp_tile(floorf(ulo * 0.0625f), TX);
+  x1 = clamp_tile(floorf(uhi * 0.0625f) + 1.0f, TX);
+  y0 = clamp_tile(floorf(vlo * 0.0625f), TY);
+  y1 = clamp_tile(floorf(vhi * 0.0625f) + 1.0f, TY);
+}
+
+// ---- launchers (each returns the launch status) --------------------------------------
+hipError_t launch_preprocess(const gs_scene& sc, const float* params, const CamK& cam,
+                             gs_proj out, hipStream_t s);
+
+struct PrebwdArgs {
+  int64_t n, ld;
+  int deg;
+  float* params;
+  const float* grad2d;
+  float* grads;      // nullable when adam
+  float* m;          // nullable: no Adam
+  float* v;
+  float lr, b1, omb1, b2, omb2, eps, inv_bc1, inv_bc2;
+};
+
+// Adam coefficients rounded to float32 from double: b1, 1 - b1, b2, 1 - b2, lr, eps,
+// 1/(1 - b1^t), 1/(1 - b2^t).
+struct AdamCoef {
+  float lr, b1, omb1, b2, omb2, eps, inv_bc1, inv_bc2;
+};
+hipError_t launch_preprocess_backward(const PrebwdArgs& a, const CamK& cam, hipStream_t s);
+
+// binning / sorting
+struct BinLayout {
+  size_t partials, info, dkA, dvA, dkB, dvB, counts, totals, rect, bsum, tkA, tvA, tkB, tvB;
+  size_t total;
+  int64_t nblk_n, nblk_k, nblk_rect;
+};
+BinLayout bin_layout(int64_t n, int64_t kcap, int32_t W, int32_t H);
+struct BinInfo {
+  unsigned long long K;
+  uint32_t dmin, dmax;
+};
+hipError_t launch_bin_reduce(int64_t n, const uint32_t* tiles, const uint32_t* dkey, char* ws,
+                             const BinLayout& L, hipStream_t s);
+hipError_t launch_bin_sort_rest(int64_t n, int64_t K, const BinInfo& info, const CamK& cam,
+                                gs_proj proj, char* ws, const BinLayout& L, uint32_t* vals,
+                                uint32_t* ranges, uint64_t* keys, hipStream_t s);
+
+// blending
+hipError_t launch_blend_forward(const CamK& cam, int64_t n, const gs_splat* splat, const uint32_t* vals,
+                                const uint32_t* ranges, float bg0, float bg1, float bg2,
+                                float* image, float* T_final, uint32_t* last_contrib,
+                                uint32_t* n_examined, uint64_t* blend_count, hipStream_t s);
+hipError_t launch_blend_backward(const CamK& cam, int64_t n, int64_t ld, const gs_splat* splat,
+                                 const uint32_t* vals, const uint32_t* ranges, float bg0,
+                                 float bg1, float bg2, const float* T_final,
+                                 const uint32_t* last_contrib, const float* dLdI, float* grad2d,
+                                 hipStream_t s);
+
+// elementwise
+hipError_t launch_fill_u32(uint32_t* p, int64_t count, uint32_t value, hipStream_t s);
+hipError_t launch_fill_f32(float* p, int64_t count, float value, hipStream_t s);
+size_t loss_workspace_bytes(int64_t count);
+hipError_t launch_loss_l1(int64_t count, const float* image, const float* target, float* loss,
+                          float* dLdI, void* ws, hipStream_t s);
+hipError_t launch_adam(int64_t count, float* params, const float* grads, float* m, float* v,
+                       const AdamCoef& c, hipStream_t s);
+
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace gsmi

@@ -1,0 +1,296 @@
+"""Thin ctypes binding of libgsmi.so (the C ABI in include/gsmi.h).
+
+Argument marshalling only: every step of the path runs in the library's HIP kernels.  torch
+supplies device memory (tensors' data pointers) and the current HIP stream.  The library must be
+built (``python -m gaussian_splatting_differentiable_preprocess_amd.build``); there is no
+fallback path -- a missing library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgsmi.so")
+
+GS_OK, GS_ERR_INVALID_ARGUMENT, GS_ERR_CAPACITY, GS_ERR_HIP, GS_ERR_UNSUPPORTED = 0, -1, -2, -3, -4
+TILE = 16
+SPLAT_FLOATS = 12  # 48-byte record: u, v, radius_x, radius_y | A, B, C, opacity | r, g, b, depth
+
+EXPORTS = (
+    "gs_version", "gs_last_error", "gs_preprocess", "gs_bin_and_sort_workspace", "gs_bin_and_sort",
+    "gs_render_forward", "gs_loss_l1_workspace", "gs_loss_l1", "gs_render_backward",
+    "gs_preprocess_backward", "gs_adam_step",
+)
+
+
+class GsError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"gsmi error {code}: {msg}")
+        self.code = code
+
+
+class GsCapacityError(GsError):
+    def __init__(self, code, msg, required):
+        super().__init__(code, msg)
+        self.required = required
+
+
+class GsCamera(ctypes.Structure):
+    _fields_ = [("viewmat", ctypes.c_float * 12), ("fx", ctypes.c_float), ("fy", ctypes.c_float),
+                ("cx", ctypes.c_float), ("cy", ctypes.c_float), ("width", ctypes.c_int32),
+                ("height", ctypes.c_int32), ("near_plane", ctypes.c_float)]
+
+
+class GsScene(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int64), ("ld", ctypes.c_int64), ("sh_degree", ctypes.c_int32)]
+
+
+class GsProj(ctypes.Structure):
+    _fields_ = [("splat", ctypes.c_void_p), ("tiles", ctypes.c_void_p), ("depth_key", ctypes.c_void_p)]
+
+
+class GsAdam(ctypes.Structure):
+    _fields_ = [("m", ctypes.c_void_p), ("v", ctypes.c_void_p), ("step", ctypes.c_int32),
+                ("lr", ctypes.c_double), ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
+                ("eps", ctypes.c_double)]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Loads libgsmi.so and declares every export; raises if the library is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m "
+                           "gaussian_splatting_differentiable_preprocess_amd.build`")
+    L = ctypes.CDLL(path)
+    P, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    SP, CP, AP = ctypes.POINTER(GsScene), ctypes.POINTER(GsCamera), ctypes.POINTER(GsAdam)
+    L.gs_version.restype = ctypes.c_int
+    L.gs_last_error.restype = ctypes.c_char_p
+    L.gs_preprocess.argtypes = [SP, P, CP, GsProj, P]
+    L.gs_bin_and_sort_workspace.argtypes = [i64, i64, i32, i32, ctypes.POINTER(sz)]
+    L.gs_bin_and_sort.argtypes = [SP, CP, GsProj, P, sz, i64, P, P, P, ctypes.POINTER(i64), P]
+    L.gs_render_forward.argtypes = [CP, i64, P, P, P, ctypes.POINTER(ctypes.c_float), P, P, P, P, P, P]
+    L.gs_loss_l1_workspace.argtypes = [i64, ctypes.POINTER(sz)]
+    L.gs_loss_l1.argtypes = [i64, P, P, P, P, P, sz, P]
+    L.gs_render_backward.argtypes = [SP, P, CP, GsProj, P, P, ctypes.POINTER(ctypes.c_float), P, P, P,
+                                     P, P, AP, P]
+    L.gs_preprocess_backward.argtypes = [SP, P, CP, P, P, AP, P]
+    L.gs_adam_step.argtypes = [i64, P, P, AP, P]
+    for name in EXPORTS:
+        if name not in ("gs_version", "gs_last_error"):
+            getattr(L, name).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def last_error() -> str:
+    return load().gs_last_error().decode()
+
+
+def _check(rc, required=None):
+    if rc != GS_OK:
+        msg = last_error()
+        if rc == GS_ERR_CAPACITY:
+            raise GsCapacityError(rc, msg, required)
+        raise GsError(rc, msg)
+
+
+# ------------------------------------------------------------------------------------------
+# marshalling helpers
+# ------------------------------------------------------------------------------------------
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def make_camera(cam) -> GsCamera:
+    """From inputs.Camera (or anything with viewmat, fx, fy, cx, cy, width, height, near)."""
+    c = GsCamera()
+    vm = np.asarray(cam.viewmat, dtype=np.float32).reshape(12)
+    for k in range(12):
+        c.viewmat[k] = float(vm[k])
+    c.fx, c.fy, c.cx, c.cy = float(cam.fx), float(cam.fy), float(cam.cx), float(cam.cy)
+    c.width, c.height = int(cam.width), int(cam.height)
+    c.near_plane = float(getattr(cam, "near", 0.01))
+    return c
+
+
+def make_scene(n, ld, sh_degree) -> GsScene:
+    return GsScene(int(n), int(ld), int(sh_degree))
+
+
+def n_tiles(width, height):
+    return ((width + TILE - 1) // TILE) * ((height + TILE - 1) // TILE)
+
+
+@dataclasses.dataclass
+class Proj:
+    splat: "object"      # float32 [ld, 12] (48-byte records)
+    tiles: "object"      # int32 [ld] (uint32 values)
+    depth_key: "object"  # int32 [ld] (uint32 values)
+
+    def c(self) -> GsProj:
+        return GsProj(self.splat.data_ptr(), self.tiles.data_ptr(), self.depth_key.data_ptr())
+
+
+def alloc_proj(ld, device="cuda") -> Proj:
+    import torch
+    return Proj(torch.empty((ld, SPLAT_FLOATS), dtype=torch.float32, device=device),
+                torch.empty(ld, dtype=torch.int32, device=device),
+                torch.empty(ld, dtype=torch.int32, device=device))
+
+
+# ------------------------------------------------------------------------------------------
+# the C-ABI calls
+# ------------------------------------------------------------------------------------------
+
+def version() -> int:
+    return load().gs_version()
+
+
+def preprocess(scene: GsScene, params, cam: GsCamera, proj: Proj, stream=None):
+    _check(load().gs_preprocess(ctypes.byref(scene), _ptr(params), ctypes.byref(cam), proj.c(), _stream(stream)))
+
+
+def bin_and_sort_workspace(n, k_capacity, width, height) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load().gs_bin_and_sort_workspace(int(n), int(k_capacity), int(width), int(height), ctypes.byref(out)))
+    return out.value
+
+
+def bin_and_sort(scene: GsScene, cam: GsCamera, proj: Proj, workspace, k_capacity, vals, ranges,
+                 keys=None, stream=None) -> int:
+    """Returns K.  Raises GsCapacityError (with .required) if K > k_capacity."""
+    k = ctypes.c_int64(0)
+    rc = load().gs_bin_and_sort(ctypes.byref(scene), ctypes.byref(cam), proj.c(), _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), int(k_capacity),
+                                _ptr(vals), _ptr(ranges), _ptr(keys), ctypes.byref(k), _stream(stream))
+    _check(rc, required=k.value)
+    return k.value
+
+
+def _bg(bg):
+    arr = (ctypes.c_float * 3)(*[float(x) for x in bg])
+    return arr
+
+
+def render_forward(cam: GsCamera, n, splat, vals, ranges, bg, image, T_final, last_contrib,
+                   n_examined=None, blend_count=None, stream=None):
+    _check(load().gs_render_forward(ctypes.byref(cam), int(n), _ptr(splat), _ptr(vals), _ptr(ranges), _bg(bg),
+                                    _ptr(image), _ptr(T_final), _ptr(last_contrib), _ptr(n_examined),
+                                    _ptr(blend_count), _stream(stream)))
+
+
+def loss_l1_workspace(count) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load().gs_loss_l1_workspace(int(count), ctypes.byref(out)))
+    return out.value
+
+
+def loss_l1(count, image, target, loss, dL_dimage, workspace, stream=None):
+    _check(load().gs_loss_l1(int(count), _ptr(image), _ptr(target), _ptr(loss), _ptr(dL_dimage),
+                             _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def make_adam(m, v, step, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8) -> GsAdam:
+    return GsAdam(m.data_ptr(), v.data_ptr(), int(step), float(lr), float(beta1), float(beta2), float(eps))
+
+
+def render_backward(scene: GsScene, params, cam: GsCamera, proj: Proj, vals, ranges, bg, T_final,
+                    last_contrib, dL_dimage, grad2d, grads=None, adam: GsAdam | None = None, stream=None):
+    _check(load().gs_render_backward(ctypes.byref(scene), _ptr(params), ctypes.byref(cam), proj.c(), _ptr(vals),
+                                     _ptr(ranges), _bg(bg), _ptr(T_final), _ptr(last_contrib), _ptr(dL_dimage),
+                                     _ptr(grad2d), _ptr(grads), ctypes.byref(adam) if adam is not None else None,
+                                     _stream(stream)))
+
+
+def preprocess_backward(scene: GsScene, params, cam: GsCamera, grad2d, grads=None, adam: GsAdam | None = None,
+                        stream=None):
+    _check(load().gs_preprocess_backward(ctypes.byref(scene), _ptr(params), ctypes.byref(cam), _ptr(grad2d),
+                                         _ptr(grads), ctypes.byref(adam) if adam is not None else None,
+                                         _stream(stream)))
+
+
+def adam_step(count, params, grads, adam: GsAdam, stream=None):
+    _check(load().gs_adam_step(int(count), _ptr(params), _ptr(grads), ctypes.byref(adam), _stream(stream)))
+
+
+# ------------------------------------------------------------------------------------------
+# buffers for one training step and the step itself (a sequence of the calls above)
+# ------------------------------------------------------------------------------------------
+
+class StepBuffers:
+    """Device buffers for training steps of one scene at one image size (allocated once with
+    torch; the library allocates nothing)."""
+
+    def __init__(self, n, ld, sh_degree, width, height, k_capacity, device="cuda"):
+        import torch
+        self.n, self.ld, self.deg, self.W, self.H = n, ld, sh_degree, width, height
+        self.R = 11 + 3 * (sh_degree + 1) ** 2
+        self.T = n_tiles(width, height)
+        f32, i32 = torch.float32, torch.int32
+        self.proj = alloc_proj(ld, device)
+        self.k_capacity = int(k_capacity)
+        self.vals = torch.empty(max(1, self.k_capacity), dtype=i32, device=device)
+        self.ranges = torch.empty((self.T, 2), dtype=i32, device=device)
+        self.ws = torch.empty(bin_and_sort_workspace(n, self.k_capacity, width, height), dtype=torch.uint8,
+                              device=device)
+        self.image = torch.empty((height, width, 3), dtype=f32, device=device)
+        self.T_final = torch.empty((height, width), dtype=f32, device=device)
+        self.last = torch.empty((height, width), dtype=i32, device=device)
+        self.dLdI = torch.empty((height, width, 3), dtype=f32, device=device)
+        self.loss = torch.zeros(1, dtype=f32, device=device)
+        self.loss_ws = torch.empty(loss_l1_workspace(3 * width * height), dtype=torch.uint8, device=device)
+        self.grad2d = torch.empty((9, ld), dtype=f32, device=device)
+        self.scene = make_scene(n, ld, sh_degree)
+
+    def grow(self, k_capacity, device="cuda"):
+        import torch
+        self.k_capacity = int(k_capacity)
+        self.vals = torch.empty(max(1, self.k_capacity), dtype=torch.int32, device=device)
+        self.ws = torch.empty(bin_and_sort_workspace(self.n, self.k_capacity, self.W, self.H), dtype=torch.uint8,
+                              device=device)
+
+
+def train_step(buf: StepBuffers, params, m, v, step, cam: GsCamera, target=None, upstream=None,
+               bg=(0.0, 0.0, 0.0), lr=1e-3, fused_adam=True, grads=None, blend_count=None):
+    """One fwd + bwd + Adam step for one view: preprocess -> bin/sort -> forward -> L1 (or
+    the given upstream dL/dI) -> backward (+ Adam).  Returns K."""
+    preprocess(buf.scene, params, cam, buf.proj)
+    while True:
+        try:
+            K = bin_and_sort(buf.scene, cam, buf.proj, buf.ws, buf.k_capacity, buf.vals, buf.ranges)
+            break
+        except GsCapacityError as e:
+            buf.grow(int(e.required * 1.25) + 1024)
+    render_forward(cam, buf.n, buf.proj.splat, buf.vals, buf.ranges, bg, buf.image, buf.T_final, buf.last,
+                   blend_count=blend_count)
+    if upstream is not None:
+        dLdI = upstream
+    else:
+        loss_l1(3 * buf.W * buf.H, buf.image, target, buf.loss, buf.dLdI, buf.loss_ws)
+        dLdI = buf.dLdI
+    adam = make_adam(m, v, step, lr)
+    if fused_adam:
+        render_backward(buf.scene, params, cam, buf.proj, buf.vals, buf.ranges, bg, buf.T_final, buf.last, dLdI,
+                        buf.grad2d, grads, adam)
+    else:
+        render_backward(buf.scene, params, cam, buf.proj, buf.vals, buf.ranges, bg, buf.T_final, buf.last, dLdI,
+                        buf.grad2d, grads)
+        adam_step(buf.R * buf.ld, params, grads, adam)
+    return K

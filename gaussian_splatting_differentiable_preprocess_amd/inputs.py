@@ -116,18 +116,24 @@ def _gyroid(x):
 
 def sample_gyroid(rng, n, iters=16, tol=1e-7):
     """Uniform seeds in [-pi, pi]^3 Newton-projected onto sin x cos y + sin y cos z +
-    sin z cos x = 0 (x <- x - f grad f / |grad f|^2, at most `iters` steps); a seed is kept
-    when |f| < tol and it stays inside the box."""
+    sin z cos x = 0 (x <- x - f grad f / |grad f|^2, at most `iters` steps; a point stops once
+    |f| < 1e-13); a seed is kept when |f| < tol and it stays inside the box."""
     pts = []
     got = 0
     while got < n:
         m = int(1.6 * (n - got)) + 4096
         x = rng.uniform(-math.pi, math.pi, (m, 3))
+        active = np.arange(m)
         for _ in range(iters):
-            f, g = _gyroid(x)
+            xa = x[active]
+            f, g = _gyroid(xa)
+            keep = np.abs(f) >= 1e-13
+            active, xa, f, g = active[keep], xa[keep], f[keep], g[keep]
+            if active.size == 0:
+                break
             g2 = np.einsum("ij,ij->i", g, g)
             step = np.where(g2 > 1e-30, f / np.maximum(g2, 1e-30), 0.0)
-            x = x - step[:, None] * g
+            x[active] = xa - step[:, None] * g
         f, g = _gyroid(x)
         ok = (np.abs(f) < tol) & np.all(np.abs(x) <= math.pi, axis=1) & np.all(np.isfinite(x), axis=1)
         pts.append(x[ok])

@@ -1,0 +1,216 @@
+/*
+ * gsmi.h -- C ABI of the MI355X (gfx950) 3D Gaussian Splatting training-step library
+ * (libgsmi.so).
+ *
+ * One training step over one GPU's share of the Gaussians is, in order:
+ *   gs_preprocess       EWA projection of every Gaussian to a 2D conic + SH colour
+ *   gs_bin_and_sort     tile binning, stable (tile, depth) radix sort, per-tile ranges
+ *   gs_render_forward   front-to-back alpha compositing per 16x16 tile
+ *   gs_loss_l1          L1 image loss and its gradient
+ *   gs_render_backward  reverse-order backward blend + preprocess backward
+ *                       (optionally fused with the Adam update)
+ *   gs_adam_step        Adam over all parameters (when not fused)
+ *
+ * The pages this follows name these stages but print no formulas:
+ *   "Scaling 3D Gaussian Splatting with Distributed Compute: Why One GPU Is Never Enough"
+ *     - Gaussian parameters: mean, covariance from scale and rotation, SH colour, opacity
+ *       (its list of what a Gaussian is parameterised by);
+ *     - projection to 2D means, depths, conics, radii and a visibility mask, with SH turned
+ *       into RGB per camera first (walkthrough steps "Project locally" and "Evaluate
+ *       spherical harmonics before communicating");
+ *     - the ~12-scalar, ~48-byte projected record (step "Ship each camera's Gaussians");
+ *     - per-tile sorted intersection lists and per-tile offsets into them (the memory
+ *       accounting passage and the trace section on intersect_offset_kernel);
+ *     - rasterization and an L1 (+ D-SSIM) loss with gradients flowing to mean, covariance,
+ *       colour and opacity, then a local Adam step (steps "Rasterize locally", "Compute
+ *       the loss locally", "Step the optimizer locally").
+ *   "Toward Distributed 3D Gaussian Splatting for High-Resolution Isosurface
+ *     Visualization", sections I and III: 3D-GS trained from synthetic orbit views.
+ * Each formula is the standard 3D-GS / EWA-splatting reading of the stage.
+ *
+ * Conventions common to every call
+ *   - All pointers to arrays are DEVICE pointers (hipMalloc'd or equivalent, coarse-grained)
+ *     unless marked "host".  The caller owns every buffer; the library never allocates or
+ *     frees device memory.  Host structs are read during the call only.
+ *   - Every call enqueues work on `stream` and returns without waiting, except
+ *     gs_bin_and_sort, which copies the intersection count to the host and synchronises
+ *     `stream` once (see there).
+ *   - Outputs must not alias inputs, except where a call says it updates in place.
+ *   - Every call returns a gs_status.  Arguments are checked before any HIP call; on an
+ *     error nothing is enqueued and gs_last_error() describes it.  No exception or abort
+ *     crosses the ABI.  Non-finite Gaussians are culled, not reported.
+ *   - Floating point is IEEE float32 throughout.
+ */
+#ifndef GSMI_H
+#define GSMI_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GSMI_VERSION 1
+#define GS_TILE 16 /* tiles are GS_TILE x GS_TILE pixels */
+
+typedef enum gs_status {
+  GS_OK = 0,
+  GS_ERR_INVALID_ARGUMENT = -1, /* null pointer, bad size, non-finite camera, ...      */
+  GS_ERR_CAPACITY = -2,         /* intersection buffers too small; *k_out = required K */
+  GS_ERR_HIP = -3,              /* a HIP runtime call failed (message in gs_last_error) */
+  GS_ERR_UNSUPPORTED = -4       /* a valid but unsupported variant                    */
+} gs_status;
+
+/* Pinhole camera.  viewmat is the row-major 3x4 world->camera transform [R | t] with
+ * camera axes x right, y down, z forward; a world point p maps to R p + t.  Pixel (px, py)
+ * has its centre at (px + 0.5, py + 0.5); u = fx x/z + cx, v = fy y/z + cy.  Gaussians
+ * with z <= near_plane are culled.  Requires width, height in [1, 32768] and finite,
+ * positive fx, fy, near_plane. */
+typedef struct gs_camera {
+  float viewmat[12];
+  float fx, fy, cx, cy;
+  int32_t width, height;
+  float near_plane;
+} gs_camera;
+
+/* Gaussian set.  Parameters are planar float32 rows of stride ld (>= n) elements:
+ *   rows 0-2 mean, 3-5 log-scale (scale = exp), 6-9 rotation quaternion (w, x, y, z; need
+ *   not be unit), 10 opacity logit (opacity = sigmoid), 11 + 3k + c SH coefficient k of
+ *   colour channel c for k < (sh_degree+1)^2.
+ * R = 11 + 3 (sh_degree+1)^2 rows (14 at degree 0, 59 at degree 3).  n in [0, 2^31 - 1],
+ * sh_degree in [0, 3]. */
+typedef struct gs_scene {
+  int64_t n;
+  int64_t ld;
+  int32_t sh_degree;
+} gs_scene;
+
+/* The projected record of one Gaussian for one camera (48 bytes, 16-byte aligned): the
+ * pages' dozen scalars -- two radii, two mean coordinates, depth, three conic entries,
+ * opacity and three colour channels -- laid out so that the blend's alpha test reads the
+ * first 32 bytes.  A culled Gaussian has every field 0. */
+typedef struct gs_splat {
+  float u, v;                 /* 2D mean, pixels                                           */
+  int32_t radius_x, radius_y; /* per-axis 3-sigma extents ceil(3 sqrt(S2_ii)), pixels      */
+  float conic_a, conic_b;     /* inverse of the 2D covariance S2: [[a, b], [b, c]]         */
+  float conic_c, opacity;     /* opacity = sigmoid(logit)                                  */
+  float r, g, b;              /* max(0.5 + sum_k Y_k(view dir) f_k, 0) per channel        */
+  float depth;                /* view-space z                                              */
+} gs_splat;
+
+/* Output of gs_preprocess, input of the later calls.  Each array has >= ld entries.
+ *   tiles[i]     number of tiles the Gaussian's 3-sigma box touches (0 = culled)
+ *   depth_key[i] the float32 bits of depth for a visible Gaussian, 0xFFFFFFFF if culled */
+typedef struct gs_proj {
+  gs_splat* splat;
+  uint32_t* tiles;
+  uint32_t* depth_key;
+} gs_proj;
+
+/* Adam state and hyper-parameters (Kingma & Ba, bias-corrected, dense over every float).
+ * m and v are planar like params (R rows of stride ld) or, for gs_adam_step, flat arrays of
+ * `count` floats.  step is the 1-based step number t.  The hyper-parameters are double so
+ * that 1 - beta and the bias corrections 1 - beta^t are formed exactly before rounding to the
+ * float32 the kernels use (1 - 0.999f alone is off by 1.3e-5). */
+typedef struct gs_adam {
+  float* m;
+  float* v;
+  int32_t step;
+  double lr, beta1, beta2, eps;
+} gs_adam;
+
+/* ---------------------------------------------------------------------------------- */
+
+/* Per-Gaussian preprocess (EWA projection + SH colour).  params: R rows of stride ld.
+ * Writes out.splat[0..n), out.tiles[0..n), out.depth_key[0..n).  One thread per Gaussian;
+ * HBM-bound. */
+int gs_preprocess(const gs_scene* scene, const float* params, const gs_camera* cam, gs_proj out,
+                  hipStream_t stream);
+
+/* Bytes of device workspace gs_bin_and_sort needs for n Gaussians, up to k_capacity
+ * intersections and a width x height image (host-only query, no HIP call). */
+int gs_bin_and_sort_workspace(int64_t n, int64_t k_capacity, int32_t width, int32_t height,
+                              size_t* bytes);
+
+/* Tile binning and sorting.  For every visible Gaussian i and every tile (tx, ty) of its
+ * 3-sigma box, one intersection with key (ty*TX + tx) << 32 | depth_key[i] and value i;
+ * the intersections are sorted ascending by key, ties in Gaussian index order (stable),
+ * which gives per-tile lists in front-to-back depth order.
+ *   vals[k_capacity]   out: sorted Gaussian indices
+ *   ranges[2*T]        out: ranges[2t], ranges[2t+1] = [start, end) of tile t in vals;
+ *                           (0, 0) for an empty tile.  T = ceil(W/16) * ceil(H/16).
+ *   keys[k_capacity]   out, nullable: the sorted 64-bit keys
+ *   workspace          device scratch of >= gs_bin_and_sort_workspace() bytes
+ *   k_out              HOST out: the number of intersections K
+ * Synchronisation: this call copies K to the host and waits for `stream` once.  If K >
+ * k_capacity it sets *k_out = K and returns GS_ERR_CAPACITY without writing vals, ranges or
+ * keys; the caller grows its buffers and calls again. */
+int gs_bin_and_sort(const gs_scene* scene, const gs_camera* cam, gs_proj proj, void* workspace,
+                    size_t workspace_bytes, int64_t k_capacity, uint32_t* vals, uint32_t* ranges,
+                    uint64_t* keys, int64_t* k_out, hipStream_t stream);
+
+/* Forward blend.  For each pixel, walks its tile's list front to back: power =
+ * -(a dx^2 + c dy^2)/2 - b dx dy with (dx, dy) = pixel centre - (u, v); skips power > 0;
+ * alpha = min(0.99, opacity e^power); skips alpha < 1/255; stops before blending an entry
+ * that would take the transmittance T below 1e-4; else C += rgb alpha T, T *= 1 - alpha.
+ *   image[H][W][3]      out: C + T bg
+ *   T_final[H][W]       out: final transmittance
+ *   last_contrib[H][W]  out: 1-based list position of the last blended entry (0 = none)
+ *   n_examined[H][W]    out, nullable: entries examined (list length, or the position of
+ *                       the entry that stopped the pixel)
+ *   blend_count         out, nullable: device uint64 to which the sum of n_examined over
+ *                       the image is ADDED (the caller zeroes it)
+ * bg is a HOST array of 3 floats.  One 256-thread workgroup per tile. */
+int gs_render_forward(const gs_camera* cam, int64_t n, const gs_splat* splat, const uint32_t* vals,
+                      const uint32_t* ranges, const float* bg, float* image, float* T_final,
+                      uint32_t* last_contrib, uint32_t* n_examined, uint64_t* blend_count,
+                      hipStream_t stream);
+
+/* Bytes of device workspace gs_loss_l1 needs for `count` elements (host-only query). */
+int gs_loss_l1_workspace(int64_t count, size_t* bytes);
+
+/* L1 loss over `count` = 3HW elements: *loss = mean |image - target| (device float),
+ * dL_dimage = sign(image - target) / count with sign(0) = 0.  The page's loss is L1 plus a
+ * lambda-weighted D-SSIM term; this call is the L1 term. */
+int gs_loss_l1(int64_t count, const float* image, const float* target, float* loss,
+               float* dL_dimage, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Backward of the step from dL/dimage.
+ *   grad2d[9][ld]  out: per-Gaussian dL/d(u, v, conic_a, conic_b, conic_c, opacity, r, g, b)
+ *                  from the reverse-order backward blend (zeroed inside, then accumulated
+ *                  with float atomics, so the summation order is not fixed)
+ *   grads[R][ld]   out, nullable: dL/dparams by the chain rule through the preprocess
+ *   adam           nullable: when given, the preprocess backward also applies the Adam
+ *                  update to params, adam->m and adam->v in place (params is then written)
+ * With grads and adam both null only the backward blend runs (grad2d is the only output and
+ * params may be null); gs_preprocess_backward then finishes the step.
+ * T_final and last_contrib are the forward's outputs for the same inputs; bg is a HOST array
+ * of 3 floats.  Culled Gaussians receive zero gradients. */
+int gs_render_backward(const gs_scene* scene, float* params, const gs_camera* cam, gs_proj proj,
+                       const uint32_t* vals, const uint32_t* ranges, const float* bg,
+                       const float* T_final, const uint32_t* last_contrib, const float* dL_dimage,
+                       float* grad2d, float* grads, const gs_adam* adam, hipStream_t stream);
+
+/* Preprocess backward alone: grads (and optionally the fused Adam update) from a given
+ * grad2d[9][ld].  Same semantics as the second half of gs_render_backward. */
+int gs_preprocess_backward(const gs_scene* scene, float* params, const gs_camera* cam,
+                           const float* grad2d, float* grads, const gs_adam* adam,
+                           hipStream_t stream);
+
+/* Adam over `count` floats, in place: m = b1 m + (1-b1) g; v = b2 v + (1-b2) g^2;
+ * params -= lr (m / (1-b1^t)) / (sqrt(v / (1-b2^t)) + eps).  adam->m and adam->v are flat
+ * arrays of `count` floats. */
+int gs_adam_step(int64_t count, float* params, const float* grads, const gs_adam* adam,
+                 hipStream_t stream);
+
+/* Message for the last error on the calling thread; valid until the next call on it. */
+const char* gs_last_error(void);
+
+int gs_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GSMI_H */

@@ -1,0 +1,78 @@
+"""The C-ABI library loads and exports every symbol include/gsmi.h declares; argument checks
+and workspace queries (host-only, no HIP call) behave as documented.  No compute call here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from gaussian_splatting_differentiable_preprocess_amd import gsmi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared():
+    src = open(os.path.join(ROOT, "include", "gsmi.h")).read()
+    return sorted(set(re.findall(r"^(?:int|const char\*)\s+(gs_\w+)\(", src, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = gsmi.load()
+    names = declared()
+    assert len(names) == len(gsmi.EXPORTS) and set(names) == set(gsmi.EXPORTS)
+    for name in names:
+        assert hasattr(L, name), name
+    assert gsmi.version() == 1
+
+
+def test_invalid_arguments_rejected_before_any_gpu_call():
+    L = gsmi.load()
+    cam = gsmi.GsCamera()
+    cam.fx = cam.fy = 100.0
+    cam.width = cam.height = 64
+    cam.near_plane = 0.01
+    cam.viewmat[0] = cam.viewmat[5] = cam.viewmat[10] = 1.0
+    bad = [
+        (gsmi.make_scene(10, 5, 0), cam, "ld"),
+        (gsmi.make_scene(-1, 5, 0), cam, "n ="),
+        (gsmi.make_scene(10, 10, 4), cam, "sh_degree"),
+    ]
+    for sc, c, msg in bad:
+        rc = L.gs_preprocess(ctypes.byref(sc), None, ctypes.byref(c), gsmi.GsProj(), None)
+        assert rc == gsmi.GS_ERR_INVALID_ARGUMENT and msg in gsmi.last_error()
+    sc = gsmi.make_scene(10, 10, 0)
+    assert L.gs_preprocess(ctypes.byref(sc), None, None, gsmi.GsProj(), None) == gsmi.GS_ERR_INVALID_ARGUMENT
+    c2 = gsmi.GsCamera.from_buffer_copy(cam)
+    c2.fx = float("nan")
+    assert L.gs_preprocess(ctypes.byref(sc), None, ctypes.byref(c2), gsmi.GsProj(), None) == -1
+    c3 = gsmi.GsCamera.from_buffer_copy(cam)
+    c3.width = 0
+    assert L.gs_preprocess(ctypes.byref(sc), None, ctypes.byref(c3), gsmi.GsProj(), None) == -1
+    # null params with n > 0
+    proj = gsmi.GsProj(16, 16, 16)
+    assert L.gs_preprocess(ctypes.byref(sc), None, ctypes.byref(cam), proj, None) == -1
+    # misaligned record buffer
+    assert L.gs_preprocess(ctypes.byref(sc), ctypes.c_void_p(64), ctypes.byref(cam), gsmi.GsProj(8, 16, 16), None) == -1
+    assert "aligned" in gsmi.last_error()
+    # Adam with a bad step / null moments
+    ad = gsmi.GsAdam(None, None, 1, 1e-3, 0.9, 0.999, 1e-8)
+    assert L.gs_adam_step(10, ctypes.c_void_p(64), ctypes.c_void_p(64), ctypes.byref(ad), None) == -1
+    ad = gsmi.GsAdam(64, 64, 0, 1e-3, 0.9, 0.999, 1e-8)
+    assert L.gs_adam_step(10, ctypes.c_void_p(64), ctypes.c_void_p(64), ctypes.byref(ad), None) == -1
+    assert L.gs_adam_step(10, ctypes.c_void_p(64), ctypes.c_void_p(64), None, None) == -1
+    # bin_and_sort: workspace too small, null k_out
+    k = ctypes.c_int64(0)
+    rc = L.gs_bin_and_sort(ctypes.byref(sc), ctypes.byref(cam), proj, ctypes.c_void_p(256), 16, 100,
+                           ctypes.c_void_p(64), ctypes.c_void_p(64), None, ctypes.byref(k), None)
+    assert rc == -1 and "workspace" in gsmi.last_error()
+
+
+def test_workspace_queries():
+    a = gsmi.bin_and_sort_workspace(4_000_000, 8_000_000, 2048, 2048)
+    b = gsmi.bin_and_sort_workspace(4_000_000, 16_000_000, 2048, 2048)
+    # 16 bytes per intersection of capacity (two ping-pong key/value pairs)
+    assert b - a >= 16 * 8_000_000 and b - a < 16 * 8_000_000 + 8 * 1024 * 1024
+    assert gsmi.bin_and_sort_workspace(0, 0, 1, 1) > 0
+    assert gsmi.loss_l1_workspace(3 * 2048 * 2048) >= 4 * (3 * 2048 * 2048) // 4096
+    with pytest.raises(gsmi.GsError):
+        gsmi.bin_and_sort_workspace(-1, 0, 16, 16)
