@@ -144,6 +144,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--unfused-adam", action="store_true", help="separate Adam kernel instead of the fused one")
     ap.add_argument("--detail", default=None, help="write a detailed JSON record to this path")
+    ap.add_argument("--views", type=int, default=0,
+                    help="use only the first N orbit views (short profiling runs); default all")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs the single-GPU hot path only: one MI355X holds the whole scene "
@@ -167,6 +169,8 @@ def main():
     log(f"[bench]   {time.time() - t0:.1f} s; target set ...")
     tparams_np = inputs.gaussian_params(cfg, inputs.STREAM_TARGET)
     cams = inputs.cameras_for(cfg)
+    if args.views:
+        cams = cams[: args.views]
     V = len(cams)
     R, N = params_np.shape
     log(f"[bench] rendering {V} target views at {W}x{H} ...")

@@ -9,14 +9,18 @@
 // and the exact derivative of that branch in reverse order (gradients to the 2D mean, conic,
 // opacity and colour, "Gradients flow back ... to mu, Sigma, c and alpha").
 //
-// Work decomposition.  One 256-thread workgroup per tile; wave w owns the 8x8 quadrant
-// (w & 1, w >> 1).  The list is consumed in batches of 256 records staged in LDS (one gather
-// per (tile, Gaussian)).  Each record gets a 4-bit mask of the quadrants its alpha >= 1/255
-// ellipse can reach (a conservative bound), and each wave walks only the records of its bit
-// with a scalar bit-scan loop, so a wave spends no VALU work on Gaussians that cannot touch
-// its pixels -- the per-pixel results are those of the plain walk.  Workgroups are mapped to
-// tiles so that each of the 8 XCDs (each with its own L2) renders a contiguous band of tiles.
-// Bound: VALU / transcendental (one exp per evaluated pair), not HBM.
+// Work decomposition.  Each 8x8 quadrant of a tile is one wave64 (one pixel per lane); the
+// four quadrant waves of a tile share a workgroup.  A tile's list is consumed in chunks of 64
+// records.  For every record the conservative pixel box of its alpha >= 1/255 ellipse is
+// formed, and sixteen ballots (one per quadrant column and row) give every lane a 64-bit mask
+// of the chunk's records whose box holds its pixel.  Each lane then walks only its own records,
+// in list order, so lanes evaluate different records at the same time: a record costs VALU
+// work only on the pixels it can reach, and the per-pixel results are those of the plain walk
+// (a skipped record has alpha < 1/255 at that pixel).  The forward's quadrant waves are
+// independent (no workgroup barrier); the backward's share per-chunk gradient sums in LDS.
+// Workgroup b renders tile b: the hardware deals consecutive workgroups to the 8 XCDs in turn,
+// which spreads the (very uneven) per-tile work evenly over them.  Bound: VALU /
+// transcendental and LDS, not HBM.
 #include "gsmi_internal.h"
 
 namespace gsmi {
@@ -37,85 +41,144 @@ __device__ __forceinline__ float eval_power(float nA, float nB, float nC, float 
 
 __device__ __forceinline__ float eval_oG(float o, float power) { return __fmul_rn(o, __expf(power)); }
 
-// Quadrants (bit q = qx + 2 qy, 8x8 each) of the tile at (x_t, y_t) whose pixel centres can
-// satisfy o e^power >= 1/255.  That region is the ellipse d^T Q d <= tau, tau = 2 ln(255 o),
-// whose bounding box has half-widths sqrt(tau C/det), sqrt(tau A/det); tau and the box are
-// widened so float32 rounding of the per-pixel test can never fall outside.
-__device__ __forceinline__ uint32_t quadrant_mask(float u, float v, float A, float B, float C, float o,
-                                                  int x_t, int y_t) {
-  if (!(o >= kAlphaMin)) return 0u;
-  const float tau = 2.0f * __logf(255.0f * o) * 1.001f + 1e-3f;
-  const float det = A * C - B * B;
-  if (!(det > 0.0f) || !__builtin_isfinite(det) || !__builtin_isfinite(u) || !__builtin_isfinite(v))
-    return 0xFu;
-  const float hx = sqrtf(tau * C / det) * 1.001f + 0.01f;
-  const float hy = sqrtf(tau * A / det) * 1.001f + 0.01f;
-  uint32_t m = 0;
+// One DPP step x += permute(x) (old value 0 = identity of the add, so the move folds into
+// v_add_f32_dpp).
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float x) {
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+// Sums each of N values over the 16 lanes of every row (all lanes of a row get the row
+// sum).  The steps are interleaved across the N values so consecutive DPP reads never
+// depend on the instruction just before them.
+template <int N>
+__device__ __forceinline__ void row_sum16(float* v) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const float xlo = (float)(x_t + (q & 1) * 8) + 0.5f, xhi = xlo + 7.0f;
-    const float ylo = (float)(y_t + (q >> 1) * 8) + 0.5f, yhi = ylo + 7.0f;
-    if (u + hx >= xlo && u - hx <= xhi && v + hy >= ylo && v - hy <= yhi) m |= 1u << q;
-  }
-  return m;
+  for (int q = 0; q < N; ++q) v[q] = dpp_add<0xB1>(v[q]);   // quad_perm [1,0,3,2]: xor 1
+#pragma unroll
+  for (int q = 0; q < N; ++q) v[q] = dpp_add<0x4E>(v[q]);   // quad_perm [2,3,0,1]: xor 2
+#pragma unroll
+  for (int q = 0; q < N; ++q) v[q] = dpp_add<0x141>(v[q]);  // row_half_mirror
+#pragma unroll
+  for (int q = 0; q < N; ++q) v[q] = dpp_add<0x140>(v[q]);  // row_mirror
 }
 
-// Workgroup -> tile: consecutive workgroups go round-robin to the 8 XCDs, so XCD x receives
-// workgroups x, x+8, ...; give it the contiguous tile band [prefix(x), prefix(x+1)).
-__device__ __forceinline__ int xcd_tile(int b, int T) {
-  const int x = b & 7, k = b >> 3;
-  int pre = 0;
-  for (int y = 0; y < x; ++y) pre += (T - y + 7) >> 3;
-  return pre + k;
-}
+constexpr int kChunk = 64;  // records staged per chunk (one per lane)
 
-// DPP sum over the 16 lanes of a row; every lane of the row gets the row sum.
-__device__ __forceinline__ float row_sum16(float x) {
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));  // xor 1
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));  // xor 2
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false)); // half-row mirror
-  x += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, false)); // row mirror
-  return x;
-}
-
-struct Staged {
-  float4 geo[kBatch];   // u, v, -A/2, -B
-  float4 col[kBatch];   // -C/2, o, r, g
-  float b[kBatch];
-  uint32_t mask[kBatch];
-  uint32_t gid[kBatch];
+// Conservative pixel-index box [x0,x1] x [y0,y1] (relative to the quadrant origin, clamped to
+// 0..7) of the pixels whose centres can satisfy o e^power >= 1/255.  That region is the ellipse
+// d^T Q d <= tau, tau = 2 ln(255 o), with half-widths sqrt(tau C/det), sqrt(tau A/det); tau and
+// the box are widened so float32 rounding of the per-pixel test can never fall outside.  Empty
+// (x0 > x1) when o < 1/255 or the box misses the quadrant.
+struct Box {
+  int x0, x1, y0, y1;
 };
 
-__device__ __forceinline__ void stage_entry(Staged& S, int e, const float4* __restrict__ splat,
-                                            uint32_t i, int64_t n, int x_t, int y_t) {
-  if ((int64_t)i >= n) {  // never for lists from gs_bin_and_sort; keeps reads in bounds
-    S.mask[e] = 0u;
-    S.gid[e] = 0u;
-    return;
+__device__ __forceinline__ Box alpha_box(float u, float v, float A, float B, float C, float o, int xq,
+                                         int yq) {
+  Box b{1, 0, 1, 0};
+  if (!(o >= kAlphaMin)) return b;
+  const float det = A * C - B * B;
+  float hx = 1e30f, hy = 1e30f;
+  if (det > 0.0f && __builtin_isfinite(det)) {
+    const float tau = 2.0f * __logf(255.0f * o) * 1.001f + 1e-3f;
+    hx = sqrtf(tau * C / det) * 1.001f + 0.01f;
+    hy = sqrtf(tau * A / det) * 1.001f + 0.01f;
   }
-  const float4 q0 = splat[3 * (int64_t)i];
-  const float4 q1 = splat[3 * (int64_t)i + 1];
-  const float4 q2 = splat[3 * (int64_t)i + 2];
-  S.geo[e] = make_float4(q0.x, q0.y, -0.5f * q1.x, -q1.y);
-  S.col[e] = make_float4(-0.5f * q1.z, q1.w, q2.x, q2.y);
-  S.b[e] = q2.z;
-  S.mask[e] = quadrant_mask(q0.x, q0.y, q1.x, q1.y, q1.z, q1.w, x_t, y_t);
-  S.gid[e] = i;
+  // pixel index p has its centre at p + 0.5: p in [u - hx - 0.5, u + hx - 0.5]
+  const float fx0 = ceilf(u - hx - 0.5f - (float)xq), fx1 = floorf(u + hx - 0.5f - (float)xq);
+  const float fy0 = ceilf(v - hy - 0.5f - (float)yq), fy1 = floorf(v + hy - 0.5f - (float)yq);
+  if (!(fx0 <= 7.0f && fx1 >= 0.0f && fy0 <= 7.0f && fy1 >= 0.0f)) return b;  // also NaN
+  b.x0 = fx0 < 0.0f ? 0 : (int)fx0;
+  b.x1 = fx1 > 7.0f ? 7 : (int)fx1;
+  b.y0 = fy0 < 0.0f ? 0 : (int)fy0;
+  b.y1 = fy1 > 7.0f ? 7 : (int)fy1;
+  return b;
 }
+
+// Per-lane masks: bit e set iff record e's box contains the lane's pixel (lx, ly).  Lane e
+// holds record e's box; COL[x] / ROW[y] are ballots over the records.
+__device__ __forceinline__ unsigned long long lane_mask(const Box& b, int lx, int ly) {
+  unsigned long long col = 0ull, row = 0ull;
+#pragma unroll
+  for (int x = 0; x < 8; ++x) {
+    const unsigned long long c = __ballot(b.x0 <= x && x <= b.x1);
+    col = (lx == x) ? c : col;
+  }
+#pragma unroll
+  for (int y = 0; y < 8; ++y) {
+    const unsigned long long r = __ballot(b.y0 <= y && y <= b.y1);
+    row = (ly == y) ? r : row;
+  }
+  return col & row;
+}
+
+// One chunk of records in LDS, indexed by slot (read per lane).
+struct Chunk {
+  float4 geo[kChunk];   // u, v, -A/2, -B
+  float4 col[kChunk];   // -C/2, o, r, g
+  float b[kChunk];
+};
+
+// The fields of a record that the blend uses (zeros past the end of a list).  Only these are
+// loaded: a loaded-but-unused register gets reused while its load is in flight, which forces
+// a wait for every outstanding load.
+struct Raw {
+  float2 uv;
+  float4 abco;  // conic A, B, C, opacity
+  float3 rgb;
+  uint32_t gid;
+};
+
+__device__ __forceinline__ uint32_t load_gid(const uint32_t* __restrict__ vals, uint32_t j, uint32_t end) {
+  return j < end ? vals[j] : 0xFFFFFFFFu;
+}
+
+__device__ __forceinline__ Raw load_raw(const float4* __restrict__ splat, uint32_t gid, int64_t n) {
+  Raw r;
+  r.gid = gid;
+  if ((int64_t)gid < n) {  // lists from gs_bin_and_sort are in range; 0xFFFFFFFF past the end
+    const float* rec = reinterpret_cast<const float*>(splat + 3 * (int64_t)gid);
+    r.uv = *reinterpret_cast<const float2*>(rec);
+    r.abco = *reinterpret_cast<const float4*>(rec + 4);
+    r.rgb = *reinterpret_cast<const float3*>(rec + 8);
+  } else {
+    r.uv = make_float2(0.f, 0.f);
+    r.abco = make_float4(0.f, 0.f, 0.f, 0.f);  // opacity 0: empty box
+    r.rgb = make_float3(0.f, 0.f, 0.f);
+  }
+  return r;
+}
+
+__device__ __forceinline__ void put(Chunk& S, int e, const Raw& r) {
+  S.geo[e] = make_float4(r.uv.x, r.uv.y, -0.5f * r.abco.x, -r.abco.y);
+  S.col[e] = make_float4(-0.5f * r.abco.z, r.abco.w, r.rgb.x, r.rgb.y);
+  S.b[e] = r.rgb.z;
+}
+
+// Makes a wave's LDS writes visible to its own later reads.
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ int lowest_bit(unsigned long long m) { return __builtin_ctzll(m); }
+__device__ __forceinline__ int highest_bit(unsigned long long m) { return 63 - __builtin_clzll(m); }
 
 __global__ __launch_bounds__(kBlock) void k_blend_forward(
     int W, int H, int TX, int T, int64_t n, const float4* __restrict__ splat,
     const uint32_t* __restrict__ vals, const uint2* __restrict__ ranges, float bg0, float bg1,
-    float bg2, float* __restrict__ image,
-    float* __restrict__ T_final, uint32_t* __restrict__ last_contrib,
+    float bg2, float* __restrict__ image, float* __restrict__ T_final, uint32_t* __restrict__ last_contrib,
     uint32_t* __restrict__ n_examined, unsigned long long* __restrict__ blend_count) {
-  __shared__ Staged S;
-  __shared__ unsigned long long s_ex[4];
-  const int tile = xcd_tile(blockIdx.x, T);
+  __shared__ Chunk stg[4];
+  const int tile = blockIdx.x;  // consecutive tiles land on different XCDs: balances the load
   const int tx = tile % TX, ty = tile / TX;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int px = tx * kTile + (w & 1) * 8 + (lane & 7);
-  const int py = ty * kTile + (w >> 1) * 8 + (lane >> 3);
+  Chunk& S = stg[w];
+  const int lx = lane & 7, ly = lane >> 3;
+  const int xq = tx * kTile + (w & 1) * 8, yq = ty * kTile + (w >> 1) * 8;  // quadrant origin
+  const int px = xq + lx, py = yq + ly;
   const bool inside = px < W && py < H;
   const float pxc = (float)px + 0.5f, pyc = (float)py + 0.5f;
   const uint2 rg = ranges[tile];
@@ -124,50 +187,49 @@ __global__ __launch_bounds__(kBlock) void k_blend_forward(
   float Tr = 1.0f, c0 = 0.f, c1 = 0.f, c2 = 0.f;
   uint32_t last = 0, examined = end - start;
   bool done = !inside;
-  const uint32_t wbit = 1u << w;
 
-  for (uint32_t b0 = start; b0 < end; b0 += kBatch) {
-    if (__syncthreads_count(!done) == 0) break;
-    const uint32_t j = b0 + tid;
-    if (j < end) stage_entry(S, tid, splat, vals[j], n, tx * kTile, ty * kTile);
-    else S.mask[tid] = 0u;
-    __syncthreads();
-    const int cnt = (int)min((uint32_t)kBatch, end - b0);
-    if (__ballot(!done) != 0ull) {
-      for (int c = 0; c * 64 < cnt; ++c) {
-        unsigned long long M = __ballot((S.mask[c * 64 + lane] & wbit) != 0u);
-        while (M) {
-          const int e = c * 64 + __builtin_ctzll(M);
-          M &= M - 1ull;
-          const float4 g = S.geo[e];
-          const float4 cl = S.col[e];
-          const float bb = S.b[e];
-          if (!done) {
-            const float dx = pxc - g.x, dy = pyc - g.y;
-            const float power = eval_power(g.z, g.w, cl.x, dx, dy);
-            if (power <= 0.0f) {
-              const float alpha = fminf(kAlphaMax, eval_oG(cl.y, power));
-              if (alpha >= kAlphaMin) {
-                const float Tn = Tr * (1.0f - alpha);
-                const uint32_t pos = b0 + (uint32_t)e - start + 1u;
-                if (Tn < kTMin) {
-                  done = true;
-                  examined = pos;
-                } else {
-                  const float wt = alpha * Tr;
-                  c0 += cl.z * wt;
-                  c1 += cl.w * wt;
-                  c2 += bb * wt;
-                  Tr = Tn;
-                  last = pos;
-                }
-              }
-            }
-          }
-          if (__ballot(!done) == 0ull) { M = 0ull; c = 4; }
+  uint32_t gnext = load_gid(vals, start + lane, end);
+  Raw cur = load_raw(splat, gnext, n);
+  gnext = load_gid(vals, start + kChunk + lane, end);
+  for (uint32_t b0 = start; b0 < end; b0 += kChunk) {
+    if (__ballot(!done) == 0ull) break;
+    const Raw nxt = load_raw(splat, gnext, n);  // next chunk in flight
+    gnext = load_gid(vals, b0 + 2 * kChunk + lane, end);
+    put(S, lane, cur);
+    const Box bx = alpha_box(cur.uv.x, cur.uv.y, cur.abco.x, cur.abco.y, cur.abco.z, cur.abco.w, xq, yq);
+    // every lane takes part in the ballots: lane e holds record e's box
+    unsigned long long m = lane_mask(bx, lx, ly);
+    if (done) m = 0ull;
+    wave_sync_lds();
+    const uint32_t base = b0 - start + 1u;  // 1-based position of slot 0
+    while (m) {  // this lane's records, in list order
+      const int e = lowest_bit(m);
+      m &= m - 1ull;
+      const float4 g = S.geo[e];
+      const float4 cl = S.col[e];
+      const float bb = S.b[e];
+      const float dx = pxc - g.x, dy = pyc - g.y;
+      const float power = eval_power(g.z, g.w, cl.x, dx, dy);
+      const float alpha = fminf(kAlphaMax, eval_oG(cl.y, power));
+      if (power <= 0.0f && alpha >= kAlphaMin) {
+        const float Tn = Tr * (1.0f - alpha);
+        const uint32_t pos = base + (uint32_t)e;
+        if (Tn < kTMin) {
+          done = true;
+          examined = pos;
+          m = 0ull;
+        } else {
+          const float wt = alpha * Tr;
+          c0 += cl.z * wt;
+          c1 += cl.w * wt;
+          c2 += bb * wt;
+          Tr = Tn;
+          last = pos;
         }
       }
     }
+    wave_sync_lds();  // this chunk's reads finish before the next chunk is staged
+    cur = nxt;
   }
 
   if (inside) {
@@ -182,9 +244,7 @@ __global__ __launch_bounds__(kBlock) void k_blend_forward(
   if (blend_count) {
     unsigned long long ex = inside ? examined : 0u;
     for (int o = 32; o > 0; o >>= 1) ex += __shfl_xor(ex, o, 64);
-    if (lane == 0) s_ex[w] = ex;
-    __syncthreads();
-    if (tid == 0) atomicAdd(blend_count, s_ex[0] + s_ex[1] + s_ex[2] + s_ex[3]);
+    if (lane == 0) atomicAdd(blend_count, ex);
   }
 }
 
@@ -193,122 +253,109 @@ __global__ __launch_bounds__(kBlock) void k_blend_backward(
     const uint32_t* __restrict__ vals, const uint2* __restrict__ ranges, float bg0, float bg1,
     float bg2, const float* __restrict__ T_final, const uint32_t* __restrict__ last_contrib,
     const float* __restrict__ dLdI, float* __restrict__ grad2d) {
-  __shared__ Staged S;
-  __shared__ float s_grad[9][kBatch];
+  __shared__ Chunk S;                // the tile's current chunk (written by wave 0)
+  __shared__ float acc[9][kChunk];   // gradient sums of the chunk's records over the tile
   __shared__ uint32_t s_max;
-  const int tile = xcd_tile(blockIdx.x, T);
+  const int tile = blockIdx.x;  // consecutive tiles land on different XCDs: balances the load
   const int tx = tile % TX, ty = tile / TX;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int px = tx * kTile + (w & 1) * 8 + (lane & 7);
-  const int py = ty * kTile + (w >> 1) * 8 + (lane >> 3);
+  const int lx = lane & 7, ly = lane >> 3;
+  const int xq = tx * kTile + (w & 1) * 8, yq = ty * kTile + (w >> 1) * 8;
+  const int px = xq + lx, py = yq + ly;
   const bool inside = px < W && py < H;
   const float pxc = (float)px + 0.5f, pyc = (float)py + 0.5f;
   const uint2 rg = ranges[tile];
   const uint32_t start = rg.x;
 
-  float Tr = 0.f, Tfin = 0.f, g0 = 0.f, g1 = 0.f, g2 = 0.f;
+  float Tr = 0.f, g0 = 0.f, g1 = 0.f, g2 = 0.f, bgT = 0.f;
   uint32_t last = 0;
   if (inside) {
     const int64_t p = (int64_t)py * W + px;
-    Tfin = Tr = T_final[p];
+    Tr = T_final[p];
     last = last_contrib[p];
     g0 = dLdI[3 * p];
     g1 = dLdI[3 * p + 1];
     g2 = dLdI[3 * p + 2];
+    bgT = Tr * (bg0 * g0 + bg1 * g1 + bg2 * g2);
   }
-  const float bgdot = bg0 * g0 + bg1 * g1 + bg2 * g2;
   float S0 = 0.f, S1 = 0.f, S2 = 0.f;  // colour accumulated behind the current entry, / T_{k+1}
 
   if (tid == 0) s_max = 0u;
-#pragma unroll
-  for (int r = 0; r < 9; ++r) s_grad[r][tid] = 0.f;
   __syncthreads();
   {
-    uint32_t m = last;
-    for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor(m, o, 64));
-    if (lane == 0) atomicMax(&s_max, m);
+    uint32_t mx = last;
+    for (int o = 32; o > 0; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor(mx, o, 64));
+    if (lane == 0) atomicMax(&s_max, mx);
   }
   __syncthreads();
   const uint32_t end_eff = start + min(s_max, rg.y - start);
-  const uint32_t wbit = 1u << w;
+  const uint32_t nchunks = (end_eff - start + kChunk - 1) / kChunk;
+  // chunk c covers [lo_c, hi_c) with hi_c = end_eff - 64 c, walked back to front
+  auto lo_of = [&](uint32_t c) -> uint32_t {
+    const uint32_t hi = end_eff - c * kChunk;
+    return hi - start > (uint32_t)kChunk ? hi - kChunk : start;
+  };
 
-  for (uint32_t b1 = end_eff; b1 > start;) {
-    const uint32_t b0 = b1 - start > (uint32_t)kBatch ? b1 - kBatch : start;
-    const int cnt = (int)(b1 - b0);
-    __syncthreads();  // the previous batch's flush has read the staged entries
-    if (tid < cnt) stage_entry(S, tid, splat, vals[b0 + tid], n, tx * kTile, ty * kTile);
-    else S.mask[tid] = 0u;
+  uint32_t gnext = nchunks > 0 ? load_gid(vals, lo_of(0) + lane, end_eff) : 0xFFFFFFFFu;
+  Raw cur = load_raw(splat, gnext, n);
+  gnext = nchunks > 1 ? load_gid(vals, lo_of(1) + lane, end_eff - kChunk) : 0xFFFFFFFFu;
+  for (uint32_t c = 0; c < nchunks; ++c) {
+    const uint32_t lo = lo_of(c);
+    const Raw nxt = load_raw(splat, gnext, n);  // next chunk in flight
+    gnext = c + 2 < nchunks ? load_gid(vals, lo_of(c + 2) + lane, end_eff - (c + 2) * kChunk) : 0xFFFFFFFFu;
+    __syncthreads();  // the previous chunk's flush has read acc and S
+    if (w == 0) put(S, lane, cur);
+    for (int k = tid; k < 9 * kChunk; k += kBlock) (&acc[0][0])[k] = 0.f;
+    const Box bx = alpha_box(cur.uv.x, cur.uv.y, cur.abco.x, cur.abco.y, cur.abco.z, cur.abco.w, xq, yq);
+    unsigned long long m = lane_mask(bx, lx, ly);  // all lanes take part in the ballots
     __syncthreads();
-    for (int c = (cnt - 1) >> 6; c >= 0; --c) {
-      unsigned long long M = __ballot((S.mask[c * 64 + lane] & wbit) != 0u);
-      while (M) {
-        const int hb = 63 - __builtin_clzll(M);
-        M &= ~(1ull << hb);
-        const int e = c * 64 + hb;
-        const uint32_t pos = b0 + (uint32_t)e - start;  // 0-based list position
-        const float4 g = S.geo[e];
-        const float4 cl = S.col[e];
-        const float bb = S.b[e];
-        float v_u = 0.f, v_v = 0.f, v_a = 0.f, v_b = 0.f, v_c = 0.f, v_o = 0.f, v_r = 0.f,
-              v_g = 0.f, v_bl = 0.f;
-        bool contrib = false;
-        if (pos < last) {
-          const float dx = pxc - g.x, dy = pyc - g.y;
-          const float power = eval_power(g.z, g.w, cl.x, dx, dy);
-          if (power <= 0.0f) {
-            const float G = __expf(power);
-            const float oG = __fmul_rn(cl.y, G);  // the same operations as eval_oG
-            const float alpha = fminf(kAlphaMax, oG);
-            if (alpha >= kAlphaMin) {
-              contrib = true;
-              const float om = 1.0f - alpha;
-              const float Tk = Tr / om;  // transmittance in front of this entry
-              const float wt = alpha * Tk;
-              v_r = wt * g0;
-              v_g = wt * g1;
-              v_bl = wt * g2;
-              const float dL_dalpha =
-                  Tk * ((cl.z - S0) * g0 + (cl.w - S1) * g1 + (bb - S2) * g2) - Tfin * bgdot / om;
-              S0 = alpha * cl.z + om * S0;
-              S1 = alpha * cl.w + om * S1;
-              S2 = alpha * bb + om * S2;
-              Tr = Tk;
-              if (oG <= kAlphaMax) {  // unclamped: alpha = o G
-                const float dpow = oG * dL_dalpha;
-                v_o = G * dL_dalpha;
-                // A = -2 nA, B = -nB, C = -2 nC
-                v_a = -0.5f * dx * dx * dpow;
-                v_b = -dx * dy * dpow;
-                v_c = -0.5f * dy * dy * dpow;
-                v_u = -(2.0f * g.z * dx + g.w * dy) * dpow;
-                v_v = -(g.w * dx + 2.0f * cl.x * dy) * dpow;
-              }
-            }
-          }
-        }
-        const unsigned long long act = __ballot(contrib);
-        if (act) {
-          const float vals9[9] = {v_u, v_v, v_a, v_b, v_c, v_o, v_r, v_g, v_bl};
-          const bool leader = (lane & 15) == 0 && ((act >> (lane & 48)) & 0xFFFFull) != 0ull;
-#pragma unroll
-          for (int r = 0; r < 9; ++r) {
-            const float s = row_sum16(vals9[r]);
-            if (leader) atomicAdd(&s_grad[r][e], s);
-          }
-        }
+    const uint32_t base = lo - start;  // 0-based position of slot 0
+    while (m) {  // this lane's records, back to front
+      const int e = highest_bit(m);
+      m &= ~(1ull << e);
+      const uint32_t pos = base + (uint32_t)e;
+      if (pos >= last) continue;  // behind the pixel's last blended entry
+      const float4 g = S.geo[e];
+      const float4 cl = S.col[e];
+      const float cb = S.b[e];
+      const float dx = pxc - g.x, dy = pyc - g.y;
+      const float power = eval_power(g.z, g.w, cl.x, dx, dy);
+      const float G = __expf(power);
+      const float oG = __fmul_rn(cl.y, G);  // the same operations as eval_oG
+      const float alpha = fminf(kAlphaMax, oG);
+      if (!(power <= 0.0f && alpha >= kAlphaMin)) continue;
+      const float om = 1.0f - alpha;
+      const float rom = __builtin_amdgcn_rcpf(om);  // om >= 0.01
+      const float Tk = Tr * rom;                    // transmittance in front of this entry
+      const float wt = alpha * Tk;
+      const float cr = cl.z, cg = cl.w;
+      const float dL_dalpha = Tk * ((cr - S0) * g0 + (cg - S1) * g1 + (cb - S2) * g2) - bgT * rom;
+      S0 = alpha * cr + om * S0;
+      S1 = alpha * cg + om * S1;
+      S2 = alpha * cb + om * S2;
+      Tr = Tk;
+      atomicAdd(&acc[6][e], wt * g0);
+      atomicAdd(&acc[7][e], wt * g1);
+      atomicAdd(&acc[8][e], wt * g2);
+      if (oG <= kAlphaMax) {  // unclamped: alpha = o G depends on o and power
+        const float dpow = oG * dL_dalpha;
+        atomicAdd(&acc[0][e], -(2.0f * g.z * dx + g.w * dy) * dpow);  // A = -2 nA, B = -nB
+        atomicAdd(&acc[1][e], -(g.w * dx + 2.0f * cl.x * dy) * dpow);  // C = -2 nC
+        atomicAdd(&acc[2][e], -0.5f * dx * dx * dpow);
+        atomicAdd(&acc[3][e], -dx * dy * dpow);
+        atomicAdd(&acc[4][e], -0.5f * dy * dy * dpow);
+        atomicAdd(&acc[5][e], G * dL_dalpha);
       }
     }
     __syncthreads();
-    if (tid < cnt) {
-      const uint32_t i = S.gid[tid];
+    if (w == 0 && (int64_t)cur.gid < n) {
 #pragma unroll
-      for (int r = 0; r < 9; ++r) {
-        const float v = s_grad[r][tid];
-        if (v != 0.f && (int64_t)i < n) unsafeAtomicAdd(grad2d + (int64_t)r * ld + i, v);
-        s_grad[r][tid] = 0.f;
+      for (int k = 0; k < 9; ++k) {
+        const float x = acc[k][lane];
+        if (x != 0.f) unsafeAtomicAdd(grad2d + (int64_t)k * ld + cur.gid, x);
       }
     }
-    b1 = b0;
+    cur = nxt;
   }
 }
 

@@ -14,7 +14,8 @@ import os
 import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libgsmi.so")
+# the in-tree build; GSMI_LIBRARY selects another build of the same ABI
+LIB_PATH = os.environ.get("GSMI_LIBRARY", os.path.join(_PKG, "libgsmi.so"))
 
 GS_OK, GS_ERR_INVALID_ARGUMENT, GS_ERR_CAPACITY, GS_ERR_HIP, GS_ERR_UNSUPPORTED = 0, -1, -2, -3, -4
 TILE = 16
