@@ -11,8 +11,10 @@ Prints ONE JSON line on stdout (progress goes to stderr):
   value        Gaussian-pixel blends per second over the timed steps (sum of n_examined, the
                list entries each pixel's forward walk examines, / wall time)
   ms_per_step  wall time per step
-  roofline     the dominant single-kernel phase against its roof (HBM bytes the method must
-               move / measured kernel time, from HIP events on the launch stream)
+  roofline     the dominant single-kernel phase against its roof, from HIP events on the
+               launch stream: HBM-bound phases as bytes the method must move / time against
+               8 TB/s, the blends as the fp32 operations the method performs / time against
+               the fp32 vector peak (see FLOPS_EVAL below)
   cpu_baseline the CPU oracle on a bounded sample of the same step (see cpu_baseline())
 """
 from __future__ import annotations
@@ -51,6 +53,62 @@ def alg_bytes(phase, N, R, K, P, T, n_vis):
     if phase == "prebwd_adam":         # params, m, v, grad2d in; params, m, v out
         return N * (24 * R + 36)
     return 0
+
+
+# fp32 operations the method performs per (pixel, list entry) pair of the blends, counting
+# add, mul, compare, min and exp as one each:
+#   every evaluated pair: dx, dy (2), power -(A dx^2 + C dy^2)/2 - B dx dy (9), exp (1),
+#     o G (1), min with 0.99 (1), the power and 1/255 tests (2)                      = 16
+#   a composited pair adds, forward: T (1 - alpha) and its test (3), alpha T (1), three
+#     colour FMAs (6)                                                                 = 10
+#   and backward: 1 - alpha, T / (1 - alpha) (3), alpha T (1), dL/dalpha (11), the three
+#     running colour sums (9), dL/drgb (3), dL/do and dL/dpower (2), dL/du, dL/dv (8),
+#     dL/dA, dL/dB, dL/dC (8), nine accumulations (9)                                 = 54
+FLOPS_EVAL, FLOPS_FWD_BLEND, FLOPS_BWD_BLEND = 16, 10, 54
+# fp32 vector peak without packed-FP32 dual issue (the build turns packed FP32 off):
+# 256 CUs x 4 SIMDs x 16 lanes x 2 flops per FMA x 2.4 GHz
+ALU_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
+
+
+def alg_flops(phase, examined, walked, composited):
+    """Operations the method performs per launch in the two blend kernels."""
+    if phase == "forward":             # walks n_examined entries per pixel
+        return FLOPS_EVAL * examined + FLOPS_FWD_BLEND * composited
+    if phase == "backward_blend":      # walks last_contrib entries per pixel, back to front
+        return FLOPS_EVAL * walked + FLOPS_BWD_BLEND * composited
+    return 0
+
+
+# the kernel behind each single-kernel phase (the backward blend phase also clears grad2d
+# with a fill kernel first, about 1% of its time)
+KERNEL_OF = {"preprocess": "k_preprocess<3>", "forward": "k_blend_forward",
+             "backward_blend": "k_blend_backward", "prebwd_adam": "k_preprocess_backward<3>"}
+
+# HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE passes over this workload,
+# each scaled by the factor the same counter reads for a plain copy of known size; keyed by
+# the SHA-256 of the kernel's source file, so a changed kernel reports null
+COUNTER_TRAFFIC = {
+    "preprocess": {"source": "preprocess.hip", "bytes": 1168086935,
+                   "sha256": "0a00a1b39df4044c4fd1d2abd3b5f77f22a9d8552ef8f074fc6ed43e694036e4"},
+    "forward": {"source": "blend.hip", "bytes": 2871083484,
+                "sha256": "2f879994c873411e8102ea12364b14ad6c1cc2962a6f434568ee3a45c83cf482"},
+    "backward_blend": {"source": "blend.hip", "bytes": 4606070019,
+                       "sha256": "2f879994c873411e8102ea12364b14ad6c1cc2962a6f434568ee3a45c83cf482"},
+    "prebwd_adam": {"source": "preprocess.hip", "bytes": 5808397827,
+                    "sha256": "0a00a1b39df4044c4fd1d2abd3b5f77f22a9d8552ef8f074fc6ed43e694036e4"},
+}
+
+
+def counter_traffic(phase):
+    rec = COUNTER_TRAFFIC.get(phase)
+    if rec is None:
+        return None
+    src = os.path.join(ROOT, "gaussian_splatting_differentiable_preprocess_amd", "csrc", rec["source"])
+    import hashlib
+    with open(src, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != rec["sha256"]:
+            return None
+    return rec["bytes"]
 
 
 def render_targets(gsmi, torch, cfg, cams, tparams_np, targets, log_every=64):
@@ -135,6 +193,27 @@ def cpu_baseline(cfg, params_np, cam, blends_full, crop=512):
             "sample": sample, "ms_per_step": sec * 1e3}
 
 
+def copy_calibration(mib, reps=10):
+    """A plain elementwise copy (out = src * 1) of mib MiB, timed with events on the current stream."""
+    import torch
+
+    n = mib * (1 << 20) // 4
+    src = torch.rand(n, device="cuda")
+    dst = torch.empty_like(src)
+    torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.mul(src, 1.0, out=dst)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nbytes = 2 * n * 4
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "ms_per_copy": round(ms, 4),
+                      "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -146,7 +225,13 @@ def main():
     ap.add_argument("--detail", default=None, help="write a detailed JSON record to this path")
     ap.add_argument("--views", type=int, default=0,
                     help="use only the first N orbit views (short profiling runs); default all")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain streaming copy (read MIB MiB, write MIB MiB) ten times: the "
+                         "known-size kernel that scales the HBM byte counters")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs the single-GPU hot path only: one MI355X holds the whole scene "
               "(4M or 18.18M Gaussians); the multi-GPU exchange is design only. Use --gpus 1.",
@@ -185,7 +270,7 @@ def main():
     buf = gsmi.StepBuffers(N, N, cfg.sh_degree, W, H, k_capacity=kcap)
     grads = torch.empty_like(p) if args.unfused_adam else None
     gcams = [gsmi.make_camera(c) for c in cams]
-    blends = torch.zeros(1, dtype=torch.int64, device="cuda")
+    blends = torch.zeros(3, dtype=torch.int64, device="cuda")
     bg = (0.0, 0.0, 0.0)
     phases = ["preprocess", "bin_and_sort", "forward", "loss", "backward_blend", "prebwd_adam"]
 
@@ -237,26 +322,44 @@ def main():
         ks.append(step(t, (args.warmup + k) % V, evs[k]))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    total_blends = int(blends.item())
+    total_blends = int(blends[0].item())
     ms_per_step = wall * 1e3 / args.steps
     ph_ms = {ph: float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)]))
              for i, ph in enumerate(phases)}
     log("[bench] per-phase ms: " + ", ".join(f"{k} {v:.3f}" for k, v in ph_ms.items()))
     log(f"[bench] {ms_per_step:.3f} ms/step, {total_blends / wall:.4g} blends/s, K mean {np.mean(ks):.0f}")
 
-    # roofline of the dominant single-kernel phase (bin_and_sort is a multi-kernel phase)
+    # roofline of the dominant single-kernel phase (bin_and_sort is a multi-kernel phase):
+    # HBM-bound phases against 8 TB/s, the blends against the fp32 vector peak
     Kmean = float(np.mean(ks))
     n_vis = N
+    sums = blends.cpu().tolist()
+    per_launch = [x / args.steps for x in sums]  # examined, walked, composited per view
     single = {ph: ph_ms[ph] for ph in ("preprocess", "forward", "backward_blend", "prebwd_adam")}
     dom = max(single, key=single.get)
-    bytes_dom = alg_bytes(dom, N, R, Kmean, P, T, n_vis)
-    achieved = bytes_dom / (ph_ms[dom] * 1e-3) / 1e9
-    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": dom,
-            "alg_bytes_per_launch": int(bytes_dom), "ms_per_launch": round(ph_ms[dom], 4)}
-    per_phase = {ph: {"ms": round(ph_ms[ph], 4),
-                      "alg_GBps": round(alg_bytes(ph, N, R, Kmean, P, T, n_vis) / (ph_ms[ph] * 1e-3) / 1e9, 1)}
-                 for ph in phases}
+    sec = ph_ms[dom] * 1e-3
+    if dom in ("forward", "backward_blend"):
+        work = alg_flops(dom, *per_launch)
+        achieved = work / sec / 1e12
+        roof = {"bound": "alu", "achieved": round(achieved, 3), "peak": round(ALU_PEAK_TFLOPS, 1),
+                "unit": "TFLOP/s", "frac": round(achieved / ALU_PEAK_TFLOPS, 4)}
+    else:
+        work = alg_bytes(dom, N, R, Kmean, P, T, n_vis)
+        achieved = work / sec / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    roof.update({"traffic": counter_traffic(dom), "kernel": KERNEL_OF[dom], "work_per_launch": work,
+                 "ms_per_launch": round(ph_ms[dom], 4)})
+    per_phase = {}
+    for ph in phases:
+        d = {"ms": round(ph_ms[ph], 4),
+             "alg_GBps": round(alg_bytes(ph, N, R, Kmean, P, T, n_vis) / (ph_ms[ph] * 1e-3) / 1e9, 1)}
+        if ph in ("forward", "backward_blend"):
+            d["alg_TFLOPs"] = round(alg_flops(ph, *per_launch) / (ph_ms[ph] * 1e-3) / 1e12, 3)
+        per_phase[ph] = d
+    log(f"[bench] roofline: {json.dumps(roof)}")
+    log(f"[bench] per view: {per_launch[0]:.4g} examined, {per_launch[1]:.4g} walked back, "
+        f"{per_launch[2]:.4g} composited (pixel, entry) pairs")
 
     # K and tile-load statistics for the last view (untimed)
     rng_np = buf.ranges.cpu().numpy()
@@ -269,7 +372,7 @@ def main():
         blends.zero_()
         step(t + 1, view)  # one untimed step to count view 0's blends at full resolution
         torch.cuda.synchronize()
-        cpu = cpu_baseline(cfg, params_np, cams[view], int(blends.item()))
+        cpu = cpu_baseline(cfg, params_np, cams[view], int(blends[0].item()))
         log(f"[bench] CPU oracle: {cpu['ms_per_step']:.0f} ms/step-equivalent on {cpu['cores']} threads")
 
     out = {

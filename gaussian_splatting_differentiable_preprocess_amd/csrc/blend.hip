@@ -185,7 +185,7 @@ __global__ __launch_bounds__(kBlock) void k_blend_forward(
   const uint32_t start = rg.x, end = rg.y;
 
   float Tr = 1.0f, c0 = 0.f, c1 = 0.f, c2 = 0.f;
-  uint32_t last = 0, examined = end - start;
+  uint32_t last = 0, examined = end - start, blended = 0;
   bool done = !inside;
 
   uint32_t gnext = load_gid(vals, start + lane, end);
@@ -225,6 +225,7 @@ __global__ __launch_bounds__(kBlock) void k_blend_forward(
           c2 += bb * wt;
           Tr = Tn;
           last = pos;
+          ++blended;
         }
       }
     }
@@ -242,9 +243,25 @@ __global__ __launch_bounds__(kBlock) void k_blend_forward(
     if (n_examined) n_examined[p] = examined;
   }
   if (blend_count) {
-    unsigned long long ex = inside ? examined : 0u;
-    for (int o = 32; o > 0; o >>= 1) ex += __shfl_xor(ex, o, 64);
-    if (lane == 0) atomicAdd(blend_count, ex);
+    unsigned long long ex = inside ? examined : 0u, lc = last, bl = blended;
+    for (int o = 32; o > 0; o >>= 1) {
+      ex += __shfl_xor(ex, o, 64);
+      lc += __shfl_xor(lc, o, 64);
+      bl += __shfl_xor(bl, o, 64);
+    }
+    // one atomic per counter and non-empty tile: same-address atomics from every wave of
+    // the image serialise and would cost more than the blending of a light view
+    __shared__ unsigned long long part[3][4];
+    if (lane == 0) {
+      part[0][w] = ex;
+      part[1][w] = lc;
+      part[2][w] = bl;
+    }
+    __syncthreads();
+    if (tid < 3) {
+      const unsigned long long x = (part[tid][0] + part[tid][1]) + (part[tid][2] + part[tid][3]);
+      if (x != 0ull) atomicAdd(blend_count + tid, x);
+    }
   }
 }
 
@@ -253,12 +270,13 @@ __global__ __launch_bounds__(kBlock) void k_blend_backward(
     const uint32_t* __restrict__ vals, const uint2* __restrict__ ranges, float bg0, float bg1,
     float bg2, const float* __restrict__ T_final, const uint32_t* __restrict__ last_contrib,
     const float* __restrict__ dLdI, float* __restrict__ grad2d) {
-  __shared__ Chunk S;                // the tile's current chunk (written by wave 0)
-  __shared__ float acc[9][kChunk];   // gradient sums of the chunk's records over the tile
-  __shared__ uint32_t s_max;
+  __shared__ Chunk stg[4];                // per quadrant wave: its current chunk
+  __shared__ float accs[4][9][kChunk];    // per quadrant wave: gradient sums of the chunk's records
   const int tile = blockIdx.x;  // consecutive tiles land on different XCDs: balances the load
   const int tx = tile % TX, ty = tile / TX;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  Chunk& S = stg[w];
+  float(&acc)[9][kChunk] = accs[w];
   const int lx = lane & 7, ly = lane >> 3;
   const int xq = tx * kTile + (w & 1) * 8, yq = ty * kTile + (w >> 1) * 8;
   const int px = xq + lx, py = yq + ly;
@@ -280,17 +298,12 @@ __global__ __launch_bounds__(kBlock) void k_blend_backward(
   }
   float S0 = 0.f, S1 = 0.f, S2 = 0.f;  // colour accumulated behind the current entry, / T_{k+1}
 
-  if (tid == 0) s_max = 0u;
-  __syncthreads();
-  {
-    uint32_t mx = last;
-    for (int o = 32; o > 0; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor(mx, o, 64));
-    if (lane == 0) atomicMax(&s_max, mx);
-  }
-  __syncthreads();
-  const uint32_t end_eff = start + min(s_max, rg.y - start);
+  // this wave walks [start, start + its largest last_contrib), back to front
+  uint32_t mx = last;
+  for (int o = 32; o > 0; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor(mx, o, 64));
+  const uint32_t end_eff = start + min(mx, rg.y - start);
   const uint32_t nchunks = (end_eff - start + kChunk - 1) / kChunk;
-  // chunk c covers [lo_c, hi_c) with hi_c = end_eff - 64 c, walked back to front
+  // chunk c covers [lo_c, hi_c) with hi_c = end_eff - 64 c
   auto lo_of = [&](uint32_t c) -> uint32_t {
     const uint32_t hi = end_eff - c * kChunk;
     return hi - start > (uint32_t)kChunk ? hi - kChunk : start;
@@ -303,12 +316,13 @@ __global__ __launch_bounds__(kBlock) void k_blend_backward(
     const uint32_t lo = lo_of(c);
     const Raw nxt = load_raw(splat, gnext, n);  // next chunk in flight
     gnext = c + 2 < nchunks ? load_gid(vals, lo_of(c + 2) + lane, end_eff - (c + 2) * kChunk) : 0xFFFFFFFFu;
-    __syncthreads();  // the previous chunk's flush has read acc and S
-    if (w == 0) put(S, lane, cur);
-    for (int k = tid; k < 9 * kChunk; k += kBlock) (&acc[0][0])[k] = 0.f;
+    put(S, lane, cur);
+#pragma unroll
+    for (int k = 0; k < 9; ++k) acc[k][lane] = 0.f;
     const Box bx = alpha_box(cur.uv.x, cur.uv.y, cur.abco.x, cur.abco.y, cur.abco.z, cur.abco.w, xq, yq);
     unsigned long long m = lane_mask(bx, lx, ly);  // all lanes take part in the ballots
-    __syncthreads();
+    const unsigned long long touched = __ballot(bx.x0 <= bx.x1 && bx.y0 <= bx.y1);
+    wave_sync_lds();
     const uint32_t base = lo - start;  // 0-based position of slot 0
     while (m) {  // this lane's records, back to front
       const int e = highest_bit(m);
@@ -347,14 +361,15 @@ __global__ __launch_bounds__(kBlock) void k_blend_backward(
         atomicAdd(&acc[5][e], G * dL_dalpha);
       }
     }
-    __syncthreads();
-    if (w == 0 && (int64_t)cur.gid < n) {
+    wave_sync_lds();
+    if (((touched >> lane) & 1ull) && (int64_t)cur.gid < n) {
 #pragma unroll
       for (int k = 0; k < 9; ++k) {
         const float x = acc[k][lane];
         if (x != 0.f) unsafeAtomicAdd(grad2d + (int64_t)k * ld + cur.gid, x);
       }
     }
+    wave_sync_lds();  // the flush has read acc before the next chunk clears it
     cur = nxt;
   }
 }

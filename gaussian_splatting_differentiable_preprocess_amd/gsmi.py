@@ -192,6 +192,8 @@ def _bg(bg):
 
 def render_forward(cam: GsCamera, n, splat, vals, ranges, bg, image, T_final, last_contrib,
                    n_examined=None, blend_count=None, stream=None):
+    if blend_count is not None and (blend_count.numel() < 3 or blend_count.element_size() != 8):
+        raise ValueError("blend_count must be a device int64 tensor of at least 3 elements")
     _check(load().gs_render_forward(ctypes.byref(cam), int(n), _ptr(splat), _ptr(vals), _ptr(ranges), _bg(bg),
                                     _ptr(image), _ptr(T_final), _ptr(last_contrib), _ptr(n_examined),
                                     _ptr(blend_count), _stream(stream)))

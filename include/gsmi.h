@@ -160,8 +160,10 @@ int gs_bin_and_sort(const gs_scene* scene, const gs_camera* cam, gs_proj proj, v
  *   last_contrib[H][W]  out: 1-based list position of the last blended entry (0 = none)
  *   n_examined[H][W]    out, nullable: entries examined (list length, or the position of
  *                       the entry that stopped the pixel)
- *   blend_count         out, nullable: device uint64 to which the sum of n_examined over
- *                       the image is ADDED (the caller zeroes it)
+ *   blend_count         out, nullable: device uint64[3] to which three image sums are
+ *                       ADDED (the caller zeroes them): [0] n_examined, [1] last_contrib
+ *                       (the entries the backward pass walks), [2] the (pixel, entry)
+ *                       pairs composited
  * bg is a HOST array of 3 floats.  One 256-thread workgroup per tile. */
 int gs_render_forward(const gs_camera* cam, int64_t n, const gs_splat* splat, const uint32_t* vals,
                       const uint32_t* ranges, const float* bg, float* image, float* T_final,

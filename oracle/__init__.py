@@ -60,7 +60,7 @@ def lib():
         L.or_bin_sort.argtypes = [i64, P, P, i32, i32, P, P]
         L.or_bin_sort.restype = i64
         L.or_ranges.argtypes = [i64, P, i32, P]
-        L.or_render_forward.argtypes = [i32, i32, P, i64, P, P, P, P, P, P, P, P, P, P, i64, i32]
+        L.or_render_forward.argtypes = [i32, i32, P, i64, P, P, P, P, P, P, P, P, P, P, P, i64, i32]
         L.or_render_bruteforce.argtypes = [i32, i32, P, i64, P, P, P, P, P, P]
         L.or_loss_l1.argtypes = [i64, P, P, P]
         L.or_loss_l1.restype = dbl
@@ -153,7 +153,7 @@ def ranges(keys, n_tiles):
 def render_forward(proj, vals, rng, W, H, bg=(0.0, 0.0, 0.0), margins=None,
                    record_decisions=False, decisions=None):
     """Tiled forward.  Returns dict(image [H][W][3], T_final, last_contrib, n_examined,
-    borderline) and, with record_decisions, 'decisions' (int8 [H*W][maxlen])."""
+    borderline, n_blended) and, with record_decisions, 'decisions' (int8 [H*W][maxlen])."""
     proj = _f64(proj)
     n = proj.shape[1]
     vals = np.ascontiguousarray(vals, np.uint32)
@@ -164,6 +164,7 @@ def render_forward(proj, vals, rng, W, H, bg=(0.0, 0.0, 0.0), margins=None,
     last = np.zeros((H, W), np.uint32)
     ex = np.zeros((H, W), np.uint32)
     bl = np.zeros((H, W), np.uint8)
+    nb = np.zeros((H, W), np.uint32)
     mg = _f64(margins) if margins is not None else None
     lens = rng[1::2].astype(np.int64) - rng[0::2].astype(np.int64)
     stride = int(max(1, lens.max() if lens.size else 1))
@@ -177,8 +178,9 @@ def render_forward(proj, vals, rng, W, H, bg=(0.0, 0.0, 0.0), margins=None,
         mode = 2
     vals_arg = vals if vals.size else np.zeros(1, np.uint32)
     lib().or_render_forward(W, H, _p(bgv), n, _p(proj), _p(vals_arg), _p(rng), _p(img), _p(Tf),
-                            _p(last), _p(ex), _p(bl), _p(mg), _p(dec), stride, mode)
-    out = dict(image=img, T_final=Tf, last_contrib=last, n_examined=ex, borderline=bl.astype(bool))
+                            _p(last), _p(ex), _p(bl), _p(nb), _p(mg), _p(dec), stride, mode)
+    out = dict(image=img, T_final=Tf, last_contrib=last, n_examined=ex, borderline=bl.astype(bool),
+               n_blended=nb)
     if record_decisions:
         out["decisions"] = dec
     return out

@@ -566,13 +566,15 @@ static void blend_pixel(int px, int py, const double* proj, int64_t n, const uin
 }
 
 /* Tiled forward render.  image [H][W][3], T_final [H][W], last_contrib [H][W],
- * n_examined [H][W], borderline [H][W] (uint8, nullable).  `dec` (nullable) is a
+ * n_examined [H][W], borderline [H][W] (uint8, nullable), n_blended [H][W] (nullable: the
+ * entries composited into each pixel).  `dec` (nullable) is a
  * per-pixel array of decision codes with row stride `dec_stride`; with `dec_mode` = 1 the
  * codes are written, with 2 they are read instead of testing the thresholds. */
 int or_render_forward(int W, int H, const double* bg, int64_t n, const double* proj,
                       const uint32_t* vals, const uint32_t* ranges, double* image, double* T_final,
                       uint32_t* last_contrib, uint32_t* n_examined, uint8_t* borderline,
-                      const double* margins, int8_t* dec, int64_t dec_stride, int dec_mode) {
+                      uint32_t* n_blended, const double* margins, int8_t* dec, int64_t dec_stride,
+                      int dec_mode) {
   const int TX = (W + TILE - 1) / TILE;
   margins_t mg = {1e-4, 1e-4, 1e-6};
   if (margins) { mg.margin_alpha = margins[0]; mg.margin_T = margins[1]; mg.margin_power = margins[2]; }
@@ -581,13 +583,14 @@ int or_render_forward(int W, int H, const double* bg, int64_t n, const double* p
     const int px = (int)(p % W), py = (int)(p / W);
     const int t = (py / TILE) * TX + px / TILE;
     double C[3];
-    int flag = 0;
+    int flag = 0, cnt = 0;
     int8_t* dp = dec ? dec + p * dec_stride : NULL;
     blend_pixel(px, py, proj, n, vals, ranges[2 * t], ranges[2 * t + 1], bg, C, &T_final[p],
-                &last_contrib[p], &n_examined[p], NULL, NULL, &mg, &flag,
+                &last_contrib[p], &n_examined[p], NULL, &cnt, &mg, &flag,
                 dec_mode == 1 ? dp : NULL, dec_mode == 2 ? dp : NULL);
     for (int ch = 0; ch < 3; ch++) image[3 * p + ch] = C[ch];
     if (borderline) borderline[p] = (uint8_t)flag;
+    if (n_blended) n_blended[p] = (uint32_t)cnt;
   }
   return 0;
 }

@@ -102,13 +102,13 @@ class GpuStep:
         self.T_final = torch.empty((H, W), dtype=torch.float32, device="cuda")
         self.last = torch.empty((H, W), dtype=torch.int32, device="cuda")
         self.nex = torch.empty((H, W), dtype=torch.int32, device="cuda")
-        self.bcount = torch.zeros(1, dtype=torch.int64, device="cuda")
+        self.bcount = torch.zeros(3, dtype=torch.int64, device="cuda")
         gsmi.render_forward(self.cam, self.n, self.proj.splat, self.vals, rg, bg, self.image, self.T_final,
                             self.last, self.nex, self.bcount)
         torch.cuda.synchronize()
         return dict(image=self.image.cpu().numpy(), T_final=self.T_final.cpu().numpy(),
                     last_contrib=self.last.cpu().numpy().view(np.uint32),
-                    n_examined=self.nex.cpu().numpy().view(np.uint32), blend_count=int(self.bcount.item()))
+                    n_examined=self.nex.cpu().numpy().view(np.uint32), blend_count=self.bcount.cpu().tolist())
 
     def loss(self, target):
         torch = self.torch

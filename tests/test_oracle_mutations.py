@@ -1,0 +1,68 @@
+"""The oracle's pins catch plausible mistakes: each case plants one mistake in a copy of the
+oracle's C source (a flipped sign, a dropped factor, a transposed operand, a wrong index, a
+broken tie-break, a missing term), rebuilds it and runs the pin suites, which must fail.
+
+Everything here runs on the CPU, in a temporary copy of the repository."""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# (name, text in oracle.c, planted replacement)
+MUTATIONS = [
+    ("J02 sign", "F->J[0][2] = -k->fx * F->xc / z;", "F->J[0][2] = k->fx * F->xc / z;"),
+    ("dA factor", "grad2d[2 * n + i] += -0.5 * dx * dx * dL_dpower;", "grad2d[2 * n + i] += -1.0 * dx * dx * dL_dpower;"),
+    ("Y5 sign", "Y[5] = -c2a * y * z;", "Y[5] = c2a * y * z;"),
+    ("dR/dx entry", "{2 * y, -4 * x, -2 * w}", "{2 * y, -4 * x, 2 * w}"),
+    ("suffix index", "(suffix[k + 1] + Tf * bgg)", "(suffix[k] + Tf * bgg)"),
+    ("rect +1", "r[1] = clamp_tile(floorf(uhi * 0.0625f) + 1.0f, TX);", "r[1] = clamp_tile(floorf(uhi * 0.0625f), TX);"),
+    ("adam bias", "const double mh = m[e] / c1, vh = v[e] / c2;", "const double mh = m[e], vh = v[e] / c2;"),
+    ("unstable sort", "if (ks[b] < ks[a])", "if (ks[b] <= ks[a])"),
+    ("no dilation", "#define DILATION 0.3 ", "#define DILATION 0.0 "),
+    ("no stop", "code = ((float)Tn < T_MIN_F) ? DEC_STOP", "code = ((float)Tn < 0.0f) ? DEC_STOP"),
+    ("V transpose", "acc += RS[r][j] * k->Rc[c][j];", "acc += RS[r][j] * k->Rc[j][c];"),
+    ("quaternion norm grad", "grads[(6 + j) * n + i] = (gq[j] - F.qn[j] * qd) / F.qlen;",
+     "grads[(6 + j) * n + i] = gq[j] / F.qlen;"),
+    ("view-dir grad", "gmu[j] += (gdir[j] - F.dir[j] * dd) / F.dist;", "gmu[j] += gdir[j] / F.dist;"),
+    ("dY13", "dY[13][0] = -c3c * (4.0 * z * z - 3.0 * x * x - y * y);",
+     "dY[13][0] = -c3c * (4.0 * z * z - x * x - y * y);"),
+    ("dL/dJ factor", "GJ[r][c] = 2.0 * acc;", "GJ[r][c] = acc;"),
+    ("clamped alpha grad", "if (list[k].clamped) continue;", "if (0) continue;"),
+    ("sigmoid grad", "grads[10 * n + i] = F.o * (1.0 - F.o) * go;", "grads[10 * n + i] = F.o * go;"),
+    ("background term", "- (suffix[k + 1] + Tf * bgg) / (1.0 - a)", "- (suffix[k + 1]) / (1.0 - a)"),
+]
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(name, old, new, tmp_path):
+    src = open(os.path.join(ROOT, "oracle", "oracle.c")).read()
+    assert src.count(old) == 1, f"mutation site for {name!r} not found once"
+    dst = tmp_path / "repo"
+    shutil.copytree(ROOT, dst, ignore=shutil.ignore_patterns(
+        ".git", "_work", "_build", "gpurun_out", "*.so", "__pycache__", "profiles"))
+    with open(dst / "oracle" / "oracle.c", "w") as f:
+        f.write(src.replace(old, new, 1))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        "tests/test_oracle_pins.py", "tests/test_oracle_gradients.py"],
+                       cwd=dst, capture_output=True, text=True, timeout=600)
+    tail = "\n".join(r.stdout.strip().splitlines()[-3:])
+    assert r.returncode == 1, f"planted mistake {name!r} was not caught by the pins:\n{tail}"
+
+
+@pytest.mark.slow
+def test_unmutated_copy_passes(tmp_path):
+    """Control: the same copy procedure without a planted mistake passes the pins."""
+    dst = tmp_path / "repo"
+    shutil.copytree(ROOT, dst, ignore=shutil.ignore_patterns(
+        ".git", "_work", "_build", "gpurun_out", "*.so", "__pycache__", "profiles"))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        "tests/test_oracle_pins.py", "tests/test_oracle_gradients.py"],
+                       cwd=dst, capture_output=True, text=True, timeout=600)
+    assert r.returncode == 0, r.stdout[-2000:]

@@ -367,6 +367,7 @@ def test_stacked_layers_stop_before_blending():
     assert out["T_final"][8, 8] == pytest.approx(1.25e-4, rel=1e-12)
     assert out["last_contrib"][8, 8] == 3
     assert out["n_examined"][8, 8] == 4
+    assert out["n_blended"][8, 8] == 3
 
 
 def _tiny_scene(seed, n, deg, W, logs=-2.0, dist=3.0):
@@ -407,6 +408,9 @@ def test_partition_of_unity_and_transmittance_invariants():
     assert (out["n_examined"] >= out["last_contrib"]).all()
     # T_final is the product of (1 - alpha) over the blended entries
     dec = oracle.render_forward(proj, vals, rg, W, W, record_decisions=True)["decisions"]
+    blended = np.isin(dec, (oracle.DEC_BLEND, oracle.DEC_BLEND_CLAMPED)).sum(axis=1)
+    np.testing.assert_array_equal(out["n_blended"].reshape(-1), blended)
+    assert (out["n_blended"] <= out["last_contrib"]).all()
     for p in range(0, W * W, 37):
         py, px = divmod(p, W)
         t = (py // 16) * ((W + 15) // 16) + px // 16
