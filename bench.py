@@ -128,7 +128,7 @@ def render_targets(gsmi, torch, cfg, cams, tparams_np, targets, log_every=64):
             except gsmi.GsCapacityError as e:
                 buf.grow(int(e.required * 1.25) + 1024)
         gsmi.render_forward(c, n, buf.proj.splat, buf.vals, buf.ranges, (0.0, 0.0, 0.0), targets[vi], buf.T_final,
-                            buf.last)
+                            buf.last, buf.render_ws)
         ks.append(K)
         if vi % log_every == 0:
             log(f"  target view {vi}: K = {K}")
@@ -285,14 +285,14 @@ def main():
         if ev is not None:
             ev[2].record()
         gsmi.render_forward(cam, N, buf.proj.splat, buf.vals, buf.ranges, bg, buf.image, buf.T_final, buf.last,
-                            blend_count=blends)
+                            buf.render_ws, blend_count=blends)
         if ev is not None:
             ev[3].record()
         gsmi.loss_l1(3 * P, buf.image, targets[view], buf.loss, buf.dLdI, buf.loss_ws)
         if ev is not None:
             ev[4].record()
         gsmi.render_backward(buf.scene, None, cam, buf.proj, buf.vals, buf.ranges, bg, buf.T_final, buf.last,
-                             buf.dLdI, buf.grad2d)
+                             buf.dLdI, buf.grad2d, buf.render_ws)
         if ev is not None:
             ev[5].record()
         adam = gsmi.make_adam(m, v, t, 1e-3)

@@ -21,13 +21,14 @@
 // Workgroup b renders tile b: the hardware deals consecutive workgroups to the 8 XCDs in turn,
 // which spreads the (very uneven) per-tile work evenly over them.  Bound: VALU /
 // transcendental and LDS, not HBM.
+#include <algorithm>
+
 #include "gsmi_internal.h"
 
 namespace gsmi {
 
 namespace {
 
-constexpr int kBatch = kBlock;
 constexpr float kAlphaMin = 1.0f / 255.0f;
 constexpr float kAlphaMax = 0.99f;
 constexpr float kTMin = 1e-4f;
@@ -41,29 +42,28 @@ __device__ __forceinline__ float eval_power(float nA, float nB, float nC, float 
 
 __device__ __forceinline__ float eval_oG(float o, float power) { return __fmul_rn(o, __expf(power)); }
 
-// One DPP step x += permute(x) (old value 0 = identity of the add, so the move folds into
-// v_add_f32_dpp).
-template <int CTRL>
+// One DPP step x += permute(x) on the rows in ROW_MASK (old value 0 = identity of the add).
+template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ float dpp_add(float x) {
-  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xF, false));
 }
 
-// Sums each of N values over the 16 lanes of every row (all lanes of a row get the row
-// sum).  The steps are interleaved across the N values so consecutive DPP reads never
-// depend on the instruction just before them.
+// Sums each of N values over each group of 8 lanes (a pixel row of a quadrant); every lane
+// gets its group's sums.  The steps are interleaved across the N values so a DPP read never
+// waits on the instruction just before it.  The lanes of a group must be all active or all
+// inactive.
 template <int N>
-__device__ __forceinline__ void row_sum16(float* v) {
+__device__ __forceinline__ void row8_sum(float* v) {
 #pragma unroll
-  for (int q = 0; q < N; ++q) v[q] = dpp_add<0xB1>(v[q]);   // quad_perm [1,0,3,2]: xor 1
+  for (int q = 0; q < N; ++q) v[q] = dpp_add<0xB1, 0xF>(v[q]);   // quad_perm [1,0,3,2]
 #pragma unroll
-  for (int q = 0; q < N; ++q) v[q] = dpp_add<0x4E>(v[q]);   // quad_perm [2,3,0,1]: xor 2
+  for (int q = 0; q < N; ++q) v[q] = dpp_add<0x4E, 0xF>(v[q]);   // quad_perm [2,3,0,1]
 #pragma unroll
-  for (int q = 0; q < N; ++q) v[q] = dpp_add<0x141>(v[q]);  // row_half_mirror
-#pragma unroll
-  for (int q = 0; q < N; ++q) v[q] = dpp_add<0x140>(v[q]);  // row_mirror
+  for (int q = 0; q < N; ++q) v[q] = dpp_add<0x141, 0xF>(v[q]);  // row_half_mirror
 }
 
 constexpr int kChunk = 64;  // records staged per chunk (one per lane)
+constexpr int kWin = kBlock;  // list entries whose gradient sums a workgroup gathers before adding them to grad2d
 
 // Conservative pixel-index box [x0,x1] x [y0,y1] (relative to the quadrant origin, clamped to
 // 0..7) of the pixels whose centres can satisfy o e^power >= 1/255.  That region is the ellipse
@@ -97,8 +97,10 @@ __device__ __forceinline__ Box alpha_box(float u, float v, float A, float B, flo
 }
 
 // Per-lane masks: bit e set iff record e's box contains the lane's pixel (lx, ly).  Lane e
-// holds record e's box; COL[x] / ROW[y] are ballots over the records.
-__device__ __forceinline__ unsigned long long lane_mask(const Box& b, int lx, int ly) {
+// holds record e's box; COL[x] / ROW[y] are ballots over the records.  *row_out (optional)
+// gets ROW[ly], the records whose box meets the lane's pixel row.
+__device__ __forceinline__ unsigned long long lane_mask(const Box& b, int lx, int ly,
+                                                     unsigned long long* row_out = nullptr) {
   unsigned long long col = 0ull, row = 0ull;
 #pragma unroll
   for (int x = 0; x < 8; ++x) {
@@ -110,6 +112,7 @@ __device__ __forceinline__ unsigned long long lane_mask(const Box& b, int lx, in
     const unsigned long long r = __ballot(b.y0 <= y && y <= b.y1);
     row = (ly == y) ? r : row;
   }
+  if (row_out) *row_out = row;
   return col & row;
 }
 
@@ -130,24 +133,33 @@ struct Raw {
   uint32_t gid;
 };
 
-__device__ __forceinline__ uint32_t load_gid(const uint32_t* __restrict__ vals, uint32_t j, uint32_t end) {
-  return j < end ? vals[j] : 0xFFFFFFFFu;
+// Loads are unconditional (the index is clamped into the list and the result masked), so every
+// pass of a chunk loop issues the same memory operations and the compiler can wait for exactly
+// the load it needs instead of for all outstanding ones.
+//   vals[j] for j < end, else 0xFFFFFFFF; `safe` is any index inside the list
+__device__ __forceinline__ uint32_t load_gid(const uint32_t* __restrict__ vals, uint32_t j, uint32_t end,
+                                             uint32_t safe) {
+  const uint32_t v = vals[j < end ? j : safe];
+  return j < end ? v : 0xFFFFFFFFu;
 }
 
+// The record of Gaussian gid, or of Gaussian 0 for gid >= n (past the end of a list); callers
+// give such a record opacity 0 (an empty box) where they use it.  The loaded registers are left
+// untouched here: overwriting a load's destination before it lands would force a wait for
+// every outstanding load.  Requires n >= 1.
 __device__ __forceinline__ Raw load_raw(const float4* __restrict__ splat, uint32_t gid, int64_t n) {
+  const float* rec = reinterpret_cast<const float*>(splat + 3 * ((int64_t)gid < n ? (int64_t)gid : 0));
   Raw r;
   r.gid = gid;
-  if ((int64_t)gid < n) {  // lists from gs_bin_and_sort are in range; 0xFFFFFFFF past the end
-    const float* rec = reinterpret_cast<const float*>(splat + 3 * (int64_t)gid);
-    r.uv = *reinterpret_cast<const float2*>(rec);
-    r.abco = *reinterpret_cast<const float4*>(rec + 4);
-    r.rgb = *reinterpret_cast<const float3*>(rec + 8);
-  } else {
-    r.uv = make_float2(0.f, 0.f);
-    r.abco = make_float4(0.f, 0.f, 0.f, 0.f);  // opacity 0: empty box
-    r.rgb = make_float3(0.f, 0.f, 0.f);
-  }
+  r.uv = *reinterpret_cast<const float2*>(rec);
+  r.abco = *reinterpret_cast<const float4*>(rec + 4);
+  r.rgb = *reinterpret_cast<const float3*>(rec + 8);
   return r;
+}
+
+// opacity of a loaded record as the blend sees it (0 past the end of a list)
+__device__ __forceinline__ float opacity_of(const Raw& r, int64_t n) {
+  return (int64_t)r.gid < n ? r.abco.w : 0.f;
 }
 
 __device__ __forceinline__ void put(Chunk& S, int e, const Raw& r) {
@@ -166,11 +178,105 @@ __device__ __forceinline__ void wave_sync_lds() {
 __device__ __forceinline__ int lowest_bit(unsigned long long m) { return __builtin_ctzll(m); }
 __device__ __forceinline__ int highest_bit(unsigned long long m) { return 63 - __builtin_clzll(m); }
 
+// ---------------------------------------------------------------------------------------------
+// Segment plan.  One workgroup: for every tile, its list length len decides
+//   items(t) = ceil(len / SEG) backward work items (0 for an empty tile),
+//   slots(t) = ceil(len / SEG) state slots if len > SEG (one per boundary + the final state),
+// SEG = 2^shift is the smallest power of two >= 2^kSegShiftMin whose slots fit the workspace.
+// Writes bnd_off (exclusive scan of slots), the item list and the header.
+// ---------------------------------------------------------------------------------------------
+constexpr int kPlanThreads = 1024;
+
+template <typename U>
+__device__ U block_sum_1024(U x, U* red) {
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  U t = 0;
+#pragma unroll
+  for (int k = 0; k < kPlanThreads / 64; ++k) t += red[k];
+  __syncthreads();
+  return t;
+}
+
+// exclusive scan over the 1024 threads
+__device__ uint32_t block_exscan_1024(uint32_t x, uint32_t* red) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  uint32_t inc = x;
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += y;
+  }
+  if (lane == 63) red[w] = inc;
+  __syncthreads();
+  uint32_t base = 0;
+  for (int k = 0; k < w; ++k) base += red[k];
+  __syncthreads();
+  return base + inc - x;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void k_seg_plan(const uint2* __restrict__ ranges, int T,
+                                                           uint32_t slots_cap, uint32_t* __restrict__ hdr,
+                                                           uint32_t* __restrict__ bnd_off,
+                                                           uint2* __restrict__ items) {
+  __shared__ unsigned long long red64[kPlanThreads / 64];
+  __shared__ uint32_t red32[kPlanThreads / 64];
+  const int per = (T + kPlanThreads - 1) / kPlanThreads;
+  const int t0 = min(T, (int)threadIdx.x * per), t1 = min(T, t0 + per);
+  int shift = kSegShiftMin;
+  for (;;) {  // every thread takes the same exit (the sum is block-wide)
+    unsigned long long s = 0;
+    for (int t = t0; t < t1; ++t) {
+      const uint2 r = ranges[t];
+      const uint32_t len = r.y - r.x;
+      if (len > (1u << shift)) s += ((len - 1u) >> shift) + 1u;
+    }
+    s = block_sum_1024(s, red64);
+    if (s <= slots_cap || shift >= 31) break;
+    ++shift;
+  }
+  const uint32_t seg = 1u << shift;
+  uint32_t my_slots = 0, my_items = 0;
+  for (int t = t0; t < t1; ++t) {
+    const uint2 r = ranges[t];
+    const uint32_t len = r.y - r.x, k = len ? ((len - 1u) >> shift) + 1u : 0u;
+    my_items += k;
+    my_slots += len > seg ? k : 0u;
+  }
+  uint32_t so = block_exscan_1024(my_slots, red32);
+  uint32_t io = block_exscan_1024(my_items, red32);
+  for (int t = t0; t < t1; ++t) {
+    const uint2 r = ranges[t];
+    const uint32_t len = r.y - r.x, k = len ? ((len - 1u) >> shift) + 1u : 0u;
+    bnd_off[t] = so;
+    so += len > seg ? k : 0u;
+    for (uint32_t j = 0; j < k; ++j) items[io + j] = make_uint2((uint32_t)t, j);
+    io += k;
+  }
+  if (t1 == T && (t0 < t1 || threadIdx.x == 0)) {  // the thread that owns the last tile
+    bnd_off[T] = so;
+    hdr[0] = (uint32_t)shift;
+    hdr[1] = io;
+    hdr[2] = so;
+    hdr[3] = 0u;
+  }
+}
+
+// pixel index inside its tile of lane (lx, ly) of quadrant wave w
+__device__ __forceinline__ int tile_pixel(int w, int lx, int ly) {
+  return (((w >> 1) << 3) + ly) * kTile + ((w & 1) << 3) + lx;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Forward.  Besides the image, a tile whose list is longer than one segment leaves each pixel's
+// (T, C) at every segment boundary it reaches and its final (T, C) in the render workspace.
+// ---------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(kBlock) void k_blend_forward(
     int W, int H, int TX, int T, int64_t n, const float4* __restrict__ splat,
     const uint32_t* __restrict__ vals, const uint2* __restrict__ ranges, float bg0, float bg1,
     float bg2, float* __restrict__ image, float* __restrict__ T_final, uint32_t* __restrict__ last_contrib,
-    uint32_t* __restrict__ n_examined, unsigned long long* __restrict__ blend_count) {
+    uint32_t* __restrict__ n_examined, unsigned long long* __restrict__ blend_count,
+    const uint32_t* __restrict__ ws_hdr, const uint32_t* __restrict__ bnd_off, float4* __restrict__ slots) {
   __shared__ Chunk stg[4];
   const int tile = blockIdx.x;  // consecutive tiles land on different XCDs: balances the load
   const int tx = tile % TX, ty = tile / TX;
@@ -182,55 +288,65 @@ __global__ __launch_bounds__(kBlock) void k_blend_forward(
   const bool inside = px < W && py < H;
   const float pxc = (float)px + 0.5f, pyc = (float)py + 0.5f;
   const uint2 rg = ranges[tile];
-  const uint32_t start = rg.x, end = rg.y;
+  const uint32_t start = rg.x, end = rg.y, len = end - start;
+  const uint32_t shift = ws_hdr[0], seg_mask = (1u << shift) - 1u;
+  const bool long_list = len > seg_mask + 1u;
+  float4* const st = slots + (size_t)(long_list ? bnd_off[tile] : 0u) * (kTile * kTile) + tile_pixel(w, lx, ly);
 
   float Tr = 1.0f, c0 = 0.f, c1 = 0.f, c2 = 0.f;
-  uint32_t last = 0, examined = end - start, blended = 0;
+  uint32_t last = 0, examined = len, blended = 0;
   bool done = !inside;
 
-  uint32_t gnext = load_gid(vals, start + lane, end);
-  Raw cur = load_raw(splat, gnext, n);
-  gnext = load_gid(vals, start + kChunk + lane, end);
-  for (uint32_t b0 = start; b0 < end; b0 += kChunk) {
-    if (__ballot(!done) == 0ull) break;
-    const Raw nxt = load_raw(splat, gnext, n);  // next chunk in flight
-    gnext = load_gid(vals, b0 + 2 * kChunk + lane, end);
-    put(S, lane, cur);
-    const Box bx = alpha_box(cur.uv.x, cur.uv.y, cur.abco.x, cur.abco.y, cur.abco.z, cur.abco.w, xq, yq);
-    // every lane takes part in the ballots: lane e holds record e's box
-    unsigned long long m = lane_mask(bx, lx, ly);
-    if (done) m = 0ull;
-    wave_sync_lds();
-    const uint32_t base = b0 - start + 1u;  // 1-based position of slot 0
-    while (m) {  // this lane's records, in list order
-      const int e = lowest_bit(m);
-      m &= m - 1ull;
-      const float4 g = S.geo[e];
-      const float4 cl = S.col[e];
-      const float bb = S.b[e];
-      const float dx = pxc - g.x, dy = pyc - g.y;
-      const float power = eval_power(g.z, g.w, cl.x, dx, dy);
-      const float alpha = fminf(kAlphaMax, eval_oG(cl.y, power));
-      if (power <= 0.0f && alpha >= kAlphaMin) {
-        const float Tn = Tr * (1.0f - alpha);
-        const uint32_t pos = base + (uint32_t)e;
-        if (Tn < kTMin) {
-          done = true;
-          examined = pos;
-          m = 0ull;
-        } else {
-          const float wt = alpha * Tr;
-          c0 += cl.z * wt;
-          c1 += cl.w * wt;
-          c2 += bb * wt;
-          Tr = Tn;
-          last = pos;
-          ++blended;
+  if (len > 0) {
+    uint32_t gnext = load_gid(vals, start + lane, end, start);
+    Raw cur = load_raw(splat, gnext, n);
+    gnext = load_gid(vals, start + kChunk + lane, end, start);
+    for (uint32_t b0 = start; b0 < end; b0 += kChunk) {
+      if (__ballot(!done) == 0ull) break;
+      const Raw nxt = load_raw(splat, gnext, n);  // next chunk in flight
+      gnext = load_gid(vals, b0 + 2 * kChunk + lane, end, start);
+      const uint32_t rel = b0 - start;
+      if (long_list && rel != 0u && (rel & seg_mask) == 0u)  // state at segment boundary rel
+        st[(size_t)((rel >> shift) - 1u) * (kTile * kTile)] = make_float4(Tr, c0, c1, c2);
+      put(S, lane, cur);
+      const Box bx = alpha_box(cur.uv.x, cur.uv.y, cur.abco.x, cur.abco.y, cur.abco.z, opacity_of(cur, n), xq, yq);
+      // every lane takes part in the ballots: lane e holds record e's box
+      unsigned long long m = lane_mask(bx, lx, ly);
+      if (done) m = 0ull;
+      wave_sync_lds();
+      const uint32_t base = rel + 1u;  // 1-based position of slot 0
+      while (m) {  // this lane's records, in list order
+        const int e = lowest_bit(m);
+        m &= m - 1ull;
+        const float4 g = S.geo[e];
+        const float4 cl = S.col[e];
+        const float bb = S.b[e];
+        const float dx = pxc - g.x, dy = pyc - g.y;
+        const float power = eval_power(g.z, g.w, cl.x, dx, dy);
+        const float alpha = fminf(kAlphaMax, eval_oG(cl.y, power));
+        if (power <= 0.0f && alpha >= kAlphaMin) {
+          const float Tn = Tr * (1.0f - alpha);
+          const uint32_t pos = base + (uint32_t)e;
+          if (Tn < kTMin) {
+            done = true;
+            examined = pos;
+            m = 0ull;
+          } else {
+            const float wt = alpha * Tr;
+            c0 += cl.z * wt;
+            c1 += cl.w * wt;
+            c2 += bb * wt;
+            Tr = Tn;
+            last = pos;
+            ++blended;
+          }
         }
       }
+      wave_sync_lds();  // this chunk's reads finish before the next chunk is staged
+      cur = nxt;
     }
-    wave_sync_lds();  // this chunk's reads finish before the next chunk is staged
-    cur = nxt;
+    if (long_list)  // final state
+      st[(size_t)((len - 1u) >> shift) * (kTile * kTile)] = make_float4(Tr, c0, c1, c2);
   }
 
   if (inside) {
@@ -265,126 +381,255 @@ __global__ __launch_bounds__(kBlock) void k_blend_forward(
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Backward.  Work item = (tile, segment k): list positions [k SEG, (k+1) SEG), walked back to
+// front by each quadrant wave over its pixels.  A pixel whose last blended entry lies beyond
+// the segment starts from the forward's state at the segment's end: T there, and the colour
+// behind it, (C_final - C_boundary) / T_boundary; otherwise from T_final with nothing behind.
+// The segments of one tile are independent, so a long list is spread over many CUs.
+// Persistent workgroups take items from a counter in the workspace until none are left.
+// The waves of a workgroup add their per-entry gradient sums into one LDS window of 256
+// entries; one global atomic per entry and value then adds the window to grad2d, so a record
+// that reaches several quadrants costs one set of atomics.
+// ---------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(kBlock) void k_blend_backward(
-    int W, int H, int TX, int T, int64_t n, int64_t ld, const float4* __restrict__ splat,
+    int W, int H, int TX, int64_t n, const float4* __restrict__ splat,
     const uint32_t* __restrict__ vals, const uint2* __restrict__ ranges, float bg0, float bg1,
     float bg2, const float* __restrict__ T_final, const uint32_t* __restrict__ last_contrib,
-    const float* __restrict__ dLdI, float* __restrict__ grad2d) {
-  __shared__ Chunk stg[4];                // per quadrant wave: its current chunk
-  __shared__ float accs[4][9][kChunk];    // per quadrant wave: gradient sums of the chunk's records
-  const int tile = blockIdx.x;  // consecutive tiles land on different XCDs: balances the load
-  const int tx = tile % TX, ty = tile / TX;
+    const float* __restrict__ dLdI, float* __restrict__ grad2d, uint32_t* __restrict__ ws_hdr,
+    const uint32_t* __restrict__ bnd_off, const uint2* __restrict__ items,
+    const float4* __restrict__ slots) {
+  __shared__ Chunk stg[4];              // per quadrant wave: its current chunk
+  __shared__ float acc[9][kWin];        // the workgroup's gradient sums over a window of entries
+  __shared__ uint32_t s_item, s_mx[4];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   Chunk& S = stg[w];
-  float(&acc)[9][kChunk] = accs[w];
   const int lx = lane & 7, ly = lane >> 3;
-  const int xq = tx * kTile + (w & 1) * 8, yq = ty * kTile + (w >> 1) * 8;
-  const int px = xq + lx, py = yq + ly;
-  const bool inside = px < W && py < H;
-  const float pxc = (float)px + 0.5f, pyc = (float)py + 0.5f;
-  const uint2 rg = ranges[tile];
-  const uint32_t start = rg.x;
+  const int pix = tile_pixel(w, lx, ly);
+  const uint32_t shift = ws_hdr[0], n_items = ws_hdr[1];
 
-  float Tr = 0.f, g0 = 0.f, g1 = 0.f, g2 = 0.f, bgT = 0.f;
-  uint32_t last = 0;
-  if (inside) {
-    const int64_t p = (int64_t)py * W + px;
-    Tr = T_final[p];
-    last = last_contrib[p];
-    g0 = dLdI[3 * p];
-    g1 = dLdI[3 * p + 1];
-    g2 = dLdI[3 * p + 2];
-    bgT = Tr * (bg0 * g0 + bg1 * g1 + bg2 * g2);
-  }
-  float S0 = 0.f, S1 = 0.f, S2 = 0.f;  // colour accumulated behind the current entry, / T_{k+1}
+  for (;;) {
+    if (tid == 0) s_item = atomicAdd(ws_hdr + 3, 1u);
+    __syncthreads();
+    const uint32_t item = s_item;
+    __syncthreads();  // every wave has read s_item before it is overwritten
+    if (item >= n_items) break;
+    const uint2 it = items[item];
+    const int tile = (int)it.x;
+    const uint32_t k = it.y;
+    const int tx = tile % TX, ty = tile / TX;
+    const int xq = tx * kTile + (w & 1) * 8, yq = ty * kTile + (w >> 1) * 8;
+    const int px = xq + lx, py = yq + ly;
+    const bool inside = px < W && py < H;
+    const float pxc = (float)px + 0.5f, pyc = (float)py + 0.5f;
+    const uint2 rg = ranges[tile];
+    const uint32_t start = rg.x, len = rg.y - rg.x;
 
-  // this wave walks [start, start + its largest last_contrib), back to front
-  uint32_t mx = last;
-  for (int o = 32; o > 0; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor(mx, o, 64));
-  const uint32_t end_eff = start + min(mx, rg.y - start);
-  const uint32_t nchunks = (end_eff - start + kChunk - 1) / kChunk;
-  // chunk c covers [lo_c, hi_c) with hi_c = end_eff - 64 c
-  auto lo_of = [&](uint32_t c) -> uint32_t {
-    const uint32_t hi = end_eff - c * kChunk;
-    return hi - start > (uint32_t)kChunk ? hi - kChunk : start;
-  };
-
-  uint32_t gnext = nchunks > 0 ? load_gid(vals, lo_of(0) + lane, end_eff) : 0xFFFFFFFFu;
-  Raw cur = load_raw(splat, gnext, n);
-  gnext = nchunks > 1 ? load_gid(vals, lo_of(1) + lane, end_eff - kChunk) : 0xFFFFFFFFu;
-  for (uint32_t c = 0; c < nchunks; ++c) {
-    const uint32_t lo = lo_of(c);
-    const Raw nxt = load_raw(splat, gnext, n);  // next chunk in flight
-    gnext = c + 2 < nchunks ? load_gid(vals, lo_of(c + 2) + lane, end_eff - (c + 2) * kChunk) : 0xFFFFFFFFu;
-    put(S, lane, cur);
-#pragma unroll
-    for (int k = 0; k < 9; ++k) acc[k][lane] = 0.f;
-    const Box bx = alpha_box(cur.uv.x, cur.uv.y, cur.abco.x, cur.abco.y, cur.abco.z, cur.abco.w, xq, yq);
-    unsigned long long m = lane_mask(bx, lx, ly);  // all lanes take part in the ballots
-    const unsigned long long touched = __ballot(bx.x0 <= bx.x1 && bx.y0 <= bx.y1);
-    wave_sync_lds();
-    const uint32_t base = lo - start;  // 0-based position of slot 0
-    while (m) {  // this lane's records, back to front
-      const int e = highest_bit(m);
-      m &= ~(1ull << e);
-      const uint32_t pos = base + (uint32_t)e;
-      if (pos >= last) continue;  // behind the pixel's last blended entry
-      const float4 g = S.geo[e];
-      const float4 cl = S.col[e];
-      const float cb = S.b[e];
-      const float dx = pxc - g.x, dy = pyc - g.y;
-      const float power = eval_power(g.z, g.w, cl.x, dx, dy);
-      const float G = __expf(power);
-      const float oG = __fmul_rn(cl.y, G);  // the same operations as eval_oG
-      const float alpha = fminf(kAlphaMax, oG);
-      if (!(power <= 0.0f && alpha >= kAlphaMin)) continue;
-      const float om = 1.0f - alpha;
-      const float rom = __builtin_amdgcn_rcpf(om);  // om >= 0.01
-      const float Tk = Tr * rom;                    // transmittance in front of this entry
-      const float wt = alpha * Tk;
-      const float cr = cl.z, cg = cl.w;
-      const float dL_dalpha = Tk * ((cr - S0) * g0 + (cg - S1) * g1 + (cb - S2) * g2) - bgT * rom;
-      S0 = alpha * cr + om * S0;
-      S1 = alpha * cg + om * S1;
-      S2 = alpha * cb + om * S2;
-      Tr = Tk;
-      atomicAdd(&acc[6][e], wt * g0);
-      atomicAdd(&acc[7][e], wt * g1);
-      atomicAdd(&acc[8][e], wt * g2);
-      if (oG <= kAlphaMax) {  // unclamped: alpha = o G depends on o and power
-        const float dpow = oG * dL_dalpha;
-        atomicAdd(&acc[0][e], -(2.0f * g.z * dx + g.w * dy) * dpow);  // A = -2 nA, B = -nB
-        atomicAdd(&acc[1][e], -(g.w * dx + 2.0f * cl.x * dy) * dpow);  // C = -2 nC
-        atomicAdd(&acc[2][e], -0.5f * dx * dx * dpow);
-        atomicAdd(&acc[3][e], -dx * dy * dpow);
-        atomicAdd(&acc[4][e], -0.5f * dy * dy * dpow);
-        atomicAdd(&acc[5][e], G * dL_dalpha);
-      }
+    float Tr = 0.f, g0 = 0.f, g1 = 0.f, g2 = 0.f, bgT = 0.f;
+    float S0 = 0.f, S1 = 0.f, S2 = 0.f;  // colour accumulated behind the current entry, / T_{k+1}
+    uint32_t last = 0;
+    if (inside) {
+      const int64_t p = (int64_t)py * W + px;
+      Tr = T_final[p];
+      last = last_contrib[p];
+      g0 = dLdI[3 * p];
+      g1 = dLdI[3 * p + 1];
+      g2 = dLdI[3 * p + 2];
+      bgT = Tr * (bg0 * g0 + bg1 * g1 + bg2 * g2);
     }
-    wave_sync_lds();
-    if (((touched >> lane) & 1ull) && (int64_t)cur.gid < n) {
-#pragma unroll
-      for (int k = 0; k < 9; ++k) {
-        const float x = acc[k][lane];
-        if (x != 0.f) unsafeAtomicAdd(grad2d + (int64_t)k * ld + cur.gid, x);
-      }
+    uint32_t mx = last;  // the wave's largest last_contrib
+    for (int o = 32; o > 0; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor(mx, o, 64));
+    if (lane == 0) s_mx[w] = mx;
+    __syncthreads();
+    const uint32_t mxb = max(max(s_mx[0], s_mx[1]), max(s_mx[2], s_mx[3]));
+    const uint32_t seg_lo = k << shift;
+    const uint32_t seg_end = seg_lo + (1u << shift);
+    const uint32_t hi_w = min(seg_end, min(mx, len));   // this wave walks [seg_lo, hi_w)
+    const uint32_t hi_b = min(seg_end, min(mxb, len));  // the workgroup walks [seg_lo, hi_b)
+    if (seg_lo >= hi_b) continue;  // workgroup-uniform: the segment lies behind every pixel's walk
+    if (last > seg_end) {  // the pixel's walk starts behind this segment
+      const float4* st = slots + (size_t)bnd_off[tile] * (kTile * kTile) + pix;
+      const float4 sb = st[(size_t)k * (kTile * kTile)];
+      const float4 sf = st[(size_t)((len - 1u) >> shift) * (kTile * kTile)];
+      const float inv = 1.0f / sb.x;  // T >= 1e-4 at every boundary
+      Tr = sb.x;
+      S0 = (sf.y - sb.y) * inv;
+      S1 = (sf.z - sb.z) * inv;
+      S2 = (sf.w - sb.w) * inv;
     }
-    wave_sync_lds();  // the flush has read acc before the next chunk clears it
-    cur = nxt;
+
+    // windows of kWin entries, top down; the waves walk a window independently, then the
+    // workgroup adds the window's sums to grad2d
+    for (uint32_t wtop = hi_b; wtop > seg_lo;) {
+      const uint32_t wlo = seg_lo + ((wtop - 1u - seg_lo) & ~(uint32_t)(kWin - 1));
+#pragma unroll
+      for (int q = 0; q < 9; ++q) acc[q][tid] = 0.f;
+      __syncthreads();
+      const uint32_t whi = min(wtop, hi_w);
+      if (whi > wlo) {  // wave-uniform
+        const uint32_t lo_abs = start + wlo, hi_abs = start + whi;
+        const uint32_t nchunks = (whi - wlo + kChunk - 1) / kChunk;
+        // chunk c covers [lo_c, hi_abs - 64 c) with lo_c = max(hi_abs - 64 (c+1), lo_abs)
+        auto lo_of = [&](uint32_t c) -> uint32_t {
+          const uint32_t hi = hi_abs - c * kChunk;
+          return hi - lo_abs > (uint32_t)kChunk ? hi - kChunk : lo_abs;
+        };
+        // positions for chunk c (>= nchunks: none), clamped into [lo_abs, hi_abs)
+        auto gid_of = [&](uint32_t c) -> uint32_t {
+          const bool real = c < nchunks;
+          const uint32_t lo = real ? lo_of(c) : lo_abs;
+          const uint32_t hi = real ? hi_abs - c * kChunk : lo_abs;
+          return load_gid(vals, lo + lane, hi, lo_abs);
+        };
+        uint32_t gnext = gid_of(0);
+        Raw cur = load_raw(splat, gnext, n);
+        gnext = gid_of(1);
+        for (uint32_t c = 0; c < nchunks; ++c) {
+          const uint32_t lo = lo_of(c);
+          const Raw nxt = load_raw(splat, gnext, n);  // next chunk in flight
+          gnext = gid_of(c + 2);
+          put(S, lane, cur);
+          const Box bx = alpha_box(cur.uv.x, cur.uv.y, cur.abco.x, cur.abco.y, cur.abco.z, opacity_of(cur, n), xq, yq);
+          unsigned long long rem;  // records whose box meets this lane's pixel row
+          const unsigned long long m = lane_mask(bx, lx, ly, &rem);  // all lanes take part in the ballots
+          wave_sync_lds();
+          const uint32_t base = lo - start;  // 0-based list position of slot 0
+          const uint32_t wbase = lo - lo_abs;  // window position of slot 0
+          // Each pixel row of the quadrant (8 lanes) takes the records reaching it back to
+          // front, its lanes on the same record; a lane takes part when the record's box holds
+          // its pixel and the record lies before its last blended entry.  The row's nine sums
+          // are formed in registers and added to the window's sums by one lane of the row.
+          for (;;) {
+            const bool has = rem != 0ull;
+            if (__ballot(has) == 0ull) break;
+            const int e = has ? highest_bit(rem) : 0;
+            rem &= ~(1ull << e);
+            const float4 g = S.geo[e];  // one address per row: a broadcast within the row
+            const float4 cl = S.col[e];
+            const float cb = S.b[e];
+            const float dx = pxc - g.x, dy = pyc - g.y;
+            const float power = eval_power(g.z, g.w, cl.x, dx, dy);
+            const float G = __expf(power);
+            const float oG = __fmul_rn(cl.y, G);  // the same operations as eval_oG
+            const float alpha = fminf(kAlphaMax, oG);
+            const bool act = has && ((m >> e) & 1ull) && base + (uint32_t)e < last && power <= 0.0f &&
+                             alpha >= kAlphaMin;
+            const unsigned long long acts = __ballot(act);
+            if (acts == 0ull) continue;
+            const float om = 1.0f - alpha;
+            const float rom = __builtin_amdgcn_rcpf(om);  // om >= 0.01
+            const float Tk = Tr * rom;                    // transmittance in front of this entry
+            const float wt = alpha * Tk;
+            const float cr = cl.z, cg = cl.w;
+            const float dL_dalpha = Tk * ((cr - S0) * g0 + (cg - S1) * g1 + (cb - S2) * g2) - bgT * rom;
+            const bool unclamped = act && oG <= kAlphaMax;  // alpha = o G depends on o and power
+            const float dpow = unclamped ? oG * dL_dalpha : 0.0f;
+            float v[9];
+            v[0] = -(2.0f * g.z * dx + g.w * dy) * dpow;  // A = -2 nA, B = -nB
+            v[1] = -(g.w * dx + 2.0f * cl.x * dy) * dpow;  // C = -2 nC
+            v[2] = -0.5f * dx * dx * dpow;
+            v[3] = -dx * dy * dpow;
+            v[4] = -0.5f * dy * dy * dpow;
+            v[5] = unclamped ? G * dL_dalpha : 0.0f;
+            v[6] = act ? wt * g0 : 0.0f;
+            v[7] = act ? wt * g1 : 0.0f;
+            v[8] = act ? wt * g2 : 0.0f;
+            if (act) {
+              S0 = alpha * cr + om * S0;
+              S1 = alpha * cg + om * S1;
+              S2 = alpha * cb + om * S2;
+              Tr = Tk;
+            }
+            row8_sum<9>(v);  // every lane of a pixel row holds the row's sums
+            if (lx == 0 && ((acts >> (ly * 8)) & 0xFFull)) {
+              const uint32_t ws = wbase + (uint32_t)e;
+#pragma unroll
+              for (int q = 0; q < 9; ++q) atomicAdd(&acc[q][ws], v[q]);
+            }
+          }
+          wave_sync_lds();  // this chunk's reads finish before the next chunk is staged
+          cur = nxt;
+        }
+      }
+      __syncthreads();
+      // one thread per entry of the window: nine global atomics for each entry with sums
+      if (wlo + (uint32_t)tid < wtop) {
+        float x[9];
+        bool any = false;
+#pragma unroll
+        for (int q = 0; q < 9; ++q) {
+          x[q] = acc[q][tid];
+          any = any || x[q] != 0.f;
+        }
+        if (any) {
+          const uint32_t gid = vals[start + wlo + tid];
+#pragma unroll
+          for (int q = 0; q < 9; ++q)
+            if (x[q] != 0.f) unsafeAtomicAdd(grad2d + 9 * (int64_t)gid + q, x[q]);
+        }
+      }
+      __syncthreads();  // the window's sums are read before the next window clears them
+      wtop = wlo;
+    }
   }
 }
 
+int cu_count() {
+  static int cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] <= 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cached[dev] = v;
+  }
+  return cached[dev];
+}
+
+size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// sizes of the fixed part of the render workspace for T tiles (slots excluded)
+size_t ws_fixed_bytes(int T) { return 256 + round256(4 * (size_t)(T + 1)) + round256(8 * (size_t)T) + 256; }
+constexpr size_t kSlotBytes = sizeof(float4) * kTile * kTile;
+
 }  // namespace
+
+size_t render_ws_bytes(int T, int64_t k_capacity) {
+  const int64_t kc = k_capacity > 0 ? k_capacity : 0;
+  const size_t slots = (size_t)T + (size_t)((kc + (1 << kSegShiftMin) - 1) >> kSegShiftMin);
+  return ws_fixed_bytes(T) + slots * (kSlotBytes + sizeof(uint2));
+}
+
+bool render_ws_layout(void* ws, size_t bytes, int T, RenderWs* out) {
+  const size_t fixed = ws_fixed_bytes(T);
+  if (!ws || bytes < fixed || (reinterpret_cast<uintptr_t>(ws) & 255u)) return false;
+  const size_t cap = (bytes - fixed) / (kSlotBytes + sizeof(uint2));
+  if (cap > 0x7FFFFFFFull) return false;
+  char* b = static_cast<char*>(ws);
+  out->hdr = reinterpret_cast<uint32_t*>(b);
+  b += 256;
+  out->bnd_off = reinterpret_cast<uint32_t*>(b);
+  b += round256(4 * (size_t)(T + 1));
+  out->items = reinterpret_cast<uint2*>(b);  // T + cap items at most
+  b += round256(8 * ((size_t)T + cap));
+  out->slots = reinterpret_cast<float4*>(b);
+  out->slots_cap = (uint32_t)cap;
+  return true;
+}
 
 hipError_t launch_blend_forward(const CamK& cam, int64_t n, const gs_splat* splat, const uint32_t* vals,
                                 const uint32_t* ranges, float bg0, float bg1, float bg2,
                                 float* image, float* T_final, uint32_t* last_contrib,
-                                uint32_t* n_examined, uint64_t* blend_count, hipStream_t s) {
+                                uint32_t* n_examined, uint64_t* blend_count, const RenderWs& ws,
+                                hipStream_t s) {
   const int T = cam.TX * cam.TY;
+  const uint2* rg = reinterpret_cast<const uint2*>(ranges);
+  hipLaunchKernelGGL(k_seg_plan, dim3(1), dim3(kPlanThreads), 0, s, rg, T, ws.slots_cap, ws.hdr, ws.bnd_off,
+                     ws.items);
   hipLaunchKernelGGL(k_blend_forward, dim3(T), dim3(kBlock), 0, s, cam.W, cam.H, cam.TX, T, n,
-                     reinterpret_cast<const float4*>(splat), vals, reinterpret_cast<const uint2*>(ranges),
-                     bg0, bg1, bg2, image, T_final, last_contrib, n_examined,
-                     reinterpret_cast<unsigned long long*>(blend_count));
+                     reinterpret_cast<const float4*>(splat), vals, rg, bg0, bg1, bg2, image, T_final,
+                     last_contrib, n_examined, reinterpret_cast<unsigned long long*>(blend_count),
+                     (const uint32_t*)ws.hdr, (const uint32_t*)ws.bnd_off, ws.slots);
   return hipGetLastError();
 }
 
@@ -392,11 +637,17 @@ hipError_t launch_blend_backward(const CamK& cam, int64_t n, int64_t ld, const g
                                  const uint32_t* vals, const uint32_t* ranges, float bg0,
                                  float bg1, float bg2, const float* T_final,
                                  const uint32_t* last_contrib, const float* dLdI, float* grad2d,
-                                 hipStream_t s) {
+                                 const RenderWs& ws, hipStream_t s) {
   const int T = cam.TX * cam.TY;
-  hipLaunchKernelGGL(k_blend_backward, dim3(T), dim3(kBlock), 0, s, cam.W, cam.H, cam.TX, T, n, ld,
+  hipError_t e = launch_fill_u32(ws.hdr + 3, 1, 0u, s);  // work-item counter
+  if (e != hipSuccess) return e;
+  // enough persistent workgroups to fill every CU; never more than the items can be
+  const int64_t most = (int64_t)T + ws.slots_cap;
+  const unsigned grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>(most, (int64_t)cu_count() * 8));
+  hipLaunchKernelGGL(k_blend_backward, dim3(grid), dim3(kBlock), 0, s, cam.W, cam.H, cam.TX, n,
                      reinterpret_cast<const float4*>(splat), vals, reinterpret_cast<const uint2*>(ranges),
-                     bg0, bg1, bg2, T_final, last_contrib, dLdI, grad2d);
+                     bg0, bg1, bg2, T_final, last_contrib, dLdI, grad2d, ws.hdr, (const uint32_t*)ws.bnd_off,
+                     (const uint2*)ws.items, (const float4*)ws.slots);
   return hipGetLastError();
 }
 

@@ -174,20 +174,31 @@ int gs_bin_and_sort(const gs_scene* scene, const gs_camera* cam, gs_proj proj, v
   return e == hipSuccess ? ok() : hip_fail(e, "gs_bin_and_sort");
 }
 
+int gs_render_workspace(int32_t width, int32_t height, int64_t k_capacity, size_t* bytes) {
+  if (!bytes || width <= 0 || height <= 0 || k_capacity < 0)
+    return fail(GS_ERR_INVALID_ARGUMENT, "invalid arguments");
+  const int T = ((width + GS_TILE - 1) / GS_TILE) * ((height + GS_TILE - 1) / GS_TILE);
+  *bytes = render_ws_bytes(T, k_capacity);
+  return ok();
+}
+
 int gs_render_forward(const gs_camera* cam, int64_t n, const gs_splat* splat, const uint32_t* vals,
                       const uint32_t* ranges, const float* bg, float* image, float* T_final,
                       uint32_t* last_contrib, uint32_t* n_examined, uint64_t* blend_count,
-                      hipStream_t stream) {
+                      void* render_ws, size_t render_ws_bytes, hipStream_t stream) {
   int st;
   if ((st = check_camera(cam))) return st;
   if (n < 0) return fail(GS_ERR_INVALID_ARGUMENT, "n < 0");
-  if ((!splat && n > 0) || !vals || !ranges || !bg || !image || !T_final || !last_contrib)
+  if ((!splat && n > 0) || !vals || !ranges || !bg || !image || !T_final || !last_contrib || !render_ws)
     return fail(GS_ERR_INVALID_ARGUMENT, "a required pointer is null");
+  RenderWs ws;
+  if (!render_ws_layout(render_ws, render_ws_bytes, (int)n_tiles(*cam), &ws))
+    return fail(GS_ERR_INVALID_ARGUMENT, "render workspace too small or not 256-byte aligned");
   if (!aligned16(splat)) return fail(GS_ERR_INVALID_ARGUMENT, "splat must be 16-byte aligned");
   if (reinterpret_cast<uintptr_t>(ranges) & 7u) return fail(GS_ERR_INVALID_ARGUMENT, "ranges must be 8-byte aligned");
   if (!(finite(bg[0]) && finite(bg[1]) && finite(bg[2]))) return fail(GS_ERR_INVALID_ARGUMENT, "bg not finite");
   const hipError_t e = launch_blend_forward(make_cam(*cam), n, splat, vals, ranges, bg[0], bg[1], bg[2], image,
-                                            T_final, last_contrib, n_examined, blend_count, stream);
+                                            T_final, last_contrib, n_examined, blend_count, ws, stream);
   return e == hipSuccess ? ok() : hip_fail(e, "gs_render_forward");
 }
 
@@ -242,13 +253,17 @@ int gs_preprocess_backward(const gs_scene* scene, float* params, const gs_camera
 int gs_render_backward(const gs_scene* scene, float* params, const gs_camera* cam, gs_proj proj,
                        const uint32_t* vals, const uint32_t* ranges, const float* bg,
                        const float* T_final, const uint32_t* last_contrib, const float* dL_dimage,
-                       float* grad2d, float* grads, const gs_adam* adam, hipStream_t stream) {
+                       float* grad2d, float* grads, const gs_adam* adam, void* render_ws,
+                       size_t render_ws_bytes, hipStream_t stream) {
   int st;
   if ((st = check_scene(scene)) || (st = check_camera(cam)) || (st = check_proj(proj, false, scene->n)) ||
       (st = check_adam(adam)))
     return st;
-  if (!vals || !ranges || !bg || !T_final || !last_contrib || !dL_dimage)
+  if (!vals || !ranges || !bg || !T_final || !last_contrib || !dL_dimage || !render_ws)
     return fail(GS_ERR_INVALID_ARGUMENT, "a required pointer is null");
+  RenderWs ws;
+  if (!render_ws_layout(render_ws, render_ws_bytes, (int)n_tiles(*cam), &ws))
+    return fail(GS_ERR_INVALID_ARGUMENT, "render workspace too small or not 256-byte aligned");
   if (scene->n > 0 && !grad2d) return fail(GS_ERR_INVALID_ARGUMENT, "grad2d is null");
   if (scene->n > 0 && (grads || adam) && !params) return fail(GS_ERR_INVALID_ARGUMENT, "params is null");
   if (reinterpret_cast<uintptr_t>(ranges) & 7u) return fail(GS_ERR_INVALID_ARGUMENT, "ranges must be 8-byte aligned");
@@ -257,7 +272,7 @@ int gs_render_backward(const gs_scene* scene, float* params, const gs_camera* ca
   hipError_t e = launch_fill_f32(grad2d, 9 * scene->ld, 0.f, stream);
   if (e == hipSuccess)
     e = launch_blend_backward(ck, scene->n, scene->ld, proj.splat, vals, ranges, bg[0], bg[1], bg[2], T_final,
-                              last_contrib, dL_dimage, grad2d, stream);
+                              last_contrib, dL_dimage, grad2d, ws, stream);
   if (e != hipSuccess) return hip_fail(e, "gs_render_backward (blend)");
   if (!grads && !adam) return ok();  // backward blend only
   return gs_preprocess_backward(scene, params, cam, grad2d, grads, adam, stream);

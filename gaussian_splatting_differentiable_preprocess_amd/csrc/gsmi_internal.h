@@ -84,15 +84,37 @@ hipError_t launch_bin_sort_rest(int64_t n, int64_t K, const BinInfo& info, const
                                 uint32_t* ranges, uint64_t* keys, hipStream_t s);
 
 // blending
+//
+// Render workspace: what the forward leaves for the backward so that long tile lists can be
+// walked back in parallel segments.  A tile list longer than one segment (kSegMin entries, or
+// a larger power of two when the workspace is short) gets one state slot per segment boundary
+// plus one for its final state; a slot holds (T, C_r, C_g, C_b) for the tile's 256 pixels.
+//   hdr[0] = log2 segment length, hdr[1] = number of backward work items, hdr[2] = slots used,
+//   hdr[3] = work-item counter of the backward
+//   bnd_off[T + 1]  first slot of each tile
+//   items[]         (tile, segment) work items of the backward, tile-major
+//   slots[][256]    float4 states
+constexpr int kSegShiftMin = 8;  // 256 list entries per segment
+struct RenderWs {
+  uint32_t* hdr;
+  uint32_t* bnd_off;
+  uint2* items;
+  float4* slots;
+  uint32_t slots_cap;
+};
+size_t render_ws_bytes(int T, int64_t k_capacity);
+bool render_ws_layout(void* ws, size_t bytes, int T, RenderWs* out);
+
 hipError_t launch_blend_forward(const CamK& cam, int64_t n, const gs_splat* splat, const uint32_t* vals,
                                 const uint32_t* ranges, float bg0, float bg1, float bg2,
                                 float* image, float* T_final, uint32_t* last_contrib,
-                                uint32_t* n_examined, uint64_t* blend_count, hipStream_t s);
+                                uint32_t* n_examined, uint64_t* blend_count, const RenderWs& ws,
+                                hipStream_t s);
 hipError_t launch_blend_backward(const CamK& cam, int64_t n, int64_t ld, const gs_splat* splat,
                                  const uint32_t* vals, const uint32_t* ranges, float bg0,
                                  float bg1, float bg2, const float* T_final,
                                  const uint32_t* last_contrib, const float* dLdI, float* grad2d,
-                                 hipStream_t s);
+                                 const RenderWs& ws, hipStream_t s);
 
 // elementwise
 hipError_t launch_fill_u32(uint32_t* p, int64_t count, uint32_t value, hipStream_t s);

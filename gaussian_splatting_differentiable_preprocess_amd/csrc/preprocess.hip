@@ -284,10 +284,11 @@ __global__ __launch_bounds__(kBlock) void k_preprocess_backward(PrebwdArgs A, Ca
     for (int ch = 0; ch < 3; ++ch) f[k][ch] = prm[(11 + 3 * k + ch) * ld + i];
 
   if (P.vis) {
-    const float gu = A.grad2d[0 * ld + i], gv = A.grad2d[1 * ld + i];
-    const float gA = A.grad2d[2 * ld + i], gB = A.grad2d[3 * ld + i], gC = A.grad2d[4 * ld + i];
-    const float go = A.grad2d[5 * ld + i];
-    const float gr[3] = {A.grad2d[6 * ld + i], A.grad2d[7 * ld + i], A.grad2d[8 * ld + i]};
+    const float* g2 = A.grad2d + 9 * i;  // this Gaussian's nine values, contiguous
+    const float gu = g2[0], gv = g2[1];
+    const float gA = g2[2], gB = g2[3], gC = g2[4];
+    const float go = g2[5];
+    const float gr[3] = {g2[6], g2[7], g2[8]};
 
     // ---- colour: raw = 0.5 + sum_k Y_k f_k, rgb = max(raw, 0) -------------------------
     const float dv0 = mu[0] - c.pos[0], dv1 = mu[1] - c.pos[1], dv2 = mu[2] - c.pos[2];

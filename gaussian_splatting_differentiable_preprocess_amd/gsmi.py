@@ -23,7 +23,7 @@ SPLAT_FLOATS = 12  # 48-byte record: u, v, radius_x, radius_y | A, B, C, opacity
 
 EXPORTS = (
     "gs_version", "gs_last_error", "gs_preprocess", "gs_bin_and_sort_workspace", "gs_bin_and_sort",
-    "gs_render_forward", "gs_loss_l1_workspace", "gs_loss_l1", "gs_render_backward",
+    "gs_render_workspace", "gs_render_forward", "gs_loss_l1_workspace", "gs_loss_l1", "gs_render_backward",
     "gs_preprocess_backward", "gs_adam_step",
 )
 
@@ -79,11 +79,12 @@ def load(path: str = LIB_PATH):
     L.gs_preprocess.argtypes = [SP, P, CP, GsProj, P]
     L.gs_bin_and_sort_workspace.argtypes = [i64, i64, i32, i32, ctypes.POINTER(sz)]
     L.gs_bin_and_sort.argtypes = [SP, CP, GsProj, P, sz, i64, P, P, P, ctypes.POINTER(i64), P]
-    L.gs_render_forward.argtypes = [CP, i64, P, P, P, ctypes.POINTER(ctypes.c_float), P, P, P, P, P, P]
+    L.gs_render_workspace.argtypes = [i32, i32, i64, ctypes.POINTER(sz)]
+    L.gs_render_forward.argtypes = [CP, i64, P, P, P, ctypes.POINTER(ctypes.c_float), P, P, P, P, P, P, sz, P]
     L.gs_loss_l1_workspace.argtypes = [i64, ctypes.POINTER(sz)]
     L.gs_loss_l1.argtypes = [i64, P, P, P, P, P, sz, P]
     L.gs_render_backward.argtypes = [SP, P, CP, GsProj, P, P, ctypes.POINTER(ctypes.c_float), P, P, P,
-                                     P, P, AP, P]
+                                     P, P, AP, P, sz, P]
     L.gs_preprocess_backward.argtypes = [SP, P, CP, P, P, AP, P]
     L.gs_adam_step.argtypes = [i64, P, P, AP, P]
     for name in EXPORTS:
@@ -190,13 +191,23 @@ def _bg(bg):
     return arr
 
 
-def render_forward(cam: GsCamera, n, splat, vals, ranges, bg, image, T_final, last_contrib,
+def render_workspace(width, height, k_capacity) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load().gs_render_workspace(int(width), int(height), int(k_capacity), ctypes.byref(out)))
+    return out.value
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def render_forward(cam: GsCamera, n, splat, vals, ranges, bg, image, T_final, last_contrib, render_ws,
                    n_examined=None, blend_count=None, stream=None):
     if blend_count is not None and (blend_count.numel() < 3 or blend_count.element_size() != 8):
         raise ValueError("blend_count must be a device int64 tensor of at least 3 elements")
     _check(load().gs_render_forward(ctypes.byref(cam), int(n), _ptr(splat), _ptr(vals), _ptr(ranges), _bg(bg),
                                     _ptr(image), _ptr(T_final), _ptr(last_contrib), _ptr(n_examined),
-                                    _ptr(blend_count), _stream(stream)))
+                                    _ptr(blend_count), _ptr(render_ws), _nbytes(render_ws), _stream(stream)))
 
 
 def loss_l1_workspace(count) -> int:
@@ -215,11 +226,12 @@ def make_adam(m, v, step, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8) -> GsAdam:
 
 
 def render_backward(scene: GsScene, params, cam: GsCamera, proj: Proj, vals, ranges, bg, T_final,
-                    last_contrib, dL_dimage, grad2d, grads=None, adam: GsAdam | None = None, stream=None):
+                    last_contrib, dL_dimage, grad2d, render_ws, grads=None, adam: GsAdam | None = None,
+                    stream=None):
     _check(load().gs_render_backward(ctypes.byref(scene), _ptr(params), ctypes.byref(cam), proj.c(), _ptr(vals),
                                      _ptr(ranges), _bg(bg), _ptr(T_final), _ptr(last_contrib), _ptr(dL_dimage),
                                      _ptr(grad2d), _ptr(grads), ctypes.byref(adam) if adam is not None else None,
-                                     _stream(stream)))
+                                     _ptr(render_ws), _nbytes(render_ws), _stream(stream)))
 
 
 def preprocess_backward(scene: GsScene, params, cam: GsCamera, grad2d, grads=None, adam: GsAdam | None = None,
@@ -253,13 +265,15 @@ class StepBuffers:
         self.ranges = torch.empty((self.T, 2), dtype=i32, device=device)
         self.ws = torch.empty(bin_and_sort_workspace(n, self.k_capacity, width, height), dtype=torch.uint8,
                               device=device)
+        self.render_ws = torch.empty(render_workspace(width, height, self.k_capacity), dtype=torch.uint8,
+                                     device=device)
         self.image = torch.empty((height, width, 3), dtype=f32, device=device)
         self.T_final = torch.empty((height, width), dtype=f32, device=device)
         self.last = torch.empty((height, width), dtype=i32, device=device)
         self.dLdI = torch.empty((height, width, 3), dtype=f32, device=device)
         self.loss = torch.zeros(1, dtype=f32, device=device)
         self.loss_ws = torch.empty(loss_l1_workspace(3 * width * height), dtype=torch.uint8, device=device)
-        self.grad2d = torch.empty((9, ld), dtype=f32, device=device)
+        self.grad2d = torch.empty((ld, 9), dtype=f32, device=device)
         self.scene = make_scene(n, ld, sh_degree)
 
     def grow(self, k_capacity, device="cuda"):
@@ -268,6 +282,8 @@ class StepBuffers:
         self.vals = torch.empty(max(1, self.k_capacity), dtype=torch.int32, device=device)
         self.ws = torch.empty(bin_and_sort_workspace(self.n, self.k_capacity, self.W, self.H), dtype=torch.uint8,
                               device=device)
+        self.render_ws = torch.empty(render_workspace(self.W, self.H, self.k_capacity), dtype=torch.uint8,
+                                     device=device)
 
 
 def train_step(buf: StepBuffers, params, m, v, step, cam: GsCamera, target=None, upstream=None,
@@ -282,7 +298,7 @@ def train_step(buf: StepBuffers, params, m, v, step, cam: GsCamera, target=None,
         except GsCapacityError as e:
             buf.grow(int(e.required * 1.25) + 1024)
     render_forward(cam, buf.n, buf.proj.splat, buf.vals, buf.ranges, bg, buf.image, buf.T_final, buf.last,
-                   blend_count=blend_count)
+                   buf.render_ws, blend_count=blend_count)
     if upstream is not None:
         dLdI = upstream
     else:
@@ -291,9 +307,9 @@ def train_step(buf: StepBuffers, params, m, v, step, cam: GsCamera, target=None,
     adam = make_adam(m, v, step, lr)
     if fused_adam:
         render_backward(buf.scene, params, cam, buf.proj, buf.vals, buf.ranges, bg, buf.T_final, buf.last, dLdI,
-                        buf.grad2d, grads, adam)
+                        buf.grad2d, buf.render_ws, grads, adam)
     else:
         render_backward(buf.scene, params, cam, buf.proj, buf.vals, buf.ranges, bg, buf.T_final, buf.last, dLdI,
-                        buf.grad2d, grads)
+                        buf.grad2d, buf.render_ws, grads)
         adam_step(buf.R * buf.ld, params, grads, adam)
     return K

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define GSMI_VERSION 1
+#define GSMI_VERSION 2
 #define GS_TILE 16 /* tiles are GS_TILE x GS_TILE pixels */
 
 typedef enum gs_status {
@@ -151,6 +151,14 @@ int gs_bin_and_sort(const gs_scene* scene, const gs_camera* cam, gs_proj proj, v
                     size_t workspace_bytes, int64_t k_capacity, uint32_t* vals, uint32_t* ranges,
                     uint64_t* keys, int64_t* k_out, hipStream_t stream);
 
+/* Bytes of the render workspace that gs_render_forward fills and gs_render_backward reads,
+ * for a width x height image and lists of up to k_capacity intersections (host-only query).
+ * It holds, for every tile list longer than one segment (256 entries, or a larger power of
+ * two if the workspace is smaller than this size), each pixel's transmittance and colour at
+ * every segment boundary and at the end of its walk, plus the backward's work list.  The
+ * backward walks the segments of a long list in parallel from these states. */
+int gs_render_workspace(int32_t width, int32_t height, int64_t k_capacity, size_t* bytes);
+
 /* Forward blend.  For each pixel, walks its tile's list front to back: power =
  * -(a dx^2 + c dy^2)/2 - b dx dy with (dx, dy) = pixel centre - (u, v); skips power > 0;
  * alpha = min(0.99, opacity e^power); skips alpha < 1/255; stops before blending an entry
@@ -164,11 +172,15 @@ int gs_bin_and_sort(const gs_scene* scene, const gs_camera* cam, gs_proj proj, v
  *                       ADDED (the caller zeroes them): [0] n_examined, [1] last_contrib
  *                       (the entries the backward pass walks), [2] the (pixel, entry)
  *                       pairs composited
+ *   render_ws           out: device workspace of render_ws_bytes >= the size
+ *                       gs_render_workspace gives for this image (256-byte aligned); a
+ *                       smaller one down to the fixed part still works, with longer
+ *                       segments.  GS_ERR_INVALID_ARGUMENT if it is below the fixed part.
  * bg is a HOST array of 3 floats.  One 256-thread workgroup per tile. */
 int gs_render_forward(const gs_camera* cam, int64_t n, const gs_splat* splat, const uint32_t* vals,
                       const uint32_t* ranges, const float* bg, float* image, float* T_final,
                       uint32_t* last_contrib, uint32_t* n_examined, uint64_t* blend_count,
-                      hipStream_t stream);
+                      void* render_ws, size_t render_ws_bytes, hipStream_t stream);
 
 /* Bytes of device workspace gs_loss_l1 needs for `count` elements (host-only query). */
 int gs_loss_l1_workspace(int64_t count, size_t* bytes);
@@ -180,7 +192,9 @@ int gs_loss_l1(int64_t count, const float* image, const float* target, float* lo
                float* dL_dimage, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Backward of the step from dL/dimage.
- *   grad2d[9][ld]  out: per-Gaussian dL/d(u, v, conic_a, conic_b, conic_c, opacity, r, g, b)
+ *   grad2d[ld][9]  out: per-Gaussian dL/d(u, v, conic_a, conic_b, conic_c, opacity, r, g, b),
+ *                  the nine values of Gaussian i contiguous at grad2d + 9 i (one or two cache
+ *                  lines take all nine accumulations of a record)
  *                  from the reverse-order backward blend (zeroed inside, then accumulated
  *                  with float atomics, so the summation order is not fixed)
  *   grads[R][ld]   out, nullable: dL/dparams by the chain rule through the preprocess
@@ -188,15 +202,18 @@ int gs_loss_l1(int64_t count, const float* image, const float* target, float* lo
  *                  update to params, adam->m and adam->v in place (params is then written)
  * With grads and adam both null only the backward blend runs (grad2d is the only output and
  * params may be null); gs_preprocess_backward then finishes the step.
- * T_final and last_contrib are the forward's outputs for the same inputs; bg is a HOST array
- * of 3 floats.  Culled Gaussians receive zero gradients. */
+ * T_final, last_contrib and render_ws are the forward's outputs for the same lists, camera and
+ * bg (render_ws unmodified since, same size); the backward only updates a work counter in
+ * it, so it may be run more than once per forward.  bg is a HOST array of 3 floats.  Culled
+ * Gaussians receive zero gradients. */
 int gs_render_backward(const gs_scene* scene, float* params, const gs_camera* cam, gs_proj proj,
                        const uint32_t* vals, const uint32_t* ranges, const float* bg,
                        const float* T_final, const uint32_t* last_contrib, const float* dL_dimage,
-                       float* grad2d, float* grads, const gs_adam* adam, hipStream_t stream);
+                       float* grad2d, float* grads, const gs_adam* adam, void* render_ws,
+                       size_t render_ws_bytes, hipStream_t stream);
 
 /* Preprocess backward alone: grads (and optionally the fused Adam update) from a given
- * grad2d[9][ld].  Same semantics as the second half of gs_render_backward. */
+ * grad2d[ld][9].  Same semantics as the second half of gs_render_backward. */
 int gs_preprocess_backward(const gs_scene* scene, float* params, const gs_camera* cam,
                            const float* grad2d, float* grads, const gs_adam* adam,
                            hipStream_t stream);

@@ -93,18 +93,22 @@ class GpuStep:
         return (K, self.keys.cpu().numpy().view(np.uint64)[:K], self.vals.cpu().numpy().view(np.uint32)[:K],
                 self.ranges.cpu().numpy().view(np.uint32))
 
-    def forward(self, bg=(0.0, 0.0, 0.0), ranges=None):
+    def forward(self, bg=(0.0, 0.0, 0.0), ranges=None, render_ws_bytes=None):
+        """render_ws_bytes: a workspace smaller than the query's (longer backward segments)."""
         torch = self.torch
         H, W = self.H, self.W
         self.bg = bg
         rg = self.ranges if ranges is None else to_t(np.asarray(ranges, np.uint32).view(np.int32))
+        nb = gsmi.render_workspace(W, H, max(1, int(self.vals.numel())))
+        self.render_ws = torch.empty(nb if render_ws_bytes is None else render_ws_bytes, dtype=torch.uint8,
+                                     device="cuda")
         self.image = torch.empty((H, W, 3), dtype=torch.float32, device="cuda")
         self.T_final = torch.empty((H, W), dtype=torch.float32, device="cuda")
         self.last = torch.empty((H, W), dtype=torch.int32, device="cuda")
         self.nex = torch.empty((H, W), dtype=torch.int32, device="cuda")
         self.bcount = torch.zeros(3, dtype=torch.int64, device="cuda")
         gsmi.render_forward(self.cam, self.n, self.proj.splat, self.vals, rg, bg, self.image, self.T_final,
-                            self.last, self.nex, self.bcount)
+                            self.last, self.render_ws, self.nex, self.bcount)
         torch.cuda.synchronize()
         return dict(image=self.image.cpu().numpy(), T_final=self.T_final.cpu().numpy(),
                     last_contrib=self.last.cpu().numpy().view(np.uint32),
@@ -126,17 +130,17 @@ class GpuStep:
 
     def backward(self, ranges=None):
         torch = self.torch
-        self.grad2d = torch.empty((9, self.ld), dtype=torch.float32, device="cuda")
+        self.grad2d = torch.empty((self.ld, 9), dtype=torch.float32, device="cuda")
         self.grads = torch.empty((self.R, self.ld), dtype=torch.float32, device="cuda")
         rg = self.ranges if ranges is None else to_t(np.asarray(ranges, np.uint32).view(np.int32))
         gsmi.render_backward(self.scene, self.params, self.cam, self.proj, self.vals, rg, self.bg, self.T_final,
-                             self.last, self.dLdI, self.grad2d, self.grads)
+                             self.last, self.dLdI, self.grad2d, self.render_ws, self.grads)
         torch.cuda.synchronize()
-        return self.grad2d.cpu().numpy(), self.grads.cpu().numpy()
+        return np.ascontiguousarray(self.grad2d.cpu().numpy().T), self.grads.cpu().numpy()  # grad2d as [9][ld]
 
     def preprocess_backward(self, grad2d):
         torch = self.torch
-        g2 = to_t(np.asarray(grad2d, np.float32))
+        g2 = to_t(np.ascontiguousarray(np.asarray(grad2d, np.float32).T))  # [9][ld] -> [ld][9]
         grads = torch.empty((self.R, self.ld), dtype=torch.float32, device="cuda")
         gsmi.preprocess_backward(self.scene, self.params, self.cam, g2, grads)
         torch.cuda.synchronize()

@@ -22,7 +22,7 @@ def test_library_exports_every_declared_symbol():
     assert len(names) == len(gsmi.EXPORTS) and set(names) == set(gsmi.EXPORTS)
     for name in names:
         assert hasattr(L, name), name
-    assert gsmi.version() == 1
+    assert gsmi.version() == 2
 
 
 def test_invalid_arguments_rejected_before_any_gpu_call():
@@ -76,3 +76,31 @@ def test_workspace_queries():
     assert gsmi.loss_l1_workspace(3 * 2048 * 2048) >= 4 * (3 * 2048 * 2048) // 4096
     with pytest.raises(gsmi.GsError):
         gsmi.bin_and_sort_workspace(-1, 0, 16, 16)
+    # render workspace: a fixed part for the tiles plus one 4 KiB state slot (and one work
+    # item) per tile and per 256 intersections of capacity
+    r0 = gsmi.render_workspace(2048, 2048, 0)
+    r1 = gsmi.render_workspace(2048, 2048, 256 * 1000)
+    assert r1 - r0 == 1000 * (4096 + 8)
+    assert r0 >= 16384 * (4096 + 8 + 4)
+    with pytest.raises(gsmi.GsError):
+        gsmi.render_workspace(0, 16, 10)
+
+
+def test_render_calls_reject_a_missing_or_short_workspace():
+    L = gsmi.load()
+    cam = gsmi.GsCamera()
+    cam.fx = cam.fy = 100.0
+    cam.width = cam.height = 64
+    cam.near_plane = 0.01
+    cam.viewmat[0] = cam.viewmat[5] = cam.viewmat[10] = 1.0
+    bg = (ctypes.c_float * 3)(0, 0, 0)
+    p = ctypes.c_void_p(4096)
+    need = gsmi.render_workspace(64, 64, 0)
+    for ws, nb in ((None, need), (p, 16), (ctypes.c_void_p(4096 + 64), need)):
+        rc = L.gs_render_forward(ctypes.byref(cam), 10, p, p, p, bg, p, p, p, None, None, ws, nb, None)
+        assert rc == gsmi.GS_ERR_INVALID_ARGUMENT
+    sc = gsmi.make_scene(10, 10, 0)
+    proj = gsmi.GsProj(4096, 4096, 4096)
+    rc = L.gs_render_backward(ctypes.byref(sc), None, ctypes.byref(cam), proj, p, p, bg, p, p, p, p, None, None,
+                              p, 16, None)
+    assert rc == gsmi.GS_ERR_INVALID_ARGUMENT and "workspace" in gsmi.last_error()

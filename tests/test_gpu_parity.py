@@ -251,15 +251,15 @@ def test_fused_adam_matches_separate_adam(name):
             g.set_upstream(d["upstream"])
         m = torch.full((R, n), 0.01, dtype=torch.float32, device="cuda")
         v = torch.full((R, n), 0.02, dtype=torch.float32, device="cuda")
-        grad2d = torch.empty((9, n), dtype=torch.float32, device="cuda")
+        grad2d = torch.empty((n, 9), dtype=torch.float32, device="cuda")
         adam = gsmi.make_adam(m, v, 3, 1e-3)
         if fused:
             gsmi.render_backward(g.scene, g.params, g.cam, g.proj, g.vals, g.ranges, BG, g.T_final, g.last, g.dLdI,
-                                 grad2d, None, adam)
+                                 grad2d, g.render_ws, None, adam)
         else:
             grads = torch.empty((R, n), dtype=torch.float32, device="cuda")
             gsmi.render_backward(g.scene, g.params, g.cam, g.proj, g.vals, g.ranges, BG, g.T_final, g.last, g.dLdI,
-                                 grad2d, grads)
+                                 grad2d, g.render_ws, grads)
             gsmi.adam_step(R * n, g.params, grads, adam)
         torch.cuda.synchronize()
         outs.append((g.params.cpu().numpy(), m.cpu().numpy(), v.cpu().numpy()))
@@ -383,3 +383,44 @@ def test_repeatable_forward_and_sort():
     np.testing.assert_array_equal(a["ranges"], b["ranges"])
     for k in ("image", "T_final", "last_contrib", "n_examined"):
         np.testing.assert_array_equal(a["fwd"][k], b["fwd"][k])
+
+
+def test_backward_segments_on_deep_lists():
+    """Tile lists of ~3000 entries with low opacity: pixels walk back across several 256-entry
+    segments, which the backward runs in parallel from the forward's boundary states.  Checked
+    against the oracle and against the same backward with a workspace too small for segments."""
+    import torch
+    say("[parity] test_backward_segments_on_deep_lists")
+    n, W = 3000, 32
+    params = inputs.small_scene(31, n, 0, logscale_mean=-1.5, logscale_std=0.2, radius=0.1)
+    params[10] = -5.0  # opacity ~0.0067: about 1500 blends before T reaches 1e-4
+    cam = inputs.lookat_camera((3.0, 0.0, 0.0), W, W)
+    up = np.random.default_rng(5).uniform(-1, 1, (W, W, 3)).astype(np.float32)
+    g = GpuStep(params, 0, cam, W, W)
+    g.preprocess()
+    K, _, vals, rg = g.bin_and_sort()
+    lens = rg.reshape(-1, 2)[:, 1].astype(np.int64) - rg.reshape(-1, 2)[:, 0]
+    fwd = g.forward(BG)
+    assert lens.max() > 8 * 256 and fwd["last_contrib"].max() > 4 * 256, (lens.max(), fwd["last_contrib"].max())
+    g.set_upstream(up)
+    g2_seg, _ = g.backward()
+    hdr = g.render_ws[:16].cpu().numpy().view(np.uint32)
+    assert hdr[0] == 8 and hdr[1] > 8, hdr[:4]  # 256-entry segments, several items per long tile
+    gproj, _ = proj_from_splat(g.proj.splat.cpu().numpy()[:n])
+    o = oracle.render_forward(gproj, vals, rg.reshape(-1, 2), W, W, BG, margins=FWD_MARGINS)
+    ok = ~o["borderline"]
+    assert np.abs(fwd["image"] - o["image"]).max(axis=-1)[ok].max() <= IMG_MAX_ABS
+    o_g2 = oracle.render_backward(gproj, vals, rg.reshape(-1, 2), W, W, up.astype(np.float64), BG)
+    for r in range(9):
+        assert rel_l2(g2_seg[r, :n], o_g2[r]) <= GRAD_REL_L2, (r, rel_l2(g2_seg[r, :n], o_g2[r]))
+    # the same lists with the fixed part of the workspace only: one segment per tile
+    g.forward(BG, render_ws_bytes=gsmi.render_workspace(W, W, 0))
+    g2_one, _ = g.backward()
+    hdr = g.render_ws[:16].cpu().numpy().view(np.uint32)
+    assert hdr[0] >= 12 and hdr[2] == 0, hdr[:4]
+    for r in range(9):
+        assert rel_l2(g2_seg[r], g2_one[r]) <= GRAD_REL_L2, (r, rel_l2(g2_seg[r], g2_one[r]))
+    say(f"[parity]   deep lists: K={K}, max list {lens.max()}, max last {fwd['last_contrib'].max()}, "
+        f"segmented vs oracle rel-L2 max {max(rel_l2(g2_seg[r, :n], o_g2[r]) for r in range(9)):.2e}, "
+        f"segmented vs one segment {max(rel_l2(g2_seg[r], g2_one[r]) for r in range(9)):.2e}")
+    torch.cuda.synchronize()
