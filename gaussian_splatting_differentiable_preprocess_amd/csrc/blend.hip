@@ -393,12 +393,13 @@ __global__ __launch_bounds__(kBlock) void k_blend_forward(
 // that reaches several quadrants costs one set of atomics.
 // ---------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(kBlock) void k_blend_backward(
-    int W, int H, int TX, int64_t n, const float4* __restrict__ splat,
+    int W, int H, int TX, int TY, int64_t n, const float4* __restrict__ splat,
     const uint32_t* __restrict__ vals, const uint2* __restrict__ ranges, float bg0, float bg1,
     float bg2, const float* __restrict__ T_final, const uint32_t* __restrict__ last_contrib,
-    const float* __restrict__ dLdI, float* __restrict__ grad2d, uint32_t* __restrict__ ws_hdr,
+    const float* __restrict__ dLdI, uint32_t* __restrict__ ws_hdr,
     const uint32_t* __restrict__ bnd_off, const uint2* __restrict__ items,
-    const float4* __restrict__ slots) {
+    const float4* __restrict__ slots, const uint32_t* __restrict__ goff,
+    const uint32_t* __restrict__ goff_blk, float* __restrict__ staging, uint64_t staging_cap) {
   __shared__ Chunk stg[4];              // per quadrant wave: its current chunk
   __shared__ float acc[9][kWin];        // the workgroup's gradient sums over a window of entries
   __shared__ uint32_t s_item, s_mx[4];
@@ -552,7 +553,8 @@ __global__ __launch_bounds__(kBlock) void k_blend_backward(
         }
       }
       __syncthreads();
-      // one thread per entry of the window: nine global atomics for each entry with sums
+      // one thread per entry of the window: the entry's sums go to its Gaussian's staging
+      // slot, the entry's place in the row-major order of the Gaussian's tile rect
       if (wlo + (uint32_t)tid < wtop) {
         float x[9];
         bool any = false;
@@ -563,15 +565,105 @@ __global__ __launch_bounds__(kBlock) void k_blend_backward(
         }
         if (any) {
           const uint32_t gid = vals[start + wlo + tid];
+          const float4 q0 = splat[3 * (int64_t)gid];  // u, v, radius_x, radius_y
+          int x0, y0, x1, y1;
+          tile_rect(q0.x, q0.y, __float_as_int(q0.z), __float_as_int(q0.w), TX, TY, x0, y0, x1, y1);
+          const uint64_t slot = (uint64_t)goff_blk[gid / kGoffBlock] + goff[gid] +
+                                (uint32_t)((ty - y0) * (x1 - x0) + (tx - x0));
+          if (slot < staging_cap) {
+            float* o = staging + 9 * slot;
 #pragma unroll
-          for (int q = 0; q < 9; ++q)
-            if (x[q] != 0.f) unsafeAtomicAdd(grad2d + 9 * (int64_t)gid + q, x[q]);
+            for (int q = 0; q < 9; ++q) o[q] = x[q];
+          }
         }
       }
       __syncthreads();  // the window's sums are read before the next window clears them
       wtop = wlo;
     }
   }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Per-Gaussian staging offsets: exclusive scan of tiles_i in Gaussian order, two levels.
+// ---------------------------------------------------------------------------------------------
+constexpr int kGoffItems = kGoffBlock / kBlock;  // 16 Gaussians per thread
+
+__global__ __launch_bounds__(kBlock) void k_goff_local(int64_t n, const uint32_t* __restrict__ tiles,
+                                                       uint32_t* __restrict__ goff, uint32_t* __restrict__ blk) {
+  __shared__ uint32_t wsum[4];
+  const int64_t base = (int64_t)blockIdx.x * kGoffBlock + (int64_t)threadIdx.x * kGoffItems;
+  uint32_t t[kGoffItems];
+  uint32_t s = 0;
+#pragma unroll
+  for (int j = 0; j < kGoffItems; ++j) {
+    t[j] = base + j < n ? tiles[base + j] : 0u;
+    s += t[j];
+  }
+  // exclusive scan of the per-thread sums over the 256 threads
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  uint32_t inc = s;
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += y;
+  }
+  if (lane == 63) wsum[w] = inc;
+  __syncthreads();
+  uint32_t pre = inc - s;
+  for (int k = 0; k < w; ++k) pre += wsum[k];
+#pragma unroll
+  for (int j = 0; j < kGoffItems; ++j) {
+    if (base + j < n) goff[base + j] = pre;
+    pre += t[j];
+  }
+  if (threadIdx.x == kBlock - 1) blk[blockIdx.x] = pre;  // the block's total
+}
+
+// exclusive scan of the nblk block totals in place (one workgroup); total entries -> hdr[4]
+__global__ __launch_bounds__(kPlanThreads) void k_goff_blocks(int64_t nblk, uint32_t* __restrict__ blk,
+                                                              uint32_t* __restrict__ hdr) {
+  __shared__ uint32_t red32[kPlanThreads / 64];
+  const int64_t per = (nblk + kPlanThreads - 1) / kPlanThreads;
+  const int64_t lo = std::min<int64_t>(nblk, (int64_t)threadIdx.x * per), hi = std::min<int64_t>(nblk, lo + per);
+  uint32_t s = 0;
+  for (int64_t b = lo; b < hi; ++b) s += blk[b];
+  uint32_t run = block_exscan_1024(s, red32);
+  for (int64_t b = lo; b < hi; ++b) {
+    const uint32_t x = blk[b];
+    blk[b] = run;
+    run += x;
+  }
+  if (threadIdx.x == kPlanThreads - 1) hdr[4] = run;  // the last thread's end is the total
+}
+
+// staging[0 .. 9 * entries) = 0; entries from hdr[4], capped at the workspace's capacity
+__global__ __launch_bounds__(kBlock) void k_clear_staging(const uint32_t* __restrict__ hdr, float4* __restrict__ st,
+                                                          uint64_t cap) {
+  const uint64_t e = std::min<uint64_t>((uint64_t)hdr[4], cap);
+  const uint64_t n4 = (9 * e + 3) / 4;  // the staging region is padded to whole float4s
+  for (uint64_t j = (uint64_t)blockIdx.x * kBlock + threadIdx.x; j < n4; j += (uint64_t)gridDim.x * kBlock)
+    st[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+// grad2d[i] = sum of Gaussian i's staged entries, in the order of its tile rect
+__global__ __launch_bounds__(kBlock) void k_gather_grad2d(int64_t n, const uint32_t* __restrict__ tiles,
+                                                          const uint32_t* __restrict__ goff,
+                                                          const uint32_t* __restrict__ goff_blk,
+                                                          const float* __restrict__ staging, uint64_t cap,
+                                                          float* __restrict__ grad2d) {
+  const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (i >= n) return;
+  const uint32_t t = tiles[i];
+  const uint64_t base = (uint64_t)goff_blk[i / kGoffBlock] + goff[i];
+  float x[9] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (uint32_t j = 0; j < t; ++j) {
+    if (base + j >= cap) break;
+    const float* e = staging + 9 * (base + j);
+#pragma unroll
+    for (int q = 0; q < 9; ++q) x[q] += e[q];
+  }
+  float* o = grad2d + 9 * i;
+#pragma unroll
+  for (int q = 0; q < 9; ++q) o[q] = x[q];
 }
 
 int cu_count() {
@@ -587,33 +679,51 @@ int cu_count() {
 }
 
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
-
-// sizes of the fixed part of the render workspace for T tiles (slots excluded)
-size_t ws_fixed_bytes(int T) { return 256 + round256(4 * (size_t)(T + 1)) + round256(8 * (size_t)T) + 256; }
 constexpr size_t kSlotBytes = sizeof(float4) * kTile * kTile;
+constexpr uint64_t kSegEntries = 1u << kSegShiftMin;
+
+size_t n_goff_blocks(int64_t n) { return (size_t)((n + kGoffBlock - 1) / kGoffBlock); }
+
+// bytes of the layout for T tiles, n Gaussians and k staged entries (k a multiple of 256)
+size_t layout_bytes(int T, int64_t n, uint64_t k) {
+  const size_t slots = (size_t)T + (size_t)(k / kSegEntries);
+  return 256 + round256(4 * (size_t)(T + 1)) + round256(4 * (size_t)n) + round256(4 * (n_goff_blocks(n) + 1)) +
+         round256(8 * ((size_t)T + slots)) + round256(kSlotBytes * slots) + round256(36 * (size_t)k + 16);
+}
+constexpr size_t kBytesPerSeg = kSlotBytes + 8 + 36 * kSegEntries;  // per 256 entries of capacity
 
 }  // namespace
 
-size_t render_ws_bytes(int T, int64_t k_capacity) {
-  const int64_t kc = k_capacity > 0 ? k_capacity : 0;
-  const size_t slots = (size_t)T + (size_t)((kc + (1 << kSegShiftMin) - 1) >> kSegShiftMin);
-  return ws_fixed_bytes(T) + slots * (kSlotBytes + sizeof(uint2));
+size_t render_ws_bytes(int T, int64_t n, int64_t k_capacity) {
+  const uint64_t kc = k_capacity > 0 ? (uint64_t)k_capacity : 0;
+  return layout_bytes(T, n, (kc + kSegEntries - 1) / kSegEntries * kSegEntries);
 }
 
-bool render_ws_layout(void* ws, size_t bytes, int T, RenderWs* out) {
-  const size_t fixed = ws_fixed_bytes(T);
-  if (!ws || bytes < fixed || (reinterpret_cast<uintptr_t>(ws) & 255u)) return false;
-  const size_t cap = (bytes - fixed) / (kSlotBytes + sizeof(uint2));
-  if (cap > 0x7FFFFFFFull) return false;
+bool render_ws_layout(void* ws, size_t bytes, int T, int64_t n, RenderWs* out) {
+  const size_t base = layout_bytes(T, n, 0);
+  if (!ws || bytes < base || (reinterpret_cast<uintptr_t>(ws) & 255u)) return false;
+  // 256 more entries of capacity cost at least kBytesPerSeg - 8 bytes (the item array may not
+  // grow by a whole 256-byte step), so this start is an upper bound; step down to the largest fit
+  uint64_t k = (bytes - base) / (kBytesPerSeg - 8) * kSegEntries;
+  while (k > 0 && layout_bytes(T, n, k) > bytes) k -= kSegEntries;
+  const size_t slots = (size_t)T + (size_t)(k / kSegEntries);
+  if (slots > 0x7FFFFFFFull) return false;
   char* b = static_cast<char*>(ws);
   out->hdr = reinterpret_cast<uint32_t*>(b);
   b += 256;
   out->bnd_off = reinterpret_cast<uint32_t*>(b);
   b += round256(4 * (size_t)(T + 1));
-  out->items = reinterpret_cast<uint2*>(b);  // T + cap items at most
-  b += round256(8 * ((size_t)T + cap));
+  out->goff = reinterpret_cast<uint32_t*>(b);
+  b += round256(4 * (size_t)n);
+  out->goff_blk = reinterpret_cast<uint32_t*>(b);
+  b += round256(4 * (n_goff_blocks(n) + 1));
+  out->items = reinterpret_cast<uint2*>(b);  // T + slots items at most
+  b += round256(8 * ((size_t)T + slots));
   out->slots = reinterpret_cast<float4*>(b);
-  out->slots_cap = (uint32_t)cap;
+  b += round256(kSlotBytes * slots);
+  out->staging = reinterpret_cast<float*>(b);
+  out->slots_cap = (uint32_t)slots;
+  out->staging_cap = k;
   return true;
 }
 
@@ -633,21 +743,32 @@ hipError_t launch_blend_forward(const CamK& cam, int64_t n, const gs_splat* spla
   return hipGetLastError();
 }
 
-hipError_t launch_blend_backward(const CamK& cam, int64_t n, int64_t ld, const gs_splat* splat,
+hipError_t launch_blend_backward(const CamK& cam, int64_t n, const gs_splat* splat, const uint32_t* tiles,
                                  const uint32_t* vals, const uint32_t* ranges, float bg0,
                                  float bg1, float bg2, const float* T_final,
                                  const uint32_t* last_contrib, const float* dLdI, float* grad2d,
                                  const RenderWs& ws, hipStream_t s) {
   const int T = cam.TX * cam.TY;
+  if (n <= 0) return hipSuccess;
+  const size_t nblk = n_goff_blocks(n);
+  hipLaunchKernelGGL(k_goff_local, dim3((unsigned)nblk), dim3(kBlock), 0, s, n, tiles, ws.goff, ws.goff_blk);
+  hipLaunchKernelGGL(k_goff_blocks, dim3(1), dim3(kPlanThreads), 0, s, (int64_t)nblk, ws.goff_blk, ws.hdr);
+  const unsigned fill_grid = (unsigned)std::max(1, cu_count() * 8);
+  hipLaunchKernelGGL(k_clear_staging, dim3(fill_grid), dim3(kBlock), 0, s, (const uint32_t*)ws.hdr,
+                     reinterpret_cast<float4*>(ws.staging), ws.staging_cap);
   hipError_t e = launch_fill_u32(ws.hdr + 3, 1, 0u, s);  // work-item counter
   if (e != hipSuccess) return e;
   // enough persistent workgroups to fill every CU; never more than the items can be
   const int64_t most = (int64_t)T + ws.slots_cap;
   const unsigned grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>(most, (int64_t)cu_count() * 8));
-  hipLaunchKernelGGL(k_blend_backward, dim3(grid), dim3(kBlock), 0, s, cam.W, cam.H, cam.TX, n,
+  hipLaunchKernelGGL(k_blend_backward, dim3(grid), dim3(kBlock), 0, s, cam.W, cam.H, cam.TX, cam.TY, n,
                      reinterpret_cast<const float4*>(splat), vals, reinterpret_cast<const uint2*>(ranges),
-                     bg0, bg1, bg2, T_final, last_contrib, dLdI, grad2d, ws.hdr, (const uint32_t*)ws.bnd_off,
-                     (const uint2*)ws.items, (const float4*)ws.slots);
+                     bg0, bg1, bg2, T_final, last_contrib, dLdI, ws.hdr, (const uint32_t*)ws.bnd_off,
+                     (const uint2*)ws.items, (const float4*)ws.slots, (const uint32_t*)ws.goff,
+                     (const uint32_t*)ws.goff_blk, ws.staging, ws.staging_cap);
+  hipLaunchKernelGGL(k_gather_grad2d, dim3((unsigned)ceil_div(n, (int64_t)kBlock)), dim3(kBlock), 0, s, n, tiles,
+                     (const uint32_t*)ws.goff, (const uint32_t*)ws.goff_blk, (const float*)ws.staging,
+                     ws.staging_cap, grad2d);
   return hipGetLastError();
 }
 

@@ -174,11 +174,11 @@ int gs_bin_and_sort(const gs_scene* scene, const gs_camera* cam, gs_proj proj, v
   return e == hipSuccess ? ok() : hip_fail(e, "gs_bin_and_sort");
 }
 
-int gs_render_workspace(int32_t width, int32_t height, int64_t k_capacity, size_t* bytes) {
-  if (!bytes || width <= 0 || height <= 0 || k_capacity < 0)
+int gs_render_workspace(int32_t width, int32_t height, int64_t n, int64_t k_capacity, size_t* bytes) {
+  if (!bytes || width <= 0 || height <= 0 || n < 0 || k_capacity < 0)
     return fail(GS_ERR_INVALID_ARGUMENT, "invalid arguments");
   const int T = ((width + GS_TILE - 1) / GS_TILE) * ((height + GS_TILE - 1) / GS_TILE);
-  *bytes = render_ws_bytes(T, k_capacity);
+  *bytes = render_ws_bytes(T, n, k_capacity);
   return ok();
 }
 
@@ -192,7 +192,7 @@ int gs_render_forward(const gs_camera* cam, int64_t n, const gs_splat* splat, co
   if ((!splat && n > 0) || !vals || !ranges || !bg || !image || !T_final || !last_contrib || !render_ws)
     return fail(GS_ERR_INVALID_ARGUMENT, "a required pointer is null");
   RenderWs ws;
-  if (!render_ws_layout(render_ws, render_ws_bytes, (int)n_tiles(*cam), &ws))
+  if (!render_ws_layout(render_ws, render_ws_bytes, (int)n_tiles(*cam), n, &ws))
     return fail(GS_ERR_INVALID_ARGUMENT, "render workspace too small or not 256-byte aligned");
   if (!aligned16(splat)) return fail(GS_ERR_INVALID_ARGUMENT, "splat must be 16-byte aligned");
   if (reinterpret_cast<uintptr_t>(ranges) & 7u) return fail(GS_ERR_INVALID_ARGUMENT, "ranges must be 8-byte aligned");
@@ -262,17 +262,16 @@ int gs_render_backward(const gs_scene* scene, float* params, const gs_camera* ca
   if (!vals || !ranges || !bg || !T_final || !last_contrib || !dL_dimage || !render_ws)
     return fail(GS_ERR_INVALID_ARGUMENT, "a required pointer is null");
   RenderWs ws;
-  if (!render_ws_layout(render_ws, render_ws_bytes, (int)n_tiles(*cam), &ws))
+  if (!render_ws_layout(render_ws, render_ws_bytes, (int)n_tiles(*cam), scene->n, &ws))
     return fail(GS_ERR_INVALID_ARGUMENT, "render workspace too small or not 256-byte aligned");
   if (scene->n > 0 && !grad2d) return fail(GS_ERR_INVALID_ARGUMENT, "grad2d is null");
+  if (scene->n > 0 && !proj.tiles) return fail(GS_ERR_INVALID_ARGUMENT, "proj.tiles is null");
   if (scene->n > 0 && (grads || adam) && !params) return fail(GS_ERR_INVALID_ARGUMENT, "params is null");
   if (reinterpret_cast<uintptr_t>(ranges) & 7u) return fail(GS_ERR_INVALID_ARGUMENT, "ranges must be 8-byte aligned");
   if (!(finite(bg[0]) && finite(bg[1]) && finite(bg[2]))) return fail(GS_ERR_INVALID_ARGUMENT, "bg not finite");
   const CamK ck = make_cam(*cam);
-  hipError_t e = launch_fill_f32(grad2d, 9 * scene->ld, 0.f, stream);
-  if (e == hipSuccess)
-    e = launch_blend_backward(ck, scene->n, scene->ld, proj.splat, vals, ranges, bg[0], bg[1], bg[2], T_final,
-                              last_contrib, dL_dimage, grad2d, ws, stream);
+  const hipError_t e = launch_blend_backward(ck, scene->n, proj.splat, proj.tiles, vals, ranges, bg[0], bg[1],
+                                             bg[2], T_final, last_contrib, dL_dimage, grad2d, ws, stream);
   if (e != hipSuccess) return hip_fail(e, "gs_render_backward (blend)");
   if (!grads && !adam) return ok();  // backward blend only
   return gs_preprocess_backward(scene, params, cam, grad2d, grads, adam, stream);

@@ -85,32 +85,44 @@ hipError_t launch_bin_sort_rest(int64_t n, int64_t K, const BinInfo& info, const
 
 // blending
 //
-// Render workspace: what the forward leaves for the backward so that long tile lists can be
-// walked back in parallel segments.  A tile list longer than one segment (kSegMin entries, or
-// a larger power of two when the workspace is short) gets one state slot per segment boundary
-// plus one for its final state; a slot holds (T, C_r, C_g, C_b) for the tile's 256 pixels.
+// Render workspace.  The forward leaves in it what the backward needs to walk long tile lists
+// back in parallel segments: a tile list longer than one segment (256 entries, or a larger
+// power of two when the workspace is short) gets one state slot per segment boundary plus one
+// for its final state; a slot holds (T, C_r, C_g, C_b) for the tile's 256 pixels.  The
+// backward gathers each list entry's nine gradient sums in `staging`, grouped by Gaussian
+// (Gaussian i's entries at goff(i) .. goff(i) + tiles_i, in the row-major order of its tile
+// rect), and then sums each Gaussian's entries into grad2d: no float atomics in memory.
 //   hdr[0] = log2 segment length, hdr[1] = number of backward work items, hdr[2] = slots used,
-//   hdr[3] = work-item counter of the backward
+//   hdr[3] = work-item counter of the backward, hdr[4] = entries (sum of tiles)
 //   bnd_off[T + 1]  first slot of each tile
+//   goff[n]         exclusive scan of tiles within blocks of kGoffBlock Gaussians; goff(i) =
+//                   goff_blk[i / kGoffBlock] + goff[i]
+//   goff_blk[]      exclusive scan of the block totals
 //   items[]         (tile, segment) work items of the backward, tile-major
 //   slots[][256]    float4 states
+//   staging[][9]    per-entry gradient sums
 constexpr int kSegShiftMin = 8;  // 256 list entries per segment
+constexpr int kGoffBlock = 4096;
 struct RenderWs {
   uint32_t* hdr;
   uint32_t* bnd_off;
+  uint32_t* goff;
+  uint32_t* goff_blk;
   uint2* items;
   float4* slots;
+  float* staging;
   uint32_t slots_cap;
+  uint64_t staging_cap;  // entries
 };
-size_t render_ws_bytes(int T, int64_t k_capacity);
-bool render_ws_layout(void* ws, size_t bytes, int T, RenderWs* out);
+size_t render_ws_bytes(int T, int64_t n, int64_t k_capacity);
+bool render_ws_layout(void* ws, size_t bytes, int T, int64_t n, RenderWs* out);
 
 hipError_t launch_blend_forward(const CamK& cam, int64_t n, const gs_splat* splat, const uint32_t* vals,
                                 const uint32_t* ranges, float bg0, float bg1, float bg2,
                                 float* image, float* T_final, uint32_t* last_contrib,
                                 uint32_t* n_examined, uint64_t* blend_count, const RenderWs& ws,
                                 hipStream_t s);
-hipError_t launch_blend_backward(const CamK& cam, int64_t n, int64_t ld, const gs_splat* splat,
+hipError_t launch_blend_backward(const CamK& cam, int64_t n, const gs_splat* splat, const uint32_t* tiles,
                                  const uint32_t* vals, const uint32_t* ranges, float bg0,
                                  float bg1, float bg2, const float* T_final,
                                  const uint32_t* last_contrib, const float* dLdI, float* grad2d,

@@ -79,7 +79,7 @@ def load(path: str = LIB_PATH):
     L.gs_preprocess.argtypes = [SP, P, CP, GsProj, P]
     L.gs_bin_and_sort_workspace.argtypes = [i64, i64, i32, i32, ctypes.POINTER(sz)]
     L.gs_bin_and_sort.argtypes = [SP, CP, GsProj, P, sz, i64, P, P, P, ctypes.POINTER(i64), P]
-    L.gs_render_workspace.argtypes = [i32, i32, i64, ctypes.POINTER(sz)]
+    L.gs_render_workspace.argtypes = [i32, i32, i64, i64, ctypes.POINTER(sz)]
     L.gs_render_forward.argtypes = [CP, i64, P, P, P, ctypes.POINTER(ctypes.c_float), P, P, P, P, P, P, sz, P]
     L.gs_loss_l1_workspace.argtypes = [i64, ctypes.POINTER(sz)]
     L.gs_loss_l1.argtypes = [i64, P, P, P, P, P, sz, P]
@@ -191,9 +191,9 @@ def _bg(bg):
     return arr
 
 
-def render_workspace(width, height, k_capacity) -> int:
+def render_workspace(width, height, n, k_capacity) -> int:
     out = ctypes.c_size_t(0)
-    _check(load().gs_render_workspace(int(width), int(height), int(k_capacity), ctypes.byref(out)))
+    _check(load().gs_render_workspace(int(width), int(height), int(n), int(k_capacity), ctypes.byref(out)))
     return out.value
 
 
@@ -265,7 +265,7 @@ class StepBuffers:
         self.ranges = torch.empty((self.T, 2), dtype=i32, device=device)
         self.ws = torch.empty(bin_and_sort_workspace(n, self.k_capacity, width, height), dtype=torch.uint8,
                               device=device)
-        self.render_ws = torch.empty(render_workspace(width, height, self.k_capacity), dtype=torch.uint8,
+        self.render_ws = torch.empty(render_workspace(width, height, n, self.k_capacity), dtype=torch.uint8,
                                      device=device)
         self.image = torch.empty((height, width, 3), dtype=f32, device=device)
         self.T_final = torch.empty((height, width), dtype=f32, device=device)
@@ -282,7 +282,7 @@ class StepBuffers:
         self.vals = torch.empty(max(1, self.k_capacity), dtype=torch.int32, device=device)
         self.ws = torch.empty(bin_and_sort_workspace(self.n, self.k_capacity, self.W, self.H), dtype=torch.uint8,
                               device=device)
-        self.render_ws = torch.empty(render_workspace(self.W, self.H, self.k_capacity), dtype=torch.uint8,
+        self.render_ws = torch.empty(render_workspace(self.W, self.H, self.n, self.k_capacity), dtype=torch.uint8,
                                      device=device)
 
 

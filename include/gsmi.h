@@ -151,13 +151,14 @@ int gs_bin_and_sort(const gs_scene* scene, const gs_camera* cam, gs_proj proj, v
                     size_t workspace_bytes, int64_t k_capacity, uint32_t* vals, uint32_t* ranges,
                     uint64_t* keys, int64_t* k_out, hipStream_t stream);
 
-/* Bytes of the render workspace that gs_render_forward fills and gs_render_backward reads,
- * for a width x height image and lists of up to k_capacity intersections (host-only query).
- * It holds, for every tile list longer than one segment (256 entries, or a larger power of
- * two if the workspace is smaller than this size), each pixel's transmittance and colour at
- * every segment boundary and at the end of its walk, plus the backward's work list.  The
- * backward walks the segments of a long list in parallel from these states. */
-int gs_render_workspace(int32_t width, int32_t height, int64_t k_capacity, size_t* bytes);
+/* Bytes of the render workspace that gs_render_forward fills and gs_render_backward uses, for
+ * a width x height image, n Gaussians and lists of up to k_capacity intersections (host-only
+ * query).  It holds, for every tile list longer than one segment (256 entries), each pixel's
+ * transmittance and colour at every segment boundary and at the end of its walk, plus the
+ * backward's work list: the backward walks the segments of a long list in parallel from these
+ * states.  It also holds the backward's per-intersection gradient sums (36 bytes each), which
+ * are summed per Gaussian into grad2d instead of accumulating grad2d with atomics. */
+int gs_render_workspace(int32_t width, int32_t height, int64_t n, int64_t k_capacity, size_t* bytes);
 
 /* Forward blend.  For each pixel, walks its tile's list front to back: power =
  * -(a dx^2 + c dy^2)/2 - b dx dy with (dx, dy) = pixel centre - (u, v); skips power > 0;
@@ -172,10 +173,10 @@ int gs_render_workspace(int32_t width, int32_t height, int64_t k_capacity, size_
  *                       ADDED (the caller zeroes them): [0] n_examined, [1] last_contrib
  *                       (the entries the backward pass walks), [2] the (pixel, entry)
  *                       pairs composited
- *   render_ws           out: device workspace of render_ws_bytes >= the size
- *                       gs_render_workspace gives for this image (256-byte aligned); a
- *                       smaller one down to the fixed part still works, with longer
- *                       segments.  GS_ERR_INVALID_ARGUMENT if it is below the fixed part.
+ *   render_ws           out: device workspace (256-byte aligned) of render_ws_bytes >= the
+ *                       size gs_render_workspace gives for this image, n and a k_capacity
+ *                       >= the number of intersections in vals; GS_ERR_INVALID_ARGUMENT if
+ *                       it is smaller than the size for k_capacity 0.
  * bg is a HOST array of 3 floats.  One 256-thread workgroup per tile. */
 int gs_render_forward(const gs_camera* cam, int64_t n, const gs_splat* splat, const uint32_t* vals,
                       const uint32_t* ranges, const float* bg, float* image, float* T_final,
@@ -193,8 +194,11 @@ int gs_loss_l1(int64_t count, const float* image, const float* target, float* lo
 
 /* Backward of the step from dL/dimage.
  *   grad2d[ld][9]  out: per-Gaussian dL/d(u, v, conic_a, conic_b, conic_c, opacity, r, g, b),
- *                  the nine values of Gaussian i contiguous at grad2d + 9 i (one or two cache
- *                  lines take all nine accumulations of a record)
+ *                  the nine values of Gaussian i at grad2d + 9 i, for i < n (rows n..ld-1 are
+ *                  not written).  Each intersection's sums are staged in render_ws and each
+ *                  Gaussian's are added in the order of its tile rect; within an intersection
+ *                  the pixel contributions meet in LDS atomics, so the summation order is not
+ *                  fixed.
  *                  from the reverse-order backward blend (zeroed inside, then accumulated
  *                  with float atomics, so the summation order is not fixed)
  *   grads[R][ld]   out, nullable: dL/dparams by the chain rule through the preprocess
@@ -203,8 +207,9 @@ int gs_loss_l1(int64_t count, const float* image, const float* target, float* lo
  * With grads and adam both null only the backward blend runs (grad2d is the only output and
  * params may be null); gs_preprocess_backward then finishes the step.
  * T_final, last_contrib and render_ws are the forward's outputs for the same lists, camera and
- * bg (render_ws unmodified since, same size); the backward only updates a work counter in
- * it, so it may be run more than once per forward.  bg is a HOST array of 3 floats.  Culled
+ * bg (render_ws unmodified since, same size); proj.tiles is the preprocess output the lists
+ * were built from.  The backward leaves the forward's part of render_ws intact, so it may be
+ * run more than once per forward.  bg is a HOST array of 3 floats.  Culled
  * Gaussians receive zero gradients. */
 int gs_render_backward(const gs_scene* scene, float* params, const gs_camera* cam, gs_proj proj,
                        const uint32_t* vals, const uint32_t* ranges, const float* bg,

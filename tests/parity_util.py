@@ -93,15 +93,13 @@ class GpuStep:
         return (K, self.keys.cpu().numpy().view(np.uint64)[:K], self.vals.cpu().numpy().view(np.uint32)[:K],
                 self.ranges.cpu().numpy().view(np.uint32))
 
-    def forward(self, bg=(0.0, 0.0, 0.0), ranges=None, render_ws_bytes=None):
-        """render_ws_bytes: a workspace smaller than the query's (longer backward segments)."""
+    def forward(self, bg=(0.0, 0.0, 0.0), ranges=None):
         torch = self.torch
         H, W = self.H, self.W
         self.bg = bg
         rg = self.ranges if ranges is None else to_t(np.asarray(ranges, np.uint32).view(np.int32))
-        nb = gsmi.render_workspace(W, H, max(1, int(self.vals.numel())))
-        self.render_ws = torch.empty(nb if render_ws_bytes is None else render_ws_bytes, dtype=torch.uint8,
-                                     device="cuda")
+        nb = gsmi.render_workspace(W, H, self.n, max(1, int(self.vals.numel())))
+        self.render_ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
         self.image = torch.empty((H, W, 3), dtype=torch.float32, device="cuda")
         self.T_final = torch.empty((H, W), dtype=torch.float32, device="cuda")
         self.last = torch.empty((H, W), dtype=torch.int32, device="cuda")

@@ -76,14 +76,14 @@ def test_workspace_queries():
     assert gsmi.loss_l1_workspace(3 * 2048 * 2048) >= 4 * (3 * 2048 * 2048) // 4096
     with pytest.raises(gsmi.GsError):
         gsmi.bin_and_sort_workspace(-1, 0, 16, 16)
-    # render workspace: a fixed part for the tiles plus one 4 KiB state slot (and one work
-    # item) per tile and per 256 intersections of capacity
-    r0 = gsmi.render_workspace(2048, 2048, 0)
-    r1 = gsmi.render_workspace(2048, 2048, 256 * 1000)
-    assert r1 - r0 == 1000 * (4096 + 8)
-    assert r0 >= 16384 * (4096 + 8 + 4)
+    # render workspace: a fixed part for the tiles and Gaussians plus, per 256 intersections of
+    # capacity, one 4 KiB state slot, one work item and 256 staged 36-byte gradient sums
+    r0 = gsmi.render_workspace(2048, 2048, 4_000_000, 0)
+    r1 = gsmi.render_workspace(2048, 2048, 4_000_000, 256 * 1000)
+    assert abs((r1 - r0) - 1000 * (4096 + 8 + 256 * 36)) <= 512
+    assert r0 >= 16384 * (4096 + 8 + 4) + 4 * 4_000_000
     with pytest.raises(gsmi.GsError):
-        gsmi.render_workspace(0, 16, 10)
+        gsmi.render_workspace(0, 16, 10, 10)
 
 
 def test_render_calls_reject_a_missing_or_short_workspace():
@@ -95,7 +95,7 @@ def test_render_calls_reject_a_missing_or_short_workspace():
     cam.viewmat[0] = cam.viewmat[5] = cam.viewmat[10] = 1.0
     bg = (ctypes.c_float * 3)(0, 0, 0)
     p = ctypes.c_void_p(4096)
-    need = gsmi.render_workspace(64, 64, 0)
+    need = gsmi.render_workspace(64, 64, 10, 0)
     for ws, nb in ((None, need), (p, 16), (ctypes.c_void_p(4096 + 64), need)):
         rc = L.gs_render_forward(ctypes.byref(cam), 10, p, p, p, bg, p, p, p, None, None, ws, nb, None)
         assert rc == gsmi.GS_ERR_INVALID_ARGUMENT
