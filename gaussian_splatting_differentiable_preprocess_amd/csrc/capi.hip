@@ -182,6 +182,17 @@ int gs_render_workspace(int32_t width, int32_t height, int64_t n, int64_t k_capa
   return ok();
 }
 
+int gs_render_workspace_capacity(int32_t width, int32_t height, int64_t n, size_t bytes,
+                                 int64_t* k_capacity) {
+  if (!k_capacity || width <= 0 || height <= 0 || n < 0) return fail(GS_ERR_INVALID_ARGUMENT, "invalid arguments");
+  const int T = ((width + GS_TILE - 1) / GS_TILE) * ((height + GS_TILE - 1) / GS_TILE);
+  RenderWs ws;
+  if (!render_ws_layout(reinterpret_cast<void*>(uintptr_t(256)), bytes, T, n, &ws))
+    return fail(GS_ERR_INVALID_ARGUMENT, "workspace smaller than the size for k_capacity 0");
+  *k_capacity = (int64_t)ws.staging_cap;
+  return ok();
+}
+
 int gs_render_forward(const gs_camera* cam, int64_t n, const gs_splat* splat, const uint32_t* vals,
                       const uint32_t* ranges, const float* bg, float* image, float* T_final,
                       uint32_t* last_contrib, uint32_t* n_examined, uint64_t* blend_count,

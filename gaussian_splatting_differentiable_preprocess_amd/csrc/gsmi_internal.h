@@ -115,6 +115,8 @@ struct RenderWs {
   uint64_t staging_cap;  // entries
 };
 size_t render_ws_bytes(int T, int64_t n, int64_t k_capacity);
+// Carves ws (bytes long) into the regions above; only the alignment of ws is read, so a
+// placeholder address serves for capacity queries.
 bool render_ws_layout(void* ws, size_t bytes, int T, int64_t n, RenderWs* out);
 
 hipError_t launch_blend_forward(const CamK& cam, int64_t n, const gs_splat* splat, const uint32_t* vals,

@@ -23,7 +23,7 @@ SPLAT_FLOATS = 12  # 48-byte record: u, v, radius_x, radius_y | A, B, C, opacity
 
 EXPORTS = (
     "gs_version", "gs_last_error", "gs_preprocess", "gs_bin_and_sort_workspace", "gs_bin_and_sort",
-    "gs_render_workspace", "gs_render_forward", "gs_loss_l1_workspace", "gs_loss_l1", "gs_render_backward",
+    "gs_render_workspace", "gs_render_workspace_capacity", "gs_render_forward", "gs_loss_l1_workspace", "gs_loss_l1", "gs_render_backward",
     "gs_preprocess_backward", "gs_adam_step",
 )
 
@@ -80,6 +80,7 @@ def load(path: str = LIB_PATH):
     L.gs_bin_and_sort_workspace.argtypes = [i64, i64, i32, i32, ctypes.POINTER(sz)]
     L.gs_bin_and_sort.argtypes = [SP, CP, GsProj, P, sz, i64, P, P, P, ctypes.POINTER(i64), P]
     L.gs_render_workspace.argtypes = [i32, i32, i64, i64, ctypes.POINTER(sz)]
+    L.gs_render_workspace_capacity.argtypes = [i32, i32, i64, sz, ctypes.POINTER(i64)]
     L.gs_render_forward.argtypes = [CP, i64, P, P, P, ctypes.POINTER(ctypes.c_float), P, P, P, P, P, P, sz, P]
     L.gs_loss_l1_workspace.argtypes = [i64, ctypes.POINTER(sz)]
     L.gs_loss_l1.argtypes = [i64, P, P, P, P, P, sz, P]
@@ -194,6 +195,12 @@ def _bg(bg):
 def render_workspace(width, height, n, k_capacity) -> int:
     out = ctypes.c_size_t(0)
     _check(load().gs_render_workspace(int(width), int(height), int(n), int(k_capacity), ctypes.byref(out)))
+    return out.value
+
+
+def render_workspace_capacity(width, height, n, nbytes) -> int:
+    out = ctypes.c_int64(0)
+    _check(load().gs_render_workspace_capacity(int(width), int(height), int(n), int(nbytes), ctypes.byref(out)))
     return out.value
 
 

@@ -160,6 +160,12 @@ int gs_bin_and_sort(const gs_scene* scene, const gs_camera* cam, gs_proj proj, v
  * are summed per Gaussian into grad2d instead of accumulating grad2d with atomics. */
 int gs_render_workspace(int32_t width, int32_t height, int64_t n, int64_t k_capacity, size_t* bytes);
 
+/* The largest intersection count a render workspace of `bytes` serves for this image and n
+ * (host-only query; the inverse of gs_render_workspace, rounded to whole 256-entry segments).
+ * GS_ERR_INVALID_ARGUMENT if `bytes` is below the size for k_capacity 0. */
+int gs_render_workspace_capacity(int32_t width, int32_t height, int64_t n, size_t bytes,
+                                 int64_t* k_capacity);
+
 /* Forward blend.  For each pixel, walks its tile's list front to back: power =
  * -(a dx^2 + c dy^2)/2 - b dx dy with (dx, dy) = pixel centre - (u, v); skips power > 0;
  * alpha = min(0.99, opacity e^power); skips alpha < 1/255; stops before blending an entry

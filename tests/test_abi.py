@@ -84,6 +84,15 @@ def test_workspace_queries():
     assert r0 >= 16384 * (4096 + 8 + 4) + 4 * 4_000_000
     with pytest.raises(gsmi.GsError):
         gsmi.render_workspace(0, 16, 10, 10)
+    # the capacity query inverts the size query: never below the capacity asked for, and no
+    # more than one 256-entry segment above it
+    for W, H in ((17, 33), (64, 64), (1024, 1024), (2048, 2048)):
+        for n in (1, 120, 3000, 262144, 4_000_000):
+            for k in (0, 1, 255, 256, 257, 12_345, 6_800_000, 10_300_000):
+                got = gsmi.render_workspace_capacity(W, H, n, gsmi.render_workspace(W, H, n, k))
+                assert k <= got < k + 512, (W, H, n, k, got)
+    with pytest.raises(gsmi.GsError):
+        gsmi.render_workspace_capacity(64, 64, 10, 100)
 
 
 def test_render_calls_reject_a_missing_or_short_workspace():
