@@ -218,7 +218,7 @@ __device__ uint32_t block_exscan_1024(uint32_t x, uint32_t* red) {
 __global__ __launch_bounds__(kPlanThreads) void k_seg_plan(const uint2* __restrict__ ranges, int T,
                                                            uint32_t slots_cap, uint32_t* __restrict__ hdr,
                                                            uint32_t* __restrict__ bnd_off,
-                                                           uint2* __restrict__ items) {
+                                                           uint32_t* __restrict__ item_off) {
   __shared__ unsigned long long red64[kPlanThreads / 64];
   __shared__ uint32_t red32[kPlanThreads / 64];
   const int per = (T + kPlanThreads - 1) / kPlanThreads;
@@ -250,16 +250,26 @@ __global__ __launch_bounds__(kPlanThreads) void k_seg_plan(const uint2* __restri
     const uint32_t len = r.y - r.x, k = len ? ((len - 1u) >> shift) + 1u : 0u;
     bnd_off[t] = so;
     so += len > seg ? k : 0u;
-    for (uint32_t j = 0; j < k; ++j) items[io + j] = make_uint2((uint32_t)t, j);
+    item_off[t] = io;
     io += k;
   }
   if (t1 == T && (t0 < t1 || threadIdx.x == 0)) {  // the thread that owns the last tile
     bnd_off[T] = so;
+    item_off[T] = io;
     hdr[0] = (uint32_t)shift;
     hdr[1] = io;
     hdr[2] = so;
     hdr[3] = 0u;
   }
+}
+
+// The item list: one wave per tile writes the tile's items (tile, 0), (tile, 1), ...
+__global__ __launch_bounds__(kBlock) void k_seg_items(int T, const uint32_t* __restrict__ item_off,
+                                                      uint2* __restrict__ items) {
+  const int t = (int)(blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6));
+  if (t >= T) return;
+  const uint32_t o = item_off[t], k = item_off[t + 1] - o;
+  for (uint32_t j = threadIdx.x & 63; j < k; j += 64) items[o + j] = make_uint2((uint32_t)t, j);
 }
 
 // pixel index inside its tile of lane (lx, ly) of quadrant wave w
@@ -687,7 +697,7 @@ size_t n_goff_blocks(int64_t n) { return (size_t)((n + kGoffBlock - 1) / kGoffBl
 // bytes of the layout for T tiles, n Gaussians and k staged entries (k a multiple of 256)
 size_t layout_bytes(int T, int64_t n, uint64_t k) {
   const size_t slots = (size_t)T + (size_t)(k / kSegEntries);
-  return 256 + round256(4 * (size_t)(T + 1)) + round256(4 * (size_t)n) + round256(4 * (n_goff_blocks(n) + 1)) +
+  return 256 + 2 * round256(4 * (size_t)(T + 1)) + round256(4 * (size_t)n) + round256(4 * (n_goff_blocks(n) + 1)) +
          round256(8 * ((size_t)T + slots)) + round256(kSlotBytes * slots) + round256(36 * (size_t)k + 16);
 }
 constexpr size_t kBytesPerSeg = kSlotBytes + 8 + 36 * kSegEntries;  // per 256 entries of capacity
@@ -713,6 +723,8 @@ bool render_ws_layout(void* ws, size_t bytes, int T, int64_t n, RenderWs* out) {
   b += 256;
   out->bnd_off = reinterpret_cast<uint32_t*>(b);
   b += round256(4 * (size_t)(T + 1));
+  out->item_off = reinterpret_cast<uint32_t*>(b);
+  b += round256(4 * (size_t)(T + 1));
   out->goff = reinterpret_cast<uint32_t*>(b);
   b += round256(4 * (size_t)n);
   out->goff_blk = reinterpret_cast<uint32_t*>(b);
@@ -735,7 +747,9 @@ hipError_t launch_blend_forward(const CamK& cam, int64_t n, const gs_splat* spla
   const int T = cam.TX * cam.TY;
   const uint2* rg = reinterpret_cast<const uint2*>(ranges);
   hipLaunchKernelGGL(k_seg_plan, dim3(1), dim3(kPlanThreads), 0, s, rg, T, ws.slots_cap, ws.hdr, ws.bnd_off,
-                     ws.items);
+                     ws.item_off);
+  hipLaunchKernelGGL(k_seg_items, dim3((unsigned)ceil_div(T, kBlock / 64)), dim3(kBlock), 0, s, T,
+                     (const uint32_t*)ws.item_off, ws.items);
   hipLaunchKernelGGL(k_blend_forward, dim3(T), dim3(kBlock), 0, s, cam.W, cam.H, cam.TX, T, n,
                      reinterpret_cast<const float4*>(splat), vals, rg, bg0, bg1, bg2, image, T_final,
                      last_contrib, n_examined, reinterpret_cast<unsigned long long*>(blend_count),

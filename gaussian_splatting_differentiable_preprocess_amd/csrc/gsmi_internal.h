@@ -95,6 +95,7 @@ hipError_t launch_bin_sort_rest(int64_t n, int64_t K, const BinInfo& info, const
 //   hdr[0] = log2 segment length, hdr[1] = number of backward work items, hdr[2] = slots used,
 //   hdr[3] = work-item counter of the backward, hdr[4] = entries (sum of tiles)
 //   bnd_off[T + 1]  first slot of each tile
+//   item_off[T + 1] first work item of each tile
 //   goff[n]         exclusive scan of tiles within blocks of kGoffBlock Gaussians; goff(i) =
 //                   goff_blk[i / kGoffBlock] + goff[i]
 //   goff_blk[]      exclusive scan of the block totals
@@ -106,6 +107,7 @@ constexpr int kGoffBlock = 4096;
 struct RenderWs {
   uint32_t* hdr;
   uint32_t* bnd_off;
+  uint32_t* item_off;
   uint32_t* goff;
   uint32_t* goff_blk;
   uint2* items;

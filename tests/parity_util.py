@@ -43,6 +43,50 @@ def to_t(x, dtype=None):
     return t.cuda()
 
 
+def proj_f32(proj):
+    """The oracle's projected record as float32 values (the record is 12 float32 scalars); the
+    oracle's later stages and the GPU stages under test both read these values."""
+    return np.asarray(proj, np.float64).astype(np.float32).astype(np.float64)
+
+
+def records_from_oracle(proj, radii, tiles):
+    """Oracle projection (planar [10][n], radii [2][n], tiles [n]) -> the GPU's 48-byte records
+    ([n][12] float32: u, v, radius bits x2, conic a b c, opacity, r g b, depth), tiles and
+    depth keys (float bits, all-ones when culled).  A layout conversion, nothing computed."""
+    p = np.asarray(proj, np.float64)
+    radii = np.asarray(radii, np.int32)
+    n = p.shape[1]
+    rec = np.zeros((n, 12), np.float32)
+    rec[:, 0], rec[:, 1] = p[0], p[1]
+    rec[:, 2], rec[:, 3] = radii[0].view(np.float32), radii[1].view(np.float32)
+    rec[:, 4], rec[:, 5], rec[:, 6], rec[:, 7] = p[4], p[5], p[6], p[3]
+    rec[:, 8], rec[:, 9], rec[:, 10], rec[:, 11] = p[7], p[8], p[9], p[2]
+    vis = (radii[0] > 0) & (radii[1] > 0)
+    dkey = np.where(vis, rec[:, 11].view(np.uint32), np.uint32(0xFFFFFFFF)).astype(np.uint32)
+    return rec, np.asarray(tiles, np.uint32), dkey
+
+
+def oracle_pipeline(params, deg, cam_flat, W, H, bg, target=None, upstream=None, margins=None):
+    """The oracle's whole step from the seeded inputs alone: preprocess, then every later stage
+    on the float32 record values; the loss on the float32 image; dL/dI rounded to float32 for
+    the backward (the form the GPU stages under test are given)."""
+    proj, radii, tiles = oracle.preprocess(params, deg, cam_flat, W, H)
+    p32 = proj_f32(proj)
+    keys, vals = oracle.bin_sort(p32, radii, W, H)
+    rg = oracle.ranges(keys, oracle.n_tiles(W, H))
+    fwd = oracle.render_forward(p32, vals, rg, W, H, bg, margins=margins)
+    img32 = fwd["image"].astype(np.float32)
+    if upstream is not None:
+        loss, dLdI = None, np.asarray(upstream, np.float64)
+    else:
+        loss, dLdI = oracle.loss_l1(img32.astype(np.float64), target)
+    dl32 = dLdI.astype(np.float32)
+    g2 = oracle.render_backward(p32, vals, rg, W, H, dl32.astype(np.float64), bg)
+    grads = oracle.preprocess_backward(params, deg, cam_flat, W, H, g2)
+    return dict(proj=proj, p32=p32, radii=radii, tiles=tiles, keys=keys, vals=vals, ranges=rg.reshape(-1, 2),
+                fwd=fwd, img32=img32, loss=loss, dLdI=dLdI, dl32=dl32, grad2d=g2, grads=grads)
+
+
 def proj_from_splat(splat, depth_key=None):
     """GPU records [n, 12] float32 -> oracle layout proj [10][n] float64, radii [2][n]."""
     s = np.asarray(splat, np.float32)
@@ -71,6 +115,29 @@ class GpuStep:
         self.T = gsmi.n_tiles(W, H)
         self.kcap = k_capacity
         self.torch = torch
+
+    def load_proj(self, rec, tiles, dkey):
+        """Puts oracle-derived records, tiles and depth keys in the GPU projection buffers."""
+        n = rec.shape[0]
+        self.proj.splat[:n].copy_(to_t(np.ascontiguousarray(rec, np.float32)))
+        self.proj.tiles[:n].copy_(to_t(np.ascontiguousarray(tiles, np.uint32).view(np.int32)))
+        self.proj.depth_key[:n].copy_(to_t(np.ascontiguousarray(dkey, np.uint32).view(np.int32)))
+        self.torch.cuda.synchronize()
+
+    def load_lists(self, vals, ranges):
+        """Puts oracle-derived sorted lists (vals [K], ranges [T][2]) on the GPU."""
+        torch = self.torch
+        vals = np.ascontiguousarray(vals, np.uint32)
+        self.vals = torch.empty(max(1, vals.size), dtype=torch.int32, device="cuda")
+        if vals.size:
+            self.vals[: vals.size].copy_(to_t(vals.view(np.int32)))
+        self.ranges = to_t(np.ascontiguousarray(np.asarray(ranges, np.uint32).reshape(-1, 2)).view(np.int32))
+        self.K = int(vals.size)
+
+    def loss_on(self, image, target):
+        """GPU L1 loss of a given float32 image."""
+        self.image = to_t(np.ascontiguousarray(image, np.float32))
+        return self.loss(target)
 
     def preprocess(self):
         gsmi.preprocess(self.scene, self.params, self.cam, self.proj)
