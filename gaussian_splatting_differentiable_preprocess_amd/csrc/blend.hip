@@ -42,24 +42,25 @@ __device__ __forceinline__ float eval_power(float nA, float nB, float nC, float 
 
 __device__ __forceinline__ float eval_oG(float o, float power) { return __fmul_rn(o, __expf(power)); }
 
-// One DPP step x += permute(x) on the rows in ROW_MASK (old value 0 = identity of the add).
-template <int CTRL, int ROW_MASK>
+// One DPP step x += permute(x) within each row of 16 lanes (every source lane is active, so the
+// move folds into v_add_f32_dpp).
+template <int CTRL>
 __device__ __forceinline__ float dpp_add(float x) {
-  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xF, false));
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 
 // Sums each of N values over each group of 8 lanes (a pixel row of a quadrant); every lane
 // gets its group's sums.  The steps are interleaved across the N values so a DPP read never
-// waits on the instruction just before it.  The lanes of a group must be all active or all
-// inactive.
+// waits on the instruction just before it.  Every lane of the wave must be active.  (Groups
+// of 16 lanes, two pixel rows, take fewer iterations but a fourth step; measured slower.)
 template <int N>
 __device__ __forceinline__ void row8_sum(float* v) {
 #pragma unroll
-  for (int q = 0; q < N; ++q) v[q] = dpp_add<0xB1, 0xF>(v[q]);   // quad_perm [1,0,3,2]
+  for (int q = 0; q < N; ++q) v[q] = dpp_add<0xB1>(v[q]);   // quad_perm [1,0,3,2]
 #pragma unroll
-  for (int q = 0; q < N; ++q) v[q] = dpp_add<0x4E, 0xF>(v[q]);   // quad_perm [2,3,0,1]
+  for (int q = 0; q < N; ++q) v[q] = dpp_add<0x4E>(v[q]);   // quad_perm [2,3,0,1]
 #pragma unroll
-  for (int q = 0; q < N; ++q) v[q] = dpp_add<0x141, 0xF>(v[q]);  // row_half_mirror
+  for (int q = 0; q < N; ++q) v[q] = dpp_add<0x141>(v[q]);  // row_half_mirror
 }
 
 constexpr int kChunk = 64;  // records staged per chunk (one per lane)
@@ -97,10 +98,10 @@ __device__ __forceinline__ Box alpha_box(float u, float v, float A, float B, flo
 }
 
 // Per-lane masks: bit e set iff record e's box contains the lane's pixel (lx, ly).  Lane e
-// holds record e's box; COL[x] / ROW[y] are ballots over the records.  *row_out (optional)
+// holds record e's box; COL[x] / ROW[y] are ballots over the records.  *rows_out (optional)
 // gets ROW[ly], the records whose box meets the lane's pixel row.
 __device__ __forceinline__ unsigned long long lane_mask(const Box& b, int lx, int ly,
-                                                     unsigned long long* row_out = nullptr) {
+                                                     unsigned long long* rows_out = nullptr) {
   unsigned long long col = 0ull, row = 0ull;
 #pragma unroll
   for (int x = 0; x < 8; ++x) {
@@ -111,8 +112,9 @@ __device__ __forceinline__ unsigned long long lane_mask(const Box& b, int lx, in
   for (int y = 0; y < 8; ++y) {
     const unsigned long long r = __ballot(b.y0 <= y && y <= b.y1);
     row = (ly == y) ? r : row;
+
   }
-  if (row_out) *row_out = row;
+  if (rows_out) *rows_out = row;
   return col & row;
 }
 
@@ -535,12 +537,13 @@ __global__ __launch_bounds__(kBlock) void k_blend_backward(
             const float dL_dalpha = Tk * ((cr - S0) * g0 + (cg - S1) * g1 + (cb - S2) * g2) - bgT * rom;
             const bool unclamped = act && oG <= kAlphaMax;  // alpha = o G depends on o and power
             const float dpow = unclamped ? oG * dL_dalpha : 0.0f;
+            // moments of dL/dpower over the pixels; the conic gradients are linear in them
             float v[9];
-            v[0] = -(2.0f * g.z * dx + g.w * dy) * dpow;  // A = -2 nA, B = -nB
-            v[1] = -(g.w * dx + 2.0f * cl.x * dy) * dpow;  // C = -2 nC
-            v[2] = -0.5f * dx * dx * dpow;
-            v[3] = -dx * dy * dpow;
-            v[4] = -0.5f * dy * dy * dpow;
+            v[0] = dx * dpow;
+            v[1] = dy * dpow;
+            v[2] = dx * v[0];
+            v[3] = dy * v[0];
+            v[4] = dy * v[1];
             v[5] = unclamped ? G * dL_dalpha : 0.0f;
             v[6] = act ? wt * g0 : 0.0f;
             v[7] = act ? wt * g1 : 0.0f;
@@ -553,9 +556,16 @@ __global__ __launch_bounds__(kBlock) void k_blend_backward(
             }
             row8_sum<9>(v);  // every lane of a pixel row holds the row's sums
             if (lx == 0 && ((acts >> (ly * 8)) & 0xFFull)) {
+              // dL/du = (A m_x + B m_y), dL/dv = (B m_x + C m_y), dL/dA = -m_xx / 2,
+              // dL/dB = -m_xy, dL/dC = -m_yy / 2 with A = -2 nA, B = -nB, C = -2 nC
               const uint32_t ws = wbase + (uint32_t)e;
+              atomicAdd(&acc[0][ws], -(2.0f * g.z * v[0] + g.w * v[1]));
+              atomicAdd(&acc[1][ws], -(g.w * v[0] + 2.0f * cl.x * v[1]));
+              atomicAdd(&acc[2][ws], -0.5f * v[2]);
+              atomicAdd(&acc[3][ws], -v[3]);
+              atomicAdd(&acc[4][ws], -0.5f * v[4]);
 #pragma unroll
-              for (int q = 0; q < 9; ++q) atomicAdd(&acc[q][ws], v[q]);
+              for (int q = 5; q < 9; ++q) atomicAdd(&acc[q][ws], v[q]);
             }
           }
           wave_sync_lds();  // this chunk's reads finish before the next chunk is staged
