@@ -17,7 +17,10 @@
 // in list order, so lanes evaluate different records at the same time: a record costs VALU
 // work only on the pixels it can reach, and the per-pixel results are those of the plain walk
 // (a skipped record has alpha < 1/255 at that pixel).  The forward's quadrant waves are
-// independent (no workgroup barrier); the backward's share per-chunk gradient sums in LDS.
+// independent (no workgroup barrier).  The forward also leaves, per pixel and chunk, the 64-bit
+// mask of the chunk's entries it composited; the backward walks exactly those entries (per
+// pixel row of 8 lanes, whose sums are formed with DPP), so no record is tested twice.  The
+// backward's waves share per-entry gradient sums in LDS.
 // Workgroup b renders tile b: the hardware deals consecutive workgroups to the 8 XCDs in turn,
 // which spreads the (very uneven) per-tile work evenly over them.  Bound: VALU /
 // transcendental and LDS, not HBM.
@@ -42,11 +45,15 @@ __device__ __forceinline__ float eval_power(float nA, float nB, float nC, float 
 
 __device__ __forceinline__ float eval_oG(float o, float power) { return __fmul_rn(o, __expf(power)); }
 
-// One DPP step x += permute(x) within each row of 16 lanes (every source lane is active, so the
-// move folds into v_add_f32_dpp).
+// One DPP step x op= permute(x) within each row of 16 lanes (every source lane is active, so
+// the move folds into the DPP form of the add / or).
 template <int CTRL>
 __device__ __forceinline__ float dpp_add(float x) {
   return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_or(uint32_t x) {
+  return x | (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, true);
 }
 
 // Sums each of N values over each group of 8 lanes (a pixel row of a quadrant); every lane
@@ -61,6 +68,18 @@ __device__ __forceinline__ void row8_sum(float* v) {
   for (int q = 0; q < N; ++q) v[q] = dpp_add<0x4E>(v[q]);   // quad_perm [2,3,0,1]
 #pragma unroll
   for (int q = 0; q < N; ++q) v[q] = dpp_add<0x141>(v[q]);  // row_half_mirror
+}
+
+// OR of a 64-bit value over each group of 8 lanes; every lane of the wave must be active.
+__device__ __forceinline__ unsigned long long row8_or(unsigned long long m) {
+  uint32_t lo = (uint32_t)m, hi = (uint32_t)(m >> 32);
+  lo = dpp_or<0xB1>(lo);
+  hi = dpp_or<0xB1>(hi);
+  lo = dpp_or<0x4E>(lo);
+  hi = dpp_or<0x4E>(hi);
+  lo = dpp_or<0x141>(lo);
+  hi = dpp_or<0x141>(hi);
+  return ((unsigned long long)hi << 32) | lo;
 }
 
 constexpr int kChunk = 64;  // records staged per chunk (one per lane)
@@ -98,10 +117,8 @@ __device__ __forceinline__ Box alpha_box(float u, float v, float A, float B, flo
 }
 
 // Per-lane masks: bit e set iff record e's box contains the lane's pixel (lx, ly).  Lane e
-// holds record e's box; COL[x] / ROW[y] are ballots over the records.  *rows_out (optional)
-// gets ROW[ly], the records whose box meets the lane's pixel row.
-__device__ __forceinline__ unsigned long long lane_mask(const Box& b, int lx, int ly,
-                                                     unsigned long long* rows_out = nullptr) {
+// holds record e's box; COL[x] / ROW[y] are ballots over the records.
+__device__ __forceinline__ unsigned long long lane_mask(const Box& b, int lx, int ly) {
   unsigned long long col = 0ull, row = 0ull;
 #pragma unroll
   for (int x = 0; x < 8; ++x) {
@@ -112,9 +129,7 @@ __device__ __forceinline__ unsigned long long lane_mask(const Box& b, int lx, in
   for (int y = 0; y < 8; ++y) {
     const unsigned long long r = __ballot(b.y0 <= y && y <= b.y1);
     row = (ly == y) ? r : row;
-
   }
-  if (rows_out) *rows_out = row;
   return col & row;
 }
 
@@ -162,6 +177,13 @@ __device__ __forceinline__ Raw load_raw(const float4* __restrict__ splat, uint32
 // opacity of a loaded record as the blend sees it (0 past the end of a list)
 __device__ __forceinline__ float opacity_of(const Raw& r, int64_t n) {
   return (int64_t)r.gid < n ? r.abco.w : 0.f;
+}
+
+// Makes the compiler wait here for the loads of r (an empty asm statement that reads them), so a
+// chunk loop entered with r still in flight does not carry that wait into every pass.
+__device__ __forceinline__ void settle(const Raw& r) {
+  asm volatile("" ::"v"(r.uv.x), "v"(r.uv.y), "v"(r.abco.x), "v"(r.abco.y), "v"(r.abco.z), "v"(r.abco.w),
+               "v"(r.rgb.x), "v"(r.rgb.y), "v"(r.rgb.z));
 }
 
 __device__ __forceinline__ void put(Chunk& S, int e, const Raw& r) {
@@ -223,39 +245,53 @@ __global__ __launch_bounds__(kPlanThreads) void k_seg_plan(const uint2* __restri
                                                            uint32_t* __restrict__ item_off) {
   __shared__ unsigned long long red64[kPlanThreads / 64];
   __shared__ uint32_t red32[kPlanThreads / 64];
-  const int per = (T + kPlanThreads - 1) / kPlanThreads;
-  const int t0 = min(T, (int)threadIdx.x * per), t1 = min(T, t0 + per);
+  // tiles are visited in rounds of 1024 consecutive tiles (thread t takes tile r*1024 + t), so
+  // every load and store of a round is coalesced
+  const int rounds = (T + kPlanThreads - 1) / kPlanThreads;
   int shift = kSegShiftMin;
   for (;;) {  // every thread takes the same exit (the sum is block-wide)
     unsigned long long s = 0;
-    for (int t = t0; t < t1; ++t) {
-      const uint2 r = ranges[t];
-      const uint32_t len = r.y - r.x;
-      if (len > (1u << shift)) s += ((len - 1u) >> shift) + 1u;
+    for (int r = 0; r < rounds; ++r) {
+      const int t = r * kPlanThreads + (int)threadIdx.x;
+      if (t < T) {
+        const uint2 rg = ranges[t];
+        const uint32_t len = rg.y - rg.x;
+        if (len > (1u << shift)) s += ((len - 1u) >> shift) + 1u;
+      }
     }
     s = block_sum_1024(s, red64);
     if (s <= slots_cap || shift >= 31) break;
     ++shift;
   }
   const uint32_t seg = 1u << shift;
-  uint32_t my_slots = 0, my_items = 0;
-  for (int t = t0; t < t1; ++t) {
-    const uint2 r = ranges[t];
-    const uint32_t len = r.y - r.x, k = len ? ((len - 1u) >> shift) + 1u : 0u;
-    my_items += k;
-    my_slots += len > seg ? k : 0u;
+  uint32_t so = 0, io = 0;  // running totals of the rounds before
+  for (int r = 0; r < rounds; ++r) {
+    const int t = r * kPlanThreads + (int)threadIdx.x;
+    uint32_t len = 0;
+    if (t < T) {
+      const uint2 rg = ranges[t];
+      len = rg.y - rg.x;
+    }
+    const uint32_t k = len ? ((len - 1u) >> shift) + 1u : 0u;
+    const uint32_t sl = len > seg ? k : 0u;
+    const uint32_t pre_s = block_exscan_1024(sl, red32);
+    const uint32_t pre_i = block_exscan_1024(k, red32);
+    if (t < T) {
+      bnd_off[t] = so + pre_s;
+      item_off[t] = io + pre_i;
+    }
+    // the round's totals: the last thread's inclusive prefix, shared through LDS
+    __shared__ uint32_t s_tot[2];
+    if (threadIdx.x == kPlanThreads - 1) {
+      s_tot[0] = pre_s + sl;
+      s_tot[1] = pre_i + k;
+    }
+    __syncthreads();
+    so += s_tot[0];
+    io += s_tot[1];
+    __syncthreads();
   }
-  uint32_t so = block_exscan_1024(my_slots, red32);
-  uint32_t io = block_exscan_1024(my_items, red32);
-  for (int t = t0; t < t1; ++t) {
-    const uint2 r = ranges[t];
-    const uint32_t len = r.y - r.x, k = len ? ((len - 1u) >> shift) + 1u : 0u;
-    bnd_off[t] = so;
-    so += len > seg ? k : 0u;
-    item_off[t] = io;
-    io += k;
-  }
-  if (t1 == T && (t0 < t1 || threadIdx.x == 0)) {  // the thread that owns the last tile
+  if (threadIdx.x == 0) {
     bnd_off[T] = so;
     item_off[T] = io;
     hdr[0] = (uint32_t)shift;
@@ -288,7 +324,8 @@ __global__ __launch_bounds__(kBlock) void k_blend_forward(
     const uint32_t* __restrict__ vals, const uint2* __restrict__ ranges, float bg0, float bg1,
     float bg2, float* __restrict__ image, float* __restrict__ T_final, uint32_t* __restrict__ last_contrib,
     uint32_t* __restrict__ n_examined, unsigned long long* __restrict__ blend_count,
-    const uint32_t* __restrict__ ws_hdr, const uint32_t* __restrict__ bnd_off, float4* __restrict__ slots) {
+    const uint32_t* __restrict__ ws_hdr, const uint32_t* __restrict__ bnd_off, float4* __restrict__ slots,
+    uint2* __restrict__ masks, uint64_t mask_cap) {
   __shared__ Chunk stg[4];
   const int tile = blockIdx.x;  // consecutive tiles land on different XCDs: balances the load
   const int tx = tile % TX, ty = tile / TX;
@@ -303,7 +340,9 @@ __global__ __launch_bounds__(kBlock) void k_blend_forward(
   const uint32_t start = rg.x, end = rg.y, len = end - start;
   const uint32_t shift = ws_hdr[0], seg_mask = (1u << shift) - 1u;
   const bool long_list = len > seg_mask + 1u;
-  float4* const st = slots + (size_t)(long_list ? bnd_off[tile] : 0u) * (kTile * kTile) + tile_pixel(w, lx, ly);
+  const int pix = tile_pixel(w, lx, ly);
+  float4* const st = slots + (size_t)(long_list ? bnd_off[tile] : 0u) * (kTile * kTile) + pix;
+  const uint64_t cbase = (uint64_t)(start / kChunk) + (uint64_t)tile;  // the tile's first mask chunk
 
   float Tr = 1.0f, c0 = 0.f, c1 = 0.f, c2 = 0.f;
   uint32_t last = 0, examined = len, blended = 0;
@@ -313,8 +352,15 @@ __global__ __launch_bounds__(kBlock) void k_blend_forward(
     uint32_t gnext = load_gid(vals, start + lane, end, start);
     Raw cur = load_raw(splat, gnext, n);
     gnext = load_gid(vals, start + kChunk + lane, end, start);
+    // The first chunk has landed before the loop starts; each pass waits for the next chunk's
+    // loads only at its end.  A chunk's composited mask is stored at the start of the next
+    // pass, so that pass's work covers the store's latency.
+    settle(cur);
+    unsigned long long pend = 0ull;
+    uint64_t pend_mc = ~0ull;
     for (uint32_t b0 = start; b0 < end; b0 += kChunk) {
       if (__ballot(!done) == 0ull) break;
+      if (pend_mc < mask_cap) masks[pend_mc * (kTile * kTile) + pix] = make_uint2((uint32_t)pend, (uint32_t)(pend >> 32));
       const Raw nxt = load_raw(splat, gnext, n);  // next chunk in flight
       gnext = load_gid(vals, b0 + 2 * kChunk + lane, end, start);
       const uint32_t rel = b0 - start;
@@ -327,6 +373,7 @@ __global__ __launch_bounds__(kBlock) void k_blend_forward(
       if (done) m = 0ull;
       wave_sync_lds();
       const uint32_t base = rel + 1u;  // 1-based position of slot 0
+      unsigned long long cm = 0ull;    // the chunk's entries composited at this pixel
       while (m) {  // this lane's records, in list order
         const int e = lowest_bit(m);
         m &= m - 1ull;
@@ -351,12 +398,16 @@ __global__ __launch_bounds__(kBlock) void k_blend_forward(
             Tr = Tn;
             last = pos;
             ++blended;
+            cm |= 1ull << e;
           }
         }
       }
+      pend = cm;
+      pend_mc = cbase + rel / kChunk;
       wave_sync_lds();  // this chunk's reads finish before the next chunk is staged
       cur = nxt;
     }
+    if (pend_mc < mask_cap) masks[pend_mc * (kTile * kTile) + pix] = make_uint2((uint32_t)pend, (uint32_t)(pend >> 32));
     if (long_list)  // final state
       st[(size_t)((len - 1u) >> shift) * (kTile * kTile)] = make_float4(Tr, c0, c1, c2);
   }
@@ -400,9 +451,9 @@ __global__ __launch_bounds__(kBlock) void k_blend_forward(
 // behind it, (C_final - C_boundary) / T_boundary; otherwise from T_final with nothing behind.
 // The segments of one tile are independent, so a long list is spread over many CUs.
 // Persistent workgroups take items from a counter in the workspace until none are left.
-// The waves of a workgroup add their per-entry gradient sums into one LDS window of 256
-// entries; one global atomic per entry and value then adds the window to grad2d, so a record
-// that reaches several quadrants costs one set of atomics.
+// Each pixel row walks the entries its pixels composited (the forward's masks), back to front;
+// the row's nine gradient sums per entry go into the workgroup's LDS sums over a window of 256
+// entries, whose sums then go to the staging area, one row per (entry, tile).
 // ---------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(kBlock) void k_blend_backward(
     int W, int H, int TX, int TY, int64_t n, const float4* __restrict__ splat,
@@ -410,7 +461,8 @@ __global__ __launch_bounds__(kBlock) void k_blend_backward(
     float bg2, const float* __restrict__ T_final, const uint32_t* __restrict__ last_contrib,
     const float* __restrict__ dLdI, uint32_t* __restrict__ ws_hdr,
     const uint32_t* __restrict__ bnd_off, const uint2* __restrict__ items,
-    const float4* __restrict__ slots, const uint32_t* __restrict__ goff,
+    const float4* __restrict__ slots, const uint2* __restrict__ masks, uint64_t mask_cap,
+    const uint32_t* __restrict__ goff,
     const uint32_t* __restrict__ goff_blk, float* __restrict__ staging, uint64_t staging_cap) {
   __shared__ Chunk stg[4];              // per quadrant wave: its current chunk
   __shared__ float acc[9][kWin];        // the workgroup's gradient sums over a window of entries
@@ -436,7 +488,8 @@ __global__ __launch_bounds__(kBlock) void k_blend_backward(
     const bool inside = px < W && py < H;
     const float pxc = (float)px + 0.5f, pyc = (float)py + 0.5f;
     const uint2 rg = ranges[tile];
-    const uint32_t start = rg.x, len = rg.y - rg.x;
+    const uint32_t start = rg.x, end = rg.y, len = rg.y - rg.x;
+    const uint64_t cbase = (uint64_t)(start / kChunk) + (uint64_t)tile;  // the tile's first mask chunk
 
     float Tr = 0.f, g0 = 0.f, g1 = 0.f, g2 = 0.f, bgT = 0.f;
     float S0 = 0.f, S1 = 0.f, S2 = 0.f;  // colour accumulated behind the current entry, / T_{k+1}
@@ -480,38 +533,36 @@ __global__ __launch_bounds__(kBlock) void k_blend_backward(
       __syncthreads();
       const uint32_t whi = min(wtop, hi_w);
       if (whi > wlo) {  // wave-uniform
-        const uint32_t lo_abs = start + wlo, hi_abs = start + whi;
-        const uint32_t nchunks = (whi - wlo + kChunk - 1) / kChunk;
-        // chunk c covers [lo_c, hi_abs - 64 c) with lo_c = max(hi_abs - 64 (c+1), lo_abs)
-        auto lo_of = [&](uint32_t c) -> uint32_t {
-          const uint32_t hi = hi_abs - c * kChunk;
-          return hi - lo_abs > (uint32_t)kChunk ? hi - kChunk : lo_abs;
-        };
-        // positions for chunk c (>= nchunks: none), clamped into [lo_abs, hi_abs)
+        // the window's chunks j (tile-relative entries [64 j, 64 j + 64)), top down
+        const uint32_t jlo = wlo / kChunk, jtop = (whi - 1u) / kChunk, nchunks = jtop - jlo + 1u;
+        // list entry of lane `lane` in chunk c (c >= nchunks: past the end of the list)
         auto gid_of = [&](uint32_t c) -> uint32_t {
-          const bool real = c < nchunks;
-          const uint32_t lo = real ? lo_of(c) : lo_abs;
-          const uint32_t hi = real ? hi_abs - c * kChunk : lo_abs;
-          return load_gid(vals, lo + lane, hi, lo_abs);
+          return load_gid(vals, c < nchunks ? start + (jtop - c) * kChunk + lane : end, end, start);
+        };
+        auto mask_of = [&](uint32_t c) -> uint2 {
+          const uint64_t mc = cbase + (c < nchunks ? jtop - c : jtop);
+          return masks[(mc < mask_cap ? mc : 0) * (kTile * kTile) + pix];
         };
         uint32_t gnext = gid_of(0);
         Raw cur = load_raw(splat, gnext, n);
+        uint2 mcur = mask_of(0);
         gnext = gid_of(1);
         for (uint32_t c = 0; c < nchunks; ++c) {
-          const uint32_t lo = lo_of(c);
+          const uint32_t j = jtop - c;
           const Raw nxt = load_raw(splat, gnext, n);  // next chunk in flight
+          const uint2 mnxt = mask_of(c + 1);
           gnext = gid_of(c + 2);
           put(S, lane, cur);
-          const Box bx = alpha_box(cur.uv.x, cur.uv.y, cur.abco.x, cur.abco.y, cur.abco.z, opacity_of(cur, n), xq, yq);
-          unsigned long long rem;  // records whose box meets this lane's pixel row
-          const unsigned long long m = lane_mask(bx, lx, ly, &rem);  // all lanes take part in the ballots
           wave_sync_lds();
-          const uint32_t base = lo - start;  // 0-based list position of slot 0
-          const uint32_t wbase = lo - lo_abs;  // window position of slot 0
-          // Each pixel row of the quadrant (8 lanes) takes the records reaching it back to
-          // front, its lanes on the same record; a lane takes part when the record's box holds
-          // its pixel and the record lies before its last blended entry.  The row's nine sums
-          // are formed in registers and added to the window's sums by one lane of the row.
+          // The entries this pixel composited in the chunk (the forward's mask): exactly those
+          // with power <= 0, alpha >= 1/255 in front of the pixel's stop.  Each pixel row of the
+          // quadrant (8 lanes) takes the entries any of its pixels composited, back to front,
+          // its lanes on the same entry; the row's nine sums are formed in registers and added
+          // to the window's sums by one lane of the row.
+          const unsigned long long mine =
+              cbase + j < mask_cap ? ((unsigned long long)mcur.y << 32) | mcur.x : 0ull;
+          unsigned long long rem = row8_or(mine);
+          const uint32_t wbase = j * kChunk - wlo;  // window position of slot 0
           for (;;) {
             const bool has = rem != 0ull;
             if (__ballot(has) == 0ull) break;
@@ -525,10 +576,7 @@ __global__ __launch_bounds__(kBlock) void k_blend_backward(
             const float G = __expf(power);
             const float oG = __fmul_rn(cl.y, G);  // the same operations as eval_oG
             const float alpha = fminf(kAlphaMax, oG);
-            const bool act = has && ((m >> e) & 1ull) && base + (uint32_t)e < last && power <= 0.0f &&
-                             alpha >= kAlphaMin;
-            const unsigned long long acts = __ballot(act);
-            if (acts == 0ull) continue;
+            const bool act = has && ((mine >> e) & 1ull);
             const float om = 1.0f - alpha;
             const float rom = __builtin_amdgcn_rcpf(om);  // om >= 0.01
             const float Tk = Tr * rom;                    // transmittance in front of this entry
@@ -555,7 +603,7 @@ __global__ __launch_bounds__(kBlock) void k_blend_backward(
               Tr = Tk;
             }
             row8_sum<9>(v);  // every lane of a pixel row holds the row's sums
-            if (lx == 0 && ((acts >> (ly * 8)) & 0xFFull)) {
+            if (lx == 0 && has) {
               // dL/du = (A m_x + B m_y), dL/dv = (B m_x + C m_y), dL/dA = -m_xx / 2,
               // dL/dB = -m_xy, dL/dC = -m_yy / 2 with A = -2 nA, B = -nB, C = -2 nC
               const uint32_t ws = wbase + (uint32_t)e;
@@ -570,6 +618,7 @@ __global__ __launch_bounds__(kBlock) void k_blend_backward(
           }
           wave_sync_lds();  // this chunk's reads finish before the next chunk is staged
           cur = nxt;
+          mcur = mnxt;
         }
       }
       __syncthreads();
@@ -700,17 +749,23 @@ int cu_count() {
 
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 constexpr size_t kSlotBytes = sizeof(float4) * kTile * kTile;
+constexpr size_t kMaskChunkBytes = sizeof(uint2) * kTile * kTile;  // one 64-bit mask per pixel
 constexpr uint64_t kSegEntries = 1u << kSegShiftMin;
 
 size_t n_goff_blocks(int64_t n) { return (size_t)((n + kGoffBlock - 1) / kGoffBlock); }
 
 // bytes of the layout for T tiles, n Gaussians and k staged entries (k a multiple of 256)
+// (tile t's 64-entry chunks start at ranges[t].x / 64 + t, so K entries need at most
+// K / 64 + T mask chunks)
 size_t layout_bytes(int T, int64_t n, uint64_t k) {
   const size_t slots = (size_t)T + (size_t)(k / kSegEntries);
+  const size_t chunks = (size_t)T + (size_t)(k / kChunk);
   return 256 + 2 * round256(4 * (size_t)(T + 1)) + round256(4 * (size_t)n) + round256(4 * (n_goff_blocks(n) + 1)) +
-         round256(8 * ((size_t)T + slots)) + round256(kSlotBytes * slots) + round256(36 * (size_t)k + 16);
+         round256(8 * ((size_t)T + slots)) + round256(kSlotBytes * slots) + kMaskChunkBytes * chunks +
+         round256(36 * (size_t)k + 16);
 }
-constexpr size_t kBytesPerSeg = kSlotBytes + 8 + 36 * kSegEntries;  // per 256 entries of capacity
+// per 256 entries of capacity
+constexpr size_t kBytesPerSeg = kSlotBytes + 8 + (kSegEntries / kChunk) * kMaskChunkBytes + 36 * kSegEntries;
 
 }  // namespace
 
@@ -743,8 +798,12 @@ bool render_ws_layout(void* ws, size_t bytes, int T, int64_t n, RenderWs* out) {
   b += round256(8 * ((size_t)T + slots));
   out->slots = reinterpret_cast<float4*>(b);
   b += round256(kSlotBytes * slots);
+  const size_t chunks = (size_t)T + (size_t)(k / kChunk);
+  out->masks = reinterpret_cast<uint2*>(b);
+  b += kMaskChunkBytes * chunks;
   out->staging = reinterpret_cast<float*>(b);
   out->slots_cap = (uint32_t)slots;
+  out->mask_cap = chunks;
   out->staging_cap = k;
   return true;
 }
@@ -763,7 +822,7 @@ hipError_t launch_blend_forward(const CamK& cam, int64_t n, const gs_splat* spla
   hipLaunchKernelGGL(k_blend_forward, dim3(T), dim3(kBlock), 0, s, cam.W, cam.H, cam.TX, T, n,
                      reinterpret_cast<const float4*>(splat), vals, rg, bg0, bg1, bg2, image, T_final,
                      last_contrib, n_examined, reinterpret_cast<unsigned long long*>(blend_count),
-                     (const uint32_t*)ws.hdr, (const uint32_t*)ws.bnd_off, ws.slots);
+                     (const uint32_t*)ws.hdr, (const uint32_t*)ws.bnd_off, ws.slots, ws.masks, ws.mask_cap);
   return hipGetLastError();
 }
 
@@ -788,8 +847,8 @@ hipError_t launch_blend_backward(const CamK& cam, int64_t n, const gs_splat* spl
   hipLaunchKernelGGL(k_blend_backward, dim3(grid), dim3(kBlock), 0, s, cam.W, cam.H, cam.TX, cam.TY, n,
                      reinterpret_cast<const float4*>(splat), vals, reinterpret_cast<const uint2*>(ranges),
                      bg0, bg1, bg2, T_final, last_contrib, dLdI, ws.hdr, (const uint32_t*)ws.bnd_off,
-                     (const uint2*)ws.items, (const float4*)ws.slots, (const uint32_t*)ws.goff,
-                     (const uint32_t*)ws.goff_blk, ws.staging, ws.staging_cap);
+                     (const uint2*)ws.items, (const float4*)ws.slots, (const uint2*)ws.masks, ws.mask_cap,
+                     (const uint32_t*)ws.goff, (const uint32_t*)ws.goff_blk, ws.staging, ws.staging_cap);
   hipLaunchKernelGGL(k_gather_grad2d, dim3((unsigned)ceil_div(n, (int64_t)kBlock)), dim3(kBlock), 0, s, n, tiles,
                      (const uint32_t*)ws.goff, (const uint32_t*)ws.goff_blk, (const float*)ws.staging,
                      ws.staging_cap, grad2d);

@@ -101,6 +101,9 @@ hipError_t launch_bin_sort_rest(int64_t n, int64_t K, const BinInfo& info, const
 //   goff_blk[]      exclusive scan of the block totals
 //   items[]         (tile, segment) work items of the backward, tile-major
 //   slots[][256]    float4 states
+//   masks[][256]    per 64-entry chunk of a tile list and pixel of the tile: the chunk's
+//                   entries the forward composited at that pixel (64-bit, as uint2 lo, hi);
+//                   tile t's chunk j is at (ranges[t].x / 64 + t + j)
 //   staging[][9]    per-entry gradient sums
 constexpr int kSegShiftMin = 8;  // 256 list entries per segment
 constexpr int kGoffBlock = 4096;
@@ -112,8 +115,10 @@ struct RenderWs {
   uint32_t* goff_blk;
   uint2* items;
   float4* slots;
+  uint2* masks;
   float* staging;
   uint32_t slots_cap;
+  uint64_t mask_cap;     // chunks
   uint64_t staging_cap;  // entries
 };
 size_t render_ws_bytes(int T, int64_t n, int64_t k_capacity);

@@ -156,8 +156,11 @@ int gs_bin_and_sort(const gs_scene* scene, const gs_camera* cam, gs_proj proj, v
  * query).  It holds, for every tile list longer than one segment (256 entries), each pixel's
  * transmittance and colour at every segment boundary and at the end of its walk, plus the
  * backward's work list: the backward walks the segments of a long list in parallel from these
- * states.  It also holds the backward's per-intersection gradient sums (36 bytes each), which
- * are summed per Gaussian into grad2d instead of accumulating grad2d with atomics. */
+ * states.  For every 64 entries of a tile list and pixel of the tile it holds the 64-bit mask
+ * of the entries the forward composited at that pixel (8 bytes per pixel per 64 entries), so
+ * the backward revisits exactly those.  It also holds the backward's per-intersection gradient
+ * sums (36 bytes each), which are summed per Gaussian into grad2d instead of accumulating
+ * grad2d with atomics. */
 int gs_render_workspace(int32_t width, int32_t height, int64_t n, int64_t k_capacity, size_t* bytes);
 
 /* The largest intersection count a render workspace of `bytes` serves for this image and n
@@ -199,14 +202,12 @@ int gs_loss_l1(int64_t count, const float* image, const float* target, float* lo
                float* dL_dimage, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Backward of the step from dL/dimage.
- *   grad2d[ld][9]  out: per-Gaussian dL/d(u, v, conic_a, conic_b, conic_c, opacity, r, g, b),
- *                  the nine values of Gaussian i at grad2d + 9 i, for i < n (rows n..ld-1 are
- *                  not written).  Each intersection's sums are staged in render_ws and each
- *                  Gaussian's are added in the order of its tile rect; within an intersection
- *                  the pixel contributions meet in LDS atomics, so the summation order is not
- *                  fixed.
- *                  from the reverse-order backward blend (zeroed inside, then accumulated
- *                  with float atomics, so the summation order is not fixed)
+ *   grad2d[ld][9]  out: per-Gaussian dL/d(u, v, conic_a, conic_b, conic_c, opacity, r, g, b)
+ *                  from the reverse-order backward blend, the nine values of Gaussian i at
+ *                  grad2d + 9 i, for i < n (rows n..ld-1 are not written).  Each
+ *                  intersection's sums are staged in render_ws and each Gaussian's are added
+ *                  in the order of its tile rect; within an intersection the pixel-row sums
+ *                  meet in LDS atomics, so the summation order is not fixed.
  *   grads[R][ld]   out, nullable: dL/dparams by the chain rule through the preprocess
  *   adam           nullable: when given, the preprocess backward also applies the Adam
  *                  update to params, adam->m and adam->v in place (params is then written)

@@ -77,11 +77,12 @@ def test_workspace_queries():
     with pytest.raises(gsmi.GsError):
         gsmi.bin_and_sort_workspace(-1, 0, 16, 16)
     # render workspace: a fixed part for the tiles and Gaussians plus, per 256 intersections of
-    # capacity, one 4 KiB state slot, one work item and 256 staged 36-byte gradient sums
+    # capacity, one 4 KiB state slot, one work item, four 2 KiB chunks of composited masks (8
+    # bytes per pixel of a tile per 64 entries) and 256 staged 36-byte gradient sums
     r0 = gsmi.render_workspace(2048, 2048, 4_000_000, 0)
     r1 = gsmi.render_workspace(2048, 2048, 4_000_000, 256 * 1000)
-    assert abs((r1 - r0) - 1000 * (4096 + 8 + 256 * 36)) <= 512
-    assert r0 >= 16384 * (4096 + 8 + 4) + 4 * 4_000_000
+    assert abs((r1 - r0) - 1000 * (4096 + 8 + 4 * 2048 + 256 * 36)) <= 512
+    assert r0 >= 16384 * (4096 + 8 + 2048 + 4) + 4 * 4_000_000
     with pytest.raises(gsmi.GsError):
         gsmi.render_workspace(0, 16, 10, 10)
     # the capacity query inverts the size query: never below the capacity asked for, and no
