@@ -210,6 +210,9 @@ __device__ __forceinline__ int highest_bit(unsigned long long m) { return 63 - _
 // Writes bnd_off (exclusive scan of slots), the item list and the header.
 // ---------------------------------------------------------------------------------------------
 constexpr int kPlanThreads = 1024;
+// list-length classes: 0 for an empty list, else 1 + floor(log2 len)
+constexpr int kLenClasses = 33;
+__device__ __forceinline__ int len_class(uint32_t len) { return len ? 32 - __clz((int)len) : 0; }
 
 template <typename U>
 __device__ U block_sum_1024(U x, U* red) {
@@ -242,9 +245,12 @@ __device__ uint32_t block_exscan_1024(uint32_t x, uint32_t* red) {
 __global__ __launch_bounds__(kPlanThreads) void k_seg_plan(const uint2* __restrict__ ranges, int T,
                                                            uint32_t slots_cap, uint32_t* __restrict__ hdr,
                                                            uint32_t* __restrict__ bnd_off,
-                                                           uint32_t* __restrict__ item_off) {
+                                                           uint32_t* __restrict__ item_off,
+                                                           uint32_t* __restrict__ order) {
   __shared__ unsigned long long red64[kPlanThreads / 64];
   __shared__ uint32_t red32[kPlanThreads / 64];
+  __shared__ uint32_t cls[kLenClasses];  // tiles per list-length class, then the classes' cursors
+  if (threadIdx.x < kLenClasses) cls[threadIdx.x] = 0u;
   // tiles are visited in rounds of 1024 consecutive tiles (thread t takes tile r*1024 + t), so
   // every load and store of a round is coalesced
   const int rounds = (T + kPlanThreads - 1) / kPlanThreads;
@@ -272,6 +278,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_seg_plan(const uint2* __restri
       const uint2 rg = ranges[t];
       len = rg.y - rg.x;
     }
+    if (t < T) atomicAdd(&cls[len_class(len)], 1u);
     const uint32_t k = len ? ((len - 1u) >> shift) + 1u : 0u;
     const uint32_t sl = len > seg ? k : 0u;
     const uint32_t pre_s = block_exscan_1024(sl, red32);
@@ -290,6 +297,23 @@ __global__ __launch_bounds__(kPlanThreads) void k_seg_plan(const uint2* __restri
     so += s_tot[0];
     io += s_tot[1];
     __syncthreads();
+  }
+  // the forward's tile order: list-length classes, longest first (within a class, any order)
+  if (threadIdx.x == 0) {
+    uint32_t run = 0;
+    for (int c = kLenClasses - 1; c >= 0; --c) {
+      const uint32_t v = cls[c];
+      cls[c] = run;
+      run += v;
+    }
+  }
+  __syncthreads();
+  for (int r = 0; r < rounds; ++r) {
+    const int t = r * kPlanThreads + (int)threadIdx.x;
+    if (t < T) {
+      const uint2 rg = ranges[t];
+      order[atomicAdd(&cls[len_class(rg.y - rg.x)], 1u)] = (uint32_t)t;
+    }
   }
   if (threadIdx.x == 0) {
     bnd_off[T] = so;
@@ -325,9 +349,12 @@ __global__ __launch_bounds__(kBlock) void k_blend_forward(
     float bg2, float* __restrict__ image, float* __restrict__ T_final, uint32_t* __restrict__ last_contrib,
     uint32_t* __restrict__ n_examined, unsigned long long* __restrict__ blend_count,
     const uint32_t* __restrict__ ws_hdr, const uint32_t* __restrict__ bnd_off, float4* __restrict__ slots,
-    uint2* __restrict__ masks, uint64_t mask_cap) {
+    uint2* __restrict__ masks, uint64_t mask_cap, const uint32_t* __restrict__ order) {
   __shared__ Chunk stg[4];
-  const int tile = blockIdx.x;  // consecutive tiles land on different XCDs: balances the load
+  // Longest lists first: a tile's waves walk its list alone, so the longest walks start at once
+  // and the short tiles fill in around them; consecutive workgroups (dealt to the 8 XCDs in
+  // turn) get lists of similar length.
+  const int tile = (int)order[blockIdx.x];
   const int tx = tile % TX, ty = tile / TX;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   Chunk& S = stg[w];
@@ -760,7 +787,8 @@ size_t n_goff_blocks(int64_t n) { return (size_t)((n + kGoffBlock - 1) / kGoffBl
 size_t layout_bytes(int T, int64_t n, uint64_t k) {
   const size_t slots = (size_t)T + (size_t)(k / kSegEntries);
   const size_t chunks = (size_t)T + (size_t)(k / kChunk);
-  return 256 + 2 * round256(4 * (size_t)(T + 1)) + round256(4 * (size_t)n) + round256(4 * (n_goff_blocks(n) + 1)) +
+  return 256 + 2 * round256(4 * (size_t)(T + 1)) + round256(4 * (size_t)T) + round256(4 * (size_t)n) +
+         round256(4 * (n_goff_blocks(n) + 1)) +
          round256(8 * ((size_t)T + slots)) + round256(kSlotBytes * slots) + kMaskChunkBytes * chunks +
          round256(36 * (size_t)k + 16);
 }
@@ -790,6 +818,8 @@ bool render_ws_layout(void* ws, size_t bytes, int T, int64_t n, RenderWs* out) {
   b += round256(4 * (size_t)(T + 1));
   out->item_off = reinterpret_cast<uint32_t*>(b);
   b += round256(4 * (size_t)(T + 1));
+  out->order = reinterpret_cast<uint32_t*>(b);
+  b += round256(4 * (size_t)T);
   out->goff = reinterpret_cast<uint32_t*>(b);
   b += round256(4 * (size_t)n);
   out->goff_blk = reinterpret_cast<uint32_t*>(b);
@@ -816,13 +846,14 @@ hipError_t launch_blend_forward(const CamK& cam, int64_t n, const gs_splat* spla
   const int T = cam.TX * cam.TY;
   const uint2* rg = reinterpret_cast<const uint2*>(ranges);
   hipLaunchKernelGGL(k_seg_plan, dim3(1), dim3(kPlanThreads), 0, s, rg, T, ws.slots_cap, ws.hdr, ws.bnd_off,
-                     ws.item_off);
+                     ws.item_off, ws.order);
   hipLaunchKernelGGL(k_seg_items, dim3((unsigned)ceil_div(T, kBlock / 64)), dim3(kBlock), 0, s, T,
                      (const uint32_t*)ws.item_off, ws.items);
   hipLaunchKernelGGL(k_blend_forward, dim3(T), dim3(kBlock), 0, s, cam.W, cam.H, cam.TX, T, n,
                      reinterpret_cast<const float4*>(splat), vals, rg, bg0, bg1, bg2, image, T_final,
                      last_contrib, n_examined, reinterpret_cast<unsigned long long*>(blend_count),
-                     (const uint32_t*)ws.hdr, (const uint32_t*)ws.bnd_off, ws.slots, ws.masks, ws.mask_cap);
+                     (const uint32_t*)ws.hdr, (const uint32_t*)ws.bnd_off, ws.slots, ws.masks, ws.mask_cap,
+                     (const uint32_t*)ws.order);
   return hipGetLastError();
 }
 

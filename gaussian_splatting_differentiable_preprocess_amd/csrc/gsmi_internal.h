@@ -96,6 +96,7 @@ hipError_t launch_bin_sort_rest(int64_t n, int64_t K, const BinInfo& info, const
 //   hdr[3] = work-item counter of the backward, hdr[4] = entries (sum of tiles)
 //   bnd_off[T + 1]  first slot of each tile
 //   item_off[T + 1] first work item of each tile
+//   order[T]        the forward's tile order: list-length classes (log2), longest first
 //   goff[n]         exclusive scan of tiles within blocks of kGoffBlock Gaussians; goff(i) =
 //                   goff_blk[i / kGoffBlock] + goff[i]
 //   goff_blk[]      exclusive scan of the block totals
@@ -111,6 +112,7 @@ struct RenderWs {
   uint32_t* hdr;
   uint32_t* bnd_off;
   uint32_t* item_off;
+  uint32_t* order;
   uint32_t* goff;
   uint32_t* goff_blk;
   uint2* items;

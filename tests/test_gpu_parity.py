@@ -392,6 +392,49 @@ def test_repeatable_forward_and_sort():
         np.testing.assert_array_equal(a["fwd"][k], b["fwd"][k])
 
 
+def test_long_lists_with_stops_in_many_segments():
+    """Tile lists of 6000 entries (24 segments of 256) with opacities spread so that pixels stop
+    in many different segments and some never stop: the forward's segment-boundary states and
+    composited masks, and the backward's segments started from them, are exercised at every
+    depth.  Forward outputs (image, T, last_contrib, n_examined) and the backward blend are
+    checked against the oracle on the same records and lists."""
+    import torch
+    say("[parity] test_long_lists_with_stops_in_many_segments")
+    n, W = 6000, 32
+    params = inputs.small_scene(37, n, 0, logscale_mean=-0.8, logscale_std=0.2, radius=0.1)
+    rng = np.random.default_rng(38)
+    params[10] = rng.uniform(-6.0, -4.0, n).astype(np.float32)  # opacity 0.0025 .. 0.018
+    # (on these inputs about 16% of the pixels stop, in segments 5 to 23 of 24)
+    cam = inputs.lookat_camera((3.0, 0.0, 0.0), W, W)
+    up = np.random.default_rng(6).uniform(-1, 1, (W, W, 3)).astype(np.float32)
+    o = oracle_pipeline(params, 0, cam.flat(), W, W, BG, upstream=up, margins=FWD_MARGINS)
+    lens = o["ranges"][:, 1].astype(np.int64) - o["ranges"][:, 0]
+    of = o["fwd"]
+    stopped = of["n_examined"] < lens.reshape(2, 2).repeat(16, 0).repeat(16, 1)
+    assert lens.max() > 16 * 256, lens
+    assert 0.05 < stopped.mean() < 0.95, stopped.mean()  # some pixels stop, some walk the whole list
+    assert len(np.unique((of["n_examined"][stopped] - 1) // 256)) > 8  # in many different segments
+    g = GpuStep(params, 0, cam, W, W)
+    g.load_proj(*records_from_oracle(o["p32"], o["radii"], o["tiles"]))
+    g.load_lists(o["vals"], o["ranges"])
+    fwd = g.forward(BG)
+    hdr = g.render_ws[:64].cpu().numpy().view(np.uint32)
+    assert hdr[0] == 8, hdr[:4]  # 256-entry segments
+    ok = ~of["borderline"]
+    assert ok.mean() > 0.9
+    assert np.abs(fwd["image"] - of["image"]).max(axis=-1)[ok].max() <= IMG_MAX_ABS
+    assert np.abs(fwd["T_final"] - of["T_final"])[ok].max() <= 1e-5
+    np.testing.assert_array_equal(fwd["last_contrib"][ok], of["last_contrib"][ok])
+    np.testing.assert_array_equal(fwd["n_examined"][ok], of["n_examined"][ok])
+    g.set_upstream(o["dl32"])
+    g2, _ = g.backward()
+    errs = [rel_l2(g2[r, :n], o["grad2d"][r]) for r in range(9)]
+    say(f"[parity]   long lists: max list {lens.max()}, {stopped.mean():.2f} of pixels stop, "
+        f"backward rel-L2 max {max(errs):.2e}")
+    assert max(errs) <= GRAD_REL_L2, errs
+    torch.cuda.synchronize()
+
+
 def test_backward_segments_on_deep_lists():
     """Tile lists of ~3000 entries with low opacity: pixels walk back across several 256-entry
     segments, which the backward runs in parallel from the forward's boundary states.  The GPU
