@@ -286,30 +286,29 @@ __device__ __forceinline__ uint32_t rect_count(uint2 r) {
   return (x1 > x0 && y1 > y0) ? (x1 - x0) * (y1 - y0) : 0u;
 }
 
-// rect_sorted[k] = tile rect of Gaussian order[k] (packed 16-bit x0|y0, x1|y1); bsum[block] =
-// intersections of the block's items.
+// rect_sorted[k] = tile rect of Gaussian order[k] (packed 16-bit x0|y0, x1|y1, from the
+// preprocess); bsum[block] = intersections of the block's items.  The gather reads the dense
+// 8-byte rect array, not the 48-byte records.
 __global__ __launch_bounds__(kBlock) void k_gather_rect(const uint32_t* __restrict__ order, int64_t n,
-                                                         const float4* __restrict__ splat, int TX,
-                                                         int TY, uint2* __restrict__ rect_sorted,
+                                                         const uint2* __restrict__ rect,
+                                                         uint2* __restrict__ rect_sorted,
                                                          uint32_t* __restrict__ bsum) {
   __shared__ uint32_t tmp[4];
-  const int64_t base = (int64_t)blockIdx.x * kGatherTile + (int64_t)threadIdx.x * kGatherItems;
+  // item j of thread t is base + j kBlock + t: every load and store of a round is coalesced
+  const int64_t base = (int64_t)blockIdx.x * kGatherTile + threadIdx.x;
   uint32_t s = 0;
+  uint2 r[kGatherItems];
+#pragma unroll
+  for (int j = 0; j < kGatherItems; ++j) {  // every gather in flight before the first use
+    const int64_t k = base + (int64_t)j * kBlock;
+    r[j] = k < n ? rect[order[k]] : make_uint2(0u, 0u);
+  }
 #pragma unroll
   for (int j = 0; j < kGatherItems; ++j) {
-    const int64_t k = base + j;
+    const int64_t k = base + (int64_t)j * kBlock;
     if (k < n) {
-      const uint32_t i = order[k];
-      const float4 q0 = splat[3 * (int64_t)i];  // u, v, radius_x, radius_y
-      const int rx = __float_as_int(q0.z), ry = __float_as_int(q0.w);
-      uint2 r = make_uint2(0u, 0u);
-      if (rx > 0 && ry > 0) {
-        int x0, y0, x1, y1;
-        tile_rect(q0.x, q0.y, rx, ry, TX, TY, x0, y0, x1, y1);
-        r = make_uint2((uint32_t)x0 | ((uint32_t)y0 << 16), (uint32_t)x1 | ((uint32_t)y1 << 16));
-      }
-      rect_sorted[k] = r;
-      s += rect_count(r);
+      rect_sorted[k] = r[j];
+      s += rect_count(r[j]);
     }
   }
   uint32_t tot;
@@ -341,35 +340,38 @@ __global__ __launch_bounds__(1024) void k_scan_blocks(uint32_t* __restrict__ bsu
 }
 
 // Writes the intersections of Gaussians order[k] (in depth order) at their scanned slots:
-// tile id (row-major over the rect) and Gaussian index.  Writes past kcap are dropped.
+// tile id (row-major over the rect) and Gaussian index.  Writes past kcap are dropped.  The
+// block's items go in rounds of kBlock consecutive items, so the loads are coalesced and the
+// threads of a round write neighbouring slots.
 __global__ __launch_bounds__(kBlock) void k_keygen(const uint2* __restrict__ rect_sorted,
                                                     const uint32_t* __restrict__ order, int64_t n,
                                                     const uint32_t* __restrict__ bsum, int TX,
                                                     int64_t kcap, uint32_t* __restrict__ tkeys,
                                                     uint32_t* __restrict__ tvals) {
   __shared__ uint32_t tmp[4];
-  const int64_t base = (int64_t)blockIdx.x * kGatherTile + (int64_t)threadIdx.x * kGatherItems;
+  const int64_t base = (int64_t)blockIdx.x * kGatherTile + threadIdx.x;
   uint2 r[kGatherItems];
-  uint32_t s = 0;
+  uint32_t gi[kGatherItems];
 #pragma unroll
   for (int j = 0; j < kGatherItems; ++j) {
-    r[j] = (base + j < n) ? rect_sorted[base + j] : make_uint2(0u, 0u);
-    s += rect_count(r[j]);
+    const int64_t k = base + (int64_t)j * kBlock;
+    r[j] = k < n ? rect_sorted[k] : make_uint2(0u, 0u);
+    gi[j] = k < n ? order[k] : 0u;
   }
-  uint32_t tot;
-  const uint32_t pre = block_excl_scan(s, tmp, &tot);
-  int64_t slot = (int64_t)bsum[blockIdx.x] + pre;
+  int64_t run = bsum[blockIdx.x];  // slots of the block's earlier rounds
 #pragma unroll
   for (int j = 0; j < kGatherItems; ++j) {
     const uint32_t c = rect_count(r[j]);
+    uint32_t tot;
+    int64_t slot = run + block_excl_scan(c, tmp, &tot);
+    run += tot;
     if (c == 0) continue;
-    const uint32_t i = order[base + j];
     const uint32_t x0 = r[j].x & 0xFFFFu, y0 = r[j].x >> 16, x1 = r[j].y & 0xFFFFu, y1 = r[j].y >> 16;
     for (uint32_t ty = y0; ty < y1; ++ty)
       for (uint32_t tx = x0; tx < x1; ++tx) {
         if (slot < kcap) {
           tkeys[slot] = ty * (uint32_t)TX + tx;
-          tvals[slot] = i;
+          tvals[slot] = gi[j];
         }
         ++slot;
       }
@@ -507,9 +509,8 @@ hipError_t launch_bin_sort_rest(int64_t n, int64_t K, const BinInfo& info, const
   uint2* rect = reinterpret_cast<uint2*>(ws + L.rect);
   uint32_t* bsum = reinterpret_cast<uint32_t*>(ws + L.bsum);
   const int64_t nb = ceil_div(n, kGatherTile);
-  const float4* sp = reinterpret_cast<const float4*>(proj.splat);
-  hipLaunchKernelGGL(k_gather_rect, dim3((unsigned)nb), dim3(kBlock), 0, s, order, n, sp, cam.TX,
-                     cam.TY, rect, bsum);
+  hipLaunchKernelGGL(k_gather_rect, dim3((unsigned)nb), dim3(kBlock), 0, s, order, n,
+                     reinterpret_cast<const uint2*>(proj.rect), rect, bsum);
   hipLaunchKernelGGL(k_scan_blocks, dim3(1), dim3(1024), 0, s, bsum, nb);
   uint32_t* tkA = reinterpret_cast<uint32_t*>(ws + L.tkA);
   uint32_t* tvA = reinterpret_cast<uint32_t*>(ws + L.tvA);

@@ -60,7 +60,10 @@ int check_proj(const gs_proj& p, bool need_aux, int64_t n) {
   if (n == 0) return GS_OK;
   if (!p.splat) return fail(GS_ERR_INVALID_ARGUMENT, "proj.splat is null");
   if (!aligned16(p.splat)) return fail(GS_ERR_INVALID_ARGUMENT, "proj.splat must be 16-byte aligned");
-  if (need_aux && (!p.tiles || !p.depth_key)) return fail(GS_ERR_INVALID_ARGUMENT, "proj.tiles / proj.depth_key is null");
+  if (need_aux && (!p.tiles || !p.depth_key || !p.rect))
+    return fail(GS_ERR_INVALID_ARGUMENT, "proj.tiles / proj.depth_key / proj.rect is null");
+  if (need_aux && (reinterpret_cast<uintptr_t>(p.rect) & 7u))
+    return fail(GS_ERR_INVALID_ARGUMENT, "proj.rect must be 8-byte aligned");
   return GS_OK;
 }
 

@@ -117,6 +117,7 @@ struct Proj {
   float Qa, Qb, Qc;  // conic
   float u, v;
   int rx, ry, tiles;
+  uint32_t rect_lo, rect_hi;  // tile rect, packed x0 | y0 << 16, x1 | y1 << 16
 };
 
 // Geometry part of the forward (everything but colour).  mu, ls, q, a: the parameters.
@@ -198,6 +199,8 @@ __device__ __forceinline__ void project_geometry(const CamK& c, const float mu[3
   const int tiles = (x1 > x0 && y1 > y0) ? (x1 - x0) * (y1 - y0) : 0;
   if (tiles == 0) return;
   P.tiles = tiles;
+  P.rect_lo = (uint32_t)x0 | ((uint32_t)y0 << 16);
+  P.rect_hi = (uint32_t)x1 | ((uint32_t)y1 << 16);
   P.vis = true;
 }
 
@@ -206,13 +209,15 @@ __global__ __launch_bounds__(kBlock) void k_preprocess(int64_t n, int64_t ld,
                                                         const float* __restrict__ params, CamK c,
                                                         float4* __restrict__ splat,
                                                         uint32_t* __restrict__ tiles,
-                                                        uint32_t* __restrict__ dkey) {
+                                                        uint32_t* __restrict__ dkey,
+                                                        uint2* __restrict__ rect) {
   constexpr int NB = (DEG + 1) * (DEG + 1);
   __shared__ float4 stage[kBlock * 3];
   const int64_t i0 = (int64_t)blockIdx.x * kBlock;
   const int64_t i = i0 + threadIdx.x;
   float4 r0 = make_float4(0.f, 0.f, 0.f, 0.f), r1 = r0, r2 = r0;
   uint32_t nt = 0, key = 0xFFFFFFFFu;
+  uint2 rc = make_uint2(0u, 0u);
   if (i < n) {
     float mu[3], ls[3], q[4];
 #pragma unroll
@@ -241,9 +246,11 @@ __global__ __launch_bounds__(kBlock) void k_preprocess(int64_t n, int64_t ld,
       r2 = make_float4(fmaxf(rgb[0], 0.f), fmaxf(rgb[1], 0.f), fmaxf(rgb[2], 0.f), P.z);
       nt = (uint32_t)P.tiles;
       key = __float_as_uint(P.z);
+      rc = make_uint2(P.rect_lo, P.rect_hi);
     }
     tiles[i] = nt;
     dkey[i] = key;
+    rect[i] = rc;
   }
   stage[3 * threadIdx.x + 0] = r0;
   stage[3 * threadIdx.x + 1] = r1;
@@ -443,11 +450,12 @@ hipError_t launch_preprocess(const gs_scene& sc, const float* params, const CamK
   if (sc.n == 0) return hipSuccess;
   const unsigned grid = (unsigned)ceil_div(sc.n, kBlock);
   float4* sp = reinterpret_cast<float4*>(out.splat);
+  uint2* rc = reinterpret_cast<uint2*>(out.rect);
   switch (sc.sh_degree) {
-    case 0: hipLaunchKernelGGL(k_preprocess<0>, dim3(grid), dim3(kBlock), 0, s, sc.n, sc.ld, params, cam, sp, out.tiles, out.depth_key); break;
-    case 1: hipLaunchKernelGGL(k_preprocess<1>, dim3(grid), dim3(kBlock), 0, s, sc.n, sc.ld, params, cam, sp, out.tiles, out.depth_key); break;
-    case 2: hipLaunchKernelGGL(k_preprocess<2>, dim3(grid), dim3(kBlock), 0, s, sc.n, sc.ld, params, cam, sp, out.tiles, out.depth_key); break;
-    default: hipLaunchKernelGGL(k_preprocess<3>, dim3(grid), dim3(kBlock), 0, s, sc.n, sc.ld, params, cam, sp, out.tiles, out.depth_key); break;
+    case 0: hipLaunchKernelGGL(k_preprocess<0>, dim3(grid), dim3(kBlock), 0, s, sc.n, sc.ld, params, cam, sp, out.tiles, out.depth_key, rc); break;
+    case 1: hipLaunchKernelGGL(k_preprocess<1>, dim3(grid), dim3(kBlock), 0, s, sc.n, sc.ld, params, cam, sp, out.tiles, out.depth_key, rc); break;
+    case 2: hipLaunchKernelGGL(k_preprocess<2>, dim3(grid), dim3(kBlock), 0, s, sc.n, sc.ld, params, cam, sp, out.tiles, out.depth_key, rc); break;
+    default: hipLaunchKernelGGL(k_preprocess<3>, dim3(grid), dim3(kBlock), 0, s, sc.n, sc.ld, params, cam, sp, out.tiles, out.depth_key, rc); break;
   }
   return hipGetLastError();
 }

@@ -51,7 +51,8 @@ class GsScene(ctypes.Structure):
 
 
 class GsProj(ctypes.Structure):
-    _fields_ = [("splat", ctypes.c_void_p), ("tiles", ctypes.c_void_p), ("depth_key", ctypes.c_void_p)]
+    _fields_ = [("splat", ctypes.c_void_p), ("tiles", ctypes.c_void_p), ("depth_key", ctypes.c_void_p),
+                ("rect", ctypes.c_void_p)]
 
 
 class GsAdam(ctypes.Structure):
@@ -146,16 +147,18 @@ class Proj:
     splat: "object"      # float32 [ld, 12] (48-byte records)
     tiles: "object"      # int32 [ld] (uint32 values)
     depth_key: "object"  # int32 [ld] (uint32 values)
+    rect: "object"       # int32 [ld, 2] (packed x0 | y0 << 16, x1 | y1 << 16)
 
     def c(self) -> GsProj:
-        return GsProj(self.splat.data_ptr(), self.tiles.data_ptr(), self.depth_key.data_ptr())
+        return GsProj(self.splat.data_ptr(), self.tiles.data_ptr(), self.depth_key.data_ptr(), self.rect.data_ptr())
 
 
 def alloc_proj(ld, device="cuda") -> Proj:
     import torch
     return Proj(torch.empty((ld, SPLAT_FLOATS), dtype=torch.float32, device=device),
                 torch.empty(ld, dtype=torch.int32, device=device),
-                torch.empty(ld, dtype=torch.int32, device=device))
+                torch.empty(ld, dtype=torch.int32, device=device),
+                torch.empty((ld, 2), dtype=torch.int32, device=device))
 
 
 # ------------------------------------------------------------------------------------------

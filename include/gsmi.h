@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define GSMI_VERSION 2
+#define GSMI_VERSION 3
 #define GS_TILE 16 /* tiles are GS_TILE x GS_TILE pixels */
 
 typedef enum gs_status {
@@ -100,13 +100,17 @@ typedef struct gs_splat {
   float depth;                /* view-space z                                              */
 } gs_splat;
 
-/* Output of gs_preprocess, input of the later calls.  Each array has >= ld entries.
+/* Output of gs_preprocess, input of the later calls.  Each array has >= ld entries (rect:
+ * >= 2 ld words, 8-byte aligned).
  *   tiles[i]     number of tiles the Gaussian's 3-sigma box touches (0 = culled)
- *   depth_key[i] the float32 bits of depth for a visible Gaussian, 0xFFFFFFFF if culled */
+ *   depth_key[i] the float32 bits of depth for a visible Gaussian, 0xFFFFFFFF if culled
+ *   rect[2i], rect[2i+1]  that box's tile rect [x0, x1) x [y0, y1), packed x0 | y0 << 16 and
+ *                x1 | y1 << 16 (both 0 if culled): the binning reads it in depth order */
 typedef struct gs_proj {
   gs_splat* splat;
   uint32_t* tiles;
   uint32_t* depth_key;
+  uint32_t* rect;
 } gs_proj;
 
 /* Adam state and hyper-parameters (Kingma & Ba, bias-corrected, dense over every float).
@@ -124,7 +128,7 @@ typedef struct gs_adam {
 /* ---------------------------------------------------------------------------------- */
 
 /* Per-Gaussian preprocess (EWA projection + SH colour).  params: R rows of stride ld.
- * Writes out.splat[0..n), out.tiles[0..n), out.depth_key[0..n).  One thread per Gaussian;
+ * Writes out.splat[0..n), out.tiles[0..n), out.depth_key[0..n), out.rect[0..2n).  One thread per Gaussian;
  * HBM-bound. */
 int gs_preprocess(const gs_scene* scene, const float* params, const gs_camera* cam, gs_proj out,
                   hipStream_t stream);

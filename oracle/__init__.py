@@ -55,6 +55,7 @@ def lib():
         L.or_quat_to_rot.argtypes = [P, P]
         L.or_preprocess.argtypes = [i64, i32, P, P, i32, i32, P, P, P]
         L.or_preprocess_margins.argtypes = [i64, i32, P, P, i32, i32, P]
+        L.or_tile_rects.argtypes = [i64, P, P, i32, i32, P]
         L.or_count_intersections.argtypes = [i64, P, P, i32, i32]
         L.or_count_intersections.restype = i64
         L.or_bin_sort.argtypes = [i64, P, P, i32, i32, P, P]
@@ -127,6 +128,17 @@ def preprocess_margins(params, sh_degree, cam_flat, W, H):
     n = params.shape[1]
     out = np.zeros((3, n))
     lib().or_preprocess_margins(n, sh_degree, _p(params), _p(_f64(cam_flat)), W, H, _p(out))
+    return out
+
+
+def tile_rects(proj, radii, W, H):
+    """-> int32 [4][n]: x0, x1, y0, y1 of each Gaussian's tile rect [x0, x1) x [y0, y1) (all 0
+    if culled); u, v are read as float32 (the binning decision)."""
+    proj = _f64(proj)
+    radii = np.ascontiguousarray(radii, np.int32)
+    n = proj.shape[1]
+    out = np.zeros((4, n), np.int32)
+    lib().or_tile_rects(n, _p(proj), _p(radii), W, H, _p(out))
     return out
 
 

@@ -410,6 +410,18 @@ int64_t or_count_intersections(int64_t n, const double* proj, const int32_t* rad
   return K;
 }
 
+/* Tile rect [x0, x1) x [y0, y1) of every Gaussian (rect[0..3][n] = x0, x1, y0, y1; all 0 for
+ * a culled one), the binning decision above (u, v read as float32). */
+void or_tile_rects(int64_t n, const double* proj, const int32_t* radii, int W, int H, int32_t* rect) {
+  const int TX = (W + TILE - 1) / TILE, TY = (H + TILE - 1) / TILE;
+  for (int64_t i = 0; i < n; i++) {
+    int r[4] = {0, 0, 0, 0};
+    if (radii[i] != 0 && radii[n + i] != 0)
+      tile_rect((float)proj[PRJ_U * n + i], (float)proj[PRJ_V * n + i], radii[i], radii[n + i], TX, TY, r);
+    for (int j = 0; j < 4; j++) rect[j * n + i] = r[j];
+  }
+}
+
 /* Stable bottom-up merge sort of (key, val) pairs by key. */
 static void merge_sort_stable(uint64_t* key, uint32_t* val, int64_t K) {
   uint64_t* k2 = (uint64_t*)malloc((size_t)(K > 0 ? K : 1) * sizeof(uint64_t));

@@ -49,10 +49,18 @@ def proj_f32(proj):
     return np.asarray(proj, np.float64).astype(np.float32).astype(np.float64)
 
 
-def records_from_oracle(proj, radii, tiles):
+def pack_rects(rect):
+    """Oracle tile rects [4][n] (x0, x1, y0, y1) -> the packed form [n][2] uint32
+    (x0 | y0 << 16, x1 | y1 << 16)."""
+    r = np.asarray(rect, np.uint32)
+    return np.stack([r[0] | (r[2] << 16), r[1] | (r[3] << 16)], axis=1).astype(np.uint32)
+
+
+def records_from_oracle(proj, radii, tiles, W, H):
     """Oracle projection (planar [10][n], radii [2][n], tiles [n]) -> the GPU's 48-byte records
-    ([n][12] float32: u, v, radius bits x2, conic a b c, opacity, r g b, depth), tiles and
-    depth keys (float bits, all-ones when culled).  A layout conversion, nothing computed."""
+    ([n][12] float32: u, v, radius bits x2, conic a b c, opacity, r g b, depth), tiles, depth
+    keys (float bits, all-ones when culled) and the oracle's tile rects, packed.  A layout
+    conversion: every value is the oracle's."""
     p = np.asarray(proj, np.float64)
     radii = np.asarray(radii, np.int32)
     n = p.shape[1]
@@ -63,7 +71,7 @@ def records_from_oracle(proj, radii, tiles):
     rec[:, 8], rec[:, 9], rec[:, 10], rec[:, 11] = p[7], p[8], p[9], p[2]
     vis = (radii[0] > 0) & (radii[1] > 0)
     dkey = np.where(vis, rec[:, 11].view(np.uint32), np.uint32(0xFFFFFFFF)).astype(np.uint32)
-    return rec, np.asarray(tiles, np.uint32), dkey
+    return rec, np.asarray(tiles, np.uint32), dkey, pack_rects(oracle.tile_rects(proj, radii, W, H))
 
 
 def oracle_pipeline(params, deg, cam_flat, W, H, bg, target=None, upstream=None, margins=None):
@@ -116,12 +124,13 @@ class GpuStep:
         self.kcap = k_capacity
         self.torch = torch
 
-    def load_proj(self, rec, tiles, dkey):
+    def load_proj(self, rec, tiles, dkey, rect):
         """Puts oracle-derived records, tiles and depth keys in the GPU projection buffers."""
         n = rec.shape[0]
         self.proj.splat[:n].copy_(to_t(np.ascontiguousarray(rec, np.float32)))
         self.proj.tiles[:n].copy_(to_t(np.ascontiguousarray(tiles, np.uint32).view(np.int32)))
         self.proj.depth_key[:n].copy_(to_t(np.ascontiguousarray(dkey, np.uint32).view(np.int32)))
+        self.proj.rect[:n].copy_(to_t(np.ascontiguousarray(rect, np.uint32).view(np.int32)))
         self.torch.cuda.synchronize()
 
     def load_lists(self, vals, ranges):
@@ -145,6 +154,7 @@ class GpuStep:
         splat = self.proj.splat.cpu().numpy()[: self.n]
         tiles = self.proj.tiles.cpu().numpy().view(np.uint32)[: self.n]
         dkey = self.proj.depth_key.cpu().numpy().view(np.uint32)[: self.n]
+        self.last_rect = self.proj.rect.cpu().numpy().view(np.uint32)[: self.n]  # [n][2], packed
         return splat, tiles, dkey
 
     def bin_and_sort(self, k_capacity=None):

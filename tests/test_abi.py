@@ -22,7 +22,7 @@ def test_library_exports_every_declared_symbol():
     assert len(names) == len(gsmi.EXPORTS) and set(names) == set(gsmi.EXPORTS)
     for name in names:
         assert hasattr(L, name), name
-    assert gsmi.version() == 2
+    assert gsmi.version() == 3
 
 
 def test_invalid_arguments_rejected_before_any_gpu_call():
@@ -49,11 +49,18 @@ def test_invalid_arguments_rejected_before_any_gpu_call():
     c3.width = 0
     assert L.gs_preprocess(ctypes.byref(sc), None, ctypes.byref(c3), gsmi.GsProj(), None) == -1
     # null params with n > 0
-    proj = gsmi.GsProj(16, 16, 16)
+    proj = gsmi.GsProj(16, 16, 16, 16)
     assert L.gs_preprocess(ctypes.byref(sc), None, ctypes.byref(cam), proj, None) == -1
-    # misaligned record buffer
-    assert L.gs_preprocess(ctypes.byref(sc), ctypes.c_void_p(64), ctypes.byref(cam), gsmi.GsProj(8, 16, 16), None) == -1
+    # misaligned record buffer, missing or misaligned tile rects
+    assert L.gs_preprocess(ctypes.byref(sc), ctypes.c_void_p(64), ctypes.byref(cam), gsmi.GsProj(8, 16, 16, 16),
+                           None) == -1
     assert "aligned" in gsmi.last_error()
+    assert L.gs_preprocess(ctypes.byref(sc), ctypes.c_void_p(64), ctypes.byref(cam), gsmi.GsProj(16, 16, 16, None),
+                           None) == -1
+    assert "rect" in gsmi.last_error()
+    assert L.gs_preprocess(ctypes.byref(sc), ctypes.c_void_p(64), ctypes.byref(cam), gsmi.GsProj(16, 16, 16, 20),
+                           None) == -1
+    assert "rect" in gsmi.last_error()
     # Adam with a bad step / null moments
     ad = gsmi.GsAdam(None, None, 1, 1e-3, 0.9, 0.999, 1e-8)
     assert L.gs_adam_step(10, ctypes.c_void_p(64), ctypes.c_void_p(64), ctypes.byref(ad), None) == -1
@@ -110,7 +117,7 @@ def test_render_calls_reject_a_missing_or_short_workspace():
         rc = L.gs_render_forward(ctypes.byref(cam), 10, p, p, p, bg, p, p, p, None, None, ws, nb, None)
         assert rc == gsmi.GS_ERR_INVALID_ARGUMENT
     sc = gsmi.make_scene(10, 10, 0)
-    proj = gsmi.GsProj(4096, 4096, 4096)
+    proj = gsmi.GsProj(4096, 4096, 4096, 4096)
     rc = L.gs_render_backward(ctypes.byref(sc), None, ctypes.byref(cam), proj, p, p, bg, p, p, p, p, None, None,
                               p, 16, None)
     assert rc == gsmi.GS_ERR_INVALID_ARGUMENT and "workspace" in gsmi.last_error()

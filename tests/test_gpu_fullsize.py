@@ -61,7 +61,7 @@ def test_gyroid_4m_2048_full_step():
     for f in (0, 1, 2, 3):  # u, v, depth, opacity
         assert (np.abs(gp[f, same] - o["proj"][f, same]) <= 1e-5 * np.abs(o["proj"][f, same])).all(), f
     say("[fullsize] GPU sort of the oracle's records")
-    g.load_proj(*records_from_oracle(o["p32"], o["radii"], o["tiles"]))
+    g.load_proj(*records_from_oracle(o["p32"], o["radii"], o["tiles"], W, H))
     Kg, keys, vals, rg = g.bin_and_sort()
     assert Kg == K
     np.testing.assert_array_equal(keys, o["keys"])
@@ -115,7 +115,7 @@ def test_bumps_18m_2048_sort_and_sampled_tiles():
     K = okeys.size
     say(f"[fullsize] K = {K}; GPU sort of the oracle's records")
     g = GpuStep(params, cfg.sh_degree, cam, W, H, k_capacity=K + 4096)
-    g.load_proj(*records_from_oracle(p32, radii, tiles))
+    g.load_proj(*records_from_oracle(p32, radii, tiles, W, H))
     Kg, keys, vals, rg = g.bin_and_sort()
     assert Kg == K
     np.testing.assert_array_equal(keys, okeys)

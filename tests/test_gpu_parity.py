@@ -9,7 +9,7 @@ import pytest
 import oracle
 from gaussian_splatting_differentiable_preprocess_amd import gsmi, inputs
 from parity_util import (BORDER_FRACTION, FWD_MARGINS, GRAD_REL_L2, IMG_MAX_ABS, PROJ_RTOL, GpuStep, oracle_pipeline,
-                         records_from_oracle,
+                         pack_rects, records_from_oracle,
                          preprocess_borderline, proj_from_splat, rel_l2, say)
 
 pytestmark = pytest.mark.gpu
@@ -66,10 +66,10 @@ def data(name):
     say(f"[parity] case {name}: K={o['keys'].size} -> GPU preprocess")
     g = GpuStep(params, deg, cam, W, H)
     d["g_splat"], d["g_tiles"], d["g_dkey"] = g.preprocess()
+    d["g_rect"] = g.last_rect
     d["g_proj"], d["g_radii"] = proj_from_splat(d["g_splat"])
     say(f"[parity] case {name}: GPU stages on the oracle's inputs")
-    rec, tiles, dkey = records_from_oracle(o["p32"], o["radii"], o["tiles"])
-    g.load_proj(rec, tiles, dkey)
+    g.load_proj(*records_from_oracle(o["p32"], o["radii"], o["tiles"], W, H))
     d["K"], d["g_keys"], d["g_vals"], d["g_ranges"] = g.bin_and_sort()
     g.load_lists(o["vals"], o["ranges"])
     d["g_fwd"] = g.forward(BG)
@@ -104,6 +104,9 @@ def test_preprocess(name):
     same = vis_o & vis_g & ~bl
     np.testing.assert_array_equal(d["g_radii"][:, same], d["o_radii"][:, same])
     np.testing.assert_array_equal(d["g_tiles"][same], d["o_tiles"][same])
+    o_rect = pack_rects(oracle.tile_rects(d["o_proj"], d["o_radii"], d["W"], d["H"]))
+    np.testing.assert_array_equal(d["g_rect"][same], o_rect[same])
+    assert (d["g_rect"][~vis_g] == 0).all()
     n_diff = int(((d["g_radii"] != d["o_radii"]).any(0) | (d["g_tiles"] != d["o_tiles"])).sum())
     say(f"[parity]   preprocess: {int(vis_o.sum())} visible, {int(bl.sum())} borderline, "
         f"{n_diff} with differing radii/tiles (all borderline)")
@@ -415,7 +418,7 @@ def test_long_lists_with_stops_in_many_segments():
     assert 0.05 < stopped.mean() < 0.95, stopped.mean()  # some pixels stop, some walk the whole list
     assert len(np.unique((of["n_examined"][stopped] - 1) // 256)) > 8  # in many different segments
     g = GpuStep(params, 0, cam, W, W)
-    g.load_proj(*records_from_oracle(o["p32"], o["radii"], o["tiles"]))
+    g.load_proj(*records_from_oracle(o["p32"], o["radii"], o["tiles"], W, W))
     g.load_lists(o["vals"], o["ranges"])
     fwd = g.forward(BG)
     hdr = g.render_ws[:64].cpu().numpy().view(np.uint32)
@@ -452,7 +455,7 @@ def test_backward_segments_on_deep_lists():
     lens = o["ranges"][:, 1].astype(np.int64) - o["ranges"][:, 0]
     assert lens.max() > 8 * 256 and o["fwd"]["last_contrib"].max() > 4 * 256, (lens.max(),)
     g = GpuStep(params, 0, cam, W, W)
-    g.load_proj(*records_from_oracle(o["p32"], o["radii"], o["tiles"]))
+    g.load_proj(*records_from_oracle(o["p32"], o["radii"], o["tiles"], W, W))
     g.load_lists(o["vals"], o["ranges"])
     fwd = g.forward(BG)
     ok = ~o["fwd"]["borderline"]

@@ -281,6 +281,26 @@ def test_binning_is_tile_interval_overlap():
     assert got == want
 
 
+def test_tile_rects_are_the_binned_tiles():
+    """Each Gaussian's tile rect holds exactly the tiles it is binned to (interval overlap,
+    pinned above), and a culled Gaussian has an empty rect."""
+    rng = np.random.default_rng(6)
+    W, H = 100, 70
+    TX = (W + 15) // 16
+    proj, radii = _random_proj(rng, 300, W, H)
+    rect = oracle.tile_rects(proj, radii, W, H)
+    keys, vals = oracle.bin_sort(proj, radii, W, H)
+    binned = {}
+    for k, v in zip(keys, vals):
+        binned.setdefault(int(v), set()).add(int(k >> 32))
+    for i in range(proj.shape[1]):
+        x0, x1, y0, y1 = (int(c) for c in rect[:, i])
+        tiles = {ty * TX + tx for ty in range(y0, y1) for tx in range(x0, x1)}
+        assert tiles == binned.get(i, set()), i
+        if radii[0, i] == 0:
+            assert (rect[:, i] == 0).all()
+
+
 def test_sort_is_numpy_stable_argsort_and_ranges_searchsorted():
     rng = np.random.default_rng(6)
     W, H = 128, 96
