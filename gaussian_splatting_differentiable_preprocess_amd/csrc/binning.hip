@@ -71,16 +71,20 @@ __global__ __launch_bounds__(kBlock) void k_bin_reduce(int64_t n, const uint32_t
   const int64_t base = (int64_t)blockIdx.x * kReduceTile;
   unsigned long long s = 0;
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-  for (int j = 0; j < kReduceTile / kBlock; ++j) {
+  constexpr int kPer = kReduceTile / kBlock;
+  uint32_t t[kPer], k[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {  // every load in flight before the first use
     const int64_t i = base + j * kBlock + threadIdx.x;
-    if (i < n) {
-      const uint32_t t = tiles[i];
-      s += t;
-      if (t > 0) {
-        const uint32_t k = dkey[i];
-        mn = min(mn, k);
-        mx = max(mx, k);
-      }
+    t[j] = i < n ? tiles[i] : 0u;
+    k[j] = i < n ? dkey[i] : 0u;
+  }
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    s += t[j];
+    if (t[j] > 0) {
+      mn = min(mn, k[j]);
+      mx = max(mx, k[j]);
     }
   }
   for (int o = 32; o > 0; o >>= 1) {

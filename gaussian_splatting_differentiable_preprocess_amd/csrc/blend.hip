@@ -203,28 +203,26 @@ __device__ __forceinline__ int lowest_bit(unsigned long long m) { return __built
 __device__ __forceinline__ int highest_bit(unsigned long long m) { return 63 - __builtin_clzll(m); }
 
 // ---------------------------------------------------------------------------------------------
-// Segment plan.  One workgroup: for every tile, its list length len decides
+// Segment plan.  For every tile, its list length len decides
 //   items(t) = ceil(len / SEG) backward work items (0 for an empty tile),
 //   slots(t) = ceil(len / SEG) state slots if len > SEG (one per boundary + the final state),
 // SEG = 2^shift is the smallest power of two >= 2^kSegShiftMin whose slots fit the workspace.
-// Writes bnd_off (exclusive scan of slots), the item list and the header.
+// The forward's tile order groups the tiles by list-length class (1 + floor(log2 len), 0 for
+// an empty list), longest first.  Three kernels over blocks of 1024 tiles: per-block sums for
+// every candidate shift and class counts; one workgroup picks the shift and turns the sums
+// into per-block offsets; then every tile writes bnd_off (exclusive scan of slots), item_off
+// and its place in the order.
 // ---------------------------------------------------------------------------------------------
 constexpr int kPlanThreads = 1024;
 // list-length classes: 0 for an empty list, else 1 + floor(log2 len)
 constexpr int kLenClasses = 33;
 __device__ __forceinline__ int len_class(uint32_t len) { return len ? 32 - __clz((int)len) : 0; }
-
-template <typename U>
-__device__ U block_sum_1024(U x, U* red) {
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
-  __syncthreads();
-  U t = 0;
-#pragma unroll
-  for (int k = 0; k < kPlanThreads / 64; ++k) t += red[k];
-  __syncthreads();
-  return t;
-}
+constexpr int kShifts = 32 - kSegShiftMin;  // candidate shifts kSegShiftMin .. 31
+// per-block partial sums: slots(shift), long tiles(shift), non-empty tiles, class counts
+constexpr int kPartSlots = 0, kPartLong = kShifts, kPartNonEmpty = 2 * kShifts, kPartClass = 2 * kShifts + 1;
+constexpr int kPartVals = kPartClass + kLenClasses;
+// per-block offsets: slots, items, then each class's first position in the order
+constexpr int kOffVals = 2 + kLenClasses;
 
 // exclusive scan over the 1024 threads
 __device__ uint32_t block_exscan_1024(uint32_t x, uint32_t* red) {
@@ -242,86 +240,125 @@ __device__ uint32_t block_exscan_1024(uint32_t x, uint32_t* red) {
   return base + inc - x;
 }
 
-__global__ __launch_bounds__(kPlanThreads) void k_seg_plan(const uint2* __restrict__ ranges, int T,
-                                                           uint32_t slots_cap, uint32_t* __restrict__ hdr,
-                                                           uint32_t* __restrict__ bnd_off,
-                                                           uint32_t* __restrict__ item_off,
-                                                           uint32_t* __restrict__ order) {
-  __shared__ unsigned long long red64[kPlanThreads / 64];
-  __shared__ uint32_t red32[kPlanThreads / 64];
-  __shared__ uint32_t cls[kLenClasses];  // tiles per list-length class, then the classes' cursors
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void k_plan_count(const uint2* __restrict__ ranges, int T,
+                                                             uint32_t* __restrict__ part) {
+  __shared__ uint32_t red[kPlanThreads / 64][2 * kShifts + 1];
+  __shared__ uint32_t cls[kLenClasses];
+  const int t = (int)(blockIdx.x * kPlanThreads + threadIdx.x), w = threadIdx.x >> 6;
+  uint32_t len = 0;
+  if (t < T) {
+    const uint2 rg = ranges[t];
+    len = rg.y - rg.x;
+  }
   if (threadIdx.x < kLenClasses) cls[threadIdx.x] = 0u;
-  // tiles are visited in rounds of 1024 consecutive tiles (thread t takes tile r*1024 + t), so
-  // every load and store of a round is coalesced
-  const int rounds = (T + kPlanThreads - 1) / kPlanThreads;
-  int shift = kSegShiftMin;
-  for (;;) {  // every thread takes the same exit (the sum is block-wide)
-    unsigned long long s = 0;
-    for (int r = 0; r < rounds; ++r) {
-      const int t = r * kPlanThreads + (int)threadIdx.x;
-      if (t < T) {
-        const uint2 rg = ranges[t];
-        const uint32_t len = rg.y - rg.x;
-        if (len > (1u << shift)) s += ((len - 1u) >> shift) + 1u;
-      }
+  __syncthreads();
+  if (t < T) atomicAdd(&cls[len_class(len)], 1u);
+  for (int q = 0; q < kShifts; ++q) {
+    const int sh = kSegShiftMin + q;
+    const bool lg = len > (1u << sh);
+    const uint32_t sl = wave_sum(lg ? ((len - 1u) >> sh) + 1u : 0u), nl = wave_sum(lg ? 1u : 0u);
+    if ((threadIdx.x & 63) == 0) {
+      red[w][kPartSlots + q] = sl;
+      red[w][kPartLong + q] = nl;
     }
-    s = block_sum_1024(s, red64);
-    if (s <= slots_cap || shift >= 31) break;
-    ++shift;
   }
-  const uint32_t seg = 1u << shift;
-  uint32_t so = 0, io = 0;  // running totals of the rounds before
-  for (int r = 0; r < rounds; ++r) {
-    const int t = r * kPlanThreads + (int)threadIdx.x;
-    uint32_t len = 0;
-    if (t < T) {
-      const uint2 rg = ranges[t];
-      len = rg.y - rg.x;
-    }
-    if (t < T) atomicAdd(&cls[len_class(len)], 1u);
-    const uint32_t k = len ? ((len - 1u) >> shift) + 1u : 0u;
-    const uint32_t sl = len > seg ? k : 0u;
-    const uint32_t pre_s = block_exscan_1024(sl, red32);
-    const uint32_t pre_i = block_exscan_1024(k, red32);
-    if (t < T) {
-      bnd_off[t] = so + pre_s;
-      item_off[t] = io + pre_i;
-    }
-    // the round's totals: the last thread's inclusive prefix, shared through LDS
-    __shared__ uint32_t s_tot[2];
-    if (threadIdx.x == kPlanThreads - 1) {
-      s_tot[0] = pre_s + sl;
-      s_tot[1] = pre_i + k;
-    }
-    __syncthreads();
-    so += s_tot[0];
-    io += s_tot[1];
-    __syncthreads();
+  const uint32_t ne = wave_sum(len > 0u ? 1u : 0u);
+  if ((threadIdx.x & 63) == 0) red[w][kPartNonEmpty] = ne;
+  __syncthreads();
+  uint32_t* out = part + (size_t)blockIdx.x * kPartVals;
+  if (threadIdx.x < 2 * kShifts + 1) {
+    uint32_t v = 0;
+    for (int k = 0; k < kPlanThreads / 64; ++k) v += red[k][threadIdx.x];
+    out[threadIdx.x] = v;
+  } else if (threadIdx.x < kPartVals) {
+    out[threadIdx.x] = cls[threadIdx.x - kPartClass];
   }
-  // the forward's tile order: list-length classes, longest first (within a class, any order)
-  if (threadIdx.x == 0) {
-    uint32_t run = 0;
-    for (int c = kLenClasses - 1; c >= 0; --c) {
-      const uint32_t v = cls[c];
-      cls[c] = run;
-      run += v;
-    }
+}
+
+// One workgroup: the shift, the header, bnd_off[T] / item_off[T] and the per-block offsets.
+__global__ __launch_bounds__(kPlanThreads) void k_plan_scan(const uint32_t* __restrict__ part, int nb, int T,
+                                                            uint32_t slots_cap, uint32_t* __restrict__ off,
+                                                            uint32_t* __restrict__ hdr,
+                                                            uint32_t* __restrict__ bnd_off,
+                                                            uint32_t* __restrict__ item_off) {
+  __shared__ uint32_t tot[kPartVals];
+  __shared__ uint32_t cbase[kLenClasses];
+  __shared__ int s_q;
+  if (threadIdx.x < kPartVals) {
+    uint32_t v = 0;
+    for (int b = 0; b < nb; ++b) v += part[(size_t)b * kPartVals + threadIdx.x];
+    tot[threadIdx.x] = v;
   }
   __syncthreads();
-  for (int r = 0; r < rounds; ++r) {
-    const int t = r * kPlanThreads + (int)threadIdx.x;
-    if (t < T) {
-      const uint2 rg = ranges[t];
-      order[atomicAdd(&cls[len_class(rg.y - rg.x)], 1u)] = (uint32_t)t;
+  if (threadIdx.x == 0) {
+    int q = 0;  // the first shift whose slots fit (the last one if none does)
+    while (q < kShifts - 1 && tot[kPartSlots + q] > slots_cap) ++q;
+    s_q = q;
+    uint32_t run = 0;  // classes longest first
+    for (int c = kLenClasses - 1; c >= 0; --c) {
+      cbase[c] = run;
+      run += tot[kPartClass + c];
+    }
+    const uint32_t slots = tot[kPartSlots + q];
+    const uint32_t items = slots + tot[kPartNonEmpty] - tot[kPartLong + q];
+    bnd_off[T] = slots;
+    item_off[T] = items;
+    hdr[0] = (uint32_t)(kSegShiftMin + q);
+    hdr[1] = items;
+    hdr[2] = slots;
+    hdr[3] = 0u;
+  }
+  __syncthreads();
+  const int q = s_q;
+  if (threadIdx.x == 0) {  // slot and item offsets of the blocks
+    uint32_t rs = 0, ri = 0;
+    for (int b = 0; b < nb; ++b) {
+      const uint32_t* pb = part + (size_t)b * kPartVals;
+      off[(size_t)b * kOffVals + 0] = rs;
+      off[(size_t)b * kOffVals + 1] = ri;
+      rs += pb[kPartSlots + q];
+      ri += pb[kPartSlots + q] + pb[kPartNonEmpty] - pb[kPartLong + q];
+    }
+  } else if (threadIdx.x <= kLenClasses) {  // each class's offsets of the blocks
+    const int c = threadIdx.x - 1;
+    uint32_t r = cbase[c];
+    for (int b = 0; b < nb; ++b) {
+      off[(size_t)b * kOffVals + 2 + c] = r;
+      r += part[(size_t)b * kPartVals + kPartClass + c];
     }
   }
-  if (threadIdx.x == 0) {
-    bnd_off[T] = so;
-    item_off[T] = io;
-    hdr[0] = (uint32_t)shift;
-    hdr[1] = io;
-    hdr[2] = so;
-    hdr[3] = 0u;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void k_plan_write(const uint2* __restrict__ ranges, int T,
+                                                             const uint32_t* __restrict__ off,
+                                                             const uint32_t* __restrict__ hdr,
+                                                             uint32_t* __restrict__ bnd_off,
+                                                             uint32_t* __restrict__ item_off,
+                                                             uint32_t* __restrict__ order) {
+  __shared__ uint32_t red32[kPlanThreads / 64];
+  __shared__ uint32_t cur[kLenClasses];
+  const int t = (int)(blockIdx.x * kPlanThreads + threadIdx.x);
+  const uint32_t* ob = off + (size_t)blockIdx.x * kOffVals;
+  if (threadIdx.x < kLenClasses) cur[threadIdx.x] = ob[2 + threadIdx.x];
+  uint32_t len = 0;
+  if (t < T) {
+    const uint2 rg = ranges[t];
+    len = rg.y - rg.x;
+  }
+  const uint32_t shift = hdr[0];
+  const uint32_t k = len ? ((len - 1u) >> shift) + 1u : 0u;
+  const uint32_t sl = len > (1u << shift) ? k : 0u;
+  const uint32_t pre_s = block_exscan_1024(sl, red32);  // (its barriers also publish cur)
+  const uint32_t pre_i = block_exscan_1024(k, red32);
+  if (t < T) {
+    bnd_off[t] = ob[0] + pre_s;
+    item_off[t] = ob[1] + pre_i;
+    order[atomicAdd(&cur[len_class(len)], 1u)] = (uint32_t)t;
   }
 }
 
@@ -686,32 +723,39 @@ constexpr int kGoffItems = kGoffBlock / kBlock;  // 16 Gaussians per thread
 
 __global__ __launch_bounds__(kBlock) void k_goff_local(int64_t n, const uint32_t* __restrict__ tiles,
                                                        uint32_t* __restrict__ goff, uint32_t* __restrict__ blk) {
-  __shared__ uint32_t wsum[4];
-  const int64_t base = (int64_t)blockIdx.x * kGoffBlock + (int64_t)threadIdx.x * kGoffItems;
-  uint32_t t[kGoffItems];
-  uint32_t s = 0;
-#pragma unroll
-  for (int j = 0; j < kGoffItems; ++j) {
-    t[j] = base + j < n ? tiles[base + j] : 0u;
-    s += t[j];
-  }
-  // exclusive scan of the per-thread sums over the 256 threads
+  __shared__ uint32_t wsum[kBlock / 64];
+  // item j of thread t is base + j kBlock + t: the block scans its kGoffBlock Gaussians in
+  // kGoffItems rounds of kBlock consecutive ones, every load and store coalesced
+  const int64_t base = (int64_t)blockIdx.x * kGoffBlock + threadIdx.x;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  uint32_t inc = s;
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(inc, o, 64);
-    if (lane >= o) inc += y;
-  }
-  if (lane == 63) wsum[w] = inc;
-  __syncthreads();
-  uint32_t pre = inc - s;
-  for (int k = 0; k < w; ++k) pre += wsum[k];
+  uint32_t t[kGoffItems];
 #pragma unroll
   for (int j = 0; j < kGoffItems; ++j) {
-    if (base + j < n) goff[base + j] = pre;
-    pre += t[j];
+    const int64_t i = base + (int64_t)j * kBlock;
+    t[j] = i < n ? tiles[i] : 0u;
   }
-  if (threadIdx.x == kBlock - 1) blk[blockIdx.x] = pre;  // the block's total
+  uint32_t run = 0;  // the block's earlier rounds
+#pragma unroll
+  for (int j = 0; j < kGoffItems; ++j) {
+    uint32_t inc = t[j];
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += y;
+    }
+    if (lane == 63) wsum[w] = inc;
+    __syncthreads();
+    uint32_t pre = inc - t[j], tot = 0;
+#pragma unroll
+    for (int k = 0; k < kBlock / 64; ++k) {
+      pre += k < w ? wsum[k] : 0u;
+      tot += wsum[k];
+    }
+    __syncthreads();
+    const int64_t i = base + (int64_t)j * kBlock;
+    if (i < n) goff[i] = run + pre;
+    run += tot;
+  }
+  if (threadIdx.x == 0) blk[blockIdx.x] = run;  // the block's total
 }
 
 // exclusive scan of the nblk block totals in place (one workgroup); total entries -> hdr[4]
@@ -780,6 +824,8 @@ constexpr size_t kMaskChunkBytes = sizeof(uint2) * kTile * kTile;  // one 64-bit
 constexpr uint64_t kSegEntries = 1u << kSegShiftMin;
 
 size_t n_goff_blocks(int64_t n) { return (size_t)((n + kGoffBlock - 1) / kGoffBlock); }
+size_t plan_blocks(int T) { return (size_t)((T + kPlanThreads - 1) / kPlanThreads); }
+size_t plan_bytes(int T) { return round256(4 * plan_blocks(T) * kPartVals) + round256(4 * plan_blocks(T) * kOffVals); }
 
 // bytes of the layout for T tiles, n Gaussians and k staged entries (k a multiple of 256)
 // (tile t's 64-entry chunks start at ranges[t].x / 64 + t, so K entries need at most
@@ -787,7 +833,7 @@ size_t n_goff_blocks(int64_t n) { return (size_t)((n + kGoffBlock - 1) / kGoffBl
 size_t layout_bytes(int T, int64_t n, uint64_t k) {
   const size_t slots = (size_t)T + (size_t)(k / kSegEntries);
   const size_t chunks = (size_t)T + (size_t)(k / kChunk);
-  return 256 + 2 * round256(4 * (size_t)(T + 1)) + round256(4 * (size_t)T) + round256(4 * (size_t)n) +
+  return 256 + 2 * round256(4 * (size_t)(T + 1)) + round256(4 * (size_t)T) + plan_bytes(T) + round256(4 * (size_t)n) +
          round256(4 * (n_goff_blocks(n) + 1)) +
          round256(8 * ((size_t)T + slots)) + round256(kSlotBytes * slots) + kMaskChunkBytes * chunks +
          round256(36 * (size_t)k + 16);
@@ -820,6 +866,10 @@ bool render_ws_layout(void* ws, size_t bytes, int T, int64_t n, RenderWs* out) {
   b += round256(4 * (size_t)(T + 1));
   out->order = reinterpret_cast<uint32_t*>(b);
   b += round256(4 * (size_t)T);
+  out->plan_part = reinterpret_cast<uint32_t*>(b);
+  b += round256(4 * plan_blocks(T) * kPartVals);
+  out->plan_off = reinterpret_cast<uint32_t*>(b);
+  b += round256(4 * plan_blocks(T) * kOffVals);
   out->goff = reinterpret_cast<uint32_t*>(b);
   b += round256(4 * (size_t)n);
   out->goff_blk = reinterpret_cast<uint32_t*>(b);
@@ -845,8 +895,12 @@ hipError_t launch_blend_forward(const CamK& cam, int64_t n, const gs_splat* spla
                                 hipStream_t s) {
   const int T = cam.TX * cam.TY;
   const uint2* rg = reinterpret_cast<const uint2*>(ranges);
-  hipLaunchKernelGGL(k_seg_plan, dim3(1), dim3(kPlanThreads), 0, s, rg, T, ws.slots_cap, ws.hdr, ws.bnd_off,
-                     ws.item_off, ws.order);
+  const int nb = (int)ceil_div(T, kPlanThreads);
+  hipLaunchKernelGGL(k_plan_count, dim3((unsigned)nb), dim3(kPlanThreads), 0, s, rg, T, ws.plan_part);
+  hipLaunchKernelGGL(k_plan_scan, dim3(1), dim3(kPlanThreads), 0, s, (const uint32_t*)ws.plan_part, nb, T,
+                     ws.slots_cap, ws.plan_off, ws.hdr, ws.bnd_off, ws.item_off);
+  hipLaunchKernelGGL(k_plan_write, dim3((unsigned)nb), dim3(kPlanThreads), 0, s, rg, T,
+                     (const uint32_t*)ws.plan_off, (const uint32_t*)ws.hdr, ws.bnd_off, ws.item_off, ws.order);
   hipLaunchKernelGGL(k_seg_items, dim3((unsigned)ceil_div(T, kBlock / 64)), dim3(kBlock), 0, s, T,
                      (const uint32_t*)ws.item_off, ws.items);
   hipLaunchKernelGGL(k_blend_forward, dim3(T), dim3(kBlock), 0, s, cam.W, cam.H, cam.TX, T, n,

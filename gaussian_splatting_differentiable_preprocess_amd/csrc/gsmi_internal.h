@@ -97,6 +97,7 @@ hipError_t launch_bin_sort_rest(int64_t n, int64_t K, const BinInfo& info, const
 //   bnd_off[T + 1]  first slot of each tile
 //   item_off[T + 1] first work item of each tile
 //   order[T]        the forward's tile order: list-length classes (log2), longest first
+//   plan_part[], plan_off[]  the segment plan's per-block partial sums and offsets
 //   goff[n]         exclusive scan of tiles within blocks of kGoffBlock Gaussians; goff(i) =
 //                   goff_blk[i / kGoffBlock] + goff[i]
 //   goff_blk[]      exclusive scan of the block totals
@@ -113,6 +114,8 @@ struct RenderWs {
   uint32_t* bnd_off;
   uint32_t* item_off;
   uint32_t* order;
+  uint32_t* plan_part;  // the segment plan's per-block sums and offsets (blocks of 1024 tiles)
+  uint32_t* plan_off;
   uint32_t* goff;
   uint32_t* goff_blk;
   uint2* items;
