@@ -11,10 +11,10 @@ Prints ONE JSON line on stdout (progress goes to stderr):
   value        Gaussian-pixel blends per second over the timed steps (sum of n_examined, the
                list entries each pixel's forward walk examines, / wall time)
   ms_per_step  wall time per step
-  roofline     the dominant single-kernel phase against its roof, from HIP events on the
-               launch stream: HBM-bound phases as bytes the method must move / time against
-               8 TB/s, the blends as the fp32 operations the method performs / time against
-               the fp32 vector peak (see FLOPS_EVAL below)
+  roofline     the dominant kernel (the preprocess backward fused with Adam, the longest
+               kernel of the step, alone in its phase) against its roof, from HIP events on the
+               launch stream: the bytes the method must move / time against 8 TB/s, with the
+               HBM bytes the counters measured for it (COUNTER_TRAFFIC)
   cpu_baseline the CPU oracle on a bounded sample of the same step (see cpu_baseline())
 """
 from __future__ import annotations
@@ -42,14 +42,14 @@ def log(*a):
 
 def alg_bytes(phase, N, R, K, P, T, n_vis):
     """Bytes the method itself must move per launch (reads + writes), by phase."""
-    if phase == "preprocess":          # params in; 48-B record + tiles + depth key out
-        return N * (4 * R + 56)
+    if phase == "preprocess":          # params in; 48-B record + tiles + depth key + tile rect out
+        return N * (4 * R + 64)
     if phase == "forward":             # per entry: index + 36 B of record; per pixel: RGB, T, last
         return K * 40 + P * 20 + T * 8
     if phase == "loss":                # image + target in, dL/dI out
         return P * 36
-    if phase == "backward_blend":      # entries + pixels (dL/dI, T, last) + grad2d zero + accumulate
-        return K * 40 + P * 20 + T * 8 + 36 * N + 36 * n_vis
+    if phase == "backward_blend":      # entries + pixels (dL/dI, T, last) + grad2d written once
+        return K * 40 + P * 20 + T * 8 + 36 * n_vis
     if phase == "prebwd_adam":         # params, m, v, grad2d in; params, m, v out
         return N * (24 * R + 36)
     return 0
@@ -79,23 +79,18 @@ def alg_flops(phase, examined, walked, composited):
     return 0
 
 
-# the kernel behind each single-kernel phase (the backward blend phase also clears grad2d
-# with a fill kernel first, about 1% of its time)
-KERNEL_OF = {"preprocess": "k_preprocess<3>", "forward": "k_blend_forward",
-             "backward_blend": "k_blend_backward", "prebwd_adam": "k_preprocess_backward<3>"}
+# the kernel of each single-kernel phase; the forward and backward blend phases also run their
+# segment plan, item lists and gradient gather, so their event time is not one kernel's
+KERNEL_OF = {"preprocess": "k_preprocess<3>", "prebwd_adam": "k_preprocess_backward<3>"}
 
 # HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE passes over this workload,
 # each scaled by the factor the same counter reads for a plain copy of known size; keyed by
 # the SHA-256 of the kernel's source file, so a changed kernel reports null
 COUNTER_TRAFFIC = {
-    "preprocess": {"source": "preprocess.hip", "bytes": 1168086935,
-                   "sha256": "0a00a1b39df4044c4fd1d2abd3b5f77f22a9d8552ef8f074fc6ed43e694036e4"},
-    "forward": {"source": "blend.hip", "bytes": 2871083484,
-                "sha256": "2f879994c873411e8102ea12364b14ad6c1cc2962a6f434568ee3a45c83cf482"},
-    "backward_blend": {"source": "blend.hip", "bytes": 4606070019,
-                       "sha256": "2f879994c873411e8102ea12364b14ad6c1cc2962a6f434568ee3a45c83cf482"},
-    "prebwd_adam": {"source": "preprocess.hip", "bytes": 5808397827,
-                    "sha256": "0a00a1b39df4044c4fd1d2abd3b5f77f22a9d8552ef8f074fc6ed43e694036e4"},
+    "preprocess": {"source": "preprocess.hip", "bytes": 1200086935,
+                   "sha256": "aba7b7749fff13f5b0d26f7edb4ffb3da7228f17b9d14e12970bdf8069bf5314"},
+    "prebwd_adam": {"source": "preprocess.hip", "bytes": 5808395587,
+                    "sha256": "aba7b7749fff13f5b0d26f7edb4ffb3da7228f17b9d14e12970bdf8069bf5314"},
 }
 
 
@@ -329,25 +324,19 @@ def main():
     log("[bench] per-phase ms: " + ", ".join(f"{k} {v:.3f}" for k, v in ph_ms.items()))
     log(f"[bench] {ms_per_step:.3f} ms/step, {total_blends / wall:.4g} blends/s, K mean {np.mean(ks):.0f}")
 
-    # roofline of the dominant single-kernel phase (bin_and_sort is a multi-kernel phase):
-    # HBM-bound phases against 8 TB/s, the blends against the fp32 vector peak
+    # roofline of the dominant kernel among the single-kernel phases (the longest kernel of the
+    # step), HBM-bound: algorithmic bytes per launch / its event time against 8 TB/s
     Kmean = float(np.mean(ks))
     n_vis = N
     sums = blends.cpu().tolist()
     per_launch = [x / args.steps for x in sums]  # examined, walked, composited per view
-    single = {ph: ph_ms[ph] for ph in ("preprocess", "forward", "backward_blend", "prebwd_adam")}
+    single = {ph: ph_ms[ph] for ph in KERNEL_OF}
     dom = max(single, key=single.get)
     sec = ph_ms[dom] * 1e-3
-    if dom in ("forward", "backward_blend"):
-        work = alg_flops(dom, *per_launch)
-        achieved = work / sec / 1e12
-        roof = {"bound": "alu", "achieved": round(achieved, 3), "peak": round(ALU_PEAK_TFLOPS, 1),
-                "unit": "TFLOP/s", "frac": round(achieved / ALU_PEAK_TFLOPS, 4)}
-    else:
-        work = alg_bytes(dom, N, R, Kmean, P, T, n_vis)
-        achieved = work / sec / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    work = alg_bytes(dom, N, R, Kmean, P, T, n_vis)
+    achieved = work / sec / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4)}
     roof.update({"traffic": counter_traffic(dom), "kernel": KERNEL_OF[dom], "work_per_launch": work,
                  "ms_per_launch": round(ph_ms[dom], 4)})
     per_phase = {}
