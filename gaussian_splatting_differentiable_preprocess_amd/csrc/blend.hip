@@ -19,8 +19,8 @@
 // (a skipped record has alpha < 1/255 at that pixel).  The forward's quadrant waves are
 // independent (no workgroup barrier).  The forward also leaves, per pixel and chunk, the 64-bit
 // mask of the chunk's entries it composited; the backward walks exactly those entries (per
-// pixel row of 8 lanes, whose sums are formed with DPP), so no record is tested twice.  The
-// backward's waves share per-entry gradient sums in LDS.
+// 2x2 pixel block of 4 lanes, whose sums are formed with DPP), so no record is tested twice.
+// The backward's waves share per-entry gradient sums in LDS.
 // Workgroup b renders tile b: the hardware deals consecutive workgroups to the 8 XCDs in turn,
 // which spreads the (very uneven) per-tile work evenly over them.  Bound: VALU /
 // transcendental and LDS, not HBM.
@@ -56,29 +56,23 @@ __device__ __forceinline__ uint32_t dpp_or(uint32_t x) {
   return x | (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, true);
 }
 
-// Sums each of N values over each group of 8 lanes (a pixel row of a quadrant); every lane
-// gets its group's sums.  The steps are interleaved across the N values so a DPP read never
-// waits on the instruction just before it.  Every lane of the wave must be active.  (Groups
-// of 16 lanes, two pixel rows, take fewer iterations but a fourth step; measured slower.)
+// Sums each of N values over each group of 4 consecutive lanes (a DPP quad); every lane gets
+// its group's sums.  Every lane of the wave must be active.
 template <int N>
-__device__ __forceinline__ void row8_sum(float* v) {
+__device__ __forceinline__ void quad_sum(float* v) {
 #pragma unroll
-  for (int q = 0; q < N; ++q) v[q] = dpp_add<0xB1>(v[q]);   // quad_perm [1,0,3,2]
+  for (int q = 0; q < N; ++q) v[q] = dpp_add<0xB1>(v[q]);  // quad_perm [1,0,3,2]
 #pragma unroll
-  for (int q = 0; q < N; ++q) v[q] = dpp_add<0x4E>(v[q]);   // quad_perm [2,3,0,1]
-#pragma unroll
-  for (int q = 0; q < N; ++q) v[q] = dpp_add<0x141>(v[q]);  // row_half_mirror
+  for (int q = 0; q < N; ++q) v[q] = dpp_add<0x4E>(v[q]);  // quad_perm [2,3,0,1]
 }
 
-// OR of a 64-bit value over each group of 8 lanes; every lane of the wave must be active.
-__device__ __forceinline__ unsigned long long row8_or(unsigned long long m) {
+// OR of a 64-bit value over each group of 4 consecutive lanes; every lane must be active.
+__device__ __forceinline__ unsigned long long quad_or(unsigned long long m) {
   uint32_t lo = (uint32_t)m, hi = (uint32_t)(m >> 32);
   lo = dpp_or<0xB1>(lo);
   hi = dpp_or<0xB1>(hi);
   lo = dpp_or<0x4E>(lo);
   hi = dpp_or<0x4E>(hi);
-  lo = dpp_or<0x141>(lo);
-  hi = dpp_or<0x141>(hi);
   return ((unsigned long long)hi << 32) | lo;
 }
 
@@ -515,9 +509,9 @@ __global__ __launch_bounds__(kBlock) void k_blend_forward(
 // behind it, (C_final - C_boundary) / T_boundary; otherwise from T_final with nothing behind.
 // The segments of one tile are independent, so a long list is spread over many CUs.
 // Persistent workgroups take items from a counter in the workspace until none are left.
-// Each pixel row walks the entries its pixels composited (the forward's masks), back to front;
-// the row's nine gradient sums per entry go into the workgroup's LDS sums over a window of 256
-// entries, whose sums then go to the staging area, one row per (entry, tile).
+// Each 2x2 pixel block walks the entries its pixels composited (the forward's masks), back to
+// front; the block's nine gradient sums per entry go into the workgroup's LDS sums over a window
+// of 256 entries, whose sums then go to the staging area, one row per (entry, tile).
 // ---------------------------------------------------------------------------------------------
 __global__ __launch_bounds__(kBlock) void k_blend_backward(
     int W, int H, int TX, int TY, int64_t n, const float4* __restrict__ splat,
@@ -533,7 +527,9 @@ __global__ __launch_bounds__(kBlock) void k_blend_backward(
   __shared__ uint32_t s_item, s_mx[4];
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   Chunk& S = stg[w];
-  const int lx = lane & 7, ly = lane >> 3;
+  // lanes 4 q .. 4 q + 3 are the 2x2 pixel block q of the quadrant (blocks row-major, pixels
+  // row-major inside a block): each block reduces over one DPP quad
+  const int lx = ((lane >> 2) & 3) * 2 + (lane & 1), ly = (lane >> 4) * 2 + ((lane >> 1) & 1);
   const int pix = tile_pixel(w, lx, ly);
   const uint32_t shift = ws_hdr[0], n_items = ws_hdr[1];
 
@@ -619,20 +615,20 @@ __global__ __launch_bounds__(kBlock) void k_blend_backward(
           put(S, lane, cur);
           wave_sync_lds();
           // The entries this pixel composited in the chunk (the forward's mask): exactly those
-          // with power <= 0, alpha >= 1/255 in front of the pixel's stop.  Each pixel row of the
-          // quadrant (8 lanes) takes the entries any of its pixels composited, back to front,
-          // its lanes on the same entry; the row's nine sums are formed in registers and added
-          // to the window's sums by one lane of the row.
+          // with power <= 0, alpha >= 1/255 in front of the pixel's stop.  Each 2x2 pixel block
+          // of the quadrant (4 lanes) takes the entries any of its pixels composited, back to
+          // front, its lanes on the same entry; the block's nine sums are formed in registers
+          // and added to the window's sums by one lane of the block.
           const unsigned long long mine =
               cbase + j < mask_cap ? ((unsigned long long)mcur.y << 32) | mcur.x : 0ull;
-          unsigned long long rem = row8_or(mine);
+          unsigned long long rem = quad_or(mine);
           const uint32_t wbase = j * kChunk - wlo;  // window position of slot 0
           for (;;) {
             const bool has = rem != 0ull;
             if (__ballot(has) == 0ull) break;
             const int e = has ? highest_bit(rem) : 0;
             rem &= ~(1ull << e);
-            const float4 g = S.geo[e];  // one address per row: a broadcast within the row
+            const float4 g = S.geo[e];  // one address per block: a broadcast within the block
             const float4 cl = S.col[e];
             const float cb = S.b[e];
             const float dx = pxc - g.x, dy = pyc - g.y;
@@ -666,8 +662,8 @@ __global__ __launch_bounds__(kBlock) void k_blend_backward(
               S2 = alpha * cb + om * S2;
               Tr = Tk;
             }
-            row8_sum<9>(v);  // every lane of a pixel row holds the row's sums
-            if (lx == 0 && has) {
+            quad_sum<9>(v);  // every lane of a pixel block holds the block's sums
+            if ((lane & 3) == 0 && has) {
               // dL/du = (A m_x + B m_y), dL/dv = (B m_x + C m_y), dL/dA = -m_xx / 2,
               // dL/dB = -m_xy, dL/dC = -m_yy / 2 with A = -2 nA, B = -nB, C = -2 nC
               const uint32_t ws = wbase + (uint32_t)e;
