@@ -48,9 +48,9 @@ def alg_bytes(phase, N, R, K, P, T, n_vis):
         return K * 40 + P * 20 + T * 8
     if phase == "loss":                # image + target in, dL/dI out
         return P * 36
-    if phase == "backward_blend":      # entries + pixels (dL/dI, T, last) + grad2d written once
+    if phase == "backward_blend":      # entries + pixels (dL/dI, T, last) + one 2D gradient per Gaussian out
         return K * 40 + P * 20 + T * 8 + 36 * n_vis
-    if phase == "prebwd_adam":         # params, m, v, grad2d in; params, m, v out
+    if phase == "prebwd_adam":         # params, m, v, one 2D gradient per Gaussian in; params, m, v out
         return N * (24 * R + 36)
     return 0
 
@@ -286,8 +286,9 @@ def main():
         gsmi.loss_l1(3 * P, buf.image, targets[view], buf.loss, buf.dLdI, buf.loss_ws)
         if ev is not None:
             ev[4].record()
+        # the fused path leaves the per-intersection sums staged for the preprocess backward
         gsmi.render_backward(buf.scene, None, cam, buf.proj, buf.vals, buf.ranges, bg, buf.T_final, buf.last,
-                             buf.dLdI, buf.grad2d, buf.render_ws)
+                             buf.dLdI, buf.grad2d if args.unfused_adam else None, buf.render_ws)
         if ev is not None:
             ev[5].record()
         adam = gsmi.make_adam(m, v, t, 1e-3)
@@ -295,7 +296,7 @@ def main():
             gsmi.preprocess_backward(buf.scene, p, cam, buf.grad2d, grads)
             gsmi.adam_step(R * N, p, grads, adam)
         else:
-            gsmi.preprocess_backward(buf.scene, p, cam, buf.grad2d, None, adam)
+            gsmi.preprocess_backward_staged(buf.scene, p, cam, buf.proj, buf.render_ws, None, adam)
         if ev is not None:
             ev[6].record()
         return K

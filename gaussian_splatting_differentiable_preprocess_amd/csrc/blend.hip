@@ -930,9 +930,10 @@ hipError_t launch_blend_backward(const CamK& cam, int64_t n, const gs_splat* spl
                      bg0, bg1, bg2, T_final, last_contrib, dLdI, ws.hdr, (const uint32_t*)ws.bnd_off,
                      (const uint2*)ws.items, (const float4*)ws.slots, (const uint2*)ws.masks, ws.mask_cap,
                      (const uint32_t*)ws.goff, (const uint32_t*)ws.goff_blk, ws.staging, ws.staging_cap);
-  hipLaunchKernelGGL(k_gather_grad2d, dim3((unsigned)ceil_div(n, (int64_t)kBlock)), dim3(kBlock), 0, s, n, tiles,
-                     (const uint32_t*)ws.goff, (const uint32_t*)ws.goff_blk, (const float*)ws.staging,
-                     ws.staging_cap, grad2d);
+  if (grad2d)  // else the sums stay staged for the preprocess backward
+    hipLaunchKernelGGL(k_gather_grad2d, dim3((unsigned)ceil_div(n, (int64_t)kBlock)), dim3(kBlock), 0, s, n,
+                       tiles, (const uint32_t*)ws.goff, (const uint32_t*)ws.goff_blk, (const float*)ws.staging,
+                       ws.staging_cap, grad2d);
   return hipGetLastError();
 }
 

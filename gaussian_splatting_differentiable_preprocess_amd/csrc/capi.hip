@@ -233,19 +233,26 @@ int gs_loss_l1(int64_t count, const float* image, const float* target, float* lo
   return e == hipSuccess ? ok() : hip_fail(e, "gs_loss_l1");
 }
 
-int gs_preprocess_backward(const gs_scene* scene, float* params, const gs_camera* cam,
-                           const float* grad2d, float* grads, const gs_adam* adam, hipStream_t stream) {
-  int st;
-  if ((st = check_scene(scene)) || (st = check_camera(cam)) || (st = check_adam(adam))) return st;
-  if (scene->n > 0 && (!params || !grad2d)) return fail(GS_ERR_INVALID_ARGUMENT, "params / grad2d is null");
-  if (scene->n > 0 && !grads && !adam)
-    return fail(GS_ERR_INVALID_ARGUMENT, "grads is null and no adam update requested");
+}  // extern "C"
+
+namespace {
+// The preprocess backward from grad2d, or (grad2d null) from the sums staged in ws.
+int run_preprocess_backward(const gs_scene* scene, float* params, const gs_camera* cam, const float* grad2d,
+                            const gsmi::RenderWs* ws, const uint32_t* tiles, float* grads, const gs_adam* adam,
+                            hipStream_t stream, const char* who) {
   PrebwdArgs a{};
   a.n = scene->n;
   a.ld = scene->ld;
   a.deg = scene->sh_degree;
   a.params = params;
   a.grad2d = grad2d;
+  if (!grad2d) {
+    a.staging = ws->staging;
+    a.goff = ws->goff;
+    a.goff_blk = ws->goff_blk;
+    a.tiles = tiles;
+    a.staging_cap = ws->staging_cap;
+  }
   a.grads = grads;
   if (adam) {
     a.m = adam->m;
@@ -261,7 +268,37 @@ int gs_preprocess_backward(const gs_scene* scene, float* params, const gs_camera
     a.inv_bc2 = c.inv_bc2;
   }
   const hipError_t e = launch_preprocess_backward(a, make_cam(*cam), stream);
-  return e == hipSuccess ? ok() : hip_fail(e, "gs_preprocess_backward");
+  return e == hipSuccess ? ok() : hip_fail(e, who);
+}
+}  // namespace
+
+extern "C" {
+
+int gs_preprocess_backward(const gs_scene* scene, float* params, const gs_camera* cam,
+                           const float* grad2d, float* grads, const gs_adam* adam, hipStream_t stream) {
+  int st;
+  if ((st = check_scene(scene)) || (st = check_camera(cam)) || (st = check_adam(adam))) return st;
+  if (scene->n > 0 && (!params || !grad2d)) return fail(GS_ERR_INVALID_ARGUMENT, "params / grad2d is null");
+  if (scene->n > 0 && !grads && !adam)
+    return fail(GS_ERR_INVALID_ARGUMENT, "grads is null and no adam update requested");
+  return run_preprocess_backward(scene, params, cam, grad2d, nullptr, nullptr, grads, adam, stream,
+                                 "gs_preprocess_backward");
+}
+
+int gs_preprocess_backward_staged(const gs_scene* scene, float* params, const gs_camera* cam, gs_proj proj,
+                                  const void* render_ws, size_t render_ws_bytes, float* grads,
+                                  const gs_adam* adam, hipStream_t stream) {
+  int st;
+  if ((st = check_scene(scene)) || (st = check_camera(cam)) || (st = check_adam(adam))) return st;
+  if (scene->n > 0 && !params) return fail(GS_ERR_INVALID_ARGUMENT, "params is null");
+  if (scene->n > 0 && !proj.tiles) return fail(GS_ERR_INVALID_ARGUMENT, "proj.tiles is null");
+  if (scene->n > 0 && !grads && !adam)
+    return fail(GS_ERR_INVALID_ARGUMENT, "grads is null and no adam update requested");
+  RenderWs ws;
+  if (!render_ws || !render_ws_layout(const_cast<void*>(render_ws), render_ws_bytes, (int)n_tiles(*cam), scene->n, &ws))
+    return fail(GS_ERR_INVALID_ARGUMENT, "render workspace too small or not 256-byte aligned");
+  return run_preprocess_backward(scene, params, cam, nullptr, &ws, proj.tiles, grads, adam, stream,
+                                 "gs_preprocess_backward_staged");
 }
 
 int gs_render_backward(const gs_scene* scene, float* params, const gs_camera* cam, gs_proj proj,
@@ -278,7 +315,6 @@ int gs_render_backward(const gs_scene* scene, float* params, const gs_camera* ca
   RenderWs ws;
   if (!render_ws_layout(render_ws, render_ws_bytes, (int)n_tiles(*cam), scene->n, &ws))
     return fail(GS_ERR_INVALID_ARGUMENT, "render workspace too small or not 256-byte aligned");
-  if (scene->n > 0 && !grad2d) return fail(GS_ERR_INVALID_ARGUMENT, "grad2d is null");
   if (scene->n > 0 && !proj.tiles) return fail(GS_ERR_INVALID_ARGUMENT, "proj.tiles is null");
   if (scene->n > 0 && (grads || adam) && !params) return fail(GS_ERR_INVALID_ARGUMENT, "params is null");
   if (reinterpret_cast<uintptr_t>(ranges) & 7u) return fail(GS_ERR_INVALID_ARGUMENT, "ranges must be 8-byte aligned");
@@ -288,7 +324,8 @@ int gs_render_backward(const gs_scene* scene, float* params, const gs_camera* ca
                                              bg[2], T_final, last_contrib, dL_dimage, grad2d, ws, stream);
   if (e != hipSuccess) return hip_fail(e, "gs_render_backward (blend)");
   if (!grads && !adam) return ok();  // backward blend only
-  return gs_preprocess_backward(scene, params, cam, grad2d, grads, adam, stream);
+  return run_preprocess_backward(scene, params, cam, grad2d, &ws, proj.tiles, grads, adam, stream,
+                                 "gs_render_backward (preprocess backward)");
 }
 
 int gs_adam_step(int64_t count, float* params, const float* grads, const gs_adam* adam, hipStream_t stream) {

@@ -52,7 +52,14 @@ struct PrebwdArgs {
   int64_t n, ld;
   int deg;
   float* params;
-  const float* grad2d;
+  const float* grad2d;  // null: each Gaussian's nine values are the sum of its staged rows
+  // the backward blend's staged per-intersection sums (used when grad2d is null): Gaussian i's
+  // rows are staging[9 (goff_blk[i / kGoffBlock] + goff[i] + j)], j < tiles[i]
+  const float* staging;
+  const uint32_t* goff;
+  const uint32_t* goff_blk;
+  const uint32_t* tiles;
+  uint64_t staging_cap;
   float* grads;      // nullable when adam
   float* m;          // nullable: no Adam
   float* v;

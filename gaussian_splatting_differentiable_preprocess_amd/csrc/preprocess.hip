@@ -295,7 +295,23 @@ __global__ __launch_bounds__(kBlock) void k_preprocess_backward(PrebwdArgs A, Ca
     for (int ch = 0; ch < 3; ++ch) f[k][ch] = __builtin_nontemporal_load(prm + (11 + 3 * k + ch) * ld + i);
 
   if (P.vis) {
-    const float* g2 = A.grad2d + 9 * i;  // this Gaussian's nine values, contiguous
+    float g2[9];  // this Gaussian's nine values: grad2d, or the sum of its staged rows
+    if (A.grad2d) {
+#pragma unroll
+      for (int k = 0; k < 9; ++k) g2[k] = A.grad2d[9 * i + k];
+    } else {
+      // the same rows in the same order as the gather into grad2d, so the values are identical
+#pragma unroll
+      for (int k = 0; k < 9; ++k) g2[k] = 0.f;
+      const uint32_t t = A.tiles[i];
+      const uint64_t base = (uint64_t)A.goff_blk[i / kGoffBlock] + A.goff[i];
+      for (uint32_t j = 0; j < t; ++j) {
+        if (base + j >= A.staging_cap) break;
+        const float* e = A.staging + 9 * (base + j);
+#pragma unroll
+        for (int k = 0; k < 9; ++k) g2[k] += e[k];
+      }
+    }
     const float gu = g2[0], gv = g2[1];
     const float gA = g2[2], gB = g2[3], gC = g2[4];
     const float go = g2[5];

@@ -24,7 +24,7 @@ SPLAT_FLOATS = 12  # 48-byte record: u, v, radius_x, radius_y | A, B, C, opacity
 EXPORTS = (
     "gs_version", "gs_last_error", "gs_preprocess", "gs_bin_and_sort_workspace", "gs_bin_and_sort",
     "gs_render_workspace", "gs_render_workspace_capacity", "gs_render_forward", "gs_loss_l1_workspace", "gs_loss_l1", "gs_render_backward",
-    "gs_preprocess_backward", "gs_adam_step",
+    "gs_preprocess_backward", "gs_preprocess_backward_staged", "gs_adam_step",
 )
 
 
@@ -88,6 +88,7 @@ def load(path: str = LIB_PATH):
     L.gs_render_backward.argtypes = [SP, P, CP, GsProj, P, P, ctypes.POINTER(ctypes.c_float), P, P, P,
                                      P, P, AP, P, sz, P]
     L.gs_preprocess_backward.argtypes = [SP, P, CP, P, P, AP, P]
+    L.gs_preprocess_backward_staged.argtypes = [SP, P, CP, GsProj, P, sz, P, AP, P]
     L.gs_adam_step.argtypes = [i64, P, P, AP, P]
     for name in EXPORTS:
         if name not in ("gs_version", "gs_last_error"):
@@ -249,6 +250,15 @@ def preprocess_backward(scene: GsScene, params, cam: GsCamera, grad2d, grads=Non
     _check(load().gs_preprocess_backward(ctypes.byref(scene), _ptr(params), ctypes.byref(cam), _ptr(grad2d),
                                          _ptr(grads), ctypes.byref(adam) if adam is not None else None,
                                          _stream(stream)))
+
+
+def preprocess_backward_staged(scene: GsScene, params, cam: GsCamera, proj: Proj, render_ws, grads=None,
+                               adam: GsAdam | None = None, stream=None):
+    """The preprocess backward from the sums a render_backward(grad2d=None) left in render_ws."""
+    _check(load().gs_preprocess_backward_staged(ctypes.byref(scene), _ptr(params), ctypes.byref(cam), proj.c(),
+                                                _ptr(render_ws), _nbytes(render_ws), _ptr(grads),
+                                                ctypes.byref(adam) if adam is not None else None,
+                                                _stream(stream)))
 
 
 def adam_step(count, params, grads, adam: GsAdam, stream=None):

@@ -206,12 +206,15 @@ int gs_loss_l1(int64_t count, const float* image, const float* target, float* lo
                float* dL_dimage, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Backward of the step from dL/dimage.
- *   grad2d[ld][9]  out: per-Gaussian dL/d(u, v, conic_a, conic_b, conic_c, opacity, r, g, b)
- *                  from the reverse-order backward blend, the nine values of Gaussian i at
- *                  grad2d + 9 i, for i < n (rows n..ld-1 are not written).  Each
+ *   grad2d[ld][9]  out, nullable: per-Gaussian dL/d(u, v, conic_a, conic_b, conic_c, opacity,
+ *                  r, g, b) from the reverse-order backward blend, the nine values of Gaussian i
+ *                  at grad2d + 9 i, for i < n (rows n..ld-1 are not written).  Each
  *                  intersection's sums are staged in render_ws and each Gaussian's are added
- *                  in the order of its tile rect; within an intersection the pixel-row sums
- *                  meet in LDS atomics, so the summation order is not fixed.
+ *                  in the order of its tile rect; within an intersection the pixel-block sums
+ *                  meet in LDS atomics, so the summation order is not fixed.  Null: the sums
+ *                  stay staged in render_ws, and the preprocess backward (here, with grads or
+ *                  adam, or gs_preprocess_backward_staged later) adds each Gaussian's in the
+ *                  same order itself, giving the same values without the grad2d round trip.
  *   grads[R][ld]   out, nullable: dL/dparams by the chain rule through the preprocess
  *   adam           nullable: when given, the preprocess backward also applies the Adam
  *                  update to params, adam->m and adam->v in place (params is then written)
@@ -233,6 +236,15 @@ int gs_render_backward(const gs_scene* scene, float* params, const gs_camera* ca
 int gs_preprocess_backward(const gs_scene* scene, float* params, const gs_camera* cam,
                            const float* grad2d, float* grads, const gs_adam* adam,
                            hipStream_t stream);
+
+/* Preprocess backward alone, reading each Gaussian's nine dL/d(2D) values as the sum of its
+ * intersections' sums that gs_render_backward (called with grad2d = NULL on the same render_ws,
+ * camera and proj) left staged in render_ws, added in the order of the Gaussian's tile rect:
+ * the values gs_render_backward would have written into grad2d.  proj.tiles is the
+ * preprocess output the lists were built from.  Otherwise as gs_preprocess_backward. */
+int gs_preprocess_backward_staged(const gs_scene* scene, float* params, const gs_camera* cam, gs_proj proj,
+                                  const void* render_ws, size_t render_ws_bytes, float* grads,
+                                  const gs_adam* adam, hipStream_t stream);
 
 /* Adam over `count` floats, in place: m = b1 m + (1-b1) g; v = b2 v + (1-b2) g^2;
  * params -= lr (m / (1-b1^t)) / (sqrt(v / (1-b2^t)) + eps).  adam->m and adam->v are flat

@@ -121,3 +121,18 @@ def test_render_calls_reject_a_missing_or_short_workspace():
     rc = L.gs_render_backward(ctypes.byref(sc), None, ctypes.byref(cam), proj, p, p, bg, p, p, p, p, None, None,
                               p, 16, None)
     assert rc == gsmi.GS_ERR_INVALID_ARGUMENT and "workspace" in gsmi.last_error()
+    # the preprocess backward from staged sums: the same workspace checks, and params, tiles
+    # and an output required
+    ad = gsmi.GsAdam(4096, 4096, 1, 1e-3, 0.9, 0.999, 1e-8)
+    for ws, nb in ((None, need), (p, 16), (ctypes.c_void_p(4096 + 64), need)):
+        rc = L.gs_preprocess_backward_staged(ctypes.byref(sc), p, ctypes.byref(cam), proj, ws, nb, None,
+                                             ctypes.byref(ad), None)
+        assert rc == gsmi.GS_ERR_INVALID_ARGUMENT and "workspace" in gsmi.last_error()
+    rc = L.gs_preprocess_backward_staged(ctypes.byref(sc), None, ctypes.byref(cam), proj, p, need, None,
+                                         ctypes.byref(ad), None)
+    assert rc == gsmi.GS_ERR_INVALID_ARGUMENT and "params" in gsmi.last_error()
+    rc = L.gs_preprocess_backward_staged(ctypes.byref(sc), p, ctypes.byref(cam), gsmi.GsProj(4096, None, 4096, 4096),
+                                         p, need, None, ctypes.byref(ad), None)
+    assert rc == gsmi.GS_ERR_INVALID_ARGUMENT and "tiles" in gsmi.last_error()
+    rc = L.gs_preprocess_backward_staged(ctypes.byref(sc), p, ctypes.byref(cam), proj, p, need, None, None, None)
+    assert rc == gsmi.GS_ERR_INVALID_ARGUMENT and "grads" in gsmi.last_error()
