@@ -88,9 +88,9 @@ KERNEL_OF = {"preprocess": "k_preprocess<3>", "prebwd_adam": "k_preprocess_backw
 # the SHA-256 of the kernel's source file, so a changed kernel reports null
 COUNTER_TRAFFIC = {
     "preprocess": {"source": "preprocess.hip", "bytes": 1200086935,
-                   "sha256": "aba7b7749fff13f5b0d26f7edb4ffb3da7228f17b9d14e12970bdf8069bf5314"},
-    "prebwd_adam": {"source": "preprocess.hip", "bytes": 5808395587,
-                    "sha256": "aba7b7749fff13f5b0d26f7edb4ffb3da7228f17b9d14e12970bdf8069bf5314"},
+                   "sha256": "7c692f702ba0d64fc7f1df3232058bd36e3e072e8e7729102dcc488c797b6a58"},
+    "prebwd_adam": {"source": "preprocess.hip", "bytes": 5943347106,
+                    "sha256": "7c692f702ba0d64fc7f1df3232058bd36e3e072e8e7729102dcc488c797b6a58"},
 }
 
 
