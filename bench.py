@@ -52,6 +52,8 @@ def alg_bytes(phase, N, R, K, P, T, n_vis):
         return K * 40 + P * 20 + T * 8 + 36 * n_vis
     if phase == "prebwd_adam":         # params, m, v, one 2D gradient per Gaussian in; params, m, v out
         return N * (24 * R + 36)
+    if phase == "image_pass":          # the fused forward + L1 + backward blend
+        return sum(alg_bytes(ph, N, R, K, P, T, n_vis) for ph in ("forward", "loss", "backward_blend"))
     return 0
 
 
@@ -76,6 +78,8 @@ def alg_flops(phase, examined, walked, composited):
         return FLOPS_EVAL * examined + FLOPS_FWD_BLEND * composited
     if phase == "backward_blend":      # walks last_contrib entries per pixel, back to front
         return FLOPS_EVAL * walked + FLOPS_BWD_BLEND * composited
+    if phase == "image_pass":          # both blends in the fused image pass
+        return sum(alg_flops(ph, examined, walked, composited) for ph in ("forward", "backward_blend"))
     return 0
 
 
@@ -217,6 +221,8 @@ def main():
     ap.add_argument("--config", default="gyroid_4m_2048")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--unfused-adam", action="store_true", help="separate Adam kernel instead of the fused one")
+    ap.add_argument("--separate-passes", action="store_true",
+                    help="forward, L1 loss and backward blend as three calls instead of the fused image pass")
     ap.add_argument("--detail", default=None, help="write a detailed JSON record to this path")
     ap.add_argument("--views", type=int, default=0,
                     help="use only the first N orbit views (short profiling runs); default all")
@@ -267,38 +273,45 @@ def main():
     gcams = [gsmi.make_camera(c) for c in cams]
     blends = torch.zeros(3, dtype=torch.int64, device="cuda")
     bg = (0.0, 0.0, 0.0)
-    phases = ["preprocess", "bin_and_sort", "forward", "loss", "backward_blend", "prebwd_adam"]
+    fused = not args.separate_passes
+    phases = (["preprocess", "bin_and_sort", "image_pass", "prebwd_adam"] if fused else
+              ["preprocess", "bin_and_sort", "forward", "loss", "backward_blend", "prebwd_adam"])
 
     def step(t, view, ev=None):
         cam = gcams[view]
-        if ev is not None:
-            ev[0].record()
+        marks = iter(ev or ())
+
+        def mark():
+            e = next(marks, None)
+            if e is not None:
+                e.record()
+
+        mark()
         gsmi.preprocess(buf.scene, p, cam, buf.proj)
-        if ev is not None:
-            ev[1].record()
+        mark()
         K = gsmi.bin_and_sort(buf.scene, cam, buf.proj, buf.ws, buf.k_capacity, buf.vals, buf.ranges)
-        if ev is not None:
-            ev[2].record()
-        gsmi.render_forward(cam, N, buf.proj.splat, buf.vals, buf.ranges, bg, buf.image, buf.T_final, buf.last,
-                            buf.render_ws, blend_count=blends)
-        if ev is not None:
-            ev[3].record()
-        gsmi.loss_l1(3 * P, buf.image, targets[view], buf.loss, buf.dLdI, buf.loss_ws)
-        if ev is not None:
-            ev[4].record()
-        # the fused path leaves the per-intersection sums staged for the preprocess backward
-        gsmi.render_backward(buf.scene, None, cam, buf.proj, buf.vals, buf.ranges, bg, buf.T_final, buf.last,
-                             buf.dLdI, buf.grad2d if args.unfused_adam else None, buf.render_ws)
-        if ev is not None:
-            ev[5].record()
+        mark()
+        g2 = buf.grad2d if args.unfused_adam else None
+        if fused:  # forward, L1 and backward blend in one kernel; the sums stay staged
+            gsmi.render_step(buf.scene, cam, buf.proj, buf.vals, buf.ranges, bg, targets[view], buf.image,
+                             buf.T_final, buf.last, buf.loss, buf.dLdI, buf.render_ws, grad2d=g2, blend_count=blends)
+            mark()
+        else:
+            gsmi.render_forward(cam, N, buf.proj.splat, buf.vals, buf.ranges, bg, buf.image, buf.T_final, buf.last,
+                                buf.render_ws, blend_count=blends)
+            mark()
+            gsmi.loss_l1(3 * P, buf.image, targets[view], buf.loss, buf.dLdI, buf.loss_ws)
+            mark()
+            gsmi.render_backward(buf.scene, None, cam, buf.proj, buf.vals, buf.ranges, bg, buf.T_final, buf.last,
+                                 buf.dLdI, g2, buf.render_ws)
+            mark()
         adam = gsmi.make_adam(m, v, t, 1e-3)
         if args.unfused_adam:
             gsmi.preprocess_backward(buf.scene, p, cam, buf.grad2d, grads)
             gsmi.adam_step(R * N, p, grads, adam)
         else:
             gsmi.preprocess_backward_staged(buf.scene, p, cam, buf.proj, buf.render_ws, None, adam)
-        if ev is not None:
-            ev[6].record()
+        mark()
         return K
 
     log(f"[bench] warmup {args.warmup} steps ...")
@@ -308,7 +321,7 @@ def main():
         step(t, w % V)
     torch.cuda.synchronize()
     blends.zero_()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)] for _ in range(args.steps)]
     ks = []
     log(f"[bench] timing {args.steps} steps ...")
     torch.cuda.synchronize()
@@ -344,7 +357,7 @@ def main():
     for ph in phases:
         d = {"ms": round(ph_ms[ph], 4),
              "alg_GBps": round(alg_bytes(ph, N, R, Kmean, P, T, n_vis) / (ph_ms[ph] * 1e-3) / 1e9, 1)}
-        if ph in ("forward", "backward_blend"):
+        if ph in ("forward", "backward_blend", "image_pass"):
             d["alg_TFLOPs"] = round(alg_flops(ph, *per_launch) / (ph_ms[ph] * 1e-3) / 1e12, 3)
         per_phase[ph] = d
     log(f"[bench] roofline: {json.dumps(roof)}")
@@ -371,6 +384,7 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": cfg.name, "gaussians": N, "sh_degree": cfg.sh_degree, "resolution": [W, H],
                    "views": V, "loss": "l1", "adam": "fused" if not args.unfused_adam else "separate",
+                   "image_pass": "fused" if fused else "separate",
                    "intersections_mean": round(Kmean), "intersections_min": int(min(ks)),
                    "intersections_max": int(max(ks))},
         "roofline": roof,

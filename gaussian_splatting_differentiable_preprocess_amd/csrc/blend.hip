@@ -196,6 +196,65 @@ __device__ __forceinline__ void wave_sync_lds() {
 __device__ __forceinline__ int lowest_bit(unsigned long long m) { return __builtin_ctzll(m); }
 __device__ __forceinline__ int highest_bit(unsigned long long m) { return 63 - __builtin_clzll(m); }
 
+// Inside the fused step (k_blend_step) one workgroup hands data to another: a tile's per-pixel
+// state, its composited masks and its work items.  Those accesses are relaxed atomics at device
+// scope, which bypass the per-XCD L2s (they are not coherent with one another), so no cache-wide
+// write-back or invalidate is needed.  Everywhere else (kDev false) they are plain accesses.
+template <bool kDev>
+__device__ __forceinline__ void put_u2(uint2* p, uint2 v) {
+  if constexpr (kDev)
+    __hip_atomic_store(reinterpret_cast<uint64_t*>(p), (uint64_t)v.x | ((uint64_t)v.y << 32), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  else
+    *p = v;
+}
+template <bool kDev>
+__device__ __forceinline__ uint2 get_u2(const uint2* p) {
+  if constexpr (kDev) {
+    const uint64_t x = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return make_uint2((uint32_t)x, (uint32_t)(x >> 32));
+  } else {
+    return *p;
+  }
+}
+template <bool kDev>
+__device__ __forceinline__ void put_f4(float4* p, float4 v) {
+  uint2* q = reinterpret_cast<uint2*>(p);
+  put_u2<kDev>(q, make_uint2(__float_as_uint(v.x), __float_as_uint(v.y)));
+  put_u2<kDev>(q + 1, make_uint2(__float_as_uint(v.z), __float_as_uint(v.w)));
+}
+template <bool kDev>
+__device__ __forceinline__ float4 get_f4(const float4* p) {
+  if constexpr (kDev) {
+    const uint2* q = reinterpret_cast<const uint2*>(p);
+    const uint2 a = get_u2<true>(q), b = get_u2<true>(q + 1);
+    return make_float4(__uint_as_float(a.x), __uint_as_float(a.y), __uint_as_float(b.x), __uint_as_float(b.y));
+  } else {
+    return *p;
+  }
+}
+template <bool kDev, typename T>
+__device__ __forceinline__ void put_32(T* p, T v) {
+  if constexpr (kDev)
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    *p = v;
+}
+template <bool kDev, typename T>
+__device__ __forceinline__ T get_32(const T* p) {
+  if constexpr (kDev)
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    return *p;
+}
+// Waits until every memory access this wave has issued has completed: its device-scope stores
+// are then visible to every XCD.
+__device__ __forceinline__ void drain_memory() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // ---------------------------------------------------------------------------------------------
 // Segment plan.  For every tile, its list length len decides
 //   items(t) = ceil(len / SEG) backward work items (0 for an empty tile),
@@ -302,10 +361,14 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_scan(const uint32_t* __re
     const uint32_t items = slots + tot[kPartNonEmpty] - tot[kPartLong + q];
     bnd_off[T] = slots;
     item_off[T] = items;
-    hdr[0] = (uint32_t)(kSegShiftMin + q);
-    hdr[1] = items;
-    hdr[2] = slots;
-    hdr[3] = 0u;
+    hdr[kHdrShift] = (uint32_t)(kSegShiftMin + q);
+    hdr[kHdrItems] = items;
+    hdr[kHdrSlots] = slots;
+    hdr[kHdrBwdNext] = 0u;
+    hdr[kHdrFwdNext] = 0u;
+    hdr[kHdrReady] = 0u;
+    hdr[kHdrRole] = 0u;
+    hdr[kHdrStall] = 0u;
   }
   __syncthreads();
   const int q = s_q;
@@ -344,7 +407,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_write(const uint2* __rest
     const uint2 rg = ranges[t];
     len = rg.y - rg.x;
   }
-  const uint32_t shift = hdr[0];
+  const uint32_t shift = hdr[kHdrShift];
   const uint32_t k = len ? ((len - 1u) >> shift) + 1u : 0u;
   const uint32_t sl = len > (1u << shift) ? k : 0u;
   const uint32_t pre_s = block_exscan_1024(sl, red32);  // (its barriers also publish cur)
@@ -356,13 +419,15 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_write(const uint2* __rest
   }
 }
 
-// The item list: one wave per tile writes the tile's items (tile, 0), (tile, 1), ...
+// The item list: one wave per tile writes the tile's items (tile, 0), (tile, 1), ...; for the
+// fused step (empty), the marker of a not yet published item instead.
+constexpr uint32_t kNoTile = 0xFFFFFFFFu;
 __global__ __launch_bounds__(kBlock) void k_seg_items(int T, const uint32_t* __restrict__ item_off,
-                                                      uint2* __restrict__ items) {
+                                                      uint2* __restrict__ items, bool empty) {
   const int t = (int)(blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6));
   if (t >= T) return;
   const uint32_t o = item_off[t], k = item_off[t + 1] - o;
-  for (uint32_t j = threadIdx.x & 63; j < k; j += 64) items[o + j] = make_uint2((uint32_t)t, j);
+  for (uint32_t j = threadIdx.x & 63; j < k; j += 64) items[o + j] = make_uint2(empty ? kNoTile : (uint32_t)t, j);
 }
 
 // pixel index inside its tile of lane (lx, ly) of quadrant wave w
@@ -374,18 +439,40 @@ __device__ __forceinline__ int tile_pixel(int w, int lx, int ly) {
 // Forward.  Besides the image, a tile whose list is longer than one segment leaves each pixel's
 // (T, C) at every segment boundary it reaches and its final (T, C) in the render workspace.
 // ---------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(kBlock) void k_blend_forward(
-    int W, int H, int TX, int T, int64_t n, const float4* __restrict__ splat,
-    const uint32_t* __restrict__ vals, const uint2* __restrict__ ranges, float bg0, float bg1,
-    float bg2, float* __restrict__ image, float* __restrict__ T_final, uint32_t* __restrict__ last_contrib,
-    uint32_t* __restrict__ n_examined, unsigned long long* __restrict__ blend_count,
-    const uint32_t* __restrict__ ws_hdr, const uint32_t* __restrict__ bnd_off, float4* __restrict__ slots,
-    uint2* __restrict__ masks, uint64_t mask_cap, const uint32_t* __restrict__ order) {
-  __shared__ Chunk stg[4];
-  // Longest lists first: a tile's waves walk its list alone, so the longest walks start at once
-  // and the short tiles fill in around them; consecutive workgroups (dealt to the 8 XCDs in
-  // turn) get lists of similar length.
-  const int tile = (int)order[blockIdx.x];
+struct FwdArgs {
+  int W, H, TX, T;
+  int64_t n;
+  const float4* splat;
+  const uint32_t* vals;
+  const uint2* ranges;
+  float bg0, bg1, bg2;
+  float* image;
+  float* T_final;
+  uint32_t* last_contrib;
+  uint32_t* n_examined;             // optional
+  unsigned long long* blend_count;  // optional
+  const uint32_t* bnd_off;
+  float4* slots;
+  uint2* masks;
+  uint64_t mask_cap;
+  const uint32_t* order;
+  // the fused step only: the L1 loss against the target image, per pixel
+  const float* target;
+  float* dLdI;
+  float* loss_part;  // per tile: sum over its pixels of |image - target|
+  float inv_n;       // 1 / (3 W H)
+};
+
+// One tile by the workgroup's four quadrant waves (kStep: the fused step, which also takes the
+// pixel's L1 loss and gradient and hands its state to other workgroups at device scope).
+template <bool kStep>
+__device__ void forward_tile(const FwdArgs& a, uint32_t shift, int tile, Chunk* stg) {
+  const int W = a.W, H = a.H, TX = a.TX;
+  const int64_t n = a.n;
+  const float4* __restrict__ splat = a.splat;
+  const uint32_t* __restrict__ vals = a.vals;
+  uint2* __restrict__ masks = a.masks;
+  const uint64_t mask_cap = a.mask_cap;
   const int tx = tile % TX, ty = tile / TX;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   Chunk& S = stg[w];
@@ -394,12 +481,12 @@ __global__ __launch_bounds__(kBlock) void k_blend_forward(
   const int px = xq + lx, py = yq + ly;
   const bool inside = px < W && py < H;
   const float pxc = (float)px + 0.5f, pyc = (float)py + 0.5f;
-  const uint2 rg = ranges[tile];
+  const uint2 rg = a.ranges[tile];
   const uint32_t start = rg.x, end = rg.y, len = end - start;
-  const uint32_t shift = ws_hdr[0], seg_mask = (1u << shift) - 1u;
+  const uint32_t seg_mask = (1u << shift) - 1u;
   const bool long_list = len > seg_mask + 1u;
   const int pix = tile_pixel(w, lx, ly);
-  float4* const st = slots + (size_t)(long_list ? bnd_off[tile] : 0u) * (kTile * kTile) + pix;
+  float4* const st = a.slots + (size_t)(long_list ? a.bnd_off[tile] : 0u) * (kTile * kTile) + pix;
   const uint64_t cbase = (uint64_t)(start / kChunk) + (uint64_t)tile;  // the tile's first mask chunk
 
   float Tr = 1.0f, c0 = 0.f, c1 = 0.f, c2 = 0.f;
@@ -418,12 +505,13 @@ __global__ __launch_bounds__(kBlock) void k_blend_forward(
     uint64_t pend_mc = ~0ull;
     for (uint32_t b0 = start; b0 < end; b0 += kChunk) {
       if (__ballot(!done) == 0ull) break;
-      if (pend_mc < mask_cap) masks[pend_mc * (kTile * kTile) + pix] = make_uint2((uint32_t)pend, (uint32_t)(pend >> 32));
+      if (pend_mc < mask_cap)
+        put_u2<kStep>(masks + pend_mc * (kTile * kTile) + pix, make_uint2((uint32_t)pend, (uint32_t)(pend >> 32)));
       const Raw nxt = load_raw(splat, gnext, n);  // next chunk in flight
       gnext = load_gid(vals, b0 + 2 * kChunk + lane, end, start);
       const uint32_t rel = b0 - start;
       if (long_list && rel != 0u && (rel & seg_mask) == 0u)  // state at segment boundary rel
-        st[(size_t)((rel >> shift) - 1u) * (kTile * kTile)] = make_float4(Tr, c0, c1, c2);
+        put_f4<kStep>(st + (size_t)((rel >> shift) - 1u) * (kTile * kTile), make_float4(Tr, c0, c1, c2));
       put(S, lane, cur);
       const Box bx = alpha_box(cur.uv.x, cur.uv.y, cur.abco.x, cur.abco.y, cur.abco.z, opacity_of(cur, n), xq, yq);
       // every lane takes part in the ballots: lane e holds record e's box
@@ -465,21 +553,39 @@ __global__ __launch_bounds__(kBlock) void k_blend_forward(
       wave_sync_lds();  // this chunk's reads finish before the next chunk is staged
       cur = nxt;
     }
-    if (pend_mc < mask_cap) masks[pend_mc * (kTile * kTile) + pix] = make_uint2((uint32_t)pend, (uint32_t)(pend >> 32));
+    if (pend_mc < mask_cap)
+      put_u2<kStep>(masks + pend_mc * (kTile * kTile) + pix, make_uint2((uint32_t)pend, (uint32_t)(pend >> 32)));
     if (long_list)  // final state
-      st[(size_t)((len - 1u) >> shift) * (kTile * kTile)] = make_float4(Tr, c0, c1, c2);
+      put_f4<kStep>(st + (size_t)((len - 1u) >> shift) * (kTile * kTile), make_float4(Tr, c0, c1, c2));
   }
 
+  float l1 = 0.f;  // the pixel's sum of |image - target| (fused step)
   if (inside) {
     const int64_t p = (int64_t)py * W + px;
-    image[3 * p + 0] = c0 + Tr * bg0;
-    image[3 * p + 1] = c1 + Tr * bg1;
-    image[3 * p + 2] = c2 + Tr * bg2;
-    T_final[p] = Tr;
-    last_contrib[p] = last;
-    if (n_examined) n_examined[p] = examined;
+    const float i0 = c0 + Tr * a.bg0, i1 = c1 + Tr * a.bg1, i2 = c2 + Tr * a.bg2;
+    a.image[3 * p + 0] = i0;
+    a.image[3 * p + 1] = i1;
+    a.image[3 * p + 2] = i2;
+    put_32<kStep>(a.T_final + p, Tr);
+    put_32<kStep>(a.last_contrib + p, last);
+    if (a.n_examined) a.n_examined[p] = examined;
+    if constexpr (kStep) {  // L1: dL/dI = sign(I - target) / (3 W H), sign(0) = 0
+      const float d0 = i0 - a.target[3 * p + 0], d1 = i1 - a.target[3 * p + 1], d2 = i2 - a.target[3 * p + 2];
+      const float q = a.inv_n;
+      put_32<true>(a.dLdI + 3 * p + 0, d0 > 0.f ? q : (d0 < 0.f ? -q : 0.f));
+      put_32<true>(a.dLdI + 3 * p + 1, d1 > 0.f ? q : (d1 < 0.f ? -q : 0.f));
+      put_32<true>(a.dLdI + 3 * p + 2, d2 > 0.f ? q : (d2 < 0.f ? -q : 0.f));
+      l1 = (fabsf(d0) + fabsf(d1)) + fabsf(d2);
+    }
   }
-  if (blend_count) {
+  if constexpr (kStep) {
+    for (int o = 32; o > 0; o >>= 1) l1 += __shfl_xor(l1, o, 64);
+    __shared__ float lpart[4];
+    if (lane == 0) lpart[w] = l1;
+    __syncthreads();
+    if (tid == 0) a.loss_part[tile] = (lpart[0] + lpart[1]) + (lpart[2] + lpart[3]);
+  }
+  if (a.blend_count) {
     unsigned long long ex = inside ? examined : 0u, lc = last, bl = blended;
     for (int o = 32; o > 0; o >>= 1) {
       ex += __shfl_xor(ex, o, 64);
@@ -497,7 +603,7 @@ __global__ __launch_bounds__(kBlock) void k_blend_forward(
     __syncthreads();
     if (tid < 3) {
       const unsigned long long x = (part[tid][0] + part[tid][1]) + (part[tid][2] + part[tid][3]);
-      if (x != 0ull) atomicAdd(blend_count + tid, x);
+      if (x != 0ull) atomicAdd(a.blend_count + tid, x);
     }
   }
 }
@@ -513,202 +619,330 @@ __global__ __launch_bounds__(kBlock) void k_blend_forward(
 // front; the block's nine gradient sums per entry go into the workgroup's LDS sums over a window
 // of 256 entries, whose sums then go to the staging area, one row per (entry, tile).
 // ---------------------------------------------------------------------------------------------
-__global__ __launch_bounds__(kBlock) void k_blend_backward(
-    int W, int H, int TX, int TY, int64_t n, const float4* __restrict__ splat,
-    const uint32_t* __restrict__ vals, const uint2* __restrict__ ranges, float bg0, float bg1,
-    float bg2, const float* __restrict__ T_final, const uint32_t* __restrict__ last_contrib,
-    const float* __restrict__ dLdI, uint32_t* __restrict__ ws_hdr,
-    const uint32_t* __restrict__ bnd_off, const uint2* __restrict__ items,
-    const float4* __restrict__ slots, const uint2* __restrict__ masks, uint64_t mask_cap,
-    const uint32_t* __restrict__ goff,
-    const uint32_t* __restrict__ goff_blk, float* __restrict__ staging, uint64_t staging_cap) {
-  __shared__ Chunk stg[4];              // per quadrant wave: its current chunk
-  __shared__ float acc[9][kWin];        // the workgroup's gradient sums over a window of entries
-  __shared__ uint32_t s_item, s_mx[4];
+struct BwdArgs {
+  int W, H, TX, TY;
+  int64_t n;
+  const float4* splat;
+  const uint32_t* vals;
+  const uint2* ranges;
+  float bg0, bg1, bg2;
+  const float* T_final;
+  const uint32_t* last_contrib;
+  const float* dLdI;
+  const uint32_t* bnd_off;
+  const float4* slots;
+  const uint2* masks;
+  uint64_t mask_cap;
+  const uint32_t* goff;
+  const uint32_t* goff_blk;
+  float* staging;
+  uint64_t staging_cap;
+};
+
+// LDS of a blending workgroup
+struct BlendShared {
+  Chunk stg[4];        // per quadrant wave: its current chunk
+  float acc[9][kWin];  // the backward's gradient sums over a window of entries
+  uint32_t mx[4];
+};
+
+// One work item (tile, segment k) by the workgroup's four quadrant waves (kStep: inside the
+// fused step, which reads the tile's state from other workgroups at device scope).
+template <bool kStep>
+__device__ void backward_item(const BwdArgs& a, uint32_t shift, uint2 it, BlendShared& sh) {
+  const int W = a.W, H = a.H, TX = a.TX, TY = a.TY;
+  const int64_t n = a.n;
+  const float4* __restrict__ splat = a.splat;
+  const uint32_t* __restrict__ vals = a.vals;
+  const uint2* __restrict__ masks = a.masks;
+  const uint64_t mask_cap = a.mask_cap;
+  const uint32_t* __restrict__ goff = a.goff;
+  const uint32_t* __restrict__ goff_blk = a.goff_blk;
+  float* __restrict__ staging = a.staging;
+  const uint64_t staging_cap = a.staging_cap;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  Chunk& S = stg[w];
+  Chunk& S = sh.stg[w];
+  float(*acc)[kWin] = sh.acc;
+  uint32_t* s_mx = sh.mx;
   // lanes 4 q .. 4 q + 3 are the 2x2 pixel block q of the quadrant (blocks row-major, pixels
   // row-major inside a block): each block reduces over one DPP quad
   const int lx = ((lane >> 2) & 3) * 2 + (lane & 1), ly = (lane >> 4) * 2 + ((lane >> 1) & 1);
   const int pix = tile_pixel(w, lx, ly);
-  const uint32_t shift = ws_hdr[0], n_items = ws_hdr[1];
+  const int tile = (int)it.x;
+  const uint32_t k = it.y;
+  const int tx = tile % TX, ty = tile / TX;
+  const int xq = tx * kTile + (w & 1) * 8, yq = ty * kTile + (w >> 1) * 8;
+  const int px = xq + lx, py = yq + ly;
+  const bool inside = px < W && py < H;
+  const float pxc = (float)px + 0.5f, pyc = (float)py + 0.5f;
+  const uint2 rg = a.ranges[tile];
+  const uint32_t start = rg.x, end = rg.y, len = rg.y - rg.x;
+  const uint64_t cbase = (uint64_t)(start / kChunk) + (uint64_t)tile;  // the tile's first mask chunk
 
+  float Tr = 0.f, g0 = 0.f, g1 = 0.f, g2 = 0.f, bgT = 0.f;
+  float S0 = 0.f, S1 = 0.f, S2 = 0.f;  // colour accumulated behind the current entry, / T_{k+1}
+  uint32_t last = 0;
+  if (inside) {
+    const int64_t p = (int64_t)py * W + px;
+    Tr = get_32<kStep>(a.T_final + p);
+    last = get_32<kStep>(a.last_contrib + p);
+    g0 = get_32<kStep>(a.dLdI + 3 * p);
+    g1 = get_32<kStep>(a.dLdI + 3 * p + 1);
+    g2 = get_32<kStep>(a.dLdI + 3 * p + 2);
+    bgT = Tr * (a.bg0 * g0 + a.bg1 * g1 + a.bg2 * g2);
+  }
+  uint32_t mx = last;  // the wave's largest last_contrib
+  for (int o = 32; o > 0; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor(mx, o, 64));
+  if (lane == 0) s_mx[w] = mx;
+  __syncthreads();
+  const uint32_t mxb = max(max(s_mx[0], s_mx[1]), max(s_mx[2], s_mx[3]));
+  const uint32_t seg_lo = k << shift;
+  const uint32_t seg_end = seg_lo + (1u << shift);
+  const uint32_t hi_w = min(seg_end, min(mx, len));   // this wave walks [seg_lo, hi_w)
+  const uint32_t hi_b = min(seg_end, min(mxb, len));  // the workgroup walks [seg_lo, hi_b)
+  if (seg_lo >= hi_b) return;  // workgroup-uniform: the segment lies behind every pixel's walk
+  if (last > seg_end) {  // the pixel's walk starts behind this segment
+    const float4* st = a.slots + (size_t)a.bnd_off[tile] * (kTile * kTile) + pix;
+    const float4 sb = get_f4<kStep>(st + (size_t)k * (kTile * kTile));
+    const float4 sf = get_f4<kStep>(st + (size_t)((len - 1u) >> shift) * (kTile * kTile));
+    const float inv = 1.0f / sb.x;  // T >= 1e-4 at every boundary
+    Tr = sb.x;
+    S0 = (sf.y - sb.y) * inv;
+    S1 = (sf.z - sb.z) * inv;
+    S2 = (sf.w - sb.w) * inv;
+  }
+
+  // windows of kWin entries, top down; the waves walk a window independently, then the
+  // workgroup adds the window's sums to grad2d
+  for (uint32_t wtop = hi_b; wtop > seg_lo;) {
+    const uint32_t wlo = seg_lo + ((wtop - 1u - seg_lo) & ~(uint32_t)(kWin - 1));
+#pragma unroll
+    for (int q = 0; q < 9; ++q) acc[q][tid] = 0.f;
+    __syncthreads();
+    const uint32_t whi = min(wtop, hi_w);
+    if (whi > wlo) {  // wave-uniform
+      // the window's chunks j (tile-relative entries [64 j, 64 j + 64)), top down
+      const uint32_t jlo = wlo / kChunk, jtop = (whi - 1u) / kChunk, nchunks = jtop - jlo + 1u;
+      // list entry of lane `lane` in chunk c (c >= nchunks: past the end of the list)
+      auto gid_of = [&](uint32_t c) -> uint32_t {
+        return load_gid(vals, c < nchunks ? start + (jtop - c) * kChunk + lane : end, end, start);
+      };
+      auto mask_of = [&](uint32_t c) -> uint2 {
+        const uint64_t mc = cbase + (c < nchunks ? jtop - c : jtop);
+        return get_u2<kStep>(masks + (mc < mask_cap ? mc : 0) * (kTile * kTile) + pix);
+      };
+      uint32_t gnext = gid_of(0);
+      Raw cur = load_raw(splat, gnext, n);
+      uint2 mcur = mask_of(0);
+      gnext = gid_of(1);
+      for (uint32_t c = 0; c < nchunks; ++c) {
+        const uint32_t j = jtop - c;
+        const Raw nxt = load_raw(splat, gnext, n);  // next chunk in flight
+        const uint2 mnxt = mask_of(c + 1);
+        gnext = gid_of(c + 2);
+        put(S, lane, cur);
+        wave_sync_lds();
+        // The entries this pixel composited in the chunk (the forward's mask): exactly those
+        // with power <= 0, alpha >= 1/255 in front of the pixel's stop.  Each 2x2 pixel block
+        // of the quadrant (4 lanes) takes the entries any of its pixels composited, back to
+        // front, its lanes on the same entry; the block's nine sums are formed in registers
+        // and added to the window's sums by one lane of the block.
+        const unsigned long long mine =
+            cbase + j < mask_cap ? ((unsigned long long)mcur.y << 32) | mcur.x : 0ull;
+        unsigned long long rem = quad_or(mine);
+        const uint32_t wbase = j * kChunk - wlo;  // window position of slot 0
+        for (;;) {
+          const bool has = rem != 0ull;
+          if (__ballot(has) == 0ull) break;
+          const int e = has ? highest_bit(rem) : 0;
+          rem &= ~(1ull << e);
+          const float4 g = S.geo[e];  // one address per block: a broadcast within the block
+          const float4 cl = S.col[e];
+          const float cb = S.b[e];
+          const float dx = pxc - g.x, dy = pyc - g.y;
+          const float power = eval_power(g.z, g.w, cl.x, dx, dy);
+          const float G = __expf(power);
+          const float oG = __fmul_rn(cl.y, G);  // the same operations as eval_oG
+          const float alpha = fminf(kAlphaMax, oG);
+          const bool act = has && ((mine >> e) & 1ull);
+          const float om = 1.0f - alpha;
+          const float rom = __builtin_amdgcn_rcpf(om);  // om >= 0.01
+          const float Tk = Tr * rom;                    // transmittance in front of this entry
+          const float wt = alpha * Tk;
+          const float cr = cl.z, cg = cl.w;
+          const float dL_dalpha = Tk * ((cr - S0) * g0 + (cg - S1) * g1 + (cb - S2) * g2) - bgT * rom;
+          const bool unclamped = act && oG <= kAlphaMax;  // alpha = o G depends on o and power
+          const float dpow = unclamped ? oG * dL_dalpha : 0.0f;
+          // moments of dL/dpower over the pixels; the conic gradients are linear in them
+          float v[9];
+          v[0] = dx * dpow;
+          v[1] = dy * dpow;
+          v[2] = dx * v[0];
+          v[3] = dy * v[0];
+          v[4] = dy * v[1];
+          v[5] = unclamped ? G * dL_dalpha : 0.0f;
+          v[6] = act ? wt * g0 : 0.0f;
+          v[7] = act ? wt * g1 : 0.0f;
+          v[8] = act ? wt * g2 : 0.0f;
+          if (act) {
+            S0 = alpha * cr + om * S0;
+            S1 = alpha * cg + om * S1;
+            S2 = alpha * cb + om * S2;
+            Tr = Tk;
+          }
+          quad_sum<9>(v);  // every lane of a pixel block holds the block's sums
+          if ((lane & 3) == 0 && has) {
+            // dL/du = (A m_x + B m_y), dL/dv = (B m_x + C m_y), dL/dA = -m_xx / 2,
+            // dL/dB = -m_xy, dL/dC = -m_yy / 2 with A = -2 nA, B = -nB, C = -2 nC
+            const uint32_t ws = wbase + (uint32_t)e;
+            atomicAdd(&acc[0][ws], -(2.0f * g.z * v[0] + g.w * v[1]));
+            atomicAdd(&acc[1][ws], -(g.w * v[0] + 2.0f * cl.x * v[1]));
+            atomicAdd(&acc[2][ws], -0.5f * v[2]);
+            atomicAdd(&acc[3][ws], -v[3]);
+            atomicAdd(&acc[4][ws], -0.5f * v[4]);
+#pragma unroll
+            for (int q = 5; q < 9; ++q) atomicAdd(&acc[q][ws], v[q]);
+          }
+        }
+        wave_sync_lds();  // this chunk's reads finish before the next chunk is staged
+        cur = nxt;
+        mcur = mnxt;
+      }
+    }
+    __syncthreads();
+    // one thread per entry of the window: the entry's sums go to its Gaussian's staging
+    // slot, the entry's place in the row-major order of the Gaussian's tile rect
+    if (wlo + (uint32_t)tid < wtop) {
+      float x[9];
+      bool any = false;
+#pragma unroll
+      for (int q = 0; q < 9; ++q) {
+        x[q] = acc[q][tid];
+        any = any || x[q] != 0.f;
+      }
+      if (any) {
+        const uint32_t gid = vals[start + wlo + tid];
+        const float4 q0 = splat[3 * (int64_t)gid];  // u, v, radius_x, radius_y
+        int x0, y0, x1, y1;
+        tile_rect(q0.x, q0.y, __float_as_int(q0.z), __float_as_int(q0.w), TX, TY, x0, y0, x1, y1);
+        const uint64_t slot = (uint64_t)goff_blk[gid / kGoffBlock] + goff[gid] +
+                              (uint32_t)((ty - y0) * (x1 - x0) + (tx - x0));
+        if (slot < staging_cap) {
+          float* o = staging + 9 * slot;
+#pragma unroll
+          for (int q = 0; q < 9; ++q) o[q] = x[q];
+        }
+      }
+    }
+    __syncthreads();  // the window's sums are read before the next window clears them
+    wtop = wlo;
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void k_blend_backward(BwdArgs a, uint32_t* __restrict__ ws_hdr,
+                                                           const uint2* __restrict__ items) {
+  __shared__ BlendShared sh;
+  __shared__ uint32_t s_item;
+  const uint32_t shift = ws_hdr[kHdrShift], n_items = ws_hdr[kHdrItems];
   for (;;) {
-    if (tid == 0) s_item = atomicAdd(ws_hdr + 3, 1u);
+    if (threadIdx.x == 0) s_item = atomicAdd(ws_hdr + kHdrBwdNext, 1u);
     __syncthreads();
     const uint32_t item = s_item;
     __syncthreads();  // every wave has read s_item before it is overwritten
     if (item >= n_items) break;
-    const uint2 it = items[item];
-    const int tile = (int)it.x;
-    const uint32_t k = it.y;
-    const int tx = tile % TX, ty = tile / TX;
-    const int xq = tx * kTile + (w & 1) * 8, yq = ty * kTile + (w >> 1) * 8;
-    const int px = xq + lx, py = yq + ly;
-    const bool inside = px < W && py < H;
-    const float pxc = (float)px + 0.5f, pyc = (float)py + 0.5f;
-    const uint2 rg = ranges[tile];
-    const uint32_t start = rg.x, end = rg.y, len = rg.y - rg.x;
-    const uint64_t cbase = (uint64_t)(start / kChunk) + (uint64_t)tile;  // the tile's first mask chunk
+    backward_item<false>(a, shift, items[item], sh);
+  }
+}
 
-    float Tr = 0.f, g0 = 0.f, g1 = 0.f, g2 = 0.f, bgT = 0.f;
-    float S0 = 0.f, S1 = 0.f, S2 = 0.f;  // colour accumulated behind the current entry, / T_{k+1}
-    uint32_t last = 0;
-    if (inside) {
-      const int64_t p = (int64_t)py * W + px;
-      Tr = T_final[p];
-      last = last_contrib[p];
-      g0 = dLdI[3 * p];
-      g1 = dLdI[3 * p + 1];
-      g2 = dLdI[3 * p + 2];
-      bgT = Tr * (bg0 * g0 + bg1 * g1 + bg2 * g2);
-    }
-    uint32_t mx = last;  // the wave's largest last_contrib
-    for (int o = 32; o > 0; o >>= 1) mx = max(mx, (uint32_t)__shfl_xor(mx, o, 64));
-    if (lane == 0) s_mx[w] = mx;
+// Persistent forward: the workgroups take tiles in the plan's order (list-length classes,
+// longest first) from a counter.  Longest first, a tile's waves walk its list alone, so the
+// longest walks start at once and the short tiles fill in around them.  A few workgroups per CU
+// suffice: fewer waves share each SIMD with the long walks, which then finish sooner.
+__global__ __launch_bounds__(kBlock) void k_blend_forward(FwdArgs a, uint32_t* __restrict__ hdr) {
+  __shared__ Chunk stg[4];
+  __shared__ uint32_t s_next;
+  const uint32_t shift = hdr[kHdrShift];
+  for (;;) {
+    if (threadIdx.x == 0) s_next = atomicAdd(hdr + kHdrFwdNext, 1u);
     __syncthreads();
-    const uint32_t mxb = max(max(s_mx[0], s_mx[1]), max(s_mx[2], s_mx[3]));
-    const uint32_t seg_lo = k << shift;
-    const uint32_t seg_end = seg_lo + (1u << shift);
-    const uint32_t hi_w = min(seg_end, min(mx, len));   // this wave walks [seg_lo, hi_w)
-    const uint32_t hi_b = min(seg_end, min(mxb, len));  // the workgroup walks [seg_lo, hi_b)
-    if (seg_lo >= hi_b) continue;  // workgroup-uniform: the segment lies behind every pixel's walk
-    if (last > seg_end) {  // the pixel's walk starts behind this segment
-      const float4* st = slots + (size_t)bnd_off[tile] * (kTile * kTile) + pix;
-      const float4 sb = st[(size_t)k * (kTile * kTile)];
-      const float4 sf = st[(size_t)((len - 1u) >> shift) * (kTile * kTile)];
-      const float inv = 1.0f / sb.x;  // T >= 1e-4 at every boundary
-      Tr = sb.x;
-      S0 = (sf.y - sb.y) * inv;
-      S1 = (sf.z - sb.z) * inv;
-      S2 = (sf.w - sb.w) * inv;
-    }
+    const uint32_t i = s_next;
+    __syncthreads();  // every wave has read s_next before it is overwritten
+    if (i >= (uint32_t)a.T) break;
+    forward_tile<false>(a, shift, (int)a.order[i], stg);
+  }
+}
 
-    // windows of kWin entries, top down; the waves walk a window independently, then the
-    // workgroup adds the window's sums to grad2d
-    for (uint32_t wtop = hi_b; wtop > seg_lo;) {
-      const uint32_t wlo = seg_lo + ((wtop - 1u - seg_lo) & ~(uint32_t)(kWin - 1));
-#pragma unroll
-      for (int q = 0; q < 9; ++q) acc[q][tid] = 0.f;
+// ---------------------------------------------------------------------------------------------
+// The fused step: forward, L1 loss and backward blend in one persistent kernel, so that the
+// backward's work fills the CUs the forward's long tile walks leave idle.
+//   - The first fwd_workers workgroups to start take tiles, longest first, and run the forward
+//     at raised wave priority.  When a tile is done (every wave's stores complete), its
+//     backward items are appended to the item list.
+//   - Every workgroup (the forward workers once the tiles run out) takes item slots in list
+//     order and waits until its slot has been published.
+// No workgroup waits for anything but a tile that a running workgroup has already taken, and
+// the forward never waits, so every wait ends; a wait is still bounded, and one that gives up
+// flags the stall word of the header and leaves its item undone.
+// ---------------------------------------------------------------------------------------------
+constexpr uint32_t kSpinLimit = 1u << 20;  // about a second of polling
+
+__global__ __launch_bounds__(kBlock) void k_blend_step(FwdArgs fa, BwdArgs ba, uint32_t* __restrict__ hdr,
+                                                       uint2* __restrict__ items,
+                                                       const uint32_t* __restrict__ item_off,
+                                                       uint32_t fwd_workers) {
+  __shared__ BlendShared sh;
+  __shared__ uint32_t s_next, s_pos;
+  __shared__ uint2 s_it;
+  const int tid = threadIdx.x;
+  const uint32_t shift = hdr[kHdrShift], n_items = hdr[kHdrItems];
+  if (tid == 0) s_next = atomicAdd(hdr + kHdrRole, 1u);
+  __syncthreads();
+  const bool forward_worker = s_next < fwd_workers;
+  __syncthreads();
+  if (forward_worker) {
+    __builtin_amdgcn_s_setprio(2);
+    for (;;) {
+      if (tid == 0) s_next = atomicAdd(hdr + kHdrFwdNext, 1u);
       __syncthreads();
-      const uint32_t whi = min(wtop, hi_w);
-      if (whi > wlo) {  // wave-uniform
-        // the window's chunks j (tile-relative entries [64 j, 64 j + 64)), top down
-        const uint32_t jlo = wlo / kChunk, jtop = (whi - 1u) / kChunk, nchunks = jtop - jlo + 1u;
-        // list entry of lane `lane` in chunk c (c >= nchunks: past the end of the list)
-        auto gid_of = [&](uint32_t c) -> uint32_t {
-          return load_gid(vals, c < nchunks ? start + (jtop - c) * kChunk + lane : end, end, start);
-        };
-        auto mask_of = [&](uint32_t c) -> uint2 {
-          const uint64_t mc = cbase + (c < nchunks ? jtop - c : jtop);
-          return masks[(mc < mask_cap ? mc : 0) * (kTile * kTile) + pix];
-        };
-        uint32_t gnext = gid_of(0);
-        Raw cur = load_raw(splat, gnext, n);
-        uint2 mcur = mask_of(0);
-        gnext = gid_of(1);
-        for (uint32_t c = 0; c < nchunks; ++c) {
-          const uint32_t j = jtop - c;
-          const Raw nxt = load_raw(splat, gnext, n);  // next chunk in flight
-          const uint2 mnxt = mask_of(c + 1);
-          gnext = gid_of(c + 2);
-          put(S, lane, cur);
-          wave_sync_lds();
-          // The entries this pixel composited in the chunk (the forward's mask): exactly those
-          // with power <= 0, alpha >= 1/255 in front of the pixel's stop.  Each 2x2 pixel block
-          // of the quadrant (4 lanes) takes the entries any of its pixels composited, back to
-          // front, its lanes on the same entry; the block's nine sums are formed in registers
-          // and added to the window's sums by one lane of the block.
-          const unsigned long long mine =
-              cbase + j < mask_cap ? ((unsigned long long)mcur.y << 32) | mcur.x : 0ull;
-          unsigned long long rem = quad_or(mine);
-          const uint32_t wbase = j * kChunk - wlo;  // window position of slot 0
-          for (;;) {
-            const bool has = rem != 0ull;
-            if (__ballot(has) == 0ull) break;
-            const int e = has ? highest_bit(rem) : 0;
-            rem &= ~(1ull << e);
-            const float4 g = S.geo[e];  // one address per block: a broadcast within the block
-            const float4 cl = S.col[e];
-            const float cb = S.b[e];
-            const float dx = pxc - g.x, dy = pyc - g.y;
-            const float power = eval_power(g.z, g.w, cl.x, dx, dy);
-            const float G = __expf(power);
-            const float oG = __fmul_rn(cl.y, G);  // the same operations as eval_oG
-            const float alpha = fminf(kAlphaMax, oG);
-            const bool act = has && ((mine >> e) & 1ull);
-            const float om = 1.0f - alpha;
-            const float rom = __builtin_amdgcn_rcpf(om);  // om >= 0.01
-            const float Tk = Tr * rom;                    // transmittance in front of this entry
-            const float wt = alpha * Tk;
-            const float cr = cl.z, cg = cl.w;
-            const float dL_dalpha = Tk * ((cr - S0) * g0 + (cg - S1) * g1 + (cb - S2) * g2) - bgT * rom;
-            const bool unclamped = act && oG <= kAlphaMax;  // alpha = o G depends on o and power
-            const float dpow = unclamped ? oG * dL_dalpha : 0.0f;
-            // moments of dL/dpower over the pixels; the conic gradients are linear in them
-            float v[9];
-            v[0] = dx * dpow;
-            v[1] = dy * dpow;
-            v[2] = dx * v[0];
-            v[3] = dy * v[0];
-            v[4] = dy * v[1];
-            v[5] = unclamped ? G * dL_dalpha : 0.0f;
-            v[6] = act ? wt * g0 : 0.0f;
-            v[7] = act ? wt * g1 : 0.0f;
-            v[8] = act ? wt * g2 : 0.0f;
-            if (act) {
-              S0 = alpha * cr + om * S0;
-              S1 = alpha * cg + om * S1;
-              S2 = alpha * cb + om * S2;
-              Tr = Tk;
-            }
-            quad_sum<9>(v);  // every lane of a pixel block holds the block's sums
-            if ((lane & 3) == 0 && has) {
-              // dL/du = (A m_x + B m_y), dL/dv = (B m_x + C m_y), dL/dA = -m_xx / 2,
-              // dL/dB = -m_xy, dL/dC = -m_yy / 2 with A = -2 nA, B = -nB, C = -2 nC
-              const uint32_t ws = wbase + (uint32_t)e;
-              atomicAdd(&acc[0][ws], -(2.0f * g.z * v[0] + g.w * v[1]));
-              atomicAdd(&acc[1][ws], -(g.w * v[0] + 2.0f * cl.x * v[1]));
-              atomicAdd(&acc[2][ws], -0.5f * v[2]);
-              atomicAdd(&acc[3][ws], -v[3]);
-              atomicAdd(&acc[4][ws], -0.5f * v[4]);
-#pragma unroll
-              for (int q = 5; q < 9; ++q) atomicAdd(&acc[q][ws], v[q]);
-            }
-          }
-          wave_sync_lds();  // this chunk's reads finish before the next chunk is staged
-          cur = nxt;
-          mcur = mnxt;
-        }
-      }
+      const uint32_t i = s_next;
       __syncthreads();
-      // one thread per entry of the window: the entry's sums go to its Gaussian's staging
-      // slot, the entry's place in the row-major order of the Gaussian's tile rect
-      if (wlo + (uint32_t)tid < wtop) {
-        float x[9];
-        bool any = false;
-#pragma unroll
-        for (int q = 0; q < 9; ++q) {
-          x[q] = acc[q][tid];
-          any = any || x[q] != 0.f;
-        }
-        if (any) {
-          const uint32_t gid = vals[start + wlo + tid];
-          const float4 q0 = splat[3 * (int64_t)gid];  // u, v, radius_x, radius_y
-          int x0, y0, x1, y1;
-          tile_rect(q0.x, q0.y, __float_as_int(q0.z), __float_as_int(q0.w), TX, TY, x0, y0, x1, y1);
-          const uint64_t slot = (uint64_t)goff_blk[gid / kGoffBlock] + goff[gid] +
-                                (uint32_t)((ty - y0) * (x1 - x0) + (tx - x0));
-          if (slot < staging_cap) {
-            float* o = staging + 9 * slot;
-#pragma unroll
-            for (int q = 0; q < 9; ++q) o[q] = x[q];
-          }
-        }
+      if (i >= (uint32_t)fa.T) break;
+      const int tile = (int)fa.order[i];
+      forward_tile<true>(fa, shift, tile, sh.stg);
+      drain_memory();
+      __syncthreads();  // the tile's state is visible to every XCD
+      const uint32_t o = item_off[tile], k = item_off[tile + 1] - o;
+      if (k != 0u) {  // workgroup-uniform
+        if (tid == 0) s_pos = atomicAdd(hdr + kHdrReady, k);
+        __syncthreads();
+        const uint32_t pos = s_pos;
+        for (uint32_t j = tid; j < k; j += kBlock) put_u2<true>(items + pos + j, make_uint2((uint32_t)tile, j));
       }
-      __syncthreads();  // the window's sums are read before the next window clears them
-      wtop = wlo;
     }
+    __builtin_amdgcn_s_setprio(0);
+  }
+  for (;;) {
+    if (tid == 0) {
+      const uint32_t b = atomicAdd(hdr + kHdrBwdNext, 1u);
+      uint2 it = make_uint2(kNoTile, 0u);
+      if (b < n_items) {
+        for (uint32_t spin = 0;; ++spin) {
+          it = get_u2<true>(items + b);
+          if (it.x != kNoTile) break;
+          if (spin == kSpinLimit) {
+            atomicOr(hdr + kHdrStall, 1u);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(4);
+        }
+      }
+      s_it = it;
+    }
+    __syncthreads();
+    const uint2 it = s_it;
+    __syncthreads();
+    if (it.x == kNoTile) break;
+    backward_item<true>(ba, shift, it, sh);
   }
 }
 
@@ -754,7 +988,7 @@ __global__ __launch_bounds__(kBlock) void k_goff_local(int64_t n, const uint32_t
   if (threadIdx.x == 0) blk[blockIdx.x] = run;  // the block's total
 }
 
-// exclusive scan of the nblk block totals in place (one workgroup); total entries -> hdr[4]
+// exclusive scan of the nblk block totals in place (one workgroup); total entries -> header
 __global__ __launch_bounds__(kPlanThreads) void k_goff_blocks(int64_t nblk, uint32_t* __restrict__ blk,
                                                               uint32_t* __restrict__ hdr) {
   __shared__ uint32_t red32[kPlanThreads / 64];
@@ -768,13 +1002,13 @@ __global__ __launch_bounds__(kPlanThreads) void k_goff_blocks(int64_t nblk, uint
     blk[b] = run;
     run += x;
   }
-  if (threadIdx.x == kPlanThreads - 1) hdr[4] = run;  // the last thread's end is the total
+  if (threadIdx.x == kPlanThreads - 1) hdr[kHdrEntries] = run;  // the last thread's end is the total
 }
 
-// staging[0 .. 9 * entries) = 0; entries from hdr[4], capped at the workspace's capacity
+// staging[0 .. 9 * entries) = 0; entries from the header, capped at the workspace's capacity
 __global__ __launch_bounds__(kBlock) void k_clear_staging(const uint32_t* __restrict__ hdr, float4* __restrict__ st,
                                                           uint64_t cap) {
-  const uint64_t e = std::min<uint64_t>((uint64_t)hdr[4], cap);
+  const uint64_t e = std::min<uint64_t>((uint64_t)hdr[kHdrEntries], cap);
   const uint64_t n4 = (9 * e + 3) / 4;  // the staging region is padded to whole float4s
   for (uint64_t j = (uint64_t)blockIdx.x * kBlock + threadIdx.x; j < n4; j += (uint64_t)gridDim.x * kBlock)
     st[j] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -829,7 +1063,7 @@ size_t plan_bytes(int T) { return round256(4 * plan_blocks(T) * kPartVals) + rou
 size_t layout_bytes(int T, int64_t n, uint64_t k) {
   const size_t slots = (size_t)T + (size_t)(k / kSegEntries);
   const size_t chunks = (size_t)T + (size_t)(k / kChunk);
-  return 256 + 2 * round256(4 * (size_t)(T + 1)) + round256(4 * (size_t)T) + plan_bytes(T) + round256(4 * (size_t)n) +
+  return 256 + 2 * round256(4 * (size_t)(T + 1)) + 2 * round256(4 * (size_t)T) + plan_bytes(T) + round256(4 * (size_t)n) +
          round256(4 * (n_goff_blocks(n) + 1)) +
          round256(8 * ((size_t)T + slots)) + round256(kSlotBytes * slots) + kMaskChunkBytes * chunks +
          round256(36 * (size_t)k + 16);
@@ -862,6 +1096,8 @@ bool render_ws_layout(void* ws, size_t bytes, int T, int64_t n, RenderWs* out) {
   b += round256(4 * (size_t)(T + 1));
   out->order = reinterpret_cast<uint32_t*>(b);
   b += round256(4 * (size_t)T);
+  out->loss_part = reinterpret_cast<float*>(b);
+  b += round256(4 * (size_t)T);
   out->plan_part = reinterpret_cast<uint32_t*>(b);
   b += round256(4 * plan_blocks(T) * kPartVals);
   out->plan_off = reinterpret_cast<uint32_t*>(b);
@@ -884,13 +1120,24 @@ bool render_ws_layout(void* ws, size_t bytes, int T, int64_t n, RenderWs* out) {
   return true;
 }
 
-hipError_t launch_blend_forward(const CamK& cam, int64_t n, const gs_splat* splat, const uint32_t* vals,
-                                const uint32_t* ranges, float bg0, float bg1, float bg2,
-                                float* image, float* T_final, uint32_t* last_contrib,
-                                uint32_t* n_examined, uint64_t* blend_count, const RenderWs& ws,
-                                hipStream_t s) {
-  const int T = cam.TX * cam.TY;
-  const uint2* rg = reinterpret_cast<const uint2*>(ranges);
+namespace {
+
+constexpr int kFwdPerCu = 3;  // forward workgroups per CU (also the fused step's forward workers)
+
+// workgroups of `kernel` that fit on one CU at once
+int resident_per_cu(const void* kernel, int* cache) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
+  if (cache[dev] <= 0) {
+    int v = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, kernel, kBlock, 0) != hipSuccess || v <= 0) v = 1;
+    cache[dev] = v;
+  }
+  return cache[dev];
+}
+
+// the segment plan, the tile order and the item list (empty markers for the fused step)
+void launch_plan(int T, const uint2* rg, const RenderWs& ws, bool empty_items, hipStream_t s) {
   const int nb = (int)ceil_div(T, kPlanThreads);
   hipLaunchKernelGGL(k_plan_count, dim3((unsigned)nb), dim3(kPlanThreads), 0, s, rg, T, ws.plan_part);
   hipLaunchKernelGGL(k_plan_scan, dim3(1), dim3(kPlanThreads), 0, s, (const uint32_t*)ws.plan_part, nb, T,
@@ -898,12 +1145,89 @@ hipError_t launch_blend_forward(const CamK& cam, int64_t n, const gs_splat* spla
   hipLaunchKernelGGL(k_plan_write, dim3((unsigned)nb), dim3(kPlanThreads), 0, s, rg, T,
                      (const uint32_t*)ws.plan_off, (const uint32_t*)ws.hdr, ws.bnd_off, ws.item_off, ws.order);
   hipLaunchKernelGGL(k_seg_items, dim3((unsigned)ceil_div(T, kBlock / 64)), dim3(kBlock), 0, s, T,
-                     (const uint32_t*)ws.item_off, ws.items);
-  hipLaunchKernelGGL(k_blend_forward, dim3(T), dim3(kBlock), 0, s, cam.W, cam.H, cam.TX, T, n,
-                     reinterpret_cast<const float4*>(splat), vals, rg, bg0, bg1, bg2, image, T_final,
-                     last_contrib, n_examined, reinterpret_cast<unsigned long long*>(blend_count),
-                     (const uint32_t*)ws.hdr, (const uint32_t*)ws.bnd_off, ws.slots, ws.masks, ws.mask_cap,
-                     (const uint32_t*)ws.order);
+                     (const uint32_t*)ws.item_off, ws.items, empty_items);
+}
+
+// the per-Gaussian staging offsets and the cleared staging rows
+void launch_staging(int64_t n, const uint32_t* tiles, const RenderWs& ws, hipStream_t s) {
+  const size_t nblk = n_goff_blocks(n);
+  hipLaunchKernelGGL(k_goff_local, dim3((unsigned)nblk), dim3(kBlock), 0, s, n, tiles, ws.goff, ws.goff_blk);
+  hipLaunchKernelGGL(k_goff_blocks, dim3(1), dim3(kPlanThreads), 0, s, (int64_t)nblk, ws.goff_blk, ws.hdr);
+  const unsigned fill_grid = (unsigned)std::max(1, cu_count() * 8);
+  hipLaunchKernelGGL(k_clear_staging, dim3(fill_grid), dim3(kBlock), 0, s, (const uint32_t*)ws.hdr,
+                     reinterpret_cast<float4*>(ws.staging), ws.staging_cap);
+}
+
+FwdArgs fwd_args(const CamK& cam, int64_t n, const gs_splat* splat, const uint32_t* vals, const uint32_t* ranges,
+                 float bg0, float bg1, float bg2, float* image, float* T_final, uint32_t* last_contrib,
+                 uint32_t* n_examined, uint64_t* blend_count, const RenderWs& ws) {
+  FwdArgs a{};
+  a.W = cam.W;
+  a.H = cam.H;
+  a.TX = cam.TX;
+  a.T = cam.TX * cam.TY;
+  a.n = n;
+  a.splat = reinterpret_cast<const float4*>(splat);
+  a.vals = vals;
+  a.ranges = reinterpret_cast<const uint2*>(ranges);
+  a.bg0 = bg0;
+  a.bg1 = bg1;
+  a.bg2 = bg2;
+  a.image = image;
+  a.T_final = T_final;
+  a.last_contrib = last_contrib;
+  a.n_examined = n_examined;
+  a.blend_count = reinterpret_cast<unsigned long long*>(blend_count);
+  a.bnd_off = ws.bnd_off;
+  a.slots = ws.slots;
+  a.masks = ws.masks;
+  a.mask_cap = ws.mask_cap;
+  a.order = ws.order;
+  return a;
+}
+
+BwdArgs bwd_args(const CamK& cam, int64_t n, const gs_splat* splat, const uint32_t* vals, const uint32_t* ranges,
+                 float bg0, float bg1, float bg2, const float* T_final, const uint32_t* last_contrib,
+                 const float* dLdI, const RenderWs& ws) {
+  BwdArgs a{};
+  a.W = cam.W;
+  a.H = cam.H;
+  a.TX = cam.TX;
+  a.TY = cam.TY;
+  a.n = n;
+  a.splat = reinterpret_cast<const float4*>(splat);
+  a.vals = vals;
+  a.ranges = reinterpret_cast<const uint2*>(ranges);
+  a.bg0 = bg0;
+  a.bg1 = bg1;
+  a.bg2 = bg2;
+  a.T_final = T_final;
+  a.last_contrib = last_contrib;
+  a.dLdI = dLdI;
+  a.bnd_off = ws.bnd_off;
+  a.slots = ws.slots;
+  a.masks = ws.masks;
+  a.mask_cap = ws.mask_cap;
+  a.goff = ws.goff;
+  a.goff_blk = ws.goff_blk;
+  a.staging = ws.staging;
+  a.staging_cap = ws.staging_cap;
+  return a;
+}
+
+}  // namespace
+
+hipError_t launch_blend_forward(const CamK& cam, int64_t n, const gs_splat* splat, const uint32_t* vals,
+                                const uint32_t* ranges, float bg0, float bg1, float bg2,
+                                float* image, float* T_final, uint32_t* last_contrib,
+                                uint32_t* n_examined, uint64_t* blend_count, const RenderWs& ws,
+                                hipStream_t s) {
+  const int T = cam.TX * cam.TY;
+  launch_plan(T, reinterpret_cast<const uint2*>(ranges), ws, false, s);
+  const FwdArgs a = fwd_args(cam, n, splat, vals, ranges, bg0, bg1, bg2, image, T_final, last_contrib, n_examined,
+                             blend_count, ws);
+  const unsigned grid = (unsigned)std::max(1, std::min(T, cu_count() * kFwdPerCu));
+  hipLaunchKernelGGL(k_blend_forward, dim3(grid), dim3(kBlock), 0, s, a, ws.hdr);
   return hipGetLastError();
 }
 
@@ -914,27 +1238,51 @@ hipError_t launch_blend_backward(const CamK& cam, int64_t n, const gs_splat* spl
                                  const RenderWs& ws, hipStream_t s) {
   const int T = cam.TX * cam.TY;
   if (n <= 0) return hipSuccess;
-  const size_t nblk = n_goff_blocks(n);
-  hipLaunchKernelGGL(k_goff_local, dim3((unsigned)nblk), dim3(kBlock), 0, s, n, tiles, ws.goff, ws.goff_blk);
-  hipLaunchKernelGGL(k_goff_blocks, dim3(1), dim3(kPlanThreads), 0, s, (int64_t)nblk, ws.goff_blk, ws.hdr);
-  const unsigned fill_grid = (unsigned)std::max(1, cu_count() * 8);
-  hipLaunchKernelGGL(k_clear_staging, dim3(fill_grid), dim3(kBlock), 0, s, (const uint32_t*)ws.hdr,
-                     reinterpret_cast<float4*>(ws.staging), ws.staging_cap);
-  hipError_t e = launch_fill_u32(ws.hdr + 3, 1, 0u, s);  // work-item counter
+  launch_staging(n, tiles, ws, s);
+  hipError_t e = launch_fill_u32(ws.hdr + kHdrBwdNext, 1, 0u, s);  // work-item counter
   if (e != hipSuccess) return e;
   // enough persistent workgroups to fill every CU; never more than the items can be
   const int64_t most = (int64_t)T + ws.slots_cap;
   const unsigned grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>(most, (int64_t)cu_count() * 8));
-  hipLaunchKernelGGL(k_blend_backward, dim3(grid), dim3(kBlock), 0, s, cam.W, cam.H, cam.TX, cam.TY, n,
-                     reinterpret_cast<const float4*>(splat), vals, reinterpret_cast<const uint2*>(ranges),
-                     bg0, bg1, bg2, T_final, last_contrib, dLdI, ws.hdr, (const uint32_t*)ws.bnd_off,
-                     (const uint2*)ws.items, (const float4*)ws.slots, (const uint2*)ws.masks, ws.mask_cap,
-                     (const uint32_t*)ws.goff, (const uint32_t*)ws.goff_blk, ws.staging, ws.staging_cap);
+  const BwdArgs a = bwd_args(cam, n, splat, vals, ranges, bg0, bg1, bg2, T_final, last_contrib, dLdI, ws);
+  hipLaunchKernelGGL(k_blend_backward, dim3(grid), dim3(kBlock), 0, s, a, ws.hdr, (const uint2*)ws.items);
   if (grad2d)  // else the sums stay staged for the preprocess backward
     hipLaunchKernelGGL(k_gather_grad2d, dim3((unsigned)ceil_div(n, (int64_t)kBlock)), dim3(kBlock), 0, s, n,
                        tiles, (const uint32_t*)ws.goff, (const uint32_t*)ws.goff_blk, (const float*)ws.staging,
                        ws.staging_cap, grad2d);
   return hipGetLastError();
+}
+
+hipError_t launch_blend_step(const CamK& cam, int64_t n, const gs_splat* splat, const uint32_t* tiles,
+                             const uint32_t* vals, const uint32_t* ranges, float bg0, float bg1, float bg2,
+                             const float* target, float* image, float* T_final, uint32_t* last_contrib,
+                             uint32_t* n_examined, uint64_t* blend_count, float* loss, float* dLdI,
+                             float* grad2d, const RenderWs& ws, hipStream_t s) {
+  const int T = cam.TX * cam.TY;
+  launch_plan(T, reinterpret_cast<const uint2*>(ranges), ws, true, s);
+  if (n > 0) launch_staging(n, tiles, ws, s);
+  FwdArgs fa = fwd_args(cam, n, splat, vals, ranges, bg0, bg1, bg2, image, T_final, last_contrib, n_examined,
+                        blend_count, ws);
+  const int64_t count = 3 * (int64_t)cam.W * cam.H;
+  fa.target = target;
+  fa.dLdI = dLdI;
+  fa.loss_part = ws.loss_part;
+  fa.inv_n = (float)(1.0 / (double)count);
+  const BwdArgs ba = bwd_args(cam, n, splat, vals, ranges, bg0, bg1, bg2, T_final, last_contrib, dLdI, ws);
+  // every workgroup resident at once: the backward wants all the occupancy it can get
+  static int resident[64];
+  const int per_cu = resident_per_cu(reinterpret_cast<const void*>(k_blend_step), resident);
+  const unsigned grid = (unsigned)std::max(1, cu_count() * per_cu);
+  const uint32_t fwd_workers = (uint32_t)std::max(1, std::min(per_cu, kFwdPerCu) * cu_count());
+  hipLaunchKernelGGL(k_blend_step, dim3(grid), dim3(kBlock), 0, s, fa, ba, ws.hdr, ws.items,
+                     (const uint32_t*)ws.item_off, fwd_workers);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (grad2d && n > 0)
+    hipLaunchKernelGGL(k_gather_grad2d, dim3((unsigned)ceil_div(n, (int64_t)kBlock)), dim3(kBlock), 0, s, n,
+                       tiles, (const uint32_t*)ws.goff, (const uint32_t*)ws.goff_blk, (const float*)ws.staging,
+                       ws.staging_cap, grad2d);
+  return launch_loss_sum(T, ws.loss_part, 1.0 / (double)count, loss, s);
 }
 
 }  // namespace gsmi

@@ -328,6 +328,28 @@ int gs_render_backward(const gs_scene* scene, float* params, const gs_camera* ca
                                  "gs_render_backward (preprocess backward)");
 }
 
+int gs_render_step(const gs_scene* scene, const gs_camera* cam, gs_proj proj, const uint32_t* vals,
+                   const uint32_t* ranges, const float* bg, const float* target, float* image,
+                   float* T_final, uint32_t* last_contrib, uint32_t* n_examined, uint64_t* blend_count,
+                   float* loss, float* dL_dimage, float* grad2d, void* render_ws, size_t render_ws_bytes,
+                   hipStream_t stream) {
+  int st;
+  if ((st = check_scene(scene)) || (st = check_camera(cam)) || (st = check_proj(proj, false, scene->n))) return st;
+  if (!vals || !ranges || !bg || !target || !image || !T_final || !last_contrib || !loss || !dL_dimage ||
+      !render_ws)
+    return fail(GS_ERR_INVALID_ARGUMENT, "a required pointer is null");
+  if (scene->n > 0 && !proj.tiles) return fail(GS_ERR_INVALID_ARGUMENT, "proj.tiles is null");
+  RenderWs ws;
+  if (!render_ws_layout(render_ws, render_ws_bytes, (int)n_tiles(*cam), scene->n, &ws))
+    return fail(GS_ERR_INVALID_ARGUMENT, "render workspace too small or not 256-byte aligned");
+  if (reinterpret_cast<uintptr_t>(ranges) & 7u) return fail(GS_ERR_INVALID_ARGUMENT, "ranges must be 8-byte aligned");
+  if (!(finite(bg[0]) && finite(bg[1]) && finite(bg[2]))) return fail(GS_ERR_INVALID_ARGUMENT, "bg not finite");
+  const hipError_t e = launch_blend_step(make_cam(*cam), scene->n, proj.splat, proj.tiles, vals, ranges, bg[0],
+                                         bg[1], bg[2], target, image, T_final, last_contrib, n_examined,
+                                         blend_count, loss, dL_dimage, grad2d, ws, stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "gs_render_step");
+}
+
 int gs_adam_step(int64_t count, float* params, const float* grads, const gs_adam* adam, hipStream_t stream) {
   int st;
   if (!adam) return fail(GS_ERR_INVALID_ARGUMENT, "adam is null");

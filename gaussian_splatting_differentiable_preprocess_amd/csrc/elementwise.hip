@@ -132,6 +132,11 @@ hipError_t launch_loss_l1(int64_t count, const float* image, const float* target
   return hipGetLastError();
 }
 
+hipError_t launch_loss_sum(int64_t count, const float* part, double inv_n, float* loss, hipStream_t s) {
+  hipLaunchKernelGGL(k_loss_final, dim3(1), dim3(1024), 0, s, count, part, count > 0 ? inv_n : 0.0, loss);
+  return hipGetLastError();
+}
+
 hipError_t launch_adam(int64_t count, float* params, const float* grads, float* m, float* v,
                        const AdamCoef& c, hipStream_t s) {
   if (count <= 0) return hipSuccess;

@@ -99,8 +99,7 @@ hipError_t launch_bin_sort_rest(int64_t n, int64_t K, const BinInfo& info, const
 // backward gathers each list entry's nine gradient sums in `staging`, grouped by Gaussian
 // (Gaussian i's entries at goff(i) .. goff(i) + tiles_i, in the row-major order of its tile
 // rect), and then sums each Gaussian's entries into grad2d: no float atomics in memory.
-//   hdr[0] = log2 segment length, hdr[1] = number of backward work items, hdr[2] = slots used,
-//   hdr[3] = work-item counter of the backward, hdr[4] = entries (sum of tiles)
+//   hdr[64]         header words (kHdr* below)
 //   bnd_off[T + 1]  first slot of each tile
 //   item_off[T + 1] first work item of each tile
 //   order[T]        the forward's tile order: list-length classes (log2), longest first
@@ -108,13 +107,25 @@ hipError_t launch_bin_sort_rest(int64_t n, int64_t K, const BinInfo& info, const
 //   goff[n]         exclusive scan of tiles within blocks of kGoffBlock Gaussians; goff(i) =
 //                   goff_blk[i / kGoffBlock] + goff[i]
 //   goff_blk[]      exclusive scan of the block totals
-//   items[]         (tile, segment) work items of the backward, tile-major
+//   items[]         (tile, segment) work items of the backward: tile-major after the forward; in
+//                   the fused step, in the order the tiles' forwards completed
 //   slots[][256]    float4 states
 //   masks[][256]    per 64-entry chunk of a tile list and pixel of the tile: the chunk's
 //                   entries the forward composited at that pixel (64-bit, as uint2 lo, hi);
 //                   tile t's chunk j is at (ranges[t].x / 64 + t + j)
+//   loss_part[T]    the fused step's per-tile sums of |image - target|
 //   staging[][9]    per-entry gradient sums
 constexpr int kSegShiftMin = 8;  // 256 list entries per segment
+// header words of the render workspace
+constexpr int kHdrShift = 0;    // log2 segment length
+constexpr int kHdrItems = 1;    // backward work items
+constexpr int kHdrSlots = 2;    // state slots used
+constexpr int kHdrBwdNext = 3;  // next backward work item (counter)
+constexpr int kHdrEntries = 4;  // staged entries (sum of tiles)
+constexpr int kHdrFwdNext = 5;  // next tile of the forward (counter)
+constexpr int kHdrReady = 6;    // fused step: work items published so far
+constexpr int kHdrRole = 7;     // fused step: workgroups started so far
+constexpr int kHdrStall = 8;    // fused step: nonzero if a workgroup gave up waiting for an item
 constexpr int kGoffBlock = 4096;
 struct RenderWs {
   uint32_t* hdr;
@@ -128,6 +139,7 @@ struct RenderWs {
   uint2* items;
   float4* slots;
   uint2* masks;
+  float* loss_part;
   float* staging;
   uint32_t slots_cap;
   uint64_t mask_cap;     // chunks
@@ -153,6 +165,15 @@ hipError_t launch_blend_backward(const CamK& cam, int64_t n, const gs_splat* spl
 hipError_t launch_fill_u32(uint32_t* p, int64_t count, uint32_t value, hipStream_t s);
 hipError_t launch_fill_f32(float* p, int64_t count, float value, hipStream_t s);
 size_t loss_workspace_bytes(int64_t count);
+// Fused forward, L1 loss and backward blend of one training step; leaves the per-intersection
+// gradient sums staged in ws for the preprocess backward.
+hipError_t launch_blend_step(const CamK& cam, int64_t n, const gs_splat* splat, const uint32_t* tiles,
+                             const uint32_t* vals, const uint32_t* ranges, float bg0, float bg1, float bg2,
+                             const float* target, float* image, float* T_final, uint32_t* last_contrib,
+                             uint32_t* n_examined, uint64_t* blend_count, float* loss, float* dLdI,
+                             float* grad2d, const RenderWs& ws, hipStream_t s);
+// *loss = inv_n * sum of part[0 .. count)
+hipError_t launch_loss_sum(int64_t count, const float* part, double inv_n, float* loss, hipStream_t s);
 hipError_t launch_loss_l1(int64_t count, const float* image, const float* target, float* loss,
                           float* dLdI, void* ws, hipStream_t s);
 hipError_t launch_adam(int64_t count, float* params, const float* grads, float* m, float* v,

@@ -24,7 +24,7 @@ SPLAT_FLOATS = 12  # 48-byte record: u, v, radius_x, radius_y | A, B, C, opacity
 EXPORTS = (
     "gs_version", "gs_last_error", "gs_preprocess", "gs_bin_and_sort_workspace", "gs_bin_and_sort",
     "gs_render_workspace", "gs_render_workspace_capacity", "gs_render_forward", "gs_loss_l1_workspace", "gs_loss_l1", "gs_render_backward",
-    "gs_preprocess_backward", "gs_preprocess_backward_staged", "gs_adam_step",
+    "gs_render_step", "gs_preprocess_backward", "gs_preprocess_backward_staged", "gs_adam_step",
 )
 
 
@@ -87,6 +87,8 @@ def load(path: str = LIB_PATH):
     L.gs_loss_l1.argtypes = [i64, P, P, P, P, P, sz, P]
     L.gs_render_backward.argtypes = [SP, P, CP, GsProj, P, P, ctypes.POINTER(ctypes.c_float), P, P, P,
                                      P, P, AP, P, sz, P]
+    L.gs_render_step.argtypes = [SP, CP, GsProj, P, P, ctypes.POINTER(ctypes.c_float), P, P, P, P, P, P, P, P, P, P,
+                                 sz, P]
     L.gs_preprocess_backward.argtypes = [SP, P, CP, P, P, AP, P]
     L.gs_preprocess_backward_staged.argtypes = [SP, P, CP, GsProj, P, sz, P, AP, P]
     L.gs_adam_step.argtypes = [i64, P, P, AP, P]
@@ -243,6 +245,18 @@ def render_backward(scene: GsScene, params, cam: GsCamera, proj: Proj, vals, ran
                                      _ptr(ranges), _bg(bg), _ptr(T_final), _ptr(last_contrib), _ptr(dL_dimage),
                                      _ptr(grad2d), _ptr(grads), ctypes.byref(adam) if adam is not None else None,
                                      _ptr(render_ws), _nbytes(render_ws), _stream(stream)))
+
+
+def render_step(scene: GsScene, cam: GsCamera, proj: Proj, vals, ranges, bg, target, image, T_final, last_contrib,
+                loss, dL_dimage, render_ws, grad2d=None, n_examined=None, blend_count=None, stream=None):
+    """Forward blend, L1 loss and backward blend of one step in one fused kernel; the gradient
+    sums stay staged in render_ws for preprocess_backward_staged (and go to grad2d if given)."""
+    if blend_count is not None and (blend_count.numel() < 3 or blend_count.element_size() != 8):
+        raise ValueError("blend_count must be a device int64 tensor of at least 3 elements")
+    _check(load().gs_render_step(ctypes.byref(scene), ctypes.byref(cam), proj.c(), _ptr(vals), _ptr(ranges), _bg(bg),
+                                 _ptr(target), _ptr(image), _ptr(T_final), _ptr(last_contrib), _ptr(n_examined),
+                                 _ptr(blend_count), _ptr(loss), _ptr(dL_dimage), _ptr(grad2d), _ptr(render_ws),
+                                 _nbytes(render_ws), _stream(stream)))
 
 
 def preprocess_backward(scene: GsScene, params, cam: GsCamera, grad2d, grads=None, adam: GsAdam | None = None,

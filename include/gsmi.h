@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define GSMI_VERSION 3
+#define GSMI_VERSION 4
 #define GS_TILE 16 /* tiles are GS_TILE x GS_TILE pixels */
 
 typedef enum gs_status {
@@ -190,7 +190,8 @@ int gs_render_workspace_capacity(int32_t width, int32_t height, int64_t n, size_
  *                       size gs_render_workspace gives for this image, n and a k_capacity
  *                       >= the number of intersections in vals; GS_ERR_INVALID_ARGUMENT if
  *                       it is smaller than the size for k_capacity 0.
- * bg is a HOST array of 3 floats.  One 256-thread workgroup per tile. */
+ * bg is a HOST array of 3 floats.  A few persistent 256-thread workgroups per CU take the
+ * tiles, longest lists first. */
 int gs_render_forward(const gs_camera* cam, int64_t n, const gs_splat* splat, const uint32_t* vals,
                       const uint32_t* ranges, const float* bg, float* image, float* T_final,
                       uint32_t* last_contrib, uint32_t* n_examined, uint64_t* blend_count,
@@ -231,6 +232,32 @@ int gs_render_backward(const gs_scene* scene, float* params, const gs_camera* ca
                        float* grad2d, float* grads, const gs_adam* adam, void* render_ws,
                        size_t render_ws_bytes, hipStream_t stream);
 
+/* The image pass of one training step, fused: the forward blend (as gs_render_forward), the L1
+ * loss against target (as gs_loss_l1) and the backward blend (as gs_render_backward with
+ * grad2d, grads and adam null) in one persistent kernel.  Workgroups that finish a tile's
+ * forward hand its backward segments to the others at once, so the backward runs beside the
+ * forward's long tile walks instead of after them ("Scaling 3D Gaussian Splatting with
+ * Distributed Compute", walkthrough steps "Rasterize locally" and "Backward pass").
+ *   target[H][W][3]     the ground-truth image
+ *   image, T_final, last_contrib, n_examined, blend_count   as gs_render_forward
+ *   loss                out: device float, mean |image - target| over the 3HW values
+ *   dL_dimage[H][W][3]  out: sign(image - target) / (3HW), sign(0) = 0
+ *   grad2d[ld][9]       out, nullable: as gs_render_backward's grad2d (the staged sums added
+ *                       per Gaussian in the order of its tile rect)
+ *   render_ws           as gs_render_forward; on return it holds the forward's state and each
+ *                       intersection's nine gradient sums, staged for
+ *                       gs_preprocess_backward_staged (same camera, proj and render_ws), which
+ *                       finishes the step.  gs_render_backward may also be run on it.
+ * proj.splat and proj.tiles are the preprocess outputs the lists were built from; bg is a HOST
+ * array of 3 floats.  A wait of one workgroup for another is bounded (about a second); should
+ * one ever give up, word 8 of render_ws (its header) is left nonzero and that work item's
+ * gradient sums are missing.  Errors as gs_render_forward. */
+int gs_render_step(const gs_scene* scene, const gs_camera* cam, gs_proj proj, const uint32_t* vals,
+                   const uint32_t* ranges, const float* bg, const float* target, float* image,
+                   float* T_final, uint32_t* last_contrib, uint32_t* n_examined, uint64_t* blend_count,
+                   float* loss, float* dL_dimage, float* grad2d, void* render_ws, size_t render_ws_bytes,
+                   hipStream_t stream);
+
 /* Preprocess backward alone: grads (and optionally the fused Adam update) from a given
  * grad2d[ld][9].  Same semantics as the second half of gs_render_backward. */
 int gs_preprocess_backward(const gs_scene* scene, float* params, const gs_camera* cam,
@@ -240,7 +267,8 @@ int gs_preprocess_backward(const gs_scene* scene, float* params, const gs_camera
 /* Preprocess backward alone, reading each Gaussian's nine dL/d(2D) values as the sum of its
  * intersections' sums that gs_render_backward (called with grad2d = NULL on the same render_ws,
  * camera and proj) left staged in render_ws, added in the order of the Gaussian's tile rect:
- * the values gs_render_backward would have written into grad2d.  proj.tiles is the
+ * the values gs_render_backward would have written into grad2d.  gs_render_step leaves the
+ * same staged sums.  proj.tiles is the
  * preprocess output the lists were built from.  Otherwise as gs_preprocess_backward. */
 int gs_preprocess_backward_staged(const gs_scene* scene, float* params, const gs_camera* cam, gs_proj proj,
                                   const void* render_ws, size_t render_ws_bytes, float* grads,

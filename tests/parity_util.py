@@ -213,6 +213,44 @@ class GpuStep:
         torch.cuda.synchronize()
         return np.ascontiguousarray(self.grad2d.cpu().numpy().T), self.grads.cpu().numpy()  # grad2d as [9][ld]
 
+    def step(self, bg, target, ranges=None):
+        """The fused image pass (forward, L1 loss and backward blend in one kernel) on the loaded
+        records and lists: the forward's outputs, the loss, dL/dI, grad2d gathered from the staged
+        sums ([9][ld]) and the workspace's stall word."""
+        torch = self.torch
+        H, W = self.H, self.W
+        self.bg = bg
+        rg = self.ranges if ranges is None else to_t(np.asarray(ranges, np.uint32).view(np.int32))
+        nb = gsmi.render_workspace(W, H, self.n, max(1, int(self.vals.numel())))
+        self.render_ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+        self.image = torch.empty((H, W, 3), dtype=torch.float32, device="cuda")
+        self.T_final = torch.empty((H, W), dtype=torch.float32, device="cuda")
+        self.last = torch.empty((H, W), dtype=torch.int32, device="cuda")
+        self.nex = torch.empty((H, W), dtype=torch.int32, device="cuda")
+        self.bcount = torch.zeros(3, dtype=torch.int64, device="cuda")
+        self.target = to_t(np.asarray(target, np.float32))
+        self.dLdI = torch.empty((H, W, 3), dtype=torch.float32, device="cuda")
+        lossv = torch.zeros(1, dtype=torch.float32, device="cuda")
+        g2 = torch.empty((max(1, self.ld), 9), dtype=torch.float32, device="cuda")
+        gsmi.render_step(self.scene, self.cam, self.proj, self.vals, rg, bg, self.target, self.image, self.T_final,
+                         self.last, lossv, self.dLdI, self.render_ws, grad2d=g2, n_examined=self.nex,
+                         blend_count=self.bcount)
+        torch.cuda.synchronize()
+        stall = int(self.render_ws[:64].cpu().numpy().view(np.uint32)[8])
+        return dict(image=self.image.cpu().numpy(), T_final=self.T_final.cpu().numpy(),
+                    last_contrib=self.last.cpu().numpy().view(np.uint32),
+                    n_examined=self.nex.cpu().numpy().view(np.uint32), blend_count=self.bcount.cpu().tolist(),
+                    loss=float(lossv.item()), dLdI=self.dLdI.cpu().numpy(),
+                    grad2d=np.ascontiguousarray(g2.cpu().numpy()[: self.ld].T), stall=stall)
+
+    def preprocess_backward_staged(self, adam=None):
+        """The preprocess backward from the sums the last step left staged: dL/dparams."""
+        torch = self.torch
+        grads = torch.empty((self.R, self.ld), dtype=torch.float32, device="cuda")
+        gsmi.preprocess_backward_staged(self.scene, self.params, self.cam, self.proj, self.render_ws, grads, adam)
+        torch.cuda.synchronize()
+        return grads.cpu().numpy()
+
     def preprocess_backward(self, grad2d):
         torch = self.torch
         g2 = to_t(np.ascontiguousarray(np.asarray(grad2d, np.float32).T))  # [9][ld] -> [ld][9]

@@ -22,7 +22,7 @@ def test_library_exports_every_declared_symbol():
     assert len(names) == len(gsmi.EXPORTS) and set(names) == set(gsmi.EXPORTS)
     for name in names:
         assert hasattr(L, name), name
-    assert gsmi.version() == 3
+    assert gsmi.version() == 4
 
 
 def test_invalid_arguments_rejected_before_any_gpu_call():
@@ -136,3 +136,33 @@ def test_render_calls_reject_a_missing_or_short_workspace():
     assert rc == gsmi.GS_ERR_INVALID_ARGUMENT and "tiles" in gsmi.last_error()
     rc = L.gs_preprocess_backward_staged(ctypes.byref(sc), p, ctypes.byref(cam), proj, p, need, None, None, None)
     assert rc == gsmi.GS_ERR_INVALID_ARGUMENT and "grads" in gsmi.last_error()
+
+
+def test_fused_step_checks_its_arguments():
+    """gs_render_step rejects a missing or short workspace, a missing target or loss output and
+    a missing tiles array before any HIP call."""
+    L = gsmi.load()
+    cam = gsmi.GsCamera()
+    cam.fx = cam.fy = 100.0
+    cam.width = cam.height = 64
+    cam.near_plane = 0.01
+    cam.viewmat[0] = cam.viewmat[5] = cam.viewmat[10] = 1.0
+    bg = (ctypes.c_float * 3)(0, 0, 0)
+    p = ctypes.c_void_p(4096)
+    need = gsmi.render_workspace(64, 64, 10, 0)
+    sc = gsmi.make_scene(10, 10, 0)
+    proj = gsmi.GsProj(4096, 4096, 4096, 4096)
+
+    def call(proj=proj, target=p, loss=p, ws=p, nb=need, ranges=p):
+        return L.gs_render_step(ctypes.byref(sc), ctypes.byref(cam), proj, p, ranges, bg, target, p, p, p, None,
+                                None, loss, p, None, ws, nb, None)
+
+    assert call(ws=None) == gsmi.GS_ERR_INVALID_ARGUMENT and "null" in gsmi.last_error()
+    for ws, nb in ((p, 16), (ctypes.c_void_p(4096 + 64), need)):
+        assert call(ws=ws, nb=nb) == gsmi.GS_ERR_INVALID_ARGUMENT and "workspace" in gsmi.last_error()
+    assert call(target=None) == gsmi.GS_ERR_INVALID_ARGUMENT and "null" in gsmi.last_error()
+    assert call(loss=None) == gsmi.GS_ERR_INVALID_ARGUMENT and "null" in gsmi.last_error()
+    assert call(proj=gsmi.GsProj(4096, None, 4096, 4096)) == gsmi.GS_ERR_INVALID_ARGUMENT
+    assert "tiles" in gsmi.last_error()
+    assert call(ranges=ctypes.c_void_p(4096 + 4)) == gsmi.GS_ERR_INVALID_ARGUMENT
+    assert "aligned" in gsmi.last_error()

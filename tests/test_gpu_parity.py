@@ -327,6 +327,124 @@ def test_staged_sums_match_grad2d(name):
     assert not np.array_equal(outs[0][0], p0.cpu().numpy())  # Adam moved the parameters
 
 
+STEP_CASES = ["tiny_ragged_d1", "tiny_odd_d2", "torus_262k_512_v0", "torus_262k_512_v5"]
+_step_cache = {}
+
+
+def _step_case(name):
+    """The case's L1 target (a seeded uniform image where the case has none) and the oracle's
+    step against it."""
+    if name in _step_cache:
+        return _step_cache[name]
+    d = data(name)
+    if d["target"] is not None:
+        target, o = d["target"], d["o"]
+    else:
+        W, H = d["W"], d["H"]
+        target = np.random.default_rng(7 + W * H).uniform(0.0, 1.0, (H, W, 3)).astype(np.float32)
+        say(f"[parity] fused step {name}: oracle step against a seeded target")
+        o = oracle_pipeline(d["params"], d["deg"], d["cam"].flat(), W, H, BG, target=target, margins=FWD_MARGINS)
+    _step_cache[name] = (target, o)
+    return target, o
+
+
+@pytest.mark.parametrize("name", STEP_CASES)
+def test_fused_step(name):
+    """The fused image pass (forward, L1 loss and backward blend in one persistent kernel) on
+    the oracle's records and lists, against the oracle: image and per-pixel outputs as the
+    forward test, the loss within the image difference, dL/dI exact wherever the image
+    difference cannot flip its sign, the gradient sums per row within the gradient bar, and the
+    preprocess backward from the staged sums likewise."""
+    d = data(name)
+    target, o = _step_case(name)
+    say(f"[parity] test_fused_step {name}")
+    W, H = d["W"], d["H"]
+    g = GpuStep(d["params"], d["deg"], d["cam"], W, H)
+    g.load_proj(*records_from_oracle(o["p32"], o["radii"], o["tiles"], W, H))
+    g.load_lists(o["vals"], o["ranges"])
+    r = g.step(BG, target)
+    assert r["stall"] == 0
+    fo = o["fwd"]
+    bl = fo["borderline"]
+    ok = ~bl
+    err = np.abs(r["image"] - fo["image"]).max(axis=-1)
+    say(f"[parity]   fused forward: max err non-borderline {err[ok].max():.3g}, borderline {int(bl.sum())}")
+    assert err[ok].max() <= IMG_MAX_ABS
+    np.testing.assert_array_equal(r["last_contrib"][ok], fo["last_contrib"][ok])
+    np.testing.assert_array_equal(r["n_examined"][ok], fo["n_examined"][ok])
+    assert np.abs(r["T_final"] - fo["T_final"])[ok].max() <= 1e-5
+    assert r["blend_count"][0] == int(r["n_examined"].astype(np.int64).sum())
+    # | |a - t| - |b - t| | <= |a - b|: the loss moves by at most the mean image difference
+    di = np.abs(r["image"].astype(np.float64) - o["img32"].astype(np.float64))
+    assert abs(r["loss"] - o["loss"]) <= di.mean() + 1e-6 * abs(o["loss"]) + 1e-9, (r["loss"], o["loss"])
+    sure = np.abs(o["img32"].astype(np.float64) - target) > di
+    np.testing.assert_allclose(r["dLdI"][sure], o["dLdI"][sure], rtol=1e-6, atol=0)
+    errs = [rel_l2(r["grad2d"][q], o["grad2d"][q]) for q in range(9)]
+    say(f"[parity]   fused backward blend rel-L2 per row: " + " ".join(f"{e:.2g}" for e in errs) +
+        f"; dL/dI sign undecided at {int((~sure).sum())} values")
+    for q, f in enumerate(oracle.GRAD2D_FIELDS):
+        assert errs[q] <= GRAD_REL_L2, (f, errs[q])
+    grads = g.preprocess_backward_staged()
+    e = rel_l2(grads, o["grads"])
+    say(f"[parity]   preprocess backward from the fused step's staged sums: rel-L2 {e:.2g}")
+    assert e <= GRAD_REL_L2
+
+
+@pytest.mark.parametrize("name", ["tiny_d3", "torus_262k_512_v0"])
+def test_fused_step_matches_separate_calls(name):
+    """On the same inputs the fused pass gives the separate forward's image and per-pixel
+    outputs bit for bit, the separate loss call's dL/dI bit for bit, and the separate backward
+    blend's sums to float rounding (LDS sums add in no fixed order); a second fused pass repeats
+    the first."""
+    import torch
+    d = data(name)
+    target, o = _step_case(name) if d["target"] is not None else (
+        np.random.default_rng(11).uniform(0.0, 1.0, (d["H"], d["W"], 3)).astype(np.float32), None)
+    say(f"[parity] test_fused_step_matches_separate_calls {name}")
+    W, H = d["W"], d["H"]
+    g = GpuStep(d["params"], d["deg"], d["cam"], W, H)
+    g.preprocess()
+    g.bin_and_sort()
+    r1 = g.step(BG, target)
+    r2 = g.step(BG, target)
+    for k in ("image", "T_final", "last_contrib", "n_examined", "dLdI"):
+        np.testing.assert_array_equal(r1[k], r2[k])
+    assert rel_l2(r2["grad2d"], r1["grad2d"]) <= 1e-5
+    f = g.forward(BG)
+    loss, dLdI = g.loss(target)
+    for k in ("image", "T_final", "last_contrib", "n_examined"):
+        np.testing.assert_array_equal(f[k], r1[k])
+    np.testing.assert_array_equal(dLdI, r1["dLdI"])
+    assert abs(loss - r1["loss"]) <= 1e-6 * abs(loss)
+    g2, _ = g.backward()
+    assert rel_l2(r1["grad2d"], g2) <= 1e-5
+    torch.cuda.synchronize()
+
+
+def test_fused_step_empty_and_culled():
+    """The fused pass over a scene with no Gaussians and over one whose Gaussians are all
+    culled: the background image, its L1 loss, and no gradient."""
+    say("[parity] test_fused_step_empty_and_culled")
+    for params, W, H in ((np.zeros((14, 0), np.float32), 48, 40), (None, 64, 64)):
+        if params is None:
+            params = inputs.small_scene(7, 200, 0, logscale_mean=-2.5)
+            params[0] += 10.0  # every mean behind the camera
+        cam = inputs.lookat_camera((3.0, 0, 0), W, H)
+        target = np.random.default_rng(3).uniform(0.0, 1.0, (H, W, 3)).astype(np.float32)
+        g = GpuStep(params, 0, cam, W, H)
+        g.preprocess()
+        K = g.bin_and_sort()[0]
+        assert K == 0
+        r = g.step(BG, target)
+        assert r["stall"] == 0
+        bgimg = np.broadcast_to(np.float32(BG), (H, W, 3))
+        np.testing.assert_allclose(r["image"], bgimg)
+        _, want = oracle.loss_l1(bgimg.astype(np.float64), target)
+        np.testing.assert_allclose(r["dLdI"], want, rtol=1e-6, atol=0)
+        assert abs(r["loss"] - float(np.abs(bgimg - target).mean())) <= 1e-6
+        assert (r["grad2d"] == 0).all()
+
+
 # ---------------------------------------------------------------------------------------
 # edge cases
 # ---------------------------------------------------------------------------------------
