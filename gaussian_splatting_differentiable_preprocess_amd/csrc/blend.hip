@@ -1122,7 +1122,8 @@ bool render_ws_layout(void* ws, size_t bytes, int T, int64_t n, RenderWs* out) {
 
 namespace {
 
-constexpr int kFwdPerCu = 3;  // forward workgroups per CU (also the fused step's forward workers)
+constexpr int kFwdPerCu = 3;      // workgroups per CU of the forward alone
+constexpr int kStepFwdPerCu = 2;  // the fused step's forward workers per CU (measured best)
 
 // workgroups of `kernel` that fit on one CU at once
 int resident_per_cu(const void* kernel, int* cache) {
@@ -1273,7 +1274,7 @@ hipError_t launch_blend_step(const CamK& cam, int64_t n, const gs_splat* splat, 
   static int resident[64];
   const int per_cu = resident_per_cu(reinterpret_cast<const void*>(k_blend_step), resident);
   const unsigned grid = (unsigned)std::max(1, cu_count() * per_cu);
-  const uint32_t fwd_workers = (uint32_t)std::max(1, std::min(per_cu, kFwdPerCu) * cu_count());
+  const uint32_t fwd_workers = (uint32_t)std::max(1, std::min(per_cu, kStepFwdPerCu) * cu_count());
   hipLaunchKernelGGL(k_blend_step, dim3(grid), dim3(kBlock), 0, s, fa, ba, ws.hdr, ws.items,
                      (const uint32_t*)ws.item_off, fwd_workers);
   hipError_t e = hipGetLastError();
