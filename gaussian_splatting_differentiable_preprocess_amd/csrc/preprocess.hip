@@ -268,55 +268,175 @@ __global__ __launch_bounds__(kBlock) void k_preprocess(int64_t n, int64_t ld,
 template <int DEG>
 __global__ __launch_bounds__(kBlock) void k_preprocess_backward(PrebwdArgs A, CamK c) {
   constexpr int NB = (DEG + 1) * (DEG + 1);
-  constexpr int R = 11 + 3 * NB;
   const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
   if (i >= A.n) return;
   const int64_t ld = A.ld;
   float* __restrict__ prm = A.params;
+  const bool adam = A.m != nullptr;
+  // Row r's gradient goes to grads and/or through Adam as soon as it is known.  Parameters,
+  // moments and the updated parameters stream through once: non-temporal loads and stores
+  // (measured 8% faster than cached ones).
+  auto finish_row = [&](int r, float gr_, float th) {
+    const int64_t e = (int64_t)r * ld + i;
+    if (A.grads) A.grads[e] = gr_;
+    if (adam) {
+      const float m = A.b1 * __builtin_nontemporal_load(A.m + e) + A.omb1 * gr_;
+      const float v = A.b2 * __builtin_nontemporal_load(A.v + e) + A.omb2 * gr_ * gr_;
+      __builtin_nontemporal_store(m, A.m + e);
+      __builtin_nontemporal_store(v, A.v + e);
+      __builtin_nontemporal_store(th - A.lr * (m * A.inv_bc1) / (sqrtf(v * A.inv_bc2) + A.eps), prm + e);
+    }
+  };
 
   float mu[3], ls[3], q[4];
-  // parameters, moments and the updated parameters stream through once: non-temporal loads and
-  // stores (measured 8% faster than cached ones)
   for (int j = 0; j < 3; ++j) mu[j] = __builtin_nontemporal_load(prm + j * ld + i);
   for (int j = 0; j < 3; ++j) ls[j] = __builtin_nontemporal_load(prm + (3 + j) * ld + i);
   for (int j = 0; j < 4; ++j) q[j] = __builtin_nontemporal_load(prm + (6 + j) * ld + i);
   const float a = __builtin_nontemporal_load(prm + 10 * ld + i);
-  Proj P;
-  project_geometry(c, mu, ls, q, a, P);
-
   float g[11];  // dL/d(mu, log-scale, q, logit)
   for (int j = 0; j < 11; ++j) g[j] = 0.f;
-  float gc[3] = {0.f, 0.f, 0.f};  // dL/drgb gated by the clamp
-  float Y[16];
-  float f[NB][3];                 // SH coefficients (kept for the Adam update)
+  float gr[3] = {0.f, 0.f, 0.f};  // dL/drgb
+  bool vis;
+  // Two phases, so that the projection's state and the 48 SH coefficients are never live at
+  // once: first the geometry (projection, conic, covariance, opacity), whose rows other than
+  // the mean are finished at once; then the colour, which adds the view-direction term to the
+  // mean's gradient and finishes the mean and SH rows.
+  {
+    Proj P;
+    project_geometry(c, mu, ls, q, a, P);
+    vis = P.vis;
+    if (vis) {
+      float g2[9];  // this Gaussian's nine values: grad2d, or the sum of its staged rows
+      if (A.grad2d) {
+#pragma unroll
+        for (int k = 0; k < 9; ++k) g2[k] = A.grad2d[9 * i + k];
+      } else {
+        // the same rows in the same order as the gather into grad2d, so the values are identical
+#pragma unroll
+        for (int k = 0; k < 9; ++k) g2[k] = 0.f;
+        const uint32_t t = A.tiles[i];
+        const uint64_t base = (uint64_t)A.goff_blk[i / kGoffBlock] + A.goff[i];
+        for (uint32_t j = 0; j < t; ++j) {
+          if (base + j >= A.staging_cap) break;
+          const float* e = A.staging + 9 * (base + j);
+#pragma unroll
+          for (int k = 0; k < 9; ++k) g2[k] += e[k];
+        }
+      }
+      const float gu = g2[0], gv = g2[1];
+      const float gA = g2[2], gB = g2[3], gC = g2[4];
+      const float go = g2[5];
+      gr[0] = g2[6];
+      gr[1] = g2[7];
+      gr[2] = g2[8];
+
+      // ---- opacity ----------------------------------------------------------------------
+      g[10] = P.o * (1.f - P.o) * go;
+
+      // ---- conic = S2^-1:  dL/dS2 = -Q G Q with G = [[gA, gB/2], [gB/2, gC]] -------------
+      const float hb = 0.5f * gB;
+      const float q00 = P.Qa * gA + P.Qb * hb, q01 = P.Qa * hb + P.Qb * gC;
+      const float q10 = P.Qb * gA + P.Qc * hb, q11 = P.Qb * hb + P.Qc * gC;
+      const float G00 = -(q00 * P.Qa + q01 * P.Qb);
+      const float G01 = -(q00 * P.Qb + q01 * P.Qc);
+      const float G11 = -(q10 * P.Qb + q11 * P.Qc);
+
+      // ---- S2 = T Sigma T^T (+0.3 I): dL/dSigma = T^T G T, dL/dT = 2 G T Sigma ---------
+      const float* T = P.T;
+      const float* S = P.Sg;
+      // GT = G T (2x3)
+      float GT0[3], GT1[3];
+      for (int k = 0; k < 3; ++k) {
+        GT0[k] = G00 * T[k] + G01 * T[3 + k];
+        GT1[k] = G01 * T[k] + G11 * T[3 + k];
+      }
+      // dL/dSigma (symmetric, xx xy xz yy yz zz) = T^T (G T)
+      float gS[6];
+      gS[0] = T[0] * GT0[0] + T[3] * GT1[0];
+      gS[1] = T[0] * GT0[1] + T[3] * GT1[1];
+      gS[2] = T[0] * GT0[2] + T[3] * GT1[2];
+      gS[3] = T[1] * GT0[1] + T[4] * GT1[1];
+      gS[4] = T[1] * GT0[2] + T[4] * GT1[2];
+      gS[5] = T[2] * GT0[2] + T[5] * GT1[2];
+      // dL/dT = 2 (G T) Sigma
+      float gT[6];
+      gT[0] = 2.f * (GT0[0] * S[0] + GT0[1] * S[1] + GT0[2] * S[2]);
+      gT[1] = 2.f * (GT0[0] * S[1] + GT0[1] * S[3] + GT0[2] * S[4]);
+      gT[2] = 2.f * (GT0[0] * S[2] + GT0[1] * S[4] + GT0[2] * S[5]);
+      gT[3] = 2.f * (GT1[0] * S[0] + GT1[1] * S[1] + GT1[2] * S[2]);
+      gT[4] = 2.f * (GT1[0] * S[1] + GT1[1] * S[3] + GT1[2] * S[4]);
+      gT[5] = 2.f * (GT1[0] * S[2] + GT1[1] * S[4] + GT1[2] * S[5]);
+      // T = J Rc: dL/dJ = dL/dT Rc^T (only J00, J02, J11, J12 vary)
+      const float gJ00 = gT[0] * c.R[0] + gT[1] * c.R[1] + gT[2] * c.R[2];
+      const float gJ02 = gT[0] * c.R[6] + gT[1] * c.R[7] + gT[2] * c.R[8];
+      const float gJ11 = gT[3] * c.R[3] + gT[4] * c.R[4] + gT[5] * c.R[5];
+      const float gJ12 = gT[3] * c.R[6] + gT[4] * c.R[7] + gT[5] * c.R[8];
+
+      // ---- camera-space position ----------------------------------------------------------
+      const float iz = P.iz, iz2 = iz * iz;
+      float gx = gu * c.fx * iz;
+      float gy = gv * c.fy * iz;
+      float gz = -(gu * c.fx * P.x + gv * c.fy * P.y) * iz2;
+      gz += -(gJ00 * c.fx + gJ11 * c.fy) * iz2;
+      // J02 = -fx xr / z: xr = x/z when unclamped, a constant when clamped
+      if (!P.xcl) {
+        gx += -gJ02 * c.fx * iz2;
+        gz += 2.f * gJ02 * c.fx * P.x * iz2 * iz;
+      } else {
+        gz += gJ02 * c.fx * P.xr * iz2;  // d(-fx xr / z)/dz with xr constant
+      }
+      if (!P.ycl) {
+        gy += -gJ12 * c.fy * iz2;
+        gz += 2.f * gJ12 * c.fy * P.y * iz2 * iz;
+      } else {
+        gz += gJ12 * c.fy * P.yr * iz2;
+      }
+      // p = Rc mu + t
+      g[0] += c.R[0] * gx + c.R[3] * gy + c.R[6] * gz;
+      g[1] += c.R[1] * gx + c.R[4] * gy + c.R[7] * gz;
+      g[2] += c.R[2] * gx + c.R[5] * gy + c.R[8] * gz;
+
+      // ---- Sigma = M M^T: dL/dM = 2 dL/dSigma M ------------------------------------------
+      const float* M = P.M;
+      float gM[9];
+      const float Sfull[9] = {gS[0], gS[1], gS[2], gS[1], gS[3], gS[4], gS[2], gS[4], gS[5]};
+      for (int r = 0; r < 3; ++r)
+        for (int k = 0; k < 3; ++k)
+          gM[3 * r + k] = 2.f * (Sfull[3 * r + 0] * M[k] + Sfull[3 * r + 1] * M[3 + k] +
+                                 Sfull[3 * r + 2] * M[6 + k]);
+      // M = Rq diag(s): dL/ds_k = sum_r gM_rk Rq_rk; dL/dRq_rk = gM_rk s_k; s = exp(l)
+      float gR[9];
+      for (int k = 0; k < 3; ++k) {
+        const float gs = gM[k] * P.Rq[k] + gM[3 + k] * P.Rq[3 + k] + gM[6 + k] * P.Rq[6 + k];
+        g[3 + k] = gs * P.s[k];
+        gR[k] = gM[k] * P.s[k];
+        gR[3 + k] = gM[3 + k] * P.s[k];
+        gR[6 + k] = gM[6 + k] * P.s[k];
+      }
+      // rotation entries -> unit quaternion (w, x, y, z)
+      const float w = P.qn[0], x = P.qn[1], y = P.qn[2], z = P.qn[3];
+      const float s01 = gR[1] + gR[3], s02 = gR[2] + gR[6], s12 = gR[5] + gR[7];
+      const float a10 = gR[3] - gR[1], a02 = gR[2] - gR[6], a21 = gR[7] - gR[5];
+      float gq[4];
+      gq[0] = 2.f * (z * a10 + y * a02 + x * a21);
+      gq[1] = 2.f * (y * s01 + z * s02 + w * a21) - 4.f * x * (gR[4] + gR[8]);
+      gq[2] = 2.f * (x * s01 + w * a02 + z * s12) - 4.f * y * (gR[0] + gR[8]);
+      gq[3] = 2.f * (w * a10 + x * s02 + y * s12) - 4.f * z * (gR[0] + gR[4]);
+      // q_hat = q / |q|
+      const float qd = w * gq[0] + x * gq[1] + y * gq[2] + z * gq[3];
+      for (int j = 0; j < 4; ++j) g[6 + j] = (gq[j] - P.qn[j] * qd) * P.inv_qlen;
+    }
+    for (int r = 3; r < 11; ++r) finish_row(r, g[r], r < 6 ? ls[r - 3] : (r < 10 ? q[r - 6] : a));
+  }
+
+  float f[NB][3];  // SH coefficients
 #pragma unroll
   for (int k = 0; k < NB; ++k)
 #pragma unroll
     for (int ch = 0; ch < 3; ++ch) f[k][ch] = __builtin_nontemporal_load(prm + (11 + 3 * k + ch) * ld + i);
-
-  if (P.vis) {
-    float g2[9];  // this Gaussian's nine values: grad2d, or the sum of its staged rows
-    if (A.grad2d) {
-#pragma unroll
-      for (int k = 0; k < 9; ++k) g2[k] = A.grad2d[9 * i + k];
-    } else {
-      // the same rows in the same order as the gather into grad2d, so the values are identical
-#pragma unroll
-      for (int k = 0; k < 9; ++k) g2[k] = 0.f;
-      const uint32_t t = A.tiles[i];
-      const uint64_t base = (uint64_t)A.goff_blk[i / kGoffBlock] + A.goff[i];
-      for (uint32_t j = 0; j < t; ++j) {
-        if (base + j >= A.staging_cap) break;
-        const float* e = A.staging + 9 * (base + j);
-#pragma unroll
-        for (int k = 0; k < 9; ++k) g2[k] += e[k];
-      }
-    }
-    const float gu = g2[0], gv = g2[1];
-    const float gA = g2[2], gB = g2[3], gC = g2[4];
-    const float go = g2[5];
-    const float gr[3] = {g2[6], g2[7], g2[8]};
-
+  float gc[3] = {0.f, 0.f, 0.f};  // dL/drgb gated by the clamp
+  float Y[16];
+  if (vis) {
     // ---- colour: raw = 0.5 + sum_k Y_k f_k, rgb = max(raw, 0) -------------------------
     const float dv0 = mu[0] - c.pos[0], dv1 = mu[1] - c.pos[1], dv2 = mu[2] - c.pos[2];
     const float idist = 1.0f / sqrtf(dv0 * dv0 + dv1 * dv1 + dv2 * dv2);
@@ -340,127 +460,12 @@ __global__ __launch_bounds__(kBlock) void k_preprocess_backward(PrebwdArgs A, Ca
     g[0] += (gdir[0] - d0 * dd) * idist;
     g[1] += (gdir[1] - d1 * dd) * idist;
     g[2] += (gdir[2] - d2 * dd) * idist;
-
-    // ---- opacity ----------------------------------------------------------------------
-    g[10] = P.o * (1.f - P.o) * go;
-
-    // ---- conic = S2^-1:  dL/dS2 = -Q G Q with G = [[gA, gB/2], [gB/2, gC]] -------------
-    const float hb = 0.5f * gB;
-    const float q00 = P.Qa * gA + P.Qb * hb, q01 = P.Qa * hb + P.Qb * gC;
-    const float q10 = P.Qb * gA + P.Qc * hb, q11 = P.Qb * hb + P.Qc * gC;
-    const float G00 = -(q00 * P.Qa + q01 * P.Qb);
-    const float G01 = -(q00 * P.Qb + q01 * P.Qc);
-    const float G11 = -(q10 * P.Qb + q11 * P.Qc);
-
-    // ---- S2 = T Sigma T^T (+0.3 I): dL/dSigma = T^T G T, dL/dT = 2 G T Sigma ---------
-    const float* T = P.T;
-    const float* S = P.Sg;
-    // GT = G T (2x3)
-    float GT0[3], GT1[3];
-    for (int k = 0; k < 3; ++k) {
-      GT0[k] = G00 * T[k] + G01 * T[3 + k];
-      GT1[k] = G01 * T[k] + G11 * T[3 + k];
-    }
-    // dL/dSigma (symmetric, xx xy xz yy yz zz) = T^T (G T)
-    float gS[6];
-    gS[0] = T[0] * GT0[0] + T[3] * GT1[0];
-    gS[1] = T[0] * GT0[1] + T[3] * GT1[1];
-    gS[2] = T[0] * GT0[2] + T[3] * GT1[2];
-    gS[3] = T[1] * GT0[1] + T[4] * GT1[1];
-    gS[4] = T[1] * GT0[2] + T[4] * GT1[2];
-    gS[5] = T[2] * GT0[2] + T[5] * GT1[2];
-    // dL/dT = 2 (G T) Sigma
-    float gT[6];
-    gT[0] = 2.f * (GT0[0] * S[0] + GT0[1] * S[1] + GT0[2] * S[2]);
-    gT[1] = 2.f * (GT0[0] * S[1] + GT0[1] * S[3] + GT0[2] * S[4]);
-    gT[2] = 2.f * (GT0[0] * S[2] + GT0[1] * S[4] + GT0[2] * S[5]);
-    gT[3] = 2.f * (GT1[0] * S[0] + GT1[1] * S[1] + GT1[2] * S[2]);
-    gT[4] = 2.f * (GT1[0] * S[1] + GT1[1] * S[3] + GT1[2] * S[4]);
-    gT[5] = 2.f * (GT1[0] * S[2] + GT1[1] * S[4] + GT1[2] * S[5]);
-    // T = J Rc: dL/dJ = dL/dT Rc^T (only J00, J02, J11, J12 vary)
-    const float gJ00 = gT[0] * c.R[0] + gT[1] * c.R[1] + gT[2] * c.R[2];
-    const float gJ02 = gT[0] * c.R[6] + gT[1] * c.R[7] + gT[2] * c.R[8];
-    const float gJ11 = gT[3] * c.R[3] + gT[4] * c.R[4] + gT[5] * c.R[5];
-    const float gJ12 = gT[3] * c.R[6] + gT[4] * c.R[7] + gT[5] * c.R[8];
-
-    // ---- camera-space position ----------------------------------------------------------
-    const float iz = P.iz, iz2 = iz * iz;
-    float gx = gu * c.fx * iz;
-    float gy = gv * c.fy * iz;
-    float gz = -(gu * c.fx * P.x + gv * c.fy * P.y) * iz2;
-    gz += -(gJ00 * c.fx + gJ11 * c.fy) * iz2;
-    // J02 = -fx xr / z: xr = x/z when unclamped, a constant when clamped
-    if (!P.xcl) {
-      gx += -gJ02 * c.fx * iz2;
-      gz += 2.f * gJ02 * c.fx * P.x * iz2 * iz;
-    } else {
-      gz += gJ02 * c.fx * P.xr * iz2;  // d(-fx xr / z)/dz with xr constant
-    }
-    if (!P.ycl) {
-      gy += -gJ12 * c.fy * iz2;
-      gz += 2.f * gJ12 * c.fy * P.y * iz2 * iz;
-    } else {
-      gz += gJ12 * c.fy * P.yr * iz2;
-    }
-    // p = Rc mu + t
-    g[0] += c.R[0] * gx + c.R[3] * gy + c.R[6] * gz;
-    g[1] += c.R[1] * gx + c.R[4] * gy + c.R[7] * gz;
-    g[2] += c.R[2] * gx + c.R[5] * gy + c.R[8] * gz;
-
-    // ---- Sigma = M M^T: dL/dM = 2 dL/dSigma M ------------------------------------------
-    const float* M = P.M;
-    float gM[9];
-    const float Sfull[9] = {gS[0], gS[1], gS[2], gS[1], gS[3], gS[4], gS[2], gS[4], gS[5]};
-    for (int r = 0; r < 3; ++r)
-      for (int k = 0; k < 3; ++k)
-        gM[3 * r + k] = 2.f * (Sfull[3 * r + 0] * M[k] + Sfull[3 * r + 1] * M[3 + k] +
-                               Sfull[3 * r + 2] * M[6 + k]);
-    // M = Rq diag(s): dL/ds_k = sum_r gM_rk Rq_rk; dL/dRq_rk = gM_rk s_k; s = exp(l)
-    float gR[9];
-    for (int k = 0; k < 3; ++k) {
-      const float gs = gM[k] * P.Rq[k] + gM[3 + k] * P.Rq[3 + k] + gM[6 + k] * P.Rq[6 + k];
-      g[3 + k] = gs * P.s[k];
-      gR[k] = gM[k] * P.s[k];
-      gR[3 + k] = gM[3 + k] * P.s[k];
-      gR[6 + k] = gM[6 + k] * P.s[k];
-    }
-    // rotation entries -> unit quaternion (w, x, y, z)
-    const float w = P.qn[0], x = P.qn[1], y = P.qn[2], z = P.qn[3];
-    const float s01 = gR[1] + gR[3], s02 = gR[2] + gR[6], s12 = gR[5] + gR[7];
-    const float a10 = gR[3] - gR[1], a02 = gR[2] - gR[6], a21 = gR[7] - gR[5];
-    float gq[4];
-    gq[0] = 2.f * (z * a10 + y * a02 + x * a21);
-    gq[1] = 2.f * (y * s01 + z * s02 + w * a21) - 4.f * x * (gR[4] + gR[8]);
-    gq[2] = 2.f * (x * s01 + w * a02 + z * s12) - 4.f * y * (gR[0] + gR[8]);
-    gq[3] = 2.f * (w * a10 + x * s02 + y * s12) - 4.f * z * (gR[0] + gR[4]);
-    // q_hat = q / |q|
-    const float qd = w * gq[0] + x * gq[1] + y * gq[2] + z * gq[3];
-    for (int j = 0; j < 4; ++j) g[6 + j] = (gq[j] - P.qn[j] * qd) * P.inv_qlen;
   }
-
-  // ---- write gradients and/or apply Adam, row by row ----------------------------------
-  const bool adam = A.m != nullptr;
+  for (int r = 0; r < 3; ++r) finish_row(r, g[r], mu[r]);
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    float gr_, th;
-    if (r < 11) {
-      gr_ = g[r];
-      th = r < 3 ? mu[r] : (r < 6 ? ls[r - 3] : (r < 10 ? q[r - 6] : a));
-    } else {
-      const int k = (r - 11) / 3, ch = (r - 11) - 3 * k;
-      gr_ = P.vis ? Y[k] * gc[ch] : 0.f;
-      th = f[k][ch];
-    }
-    const int64_t e = (int64_t)r * ld + i;
-    if (A.grads) A.grads[e] = gr_;
-    if (adam) {
-      const float m = A.b1 * __builtin_nontemporal_load(A.m + e) + A.omb1 * gr_;
-      const float v = A.b2 * __builtin_nontemporal_load(A.v + e) + A.omb2 * gr_ * gr_;
-      __builtin_nontemporal_store(m, A.m + e);
-      __builtin_nontemporal_store(v, A.v + e);
-      __builtin_nontemporal_store(th - A.lr * (m * A.inv_bc1) / (sqrtf(v * A.inv_bc2) + A.eps), prm + e);
-    }
-  }
+  for (int k = 0; k < NB; ++k)
+#pragma unroll
+    for (int ch = 0; ch < 3; ++ch) finish_row(11 + 3 * k + ch, vis ? Y[k] * gc[ch] : 0.f, f[k][ch]);
 }
 
 }  // namespace
