@@ -83,18 +83,23 @@ def alg_flops(phase, examined, walked, composited):
     return 0
 
 
-# the kernel of each single-kernel phase; the forward and backward blend phases also run their
-# segment plan, item lists and gradient gather, so their event time is not one kernel's
-KERNEL_OF = {"preprocess": "k_preprocess<3>", "prebwd_adam": "k_preprocess_backward<3>"}
+# the kernel of each single-kernel phase and what bounds it: the image pass is the fused blend
+# kernel plus a one-workgroup sum of the per-tile losses (a few microseconds); the separate
+# forward and backward phases also run their plan and staging kernels, so their event time is
+# not one kernel's
+KERNEL_OF = {"preprocess": ("k_preprocess<3>", "hbm"), "image_pass": ("k_blend_step", "alu"),
+             "prebwd_adam": ("k_preprocess_backward<3>", "hbm")}
 
 # HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE passes over this workload,
 # each scaled by the factor the same counter reads for a plain copy of known size; keyed by
 # the SHA-256 of the kernel's source file, so a changed kernel reports null
 COUNTER_TRAFFIC = {
-    "preprocess": {"source": "preprocess.hip", "bytes": 1200086935,
-                   "sha256": "7c692f702ba0d64fc7f1df3232058bd36e3e072e8e7729102dcc488c797b6a58"},
-    "prebwd_adam": {"source": "preprocess.hip", "bytes": 5943347106,
-                    "sha256": "7c692f702ba0d64fc7f1df3232058bd36e3e072e8e7729102dcc488c797b6a58"},
+    "preprocess": {"source": "preprocess.hip", "bytes": 1200081815,
+                   "sha256": "b65eac29a7e37f262ed39af1cfcbf9a9d1656e0873ea93e7e89e8f5ee9b2d2c6"},
+    "image_pass": {"source": "blend.hip", "bytes": 6697713812,
+                   "sha256": "237a7aba22a2e8da715a13a7cfdcd4ade266f2e2f979a826101fca476c61cccc"},
+    "prebwd_adam": {"source": "preprocess.hip", "bytes": 5943349650,
+                    "sha256": "b65eac29a7e37f262ed39af1cfcbf9a9d1656e0873ea93e7e89e8f5ee9b2d2c6"},
 }
 
 
@@ -274,7 +279,7 @@ def main():
     blends = torch.zeros(3, dtype=torch.int64, device="cuda")
     bg = (0.0, 0.0, 0.0)
     fused = not args.separate_passes
-    phases = (["preprocess", "bin_and_sort", "image_pass", "prebwd_adam"] if fused else
+    phases = (["preprocess", "bin_and_sort", "render_plan", "image_pass", "prebwd_adam"] if fused else
               ["preprocess", "bin_and_sort", "forward", "loss", "backward_blend", "prebwd_adam"])
 
     def step(t, view, ev=None):
@@ -293,6 +298,8 @@ def main():
         mark()
         g2 = buf.grad2d if args.unfused_adam else None
         if fused:  # forward, L1 and backward blend in one kernel; the sums stay staged
+            gsmi.render_plan(buf.scene, cam, buf.proj, buf.ranges, buf.render_ws)
+            mark()
             gsmi.render_step(buf.scene, cam, buf.proj, buf.vals, buf.ranges, bg, targets[view], buf.image,
                              buf.T_final, buf.last, buf.loss, buf.dLdI, buf.render_ws, grad2d=g2, blend_count=blends)
             mark()
@@ -344,14 +351,21 @@ def main():
     n_vis = N
     sums = blends.cpu().tolist()
     per_launch = [x / args.steps for x in sums]  # examined, walked, composited per view
-    single = {ph: ph_ms[ph] for ph in KERNEL_OF}
+    single = {ph: ph_ms[ph] for ph in KERNEL_OF if ph in ph_ms}
     dom = max(single, key=single.get)
     sec = ph_ms[dom] * 1e-3
-    work = alg_bytes(dom, N, R, Kmean, P, T, n_vis)
-    achieved = work / sec / 1e9
-    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    roof.update({"traffic": counter_traffic(dom), "kernel": KERNEL_OF[dom], "work_per_launch": work,
+    kname, bound = KERNEL_OF[dom]
+    if bound == "alu":
+        work = alg_flops(dom, *per_launch)
+        achieved = work / sec / 1e12
+        roof = {"bound": "alu", "achieved": round(achieved, 2), "peak": round(ALU_PEAK_TFLOPS, 1),
+                "unit": "TFLOP/s", "frac": round(achieved / ALU_PEAK_TFLOPS, 4)}
+    else:
+        work = alg_bytes(dom, N, R, Kmean, P, T, n_vis)
+        achieved = work / sec / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    roof.update({"traffic": counter_traffic(dom), "kernel": kname, "work_per_launch": work,
                  "ms_per_launch": round(ph_ms[dom], 4)})
     per_phase = {}
     for ph in phases:

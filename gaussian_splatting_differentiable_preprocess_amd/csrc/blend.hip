@@ -1254,14 +1254,19 @@ hipError_t launch_blend_backward(const CamK& cam, int64_t n, const gs_splat* spl
   return hipGetLastError();
 }
 
+hipError_t launch_step_plan(const CamK& cam, int64_t n, const uint32_t* tiles, const uint32_t* ranges,
+                            const RenderWs& ws, hipStream_t s) {
+  launch_plan(cam.TX * cam.TY, reinterpret_cast<const uint2*>(ranges), ws, true, s);
+  if (n > 0) launch_staging(n, tiles, ws, s);
+  return hipGetLastError();
+}
+
 hipError_t launch_blend_step(const CamK& cam, int64_t n, const gs_splat* splat, const uint32_t* tiles,
                              const uint32_t* vals, const uint32_t* ranges, float bg0, float bg1, float bg2,
                              const float* target, float* image, float* T_final, uint32_t* last_contrib,
                              uint32_t* n_examined, uint64_t* blend_count, float* loss, float* dLdI,
                              float* grad2d, const RenderWs& ws, hipStream_t s) {
   const int T = cam.TX * cam.TY;
-  launch_plan(T, reinterpret_cast<const uint2*>(ranges), ws, true, s);
-  if (n > 0) launch_staging(n, tiles, ws, s);
   FwdArgs fa = fwd_args(cam, n, splat, vals, ranges, bg0, bg1, bg2, image, T_final, last_contrib, n_examined,
                         blend_count, ws);
   const int64_t count = 3 * (int64_t)cam.W * cam.H;

@@ -165,8 +165,12 @@ hipError_t launch_blend_backward(const CamK& cam, int64_t n, const gs_splat* spl
 hipError_t launch_fill_u32(uint32_t* p, int64_t count, uint32_t value, hipStream_t s);
 hipError_t launch_fill_f32(float* p, int64_t count, float value, hipStream_t s);
 size_t loss_workspace_bytes(int64_t count);
-// Fused forward, L1 loss and backward blend of one training step; leaves the per-intersection
-// gradient sums staged in ws for the preprocess backward.
+// The fused step's preparation: segment plan, tile order, empty item list, staging offsets and
+// cleared staging rows.
+hipError_t launch_step_plan(const CamK& cam, int64_t n, const uint32_t* tiles, const uint32_t* ranges,
+                            const RenderWs& ws, hipStream_t s);
+// Fused forward, L1 loss and backward blend of one training step (after launch_step_plan);
+// leaves the per-intersection gradient sums staged in ws for the preprocess backward.
 hipError_t launch_blend_step(const CamK& cam, int64_t n, const gs_splat* splat, const uint32_t* tiles,
                              const uint32_t* vals, const uint32_t* ranges, float bg0, float bg1, float bg2,
                              const float* target, float* image, float* T_final, uint32_t* last_contrib,

@@ -24,7 +24,7 @@ SPLAT_FLOATS = 12  # 48-byte record: u, v, radius_x, radius_y | A, B, C, opacity
 EXPORTS = (
     "gs_version", "gs_last_error", "gs_preprocess", "gs_bin_and_sort_workspace", "gs_bin_and_sort",
     "gs_render_workspace", "gs_render_workspace_capacity", "gs_render_forward", "gs_loss_l1_workspace", "gs_loss_l1", "gs_render_backward",
-    "gs_render_step", "gs_preprocess_backward", "gs_preprocess_backward_staged", "gs_adam_step",
+    "gs_render_plan", "gs_render_step", "gs_preprocess_backward", "gs_preprocess_backward_staged", "gs_adam_step",
 )
 
 
@@ -87,6 +87,7 @@ def load(path: str = LIB_PATH):
     L.gs_loss_l1.argtypes = [i64, P, P, P, P, P, sz, P]
     L.gs_render_backward.argtypes = [SP, P, CP, GsProj, P, P, ctypes.POINTER(ctypes.c_float), P, P, P,
                                      P, P, AP, P, sz, P]
+    L.gs_render_plan.argtypes = [SP, CP, GsProj, P, P, sz, P]
     L.gs_render_step.argtypes = [SP, CP, GsProj, P, P, ctypes.POINTER(ctypes.c_float), P, P, P, P, P, P, P, P, P, P,
                                  sz, P]
     L.gs_preprocess_backward.argtypes = [SP, P, CP, P, P, AP, P]
@@ -247,10 +248,17 @@ def render_backward(scene: GsScene, params, cam: GsCamera, proj: Proj, vals, ran
                                      _ptr(render_ws), _nbytes(render_ws), _stream(stream)))
 
 
+def render_plan(scene: GsScene, cam: GsCamera, proj: Proj, ranges, render_ws, stream=None):
+    """Prepares render_ws for render_step over the lists of these ranges."""
+    _check(load().gs_render_plan(ctypes.byref(scene), ctypes.byref(cam), proj.c(), _ptr(ranges), _ptr(render_ws),
+                                 _nbytes(render_ws), _stream(stream)))
+
+
 def render_step(scene: GsScene, cam: GsCamera, proj: Proj, vals, ranges, bg, target, image, T_final, last_contrib,
                 loss, dL_dimage, render_ws, grad2d=None, n_examined=None, blend_count=None, stream=None):
-    """Forward blend, L1 loss and backward blend of one step in one fused kernel; the gradient
-    sums stay staged in render_ws for preprocess_backward_staged (and go to grad2d if given)."""
+    """Forward blend, L1 loss and backward blend of one step in one fused kernel (after
+    render_plan on the same render_ws); the gradient sums stay staged in render_ws for
+    preprocess_backward_staged (and go to grad2d if given)."""
     if blend_count is not None and (blend_count.numel() < 3 or blend_count.element_size() != 8):
         raise ValueError("blend_count must be a device int64 tensor of at least 3 elements")
     _check(load().gs_render_step(ctypes.byref(scene), ctypes.byref(cam), proj.c(), _ptr(vals), _ptr(ranges), _bg(bg),

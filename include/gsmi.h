@@ -232,6 +232,14 @@ int gs_render_backward(const gs_scene* scene, float* params, const gs_camera* ca
                        float* grad2d, float* grads, const gs_adam* adam, void* render_ws,
                        size_t render_ws_bytes, hipStream_t stream);
 
+/* Prepares render_ws for gs_render_step over these lists (ranges from gs_bin_and_sort, proj.tiles
+ * from gs_preprocess, the same camera): the segment plan and tile order of the forward, an empty
+ * list of backward work items, and each Gaussian's cleared staging rows for the gradient sums.
+ * Kept apart from gs_render_step so that the fused kernel can be timed alone.  Errors as
+ * gs_render_forward. */
+int gs_render_plan(const gs_scene* scene, const gs_camera* cam, gs_proj proj, const uint32_t* ranges,
+                   void* render_ws, size_t render_ws_bytes, hipStream_t stream);
+
 /* The image pass of one training step, fused: the forward blend (as gs_render_forward), the L1
  * loss against target (as gs_loss_l1) and the backward blend (as gs_render_backward with
  * grad2d, grads and adam null) in one persistent kernel.  Workgroups that finish a tile's
@@ -244,7 +252,8 @@ int gs_render_backward(const gs_scene* scene, float* params, const gs_camera* ca
  *   dL_dimage[H][W][3]  out: sign(image - target) / (3HW), sign(0) = 0
  *   grad2d[ld][9]       out, nullable: as gs_render_backward's grad2d (the staged sums added
  *                       per Gaussian in the order of its tile rect)
- *   render_ws           as gs_render_forward; on return it holds the forward's state and each
+ *   render_ws           as left by gs_render_plan for the same lists, camera and proj (call it
+ *                       first, once per step); on return it holds the forward's state and each
  *                       intersection's nine gradient sums, staged for
  *                       gs_preprocess_backward_staged (same camera, proj and render_ws), which
  *                       finishes the step.  gs_render_backward may also be run on it.

@@ -166,3 +166,28 @@ def test_fused_step_checks_its_arguments():
     assert "tiles" in gsmi.last_error()
     assert call(ranges=ctypes.c_void_p(4096 + 4)) == gsmi.GS_ERR_INVALID_ARGUMENT
     assert "aligned" in gsmi.last_error()
+
+
+def test_render_plan_checks_its_arguments():
+    """gs_render_plan rejects a missing or short workspace, missing ranges or tiles and
+    misaligned ranges before any HIP call."""
+    L = gsmi.load()
+    cam = gsmi.GsCamera()
+    cam.fx = cam.fy = 100.0
+    cam.width = cam.height = 64
+    cam.near_plane = 0.01
+    cam.viewmat[0] = cam.viewmat[5] = cam.viewmat[10] = 1.0
+    p = ctypes.c_void_p(4096)
+    need = gsmi.render_workspace(64, 64, 10, 0)
+    sc = gsmi.make_scene(10, 10, 0)
+    proj = gsmi.GsProj(4096, 4096, 4096, 4096)
+    call = lambda proj=proj, ranges=p, ws=p, nb=need: L.gs_render_plan(ctypes.byref(sc), ctypes.byref(cam), proj,
+                                                                        ranges, ws, nb, None)
+    assert call(ws=None) == gsmi.GS_ERR_INVALID_ARGUMENT and "null" in gsmi.last_error()
+    assert call(ranges=None) == gsmi.GS_ERR_INVALID_ARGUMENT and "null" in gsmi.last_error()
+    for ws, nb in ((p, 16), (ctypes.c_void_p(4096 + 64), need)):
+        assert call(ws=ws, nb=nb) == gsmi.GS_ERR_INVALID_ARGUMENT and "workspace" in gsmi.last_error()
+    assert call(proj=gsmi.GsProj(4096, None, 4096, 4096)) == gsmi.GS_ERR_INVALID_ARGUMENT
+    assert "tiles" in gsmi.last_error()
+    assert call(ranges=ctypes.c_void_p(4096 + 4)) == gsmi.GS_ERR_INVALID_ARGUMENT
+    assert "aligned" in gsmi.last_error()
