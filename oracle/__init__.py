@@ -65,6 +65,8 @@ def lib():
         L.or_render_bruteforce.argtypes = [i32, i32, P, i64, P, P, P, P, P, P]
         L.or_loss_l1.argtypes = [i64, P, P, P]
         L.or_loss_l1.restype = dbl
+        L.or_loss_l1_dssim.argtypes = [i32, i32, P, P, dbl, P, P]
+        L.or_loss_l1_dssim.restype = dbl
         L.or_render_backward.argtypes = [i32, i32, P, i64, P, P, P, P, P, P, i64]
         L.or_preprocess_backward.argtypes = [i64, i32, P, P, i32, i32, P, P]
         L.or_adam.argtypes = [i64, P, P, P, P, i32, dbl, dbl, dbl, dbl]
@@ -217,6 +219,18 @@ def loss_l1(image, target):
     g = np.zeros_like(image)
     L = lib().or_loss_l1(image.size, _p(image), _p(target), _p(g))
     return L, g
+
+
+def loss_l1_dssim(image, target, lam=0.2):
+    """L1 + D-SSIM loss of an [H][W][3] image -> (L, mean L1, mean SSIM, dL/dimage float64)."""
+    image = _f64(image)
+    target = _f64(target)
+    H, W = image.shape[0], image.shape[1]
+    assert image.shape == (H, W, 3) and target.shape == image.shape
+    g = np.zeros_like(image)
+    parts = np.zeros(2)
+    L = lib().or_loss_l1_dssim(W, H, _p(image), _p(target), float(lam), _p(parts), _p(g))
+    return L, float(parts[0]), float(parts[1]), g
 
 
 def render_backward(proj, vals, rng, W, H, dLdI, bg=(0.0, 0.0, 0.0), decisions=None):

@@ -664,6 +664,117 @@ double or_loss_l1(int64_t count, const double* image, const double* target, doub
 }
 
 /* ------------------------------------------------------------------------------------ */
+/* L1 + D-SSIM loss ([Scaling], the loss passage: a lambda-weighted combination of an L1   */
+/* term and a D-SSIM term; step "Compute the loss locally": L1 and fused SSIM)            */
+/* ------------------------------------------------------------------------------------ */
+/* The pages print neither the formula nor its constants.  Reading taken: SSIM of Wang et
+ * al. with an 11x11 Gaussian window of standard deviation 1.5 (normalised to sum 1),
+ * C1 = 0.01^2 and C2 = 0.03^2 for a data range of 1, computed per colour channel over the
+ * window positions that lie wholly inside the image (no padding), and averaged over
+ * channels and positions; D-SSIM = 1 - SSIM and
+ *     L = (1 - lambda) * mean |I - I*| + lambda * (1 - SSIM).
+ * Per position p (top-left corner of its window) and channel:
+ *     mu_x = sum_w x, mu_y = sum_w y, var_x = sum_w x^2 - mu_x^2, var_y likewise,
+ *     cov = sum_w x y - mu_x mu_y,
+ *     S = (2 mu_x mu_y + C1)(2 cov + C2) / ((mu_x^2 + mu_y^2 + C1)(var_x + var_y + C2)).
+ * The gradient with respect to the rendered image x follows the chain rule through the
+ * three window sums that depend on x (sum_w x, sum_w x^2, sum_w x y):
+ *     dS/d(sum_w x)   = S (2 mu_y / A - 2 mu_y / B - 2 mu_x / C + 2 mu_x / D)
+ *     dS/d(sum_w x^2) = -S / D
+ *     dS/d(sum_w x y) = 2 S / B
+ * with A, B, C, D the four factors above in order, and each window sum passes its partial
+ * back to every pixel of its window with the window weight (times 1, 2x or y).
+ * image, target, dLdI: [H][W][3].  parts (nullable) receives {mean L1, mean SSIM}.
+ * Returns L, or NAN when the image is smaller than the window. */
+#define SSIM_WIN 11
+#define SSIM_SIGMA 1.5
+#define SSIM_C1 (0.01 * 0.01)
+#define SSIM_C2 (0.03 * 0.03)
+
+double or_loss_l1_dssim(int W, int H, const double* image, const double* target, double lambda,
+                        double* parts, double* dLdI) {
+  if (W < SSIM_WIN || H < SSIM_WIN) return NAN;
+  double g[SSIM_WIN], gsum = 0.0;
+  for (int a = 0; a < SSIM_WIN; a++) {
+    const double d = (double)(a - SSIM_WIN / 2);
+    g[a] = exp(-d * d / (2.0 * SSIM_SIGMA * SSIM_SIGMA));
+    gsum += g[a];
+  }
+  for (int a = 0; a < SSIM_WIN; a++) g[a] /= gsum;
+  const int Wv = W - SSIM_WIN + 1, Hv = H - SSIM_WIN + 1;
+  const int64_t nv = (int64_t)Wv * Hv, npx = (int64_t)W * H;
+  /* per channel and valid position: dS/d(sum x), dS/d(sum x^2), dS/d(sum xy) */
+  double* d_mu = (double*)malloc((size_t)(3 * nv) * sizeof(double));
+  double* d_xx = (double*)malloc((size_t)(3 * nv) * sizeof(double));
+  double* d_xy = (double*)malloc((size_t)(3 * nv) * sizeof(double));
+  double ssim_sum = 0.0;
+#pragma omp parallel for reduction(+ : ssim_sum) schedule(static)
+  for (int r = 0; r < Hv; r++) {
+    for (int s = 0; s < Wv; s++) {
+      for (int c = 0; c < 3; c++) {
+        double mx = 0.0, my = 0.0, exx = 0.0, eyy = 0.0, exy = 0.0;
+        for (int a = 0; a < SSIM_WIN; a++)
+          for (int b = 0; b < SSIM_WIN; b++) {
+            const double w = g[a] * g[b];
+            const int64_t e = ((int64_t)(r + a) * W + (s + b)) * 3 + c;
+            const double x = image[e], y = target[e];
+            mx += w * x;
+            my += w * y;
+            exx += w * x * x;
+            eyy += w * y * y;
+            exy += w * x * y;
+          }
+        const double vx = exx - mx * mx, vy = eyy - my * my, cxy = exy - mx * my;
+        const double A = 2.0 * mx * my + SSIM_C1, B = 2.0 * cxy + SSIM_C2;
+        const double C = mx * mx + my * my + SSIM_C1, D = vx + vy + SSIM_C2;
+        const double S = (A * B) / (C * D);
+        ssim_sum += S;
+        const int64_t p = (int64_t)c * nv + (int64_t)r * Wv + s;
+        d_mu[p] = S * (2.0 * my / A - 2.0 * my / B - 2.0 * mx / C + 2.0 * mx / D);
+        d_xx[p] = -S / D;
+        d_xy[p] = 2.0 * S / B;
+      }
+    }
+  }
+  const double M = 3.0 * (double)nv;
+  const double ssim = ssim_sum / M;
+  double l1_sum = 0.0;
+  for (int64_t e = 0; e < 3 * npx; e++) l1_sum += fabs(image[e] - target[e]);
+  const double l1 = l1_sum / (3.0 * (double)npx);
+#pragma omp parallel for schedule(static)
+  for (int qr = 0; qr < H; qr++) {
+    for (int qs = 0; qs < W; qs++) {
+      for (int c = 0; c < 3; c++) {
+        const int64_t e = ((int64_t)qr * W + qs) * 3 + c;
+        const double x = image[e], y = target[e];
+        double dS = 0.0; /* d(sum over positions and channels of S) / dx */
+        for (int a = 0; a < SSIM_WIN; a++) {
+          const int r = qr - a;
+          if (r < 0 || r >= Hv) continue;
+          for (int b = 0; b < SSIM_WIN; b++) {
+            const int s = qs - b;
+            if (s < 0 || s >= Wv) continue;
+            const int64_t p = (int64_t)c * nv + (int64_t)r * Wv + s;
+            dS += g[a] * g[b] * (d_mu[p] + 2.0 * x * d_xx[p] + y * d_xy[p]);
+          }
+        }
+        const double d = x - y;
+        const double sgn = d > 0.0 ? 1.0 : (d < 0.0 ? -1.0 : 0.0);
+        dLdI[e] = (1.0 - lambda) * sgn / (3.0 * (double)npx) - lambda * dS / M;
+      }
+    }
+  }
+  free(d_mu);
+  free(d_xx);
+  free(d_xy);
+  if (parts) {
+    parts[0] = l1;
+    parts[1] = ssim;
+  }
+  return (1.0 - lambda) * l1 + lambda * (1.0 - ssim);
+}
+
+/* ------------------------------------------------------------------------------------ */
 /* backward blend: exact derivative of the branch the forward took                       */
 /* ------------------------------------------------------------------------------------ */
 /* grad2d [9][n] (u, v, A, B, C, opacity, r, g, b), accumulated in double over pixels in

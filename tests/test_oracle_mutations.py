@@ -36,6 +36,12 @@ MUTATIONS = [
     ("clamped alpha grad", "if (list[k].clamped) continue;", "if (0) continue;"),
     ("sigmoid grad", "grads[10 * n + i] = F.o * (1.0 - F.o) * go;", "grads[10 * n + i] = F.o * go;"),
     ("background term", "- (suffix[k + 1] + Tf * bgg) / (1.0 - a)", "- (suffix[k + 1]) / (1.0 - a)"),
+    ("ssim C2", "D = vx + vy + SSIM_C2;", "D = vx + vy;"),
+    ("ssim variance sign", "const double vx = exx - mx * mx,", "const double vx = exx + mx * mx,"),
+    ("ssim window sigma", "#define SSIM_SIGMA 1.5", "#define SSIM_SIGMA 1.0"),
+    ("dssim cov grad", "d_xy[p] = 2.0 * S / B;", "d_xy[p] = S / B;"),
+    ("dssim mean grad", "- 2.0 * mx / C + 2.0 * mx / D", "+ 2.0 * mx / C + 2.0 * mx / D"),
+    ("dssim lambda", "dLdI[e] = (1.0 - lambda) * sgn", "dLdI[e] = lambda * sgn"),
 ]
 
 
@@ -50,7 +56,7 @@ def test_planted_mistake_is_caught(name, old, new, tmp_path):
     with open(dst / "oracle" / "oracle.c", "w") as f:
         f.write(src.replace(old, new, 1))
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        "tests/test_oracle_pins.py", "tests/test_oracle_gradients.py"],
+                        "tests/test_oracle_pins.py", "tests/test_oracle_gradients.py", "tests/test_oracle_ssim.py"],
                        cwd=dst, capture_output=True, text=True, timeout=600)
     tail = "\n".join(r.stdout.strip().splitlines()[-3:])
     assert r.returncode == 1, f"planted mistake {name!r} was not caught by the pins:\n{tail}"
@@ -63,6 +69,6 @@ def test_unmutated_copy_passes(tmp_path):
     shutil.copytree(ROOT, dst, ignore=shutil.ignore_patterns(
         ".git", "_work", "_build", "gpurun_out", "*.so", "__pycache__", "profiles"))
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        "tests/test_oracle_pins.py", "tests/test_oracle_gradients.py"],
+                        "tests/test_oracle_pins.py", "tests/test_oracle_gradients.py", "tests/test_oracle_ssim.py"],
                        cwd=dst, capture_output=True, text=True, timeout=600)
     assert r.returncode == 0, r.stdout[-2000:]
