@@ -11,10 +11,11 @@ Prints ONE JSON line on stdout (progress goes to stderr):
   value        Gaussian-pixel blends per second over the timed steps (sum of n_examined, the
                list entries each pixel's forward walk examines, / wall time)
   ms_per_step  wall time per step
-  roofline     the dominant kernel (the preprocess backward fused with Adam, the longest
-               kernel of the step, alone in its phase) against its roof, from HIP events on the
-               launch stream: the bytes the method must move / time against 8 TB/s, with the
-               HBM bytes the counters measured for it (COUNTER_TRAFFIC)
+  roofline     the dominant kernel (the longest single-kernel phase of the step: the fused image
+               pass k_blend_step by default) against its roof, from HIP events on the launch
+               stream: the method's flops (or bytes) per launch / time against the fp32 vector
+               peak (or 8 TB/s), with the HBM bytes the counters measured for it
+               (COUNTER_TRAFFIC)
   cpu_baseline the CPU oracle on a bounded sample of the same step (see cpu_baseline())
 """
 from __future__ import annotations
@@ -67,13 +68,20 @@ def alg_bytes(phase, N, R, K, P, T, n_vis):
 #     running colour sums (9), dL/drgb (3), dL/do and dL/dpower (2), dL/du, dL/dv (8),
 #     dL/dA, dL/dB, dL/dC (8), nine accumulations (9)                                 = 54
 FLOPS_EVAL, FLOPS_FWD_BLEND, FLOPS_BWD_BLEND = 16, 10, 54
+# fp32 operations of the L1 + D-SSIM loss per (pixel, channel) value, 11-tap separable windows:
+#   five horizontal window sums (x, y, x^2, y^2, xy: 10 per tap) and five vertical ones (2 per
+#   tap and sum): 110 + 110; SSIM and its three partials: 40; the three partial maps summed
+#   horizontally and vertically: 66 + 66; the combination with x, y and the L1 sign: 8  = 400
+FLOPS_SSIM = 400
 # fp32 vector peak without packed-FP32 dual issue (the build turns packed FP32 off):
 # 256 CUs x 4 SIMDs x 16 lanes x 2 flops per FMA x 2.4 GHz
 ALU_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
 
 
-def alg_flops(phase, examined, walked, composited):
-    """Operations the method performs per launch in the two blend kernels."""
+def alg_flops(phase, examined, walked, composited, ssim_values=0):
+    """Operations the method performs per launch in the two blend kernels (and the D-SSIM loss)."""
+    if phase == "loss":                # only the D-SSIM loss is counted (ssim_values = 3HW)
+        return FLOPS_SSIM * ssim_values
     if phase == "forward":             # walks n_examined entries per pixel
         return FLOPS_EVAL * examined + FLOPS_FWD_BLEND * composited
     if phase == "backward_blend":      # walks last_contrib entries per pixel, back to front
@@ -228,6 +236,9 @@ def main():
     ap.add_argument("--unfused-adam", action="store_true", help="separate Adam kernel instead of the fused one")
     ap.add_argument("--separate-passes", action="store_true",
                     help="forward, L1 loss and backward blend as three calls instead of the fused image pass")
+    ap.add_argument("--dssim", type=float, default=None, metavar="LAMBDA",
+                    help="L1 + D-SSIM loss weighted by LAMBDA instead of L1 (the forward, the loss and the "
+                         "backward blend then run as three calls)")
     ap.add_argument("--detail", default=None, help="write a detailed JSON record to this path")
     ap.add_argument("--views", type=int, default=0,
                     help="use only the first N orbit views (short profiling runs); default all")
@@ -278,7 +289,9 @@ def main():
     gcams = [gsmi.make_camera(c) for c in cams]
     blends = torch.zeros(3, dtype=torch.int64, device="cuda")
     bg = (0.0, 0.0, 0.0)
-    fused = not args.separate_passes
+    fused = not args.separate_passes and args.dssim is None
+    dssim_ws = (torch.empty(gsmi.loss_l1_dssim_workspace(W, H), dtype=torch.uint8, device="cuda")
+                if args.dssim is not None else None)
     phases = (["preprocess", "bin_and_sort", "render_plan", "image_pass", "prebwd_adam"] if fused else
               ["preprocess", "bin_and_sort", "forward", "loss", "backward_blend", "prebwd_adam"])
 
@@ -307,7 +320,10 @@ def main():
             gsmi.render_forward(cam, N, buf.proj.splat, buf.vals, buf.ranges, bg, buf.image, buf.T_final, buf.last,
                                 buf.render_ws, blend_count=blends)
             mark()
-            gsmi.loss_l1(3 * P, buf.image, targets[view], buf.loss, buf.dLdI, buf.loss_ws)
+            if args.dssim is not None:
+                gsmi.loss_l1_dssim(W, H, buf.image, targets[view], args.dssim, buf.loss, buf.dLdI, dssim_ws)
+            else:
+                gsmi.loss_l1(3 * P, buf.image, targets[view], buf.loss, buf.dLdI, buf.loss_ws)
             mark()
             gsmi.render_backward(buf.scene, None, cam, buf.proj, buf.vals, buf.ranges, bg, buf.T_final, buf.last,
                                  buf.dLdI, g2, buf.render_ws)
@@ -371,8 +387,8 @@ def main():
     for ph in phases:
         d = {"ms": round(ph_ms[ph], 4),
              "alg_GBps": round(alg_bytes(ph, N, R, Kmean, P, T, n_vis) / (ph_ms[ph] * 1e-3) / 1e9, 1)}
-        if ph in ("forward", "backward_blend", "image_pass"):
-            d["alg_TFLOPs"] = round(alg_flops(ph, *per_launch) / (ph_ms[ph] * 1e-3) / 1e12, 3)
+        if ph in ("forward", "backward_blend", "image_pass") or (ph == "loss" and args.dssim is not None):
+            d["alg_TFLOPs"] = round(alg_flops(ph, *per_launch, ssim_values=3 * P) / (ph_ms[ph] * 1e-3) / 1e12, 3)
         per_phase[ph] = d
     log(f"[bench] roofline: {json.dumps(roof)}")
     log(f"[bench] per view: {per_launch[0]:.4g} examined, {per_launch[1]:.4g} walked back, "
@@ -397,7 +413,7 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": cfg.name, "gaussians": N, "sh_degree": cfg.sh_degree, "resolution": [W, H],
-                   "views": V, "loss": "l1", "adam": "fused" if not args.unfused_adam else "separate",
+                   "views": V, "loss": "l1" if args.dssim is None else f"l1+dssim(lambda={args.dssim})", "adam": "fused" if not args.unfused_adam else "separate",
                    "image_pass": "fused" if fused else "separate",
                    "intersections_mean": round(Kmean), "intersections_min": int(min(ks)),
                    "intersections_max": int(max(ks))},

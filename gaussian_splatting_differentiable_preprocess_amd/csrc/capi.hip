@@ -233,6 +233,27 @@ int gs_loss_l1(int64_t count, const float* image, const float* target, float* lo
   return e == hipSuccess ? ok() : hip_fail(e, "gs_loss_l1");
 }
 
+int gs_loss_l1_dssim_workspace(int32_t width, int32_t height, size_t* bytes) {
+  if (!bytes) return fail(GS_ERR_INVALID_ARGUMENT, "bytes is null");
+  if (width < 11 || height < 11) return fail(GS_ERR_INVALID_ARGUMENT, "image smaller than the 11x11 SSIM window");
+  *bytes = ssim_workspace_bytes(width, height);
+  return ok();
+}
+
+int gs_loss_l1_dssim(int32_t width, int32_t height, const float* image, const float* target, float lambda,
+                     float* loss, float* dL_dimage, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream) {
+  if (width < 11 || height < 11) return fail(GS_ERR_INVALID_ARGUMENT, "image smaller than the 11x11 SSIM window");
+  if (!(lambda >= 0.f && lambda <= 1.f)) return fail(GS_ERR_INVALID_ARGUMENT, "lambda must be in [0, 1]");
+  if (!image || !target || !loss || !dL_dimage || !workspace)
+    return fail(GS_ERR_INVALID_ARGUMENT, "a required pointer is null");
+  if (workspace_bytes < ssim_workspace_bytes(width, height))
+    return fail(GS_ERR_INVALID_ARGUMENT, "D-SSIM workspace too small");
+  const hipError_t e =
+      launch_loss_l1_dssim(width, height, image, target, lambda, loss, dL_dimage, workspace, stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "gs_loss_l1_dssim");
+}
+
 }  // extern "C"
 
 namespace {

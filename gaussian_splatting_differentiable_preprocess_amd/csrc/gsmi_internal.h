@@ -180,6 +180,11 @@ hipError_t launch_blend_step(const CamK& cam, int64_t n, const gs_splat* splat, 
 hipError_t launch_loss_sum(int64_t count, const float* part, double inv_n, float* loss, hipStream_t s);
 hipError_t launch_loss_l1(int64_t count, const float* image, const float* target, float* loss,
                           float* dLdI, void* ws, hipStream_t s);
+// L1 + D-SSIM loss (ssim.hip): workspace bytes for a W x H image (W, H >= 11), and the launch
+// writing loss[0..2] = (L, mean L1, mean SSIM) and dL/dimage.
+size_t ssim_workspace_bytes(int W, int H);
+hipError_t launch_loss_l1_dssim(int W, int H, const float* image, const float* target, float lambda,
+                                float* loss, float* dLdI, void* ws, hipStream_t s);
 hipError_t launch_adam(int64_t count, float* params, const float* grads, float* m, float* v,
                        const AdamCoef& c, hipStream_t s);
 

@@ -23,7 +23,8 @@ SPLAT_FLOATS = 12  # 48-byte record: u, v, radius_x, radius_y | A, B, C, opacity
 
 EXPORTS = (
     "gs_version", "gs_last_error", "gs_preprocess", "gs_bin_and_sort_workspace", "gs_bin_and_sort",
-    "gs_render_workspace", "gs_render_workspace_capacity", "gs_render_forward", "gs_loss_l1_workspace", "gs_loss_l1", "gs_render_backward",
+    "gs_render_workspace", "gs_render_workspace_capacity", "gs_render_forward", "gs_loss_l1_workspace", "gs_loss_l1",
+    "gs_loss_l1_dssim_workspace", "gs_loss_l1_dssim", "gs_render_backward",
     "gs_render_plan", "gs_render_step", "gs_preprocess_backward", "gs_preprocess_backward_staged", "gs_adam_step",
 )
 
@@ -85,6 +86,8 @@ def load(path: str = LIB_PATH):
     L.gs_render_forward.argtypes = [CP, i64, P, P, P, ctypes.POINTER(ctypes.c_float), P, P, P, P, P, P, sz, P]
     L.gs_loss_l1_workspace.argtypes = [i64, ctypes.POINTER(sz)]
     L.gs_loss_l1.argtypes = [i64, P, P, P, P, P, sz, P]
+    L.gs_loss_l1_dssim_workspace.argtypes = [i32, i32, ctypes.POINTER(sz)]
+    L.gs_loss_l1_dssim.argtypes = [i32, i32, P, P, ctypes.c_float, P, P, P, sz, P]
     L.gs_render_backward.argtypes = [SP, P, CP, GsProj, P, P, ctypes.POINTER(ctypes.c_float), P, P, P,
                                      P, P, AP, P, sz, P]
     L.gs_render_plan.argtypes = [SP, CP, GsProj, P, P, sz, P]
@@ -235,6 +238,18 @@ def loss_l1(count, image, target, loss, dL_dimage, workspace, stream=None):
                              _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
+def loss_l1_dssim_workspace(width, height) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load().gs_loss_l1_dssim_workspace(int(width), int(height), ctypes.byref(out)))
+    return out.value
+
+
+def loss_l1_dssim(width, height, image, target, lam, loss, dL_dimage, workspace, stream=None):
+    """loss: device float[3] <- (L, mean L1, mean SSIM); dL_dimage [H][W][3]."""
+    _check(load().gs_loss_l1_dssim(int(width), int(height), _ptr(image), _ptr(target), float(lam), _ptr(loss),
+                                   _ptr(dL_dimage), _ptr(workspace), _nbytes(workspace), _stream(stream)))
+
+
 def make_adam(m, v, step, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8) -> GsAdam:
     return GsAdam(m.data_ptr(), v.data_ptr(), int(step), float(lr), float(beta1), float(beta2), float(eps))
 
@@ -313,8 +328,9 @@ class StepBuffers:
         self.T_final = torch.empty((height, width), dtype=f32, device=device)
         self.last = torch.empty((height, width), dtype=i32, device=device)
         self.dLdI = torch.empty((height, width, 3), dtype=f32, device=device)
-        self.loss = torch.zeros(1, dtype=f32, device=device)
+        self.loss = torch.zeros(3, dtype=f32, device=device)  # (L, mean L1, mean SSIM) with D-SSIM
         self.loss_ws = torch.empty(loss_l1_workspace(3 * width * height), dtype=torch.uint8, device=device)
+        self.dssim_ws = None  # allocated on the first L1 + D-SSIM step
         self.grad2d = torch.empty((ld, 9), dtype=f32, device=device)
         self.scene = make_scene(n, ld, sh_degree)
 
@@ -329,9 +345,10 @@ class StepBuffers:
 
 
 def train_step(buf: StepBuffers, params, m, v, step, cam: GsCamera, target=None, upstream=None,
-               bg=(0.0, 0.0, 0.0), lr=1e-3, fused_adam=True, grads=None, blend_count=None):
-    """One fwd + bwd + Adam step for one view: preprocess -> bin/sort -> forward -> L1 (or
-    the given upstream dL/dI) -> backward (+ Adam).  Returns K."""
+               bg=(0.0, 0.0, 0.0), lr=1e-3, fused_adam=True, grads=None, blend_count=None, dssim_lambda=None):
+    """One fwd + bwd + Adam step for one view: preprocess -> bin/sort -> forward -> L1, or
+    L1 + D-SSIM weighted by `dssim_lambda`, or the given upstream dL/dI -> backward (+ Adam).
+    Returns K."""
     preprocess(buf.scene, params, cam, buf.proj)
     while True:
         try:
@@ -343,6 +360,13 @@ def train_step(buf: StepBuffers, params, m, v, step, cam: GsCamera, target=None,
                    buf.render_ws, blend_count=blend_count)
     if upstream is not None:
         dLdI = upstream
+    elif dssim_lambda is not None:
+        if buf.dssim_ws is None:
+            import torch
+            buf.dssim_ws = torch.empty(loss_l1_dssim_workspace(buf.W, buf.H), dtype=torch.uint8,
+                                       device=buf.image.device)
+        loss_l1_dssim(buf.W, buf.H, buf.image, target, dssim_lambda, buf.loss, buf.dLdI, buf.dssim_ws)
+        dLdI = buf.dLdI
     else:
         loss_l1(3 * buf.W * buf.H, buf.image, target, buf.loss, buf.dLdI, buf.loss_ws)
         dLdI = buf.dLdI

@@ -7,6 +7,7 @@
  *   gs_bin_and_sort     tile binning, stable (tile, depth) radix sort, per-tile ranges
  *   gs_render_forward   front-to-back alpha compositing per 16x16 tile
  *   gs_loss_l1          L1 image loss and its gradient
+ *   gs_loss_l1_dssim    L1 + lambda-weighted D-SSIM image loss and its gradient
  *   gs_render_backward  reverse-order backward blend + preprocess backward
  *                       (optionally fused with the Adam update)
  *   gs_adam_step        Adam over all parameters (when not fused)
@@ -52,7 +53,7 @@
 extern "C" {
 #endif
 
-#define GSMI_VERSION 4
+#define GSMI_VERSION 5
 #define GS_TILE 16 /* tiles are GS_TILE x GS_TILE pixels */
 
 typedef enum gs_status {
@@ -205,6 +206,32 @@ int gs_loss_l1_workspace(int64_t count, size_t* bytes);
  * lambda-weighted D-SSIM term; this call is the L1 term. */
 int gs_loss_l1(int64_t count, const float* image, const float* target, float* loss,
                float* dL_dimage, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of device workspace gs_loss_l1_dssim needs for a width x height image (host-only
+ * query): 36 bytes per SSIM window position plus per-workgroup sums, about 36 W H.
+ * GS_ERR_INVALID_ARGUMENT if width or height is below 11 or bytes is null. */
+int gs_loss_l1_dssim_workspace(int32_t width, int32_t height, size_t* bytes);
+
+/* L1 + D-SSIM loss ("Scaling 3D Gaussian Splatting with Distributed Compute", the loss passage:
+ * an L1 term and a D-SSIM term weighted by lambda; step "Compute the loss locally": L1 and a
+ * fused SSIM).  The pages give no window or constants; this call takes SSIM with an 11x11
+ * Gaussian window of standard deviation 1.5 (normalised to sum 1), C1 = 0.01^2, C2 = 0.03^2
+ * (images in [0, 1]), per colour channel over the (W - 10)(H - 10) window positions wholly
+ * inside the image, and
+ *     L = (1 - lambda) mean |image - target| + lambda (1 - mean SSIM).
+ *   image, target[H][W][3]  device, float32, interleaved RGB rows (as gs_render_forward writes)
+ *   lambda                  in [0, 1] (0.2 is the usual weight)
+ *   loss                    out: device float[3] = (L, mean |image - target|, mean SSIM)
+ *   dL_dimage[H][W][3]      out: dL/dimage, the exact derivative of L (sign(0) = 0 in the L1
+ *                           term); may be passed to gs_render_backward
+ *   workspace               device, >= gs_loss_l1_dssim_workspace bytes; its contents on entry
+ *                           are ignored and it must not be shared by calls in flight together
+ * Sums run per workgroup in float32 and across workgroups in double, in a fixed order: the
+ * result is deterministic.  GS_ERR_INVALID_ARGUMENT for width or height below 11, lambda
+ * outside [0, 1] or not finite, a null pointer or a short workspace. */
+int gs_loss_l1_dssim(int32_t width, int32_t height, const float* image, const float* target, float lambda,
+                     float* loss, float* dL_dimage, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream);
 
 /* Backward of the step from dL/dimage.
  *   grad2d[ld][9]  out, nullable: per-Gaussian dL/d(u, v, conic_a, conic_b, conic_c, opacity,

@@ -275,10 +275,11 @@ def n_tiles(W, H):
 
 
 def train_step_reference(params, sh_degree, cam_flat, W, H, target=None, upstream=None,
-                         m=None, v=None, t=1, lr=1e-3, bg=(0.0, 0.0, 0.0)):
+                         m=None, v=None, t=1, lr=1e-3, bg=(0.0, 0.0, 0.0), dssim_lambda=None):
     """The whole step in the oracle: preprocess -> bin/sort -> ranges -> forward -> loss
-    (L1 against `target`, or the given upstream dL/dI) -> backward -> preprocess backward
-    -> Adam.  Returns a dict with every intermediate."""
+    (L1 against `target`, L1 + D-SSIM when `dssim_lambda` is given, or the given upstream
+    dL/dI) -> backward -> preprocess backward -> Adam.  Returns a dict with every
+    intermediate."""
     proj, radii, tiles = preprocess(params, sh_degree, cam_flat, W, H)
     keys, vals = bin_sort(proj, radii, W, H)
     rg = ranges(keys, n_tiles(W, H))
@@ -286,6 +287,8 @@ def train_step_reference(params, sh_degree, cam_flat, W, H, target=None, upstrea
     if upstream is not None:
         dLdI = _f64(upstream)
         loss = float((dLdI * fwd["image"]).sum())
+    elif dssim_lambda is not None:
+        loss, _, _, dLdI = loss_l1_dssim(fwd["image"], target, dssim_lambda)
     else:
         loss, dLdI = loss_l1(fwd["image"], target)
     g2 = render_backward(proj, vals, rg, W, H, dLdI, bg)

@@ -22,7 +22,7 @@ def test_library_exports_every_declared_symbol():
     assert len(names) == len(gsmi.EXPORTS) and set(names) == set(gsmi.EXPORTS)
     for name in names:
         assert hasattr(L, name), name
-    assert gsmi.version() == 4
+    assert gsmi.version() == 5
 
 
 def test_invalid_arguments_rejected_before_any_gpu_call():
@@ -101,6 +101,31 @@ def test_workspace_queries():
                 assert k <= got < k + 512, (W, H, n, k, got)
     with pytest.raises(gsmi.GsError):
         gsmi.render_workspace_capacity(64, 64, 10, 100)
+
+
+def test_loss_l1_dssim_checks_its_arguments():
+    L = gsmi.load()
+    need = gsmi.loss_l1_dssim_workspace(2048, 2048)
+    # nine float32 partials per window position plus the per-workgroup sums
+    assert 36 * 2038 * 2038 <= need < 36 * 2038 * 2038 + 64 * 1024
+    assert gsmi.loss_l1_dssim_workspace(11, 11) >= 36
+    for W, H in ((10, 64), (64, 10), (0, 0)):
+        with pytest.raises(gsmi.GsError):
+            gsmi.loss_l1_dssim_workspace(W, H)
+    P = ctypes.c_void_p(256)
+    f = ctypes.c_float
+    ws = gsmi.loss_l1_dssim_workspace(64, 64)
+    assert L.gs_loss_l1_dssim(64, 10, P, P, f(0.2), P, P, P, ws, None) == -1 and "window" in gsmi.last_error()
+    for lam in (-0.1, 1.5, float("nan"), float("inf")):
+        assert L.gs_loss_l1_dssim(64, 64, P, P, f(lam), P, P, P, ws, None) == -1
+        assert "lambda" in gsmi.last_error()
+    for k in range(5):
+        args = [P, P, P, P, P]
+        args[k] = None
+        assert L.gs_loss_l1_dssim(64, 64, args[0], args[1], f(0.2), args[2], args[3], args[4], ws, None) == -1
+        assert "null" in gsmi.last_error()
+    assert L.gs_loss_l1_dssim(64, 64, P, P, f(0.2), P, P, P, ws - 1, None) == -1
+    assert "workspace" in gsmi.last_error()
 
 
 def test_render_calls_reject_a_missing_or_short_workspace():
