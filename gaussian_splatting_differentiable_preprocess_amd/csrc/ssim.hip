@@ -25,6 +25,8 @@
 //   k_ssim_grad    the same shape over the partials: horizontal then vertical window sums of
 //                  the three partial maps (zero outside the positions), combined with x and y
 //                  into dL/dx, plus the L1 sum.
+// Both fetch each row two steps before they stage it in LDS, so the loads of the next rows
+// overlap the window sums of the current one (one barrier per row, two LDS buffers).
 // A final one-workgroup kernel sums the per-workgroup partial sums in double.
 #include "gsmi_internal.h"
 
@@ -60,12 +62,48 @@ __global__ __launch_bounds__(kSsimThreads) void k_ssim_stats(int W, int H, const
   const int col = c0 + j;                                 // window position column
   const int nrows = min(kRows + kHalf, H - r0);           // input rows this workgroup reads
   const int span = min(kSpan, W - c0);                    // staged pixel columns
+  // Each thread stages the same two of a row's 3 x 266 interleaved values at every row:
+  // element e -> pixel column e / 3, channel e % 3 (zero past the image's right edge).
+  const int e0 = threadIdx.x, e1 = threadIdx.x + kSsimThreads;
+  const int pc0 = e0 / 3, pch0 = e0 - 3 * pc0, pc1 = e1 / 3, pch1 = e1 - 3 * pc1;
+  const bool ok0 = pc0 < span, ok1 = pc1 < span, has1 = e1 < 3 * kSpan;
+  const float* __restrict__ img_b = img + (int64_t)c0 * 3;
+  const float* __restrict__ tgt_b = tgt + (int64_t)c0 * 3;
+  // rows are fetched two steps ahead of their use, so the loads overlap the window sums
+  auto fetch = [&](int i, float4& f) {
+    f = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (i < nrows) {
+      const int64_t off = (int64_t)(r0 + i) * W * 3;
+      if (ok0) {
+        f.x = img_b[off + e0];
+        f.y = tgt_b[off + e0];
+      }
+      if (ok1) {
+        f.z = img_b[off + e1];
+        f.w = tgt_b[off + e1];
+      }
+    }
+  };
+  auto stage = [&](int buf, const float4& f) {
+    sx[buf][pch0][pc0] = f.x;
+    sy[buf][pch0][pc0] = f.y;
+    if (has1) {
+      sx[buf][pch1][pc1] = f.z;
+      sy[buf][pch1][pc1] = f.w;
+    }
+  };
   float ring[kWin][5];
 #pragma unroll
   for (int a = 0; a < kWin; ++a)
 #pragma unroll
     for (int q = 0; q < 5; ++q) ring[a][q] = 0.f;
   float acc = 0.f;
+  float4 fa, fb;  // rows i + 1 and i + 2
+  fetch(0, fa);
+  stage(0, fa);
+  fetch(1, fa);
+  fetch(2, fb);
+  __syncthreads();
 
   for (int base = 0; base < nrows; base += kWin) {
 #pragma unroll
@@ -73,18 +111,6 @@ __global__ __launch_bounds__(kSsimThreads) void k_ssim_stats(int W, int H, const
       const int i = base + s;
       if (i < nrows) {  // uniform over the workgroup
         const int buf = i & 1;
-        const int64_t rowoff = ((int64_t)(r0 + i) * W + c0) * 3;
-        for (int e = threadIdx.x; e < 3 * kSpan; e += kSsimThreads) {
-          const int pc = e / 3, pch = e - 3 * pc;
-          float xv = 0.f, yv = 0.f;
-          if (pc < span) {
-            xv = img[rowoff + e];
-            yv = tgt[rowoff + e];
-          }
-          sx[buf][pch][pc] = xv;
-          sy[buf][pch][pc] = yv;
-        }
-        __syncthreads();
         float h0 = 0.f, h1 = 0.f, h2 = 0.f, h3 = 0.f, h4 = 0.f;
 #pragma unroll
         for (int b = 0; b < kWin; ++b) {
@@ -127,6 +153,11 @@ __global__ __launch_bounds__(kSsimThreads) void k_ssim_stats(int W, int H, const
             dmap[6 * nv + o] = 2.f * S / B;
           }
         }
+        // row i + 1 into the other buffer (last read at step i - 1, before that step's barrier)
+        stage(buf ^ 1, fa);
+        fa = fb;
+        fetch(i + 3, fb);
+        __syncthreads();
       }
     }
   }
@@ -152,12 +183,65 @@ __global__ __launch_bounds__(kSsimThreads) void k_ssim_grad(int W, int H, const 
   const int ch = threadIdx.x / kCols, j = threadIdx.x % kCols;
   const int qc = c0 + j;                           // pixel column
   const int nrows = min(kRows, H - r0) + kHalf;    // partial-map rows r0 - 10 .. r0 + rows - 1
+  // Each thread stages the same four of a row's 9 x 266 partials at every row: element
+  // e -> map row e / 266 (map * 3 + channel), staged column e % 266 = position column
+  // c0 - 10 + e % 266 (zero outside the positions).
+  int64_t moff[4];
+  int mrow[4], mcol[4];
+  bool mok[4], mhas[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = threadIdx.x + q * kSsimThreads;
+    mhas[q] = e < 9 * kSpan;
+    mrow[q] = e / kSpan;
+    mcol[q] = e - mrow[q] * kSpan;
+    const int pc = c0 - kHalf + mcol[q];
+    mok[q] = mhas[q] && pc >= 0 && pc < Wv;
+    const int m = mrow[q] / 3, c = mrow[q] - 3 * m;
+    moff[q] = mok[q] ? (int64_t)m * 3 * nv + (int64_t)c * nv + pc : 0;
+  }
+  // step i stages position row r0 - 10 + i and outputs pixel row r0 + i - 10 (i >= 10); both
+  // are fetched two steps ahead of their use, so the loads overlap the window sums
+  struct Pf {
+    float v[4];
+    float x, y;
+  };
+  auto fetch = [&](int i, Pf& f) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) f.v[q] = 0.f;
+    f.x = f.y = 0.f;
+    if (i < nrows) {
+      const int pr = r0 - kHalf + i;
+      if (pr >= 0 && pr < Hv) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (mok[q]) f.v[q] = dmap[moff[q] + (int64_t)pr * Wv];
+      }
+      if (i >= kHalf && qc < W) {
+        const int64_t e = ((int64_t)(r0 + i - kHalf) * W + qc) * 3 + ch;
+        f.x = img[e];
+        f.y = tgt[e];
+      }
+    }
+  };
+  auto stage = [&](int buf, const Pf& f) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (mhas[q]) sd[buf][mrow[q]][mcol[q]] = f.v[q];
+  };
   float ring[kWin][3];
 #pragma unroll
   for (int a = 0; a < kWin; ++a)
 #pragma unroll
     for (int q = 0; q < 3; ++q) ring[a][q] = 0.f;
   float acc = 0.f;
+  Pf fa, fb;  // steps i + 1 and i + 2
+  fetch(0, fa);
+  stage(0, fa);
+  float xc = fa.x, yc = fa.y;  // step i's pixel
+  fetch(1, fa);
+  fetch(2, fb);
+  __syncthreads();
 
   for (int base = 0; base < nrows; base += kWin) {
 #pragma unroll
@@ -165,19 +249,6 @@ __global__ __launch_bounds__(kSsimThreads) void k_ssim_grad(int W, int H, const 
       const int i = base + s;
       if (i < nrows) {  // uniform over the workgroup
         const int buf = i & 1;
-        const int pr = r0 - kHalf + i;  // window position row staged at this step
-        const bool row_ok = pr >= 0 && pr < Hv;
-        for (int e = threadIdx.x; e < 9 * kSpan; e += kSsimThreads) {
-          const int mc = e / kSpan, lc = e - mc * kSpan;
-          const int pc = c0 - kHalf + lc;
-          float v = 0.f;
-          if (row_ok && pc >= 0 && pc < Wv) {
-            const int m = mc / 3, c = mc - 3 * m;
-            v = dmap[(int64_t)m * 3 * nv + (int64_t)c * nv + (int64_t)pr * Wv + pc];
-          }
-          sd[buf][mc][lc] = v;
-        }
-        __syncthreads();
         float h0 = 0.f, h1 = 0.f, h2 = 0.f;
 #pragma unroll
         for (int b = 0; b < kWin; ++b) {
@@ -204,14 +275,20 @@ __global__ __launch_bounds__(kSsimThreads) void k_ssim_grad(int W, int H, const 
           const int qr = r0 + i - kHalf;
           if (qc < W) {
             const int64_t e = ((int64_t)qr * W + qc) * 3 + ch;
-            const float x = img[e], y = tgt[e];
-            const float d = x - y;
+            const float d = xc - yc;
             acc += fabsf(d);
-            const float dS = gm + 2.f * x * gxx + y * gxy;
+            const float dS = gm + 2.f * xc * gxx + yc * gxy;
             const float sg = d > 0.f ? k.l1_scale : (d < 0.f ? -k.l1_scale : 0.f);
             dLdI[e] = sg - k.s_scale * dS;
           }
         }
+        // step i + 1's row into the other buffer (last read at step i - 1, before its barrier)
+        stage(buf ^ 1, fa);
+        xc = fa.x;
+        yc = fa.y;
+        fa = fb;
+        fetch(i + 3, fb);
+        __syncthreads();
       }
     }
   }
