@@ -14,6 +14,7 @@ pinned by the pages, which print no rendered values.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 import subprocess
 
@@ -298,3 +299,29 @@ def train_step_reference(params, sh_degree, cam_flat, W, H, target=None, upstrea
     if m is not None:
         out["params_new"], out["m_new"], out["v_new"] = adam(params, grads, m, v, t, lr)
     return out
+
+
+def adam_batch_hparams(lr, beta1, beta2, eps, batch):
+    """Adam's hyper-parameters for `batch` views per optimizer step ("Scaling 3D Gaussian
+    Splatting with Distributed Compute", the batch-size passage): the learning rate scales as
+    sqrt(BS), epsilon as 1/sqrt(BS), and each momentum coefficient is decayed linearly,
+    beta <- 1 - BS (1 - beta), which takes beta1 = 0.9 to zero at BS = 10 as the page says.
+    Returns (lr, beta1, beta2, eps)."""
+    s = math.sqrt(batch)
+    return lr * s, 1.0 - batch * (1.0 - beta1), 1.0 - batch * (1.0 - beta2), eps / s
+
+
+def train_batch_reference(params, sh_degree, cam_flats, W, H, targets, m, v, t, lr=1e-3, beta1=0.9,
+                          beta2=0.999, eps=1e-8, bg=(0.0, 0.0, 0.0), dssim_lambda=None):
+    """One optimizer step over a batch of views (the batch-size passage of the same page): the
+    loss is the mean of the views' losses, so the gradient is the mean of their gradients, and
+    one Adam step with the batch-scaled hyper-parameters follows.  Returns (params_new, m_new,
+    v_new, grads)."""
+    grads = None
+    for c, tgt in zip(cam_flats, targets):
+        g = train_step_reference(params, sh_degree, c, W, H, target=tgt, bg=bg, dssim_lambda=dssim_lambda)["grads"]
+        grads = g if grads is None else grads + g
+    grads = grads / len(cam_flats)
+    lr_b, b1_b, b2_b, eps_b = adam_batch_hparams(lr, beta1, beta2, eps, len(cam_flats))
+    p_new, m_new, v_new = adam(params, grads, m, v, t, lr_b, b1_b, b2_b, eps_b)
+    return p_new, m_new, v_new, grads
