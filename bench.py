@@ -41,8 +41,10 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def alg_bytes(phase, N, R, K, P, T, n_vis):
-    """Bytes the method itself must move per launch (reads + writes), by phase."""
+def alg_bytes(phase, N, R, K, P, T, n_vis, batch=1):
+    """Bytes the method itself must move per launch (reads + writes), by phase; with batch > 1
+    the preprocess backward's mean over the batch's views (the first writes the accumulator, the
+    middle ones read and write it, the last reads it and runs Adam)."""
     if phase == "preprocess":          # params in; 48-B record + tiles + depth key + tile rect out
         return N * (4 * R + 64)
     if phase == "forward":             # per entry: index + 36 B of record; per pixel: RGB, T, last
@@ -52,6 +54,8 @@ def alg_bytes(phase, N, R, K, P, T, n_vis):
     if phase == "backward_blend":      # entries + pixels (dL/dI, T, last) + one 2D gradient per Gaussian out
         return K * 40 + P * 20 + T * 8 + 36 * n_vis
     if phase == "prebwd_adam":         # params, m, v, one 2D gradient per Gaussian in; params, m, v out
+        if batch > 1:
+            return N * ((8 * R + (batch - 2) * 12 * R + 28 * R) / batch + 36)
         return N * (24 * R + 36)
     if phase == "image_pass":          # the fused forward + L1 + backward blend
         return sum(alg_bytes(ph, N, R, K, P, T, n_vis) for ph in ("forward", "loss", "backward_blend"))
@@ -98,9 +102,10 @@ def alg_flops(phase, examined, walked, composited, ssim_values=0):
 KERNEL_OF = {"preprocess": ("k_preprocess<3>", "hbm"), "image_pass": ("k_blend_step", "alu"),
              "prebwd_adam": ("k_preprocess_backward<3>", "hbm")}
 
-# HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE passes over this workload,
-# each scaled by the factor the same counter reads for a plain copy of known size; keyed by
-# the SHA-256 of the kernel's source file, so a changed kernel reports null
+# HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE passes over the workload named
+# (gyroid_4m_2048), each scaled by the factor the same counter reads for a plain copy of known
+# size; keyed by the SHA-256 of the kernel's source file, so a changed kernel (or another
+# workload) reports null
 COUNTER_TRAFFIC = {
     "preprocess": {"source": "preprocess.hip", "bytes": 1200081815,
                    "sha256": "b65eac29a7e37f262ed39af1cfcbf9a9d1656e0873ea93e7e89e8f5ee9b2d2c6"},
@@ -111,9 +116,12 @@ COUNTER_TRAFFIC = {
 }
 
 
-def counter_traffic(phase):
+COUNTER_WORKLOAD = "gyroid_4m_2048"
+
+
+def counter_traffic(phase, workload):
     rec = COUNTER_TRAFFIC.get(phase)
-    if rec is None:
+    if rec is None or workload != COUNTER_WORKLOAD:
         return None
     src = os.path.join(ROOT, "gaussian_splatting_differentiable_preprocess_amd", "csrc", rec["source"])
     import hashlib
@@ -239,6 +247,10 @@ def main():
     ap.add_argument("--dssim", type=float, default=None, metavar="LAMBDA",
                     help="L1 + D-SSIM loss weighted by LAMBDA instead of L1 (the forward, the loss and the "
                          "backward blend then run as three calls)")
+    ap.add_argument("--batch", type=int, default=1, metavar="BS",
+                    help="views per optimizer step: each view's preprocess backward adds 1/BS of its gradient "
+                         "to an accumulator and every BS-th view's runs Adam with the batch-scaled "
+                         "hyper-parameters (a timed step is still one view)")
     ap.add_argument("--detail", default=None, help="write a detailed JSON record to this path")
     ap.add_argument("--views", type=int, default=0,
                     help="use only the first N orbit views (short profiling runs); default all")
@@ -286,6 +298,9 @@ def main():
     kcap = int(1.5 * max(tks)) + 4096
     buf = gsmi.StepBuffers(N, N, cfg.sh_degree, W, H, k_capacity=kcap)
     grads = torch.empty_like(p) if args.unfused_adam else None
+    if args.batch > 1 and args.unfused_adam:
+        raise SystemExit("--batch accumulates in the fused preprocess backward; drop --unfused-adam")
+    grads_acc = torch.empty_like(p) if args.batch > 1 else None
     gcams = [gsmi.make_camera(c) for c in cams]
     blends = torch.zeros(3, dtype=torch.int64, device="cuda")
     bg = (0.0, 0.0, 0.0)
@@ -328,6 +343,14 @@ def main():
             gsmi.render_backward(buf.scene, None, cam, buf.proj, buf.vals, buf.ranges, bg, buf.T_final, buf.last,
                                  buf.dLdI, g2, buf.render_ws)
             mark()
+        if args.batch > 1:  # t counts views; the optimizer steps once per batch
+            j = (t - 1) % args.batch
+            adam = (gsmi.adam_batch(gsmi.make_adam(m, v, (t - 1) // args.batch + 1, 1e-3), args.batch)
+                    if j == args.batch - 1 else None)
+            gsmi.preprocess_backward_accumulate(buf.scene, p, cam, buf.proj, buf.render_ws, grads_acc, j == 0,
+                                                1.0 / args.batch, adam)
+            mark()
+            return K
         adam = gsmi.make_adam(m, v, t, 1e-3)
         if args.unfused_adam:
             gsmi.preprocess_backward(buf.scene, p, cam, buf.grad2d, grads)
@@ -377,16 +400,16 @@ def main():
         roof = {"bound": "alu", "achieved": round(achieved, 2), "peak": round(ALU_PEAK_TFLOPS, 1),
                 "unit": "TFLOP/s", "frac": round(achieved / ALU_PEAK_TFLOPS, 4)}
     else:
-        work = alg_bytes(dom, N, R, Kmean, P, T, n_vis)
+        work = alg_bytes(dom, N, R, Kmean, P, T, n_vis, args.batch)
         achieved = work / sec / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    roof.update({"traffic": counter_traffic(dom), "kernel": kname, "work_per_launch": work,
+    roof.update({"traffic": counter_traffic(dom, cfg.name), "kernel": kname, "work_per_launch": work,
                  "ms_per_launch": round(ph_ms[dom], 4)})
     per_phase = {}
     for ph in phases:
         d = {"ms": round(ph_ms[ph], 4),
-             "alg_GBps": round(alg_bytes(ph, N, R, Kmean, P, T, n_vis) / (ph_ms[ph] * 1e-3) / 1e9, 1)}
+             "alg_GBps": round(alg_bytes(ph, N, R, Kmean, P, T, n_vis, args.batch) / (ph_ms[ph] * 1e-3) / 1e9, 1)}
         if ph in ("forward", "backward_blend", "image_pass") or (ph == "loss" and args.dssim is not None):
             d["alg_TFLOPs"] = round(alg_flops(ph, *per_launch, ssim_values=3 * P) / (ph_ms[ph] * 1e-3) / 1e12, 3)
         per_phase[ph] = d
@@ -413,7 +436,7 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": cfg.name, "gaussians": N, "sh_degree": cfg.sh_degree, "resolution": [W, H],
-                   "views": V, "loss": "l1" if args.dssim is None else f"l1+dssim(lambda={args.dssim})", "adam": "fused" if not args.unfused_adam else "separate",
+                   "views": V, "loss": "l1" if args.dssim is None else f"l1+dssim(lambda={args.dssim})", "adam": "fused" if not args.unfused_adam else "separate", "batch": args.batch,
                    "image_pass": "fused" if fused else "separate",
                    "intersections_mean": round(Kmean), "intersections_min": int(min(ks)),
                    "intersections_max": int(max(ks))},

@@ -260,8 +260,11 @@ namespace {
 // The preprocess backward from grad2d, or (grad2d null) from the sums staged in ws.
 int run_preprocess_backward(const gs_scene* scene, float* params, const gs_camera* cam, const float* grad2d,
                             const gsmi::RenderWs* ws, const uint32_t* tiles, float* grads, const gs_adam* adam,
-                            hipStream_t stream, const char* who) {
+                            hipStream_t stream, const char* who, const float* gacc = nullptr,
+                            float gscale = 1.0f) {
   PrebwdArgs a{};
+  a.gacc = gacc;
+  a.gscale = gscale;
   a.n = scene->n;
   a.ld = scene->ld;
   a.deg = scene->sh_degree;
@@ -320,6 +323,43 @@ int gs_preprocess_backward_staged(const gs_scene* scene, float* params, const gs
     return fail(GS_ERR_INVALID_ARGUMENT, "render workspace too small or not 256-byte aligned");
   return run_preprocess_backward(scene, params, cam, nullptr, &ws, proj.tiles, grads, adam, stream,
                                  "gs_preprocess_backward_staged");
+}
+
+int gs_preprocess_backward_accumulate(const gs_scene* scene, float* params, const gs_camera* cam, gs_proj proj,
+                                      const void* render_ws, size_t render_ws_bytes, float* grads_acc,
+                                      int32_t first, float scale, const gs_adam* adam, hipStream_t stream) {
+  int st;
+  if ((st = check_scene(scene)) || (st = check_camera(cam)) || (st = check_adam(adam))) return st;
+  if (!std::isfinite(scale)) return fail(GS_ERR_INVALID_ARGUMENT, "scale not finite");
+  if (first != 0 && first != 1) return fail(GS_ERR_INVALID_ARGUMENT, "first must be 0 or 1");
+  if (scene->n > 0 && !params) return fail(GS_ERR_INVALID_ARGUMENT, "params is null");
+  if (scene->n > 0 && !proj.tiles) return fail(GS_ERR_INVALID_ARGUMENT, "proj.tiles is null");
+  if (scene->n > 0 && !grads_acc && !(first && adam))
+    return fail(GS_ERR_INVALID_ARGUMENT, "grads_acc is null");
+  RenderWs ws;
+  if (!render_ws || !render_ws_layout(const_cast<void*>(render_ws), render_ws_bytes, (int)n_tiles(*cam), scene->n, &ws))
+    return fail(GS_ERR_INVALID_ARGUMENT, "render workspace too small or not 256-byte aligned");
+  // not first: add to the accumulated rows; with adam the total goes through Adam and the
+  // accumulator is left as it was
+  return run_preprocess_backward(scene, params, cam, nullptr, &ws, proj.tiles, adam ? nullptr : grads_acc, adam,
+                                 stream, "gs_preprocess_backward_accumulate", first ? nullptr : grads_acc, scale);
+}
+
+int gs_adam_batch(const gs_adam* adam, int32_t batch, gs_adam* out) {
+  if (!adam || !out) return fail(GS_ERR_INVALID_ARGUMENT, "adam / out is null");
+  if (batch < 1) return fail(GS_ERR_INVALID_ARGUMENT, "batch must be >= 1");
+  gs_adam r = *adam;
+  const double s = std::sqrt((double)batch);
+  r.lr = adam->lr * s;
+  r.eps = adam->eps / s;
+  r.beta1 = 1.0 - (double)batch * (1.0 - adam->beta1);
+  r.beta2 = 1.0 - (double)batch * (1.0 - adam->beta2);
+  if (!(r.beta1 >= 0.0 && r.beta2 >= 0.0))
+    return fail(GS_ERR_INVALID_ARGUMENT, "batch %d takes a momentum coefficient below zero", batch);
+  int st;
+  if ((st = check_adam(&r))) return st;
+  *out = r;
+  return ok();
 }
 
 int gs_render_backward(const gs_scene* scene, float* params, const gs_camera* cam, gs_proj proj,

@@ -60,6 +60,10 @@ struct PrebwdArgs {
   const uint32_t* goff_blk;
   const uint32_t* tiles;
   uint64_t staging_cap;
+  // Batched steps: the row's gradient is gscale * (this view's) + gacc[row] when gacc is
+  // non-null (gacc may be grads: each element is read before it is written, by one thread)
+  const float* gacc;
+  float gscale;
   float* grads;      // nullable when adam
   float* m;          // nullable: no Adam
   float* v;

@@ -271,7 +271,8 @@ __global__ __launch_bounds__(kBlock) void k_preprocess(int64_t n, int64_t ld,
 }
 
 // Backward through the per-Gaussian forward, optionally followed by the Adam update of every
-// parameter row of this Gaussian (m, v non-null).
+// parameter row of this Gaussian (m, v non-null).  For batched steps each row's gradient is
+// scaled (the batch mean) and added to the gradient accumulated over the batch's earlier views.
 template <int DEG>
 __global__ __launch_bounds__(kBlock) void k_preprocess_backward(PrebwdArgs A, CamK c) {
   constexpr int NB = (DEG + 1) * (DEG + 1);
@@ -283,8 +284,10 @@ __global__ __launch_bounds__(kBlock) void k_preprocess_backward(PrebwdArgs A, Ca
   // Row r's gradient goes to grads and/or through Adam as soon as it is known.  Parameters,
   // moments and the updated parameters stream through once: non-temporal loads and stores
   // (measured 8% faster than cached ones).
-  auto finish_row = [&](int r, float gr_, float th) {
+  auto finish_row = [&](int r, float gv, float th) {
     const int64_t e = (int64_t)r * ld + i;
+    float gr_ = A.gscale * gv;
+    if (A.gacc) gr_ += A.gacc[e];
     if (A.grads) A.grads[e] = gr_;
     if (adam) {
       const float m = A.b1 * __builtin_nontemporal_load(A.m + e) + A.omb1 * gr_;

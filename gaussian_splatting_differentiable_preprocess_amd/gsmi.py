@@ -26,6 +26,7 @@ EXPORTS = (
     "gs_render_workspace", "gs_render_workspace_capacity", "gs_render_forward", "gs_loss_l1_workspace", "gs_loss_l1",
     "gs_loss_l1_dssim_workspace", "gs_loss_l1_dssim", "gs_render_backward",
     "gs_render_plan", "gs_render_step", "gs_preprocess_backward", "gs_preprocess_backward_staged", "gs_adam_step",
+    "gs_preprocess_backward_accumulate", "gs_adam_batch",
 )
 
 
@@ -96,6 +97,8 @@ def load(path: str = LIB_PATH):
     L.gs_preprocess_backward.argtypes = [SP, P, CP, P, P, AP, P]
     L.gs_preprocess_backward_staged.argtypes = [SP, P, CP, GsProj, P, sz, P, AP, P]
     L.gs_adam_step.argtypes = [i64, P, P, AP, P]
+    L.gs_preprocess_backward_accumulate.argtypes = [SP, P, CP, GsProj, P, sz, P, i32, ctypes.c_float, AP, P]
+    L.gs_adam_batch.argtypes = [AP, i32, AP]
     for name in EXPORTS:
         if name not in ("gs_version", "gs_last_error"):
             getattr(L, name).restype = ctypes.c_int
@@ -298,6 +301,20 @@ def preprocess_backward_staged(scene: GsScene, params, cam: GsCamera, proj: Proj
                                                 _stream(stream)))
 
 
+def preprocess_backward_accumulate(scene: GsScene, params, cam: GsCamera, proj: Proj, render_ws, grads_acc, first,
+                                   scale, adam: GsAdam | None = None, stream=None):
+    _check(load().gs_preprocess_backward_accumulate(
+        ctypes.byref(scene), _ptr(params), ctypes.byref(cam), proj.c(), _ptr(render_ws), _nbytes(render_ws),
+        _ptr(grads_acc), int(bool(first)), float(scale), ctypes.byref(adam) if adam is not None else None,
+        _stream(stream)))
+
+
+def adam_batch(adam: GsAdam, batch) -> GsAdam:
+    out = GsAdam()
+    _check(load().gs_adam_batch(ctypes.byref(adam), int(batch), ctypes.byref(out)))
+    return out
+
+
 def adam_step(count, params, grads, adam: GsAdam, stream=None):
     _check(load().gs_adam_step(int(count), _ptr(params), _ptr(grads), ctypes.byref(adam), _stream(stream)))
 
@@ -379,3 +396,44 @@ def train_step(buf: StepBuffers, params, m, v, step, cam: GsCamera, target=None,
                         buf.grad2d, buf.render_ws, grads)
         adam_step(buf.R * buf.ld, params, grads, adam)
     return K
+
+
+def train_batch(buf: StepBuffers, params, m, v, step, cams, targets, grads_acc, bg=(0.0, 0.0, 0.0), lr=1e-3,
+                beta1=0.9, beta2=0.999, eps=1e-8, dssim_lambda=None, blend_count=None):
+    """One optimizer step over a batch of views ("Scaling 3D Gaussian Splatting with Distributed
+    Compute", the batch-size passage): per view preprocess -> bin/sort -> image pass (the fused
+    forward + L1 + backward, or forward, L1 + D-SSIM and backward as three calls) -> preprocess
+    backward adding 1/BS of the view's gradient into grads_acc; the last view's backward runs the
+    Adam update on the batch mean with gs_adam_batch's hyper-parameters.  `step` counts
+    optimizer steps (batches).  Returns the views' intersection counts."""
+    B = len(cams)
+    if B < 1 or len(targets) != B:
+        raise ValueError("one target per camera, at least one camera")
+    adam = adam_batch(make_adam(m, v, step, lr, beta1, beta2, eps), B)
+    ks = []
+    for j, (cam, tgt) in enumerate(zip(cams, targets)):
+        preprocess(buf.scene, params, cam, buf.proj)
+        while True:
+            try:
+                K = bin_and_sort(buf.scene, cam, buf.proj, buf.ws, buf.k_capacity, buf.vals, buf.ranges)
+                break
+            except GsCapacityError as e:
+                buf.grow(int(e.required * 1.25) + 1024)
+        if dssim_lambda is None:
+            render_plan(buf.scene, cam, buf.proj, buf.ranges, buf.render_ws)
+            render_step(buf.scene, cam, buf.proj, buf.vals, buf.ranges, bg, tgt, buf.image, buf.T_final, buf.last,
+                        buf.loss, buf.dLdI, buf.render_ws, blend_count=blend_count)
+        else:
+            if buf.dssim_ws is None:
+                import torch
+                buf.dssim_ws = torch.empty(loss_l1_dssim_workspace(buf.W, buf.H), dtype=torch.uint8,
+                                           device=buf.image.device)
+            render_forward(cam, buf.n, buf.proj.splat, buf.vals, buf.ranges, bg, buf.image, buf.T_final, buf.last,
+                           buf.render_ws, blend_count=blend_count)
+            loss_l1_dssim(buf.W, buf.H, buf.image, tgt, dssim_lambda, buf.loss, buf.dLdI, buf.dssim_ws)
+            render_backward(buf.scene, None, cam, buf.proj, buf.vals, buf.ranges, bg, buf.T_final, buf.last,
+                            buf.dLdI, None, buf.render_ws)
+        preprocess_backward_accumulate(buf.scene, params, cam, buf.proj, buf.render_ws, grads_acc, j == 0, 1.0 / B,
+                                       adam if j == B - 1 else None)
+        ks.append(K)
+    return ks

@@ -11,6 +11,8 @@
  *   gs_render_backward  reverse-order backward blend + preprocess backward
  *                       (optionally fused with the Adam update)
  *   gs_adam_step        Adam over all parameters (when not fused)
+ * and, for batched steps (several views per optimizer step), gs_preprocess_backward_accumulate
+ * with gs_adam_batch.
  *
  * The pages this follows name these stages but print no formulas:
  *   "Scaling 3D Gaussian Splatting with Distributed Compute: Why One GPU Is Never Enough"
@@ -53,7 +55,7 @@
 extern "C" {
 #endif
 
-#define GSMI_VERSION 5
+#define GSMI_VERSION 6
 #define GS_TILE 16 /* tiles are GS_TILE x GS_TILE pixels */
 
 typedef enum gs_status {
@@ -309,6 +311,31 @@ int gs_preprocess_backward(const gs_scene* scene, float* params, const gs_camera
 int gs_preprocess_backward_staged(const gs_scene* scene, float* params, const gs_camera* cam, gs_proj proj,
                                   const void* render_ws, size_t render_ws_bytes, float* grads,
                                   const gs_adam* adam, hipStream_t stream);
+
+/* Batched steps ("Scaling 3D Gaussian Splatting with Distributed Compute", the batch-size
+ * passage: several camera views per optimizer step; the batch's loss is the mean of its views'
+ * losses, so its gradient is the mean of theirs).  The preprocess backward of one view of the
+ * batch, from the sums staged in render_ws (as gs_preprocess_backward_staged):
+ *   grads_acc[R][ld]  the gradient accumulated over the batch's earlier views
+ *   first             1 for the batch's first view (grads_acc is not read), else 0
+ *   scale             this view's weight, normally 1 / BS
+ *   adam              NULL for every view but the last: grads_acc <- (first ? 0 : grads_acc)
+ *                     + scale * g.  For the last view: the total (first ? 0 : grads_acc) +
+ *                     scale * g goes through the Adam update of params, m and v (with the
+ *                     batch's hyper-parameters, gs_adam_batch) and grads_acc is not written; it
+ *                     may then be NULL when first is 1 (a batch of one).
+ * Rows n..ld-1 are not touched.  GS_ERR_INVALID_ARGUMENT as gs_preprocess_backward_staged, and
+ * for first outside {0, 1}, a non-finite scale or a missing grads_acc. */
+int gs_preprocess_backward_accumulate(const gs_scene* scene, float* params, const gs_camera* cam, gs_proj proj,
+                                      const void* render_ws, size_t render_ws_bytes, float* grads_acc,
+                                      int32_t first, float scale, const gs_adam* adam, hipStream_t stream);
+
+/* Adam's hyper-parameters for `batch` views per optimizer step (host only; the same page's
+ * batch-size passage): lr * sqrt(batch), eps / sqrt(batch), and each momentum coefficient
+ * decayed linearly, beta <- 1 - batch (1 - beta), so beta1 = 0.9 reaches 0 at batch 10.  m, v
+ * and step are copied.  GS_ERR_INVALID_ARGUMENT for batch < 1, a null pointer, or a batch that
+ * takes a coefficient below zero (batch > 10 at beta1 = 0.9). */
+int gs_adam_batch(const gs_adam* adam, int32_t batch, gs_adam* out);
 
 /* Adam over `count` floats, in place: m = b1 m + (1-b1) g; v = b2 v + (1-b2) g^2;
  * params -= lr (m / (1-b1^t)) / (sqrt(v / (1-b2^t)) + eps).  adam->m and adam->v are flat

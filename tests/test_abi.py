@@ -22,7 +22,7 @@ def test_library_exports_every_declared_symbol():
     assert len(names) == len(gsmi.EXPORTS) and set(names) == set(gsmi.EXPORTS)
     for name in names:
         assert hasattr(L, name), name
-    assert gsmi.version() == 5
+    assert gsmi.version() == 6
 
 
 def test_invalid_arguments_rejected_before_any_gpu_call():
@@ -126,6 +126,47 @@ def test_loss_l1_dssim_checks_its_arguments():
         assert "null" in gsmi.last_error()
     assert L.gs_loss_l1_dssim(64, 64, P, P, f(0.2), P, P, P, ws - 1, None) == -1
     assert "workspace" in gsmi.last_error()
+
+
+def test_adam_batch_scaling_and_checks():
+    import math
+    m = ctypes.c_void_p(256)
+    base = gsmi.GsAdam(256, 256, 3, 1e-3, 0.9, 0.999, 1e-8)
+    for bs in (1, 2, 4, 10):
+        a = gsmi.adam_batch(base, bs)
+        assert a.lr == pytest.approx(1e-3 * math.sqrt(bs), rel=1e-15)
+        assert a.eps == pytest.approx(1e-8 / math.sqrt(bs), rel=1e-15)
+        assert a.beta1 == pytest.approx(1 - bs * 0.1, abs=1e-15)
+        assert a.beta2 == pytest.approx(1 - bs * 0.001, abs=1e-15)
+        assert a.step == 3 and a.m == 256 and a.v == 256
+    assert gsmi.adam_batch(base, 10).beta1 == pytest.approx(0.0, abs=1e-15)
+    for bs in (0, -1, 11):
+        with pytest.raises(gsmi.GsError):
+            gsmi.adam_batch(base, bs)
+    del m
+
+
+def test_preprocess_backward_accumulate_checks_its_arguments():
+    L = gsmi.load()
+    cam = gsmi.GsCamera()
+    cam.fx = cam.fy = 100.0
+    cam.width = cam.height = 64
+    cam.near_plane = 0.01
+    cam.viewmat[0] = cam.viewmat[5] = cam.viewmat[10] = 1.0
+    sc = gsmi.make_scene(10, 10, 0)
+    proj = gsmi.GsProj(256, 256, 256, 256)
+    P = ctypes.c_void_p(256)
+    ws = gsmi.render_workspace(64, 64, 10, 1000)
+    f = ctypes.c_float
+    call = lambda grads, first, scale, adam=None, nbytes=ws: L.gs_preprocess_backward_accumulate(
+        ctypes.byref(sc), P, ctypes.byref(cam), proj, P, nbytes, grads, first, f(scale), adam, None)
+    assert call(None, 0, 0.5) == -1 and "grads_acc" in gsmi.last_error()
+    assert call(None, 1, 0.5) == -1 and "grads_acc" in gsmi.last_error()
+    assert call(P, 2, 0.5) == -1 and "first" in gsmi.last_error()
+    assert call(P, 0, float("nan")) == -1 and "scale" in gsmi.last_error()
+    assert call(P, 0, 0.5, nbytes=16) == -1 and "workspace" in gsmi.last_error()
+    bad = gsmi.GsAdam(None, None, 1, 1e-3, 0.9, 0.999, 1e-8)
+    assert call(P, 1, 1.0, ctypes.byref(bad)) == -1
 
 
 def test_render_calls_reject_a_missing_or_short_workspace():
