@@ -325,3 +325,87 @@ def train_batch_reference(params, sh_degree, cam_flats, W, H, targets, m, v, t, 
     lr_b, b1_b, b2_b, eps_b = adam_batch_hparams(lr, beta1, beta2, eps, len(cam_flats))
     p_new, m_new, v_new = adam(params, grads, m, v, t, lr_b, b1_b, b2_b, eps_b)
     return p_new, m_new, v_new, grads
+
+
+# ------------------------------------------------------------------------------------------
+# Adaptive density control: clone, split, prune
+# ------------------------------------------------------------------------------------------
+# "Scaling 3D Gaussian Splatting with Distributed Compute" names adaptive density control
+# (pruning and densifying, growing N) and its intervals in steps, and prints none of its rules.
+# The reading taken is 3D-GS's: the statistic is each Gaussian's view-space 2D mean gradient
+# norm in normalised device units, averaged over the views that saw it; a Gaussian at or above
+# the gradient threshold is cloned when its largest scale is at most percent_dense x the scene
+# extent and split in two otherwise; Gaussians below the minimum opacity are removed.  The
+# decisions are taken on float32 values in forms both sides evaluate exactly: the averaged
+# statistic (one float32 division), the largest log-scale against log(percent_dense x extent),
+# and the opacity logit against logit(min_opacity).
+DENS_KEEP, DENS_CLONE, DENS_SPLIT, DENS_PRUNE = 0, 1, 2, 3
+
+
+def densify_view_stats(grad2d, radii, W, H):
+    """One view's contribution to the densification statistics: the norm of (dL/du W/2,
+    dL/dv H/2) -- the mean's gradient in normalised device units -- and 1, for every Gaussian
+    the view sees (radius > 0); 0 and 0 elsewhere."""
+    vis = np.asarray(radii)[0] > 0
+    g = _f64(grad2d)
+    norm = np.sqrt((g[0] * (0.5 * W)) ** 2 + (g[1] * (0.5 * H)) ** 2)
+    return np.where(vis, norm, 0.0), vis.astype(np.float64)
+
+
+def densify_thresholds(grad_threshold, percent_dense, extent, min_opacity):
+    """The three float32 thresholds the decisions compare against."""
+    return (np.float32(grad_threshold), np.float32(math.log(percent_dense * extent)),
+            np.float32(math.log(min_opacity / (1.0 - min_opacity))))
+
+
+def densify_codes(params, grad_acc, count, grad_threshold=2e-4, percent_dense=0.01, extent=1.0,
+                  min_opacity=0.005):
+    """Per Gaussian: prune when its opacity is below min_opacity; otherwise, when its averaged
+    statistic reaches grad_threshold, clone (largest scale <= percent_dense x extent) or split."""
+    p = np.asarray(params, dtype=np.float32)
+    acc = np.asarray(grad_acc, dtype=np.float32)
+    cnt = np.asarray(count, dtype=np.float32)
+    t_grad, t_lscale, t_logit = densify_thresholds(grad_threshold, percent_dense, extent, min_opacity)
+    n = p.shape[1]
+    codes = np.zeros(n, dtype=np.int32)
+    for i in range(n):
+        if p[10, i] < t_logit:
+            codes[i] = DENS_PRUNE
+            continue
+        g = acc[i] / cnt[i] if cnt[i] > 0 else np.float32(0.0)
+        if g >= t_grad:
+            codes[i] = DENS_SPLIT if max(p[3, i], p[4, i], p[5, i]) > t_lscale else DENS_CLONE
+    return codes
+
+
+def densify(params, m, v, grad_acc, count, z, grad_threshold=2e-4, percent_dense=0.01, extent=1.0,
+            min_opacity=0.005, split_factor=1.6):
+    """One densification.  Output Gaussians, in this order: the kept ones (neither pruned nor
+    split) in index order; a copy of each cloned one in index order; the first child of each
+    split one in index order; the second children likewise.  A split Gaussian's child k takes
+    mean mu + R(q) (s * z[k]) with s = exp(log-scale) and z[k] the standard normal draw given
+    for it (z: [2][3][n]), log-scale minus log(split_factor), and the parent's rotation,
+    opacity and colour.  Kept Gaussians keep their Adam moments; new ones start at zero.
+    Returns (params, m, v) as float64 [R][n_out], and the codes."""
+    P = _f64(params)
+    codes = densify_codes(params, grad_acc, count, grad_threshold, percent_dense, extent, min_opacity)
+    kept = np.nonzero((codes == DENS_KEEP) | (codes == DENS_CLONE))[0]
+    clones = np.nonzero(codes == DENS_CLONE)[0]
+    splits = np.nonzero(codes == DENS_SPLIT)[0]
+    zz = _f64(z)
+    children = []
+    for k in range(2):
+        c = P[:, splits].copy()
+        for col, i in enumerate(splits):
+            s = np.exp(P[3:6, i])
+            q = P[6:10, i]
+            Rq = quat_to_rot(q / np.linalg.norm(q))
+            c[0:3, col] = P[0:3, i] + Rq @ (s * zz[k, :, i])
+            c[3:6, col] = P[3:6, i] - math.log(split_factor)
+        children.append(c)
+    out = np.concatenate([P[:, kept], P[:, clones], children[0], children[1]], axis=1)
+    R = P.shape[0]
+    n_new = out.shape[1] - kept.size
+    m_out = np.concatenate([_f64(m)[:, kept], np.zeros((R, n_new))], axis=1)
+    v_out = np.concatenate([_f64(v)[:, kept], np.zeros((R, n_new))], axis=1)
+    return out, m_out, v_out, codes
