@@ -107,12 +107,12 @@ KERNEL_OF = {"preprocess": ("k_preprocess<3>", "hbm"), "image_pass": ("k_blend_s
 # size; keyed by the SHA-256 of the kernel's source file, so a changed kernel (or another
 # workload) reports null
 COUNTER_TRAFFIC = {
-    "preprocess": {"source": "preprocess.hip", "bytes": 1200081815,
-                   "sha256": "b65eac29a7e37f262ed39af1cfcbf9a9d1656e0873ea93e7e89e8f5ee9b2d2c6"},
-    "image_pass": {"source": "blend.hip", "bytes": 6697713812,
+    "preprocess": {"source": "preprocess.hip", "bytes": 1200081816,
+                   "sha256": "bdf2d6b2bfda6bd9c4ee0579c394aa49af9704b4d3f8a784a63a7e38fb911657"},
+    "image_pass": {"source": "blend.hip", "bytes": 6699852548,
                    "sha256": "237a7aba22a2e8da715a13a7cfdcd4ade266f2e2f979a826101fca476c61cccc"},
-    "prebwd_adam": {"source": "preprocess.hip", "bytes": 5943349650,
-                    "sha256": "b65eac29a7e37f262ed39af1cfcbf9a9d1656e0873ea93e7e89e8f5ee9b2d2c6"},
+    "prebwd_adam": {"source": "preprocess.hip", "bytes": 5943376226,
+                    "sha256": "bdf2d6b2bfda6bd9c4ee0579c394aa49af9704b4d3f8a784a63a7e38fb911657"},
 }
 
 

@@ -362,6 +362,77 @@ int gs_adam_batch(const gs_adam* adam, int32_t batch, gs_adam* out) {
   return ok();
 }
 
+int gs_densify_stats(const gs_scene* scene, const gs_camera* cam, gs_proj proj, const void* render_ws,
+                     size_t render_ws_bytes, float* grad_acc, float* count, hipStream_t stream) {
+  int st;
+  if ((st = check_scene(scene)) || (st = check_camera(cam))) return st;
+  if (scene->n > 0 && (!proj.splat || !proj.tiles || !grad_acc || !count))
+    return fail(GS_ERR_INVALID_ARGUMENT, "a required pointer is null");
+  RenderWs ws;
+  if (!render_ws || !render_ws_layout(const_cast<void*>(render_ws), render_ws_bytes, (int)n_tiles(*cam), scene->n, &ws))
+    return fail(GS_ERR_INVALID_ARGUMENT, "render workspace too small or not 256-byte aligned");
+  const hipError_t e = launch_densify_stats(scene->n, proj.splat, proj.tiles, ws, 0.5f * (float)cam->width,
+                                            0.5f * (float)cam->height, grad_acc, count, stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "gs_densify_stats");
+}
+
+int gs_densify_workspace(int64_t n, size_t* bytes) {
+  if (!bytes || n < 0) return fail(GS_ERR_INVALID_ARGUMENT, "invalid arguments");
+  *bytes = densify_workspace_bytes(n);
+  return ok();
+}
+
+int gs_densify(const gs_scene* scene, const float* params, const float* m, const float* v, const float* grad_acc,
+               const float* count, const float* z, const gs_densify_opts* opts, float* params_out, float* m_out,
+               float* v_out, int64_t ld_out, int64_t* n_out, int32_t* codes, void* workspace,
+               size_t workspace_bytes, hipStream_t stream) {
+  int st;
+  if ((st = check_scene(scene))) return st;
+  if (!opts || !n_out) return fail(GS_ERR_INVALID_ARGUMENT, "opts / n_out is null");
+  if (!(opts->percent_dense > 0.0 && opts->extent > 0.0 && opts->min_opacity > 0.0 && opts->min_opacity < 1.0 &&
+        opts->split_factor > 0.0 && std::isfinite(opts->grad_threshold) && std::isfinite(opts->percent_dense) &&
+        std::isfinite(opts->extent) && std::isfinite(opts->split_factor)))
+    return fail(GS_ERR_INVALID_ARGUMENT, "densify options out of range");
+  if (ld_out < 0) return fail(GS_ERR_INVALID_ARGUMENT, "ld_out < 0");
+  if (scene->n > 0 && (!params || !m || !v || !grad_acc || !count || !z || !workspace))
+    return fail(GS_ERR_INVALID_ARGUMENT, "a required pointer is null");
+  if (ld_out > 0 && (!params_out || !m_out || !v_out))
+    return fail(GS_ERR_INVALID_ARGUMENT, "an output pointer is null");
+  if (scene->n > 0 && workspace_bytes < densify_workspace_bytes(scene->n))
+    return fail(GS_ERR_INVALID_ARGUMENT, "densify workspace too small");
+  if (scene->n > 0 && (params_out == params || m_out == m || v_out == v))
+    return fail(GS_ERR_INVALID_ARGUMENT, "outputs must not alias inputs");
+  *n_out = 0;
+  if (scene->n == 0) return ok();
+  DensifyLaunch d{};
+  d.n = scene->n;
+  d.ld = scene->ld;
+  d.ld_out = ld_out;
+  d.R = rows_for_degree(scene->sh_degree);
+  d.params = params;
+  d.m = m;
+  d.v = v;
+  d.grad_acc = grad_acc;
+  d.count = count;
+  d.z = z;
+  d.t_grad = (float)opts->grad_threshold;
+  d.t_lscale = (float)std::log(opts->percent_dense * opts->extent);
+  d.t_logit = (float)std::log(opts->min_opacity / (1.0 - opts->min_opacity));
+  d.log_split = (float)std::log(opts->split_factor);
+  d.params_out = params_out;
+  d.m_out = m_out;
+  d.v_out = v_out;
+  d.codes = codes;
+  d.ws = workspace;
+  uint32_t tot[3] = {0, 0, 0};
+  const hipError_t e = launch_densify(d, tot, stream);
+  if (e != hipSuccess) return hip_fail(e, "gs_densify");
+  *n_out = (int64_t)tot[0] + tot[1] + 2 * (int64_t)tot[2];
+  if (*n_out > ld_out) return fail(GS_ERR_CAPACITY, "%lld Gaussians after densification exceed ld_out %lld",
+                                   (long long)*n_out, (long long)ld_out);
+  return ok();
+}
+
 int gs_render_backward(const gs_scene* scene, float* params, const gs_camera* cam, gs_proj proj,
                        const uint32_t* vals, const uint32_t* ranges, const float* bg,
                        const float* T_final, const uint32_t* last_contrib, const float* dL_dimage,

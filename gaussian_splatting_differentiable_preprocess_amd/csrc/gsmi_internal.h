@@ -189,6 +189,29 @@ hipError_t launch_loss_l1(int64_t count, const float* image, const float* target
 size_t ssim_workspace_bytes(int W, int H);
 hipError_t launch_loss_l1_dssim(int W, int H, const float* image, const float* target, float lambda,
                                 float* loss, float* dLdI, void* ws, hipStream_t s);
+// Adaptive density control (densify.hip).
+hipError_t launch_densify_stats(int64_t n, const gs_splat* splat, const uint32_t* tiles, const RenderWs& ws,
+                                float half_w, float half_h, float* grad_acc, float* count, hipStream_t s);
+struct DensifyLaunch {
+  int64_t n, ld, ld_out;
+  int R;
+  const float* params;
+  const float* m;
+  const float* v;
+  const float* grad_acc;
+  const float* count;
+  const float* z;
+  float t_grad, t_lscale, t_logit, log_split;  // float32 thresholds formed in double
+  float* params_out;
+  float* m_out;
+  float* v_out;
+  int32_t* codes;
+  void* ws;
+};
+size_t densify_workspace_bytes(int64_t n);
+// Classifies and counts (then synchronises s to read the three totals into totals_host); writes
+// the output only when it fits ld_out.
+hipError_t launch_densify(const DensifyLaunch& d, uint32_t totals_host[3], hipStream_t s);
 hipError_t launch_adam(int64_t count, float* params, const float* grads, float* m, float* v,
                        const AdamCoef& c, hipStream_t s);
 

@@ -26,7 +26,7 @@ EXPORTS = (
     "gs_render_workspace", "gs_render_workspace_capacity", "gs_render_forward", "gs_loss_l1_workspace", "gs_loss_l1",
     "gs_loss_l1_dssim_workspace", "gs_loss_l1_dssim", "gs_render_backward",
     "gs_render_plan", "gs_render_step", "gs_preprocess_backward", "gs_preprocess_backward_staged", "gs_adam_step",
-    "gs_preprocess_backward_accumulate", "gs_adam_batch",
+    "gs_preprocess_backward_accumulate", "gs_adam_batch", "gs_densify_stats", "gs_densify_workspace", "gs_densify",
 )
 
 
@@ -66,6 +66,16 @@ class GsAdam(ctypes.Structure):
 _lib = None
 
 
+class GsDensifyOpts(ctypes.Structure):
+    _fields_ = [("grad_threshold", ctypes.c_double), ("percent_dense", ctypes.c_double),
+                ("extent", ctypes.c_double), ("min_opacity", ctypes.c_double), ("split_factor", ctypes.c_double)]
+
+
+def densify_opts(grad_threshold=2e-4, percent_dense=0.01, extent=1.0, min_opacity=0.005,
+                 split_factor=1.6) -> GsDensifyOpts:
+    return GsDensifyOpts(grad_threshold, percent_dense, extent, min_opacity, split_factor)
+
+
 def load(path: str = LIB_PATH):
     """Loads libgsmi.so and declares every export; raises if the library is not built."""
     global _lib
@@ -99,6 +109,10 @@ def load(path: str = LIB_PATH):
     L.gs_adam_step.argtypes = [i64, P, P, AP, P]
     L.gs_preprocess_backward_accumulate.argtypes = [SP, P, CP, GsProj, P, sz, P, i32, ctypes.c_float, AP, P]
     L.gs_adam_batch.argtypes = [AP, i32, AP]
+    L.gs_densify_stats.argtypes = [SP, CP, GsProj, P, sz, P, P, P]
+    L.gs_densify_workspace.argtypes = [i64, ctypes.POINTER(sz)]
+    L.gs_densify.argtypes = [SP, P, P, P, P, P, P, ctypes.POINTER(GsDensifyOpts), P, P, P, i64,
+                             ctypes.POINTER(i64), P, P, sz, P]
     for name in EXPORTS:
         if name not in ("gs_version", "gs_last_error"):
             getattr(L, name).restype = ctypes.c_int
@@ -313,6 +327,29 @@ def adam_batch(adam: GsAdam, batch) -> GsAdam:
     out = GsAdam()
     _check(load().gs_adam_batch(ctypes.byref(adam), int(batch), ctypes.byref(out)))
     return out
+
+
+def densify_stats(scene: GsScene, cam: GsCamera, proj: Proj, render_ws, grad_acc, count, stream=None):
+    _check(load().gs_densify_stats(ctypes.byref(scene), ctypes.byref(cam), proj.c(), _ptr(render_ws),
+                                   _nbytes(render_ws), _ptr(grad_acc), _ptr(count), _stream(stream)))
+
+
+def densify_workspace(n) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load().gs_densify_workspace(int(n), ctypes.byref(out)))
+    return out.value
+
+
+def densify(scene: GsScene, params, m, v, grad_acc, count, z, opts: GsDensifyOpts, params_out, m_out, v_out,
+            ld_out, workspace, codes=None, stream=None) -> int:
+    """One clone / split / prune pass; returns the new Gaussian count (GsCapacityError when it
+    exceeds ld_out)."""
+    n_out = ctypes.c_int64(0)
+    rc = load().gs_densify(ctypes.byref(scene), _ptr(params), _ptr(m), _ptr(v), _ptr(grad_acc), _ptr(count), _ptr(z),
+                           ctypes.byref(opts), _ptr(params_out), _ptr(m_out), _ptr(v_out), int(ld_out),
+                           ctypes.byref(n_out), _ptr(codes), _ptr(workspace), _nbytes(workspace), _stream(stream))
+    _check(rc, required=n_out.value)
+    return n_out.value
 
 
 def adam_step(count, params, grads, adam: GsAdam, stream=None):

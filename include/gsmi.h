@@ -12,7 +12,7 @@
  *                       (optionally fused with the Adam update)
  *   gs_adam_step        Adam over all parameters (when not fused)
  * and, for batched steps (several views per optimizer step), gs_preprocess_backward_accumulate
- * with gs_adam_batch.
+ * with gs_adam_batch; adaptive density control with gs_densify_stats and gs_densify.
  *
  * The pages this follows name these stages but print no formulas:
  *   "Scaling 3D Gaussian Splatting with Distributed Compute: Why One GPU Is Never Enough"
@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define GSMI_VERSION 6
+#define GSMI_VERSION 7
 #define GS_TILE 16 /* tiles are GS_TILE x GS_TILE pixels */
 
 typedef enum gs_status {
@@ -336,6 +336,54 @@ int gs_preprocess_backward_accumulate(const gs_scene* scene, float* params, cons
  * and step are copied.  GS_ERR_INVALID_ARGUMENT for batch < 1, a null pointer, or a batch that
  * takes a coefficient below zero (batch > 10 at beta1 = 0.9). */
 int gs_adam_batch(const gs_adam* adam, int32_t batch, gs_adam* out);
+
+/* Adaptive density control ("Scaling 3D Gaussian Splatting with Distributed Compute": pruning
+ * and densifying, which grow N and drive memory; the page gives no rules, so these follow
+ * 3D-GS).  Options (double, formed into float32 thresholds once):
+ *   grad_threshold  averaged 2D-gradient statistic at or above which a Gaussian densifies
+ *                   (3D-GS: 2e-4)
+ *   percent_dense, extent   clone when the largest scale is <= percent_dense * extent, else
+ *                   split (3D-GS: 0.01 x the scene's extent)
+ *   min_opacity     prune below this opacity (3D-GS: 0.005)
+ *   split_factor    a split child's scales are the parent's / split_factor (3D-GS: 1.6) */
+typedef struct gs_densify_opts {
+  double grad_threshold, percent_dense, extent, min_opacity, split_factor;
+} gs_densify_opts;
+
+/* Densification statistics of one view, after its backward blend (gs_render_step, or
+ * gs_render_backward with grad2d = NULL) on the same render_ws, camera and proj: every
+ * Gaussian with radius_x > 0 adds |(dL/du W/2, dL/dv H/2)| -- its 2D mean's gradient in
+ * normalised device units, from the staged sums in the order gs_preprocess_backward_staged
+ * adds them -- to grad_acc[i] and 1 to count[i] (both device float[n], accumulated over views;
+ * the caller zeroes them after each densification).  Asynchronous. */
+int gs_densify_stats(const gs_scene* scene, const gs_camera* cam, gs_proj proj, const void* render_ws,
+                     size_t render_ws_bytes, float* grad_acc, float* count, hipStream_t stream);
+
+/* Bytes of device workspace gs_densify needs for n Gaussians (host-only query). */
+int gs_densify_workspace(int64_t n, size_t* bytes);
+
+/* One clone / split / prune pass over the scene's n Gaussians.
+ *   params, m, v[R][ld]   in: parameters and Adam moments
+ *   grad_acc, count[n]    in: the statistics from gs_densify_stats
+ *   z[2][3][ld]           in: standard normal draws, z[k][j][i] for split child k of Gaussian i
+ *   params_out, m_out, v_out[R][ld_out]  out (must not alias the inputs)
+ *   n_out                 host out: the Gaussian count after the pass
+ *   codes[n]              out, nullable: 0 kept, 1 cloned, 2 split, 3 pruned
+ * Gaussian i is pruned when its opacity logit is below logit(min_opacity); otherwise, when
+ * grad_acc[i] / count[i] (0 when count is 0) reaches grad_threshold, it is cloned when its
+ * largest log-scale is at most log(percent_dense * extent) and split otherwise.  Output order:
+ * the kept Gaussians (neither pruned nor split, clones' originals included) in index order with
+ * their moments; one copy of each cloned Gaussian in index order; the first child of each split
+ * Gaussian in index order; then the second children.  Child k: mean mu + R(q) (exp(l) * z[k]),
+ * log-scale l - log(split_factor), rotation, opacity and colour copied.  New Gaussians start
+ * with zero moments.  The call counts first, copies the three totals to the host and
+ * synchronises `stream`; when n_out > ld_out it returns GS_ERR_CAPACITY with *n_out set and
+ * writes nothing.  GS_ERR_INVALID_ARGUMENT for null pointers, aliasing outputs, a short
+ * workspace or options out of range. */
+int gs_densify(const gs_scene* scene, const float* params, const float* m, const float* v, const float* grad_acc,
+               const float* count, const float* z, const gs_densify_opts* opts, float* params_out, float* m_out,
+               float* v_out, int64_t ld_out, int64_t* n_out, int32_t* codes, void* workspace,
+               size_t workspace_bytes, hipStream_t stream);
 
 /* Adam over `count` floats, in place: m = b1 m + (1-b1) g; v = b2 v + (1-b2) g^2;
  * params -= lr (m / (1-b1^t)) / (sqrt(v / (1-b2^t)) + eps).  adam->m and adam->v are flat

@@ -22,7 +22,7 @@ def test_library_exports_every_declared_symbol():
     assert len(names) == len(gsmi.EXPORTS) and set(names) == set(gsmi.EXPORTS)
     for name in names:
         assert hasattr(L, name), name
-    assert gsmi.version() == 6
+    assert gsmi.version() == 7
 
 
 def test_invalid_arguments_rejected_before_any_gpu_call():
@@ -167,6 +167,49 @@ def test_preprocess_backward_accumulate_checks_its_arguments():
     assert call(P, 0, 0.5, nbytes=16) == -1 and "workspace" in gsmi.last_error()
     bad = gsmi.GsAdam(None, None, 1, 1e-3, 0.9, 0.999, 1e-8)
     assert call(P, 1, 1.0, ctypes.byref(bad)) == -1
+
+
+def test_densify_checks_its_arguments():
+    L = gsmi.load()
+    sc = gsmi.make_scene(1000, 1000, 0)
+    P = ctypes.c_void_p(256)
+    Q = ctypes.c_void_p(512)
+    ws = gsmi.densify_workspace(1000)
+    assert ws >= 4 * 3 * 4 and gsmi.densify_workspace(18_180_000) >= 12 * (18_180_000 // 256)
+    n_out = ctypes.c_int64(-5)
+    ok = gsmi.densify_opts()
+
+    def call(opts=ok, outs=(Q, Q, Q), ld_out=3000, nbytes=ws, ins=(P, P, P, P, P, P), wsp=P):
+        return L.gs_densify(ctypes.byref(sc), *ins, ctypes.byref(opts), *outs, ld_out, ctypes.byref(n_out), None,
+                            wsp, nbytes, None)
+    for bad in (gsmi.densify_opts(percent_dense=0), gsmi.densify_opts(extent=-1), gsmi.densify_opts(min_opacity=1.0),
+                gsmi.densify_opts(split_factor=0), gsmi.densify_opts(grad_threshold=float("nan"))):
+        assert call(opts=bad) == -1 and "options" in gsmi.last_error()
+    for k in range(6):
+        ins = [P] * 6
+        ins[k] = None
+        assert call(ins=tuple(ins)) == -1 and "null" in gsmi.last_error()
+    assert call(outs=(None, Q, Q)) == -1 and "output" in gsmi.last_error()
+    assert call(outs=(P, Q, Q)) == -1 and "alias" in gsmi.last_error()
+    assert call(nbytes=ws - 1) == -1 and "workspace" in gsmi.last_error()
+    assert call(ld_out=-1) == -1
+    assert L.gs_densify(ctypes.byref(sc), P, P, P, P, P, P, None, Q, Q, Q, 10, ctypes.byref(n_out), None, P, ws,
+                        None) == -1
+    # an empty scene needs no pointers and yields zero Gaussians without a GPU call
+    e = gsmi.make_scene(0, 0, 0)
+    assert L.gs_densify(ctypes.byref(e), None, None, None, None, None, None, ctypes.byref(ok), None, None, None, 0,
+                        ctypes.byref(n_out), None, None, 0, None) == 0 and n_out.value == 0
+    # statistics: null accumulators, short render workspace
+    cam = gsmi.GsCamera()
+    cam.fx = cam.fy = 100.0
+    cam.width = cam.height = 64
+    cam.near_plane = 0.01
+    cam.viewmat[0] = cam.viewmat[5] = cam.viewmat[10] = 1.0
+    proj = gsmi.GsProj(256, 256, 256, 256)
+    rws = gsmi.render_workspace(64, 64, 1000, 1000)
+    assert L.gs_densify_stats(ctypes.byref(sc), ctypes.byref(cam), proj, P, rws, None, P, None) == -1
+    assert L.gs_densify_stats(ctypes.byref(sc), ctypes.byref(cam), proj, P, 16, P, P, None) == -1
+    assert "workspace" in gsmi.last_error()
 
 
 def test_render_calls_reject_a_missing_or_short_workspace():

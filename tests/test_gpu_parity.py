@@ -163,11 +163,14 @@ def test_forward(name):
     assert abs(g["blend_count"][2] - int(o["n_blended"].astype(np.int64).sum())) <= slack
 
 
-@pytest.mark.parametrize("name", CASES)
+# the other cases take a seeded upstream dL/dI instead of a loss
+LOSS_CASES = [c for c in CASES if c.startswith("torus")]
+
+
+@pytest.mark.parametrize("name", LOSS_CASES)
 def test_loss(name):
     d = data(name)
-    if d["target"] is None:
-        pytest.skip("configuration without a loss (seeded upstream gradient)")
+    assert d["target"] is not None
     say(f"[parity] test_loss {name}")
     o = d["o"]
     assert abs(d["g_loss"] - o["loss"]) <= 1e-6 * abs(o["loss"]) + 1e-9
