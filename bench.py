@@ -251,6 +251,9 @@ def main():
                     help="views per optimizer step: each view's preprocess backward adds 1/BS of its gradient "
                          "to an accumulator and every BS-th view's runs Adam with the batch-scaled "
                          "hyper-parameters (a timed step is still one view)")
+    ap.add_argument("--densify", action="store_true",
+                    help="accumulate the densification statistics in every step (gs_densify_stats, its own "
+                         "phase) and time one clone/split/prune pass (gs_densify) after the timed steps")
     ap.add_argument("--detail", default=None, help="write a detailed JSON record to this path")
     ap.add_argument("--views", type=int, default=0,
                     help="use only the first N orbit views (short profiling runs); default all")
@@ -305,9 +308,14 @@ def main():
     blends = torch.zeros(3, dtype=torch.int64, device="cuda")
     bg = (0.0, 0.0, 0.0)
     fused = not args.separate_passes and args.dssim is None
+    if args.densify and not fused:
+        raise SystemExit("--densify reads the fused image pass's staged sums; drop --separate-passes / --dssim")
+    dens_acc = torch.zeros(N, device="cuda") if args.densify else None
+    dens_cnt = torch.zeros(N, device="cuda") if args.densify else None
     dssim_ws = (torch.empty(gsmi.loss_l1_dssim_workspace(W, H), dtype=torch.uint8, device="cuda")
                 if args.dssim is not None else None)
-    phases = (["preprocess", "bin_and_sort", "render_plan", "image_pass", "prebwd_adam"] if fused else
+    phases = (["preprocess", "bin_and_sort", "render_plan", "image_pass"] + (["densify_stats"] if args.densify else [])
+              + ["prebwd_adam"] if fused else
               ["preprocess", "bin_and_sort", "forward", "loss", "backward_blend", "prebwd_adam"])
 
     def step(t, view, ev=None):
@@ -331,6 +339,9 @@ def main():
             gsmi.render_step(buf.scene, cam, buf.proj, buf.vals, buf.ranges, bg, targets[view], buf.image,
                              buf.T_final, buf.last, buf.loss, buf.dLdI, buf.render_ws, grad2d=g2, blend_count=blends)
             mark()
+            if args.densify:
+                gsmi.densify_stats(buf.scene, cam, buf.proj, buf.render_ws, dens_acc, dens_cnt)
+                mark()
         else:
             gsmi.render_forward(cam, N, buf.proj.splat, buf.vals, buf.ranges, bg, buf.image, buf.T_final, buf.last,
                                 buf.render_ws, blend_count=blends)
@@ -417,6 +428,26 @@ def main():
     log(f"[bench] per view: {per_launch[0]:.4g} examined, {per_launch[1]:.4g} walked back, "
         f"{per_launch[2]:.4g} composited (pixel, entry) pairs")
 
+    dens = None
+    if args.densify:  # one clone / split / prune pass over the statistics of the timed steps
+        z = torch.randn((2, 3, N), generator=torch.Generator(device="cuda").manual_seed(5), device="cuda")
+        cap = 2 * N
+        outs = [torch.empty((R, cap), device="cuda") for _ in range(3)]
+        dws = torch.empty(gsmi.densify_workspace(N), dtype=torch.uint8, device="cuda")
+        codes = torch.empty(N, dtype=torch.int32, device="cuda")
+        opts = gsmi.densify_opts(extent=cfg.bound_radius)  # the radius of a sphere holding the surface
+        torch.cuda.synchronize()
+        t0d = time.perf_counter()
+        n_out = gsmi.densify(buf.scene, p, m, v, dens_acc, dens_cnt, z, opts, *outs, cap, dws, codes=codes)
+        torch.cuda.synchronize()
+        dms = (time.perf_counter() - t0d) * 1e3
+        k = torch.bincount(codes.long(), minlength=4).tolist()
+        dbytes = N * (12 * R + 8) + n_out * 12 * R + 24 * k[2]
+        dens = {"ms_wall_incl_count_readback": round(dms, 4), "n_in": N, "n_out": n_out,
+                "kept": k[0], "cloned": k[1], "split": k[2], "pruned": k[3], "alg_bytes": dbytes,
+                "alg_GBps": round(dbytes / (dms * 1e-3) / 1e9, 1), "extent": opts.extent}
+        log(f"[bench] densify: {json.dumps(dens)}")
+
     # K and tile-load statistics for the last view (untimed)
     rng_np = buf.ranges.cpu().numpy()
     hist = tile_histogram(rng_np)
@@ -445,7 +476,7 @@ def main():
     }
     if args.detail:
         with open(args.detail, "w") as f:
-            json.dump(dict(out, per_phase=per_phase, tile_list_lengths=hist, target_K=tks), f, indent=1)
+            json.dump(dict(out, per_phase=per_phase, tile_list_lengths=hist, target_K=tks, densify=dens), f, indent=1)
     print(json.dumps(out), flush=True)
 
 
