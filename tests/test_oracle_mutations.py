@@ -45,6 +45,15 @@ MUTATIONS = [
 ]
 
 
+PIN_SUITES = ["tests/test_oracle_pins.py", "tests/test_oracle_gradients.py"]
+SSIM_SUITE = ["tests/test_oracle_ssim.py"]
+
+
+def suites_for(name):
+    """The D-SSIM loss has its own pin suite; the other mistakes face the step's pins."""
+    return SSIM_SUITE if "ssim" in name else PIN_SUITES
+
+
 @pytest.mark.slow
 @pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
 def test_planted_mistake_is_caught(name, old, new, tmp_path):
@@ -55,8 +64,7 @@ def test_planted_mistake_is_caught(name, old, new, tmp_path):
         ".git", "_work", "_build", "gpurun_out", "*.so", "__pycache__", "profiles"))
     with open(dst / "oracle" / "oracle.c", "w") as f:
         f.write(src.replace(old, new, 1))
-    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        "tests/test_oracle_pins.py", "tests/test_oracle_gradients.py", "tests/test_oracle_ssim.py"],
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider", *suites_for(name)],
                        cwd=dst, capture_output=True, text=True, timeout=600)
     tail = "\n".join(r.stdout.strip().splitlines()[-3:])
     assert r.returncode == 1, f"planted mistake {name!r} was not caught by the pins:\n{tail}"
@@ -68,7 +76,6 @@ def test_unmutated_copy_passes(tmp_path):
     dst = tmp_path / "repo"
     shutil.copytree(ROOT, dst, ignore=shutil.ignore_patterns(
         ".git", "_work", "_build", "gpurun_out", "*.so", "__pycache__", "profiles"))
-    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        "tests/test_oracle_pins.py", "tests/test_oracle_gradients.py", "tests/test_oracle_ssim.py"],
-                       cwd=dst, capture_output=True, text=True, timeout=600)
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider", *PIN_SUITES,
+                        *SSIM_SUITE], cwd=dst, capture_output=True, text=True, timeout=600)
     assert r.returncode == 0, r.stdout[-2000:]
