@@ -213,6 +213,17 @@ def cpu_baseline(cfg, params_np, cam, blends_full, crop=512):
             "sample": sample, "ms_per_step": sec * 1e3}
 
 
+def gpu_state():
+    """Clocks and power of the GPU as rocm-smi reports them (None where it is unavailable)."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--json"], capture_output=True, text=True,
+                           timeout=20)
+        return json.loads(r.stdout) if r.returncode == 0 and r.stdout.strip() else None
+    except (OSError, ValueError, subprocess.SubprocessError):
+        return None
+
+
 def copy_calibration(mib, reps=10):
     """A plain elementwise copy (out = src * 1) of mib MiB, timed with events on the current stream."""
     import torch
@@ -425,6 +436,17 @@ def main():
             d["alg_TFLOPs"] = round(alg_flops(ph, *per_launch, ssim_values=3 * P) / (ph_ms[ph] * 1e-3) / 1e12, 3)
         per_phase[ph] = d
     log(f"[bench] roofline: {json.dumps(roof)}")
+    # per-step event time (first mark to last) over the timed views, and the pair rates
+    step_ms = np.array([evs[k][0].elapsed_time(evs[k][-1]) for k in range(args.steps)])
+    step_stats = {"mean": round(float(step_ms.mean()), 4), "median": round(float(np.median(step_ms)), 4),
+                  "p90": round(float(np.percentile(step_ms, 90)), 4), "min": round(float(step_ms.min()), 4),
+                  "max": round(float(step_ms.max()), 4)}
+    blend_ph = "image_pass" if fused else "forward"
+    rates = {"examined_pairs_per_s_of_step": per_launch[0] / (ms_per_step * 1e-3),
+             "composited_pairs_per_s_of_step": per_launch[2] / (ms_per_step * 1e-3),
+             "examined_pairs_per_s_of_" + blend_ph: per_launch[0] / (ph_ms[blend_ph] * 1e-3)}
+    if not fused:
+        rates["walked_pairs_per_s_of_backward_blend"] = per_launch[1] / (ph_ms["backward_blend"] * 1e-3)
     log(f"[bench] per view: {per_launch[0]:.4g} examined, {per_launch[1]:.4g} walked back, "
         f"{per_launch[2]:.4g} composited (pixel, entry) pairs")
 
@@ -476,7 +498,10 @@ def main():
     }
     if args.detail:
         with open(args.detail, "w") as f:
-            json.dump(dict(out, per_phase=per_phase, tile_list_lengths=hist, target_K=tks, densify=dens), f, indent=1)
+            json.dump(dict(out, per_phase=per_phase, step_event_ms=step_stats, pair_rates=rates,
+                           pairs_per_view={"examined": per_launch[0], "walked": per_launch[1],
+                                           "composited": per_launch[2]},
+                           tile_list_lengths=hist, target_K=tks, densify=dens, gpu_state=gpu_state()), f, indent=1)
     print(json.dumps(out), flush=True)
 
 

@@ -38,7 +38,7 @@ constexpr int kWin = 11;
 constexpr int kHalf = kWin - 1;          // 10: window extent beyond its first row / column
 constexpr int kCols = 256;               // window positions (or pixels) per workgroup row
 constexpr int kSsimThreads = 3 * kCols;  // one thread per (channel, column)
-constexpr int kRows = 32;                // output rows per workgroup
+constexpr int kRows = 64;                // output rows per workgroup
 constexpr int kSpan = kCols + kHalf;     // 266 staged columns per row
 constexpr int kSpanPad = 272;
 

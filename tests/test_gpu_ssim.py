@@ -1,7 +1,7 @@
 """GPU parity of the L1 + D-SSIM loss (gs_loss_l1_dssim) against the CPU oracle on the same seeded
 images: the three loss values within relative 1e-5, dL/dimage within relative L2 1e-3 (the
 gradient bar) and within 1e-3 of its largest entry elementwise.  Sizes cover the smallest image
-the 11x11 window fits, ragged strips and row blocks of the kernels' 256-column x 32-row
+the 11x11 window fits, ragged strips and row blocks of the kernels' 256-column x 64-row
 workgroups, and the full 2048x2048 image the step renders."""
 import numpy as np
 import pytest
