@@ -17,8 +17,8 @@
 //
 // Radix passes are reduce-then-scan with 8-bit digits: a histogram kernel (LDS atomics), a
 // per-digit scan over blocks, and a scatter kernel that ranks each 4096-item block stably
-// (wave64 ballot match of the digit per round of 256 items), sorts the block in LDS and writes
-// runs of equal digits contiguously.  All kernels are HBM-bound.
+// (each wave ranks a contiguous quarter of it with wave64 ballot matches of the digit, 64
+// items per round), sorts the block in LDS and writes runs of equal digits contiguously.
 #include "gsmi_internal.h"
 
 namespace gsmi {
@@ -190,6 +190,18 @@ __global__ __launch_bounds__(kBlock) void k_radix_scan(uint32_t* __restrict__ co
   if (threadIdx.x == 0) totals[blockIdx.x] = tot;
 }
 
+// Makes a wave's LDS writes visible to its own later reads (other lanes included).
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Each wave ranks a contiguous quarter of the block (1024 items, 16 rounds of 64) on its own:
+// the wave's running count per digit lives in its row of wcnt, read and advanced once per round
+// by the round's lanes of that digit, with no workgroup barrier between rounds.  The four
+// waves' counts then give each wave its offset inside the block's run of each digit (waves in
+// index order), so the block is sorted stably in LDS and written out in runs of equal digits.
 __global__ __launch_bounds__(kBlock) void k_radix_scatter(
     const uint32_t* __restrict__ keys_in, const uint32_t* __restrict__ vals_in, int64_t n, int shift,
     int xform, uint32_t lo, uint32_t hi, const uint32_t* __restrict__ counts,
@@ -198,8 +210,6 @@ __global__ __launch_bounds__(kBlock) void k_radix_scatter(
   __shared__ uint32_t s_keys[kRadixTile];
   __shared__ uint32_t s_vals[kRadixTile];
   __shared__ uint32_t wcnt[4][256];
-  __shared__ uint32_t woff[4][256];
-  __shared__ uint32_t running[256];
   __shared__ uint32_t gbase[256];
   __shared__ uint32_t lstart[256];
   __shared__ uint32_t tmp[4];
@@ -212,16 +222,16 @@ __global__ __launch_bounds__(kBlock) void k_radix_scatter(
     uint32_t tot;
     const uint32_t dbase = block_excl_scan(totals[tid], tmp, &tot);
     gbase[tid] = dbase + counts[(int64_t)tid * nblk + blockIdx.x];
-    running[tid] = 0;
     for (int k = 0; k < 4; ++k) wcnt[k][tid] = 0;
   }
   __syncthreads();
 
   uint32_t mk[kItems], mv[kItems], mr[kItems];
   const unsigned long long lt = __lanemask_lt();
+  const int64_t wbase = base + (int64_t)w * (kItems * 64);
 #pragma unroll
   for (int r = 0; r < kItems; ++r) {
-    const int64_t idx = base + r * kBlock + tid;
+    const int64_t idx = wbase + r * 64 + lane;
     const bool valid = idx < n;
     uint32_t k = 0, v = 0;
     if (valid) {
@@ -238,35 +248,32 @@ __global__ __launch_bounds__(kBlock) void k_radix_scatter(
       peers &= bit ? bb : ~bb;
     }
     const uint32_t rank = (uint32_t)__popcll(peers & lt);
-    if (valid && rank == 0) wcnt[w][d] = (uint32_t)__popcll(peers);
-    __syncthreads();
-    {
-      const uint32_t c0 = wcnt[0][tid], c1 = wcnt[1][tid], c2 = wcnt[2][tid], c3 = wcnt[3][tid];
-      const uint32_t run = running[tid];
-      woff[0][tid] = run;
-      woff[1][tid] = run + c0;
-      woff[2][tid] = run + c0 + c1;
-      woff[3][tid] = run + c0 + c1 + c2;
-      running[tid] = run + c0 + c1 + c2 + c3;
-      wcnt[0][tid] = wcnt[1][tid] = wcnt[2][tid] = wcnt[3][tid] = 0;
-    }
-    __syncthreads();
+    const uint32_t before = wcnt[w][d];
     mk[r] = k;
     mv[r] = v;
-    mr[r] = valid ? woff[w][d] + rank : 0xFFFFFFFFu;
+    mr[r] = valid ? before + rank : 0xFFFFFFFFu;
+    wave_sync_lds();  // every lane has read the counts before the leaders advance them
+    if (valid && rank == 0) wcnt[w][d] = before + (uint32_t)__popcll(peers);
+    wave_sync_lds();
   }
   (void)lane;
-  // local start of each digit inside the block
+  __syncthreads();
+  // per digit: each wave's offset inside the block's run, and the run's start in the block
   {
+    const uint32_t c0 = wcnt[0][tid], c1 = wcnt[1][tid], c2 = wcnt[2][tid], c3 = wcnt[3][tid];
     uint32_t tot;
-    lstart[tid] = block_excl_scan(running[tid], tmp, &tot);
+    lstart[tid] = block_excl_scan(c0 + c1 + c2 + c3, tmp, &tot);
+    wcnt[0][tid] = 0;
+    wcnt[1][tid] = c0;
+    wcnt[2][tid] = c0 + c1;
+    wcnt[3][tid] = c0 + c1 + c2;
   }
   __syncthreads();
 #pragma unroll
   for (int r = 0; r < kItems; ++r) {
     if (mr[r] != 0xFFFFFFFFu) {
       const uint32_t d = (mk[r] >> shift) & 255u;
-      const uint32_t pos = lstart[d] + mr[r];
+      const uint32_t pos = lstart[d] + wcnt[w][d] + mr[r];
       s_keys[pos] = mk[r];
       s_vals[pos] = mv[r];
     }
