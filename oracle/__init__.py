@@ -366,16 +366,25 @@ def densify_codes(params, grad_acc, count, grad_threshold=2e-4, percent_dense=0.
     acc = np.asarray(grad_acc, dtype=np.float32)
     cnt = np.asarray(count, dtype=np.float32)
     t_grad, t_lscale, t_logit = densify_thresholds(grad_threshold, percent_dense, extent, min_opacity)
-    n = p.shape[1]
-    codes = np.zeros(n, dtype=np.int32)
-    for i in range(n):
-        if p[10, i] < t_logit:
-            codes[i] = DENS_PRUNE
-            continue
-        g = acc[i] / cnt[i] if cnt[i] > 0 else np.float32(0.0)
-        if g >= t_grad:
-            codes[i] = DENS_SPLIT if max(p[3, i], p[4, i], p[5, i]) > t_lscale else DENS_CLONE
+    seen = cnt > 0
+    g = np.zeros_like(acc)
+    g[seen] = acc[seen] / cnt[seen]                      # one float32 division
+    largest = np.maximum(np.maximum(p[3], p[4]), p[5])   # largest log-scale
+    codes = np.full(p.shape[1], DENS_KEEP, dtype=np.int32)
+    dense = g >= t_grad
+    codes[dense & (largest <= t_lscale)] = DENS_CLONE
+    codes[dense & (largest > t_lscale)] = DENS_SPLIT
+    codes[p[10] < t_logit] = DENS_PRUNE
     return codes
+
+
+def _rotations(q):
+    """Rotation matrices [n][3][3] of the quaternions q [4][n] = (w, x, y, z) after normalising."""
+    w, x, y, z = np.asarray(q, dtype=np.float64) / np.linalg.norm(q, axis=0)
+    return np.stack([
+        np.stack([1 - 2 * (y * y + z * z), 2 * (x * y - w * z), 2 * (x * z + w * y)], -1),
+        np.stack([2 * (x * y + w * z), 1 - 2 * (x * x + z * z), 2 * (y * z - w * x)], -1),
+        np.stack([2 * (x * z - w * y), 2 * (y * z + w * x), 1 - 2 * (x * x + y * y)], -1)], 1)
 
 
 def densify(params, m, v, grad_acc, count, z, grad_threshold=2e-4, percent_dense=0.01, extent=1.0,
@@ -393,15 +402,14 @@ def densify(params, m, v, grad_acc, count, z, grad_threshold=2e-4, percent_dense
     clones = np.nonzero(codes == DENS_CLONE)[0]
     splits = np.nonzero(codes == DENS_SPLIT)[0]
     zz = _f64(z)
+    Rq = _rotations(P[6:10, splits])                     # [n_split][3][3]
+    s = np.exp(P[3:6, splits])                           # [3][n_split]
     children = []
     for k in range(2):
         c = P[:, splits].copy()
-        for col, i in enumerate(splits):
-            s = np.exp(P[3:6, i])
-            q = P[6:10, i]
-            Rq = quat_to_rot(q / np.linalg.norm(q))
-            c[0:3, col] = P[0:3, i] + Rq @ (s * zz[k, :, i])
-            c[3:6, col] = P[3:6, i] - math.log(split_factor)
+        d = s * zz[k][:, splits]                         # s * z[k], [3][n_split]
+        c[0:3] = P[0:3, splits] + np.einsum("nij,jn->in", Rq, d)
+        c[3:6] = P[3:6, splits] - math.log(split_factor)
         children.append(c)
     out = np.concatenate([P[:, kept], P[:, clones], children[0], children[1]], axis=1)
     R = P.shape[0]

@@ -112,3 +112,37 @@ def test_densify_stats_after_a_step():
     say(f"[densify]   statistic rel-L2 {e:.3g}; {int(seen.sum())} seen, {mism} visibility mismatches")
     assert mism <= max(2, 1e-3 * n)
     assert e <= 1e-2
+
+
+@pytest.mark.slow
+def test_densify_full_size_gyroid_4m():
+    """The 4M-Gaussian gyroid scene (SH 3) with seeded statistics that send every outcome to
+    hundreds of thousands of Gaussians: codes, count and order bit-exact, every output column
+    compared."""
+    cfg = inputs.CONFIGS["gyroid_4m_2048"]
+    say("[densify] gyroid_4m: drawing the scene")
+    params = inputs.gaussian_params(cfg)
+    n = params.shape[1]
+    rng = np.random.default_rng(99)
+    params[10] = rng.normal(-2.0, 2.0, n).astype(np.float32)
+    acc = rng.uniform(0, 1e-3, n).astype(np.float32)
+    cnt = rng.integers(0, 4, n).astype(np.float32)
+    z = rng.standard_normal((2, 3, n)).astype(np.float32)
+    m = np.zeros_like(params)
+    v = np.zeros_like(params)
+    opts = dict(extent=0.35)  # 0.01 x extent near the scene's typical largest scale: clones and splits
+    say("[densify] gyroid_4m: oracle")
+    want, wm, wv, wcodes = oracle.densify(params, m, v, acc, cnt, z, **opts)
+    n_out, got, gm, gv, codes = _gpu_densify(params, m, v, acc, cnt, z, 3, 2 * n, gsmi.densify_opts(**opts))
+    k = np.bincount(wcodes, minlength=4)
+    say(f"[densify]   kept {k[0]}, cloned {k[1]}, split {k[2]}, pruned {k[3]} -> {n_out}")
+    assert min(k) > 1000
+    np.testing.assert_array_equal(codes, wcodes)
+    assert n_out == want.shape[1]
+    n_copy = int(k[0] + 2 * k[1])
+    np.testing.assert_array_equal(got[:, :n_copy], want[:, :n_copy].astype(np.float32))
+    assert (gm == 0).all() and (gv == 0).all()
+    ch = slice(n_copy, n_out)
+    np.testing.assert_allclose(got[0:3, ch], want[0:3, ch], rtol=0, atol=4e-6)
+    np.testing.assert_allclose(got[3:6, ch], want[3:6, ch], rtol=0, atol=2e-6)
+    np.testing.assert_array_equal(got[6:, ch], want[6:, ch].astype(np.float32))
