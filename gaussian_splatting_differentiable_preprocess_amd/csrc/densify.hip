@@ -74,8 +74,9 @@ __device__ __forceinline__ uint32_t dens_code(const DensArgs& a, int64_t i) {
   const float c = a.count[i];
   const float g = c > 0.f ? a.grad_acc[i] / c : 0.f;
   if (!(g >= a.t_grad)) return kKeep;
+  // fmaxf skips a NaN operand; with all three NaN the Gaussian is kept as it is
   const float l = fmaxf(fmaxf(p[3 * a.ld + i], p[4 * a.ld + i]), p[5 * a.ld + i]);
-  return l > a.t_lscale ? kSplit : kClone;
+  return l > a.t_lscale ? kSplit : (l <= a.t_lscale ? kClone : kKeep);
 }
 
 // Exclusive scan of (kept, clone, split) flags over the workgroup's 256 Gaussians.

@@ -378,7 +378,9 @@ int gs_densify_workspace(int64_t n, size_t* bytes);
  * log-scale l - log(split_factor), rotation, opacity and colour copied.  New Gaussians start
  * with zero moments.  The call counts first, copies the three totals to the host and
  * synchronises `stream`; when n_out > ld_out it returns GS_ERR_CAPACITY with *n_out set and
- * writes nothing.  GS_ERR_INVALID_ARGUMENT for null pointers, aliasing outputs, a short
+ * writes nothing.  Every comparison with NaN is false: a NaN statistic never densifies, a NaN
+ * logit never prunes, three NaN log-scales neither clone nor split (a NaN among them is
+ * skipped).  GS_ERR_INVALID_ARGUMENT for null pointers, aliasing outputs, a short
  * workspace or options out of range. */
 int gs_densify(const gs_scene* scene, const float* params, const float* m, const float* v, const float* grad_acc,
                const float* count, const float* z, const gs_densify_opts* opts, float* params_out, float* m_out,

@@ -369,12 +369,14 @@ def densify_codes(params, grad_acc, count, grad_threshold=2e-4, percent_dense=0.
     seen = cnt > 0
     g = np.zeros_like(acc)
     g[seen] = acc[seen] / cnt[seen]                      # one float32 division
-    largest = np.maximum(np.maximum(p[3], p[4]), p[5])   # largest log-scale
+    largest = np.fmax(np.fmax(p[3], p[4]), p[5])         # largest log-scale (a NaN one skipped)
     codes = np.full(p.shape[1], DENS_KEEP, dtype=np.int32)
     dense = g >= t_grad
     codes[dense & (largest <= t_lscale)] = DENS_CLONE
     codes[dense & (largest > t_lscale)] = DENS_SPLIT
     codes[p[10] < t_logit] = DENS_PRUNE
+    # every comparison with NaN is false: a NaN statistic never densifies, a NaN logit never
+    # prunes, and three NaN log-scales neither clone nor split
     return codes
 
 

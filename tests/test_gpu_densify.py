@@ -146,3 +146,27 @@ def test_densify_full_size_gyroid_4m():
     np.testing.assert_allclose(got[0:3, ch], want[0:3, ch], rtol=0, atol=4e-6)
     np.testing.assert_allclose(got[3:6, ch], want[3:6, ch], rtol=0, atol=2e-6)
     np.testing.assert_array_equal(got[6:, ch], want[6:, ch].astype(np.float32))
+
+
+def test_densify_non_finite_inputs():
+    """Every comparison with NaN is false on both sides: a NaN statistic never densifies, a NaN
+    logit never prunes, three NaN log-scales neither clone nor split, and a NaN among the
+    log-scales is skipped by the largest-scale test."""
+    params, m, v, acc, cnt, z = _inputs(600, 1, 11)
+    acc[0:50] = np.nan
+    params[10, 50:100] = np.nan
+    params[3:6, 100:150] = np.nan
+    params[4, 150:200] = np.nan
+    acc[100:200] = 5e-3  # dense: only the largest-scale test decides
+    cnt[100:200] = 1.0
+    want, wm, wv, wcodes = oracle.densify(params, m, v, acc, cnt, z)
+    keep_or_prune = (wcodes == oracle.DENS_KEEP) | (wcodes == oracle.DENS_PRUNE)
+    assert keep_or_prune[0:50].all() and keep_or_prune[100:150].all()
+    assert (wcodes[50:100] != oracle.DENS_PRUNE).all()
+    assert (wcodes[150:200] != oracle.DENS_KEEP).any()
+    n_out, got, gm, gv, codes = _gpu_densify(params, m, v, acc, cnt, z, 1, 3 * 600, gsmi.densify_opts())
+    np.testing.assert_array_equal(codes, wcodes)
+    assert n_out == want.shape[1]
+    k = np.bincount(wcodes, minlength=4)
+    n_copy = int(k[0] + 2 * k[1])
+    np.testing.assert_array_equal(got[:, :n_copy], want[:, :n_copy].astype(np.float32))
