@@ -10,8 +10,11 @@ sample of tiles (the heaviest ones and a seeded random set), both sides given th
 with every other tile emptied.  Set GSMI_FULLSIZE_18M=0 to skip it (its scene takes about a
 minute to draw on the host).
 
-Upstream dL/dI is the seeded U(-1, 1) field of each configuration (the L1 loss is covered by the
-smaller cases)."""
+gyroid_4m_1024 and gyroid_4m_2048 with the L1 loss against a seeded target: the fused image pass
+and the preprocess backward from its staged sums -- the launch configuration the bench times --
+on the oracle's records and lists and end to end.
+
+Elsewhere upstream dL/dI is the seeded U(-1, 1) field of the configuration."""
 from __future__ import annotations
 
 import os
@@ -93,6 +96,51 @@ def test_gyroid_4m_2048_full_step():
     ee = rel_l2(grads_e, o["grads"])
     say(f"[fullsize] e2e: image frac > 1e-4 {frac_bad:.3g}, grads rel-L2 {ee:.3g}")
     assert frac_bad <= 1e-3 and ee <= 1e-2
+
+
+@pytest.mark.parametrize("name", ["gyroid_4m_1024", "gyroid_4m_2048"])
+def test_gyroid_4m_fused_step_with_l1(name):
+    """The step as the bench runs it: the fused image pass (forward, L1 against a target and
+    backward blend in one persistent kernel, gs_render_step) and the preprocess backward from
+    the staged sums, at 1024^2 and 2048^2.  Stage parity on the oracle's records and lists,
+    then the whole step from the parameters."""
+    cfg = inputs.CONFIGS[name]
+    W = H = cfg.res
+    say(f"[fullsize] {name}: drawing the scene")
+    params = inputs.gaussian_params(cfg)
+    cam = inputs.cameras_for(cfg)[7]
+    target = np.random.default_rng(cfg.index).uniform(0, 1, (H, W, 3)).astype(np.float32)
+    R, n = params.shape
+    say(f"[fullsize] {name}: oracle step with the L1 loss")
+    o = oracle_pipeline(params, cfg.sh_degree, cam.flat(), W, H, BG, target=target, margins=FWD_MARGINS)
+    K = o["keys"].size
+    say(f"[fullsize] {name}: K = {K}; fused pass on the oracle's records and lists")
+    g = GpuStep(params, cfg.sh_degree, cam, W, H, k_capacity=K + 4096)
+    g.load_proj(*records_from_oracle(o["p32"], o["radii"], o["tiles"], W, H))
+    g.load_lists(o["vals"], o["ranges"])
+    r = g.step(BG, target)
+    assert r["stall"] == 0
+    _compare_forward(r, o["fwd"], W * H, "fused")
+    assert r["loss"] == pytest.approx(o["loss"], rel=1e-5)
+    errs = [rel_l2(r["grad2d"][k, :n], o["grad2d"][k]) for k in range(9)]
+    say("[fullsize] fused backward blend rel-L2 per row: " + " ".join(f"{e:.2g}" for e in errs))
+    assert max(errs) <= GRAD_REL_L2
+    e = rel_l2(g.preprocess_backward_staged(), o["grads"])
+    say(f"[fullsize] preprocess backward from the staged sums rel-L2 {e:.3g}")
+    assert e <= GRAD_REL_L2
+    say(f"[fullsize] {name}: the whole step from the parameters")
+    e2 = GpuStep(params, cfg.sh_degree, cam, W, H, k_capacity=K + 4096)
+    e2.preprocess()
+    e2.bin_and_sort()
+    r2 = e2.step(BG, target)
+    assert r2["stall"] == 0
+    err = np.abs(r2["image"] - o["fwd"]["image"]).max(axis=-1)
+    frac_bad = float((err[~o["fwd"]["borderline"]] > IMG_MAX_ABS).mean())
+    ee = rel_l2(e2.preprocess_backward_staged(), o["grads"])
+    say(f"[fullsize] e2e fused: image frac > 1e-4 {frac_bad:.3g}, loss {r2['loss']:.7g} vs {o['loss']:.7g}, "
+        f"grads rel-L2 {ee:.3g}")
+    assert frac_bad <= 1e-3 and ee <= 1e-2
+    assert r2["loss"] == pytest.approx(o["loss"], rel=1e-4)
 
 
 @pytest.mark.skipif(os.environ.get("GSMI_FULLSIZE_18M", "1") == "0", reason="GSMI_FULLSIZE_18M=0")
