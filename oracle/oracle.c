@@ -707,8 +707,9 @@ double or_loss_l1_dssim(int W, int H, const double* image, const double* target,
   double* d_mu = (double*)malloc((size_t)(3 * nv) * sizeof(double));
   double* d_xx = (double*)malloc((size_t)(3 * nv) * sizeof(double));
   double* d_xy = (double*)malloc((size_t)(3 * nv) * sizeof(double));
-  double ssim_sum = 0.0;
-#pragma omp parallel for reduction(+ : ssim_sum) schedule(static)
+  /* per-row sums, added in row order afterwards: the total does not depend on the threads */
+  double* ssim_row = (double*)calloc((size_t)Hv, sizeof(double));
+#pragma omp parallel for schedule(static)
   for (int r = 0; r < Hv; r++) {
     for (int s = 0; s < Wv; s++) {
       for (int c = 0; c < 3; c++) {
@@ -728,7 +729,7 @@ double or_loss_l1_dssim(int W, int H, const double* image, const double* target,
         const double A = 2.0 * mx * my + SSIM_C1, B = 2.0 * cxy + SSIM_C2;
         const double C = mx * mx + my * my + SSIM_C1, D = vx + vy + SSIM_C2;
         const double S = (A * B) / (C * D);
-        ssim_sum += S;
+        ssim_row[r] += S;
         const int64_t p = (int64_t)c * nv + (int64_t)r * Wv + s;
         d_mu[p] = S * (2.0 * my / A - 2.0 * my / B - 2.0 * mx / C + 2.0 * mx / D);
         d_xx[p] = -S / D;
@@ -736,6 +737,9 @@ double or_loss_l1_dssim(int W, int H, const double* image, const double* target,
       }
     }
   }
+  double ssim_sum = 0.0;
+  for (int r = 0; r < Hv; r++) ssim_sum += ssim_row[r];
+  free(ssim_row);
   const double M = 3.0 * (double)nv;
   const double ssim = ssim_sum / M;
   double l1_sum = 0.0;

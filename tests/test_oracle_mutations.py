@@ -46,6 +46,15 @@ MUTATIONS = [
 
 
 PIN_SUITES = ["tests/test_oracle_pins.py", "tests/test_oracle_gradients.py"]
+PACKAGE = "gaussian_splatting_differentiable_preprocess_amd"
+
+
+def copy_sources(dst):
+    """The sources the pin suites need: the oracle, the tests and the package's Python files
+    (the seeded inputs), without built libraries."""
+    skip = shutil.ignore_patterns("*.so", "*.so.tmp*", "_build", "__pycache__")
+    for d in ("oracle", "tests", PACKAGE, "include"):
+        shutil.copytree(os.path.join(ROOT, d), dst / d, ignore=skip)
 SSIM_SUITE = ["tests/test_oracle_ssim.py"]
 
 
@@ -60,8 +69,7 @@ def test_planted_mistake_is_caught(name, old, new, tmp_path):
     src = open(os.path.join(ROOT, "oracle", "oracle.c")).read()
     assert src.count(old) == 1, f"mutation site for {name!r} not found once"
     dst = tmp_path / "repo"
-    shutil.copytree(ROOT, dst, ignore=shutil.ignore_patterns(
-        ".git", "_work", "_build", "gpurun_out", "*.so", "__pycache__", "profiles"))
+    copy_sources(dst)
     with open(dst / "oracle" / "oracle.c", "w") as f:
         f.write(src.replace(old, new, 1))
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider", *suites_for(name)],
@@ -74,8 +82,7 @@ def test_planted_mistake_is_caught(name, old, new, tmp_path):
 def test_unmutated_copy_passes(tmp_path):
     """Control: the same copy procedure without a planted mistake passes the pins."""
     dst = tmp_path / "repo"
-    shutil.copytree(ROOT, dst, ignore=shutil.ignore_patterns(
-        ".git", "_work", "_build", "gpurun_out", "*.so", "__pycache__", "profiles"))
+    copy_sources(dst)
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider", *PIN_SUITES,
                         *SSIM_SUITE], cwd=dst, capture_output=True, text=True, timeout=600)
     assert r.returncode == 0, r.stdout[-2000:]
