@@ -52,6 +52,8 @@ def lib():
         P = ctypes.c_void_p
         i64, i32, dbl = ctypes.c_int64, ctypes.c_int, ctypes.c_double
         L.or_rows_for_degree.argtypes = [i32]
+        L.or_set_num_threads.argtypes = [i32]
+        L.or_get_max_threads.restype = i32
         L.or_sh_basis.argtypes = [i32, dbl, dbl, dbl, P]
         L.or_quat_to_rot.argtypes = [P, P]
         L.or_preprocess.argtypes = [i64, i32, P, P, i32, i32, P, P, P]
@@ -62,7 +64,7 @@ def lib():
         L.or_bin_sort.argtypes = [i64, P, P, i32, i32, P, P]
         L.or_bin_sort.restype = i64
         L.or_ranges.argtypes = [i64, P, i32, P]
-        L.or_render_forward.argtypes = [i32, i32, P, i64, P, P, P, P, P, P, P, P, P, P, P, i64, i32]
+        L.or_render_forward.argtypes = [i32, i32, P, i64, P, P, P, P, P, P, P, P, P, P, P, i64, i32, P]
         L.or_render_bruteforce.argtypes = [i32, i32, P, i64, P, P, P, P, P, P]
         L.or_loss_l1.argtypes = [i64, P, P, P]
         L.or_loss_l1.restype = dbl
@@ -82,6 +84,15 @@ def _p(a):
 
 def _f64(a):
     return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def set_num_threads(n):
+    """OpenMP threads of the oracle's parallel loops."""
+    lib().or_set_num_threads(int(n))
+
+
+def max_threads():
+    return lib().or_get_max_threads()
 
 
 def rows_for_degree(d):
@@ -166,9 +177,11 @@ def ranges(keys, n_tiles):
 
 
 def render_forward(proj, vals, rng, W, H, bg=(0.0, 0.0, 0.0), margins=None,
-                   record_decisions=False, decisions=None):
+                   record_decisions=False, decisions=None, walk=False):
     """Tiled forward.  Returns dict(image [H][W][3], T_final, last_contrib, n_examined,
-    borderline, n_blended) and, with record_decisions, 'decisions' (int8 [H*W][maxlen])."""
+    borderline, n_blended), with record_decisions 'decisions' (int8 [H*W][maxlen]) and with walk
+    'walk' (uint64 [H][W]: a hash of the Gaussians each pixel composited, in order, and the one
+    that stopped it)."""
     proj = _f64(proj)
     n = proj.shape[1]
     vals = np.ascontiguousarray(vals, np.uint32)
@@ -192,10 +205,13 @@ def render_forward(proj, vals, rng, W, H, bg=(0.0, 0.0, 0.0), margins=None,
         stride = dec.shape[1]
         mode = 2
     vals_arg = vals if vals.size else np.zeros(1, np.uint32)
+    wh = np.zeros((H, W), np.uint64) if walk else None
     lib().or_render_forward(W, H, _p(bgv), n, _p(proj), _p(vals_arg), _p(rng), _p(img), _p(Tf),
-                            _p(last), _p(ex), _p(bl), _p(nb), _p(mg), _p(dec), stride, mode)
+                            _p(last), _p(ex), _p(bl), _p(nb), _p(mg), _p(dec), stride, mode, _p(wh))
     out = dict(image=img, T_final=Tf, last_contrib=last, n_examined=ex, borderline=bl.astype(bool),
                n_blended=nb)
+    if walk:
+        out["walk"] = wh
     if record_decisions:
         out["decisions"] = dec
     return out

@@ -38,6 +38,7 @@
  *   radii int32 [2][n]; tiles uint32 [n].  A culled Gaussian has all of these 0.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -64,6 +65,10 @@
 #define GUARD 1.3                    /* guard band for x/z, y/z inside the Jacobian     */
 
 int or_rows_for_degree(int d) { return 11 + 3 * (d + 1) * (d + 1); }
+
+/* The OpenMP threads of the embarrassingly parallel loops below (timing runs set them). */
+void or_set_num_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+int or_get_max_threads(void) { return omp_get_max_threads(); }
 
 /* ------------------------------------------------------------------------------------ */
 /* camera                                                                               */
@@ -507,14 +512,30 @@ typedef struct {
   double margin_power;  /* absolute margin above 0 */
 } margins_t;
 
+/* A running hash of the branch sequence a pixel's walk takes (FNV-1a over 64-bit words): the
+ * index of every composited entry in order, then the index of the entry that stopped the walk
+ * (flagged by the top bit) or nothing when the list ran out.  Two walks hash equal exactly when
+ * (up to hash collisions) they composited the same Gaussians in the same order and stopped at the
+ * same one.  Instrumentation only: it takes no part in the blend. */
+static uint64_t walk_hash(uint64_t h, uint64_t word) {
+  for (int b = 0; b < 8; b++) {
+    h ^= (word >> (8 * b)) & 0xffu;
+    h *= 0x100000001b3ull;
+  }
+  return h;
+}
+#define WALK_HASH_SEED 0xcbf29ce484222325ull
+
 /* Blends pixel (px, py) over the list vals[start..end).  Writes the colour, the final
  * transmittance and the 1-based positions of the last blended / last examined entry.  If
- * `out` is non-null the composited entries are appended to it (size >= end-start). */
+ * `out` is non-null the composited entries are appended to it (size >= end-start); if `hash`
+ * is non-null it receives the walk's hash (walk_hash). */
 static void blend_pixel(int px, int py, const double* proj, int64_t n, const uint32_t* vals,
                         uint32_t start, uint32_t end, const double bg[3], double C[3],
                         double* T_final, uint32_t* last_contrib, uint32_t* n_examined,
                         contrib_t* out, int* n_out, const margins_t* mg, int* borderline,
-                        int8_t* dec_out, const int8_t* dec_in) {
+                        int8_t* dec_out, const int8_t* dec_in, uint64_t* hash) {
+  uint64_t h = WALK_HASH_SEED;
   double T = 1.0;
   C[0] = C[1] = C[2] = 0.0;
   uint32_t last = 0, examined = end - start;
@@ -554,8 +575,10 @@ static void blend_pixel(int px, int py, const double* proj, int64_t n, const uin
     if (code == DEC_SKIP) continue;
     if (code == DEC_STOP) {
       examined = j - start + 1;
+      h = walk_hash(h, (uint64_t)i | 0x8000000000000000ull);
       break;
     }
+    h = walk_hash(h, (uint64_t)i);
     const int clamped = code == DEC_BLEND_CLAMPED;
     const double alpha = clamped ? ALPHA_MAX : oG;
     for (int ch = 0; ch < 3; ch++) C[ch] += proj[(PRJ_R + ch) * n + i] * alpha * T;
@@ -575,18 +598,19 @@ static void blend_pixel(int px, int py, const double* proj, int64_t n, const uin
   *n_examined = examined;
   if (n_out) *n_out = cnt;
   if (borderline) *borderline = flag;
+  if (hash) *hash = h;
 }
 
 /* Tiled forward render.  image [H][W][3], T_final [H][W], last_contrib [H][W],
  * n_examined [H][W], borderline [H][W] (uint8, nullable), n_blended [H][W] (nullable: the
- * entries composited into each pixel).  `dec` (nullable) is a
- * per-pixel array of decision codes with row stride `dec_stride`; with `dec_mode` = 1 the
- * codes are written, with 2 they are read instead of testing the thresholds. */
+ * entries composited into each pixel), walk [H][W] (nullable: each pixel's walk hash).  `dec`
+ * (nullable) is a per-pixel array of decision codes with row stride `dec_stride`; with
+ * `dec_mode` = 1 the codes are written, with 2 they are read instead of testing the thresholds. */
 int or_render_forward(int W, int H, const double* bg, int64_t n, const double* proj,
                       const uint32_t* vals, const uint32_t* ranges, double* image, double* T_final,
                       uint32_t* last_contrib, uint32_t* n_examined, uint8_t* borderline,
                       uint32_t* n_blended, const double* margins, int8_t* dec, int64_t dec_stride,
-                      int dec_mode) {
+                      int dec_mode, uint64_t* walk) {
   const int TX = (W + TILE - 1) / TILE;
   margins_t mg = {1e-4, 1e-4, 1e-6};
   if (margins) { mg.margin_alpha = margins[0]; mg.margin_T = margins[1]; mg.margin_power = margins[2]; }
@@ -599,7 +623,7 @@ int or_render_forward(int W, int H, const double* bg, int64_t n, const double* p
     int8_t* dp = dec ? dec + p * dec_stride : NULL;
     blend_pixel(px, py, proj, n, vals, ranges[2 * t], ranges[2 * t + 1], bg, C, &T_final[p],
                 &last_contrib[p], &n_examined[p], NULL, &cnt, &mg, &flag,
-                dec_mode == 1 ? dp : NULL, dec_mode == 2 ? dp : NULL);
+                dec_mode == 1 ? dp : NULL, dec_mode == 2 ? dp : NULL, walk ? &walk[p] : NULL);
     for (int ch = 0; ch < 3; ch++) image[3 * p + ch] = C[ch];
     if (borderline) borderline[p] = (uint8_t)flag;
     if (n_blended) n_blended[p] = (uint32_t)cnt;
@@ -639,7 +663,7 @@ int or_render_bruteforce(int W, int H, const double* bg, int64_t n, const double
     for (int64_t j = 0; j < m; j++) list[j] = (uint32_t)(order[j] & 0xffffffffu);
     double C[3];
     blend_pixel(px, py, proj, n, list, 0, (uint32_t)m, bg, C, &T_final[p], &last_contrib[p],
-                &n_examined[p], NULL, NULL, NULL, NULL, NULL, NULL);
+                &n_examined[p], NULL, NULL, NULL, NULL, NULL, NULL, NULL);
     for (int ch = 0; ch < 3; ch++) image[3 * p + ch] = C[ch];
   }
   (void)TY;
@@ -801,7 +825,7 @@ int or_render_backward(int W, int H, const double* bg, int64_t n, const double* 
     uint32_t last, ex;
     int cnt = 0;
     blend_pixel(px, py, proj, n, vals, ranges[2 * t], ranges[2 * t + 1], bg, C, &Tf, &last, &ex,
-                list, &cnt, NULL, NULL, NULL, dec ? dec + p * dec_stride : NULL);
+                list, &cnt, NULL, NULL, NULL, dec ? dec + p * dec_stride : NULL, NULL);
     const double* g = &dLdI[3 * p];
     const double bgg = bg[0] * g[0] + bg[1] * g[1] + bg[2] * g[2];
     /* suffix[k] = sum_{j >= k} alpha_j T_j (rgb_j . g) */
