@@ -62,36 +62,44 @@ def alg_bytes(phase, N, R, K, P, T, n_vis, batch=1):
     return 0
 
 
-# fp32 operations the method performs per (pixel, list entry) pair of the blends, counting
-# add, mul, compare, min and exp as one each:
-#   every evaluated pair: dx, dy (2), power -(A dx^2 + C dy^2)/2 - B dx dy (9), exp (1),
-#     o G (1), min with 0.99 (1), the power and 1/255 tests (2)                      = 16
+# fp32 operations per (pixel, list entry) pair of the blends, counting add, mul, compare, min
+# and exp as one each:
+#   an evaluated pair (alpha formed at the pixel): dx, dy (2), power -(A dx^2 + C dy^2)/2 -
+#     B dx dy (9), exp (1), o G (1), min with 0.99 (1), the power and 1/255 tests (2)  = 16
 #   a composited pair adds, forward: T (1 - alpha) and its test (3), alpha T (1), three
 #     colour FMAs (6)                                                                 = 10
-#   and backward: 1 - alpha, T / (1 - alpha) (3), alpha T (1), dL/dalpha (11), the three
-#     running colour sums (9), dL/drgb (3), dL/do and dL/dpower (2), dL/du, dL/dv (8),
-#     dL/dA, dL/dB, dL/dC (8), nine accumulations (9)                                 = 54
+#   and backward, which evaluates the pair again (16) and then: 1 - alpha, T / (1 - alpha)
+#     (3), alpha T (1), dL/dalpha (11), the three running colour sums (9), dL/drgb (3),
+#     dL/do and dL/dpower (2), dL/du, dL/dv (8), dL/dA, dL/dB, dL/dC (8), nine
+#     accumulations (9)                                                               = 54
+# The forward evaluates only the pairs whose record's conservative alpha box holds the pixel
+# (blend_count[3]); the examined pairs outside it are rejected without evaluating alpha, and
+# the backward evaluates only the composited pairs.  So the work credited per launch is
+#   16 x evaluated + 10 x composited (forward) + (16 + 54) x composited (backward).
 FLOPS_EVAL, FLOPS_FWD_BLEND, FLOPS_BWD_BLEND = 16, 10, 54
 # fp32 operations of the L1 + D-SSIM loss per (pixel, channel) value, 11-tap separable windows:
 #   five horizontal window sums (x, y, x^2, y^2, xy: 10 per tap) and five vertical ones (2 per
 #   tap and sum): 110 + 110; SSIM and its three partials: 40; the three partial maps summed
 #   horizontally and vertically: 66 + 66; the combination with x, y and the L1 sign: 8  = 400
 FLOPS_SSIM = 400
-# fp32 vector peak without packed-FP32 dual issue (the build turns packed FP32 off):
-# 256 CUs x 4 SIMDs x 16 lanes x 2 flops per FMA x 2.4 GHz
-ALU_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
+# MI355X's published fp32 vector peak (packed FP32 dual issue: 256 CUs x 4 SIMDs x 16 lanes x
+# 2 flops per FMA x 2 x 2.4 GHz); this library is built without packed FP32 instructions, so
+# half of it is the most its kernels can issue (reported beside it)
+ALU_PEAK_TFLOPS = 157.3
+ALU_PEAK_NONPACKED_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
 
 
-def alg_flops(phase, examined, walked, composited, ssim_values=0):
-    """Operations the method performs per launch in the two blend kernels (and the D-SSIM loss)."""
+def alg_flops(phase, examined, walked, composited, evaluated, ssim_values=0):
+    """Operations performed per launch in the two blend kernels (and the D-SSIM loss): the pairs
+    the kernels evaluate, not the examined pairs the box test rejects."""
     if phase == "loss":                # only the D-SSIM loss is counted (ssim_values = 3HW)
         return FLOPS_SSIM * ssim_values
-    if phase == "forward":             # walks n_examined entries per pixel
-        return FLOPS_EVAL * examined + FLOPS_FWD_BLEND * composited
-    if phase == "backward_blend":      # walks last_contrib entries per pixel, back to front
-        return FLOPS_EVAL * walked + FLOPS_BWD_BLEND * composited
+    if phase == "forward":
+        return FLOPS_EVAL * evaluated + FLOPS_FWD_BLEND * composited
+    if phase == "backward_blend":      # evaluates the composited pairs again, back to front
+        return (FLOPS_EVAL + FLOPS_BWD_BLEND) * composited
     if phase == "image_pass":          # both blends in the fused image pass
-        return sum(alg_flops(ph, examined, walked, composited) for ph in ("forward", "backward_blend"))
+        return sum(alg_flops(ph, examined, walked, composited, evaluated) for ph in ("forward", "backward_blend"))
     return 0
 
 
@@ -148,7 +156,7 @@ def render_targets(gsmi, torch, cfg, cams, tparams_np, targets, log_every=64):
             except gsmi.GsCapacityError as e:
                 buf.grow(int(e.required * 1.25) + 1024)
         gsmi.render_forward(c, n, buf.proj.splat, buf.vals, buf.ranges, (0.0, 0.0, 0.0), targets[vi], buf.T_final,
-                            buf.last, buf.render_ws)
+                            buf.last, buf.render_ws, k=K)
         ks.append(K)
         if vi % log_every == 0:
             log(f"  target view {vi}: K = {K}")
@@ -166,51 +174,70 @@ def tile_histogram(ranges_np):
             "log2_bins": {f"<{e}": h for e, h in zip(edges[1:] + ["inf"], hist)}}
 
 
-def cpu_baseline(cfg, params_np, cam, blends_full, crop=512):
-    """The CPU oracle (test infrastructure, untouched) on a bounded sample of one step:
-    every per-Gaussian stage over all N Gaussians (preprocess, preprocess backward, Adam) and
-    the per-pixel stages (bin/sort, ranges, forward, L1, backward blend) on a crop x crop
-    window at the image centre; the window's time is scaled by full-image blends / window
-    blends to one full step."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(cfg, params_np, cams, budget_s=30.0):
+    """The CPU oracle (test infrastructure, untouched) running whole steps of the same workload:
+    preprocess, bin/sort, forward, loss (L1 against a seeded uniform target, or the seeded upstream
+    dL/dI), backward blend, preprocess backward and Adam over every Gaussian and pixel.  Views in
+    the order 0, 112, 224, 336 of the orbit (every view of a smaller set; the single camera
+    repeated), until `budget_s` of oracle time is spent (at least one step).  Configurations of
+    at most 262,144 Gaussians are also timed on one thread."""
     import oracle
 
     oracle.build()
     threads = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+    oracle.set_num_threads(threads)
     deg, W = cfg.sh_degree, cfg.res
+    V = len(cams)
+    order = [0, 112, 224, 336] if V >= 448 else (list(range(V)) if V > 1 else [0] * 5)
+    order = [v for v in order if v < V]
     p64 = params_np.astype(np.float64)
-    c = cam.flat()
-    t0 = time.perf_counter()
-    oracle.preprocess(p64, deg, c, W, W)
-    t_pre = time.perf_counter() - t0
-    # the crop camera: same pose and focal length, principal point shifted to the window
-    off = (W - crop) / 2.0
-    cc = c.copy()
-    cc[14] -= off
-    cc[15] -= off
-    proj, radii, _ = oracle.preprocess(p64, deg, cc, crop, crop)
-    target = np.zeros((crop, crop, 3))
-    t0 = time.perf_counter()
-    keys, vals = oracle.bin_sort(proj, radii, crop, crop)
-    rg = oracle.ranges(keys, oracle.n_tiles(crop, crop))
-    fwd = oracle.render_forward(proj, vals, rg, crop, crop)
-    _, dLdI = oracle.loss_l1(fwd["image"], target)
-    g2 = oracle.render_backward(proj, vals, rg, crop, crop, dLdI)
-    t_pix = time.perf_counter() - t0
-    blends_crop = int(fwd["n_examined"].astype(np.int64).sum())
-    t0 = time.perf_counter()
-    grads = oracle.preprocess_backward(p64, deg, c, W, W, np.zeros((9, p64.shape[1])))
-    t_pb = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    oracle.adam(p64, grads, np.zeros_like(p64), np.zeros_like(p64), 1)
-    t_adam = time.perf_counter() - t0
-    scale = blends_full / max(blends_crop, 1)
-    sec = t_pre + t_pb + t_adam + t_pix * scale
-    sample = (f"all {p64.shape[1]} Gaussians for preprocess ({t_pre:.2f} s), preprocess backward "
-              f"({t_pb:.2f} s) and Adam ({t_adam:.2f} s); bin/sort/forward/L1/backward blend on the "
-              f"central {crop}x{crop} window of view 0 ({t_pix:.2f} s, {blends_crop} blends) scaled by "
-              f"{scale:.1f} to the full image's {blends_full} blends")
-    return {"value": blends_full / sec, "unit": "Gaussian-pixel blends/s", "cores": threads, "kind": "oracle",
-            "sample": sample, "ms_per_step": sec * 1e3}
+    up = inputs_mod().upstream_gradient(cfg, W, W).astype(np.float64) if cfg.loss == "upstream" else None
+    target = None if up is not None else np.random.default_rng(cfg.index).uniform(0, 1, (W, W, 3))
+
+    def run(nthreads, budget):
+        oracle.set_num_threads(nthreads)
+        times, blends, views = [], 0, []
+        for v in order:
+            t0 = time.perf_counter()
+            out = oracle.train_step_reference(p64, deg, cams[v].flat(), W, W, target=target, upstream=up,
+                                              m=np.zeros_like(p64), v=np.zeros_like(p64), t=1)
+            times.append(time.perf_counter() - t0)
+            blends += int(out["n_examined"].astype(np.int64).sum())
+            views.append(v)
+            del out
+            if sum(times) >= budget:
+                break
+        return times, blends, views
+
+    times, blends, views = run(threads, budget_s)
+    sec = sum(times)
+    res = {"value": blends / sec, "unit": "Gaussian-pixel blends/s", "cores": threads, "kind": "oracle",
+           "cpu_model": cpu_model(), "ms_per_step": round(1e3 * sec / len(times), 1),
+           "sample": (f"{len(times)} whole oracle steps (views {views} of {V}; every Gaussian and pixel; "
+                      f"{'seeded upstream dL/dI' if up is not None else 'L1 against a seeded uniform target'}; "
+                      f"Adam included) in {sec:.1f} s on {threads} OpenMP threads, time-boxed at {budget_s:.0f} s")}
+    if cfg.n <= 262144:
+        t1, b1, v1 = run(1, budget_s / 2)
+        res["single_thread"] = {"value": b1 / sum(t1), "ms_per_step": round(1e3 * sum(t1) / len(t1), 1),
+                                "steps": len(t1)}
+    oracle.set_num_threads(threads)
+    return res
+
+
+def inputs_mod():
+    from gaussian_splatting_differentiable_preprocess_amd import inputs
+    return inputs
 
 
 def gpu_state():
@@ -248,10 +275,13 @@ def copy_calibration(mib, reps=10):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=448)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: 200 for the 16K sphere -- 200 fwd+bwd repetitions -- and the "
+                         "262K torus -- its 8 views x 25 --, else one 448-view epoch)")
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="gyroid_4m_2048")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=30.0, help="seconds of oracle steps in the CPU baseline")
     ap.add_argument("--unfused-adam", action="store_true", help="separate Adam kernel instead of the fused one")
     ap.add_argument("--separate-passes", action="store_true",
                     help="forward, L1 loss and backward blend as three calls instead of the fused image pass")
@@ -288,23 +318,32 @@ def main():
     gsmi.load()
     torch.cuda.set_device(0)
     cfg = inputs.CONFIGS[args.config]
+    if args.steps is None:
+        args.steps = 200 if cfg.n <= 262144 else 448
+    upstream_mode = cfg.loss == "upstream"  # seeded dL/dI instead of a loss (the 16K sphere)
+    if upstream_mode and (args.dssim is not None or args.batch > 1 or args.densify):
+        raise SystemExit(f"{cfg.name} takes a seeded upstream dL/dI: no loss, batch or density control modes")
     W = H = cfg.res
     P = W * H
     T = gsmi.n_tiles(W, H)
     log(f"[bench] {cfg.name}: generating {cfg.n} Gaussians (scene) ...")
     t0 = time.time()
     params_np = inputs.gaussian_params(cfg)
-    log(f"[bench]   {time.time() - t0:.1f} s; target set ...")
-    tparams_np = inputs.gaussian_params(cfg, inputs.STREAM_TARGET)
     cams = inputs.cameras_for(cfg)
     if args.views:
         cams = cams[: args.views]
     V = len(cams)
     R, N = params_np.shape
-    log(f"[bench] rendering {V} target views at {W}x{H} ...")
-    targets = torch.empty((V, H, W, 3), dtype=torch.float32, device="cuda")
-    tks = render_targets(gsmi, torch, cfg, cams, tparams_np, targets)
-    del tparams_np
+    if upstream_mode:
+        up_t = torch.from_numpy(inputs.upstream_gradient(cfg, W, H)).cuda()
+        targets, tks = None, [3 * N]
+    else:
+        log(f"[bench]   {time.time() - t0:.1f} s; target set ...")
+        tparams_np = inputs.gaussian_params(cfg, inputs.STREAM_TARGET)
+        log(f"[bench] rendering {V} target views at {W}x{H} ...")
+        targets = torch.empty((V, H, W, 3), dtype=torch.float32, device="cuda")
+        tks = render_targets(gsmi, torch, cfg, cams, tparams_np, targets)
+        del tparams_np
 
     p = torch.from_numpy(params_np).cuda()
     m = torch.zeros_like(p)
@@ -316,9 +355,9 @@ def main():
         raise SystemExit("--batch accumulates in the fused preprocess backward; drop --unfused-adam")
     grads_acc = torch.empty_like(p) if args.batch > 1 else None
     gcams = [gsmi.make_camera(c) for c in cams]
-    blends = torch.zeros(3, dtype=torch.int64, device="cuda")
+    blends = torch.zeros(4, dtype=torch.int64, device="cuda")
     bg = (0.0, 0.0, 0.0)
-    fused = not args.separate_passes and args.dssim is None
+    fused = not args.separate_passes and args.dssim is None and not upstream_mode
     if args.densify and not fused:
         raise SystemExit("--densify reads the fused image pass's staged sums; drop --separate-passes / --dssim")
     dens_acc = torch.zeros(N, device="cuda") if args.densify else None
@@ -327,7 +366,8 @@ def main():
                 if args.dssim is not None else None)
     phases = (["preprocess", "bin_and_sort", "render_plan", "image_pass"] + (["densify_stats"] if args.densify else [])
               + ["prebwd_adam"] if fused else
-              ["preprocess", "bin_and_sort", "forward", "loss", "backward_blend", "prebwd_adam"])
+              ["preprocess", "bin_and_sort", "forward"] + ([] if upstream_mode else ["loss"]) +
+              ["backward_blend", "prebwd_adam"])
 
     def step(t, view, ev=None):
         cam = gcams[view]
@@ -345,25 +385,31 @@ def main():
         mark()
         g2 = buf.grad2d if args.unfused_adam else None
         if fused:  # forward, L1 and backward blend in one kernel; the sums stay staged
-            gsmi.render_plan(buf.scene, cam, buf.proj, buf.ranges, buf.render_ws)
+            gsmi.render_plan(buf.scene, cam, buf.proj, buf.ranges, buf.render_ws, k=K)
             mark()
             gsmi.render_step(buf.scene, cam, buf.proj, buf.vals, buf.ranges, bg, targets[view], buf.image,
-                             buf.T_final, buf.last, buf.loss, buf.dLdI, buf.render_ws, grad2d=g2, blend_count=blends)
+                             buf.T_final, buf.last, buf.loss, buf.dLdI, buf.render_ws, grad2d=g2, blend_count=blends,
+                             k=K)
             mark()
             if args.densify:
                 gsmi.densify_stats(buf.scene, cam, buf.proj, buf.render_ws, dens_acc, dens_cnt)
                 mark()
         else:
             gsmi.render_forward(cam, N, buf.proj.splat, buf.vals, buf.ranges, bg, buf.image, buf.T_final, buf.last,
-                                buf.render_ws, blend_count=blends)
+                                buf.render_ws, blend_count=blends, k=K)
             mark()
-            if args.dssim is not None:
+            if upstream_mode:
+                dl = up_t
+            elif args.dssim is not None:
                 gsmi.loss_l1_dssim(W, H, buf.image, targets[view], args.dssim, buf.loss, buf.dLdI, dssim_ws)
+                dl = buf.dLdI
+                mark()
             else:
                 gsmi.loss_l1(3 * P, buf.image, targets[view], buf.loss, buf.dLdI, buf.loss_ws)
-            mark()
+                dl = buf.dLdI
+                mark()
             gsmi.render_backward(buf.scene, None, cam, buf.proj, buf.vals, buf.ranges, bg, buf.T_final, buf.last,
-                                 buf.dLdI, g2, buf.render_ws)
+                                 dl, g2, buf.render_ws, k=K)
             mark()
         if args.batch > 1:  # t counts views; the optimizer steps once per batch
             j = (t - 1) % args.batch
@@ -399,6 +445,11 @@ def main():
         ks.append(step(t, (args.warmup + k) % V, evs[k]))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # the device-side checks of every timed step: a bounded wait that gave up, or lists that
+    # outgrew the workspace, would have left results incomplete
+    flags, need = gsmi.render_status(buf.render_ws, raise_error=False)
+    if flags:
+        raise SystemExit(f"render status flags {flags} (need {need} intersections): timed results not valid")
     total_blends = int(blends[0].item())
     ms_per_step = wall * 1e3 / args.steps
     ph_ms = {ph: float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)]))
@@ -411,29 +462,36 @@ def main():
     Kmean = float(np.mean(ks))
     n_vis = N
     sums = blends.cpu().tolist()
-    per_launch = [x / args.steps for x in sums]  # examined, walked, composited per view
+    per_launch = [x / args.steps for x in sums]  # examined, walked, composited, evaluated per view
     single = {ph: ph_ms[ph] for ph in KERNEL_OF if ph in ph_ms}
     dom = max(single, key=single.get)
     sec = ph_ms[dom] * 1e-3
     kname, bound = KERNEL_OF[dom]
+    traffic = counter_traffic(dom, cfg.name)
+    bytes_alg = alg_bytes(dom, N, R, Kmean, P, T, n_vis, args.batch)
     if bound == "alu":
         work = alg_flops(dom, *per_launch)
         achieved = work / sec / 1e12
-        roof = {"bound": "alu", "achieved": round(achieved, 2), "peak": round(ALU_PEAK_TFLOPS, 1),
-                "unit": "TFLOP/s", "frac": round(achieved / ALU_PEAK_TFLOPS, 4)}
+        roof = {"bound": "alu", "achieved": round(achieved, 2), "peak": ALU_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / ALU_PEAK_TFLOPS, 4),
+                "frac_of_nonpacked_peak": round(achieved / ALU_PEAK_NONPACKED_TFLOPS, 4)}
     else:
-        work = alg_bytes(dom, N, R, Kmean, P, T, n_vis, args.batch)
+        work = bytes_alg
         achieved = work / sec / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4)}
-    roof.update({"traffic": counter_traffic(dom, cfg.name), "kernel": kname, "work_per_launch": work,
-                 "ms_per_launch": round(ph_ms[dom], 4)})
+    roof.update({"traffic": traffic, "traffic_over_alg_bytes": round(traffic / bytes_alg, 2) if traffic else None,
+                 "kernel": kname, "work_per_launch": work, "ms_per_launch": round(ph_ms[dom], 4)})
     per_phase = {}
     for ph in phases:
         d = {"ms": round(ph_ms[ph], 4),
              "alg_GBps": round(alg_bytes(ph, N, R, Kmean, P, T, n_vis, args.batch) / (ph_ms[ph] * 1e-3) / 1e9, 1)}
         if ph in ("forward", "backward_blend", "image_pass") or (ph == "loss" and args.dssim is not None):
             d["alg_TFLOPs"] = round(alg_flops(ph, *per_launch, ssim_values=3 * P) / (ph_ms[ph] * 1e-3) / 1e12, 3)
+            if ph in ("forward", "image_pass"):  # every examined pair evaluated, as a plain walk would
+                d["examined_equiv_TFLOPs"] = round(
+                    alg_flops(ph, per_launch[0], per_launch[1], per_launch[2], per_launch[0]) /
+                    (ph_ms[ph] * 1e-3) / 1e12, 3)
         per_phase[ph] = d
     log(f"[bench] roofline: {json.dumps(roof)}")
     # per-step event time (first mark to last) over the timed views, and the pair rates
@@ -447,8 +505,8 @@ def main():
              "examined_pairs_per_s_of_" + blend_ph: per_launch[0] / (ph_ms[blend_ph] * 1e-3)}
     if not fused:
         rates["walked_pairs_per_s_of_backward_blend"] = per_launch[1] / (ph_ms["backward_blend"] * 1e-3)
-    log(f"[bench] per view: {per_launch[0]:.4g} examined, {per_launch[1]:.4g} walked back, "
-        f"{per_launch[2]:.4g} composited (pixel, entry) pairs")
+    log(f"[bench] per view: {per_launch[0]:.4g} examined, {per_launch[3]:.4g} evaluated, {per_launch[1]:.4g} walked "
+        f"back, {per_launch[2]:.4g} composited (pixel, entry) pairs")
 
     dens = None
     if args.densify:  # one clone / split / prune pass over the statistics of the timed steps
@@ -476,31 +534,30 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        log("[bench] CPU oracle baseline on a bounded sample ...")
-        view = 0
-        blends.zero_()
-        step(t + 1, view)  # one untimed step to count view 0's blends at full resolution
-        torch.cuda.synchronize()
-        cpu = cpu_baseline(cfg, params_np, cams[view], int(blends[0].item()))
-        log(f"[bench] CPU oracle: {cpu['ms_per_step']:.0f} ms/step-equivalent on {cpu['cores']} threads")
+        log("[bench] CPU oracle baseline: whole steps, time-boxed ...")
+        cpu = cpu_baseline(cfg, params_np, cams, budget_s=args.cpu_budget)
+        log(f"[bench] CPU oracle: {cpu['ms_per_step']:.0f} ms/step on {cpu['cores']} threads ({cpu['sample']})")
 
     out = {
         "metric": METRIC, "value": total_blends / wall, "unit": "Gaussian-pixel blends/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": cfg.name, "gaussians": N, "sh_degree": cfg.sh_degree, "resolution": [W, H],
-                   "views": V, "loss": "l1" if args.dssim is None else f"l1+dssim(lambda={args.dssim})", "adam": "fused" if not args.unfused_adam else "separate", "batch": args.batch,
+                   "views": V, "loss": ("seeded upstream dL/dI" if upstream_mode else "l1" if args.dssim is None
+                                        else f"l1+dssim(lambda={args.dssim})"),
+                   "adam": "fused" if not args.unfused_adam else "separate", "batch": args.batch,
                    "image_pass": "fused" if fused else "separate",
                    "intersections_mean": round(Kmean), "intersections_min": int(min(ks)),
                    "intersections_max": int(max(ks))},
         "roofline": roof,
         "cpu_baseline": cpu,
+        "render_status_flags": flags,
     }
     if args.detail:
         with open(args.detail, "w") as f:
             json.dump(dict(out, per_phase=per_phase, step_event_ms=step_stats, pair_rates=rates,
                            pairs_per_view={"examined": per_launch[0], "walked": per_launch[1],
-                                           "composited": per_launch[2]},
+                                           "composited": per_launch[2], "evaluated": per_launch[3]},
                            tile_list_lengths=hist, target_K=tks, densify=dens, gpu_state=gpu_state()), f, indent=1)
     print(json.dumps(out), flush=True)
 

@@ -271,9 +271,11 @@ constexpr int kPlanThreads = 1024;
 constexpr int kLenClasses = 33;
 __device__ __forceinline__ int len_class(uint32_t len) { return len ? 32 - __clz((int)len) : 0; }
 constexpr int kShifts = 32 - kSegShiftMin;  // candidate shifts kSegShiftMin .. 31
-// per-block partial sums: slots(shift), long tiles(shift), non-empty tiles, class counts
+// per-block partial sums: slots(shift), long tiles(shift), non-empty tiles, class counts, and the
+// largest list end (a maximum, not a sum)
 constexpr int kPartSlots = 0, kPartLong = kShifts, kPartNonEmpty = 2 * kShifts, kPartClass = 2 * kShifts + 1;
-constexpr int kPartVals = kPartClass + kLenClasses;
+constexpr int kPartMaxEnd = kPartClass + kLenClasses;
+constexpr int kPartVals = kPartMaxEnd + 1;
 // per-block offsets: slots, items, then each class's first position in the order
 constexpr int kOffVals = 2 + kLenClasses;
 
@@ -302,12 +304,16 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_count(const uint2* __rest
                                                              uint32_t* __restrict__ part) {
   __shared__ uint32_t red[kPlanThreads / 64][2 * kShifts + 1];
   __shared__ uint32_t cls[kLenClasses];
+  __shared__ uint32_t emax[kPlanThreads / 64];
   const int t = (int)(blockIdx.x * kPlanThreads + threadIdx.x), w = threadIdx.x >> 6;
-  uint32_t len = 0;
+  uint32_t len = 0, end = 0;
   if (t < T) {
     const uint2 rg = ranges[t];
     len = rg.y - rg.x;
+    end = rg.y;
   }
+  for (int o = 32; o > 0; o >>= 1) end = max(end, (uint32_t)__shfl_xor(end, o, 64));
+  if ((threadIdx.x & 63) == 0) emax[w] = end;
   if (threadIdx.x < kLenClasses) cls[threadIdx.x] = 0u;
   __syncthreads();
   if (t < T) atomicAdd(&cls[len_class(len)], 1u);
@@ -328,23 +334,35 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_count(const uint2* __rest
     uint32_t v = 0;
     for (int k = 0; k < kPlanThreads / 64; ++k) v += red[k][threadIdx.x];
     out[threadIdx.x] = v;
-  } else if (threadIdx.x < kPartVals) {
+  } else if (threadIdx.x < kPartMaxEnd) {
     out[threadIdx.x] = cls[threadIdx.x - kPartClass];
+  } else if (threadIdx.x == kPartMaxEnd) {
+    uint32_t v = 0;
+    for (int k = 0; k < kPlanThreads / 64; ++k) v = max(v, emax[k]);
+    out[threadIdx.x] = v;
   }
 }
 
 // One workgroup: the shift, the header, bnd_off[T] / item_off[T] and the per-block offsets.
+// The lists need room for their largest end: a workspace that holds fewer intersections sets the
+// capacity flag (the kernels then stay inside the workspace and the results are not valid).  The
+// status words are not cleared here: they gather the flags of every call until read.
 __global__ __launch_bounds__(kPlanThreads) void k_plan_scan(const uint32_t* __restrict__ part, int nb, int T,
-                                                            uint32_t slots_cap, uint32_t* __restrict__ off,
+                                                            uint32_t slots_cap, uint64_t entries_cap,
+                                                            uint32_t* __restrict__ off,
                                                             uint32_t* __restrict__ hdr,
                                                             uint32_t* __restrict__ bnd_off,
                                                             uint32_t* __restrict__ item_off) {
   __shared__ uint32_t tot[kPartVals];
   __shared__ uint32_t cbase[kLenClasses];
   __shared__ int s_q;
-  if (threadIdx.x < kPartVals) {
+  if (threadIdx.x < kPartMaxEnd) {
     uint32_t v = 0;
     for (int b = 0; b < nb; ++b) v += part[(size_t)b * kPartVals + threadIdx.x];
+    tot[threadIdx.x] = v;
+  } else if (threadIdx.x == kPartMaxEnd) {
+    uint32_t v = 0;
+    for (int b = 0; b < nb; ++b) v = max(v, part[(size_t)b * kPartVals + threadIdx.x]);
     tot[threadIdx.x] = v;
   }
   __syncthreads();
@@ -368,7 +386,10 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_scan(const uint32_t* __re
     hdr[kHdrFwdNext] = 0u;
     hdr[kHdrReady] = 0u;
     hdr[kHdrRole] = 0u;
-    hdr[kHdrStall] = 0u;
+    if ((uint64_t)tot[kPartMaxEnd] > entries_cap) {
+      hdr[kHdrFlags] |= kFlagCapacity;
+      hdr[kHdrNeed] = max(hdr[kHdrNeed], tot[kPartMaxEnd]);
+    }
   }
   __syncthreads();
   const int q = s_q;
@@ -491,6 +512,7 @@ __device__ void forward_tile(const FwdArgs& a, uint32_t shift, int tile, Chunk* 
 
   float Tr = 1.0f, c0 = 0.f, c1 = 0.f, c2 = 0.f;
   uint32_t last = 0, examined = len, blended = 0;
+  uint32_t evaluated = 0;  // (pixel, entry) pairs whose alpha is evaluated: the mask bits walked
   bool done = !inside;
 
   if (len > 0) {
@@ -517,6 +539,7 @@ __device__ void forward_tile(const FwdArgs& a, uint32_t shift, int tile, Chunk* 
       // every lane takes part in the ballots: lane e holds record e's box
       unsigned long long m = lane_mask(bx, lx, ly);
       if (done) m = 0ull;
+      evaluated += (uint32_t)__popcll(m);
       wave_sync_lds();
       const uint32_t base = rel + 1u;  // 1-based position of slot 0
       unsigned long long cm = 0ull;    // the chunk's entries composited at this pixel
@@ -535,6 +558,7 @@ __device__ void forward_tile(const FwdArgs& a, uint32_t shift, int tile, Chunk* 
           if (Tn < kTMin) {
             done = true;
             examined = pos;
+            evaluated -= (uint32_t)__popcll(m);  // the entries behind the stop are not evaluated
             m = 0ull;
           } else {
             const float wt = alpha * Tr;
@@ -586,22 +610,24 @@ __device__ void forward_tile(const FwdArgs& a, uint32_t shift, int tile, Chunk* 
     if (tid == 0) a.loss_part[tile] = (lpart[0] + lpart[1]) + (lpart[2] + lpart[3]);
   }
   if (a.blend_count) {
-    unsigned long long ex = inside ? examined : 0u, lc = last, bl = blended;
+    unsigned long long ex = inside ? examined : 0u, lc = last, bl = blended, ev = evaluated;
     for (int o = 32; o > 0; o >>= 1) {
       ex += __shfl_xor(ex, o, 64);
       lc += __shfl_xor(lc, o, 64);
       bl += __shfl_xor(bl, o, 64);
+      ev += __shfl_xor(ev, o, 64);
     }
     // one atomic per counter and non-empty tile: same-address atomics from every wave of
     // the image serialise and would cost more than the blending of a light view
-    __shared__ unsigned long long part[3][4];
+    __shared__ unsigned long long part[4][4];
     if (lane == 0) {
       part[0][w] = ex;
       part[1][w] = lc;
       part[2][w] = bl;
+      part[3][w] = ev;
     }
     __syncthreads();
-    if (tid < 3) {
+    if (tid < 4) {
       const unsigned long long x = (part[tid][0] + part[tid][1]) + (part[tid][2] + part[tid][3]);
       if (x != 0ull) atomicAdd(a.blend_count + tid, x);
     }
@@ -930,7 +956,7 @@ __global__ __launch_bounds__(kBlock) void k_blend_step(FwdArgs fa, BwdArgs ba, u
           it = get_u2<true>(items + b);
           if (it.x != kNoTile) break;
           if (spin == kSpinLimit) {
-            atomicOr(hdr + kHdrStall, 1u);
+            atomicOr(hdr + kHdrFlags, kFlagStall);
             break;
           }
           __builtin_amdgcn_s_sleep(4);
@@ -988,9 +1014,10 @@ __global__ __launch_bounds__(kBlock) void k_goff_local(int64_t n, const uint32_t
   if (threadIdx.x == 0) blk[blockIdx.x] = run;  // the block's total
 }
 
-// exclusive scan of the nblk block totals in place (one workgroup); total entries -> header
+// exclusive scan of the nblk block totals in place (one workgroup); total entries -> header, and
+// the capacity flag when the staging area holds fewer
 __global__ __launch_bounds__(kPlanThreads) void k_goff_blocks(int64_t nblk, uint32_t* __restrict__ blk,
-                                                              uint32_t* __restrict__ hdr) {
+                                                              uint32_t* __restrict__ hdr, uint64_t entries_cap) {
   __shared__ uint32_t red32[kPlanThreads / 64];
   const int64_t per = (nblk + kPlanThreads - 1) / kPlanThreads;
   const int64_t lo = std::min<int64_t>(nblk, (int64_t)threadIdx.x * per), hi = std::min<int64_t>(nblk, lo + per);
@@ -1002,7 +1029,13 @@ __global__ __launch_bounds__(kPlanThreads) void k_goff_blocks(int64_t nblk, uint
     blk[b] = run;
     run += x;
   }
-  if (threadIdx.x == kPlanThreads - 1) hdr[kHdrEntries] = run;  // the last thread's end is the total
+  if (threadIdx.x == kPlanThreads - 1) {  // the last thread's end is the total
+    hdr[kHdrEntries] = run;
+    if ((uint64_t)run > entries_cap) {
+      hdr[kHdrFlags] |= kFlagCapacity;
+      hdr[kHdrNeed] = max(hdr[kHdrNeed], run);
+    }
+  }
 }
 
 // staging[0 .. 9 * entries) = 0; entries from the header, capped at the workspace's capacity
@@ -1142,7 +1175,7 @@ void launch_plan(int T, const uint2* rg, const RenderWs& ws, bool empty_items, h
   const int nb = (int)ceil_div(T, kPlanThreads);
   hipLaunchKernelGGL(k_plan_count, dim3((unsigned)nb), dim3(kPlanThreads), 0, s, rg, T, ws.plan_part);
   hipLaunchKernelGGL(k_plan_scan, dim3(1), dim3(kPlanThreads), 0, s, (const uint32_t*)ws.plan_part, nb, T,
-                     ws.slots_cap, ws.plan_off, ws.hdr, ws.bnd_off, ws.item_off);
+                     ws.slots_cap, (uint64_t)ws.staging_cap, ws.plan_off, ws.hdr, ws.bnd_off, ws.item_off);
   hipLaunchKernelGGL(k_plan_write, dim3((unsigned)nb), dim3(kPlanThreads), 0, s, rg, T,
                      (const uint32_t*)ws.plan_off, (const uint32_t*)ws.hdr, ws.bnd_off, ws.item_off, ws.order);
   hipLaunchKernelGGL(k_seg_items, dim3((unsigned)ceil_div(T, kBlock / 64)), dim3(kBlock), 0, s, T,
@@ -1153,7 +1186,8 @@ void launch_plan(int T, const uint2* rg, const RenderWs& ws, bool empty_items, h
 void launch_staging(int64_t n, const uint32_t* tiles, const RenderWs& ws, hipStream_t s) {
   const size_t nblk = n_goff_blocks(n);
   hipLaunchKernelGGL(k_goff_local, dim3((unsigned)nblk), dim3(kBlock), 0, s, n, tiles, ws.goff, ws.goff_blk);
-  hipLaunchKernelGGL(k_goff_blocks, dim3(1), dim3(kPlanThreads), 0, s, (int64_t)nblk, ws.goff_blk, ws.hdr);
+  hipLaunchKernelGGL(k_goff_blocks, dim3(1), dim3(kPlanThreads), 0, s, (int64_t)nblk, ws.goff_blk, ws.hdr,
+                     (uint64_t)ws.staging_cap);
   const unsigned fill_grid = (unsigned)std::max(1, cu_count() * 8);
   hipLaunchKernelGGL(k_clear_staging, dim3(fill_grid), dim3(kBlock), 0, s, (const uint32_t*)ws.hdr,
                      reinterpret_cast<float4*>(ws.staging), ws.staging_cap);

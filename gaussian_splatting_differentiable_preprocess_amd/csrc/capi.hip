@@ -94,9 +94,32 @@ int64_t n_tiles(const gs_camera& c) {
   return (int64_t)((c.width + GS_TILE - 1) / GS_TILE) * ((c.height + GS_TILE - 1) / GS_TILE);
 }
 
+// k intersections must fit the render workspace's capacity; the message names the size that fits
+int check_render_capacity(const gs_camera& c, int64_t n, int64_t k, const gsmi::RenderWs& ws, size_t bytes) {
+  if (k < 0 || k > 4294967295LL) return fail(GS_ERR_INVALID_ARGUMENT, "k = %lld out of range", (long long)k);
+  if ((uint64_t)k > ws.staging_cap) {
+    const size_t need = gsmi::render_ws_bytes((int)n_tiles(c), n, k);
+    return fail(GS_ERR_CAPACITY, "render workspace of %zu bytes holds %llu intersections, %lld given: it needs %zu bytes",
+                bytes, (unsigned long long)ws.staging_cap, (long long)k, need);
+  }
+  return GS_OK;
+}
+
 }  // namespace
 
 namespace gsmi {
+
+int fail_status(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok_status() { return ok(); }
+
+int hip_status(hipError_t e, const char* where) { return hip_fail(e, where); }
 
 CamK make_cam(const gs_camera& c) {
   CamK k{};
@@ -197,7 +220,7 @@ int gs_render_workspace_capacity(int32_t width, int32_t height, int64_t n, size_
 }
 
 int gs_render_forward(const gs_camera* cam, int64_t n, const gs_splat* splat, const uint32_t* vals,
-                      const uint32_t* ranges, const float* bg, float* image, float* T_final,
+                      const uint32_t* ranges, int64_t k, const float* bg, float* image, float* T_final,
                       uint32_t* last_contrib, uint32_t* n_examined, uint64_t* blend_count,
                       void* render_ws, size_t render_ws_bytes, hipStream_t stream) {
   int st;
@@ -208,6 +231,7 @@ int gs_render_forward(const gs_camera* cam, int64_t n, const gs_splat* splat, co
   RenderWs ws;
   if (!render_ws_layout(render_ws, render_ws_bytes, (int)n_tiles(*cam), n, &ws))
     return fail(GS_ERR_INVALID_ARGUMENT, "render workspace too small or not 256-byte aligned");
+  if ((st = check_render_capacity(*cam, n, k, ws, render_ws_bytes))) return st;
   if (!aligned16(splat)) return fail(GS_ERR_INVALID_ARGUMENT, "splat must be 16-byte aligned");
   if (reinterpret_cast<uintptr_t>(ranges) & 7u) return fail(GS_ERR_INVALID_ARGUMENT, "ranges must be 8-byte aligned");
   if (!(finite(bg[0]) && finite(bg[1]) && finite(bg[2]))) return fail(GS_ERR_INVALID_ARGUMENT, "bg not finite");
@@ -434,7 +458,7 @@ int gs_densify(const gs_scene* scene, const float* params, const float* m, const
 }
 
 int gs_render_backward(const gs_scene* scene, float* params, const gs_camera* cam, gs_proj proj,
-                       const uint32_t* vals, const uint32_t* ranges, const float* bg,
+                       const uint32_t* vals, const uint32_t* ranges, int64_t k, const float* bg,
                        const float* T_final, const uint32_t* last_contrib, const float* dL_dimage,
                        float* grad2d, float* grads, const gs_adam* adam, void* render_ws,
                        size_t render_ws_bytes, hipStream_t stream) {
@@ -447,6 +471,7 @@ int gs_render_backward(const gs_scene* scene, float* params, const gs_camera* ca
   RenderWs ws;
   if (!render_ws_layout(render_ws, render_ws_bytes, (int)n_tiles(*cam), scene->n, &ws))
     return fail(GS_ERR_INVALID_ARGUMENT, "render workspace too small or not 256-byte aligned");
+  if ((st = check_render_capacity(*cam, scene->n, k, ws, render_ws_bytes))) return st;
   if (scene->n > 0 && !proj.tiles) return fail(GS_ERR_INVALID_ARGUMENT, "proj.tiles is null");
   if (scene->n > 0 && (grads || adam) && !params) return fail(GS_ERR_INVALID_ARGUMENT, "params is null");
   if (reinterpret_cast<uintptr_t>(ranges) & 7u) return fail(GS_ERR_INVALID_ARGUMENT, "ranges must be 8-byte aligned");
@@ -460,7 +485,7 @@ int gs_render_backward(const gs_scene* scene, float* params, const gs_camera* ca
                                  "gs_render_backward (preprocess backward)");
 }
 
-int gs_render_plan(const gs_scene* scene, const gs_camera* cam, gs_proj proj, const uint32_t* ranges,
+int gs_render_plan(const gs_scene* scene, const gs_camera* cam, gs_proj proj, const uint32_t* ranges, int64_t k,
                    void* render_ws, size_t render_ws_bytes, hipStream_t stream) {
   int st;
   if ((st = check_scene(scene)) || (st = check_camera(cam))) return st;
@@ -469,13 +494,14 @@ int gs_render_plan(const gs_scene* scene, const gs_camera* cam, gs_proj proj, co
   RenderWs ws;
   if (!render_ws_layout(render_ws, render_ws_bytes, (int)n_tiles(*cam), scene->n, &ws))
     return fail(GS_ERR_INVALID_ARGUMENT, "render workspace too small or not 256-byte aligned");
+  if ((st = check_render_capacity(*cam, scene->n, k, ws, render_ws_bytes))) return st;
   if (reinterpret_cast<uintptr_t>(ranges) & 7u) return fail(GS_ERR_INVALID_ARGUMENT, "ranges must be 8-byte aligned");
   const hipError_t e = launch_step_plan(make_cam(*cam), scene->n, proj.tiles, ranges, ws, stream);
   return e == hipSuccess ? ok() : hip_fail(e, "gs_render_plan");
 }
 
 int gs_render_step(const gs_scene* scene, const gs_camera* cam, gs_proj proj, const uint32_t* vals,
-                   const uint32_t* ranges, const float* bg, const float* target, float* image,
+                   const uint32_t* ranges, int64_t k, const float* bg, const float* target, float* image,
                    float* T_final, uint32_t* last_contrib, uint32_t* n_examined, uint64_t* blend_count,
                    float* loss, float* dL_dimage, float* grad2d, void* render_ws, size_t render_ws_bytes,
                    hipStream_t stream) {
@@ -488,12 +514,45 @@ int gs_render_step(const gs_scene* scene, const gs_camera* cam, gs_proj proj, co
   RenderWs ws;
   if (!render_ws_layout(render_ws, render_ws_bytes, (int)n_tiles(*cam), scene->n, &ws))
     return fail(GS_ERR_INVALID_ARGUMENT, "render workspace too small or not 256-byte aligned");
+  if ((st = check_render_capacity(*cam, scene->n, k, ws, render_ws_bytes))) return st;
   if (reinterpret_cast<uintptr_t>(ranges) & 7u) return fail(GS_ERR_INVALID_ARGUMENT, "ranges must be 8-byte aligned");
   if (!(finite(bg[0]) && finite(bg[1]) && finite(bg[2]))) return fail(GS_ERR_INVALID_ARGUMENT, "bg not finite");
   const hipError_t e = launch_blend_step(make_cam(*cam), scene->n, proj.splat, proj.tiles, vals, ranges, bg[0],
                                          bg[1], bg[2], target, image, T_final, last_contrib, n_examined,
                                          blend_count, loss, dL_dimage, grad2d, ws, stream);
   return e == hipSuccess ? ok() : hip_fail(e, "gs_render_step");
+}
+
+int gs_render_init(void* render_ws, size_t render_ws_bytes, hipStream_t stream) {
+  if (!render_ws) return fail(GS_ERR_INVALID_ARGUMENT, "render_ws is null");
+  if (render_ws_bytes < 256 || (reinterpret_cast<uintptr_t>(render_ws) & 255u))
+    return fail(GS_ERR_INVALID_ARGUMENT, "render workspace too small or not 256-byte aligned");
+  const hipError_t e = launch_fill_u32(static_cast<uint32_t*>(render_ws), kHdrStatusWords, 0u, stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "gs_render_init");
+}
+
+int gs_render_status(void* render_ws, size_t render_ws_bytes, uint32_t* flags, int64_t* required,
+                     hipStream_t stream) {
+  if (flags) *flags = 0u;
+  if (required) *required = 0;
+  if (!render_ws) return fail(GS_ERR_INVALID_ARGUMENT, "render_ws is null");
+  if (render_ws_bytes < 256 || (reinterpret_cast<uintptr_t>(render_ws) & 255u))
+    return fail(GS_ERR_INVALID_ARGUMENT, "render workspace too small or not 256-byte aligned");
+  uint32_t hdr[kHdrStatusWords];
+  hipError_t e = hipMemcpyAsync(hdr, render_ws, sizeof(hdr), hipMemcpyDeviceToHost, stream);
+  // read, then clear the status words (a fill kernel, ordered after the copy on the stream)
+  if (e == hipSuccess) e = launch_fill_u32(static_cast<uint32_t*>(render_ws) + kHdrFlags, 2, 0u, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "gs_render_status");
+  const uint32_t f = hdr[kHdrFlags];
+  if (flags) *flags = f;
+  if (required) *required = (int64_t)hdr[kHdrNeed];
+  if (f & kFlagCapacity)
+    return fail(GS_ERR_CAPACITY, "the lists need %u intersections, more than the render workspace holds: its "
+                "results are not valid", hdr[kHdrNeed]);
+  if (f & kFlagStall)
+    return fail(GS_ERR_INCOMPLETE, "a bounded wait of the fused image pass gave up: some gradient sums are missing");
+  return ok();
 }
 
 int gs_adam_step(int64_t count, float* params, const float* grads, const gs_adam* adam, hipStream_t stream) {

@@ -129,7 +129,11 @@ constexpr int kHdrEntries = 4;  // staged entries (sum of tiles)
 constexpr int kHdrFwdNext = 5;  // next tile of the forward (counter)
 constexpr int kHdrReady = 6;    // fused step: work items published so far
 constexpr int kHdrRole = 7;     // fused step: workgroups started so far
-constexpr int kHdrStall = 8;    // fused step: nonzero if a workgroup gave up waiting for an item
+constexpr int kHdrFlags = 8;    // status bits (kFlag* below): set by the kernels, kept until read
+constexpr int kHdrNeed = 9;     // the most intersections lists needed (largest list end, or staged entries)
+constexpr int kHdrStatusWords = 16;  // header words gs_render_init clears
+constexpr uint32_t kFlagStall = 1u;     // fused step: a workgroup gave up waiting for a work item
+constexpr uint32_t kFlagCapacity = 2u;  // the lists need more intersections than the workspace holds
 constexpr int kGoffBlock = 4096;
 struct RenderWs {
   uint32_t* hdr;
@@ -216,5 +220,11 @@ hipError_t launch_adam(int64_t count, float* params, const float* grads, float* 
                        const AdamCoef& c, hipStream_t s);
 
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// The C ABI's error reporting (capi.hip): sets the calling thread's message and returns `code`;
+// ok_status() clears it and returns GS_OK; hip_status() reports a failed HIP call.
+int fail_status(int code, const char* fmt, ...);
+int ok_status();
+int hip_status(hipError_t e, const char* where);
 
 }  // namespace gsmi

@@ -17,7 +17,9 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 # the in-tree build; GSMI_LIBRARY selects another build of the same ABI
 LIB_PATH = os.environ.get("GSMI_LIBRARY", os.path.join(_PKG, "libgsmi.so"))
 
-GS_OK, GS_ERR_INVALID_ARGUMENT, GS_ERR_CAPACITY, GS_ERR_HIP, GS_ERR_UNSUPPORTED = 0, -1, -2, -3, -4
+GS_OK, GS_ERR_INVALID_ARGUMENT, GS_ERR_CAPACITY, GS_ERR_HIP, GS_ERR_UNSUPPORTED, GS_ERR_INCOMPLETE = 0, -1, -2, -3, -4, -5
+# bits of gs_render_status's flags
+RENDER_FLAG_STALL, RENDER_FLAG_CAPACITY = 1, 2
 TILE = 16
 SPLAT_FLOATS = 12  # 48-byte record: u, v, radius_x, radius_y | A, B, C, opacity | r, g, b, depth
 
@@ -25,7 +27,7 @@ EXPORTS = (
     "gs_version", "gs_last_error", "gs_preprocess", "gs_bin_and_sort_workspace", "gs_bin_and_sort",
     "gs_render_workspace", "gs_render_workspace_capacity", "gs_render_forward", "gs_loss_l1_workspace", "gs_loss_l1",
     "gs_loss_l1_dssim_workspace", "gs_loss_l1_dssim", "gs_render_backward",
-    "gs_render_plan", "gs_render_step", "gs_preprocess_backward", "gs_preprocess_backward_staged", "gs_adam_step",
+    "gs_render_plan", "gs_render_step", "gs_render_init", "gs_render_status", "gs_preprocess_backward", "gs_preprocess_backward_staged", "gs_adam_step",
     "gs_preprocess_backward_accumulate", "gs_adam_batch", "gs_densify_stats", "gs_densify_workspace", "gs_densify",
 )
 
@@ -94,16 +96,18 @@ def load(path: str = LIB_PATH):
     L.gs_bin_and_sort.argtypes = [SP, CP, GsProj, P, sz, i64, P, P, P, ctypes.POINTER(i64), P]
     L.gs_render_workspace.argtypes = [i32, i32, i64, i64, ctypes.POINTER(sz)]
     L.gs_render_workspace_capacity.argtypes = [i32, i32, i64, sz, ctypes.POINTER(i64)]
-    L.gs_render_forward.argtypes = [CP, i64, P, P, P, ctypes.POINTER(ctypes.c_float), P, P, P, P, P, P, sz, P]
+    L.gs_render_forward.argtypes = [CP, i64, P, P, P, i64, ctypes.POINTER(ctypes.c_float), P, P, P, P, P, P, sz, P]
     L.gs_loss_l1_workspace.argtypes = [i64, ctypes.POINTER(sz)]
     L.gs_loss_l1.argtypes = [i64, P, P, P, P, P, sz, P]
     L.gs_loss_l1_dssim_workspace.argtypes = [i32, i32, ctypes.POINTER(sz)]
     L.gs_loss_l1_dssim.argtypes = [i32, i32, P, P, ctypes.c_float, P, P, P, sz, P]
-    L.gs_render_backward.argtypes = [SP, P, CP, GsProj, P, P, ctypes.POINTER(ctypes.c_float), P, P, P,
+    L.gs_render_backward.argtypes = [SP, P, CP, GsProj, P, P, i64, ctypes.POINTER(ctypes.c_float), P, P, P,
                                      P, P, AP, P, sz, P]
-    L.gs_render_plan.argtypes = [SP, CP, GsProj, P, P, sz, P]
-    L.gs_render_step.argtypes = [SP, CP, GsProj, P, P, ctypes.POINTER(ctypes.c_float), P, P, P, P, P, P, P, P, P, P,
-                                 sz, P]
+    L.gs_render_plan.argtypes = [SP, CP, GsProj, P, i64, P, sz, P]
+    L.gs_render_step.argtypes = [SP, CP, GsProj, P, P, i64, ctypes.POINTER(ctypes.c_float), P, P, P, P, P, P, P, P, P,
+                                 P, sz, P]
+    L.gs_render_init.argtypes = [P, sz, P]
+    L.gs_render_status.argtypes = [P, sz, ctypes.POINTER(ctypes.c_uint32), ctypes.POINTER(i64), P]
     L.gs_preprocess_backward.argtypes = [SP, P, CP, P, P, AP, P]
     L.gs_preprocess_backward_staged.argtypes = [SP, P, CP, GsProj, P, sz, P, AP, P]
     L.gs_adam_step.argtypes = [i64, P, P, AP, P]
@@ -130,6 +134,12 @@ def _check(rc, required=None):
         if rc == GS_ERR_CAPACITY:
             raise GsCapacityError(rc, msg, required)
         raise GsError(rc, msg)
+
+
+def _k(k, vals):
+    """The intersection count passed to the render calls: the caller's K, or when none is given the
+    length of the vals buffer, which bounds it."""
+    return int(vals.numel()) if k is None else int(k)
 
 
 # ------------------------------------------------------------------------------------------
@@ -236,10 +246,11 @@ def _nbytes(t):
 
 
 def render_forward(cam: GsCamera, n, splat, vals, ranges, bg, image, T_final, last_contrib, render_ws,
-                   n_examined=None, blend_count=None, stream=None):
-    if blend_count is not None and (blend_count.numel() < 3 or blend_count.element_size() != 8):
-        raise ValueError("blend_count must be a device int64 tensor of at least 3 elements")
-    _check(load().gs_render_forward(ctypes.byref(cam), int(n), _ptr(splat), _ptr(vals), _ptr(ranges), _bg(bg),
+                   n_examined=None, blend_count=None, stream=None, k=None):
+    if blend_count is not None and (blend_count.numel() < 4 or blend_count.element_size() != 8):
+        raise ValueError("blend_count must be a device int64 tensor of at least 4 elements")
+    _check(load().gs_render_forward(ctypes.byref(cam), int(n), _ptr(splat), _ptr(vals), _ptr(ranges), _k(k, vals),
+                                    _bg(bg),
                                     _ptr(image), _ptr(T_final), _ptr(last_contrib), _ptr(n_examined),
                                     _ptr(blend_count), _ptr(render_ws), _nbytes(render_ws), _stream(stream)))
 
@@ -273,30 +284,60 @@ def make_adam(m, v, step, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8) -> GsAdam:
 
 def render_backward(scene: GsScene, params, cam: GsCamera, proj: Proj, vals, ranges, bg, T_final,
                     last_contrib, dL_dimage, grad2d, render_ws, grads=None, adam: GsAdam | None = None,
-                    stream=None):
+                    stream=None, k=None):
     _check(load().gs_render_backward(ctypes.byref(scene), _ptr(params), ctypes.byref(cam), proj.c(), _ptr(vals),
-                                     _ptr(ranges), _bg(bg), _ptr(T_final), _ptr(last_contrib), _ptr(dL_dimage),
+                                     _ptr(ranges), _k(k, vals), _bg(bg), _ptr(T_final), _ptr(last_contrib), _ptr(dL_dimage),
                                      _ptr(grad2d), _ptr(grads), ctypes.byref(adam) if adam is not None else None,
                                      _ptr(render_ws), _nbytes(render_ws), _stream(stream)))
 
 
-def render_plan(scene: GsScene, cam: GsCamera, proj: Proj, ranges, render_ws, stream=None):
-    """Prepares render_ws for render_step over the lists of these ranges."""
-    _check(load().gs_render_plan(ctypes.byref(scene), ctypes.byref(cam), proj.c(), _ptr(ranges), _ptr(render_ws),
-                                 _nbytes(render_ws), _stream(stream)))
+def render_plan(scene: GsScene, cam: GsCamera, proj: Proj, ranges, render_ws, stream=None, k=None):
+    """Prepares render_ws for render_step over the lists of these ranges (k intersections; when not
+    given, the largest count the workspace holds is assumed and only the device check applies)."""
+    if k is None:
+        k = render_workspace_capacity(cam.width, cam.height, scene.n, _nbytes(render_ws))
+    _check(load().gs_render_plan(ctypes.byref(scene), ctypes.byref(cam), proj.c(), _ptr(ranges), int(k),
+                                 _ptr(render_ws), _nbytes(render_ws), _stream(stream)))
 
 
 def render_step(scene: GsScene, cam: GsCamera, proj: Proj, vals, ranges, bg, target, image, T_final, last_contrib,
-                loss, dL_dimage, render_ws, grad2d=None, n_examined=None, blend_count=None, stream=None):
+                loss, dL_dimage, render_ws, grad2d=None, n_examined=None, blend_count=None, stream=None, k=None):
     """Forward blend, L1 loss and backward blend of one step in one fused kernel (after
     render_plan on the same render_ws); the gradient sums stay staged in render_ws for
     preprocess_backward_staged (and go to grad2d if given)."""
-    if blend_count is not None and (blend_count.numel() < 3 or blend_count.element_size() != 8):
-        raise ValueError("blend_count must be a device int64 tensor of at least 3 elements")
-    _check(load().gs_render_step(ctypes.byref(scene), ctypes.byref(cam), proj.c(), _ptr(vals), _ptr(ranges), _bg(bg),
+    if blend_count is not None and (blend_count.numel() < 4 or blend_count.element_size() != 8):
+        raise ValueError("blend_count must be a device int64 tensor of at least 4 elements")
+    _check(load().gs_render_step(ctypes.byref(scene), ctypes.byref(cam), proj.c(), _ptr(vals), _ptr(ranges),
+                                 _k(k, vals), _bg(bg),
                                  _ptr(target), _ptr(image), _ptr(T_final), _ptr(last_contrib), _ptr(n_examined),
                                  _ptr(blend_count), _ptr(loss), _ptr(dL_dimage), _ptr(grad2d), _ptr(render_ws),
                                  _nbytes(render_ws), _stream(stream)))
+
+
+def render_init(render_ws, stream=None):
+    """Clears a new render workspace's status words."""
+    _check(load().gs_render_init(_ptr(render_ws), _nbytes(render_ws), _stream(stream)))
+
+
+def new_render_ws(width, height, n, k_capacity, device="cuda"):
+    """A render workspace for up to k_capacity intersections, its status words cleared."""
+    import torch
+    ws = torch.empty(render_workspace(width, height, n, k_capacity), dtype=torch.uint8, device=device)
+    render_init(ws)
+    return ws
+
+
+def render_status(render_ws, stream=None, raise_error=True):
+    """The render workspace's device-side status since the last read: (flags, required
+    intersections); the status words are cleared.  Synchronises the stream.  Raises
+    GsCapacityError / GsError for a flagged workspace unless raise_error is False."""
+    flags = ctypes.c_uint32(0)
+    req = ctypes.c_int64(0)
+    rc = load().gs_render_status(_ptr(render_ws), _nbytes(render_ws), ctypes.byref(flags), ctypes.byref(req),
+                                 _stream(stream))
+    if raise_error:
+        _check(rc, required=req.value)
+    return flags.value, req.value
 
 
 def preprocess_backward(scene: GsScene, params, cam: GsCamera, grad2d, grads=None, adam: GsAdam | None = None,
@@ -376,8 +417,7 @@ class StepBuffers:
         self.ranges = torch.empty((self.T, 2), dtype=i32, device=device)
         self.ws = torch.empty(bin_and_sort_workspace(n, self.k_capacity, width, height), dtype=torch.uint8,
                               device=device)
-        self.render_ws = torch.empty(render_workspace(width, height, n, self.k_capacity), dtype=torch.uint8,
-                                     device=device)
+        self.render_ws = new_render_ws(width, height, n, self.k_capacity, device)
         self.image = torch.empty((height, width, 3), dtype=f32, device=device)
         self.T_final = torch.empty((height, width), dtype=f32, device=device)
         self.last = torch.empty((height, width), dtype=i32, device=device)
@@ -394,8 +434,7 @@ class StepBuffers:
         self.vals = torch.empty(max(1, self.k_capacity), dtype=torch.int32, device=device)
         self.ws = torch.empty(bin_and_sort_workspace(self.n, self.k_capacity, self.W, self.H), dtype=torch.uint8,
                               device=device)
-        self.render_ws = torch.empty(render_workspace(self.W, self.H, self.n, self.k_capacity), dtype=torch.uint8,
-                                     device=device)
+        self.render_ws = new_render_ws(self.W, self.H, self.n, self.k_capacity, device)
 
 
 def train_step(buf: StepBuffers, params, m, v, step, cam: GsCamera, target=None, upstream=None,
@@ -411,7 +450,7 @@ def train_step(buf: StepBuffers, params, m, v, step, cam: GsCamera, target=None,
         except GsCapacityError as e:
             buf.grow(int(e.required * 1.25) + 1024)
     render_forward(cam, buf.n, buf.proj.splat, buf.vals, buf.ranges, bg, buf.image, buf.T_final, buf.last,
-                   buf.render_ws, blend_count=blend_count)
+                   buf.render_ws, blend_count=blend_count, k=K)
     if upstream is not None:
         dLdI = upstream
     elif dssim_lambda is not None:
@@ -427,10 +466,10 @@ def train_step(buf: StepBuffers, params, m, v, step, cam: GsCamera, target=None,
     adam = make_adam(m, v, step, lr)
     if fused_adam:
         render_backward(buf.scene, params, cam, buf.proj, buf.vals, buf.ranges, bg, buf.T_final, buf.last, dLdI,
-                        buf.grad2d, buf.render_ws, grads, adam)
+                        buf.grad2d, buf.render_ws, grads, adam, k=K)
     else:
         render_backward(buf.scene, params, cam, buf.proj, buf.vals, buf.ranges, bg, buf.T_final, buf.last, dLdI,
-                        buf.grad2d, buf.render_ws, grads)
+                        buf.grad2d, buf.render_ws, grads, k=K)
         adam_step(buf.R * buf.ld, params, grads, adam)
     return K
 
@@ -457,19 +496,19 @@ def train_batch(buf: StepBuffers, params, m, v, step, cams, targets, grads_acc, 
             except GsCapacityError as e:
                 buf.grow(int(e.required * 1.25) + 1024)
         if dssim_lambda is None:
-            render_plan(buf.scene, cam, buf.proj, buf.ranges, buf.render_ws)
+            render_plan(buf.scene, cam, buf.proj, buf.ranges, buf.render_ws, k=K)
             render_step(buf.scene, cam, buf.proj, buf.vals, buf.ranges, bg, tgt, buf.image, buf.T_final, buf.last,
-                        buf.loss, buf.dLdI, buf.render_ws, blend_count=blend_count)
+                        buf.loss, buf.dLdI, buf.render_ws, blend_count=blend_count, k=K)
         else:
             if buf.dssim_ws is None:
                 import torch
                 buf.dssim_ws = torch.empty(loss_l1_dssim_workspace(buf.W, buf.H), dtype=torch.uint8,
                                            device=buf.image.device)
             render_forward(cam, buf.n, buf.proj.splat, buf.vals, buf.ranges, bg, buf.image, buf.T_final, buf.last,
-                           buf.render_ws, blend_count=blend_count)
+                           buf.render_ws, blend_count=blend_count, k=K)
             loss_l1_dssim(buf.W, buf.H, buf.image, tgt, dssim_lambda, buf.loss, buf.dLdI, buf.dssim_ws)
             render_backward(buf.scene, None, cam, buf.proj, buf.vals, buf.ranges, bg, buf.T_final, buf.last,
-                            buf.dLdI, None, buf.render_ws)
+                            buf.dLdI, None, buf.render_ws, k=K)
         preprocess_backward_accumulate(buf.scene, params, cam, buf.proj, buf.render_ws, grads_acc, j == 0, 1.0 / B,
                                        adam if j == B - 1 else None)
         ks.append(K)

@@ -36,8 +36,9 @@
  *     unless marked "host".  The caller owns every buffer; the library never allocates or
  *     frees device memory.  Host structs are read during the call only.
  *   - Every call enqueues work on `stream` and returns without waiting, except
- *     gs_bin_and_sort, which copies the intersection count to the host and synchronises
- *     `stream` once (see there).
+ *     gs_bin_and_sort and gs_densify, which copy a count to the host and synchronise
+ *     `stream` once, and gs_render_status, which reads the render workspace's status words
+ *     (see there).
  *   - Outputs must not alias inputs, except where a call says it updates in place.
  *   - Every call returns a gs_status.  Arguments are checked before any HIP call; on an
  *     error nothing is enqueued and gs_last_error() describes it.  No exception or abort
@@ -55,7 +56,7 @@
 extern "C" {
 #endif
 
-#define GSMI_VERSION 7
+#define GSMI_VERSION 8
 #define GS_TILE 16 /* tiles are GS_TILE x GS_TILE pixels */
 
 typedef enum gs_status {
@@ -63,7 +64,8 @@ typedef enum gs_status {
   GS_ERR_INVALID_ARGUMENT = -1, /* null pointer, bad size, non-finite camera, ...      */
   GS_ERR_CAPACITY = -2,         /* intersection buffers too small; *k_out = required K */
   GS_ERR_HIP = -3,              /* a HIP runtime call failed (message in gs_last_error) */
-  GS_ERR_UNSUPPORTED = -4       /* a valid but unsupported variant                    */
+  GS_ERR_UNSUPPORTED = -4,      /* a valid but unsupported variant                    */
+  GS_ERR_INCOMPLETE = -5        /* a bounded device-side wait gave up (gs_render_status) */
 } gs_status;
 
 /* Pinhole camera.  viewmat is the row-major 3x4 world->camera transform [R | t] with
@@ -130,9 +132,23 @@ typedef struct gs_adam {
 
 /* ---------------------------------------------------------------------------------- */
 
-/* Per-Gaussian preprocess (EWA projection + SH colour).  params: R rows of stride ld.
- * Writes out.splat[0..n), out.tiles[0..n), out.depth_key[0..n), out.rect[0..2n).  One thread per Gaussian;
- * HBM-bound. */
+/* Per-Gaussian preprocess ("Scaling 3D Gaussian Splatting with Distributed Compute", walkthrough
+ * steps "Project locally" -- 2D means, depths, conics, radii and visibility per camera -- and
+ * "Evaluate spherical harmonics before communicating" -- SH to RGB once per camera; the Gaussian's
+ * parameters are the page's list: mean, covariance from scale and rotation, SH colour, opacity).
+ * For each Gaussian i < n: scale = exp(log-scale), opacity = sigmoid(logit), rotation from the
+ * normalised quaternion, Sigma = R S S^T R^T, view-space mean p = W mu + t (culled if z <=
+ * near_plane or not finite), the EWA Jacobian J at p (x/z, y/z clamped to 1.3x the half field of
+ * view), S2 = J W Sigma W^T J^T + 0.3 I (culled if det <= 0), conic = S2^-1, per-axis 3-sigma radii
+ * ceil(3 sqrt(S2_ii)), the tile rect of the box (u +- radius_x, v +- radius_y) (culled if empty),
+ * and rgb = max(0.5 + sum_k Y_k(dir) f_k, 0) with dir the unit vector from the camera centre to mu
+ * and Y_k the real SH basis with the Condon-Shortley phase (l = 0..sh_degree, m = -l..l).
+ *   params[R][ld]  device, read only
+ *   out            device arrays of >= ld entries (rect: 2 ld words); writes out.splat[0..n),
+ *                  out.tiles[0..n), out.depth_key[0..n), out.rect[0..2n); a culled Gaussian gets an
+ *                  all-zero record, tiles 0, depth key 0xFFFFFFFF and rect (0, 0)
+ * GS_ERR_INVALID_ARGUMENT for a bad scene or camera, a null params (n > 0) or a null / misaligned
+ * proj array.  One thread per Gaussian; HBM-bound. */
 int gs_preprocess(const gs_scene* scene, const float* params, const gs_camera* cam, gs_proj out,
                   hipStream_t stream);
 
@@ -141,8 +157,11 @@ int gs_preprocess(const gs_scene* scene, const float* params, const gs_camera* c
 int gs_bin_and_sort_workspace(int64_t n, int64_t k_capacity, int32_t width, int32_t height,
                               size_t* bytes);
 
-/* Tile binning and sorting.  For every visible Gaussian i and every tile (tx, ty) of its
- * 3-sigma box, one intersection with key (ty*TX + tx) << 32 | depth_key[i] and value i;
+/* Tile binning and sorting ("Scaling 3D Gaussian Splatting with Distributed Compute": the per-tile
+ * sorted intersection lists of the memory-accounting passage, and the trace section's
+ * intersection-offset kernel, one thread per intersection; the ties by Gaussian index are this
+ * library's rule, which makes the order unique).  For every visible Gaussian i and every tile
+ * (tx, ty) of its 3-sigma box, one intersection with key (ty*TX + tx) << 32 | depth_key[i] and value i;
  * the intersections are sorted ascending by key, ties in Gaussian index order (stable),
  * which gives per-tile lists in front-to-back depth order.
  *   vals[k_capacity]   out: sorted Gaussian indices
@@ -176,7 +195,9 @@ int gs_render_workspace(int32_t width, int32_t height, int64_t n, int64_t k_capa
 int gs_render_workspace_capacity(int32_t width, int32_t height, int64_t n, size_t bytes,
                                  int64_t* k_capacity);
 
-/* Forward blend.  For each pixel, walks its tile's list front to back: power =
+/* Forward blend ("Scaling 3D Gaussian Splatting with Distributed Compute", walkthrough step
+ * "Rasterize locally": alpha compositing of each camera's Gaussians over screen tiles, front to
+ * back, with early termination).  For each pixel, walks its tile's list front to back: power =
  * -(a dx^2 + c dy^2)/2 - b dx dy with (dx, dy) = pixel centre - (u, v); skips power > 0;
  * alpha = min(0.99, opacity e^power); skips alpha < 1/255; stops before blending an entry
  * that would take the transmittance T below 1e-4; else C += rgb alpha T, T *= 1 - alpha.
@@ -185,18 +206,26 @@ int gs_render_workspace_capacity(int32_t width, int32_t height, int64_t n, size_
  *   last_contrib[H][W]  out: 1-based list position of the last blended entry (0 = none)
  *   n_examined[H][W]    out, nullable: entries examined (list length, or the position of
  *                       the entry that stopped the pixel)
- *   blend_count         out, nullable: device uint64[3] to which three image sums are
+ *   k                   the number of intersections in vals (gs_bin_and_sort's K)
+ *   blend_count         out, nullable: device uint64[4] to which four image sums are
  *                       ADDED (the caller zeroes them): [0] n_examined, [1] last_contrib
  *                       (the entries the backward pass walks), [2] the (pixel, entry)
- *                       pairs composited
+ *                       pairs composited, [3] the (pixel, entry) pairs whose alpha the
+ *                       kernel evaluates (the rest of the examined pairs are rejected by a
+ *                       conservative per-record pixel box without evaluating alpha)
  *   render_ws           out: device workspace (256-byte aligned) of render_ws_bytes >= the
  *                       size gs_render_workspace gives for this image, n and a k_capacity
- *                       >= the number of intersections in vals; GS_ERR_INVALID_ARGUMENT if
- *                       it is smaller than the size for k_capacity 0.
+ *                       >= k; GS_ERR_INVALID_ARGUMENT if it is smaller than the size for
+ *                       k_capacity 0, GS_ERR_CAPACITY (nothing enqueued; the message gives the
+ *                       size needed) if it holds fewer than k intersections.  Should the lists
+ *                       themselves need more than it holds (k understated), the kernels stay
+ *                       inside the workspace, the results are not valid and gs_render_status
+ *                       reports GS_ERR_CAPACITY.  A new workspace is cleared once with
+ *                       gs_render_init.
  * bg is a HOST array of 3 floats.  A few persistent 256-thread workgroups per CU take the
  * tiles, longest lists first. */
 int gs_render_forward(const gs_camera* cam, int64_t n, const gs_splat* splat, const uint32_t* vals,
-                      const uint32_t* ranges, const float* bg, float* image, float* T_final,
+                      const uint32_t* ranges, int64_t k, const float* bg, float* image, float* T_final,
                       uint32_t* last_contrib, uint32_t* n_examined, uint64_t* blend_count,
                       void* render_ws, size_t render_ws_bytes, hipStream_t stream);
 
@@ -235,7 +264,13 @@ int gs_loss_l1_dssim(int32_t width, int32_t height, const float* image, const fl
                      float* loss, float* dL_dimage, void* workspace, size_t workspace_bytes,
                      hipStream_t stream);
 
-/* Backward of the step from dL/dimage.
+/* Backward of the step from dL/dimage ("Scaling 3D Gaussian Splatting with Distributed Compute",
+ * the loss passage -- gradients flow back through the rasterizer to the mean, covariance, colour
+ * and opacity -- and walkthrough step "Backward pass"): the exact derivative of the branch the
+ * forward took at every pixel, in reverse list order from last_contrib (alpha clamped at 0.99
+ * passes no gradient to opacity or power; skipped entries contribute nothing), then the chain
+ * rule back through the preprocess to every parameter row.
+ *   k              the number of intersections in vals; capacity errors as gs_render_forward
  *   grad2d[ld][9]  out, nullable: per-Gaussian dL/d(u, v, conic_a, conic_b, conic_c, opacity,
  *                  r, g, b) from the reverse-order backward blend, the nine values of Gaussian i
  *                  at grad2d + 9 i, for i < n (rows n..ld-1 are not written).  Each
@@ -256,7 +291,7 @@ int gs_loss_l1_dssim(int32_t width, int32_t height, const float* image, const fl
  * run more than once per forward.  bg is a HOST array of 3 floats.  Culled
  * Gaussians receive zero gradients. */
 int gs_render_backward(const gs_scene* scene, float* params, const gs_camera* cam, gs_proj proj,
-                       const uint32_t* vals, const uint32_t* ranges, const float* bg,
+                       const uint32_t* vals, const uint32_t* ranges, int64_t k, const float* bg,
                        const float* T_final, const uint32_t* last_contrib, const float* dL_dimage,
                        float* grad2d, float* grads, const gs_adam* adam, void* render_ws,
                        size_t render_ws_bytes, hipStream_t stream);
@@ -264,9 +299,9 @@ int gs_render_backward(const gs_scene* scene, float* params, const gs_camera* ca
 /* Prepares render_ws for gs_render_step over these lists (ranges from gs_bin_and_sort, proj.tiles
  * from gs_preprocess, the same camera): the segment plan and tile order of the forward, an empty
  * list of backward work items, and each Gaussian's cleared staging rows for the gradient sums.
- * Kept apart from gs_render_step so that the fused kernel can be timed alone.  Errors as
- * gs_render_forward. */
-int gs_render_plan(const gs_scene* scene, const gs_camera* cam, gs_proj proj, const uint32_t* ranges,
+ * k is the number of intersections in the lists.  Kept apart from gs_render_step so that the fused
+ * kernel can be timed alone.  Errors as gs_render_forward. */
+int gs_render_plan(const gs_scene* scene, const gs_camera* cam, gs_proj proj, const uint32_t* ranges, int64_t k,
                    void* render_ws, size_t render_ws_bytes, hipStream_t stream);
 
 /* The image pass of one training step, fused: the forward blend (as gs_render_forward), the L1
@@ -287,14 +322,32 @@ int gs_render_plan(const gs_scene* scene, const gs_camera* cam, gs_proj proj, co
  *                       gs_preprocess_backward_staged (same camera, proj and render_ws), which
  *                       finishes the step.  gs_render_backward may also be run on it.
  * proj.splat and proj.tiles are the preprocess outputs the lists were built from; bg is a HOST
- * array of 3 floats.  A wait of one workgroup for another is bounded (about a second); should
- * one ever give up, word 8 of render_ws (its header) is left nonzero and that work item's
- * gradient sums are missing.  Errors as gs_render_forward. */
+ * array of 3 floats; k as gs_render_forward.  A wait of one workgroup for another is bounded
+ * (about a second); should one ever give up, that work item's gradient sums are missing and
+ * gs_render_status reports GS_ERR_INCOMPLETE.  Errors as gs_render_forward. */
 int gs_render_step(const gs_scene* scene, const gs_camera* cam, gs_proj proj, const uint32_t* vals,
-                   const uint32_t* ranges, const float* bg, const float* target, float* image,
+                   const uint32_t* ranges, int64_t k, const float* bg, const float* target, float* image,
                    float* T_final, uint32_t* last_contrib, uint32_t* n_examined, uint64_t* blend_count,
                    float* loss, float* dL_dimage, float* grad2d, void* render_ws, size_t render_ws_bytes,
                    hipStream_t stream);
+
+/* Clears the status words of a render workspace (its first 64 bytes) before its first use, so that
+ * gs_render_status reports only what the calls on it flag.  Asynchronous (a fill kernel on
+ * `stream`).  GS_ERR_INVALID_ARGUMENT for a null, short or misaligned workspace. */
+int gs_render_init(void* render_ws, size_t render_ws_bytes, hipStream_t stream);
+
+/* Status of the device-side checks the render calls on render_ws made since gs_render_init or the
+ * last gs_render_status on it: the kernels set status bits and never clear them, so one call after
+ * many steps covers them all.  Copies the status words to the host, clears them (a fill kernel)
+ * and SYNCHRONISES `stream`.
+ *   flags     host out, nullable: bit 0 a bounded wait of gs_render_step gave up, bit 1 some lists
+ *             needed more intersections than the workspace holds
+ *   required  host out, nullable: the most intersections those lists needed (their largest end,
+ *             or the staged entries when larger); 0 when bit 1 is clear
+ * Returns GS_ERR_CAPACITY when bit 1 is set (the image and gradients of those calls are not
+ * valid), else GS_ERR_INCOMPLETE when bit 0 is set (some gradient sums are missing), else GS_OK. */
+int gs_render_status(void* render_ws, size_t render_ws_bytes, uint32_t* flags, int64_t* required,
+                     hipStream_t stream);
 
 /* Preprocess backward alone: grads (and optionally the fused Adam update) from a given
  * grad2d[ld][9].  Same semantics as the second half of gs_render_backward. */
@@ -387,9 +440,15 @@ int gs_densify(const gs_scene* scene, const float* params, const float* m, const
                float* v_out, int64_t ld_out, int64_t* n_out, int32_t* codes, void* workspace,
                size_t workspace_bytes, hipStream_t stream);
 
-/* Adam over `count` floats, in place: m = b1 m + (1-b1) g; v = b2 v + (1-b2) g^2;
- * params -= lr (m / (1-b1^t)) / (sqrt(v / (1-b2^t)) + eps).  adam->m and adam->v are flat
- * arrays of `count` floats. */
+/* Adam ("Scaling 3D Gaussian Splatting with Distributed Compute", walkthrough step "Step the
+ * optimizer locally", over the parameters and the two moment buffers the memory-accounting
+ * passage counts per Gaussian; Kingma & Ba's bias-corrected update) over `count` floats, in place:
+ * m = b1 m + (1-b1) g; v = b2 v + (1-b2) g^2; params -= lr (m / (1-b1^t)) / (sqrt(v / (1-b2^t)) + eps).
+ *   params, grads  device float[count]; grads is read only
+ *   adam           HOST struct: adam->m, adam->v device float[count] (in place), step t >= 1,
+ *                  lr, beta1, beta2 in [0, 1), eps
+ * Every float is updated, a zero gradient included (dense).  GS_ERR_INVALID_ARGUMENT for a null
+ * adam, count < 0, null arrays or hyper-parameters out of range.  Asynchronous. */
 int gs_adam_step(int64_t count, float* params, const float* grads, const gs_adam* adam,
                  hipStream_t stream);
 

@@ -22,7 +22,7 @@ def test_library_exports_every_declared_symbol():
     assert len(names) == len(gsmi.EXPORTS) and set(names) == set(gsmi.EXPORTS)
     for name in names:
         assert hasattr(L, name), name
-    assert gsmi.version() == 7
+    assert gsmi.version() == 8
 
 
 def test_invalid_arguments_rejected_before_any_gpu_call():
@@ -223,11 +223,11 @@ def test_render_calls_reject_a_missing_or_short_workspace():
     p = ctypes.c_void_p(4096)
     need = gsmi.render_workspace(64, 64, 10, 0)
     for ws, nb in ((None, need), (p, 16), (ctypes.c_void_p(4096 + 64), need)):
-        rc = L.gs_render_forward(ctypes.byref(cam), 10, p, p, p, bg, p, p, p, None, None, ws, nb, None)
+        rc = L.gs_render_forward(ctypes.byref(cam), 10, p, p, p, 0, bg, p, p, p, None, None, ws, nb, None)
         assert rc == gsmi.GS_ERR_INVALID_ARGUMENT
     sc = gsmi.make_scene(10, 10, 0)
     proj = gsmi.GsProj(4096, 4096, 4096, 4096)
-    rc = L.gs_render_backward(ctypes.byref(sc), None, ctypes.byref(cam), proj, p, p, bg, p, p, p, p, None, None,
+    rc = L.gs_render_backward(ctypes.byref(sc), None, ctypes.byref(cam), proj, p, p, 0, bg, p, p, p, p, None, None,
                               p, 16, None)
     assert rc == gsmi.GS_ERR_INVALID_ARGUMENT and "workspace" in gsmi.last_error()
     # the preprocess backward from staged sums: the same workspace checks, and params, tiles
@@ -263,7 +263,7 @@ def test_fused_step_checks_its_arguments():
     proj = gsmi.GsProj(4096, 4096, 4096, 4096)
 
     def call(proj=proj, target=p, loss=p, ws=p, nb=need, ranges=p):
-        return L.gs_render_step(ctypes.byref(sc), ctypes.byref(cam), proj, p, ranges, bg, target, p, p, p, None,
+        return L.gs_render_step(ctypes.byref(sc), ctypes.byref(cam), proj, p, ranges, 0, bg, target, p, p, p, None,
                                 None, loss, p, None, ws, nb, None)
 
     assert call(ws=None) == gsmi.GS_ERR_INVALID_ARGUMENT and "null" in gsmi.last_error()
@@ -291,7 +291,7 @@ def test_render_plan_checks_its_arguments():
     sc = gsmi.make_scene(10, 10, 0)
     proj = gsmi.GsProj(4096, 4096, 4096, 4096)
     call = lambda proj=proj, ranges=p, ws=p, nb=need: L.gs_render_plan(ctypes.byref(sc), ctypes.byref(cam), proj,
-                                                                        ranges, ws, nb, None)
+                                                                        ranges, 0, ws, nb, None)
     assert call(ws=None) == gsmi.GS_ERR_INVALID_ARGUMENT and "null" in gsmi.last_error()
     assert call(ranges=None) == gsmi.GS_ERR_INVALID_ARGUMENT and "null" in gsmi.last_error()
     for ws, nb in ((p, 16), (ctypes.c_void_p(4096 + 64), need)):
@@ -300,3 +300,55 @@ def test_render_plan_checks_its_arguments():
     assert "tiles" in gsmi.last_error()
     assert call(ranges=ctypes.c_void_p(4096 + 4)) == gsmi.GS_ERR_INVALID_ARGUMENT
     assert "aligned" in gsmi.last_error()
+
+
+def test_render_calls_report_a_workspace_short_of_the_intersections():
+    """A render workspace sized for fewer intersections than the lists hold is a capacity error
+    (GS_ERR_CAPACITY, nothing enqueued, the message naming the size needed) on every call that
+    fills or reads it, never a silently partial result; k itself is range-checked."""
+    L = gsmi.load()
+    cam = gsmi.GsCamera()
+    cam.fx = cam.fy = 100.0
+    cam.width = cam.height = 64
+    cam.near_plane = 0.01
+    cam.viewmat[0] = cam.viewmat[5] = cam.viewmat[10] = 1.0
+    bg = (ctypes.c_float * 3)(0, 0, 0)
+    p = ctypes.c_void_p(4096)
+    n = 100
+    nb = gsmi.render_workspace(64, 64, n, 1000)
+    cap = gsmi.render_workspace_capacity(64, 64, n, nb)
+    assert 1000 <= cap < 1000 + 256
+    need = gsmi.render_workspace(64, 64, n, 5000)
+    sc = gsmi.make_scene(n, n, 0)
+    proj = gsmi.GsProj(4096, 4096, 4096, 4096)
+    ad = gsmi.GsAdam(4096, 4096, 1, 1e-3, 0.9, 0.999, 1e-8)
+    calls = {
+        "forward": lambda k: L.gs_render_forward(ctypes.byref(cam), n, p, p, p, k, bg, p, p, p, None, None, p, nb, None),
+        "plan": lambda k: L.gs_render_plan(ctypes.byref(sc), ctypes.byref(cam), proj, p, k, p, nb, None),
+        "step": lambda k: L.gs_render_step(ctypes.byref(sc), ctypes.byref(cam), proj, p, p, k, bg, p, p, p, p, None,
+                                           None, p, p, None, p, nb, None),
+        "backward": lambda k: L.gs_render_backward(ctypes.byref(sc), p, ctypes.byref(cam), proj, p, p, k, bg, p, p,
+                                                   p, None, None, ctypes.byref(ad), p, nb, None),
+    }
+    for name, call in calls.items():
+        assert call(5000) == gsmi.GS_ERR_CAPACITY, name
+        msg = gsmi.last_error()
+        assert f"needs {need} bytes" in msg and str(cap) in msg, (name, msg)
+        assert call(cap + 1) == gsmi.GS_ERR_CAPACITY, name
+        assert call(-1) == gsmi.GS_ERR_INVALID_ARGUMENT and "k =" in gsmi.last_error(), name
+        assert call(1 << 33) == gsmi.GS_ERR_INVALID_ARGUMENT, name
+
+
+def test_render_status_checks_its_arguments():
+    """gs_render_status needs an aligned workspace of at least its header, and clears its outputs
+    before any HIP call."""
+    L = gsmi.load()
+    flags = ctypes.c_uint32(7)
+    req = ctypes.c_int64(7)
+    assert L.gs_render_status(None, 4096, ctypes.byref(flags), ctypes.byref(req), None) == gsmi.GS_ERR_INVALID_ARGUMENT
+    assert flags.value == 0 and req.value == 0
+    assert L.gs_render_status(ctypes.c_void_p(4096), 16, None, None, None) == gsmi.GS_ERR_INVALID_ARGUMENT
+    assert L.gs_render_status(ctypes.c_void_p(4096 + 64), 4096, None, None, None) == gsmi.GS_ERR_INVALID_ARGUMENT
+    assert "workspace" in gsmi.last_error()
+    for ws, nb in ((None, 4096), (ctypes.c_void_p(4096), 16), (ctypes.c_void_p(4096 + 64), 4096)):
+        assert L.gs_render_init(ws, nb, None) == gsmi.GS_ERR_INVALID_ARGUMENT

@@ -1,20 +1,30 @@
-"""GPU parity of the batched optimizer step (several views per Adam step) against the oracle's
-train_batch_reference on the same seeded inputs: the batch-mean gradient accumulated by
-gs_preprocess_backward_accumulate, then params, m and v after the last view's fused Adam update
-with gs_adam_batch's hyper-parameters.  Both sides run each view's whole step from the
-parameters, so a few pixels may take different float32 decisions: the bars are the end-to-end
-ones (relative L2 1e-2), and the measured errors are printed."""
+"""GPU parity of the batched optimizer step ("Scaling 3D Gaussian Splatting with Distributed
+Compute", the batch-size passage: several views per Adam step, lr * sqrt(BS), eps / sqrt(BS),
+beta <- 1 - BS (1 - beta)) against the oracle.
+
+Stage: every view's fused image pass runs on the oracle's records and lists, and
+gs_preprocess_backward_accumulate adds 1/BS of each view's gradient from the staged sums; the
+batch-mean gradient must meet the gradient bar (relative L2 1e-3, per parameter group and
+overall) against the mean of the oracle's per-view gradients, and the last view's fused Adam
+update (gs_adam_batch's hyper-parameters) must give the oracle's Adam of that same gradient to
+1e-6 relative to the operands.  Cases: BS 1, 3, 4 and 10 on small scenes, and two torus views.
+
+End to end: train_batch from the parameters against the oracle's batch step, with the decision
+flips of every view counted and their Gaussians left out (parity_util.e2e_exclusion)."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
 from gaussian_splatting_differentiable_preprocess_amd import gsmi, inputs
-from parity_util import rel_l2, say
+from parity_util import (FWD_MARGINS, GRAD_REL_L2, EXCLUDED_FRACTION, GpuStep, e2e_exclusion, oracle_pipeline,
+                         preprocess_borderline, proj_from_splat, records_from_oracle, rel_l2, say, stage_exclusion)
 
 pytestmark = pytest.mark.gpu
 
-E2E_REL = 1e-2
+BG = (0.0, 0.0, 0.0)
+GROUPS = {"mean": slice(0, 3), "scale": slice(3, 6), "rot": slice(6, 10), "opacity": slice(10, 11),
+          "sh": slice(11, None)}
 
 
 def _tiny(seed, n, deg, W, H, views):
@@ -36,82 +46,170 @@ def _torus(views):
     return params, 3, cams, 512, 512, tgts
 
 
-def _run(params, deg, cams, W, H, tgts, step, dssim=None):
-    """-> (mean gradient, params, m, v after the batch step) from the GPU, and the oracle's."""
-    R, n = params.shape
+def _moments(R, n):
     rng = np.random.default_rng(77)
-    m0 = (1e-3 * rng.standard_normal((R, n))).astype(np.float32)
-    v0 = (1e-6 * rng.random((R, n))).astype(np.float32)
-    say(f"[batch] {n} Gaussians, SH {deg}, {len(cams)} views at {W}x{H}, step {step}, dssim {dssim}: oracle")
-    po, mo, vo, go = oracle.train_batch_reference(params, deg, [c.flat() for c in cams], W, H, tgts, m0, v0, step,
-                                                  dssim_lambda=dssim)
+    return (1e-3 * rng.standard_normal((R, n))).astype(np.float32), (1e-6 * rng.random((R, n))).astype(np.float32)
+
+
+def _adam_close(p_g, m_g, v_g, th, g, m0, v0, step, B):
+    """GPU Adam outputs against the oracle's Adam of gradient g with the batch hyper-parameters, to
+    1e-6 relative to the operands (theta - update and b1 m + (1 - b1) g can cancel)."""
+    lr, b1, b2, eps = oracle.adam_batch_hparams(1e-3, 0.9, 0.999, 1e-8, B)
+    p_o, m_o, v_o = oracle.adam(th, g, m0, v0, step, lr, b1, b2, eps)
+    assert (np.abs(p_g - p_o) <= 1e-6 * np.maximum(np.abs(th), np.abs(p_o)) + 1e-12).all()
+    assert (np.abs(m_g - m_o) <= 1e-6 * np.maximum(np.abs(m0), np.abs(g)) + 1e-12).all()
+    assert (np.abs(v_g - v_o) <= 1e-6 * np.maximum(v_o, v0) + 1e-15).all()
+    return float(np.abs(p_g - p_o).max())
+
+
+def _stage(params, deg, cams, W, H, tgts, step):
+    """Stage parity of the accumulate kernel and the batch Adam (module docstring)."""
+    R, n = params.shape
+    B = len(cams)
+    distinct = {}
+    for c, t in zip(cams, tgts):
+        distinct.setdefault(id(c), (c, t))
+    say(f"[batch] stage: {n} Gaussians, SH {deg}, BS {B} ({len(distinct)} distinct views) at {W}x{H}: oracle")
+    views = {}
+    keep = np.ones(n, bool)
+    for key, (c, t) in distinct.items():
+        o = oracle_pipeline(params, deg, c.flat(), W, H, BG, target=t, margins=FWD_MARGINS)
+        g = GpuStep(params, deg, c, W, H)
+        g.load_proj(*records_from_oracle(o["p32"], o["radii"], o["tiles"], W, H))
+        g.load_lists(o["vals"], o["ranges"])
+        r = g.step(BG, t)  # the fused image pass; its gradient sums stay staged in the view's workspace
+        assert r["stall"] == 0
+        keep &= ~stage_exclusion(o, r, W, H, t)[0]
+        views[key] = (o, g)
+    go = sum(views[id(c)][0]["grads"] for c in cams) / B
+    say(f"[batch]   {int((~keep).sum())} Gaussians at borderline or sign-flipped pixels left out")
+
+    def accumulate(acc, adam=None):
+        for j, c in enumerate(cams):
+            g = views[id(c)][1]
+            gsmi.preprocess_backward_accumulate(g.scene, g.params, g.cam, g.proj, g.render_ws, acc, j == 0, 1.0 / B,
+                                                adam if j == B - 1 else None)
+
+    g0 = views[id(cams[0])][1]
+    acc = torch.full_like(g0.params, float("nan"))  # the first view must not read it
+    accumulate(acc)
+    torch.cuda.synchronize()
+    gg = acc.cpu().numpy()
+    e = rel_l2(gg[:, keep], go[:, keep])
+    eg = {k: rel_l2(gg[sl][:, keep], go[sl][:, keep]) for k, sl in GROUPS.items()}
+    say(f"[batch]   mean gradient rel-L2 {e:.3g} (" + ", ".join(f"{k} {v:.2g}" for k, v in eg.items()) + ")")
+    assert e <= GRAD_REL_L2 and max(eg.values()) <= GRAD_REL_L2
+    # the same sums again with Adam fused into the last view: the update of exactly gg
+    m0, v0 = _moments(R, n)
+    mt, vt = torch.from_numpy(m0).cuda(), torch.from_numpy(v0).cuda()
+    p0 = g0.params.clone()
+    adam = gsmi.adam_batch(gsmi.make_adam(mt, vt, step, 1e-3), B)
+    accumulate(torch.full_like(g0.params, float("nan")), adam)
+    torch.cuda.synchronize()
+    # every view's GpuStep shares the same parameter values; the last view's is the one updated
+    p_new = views[id(cams[-1])][1].params.cpu().numpy()
+    d = _adam_close(p_new, mt.cpu().numpy(), vt.cpu().numpy(), p0.cpu().numpy(), gg, m0, v0, step, B)
+    say(f"[batch]   fused batch Adam vs the oracle's Adam of the same gradient: max |dparam| {d:.3g}")
+
+
+def _e2e(params, deg, cams, W, H, tgts, step):
+    """train_batch from the parameters against the oracle's batch step under the flip rule."""
+    R, n = params.shape
+    B = len(cams)
+    say(f"[batch] e2e: {n} Gaussians, SH {deg}, BS {B} at {W}x{H}")
+    ex = np.zeros(n, bool)
+    go = np.zeros((R, n))
+    for c, t in zip(cams, tgts):
+        o = oracle_pipeline(params, deg, c.flat(), W, H, BG, target=t, margins=FWD_MARGINS)
+        go += o["grads"] / B
+        # the GPU's own walk of this view (its forward is deterministic: the same as inside train_batch)
+        g = GpuStep(params, deg, c, W, H)
+        splat, tiles, _ = g.preprocess()
+        rec, radii = proj_from_splat(splat)
+        g.bin_and_sort()
+        r = g.step(BG, t)
+        e = dict(rec=rec.astype(np.float32).astype(np.float64), radii=radii, tiles=tiles, image=r["image"],
+                 last_contrib=r["last_contrib"], n_examined=r["n_examined"],
+                 vals=g.vals.cpu().numpy().view(np.uint32)[: g.K], ranges=g.ranges.cpu().numpy().view(np.uint32))
+        bl = preprocess_borderline(params, deg, c.flat(), W, H, o["proj"][0], o["proj"][1], o["radii"])
+        x, _, rep = e2e_exclusion(o, e, W, H, BG, target=t, pre_bl=bl)
+        ex |= x
+        say(f"[batch]   view: {rep['flipped']} flipped px, {rep['excluded']} Gaussians excluded")
+    m0, v0 = _moments(R, n)
+    lr, b1, b2, eps = oracle.adam_batch_hparams(1e-3, 0.9, 0.999, 1e-8, B)
+    po, mo, vo = oracle.adam(params, go, m0, v0, step, lr, b1, b2, eps)
     buf = gsmi.StepBuffers(n, n, deg, W, H, k_capacity=max(4 * n, 1 << 16))
     gcams = [gsmi.make_camera(c) for c in cams]
     gt = [torch.from_numpy(t).cuda() for t in tgts]
-    # the accumulated mean gradient alone (no Adam): every view adds 1/BS of its gradient
     p = torch.from_numpy(params).cuda()
-    acc = torch.full_like(p, float("nan"))  # the first view must not read it
-    B = len(cams)
+    acc = torch.full_like(p, float("nan"))
+    # the batch-mean gradient alone (no Adam), then the whole batch step with Adam fused
     for j in range(B):
         gsmi.preprocess(buf.scene, p, gcams[j], buf.proj)
-        gsmi.bin_and_sort(buf.scene, gcams[j], buf.proj, buf.ws, buf.k_capacity, buf.vals, buf.ranges)
-        if dssim is None:
-            gsmi.render_plan(buf.scene, gcams[j], buf.proj, buf.ranges, buf.render_ws)
-            gsmi.render_step(buf.scene, gcams[j], buf.proj, buf.vals, buf.ranges, (0.0, 0.0, 0.0), gt[j], buf.image,
-                             buf.T_final, buf.last, buf.loss, buf.dLdI, buf.render_ws)
-        else:
-            ws = torch.empty(gsmi.loss_l1_dssim_workspace(W, H), dtype=torch.uint8, device="cuda")
-            gsmi.render_forward(gcams[j], n, buf.proj.splat, buf.vals, buf.ranges, (0.0, 0.0, 0.0), buf.image,
-                                buf.T_final, buf.last, buf.render_ws)
-            gsmi.loss_l1_dssim(W, H, buf.image, gt[j], dssim, buf.loss, buf.dLdI, ws)
-            gsmi.render_backward(buf.scene, None, gcams[j], buf.proj, buf.vals, buf.ranges, (0.0, 0.0, 0.0),
-                                 buf.T_final, buf.last, buf.dLdI, None, buf.render_ws)
+        K = gsmi.bin_and_sort(buf.scene, gcams[j], buf.proj, buf.ws, buf.k_capacity, buf.vals, buf.ranges)
+        gsmi.render_plan(buf.scene, gcams[j], buf.proj, buf.ranges, buf.render_ws, k=K)
+        gsmi.render_step(buf.scene, gcams[j], buf.proj, buf.vals, buf.ranges, BG, gt[j], buf.image, buf.T_final,
+                         buf.last, buf.loss, buf.dLdI, buf.render_ws, k=K)
         gsmi.preprocess_backward_accumulate(buf.scene, p, gcams[j], buf.proj, buf.render_ws, acc, j == 0, 1.0 / B)
-    torch.cuda.synchronize()
-    g_gpu = acc.cpu().numpy()
-    # the whole batch step through train_batch (Adam fused into the last view's backward)
-    m = torch.from_numpy(m0).cuda()
-    v = torch.from_numpy(v0).cuda()
-    acc2 = torch.empty_like(p)
-    gsmi.train_batch(buf, p, m, v, step, gcams, gt, acc2, dssim_lambda=dssim)
-    torch.cuda.synchronize()
-    return (g_gpu, p.cpu().numpy(), m.cpu().numpy(), v.cpu().numpy()), (go, po, mo, vo)
-
-
-def _check(params, got, want):
-    g, p, m, v = got
-    go, po, mo, vo = want
-    assert np.isfinite(g).all() and np.isfinite(p).all()
-    eg = rel_l2(g, go)
-    em = rel_l2(m, mo)
-    ev = rel_l2(v, vo)
-    ep = rel_l2(p - params, po - params)
-    say(f"[batch]   rel-L2: mean gradient {eg:.3g}, m {em:.3g}, v {ev:.3g}, parameter update {ep:.3g}")
-    assert eg <= E2E_REL and em <= E2E_REL and ev <= E2E_REL and ep <= E2E_REL
+    gg = acc.cpu().numpy()
+    mt, vt = torch.from_numpy(m0).cuda(), torch.from_numpy(v0).cuda()
+    gsmi.train_batch(buf, p, mt, vt, step, gcams, gt, torch.empty_like(p))
+    gsmi.render_status(buf.render_ws)
+    keep = ~ex
+    pg, mg, vg = p.cpu().numpy(), mt.cpu().numpy(), vt.cpu().numpy()
+    errs = dict(gradient=rel_l2(gg[:, keep], go[:, keep]), m=rel_l2(mg[:, keep], mo[:, keep]),
+                v=rel_l2(vg[:, keep], vo[:, keep]),
+                update=rel_l2((pg - params)[:, keep], (po - params)[:, keep]))
+    vis = int((np.abs(go) > 0).any(axis=0).sum())
+    say(f"[batch]   {int(ex.sum())} of {vis} touched Gaussians excluded; rel-L2 on the rest: " +
+        ", ".join(f"{k} {v:.3g}" for k, v in errs.items()) + f"; unexcluded gradient {rel_l2(gg, go):.3g}")
+    assert ex.sum() <= max(8, EXCLUDED_FRACTION * vis)
+    assert max(errs.values()) <= GRAD_REL_L2, errs
 
 
 @pytest.mark.parametrize("views", [1, 3, 4])
-def test_batch_tiny(views):
-    params, deg, cams, W, H, tgts = _tiny(300, 500, 3, 64, 64, views)
-    got, want = _run(params, deg, cams, W, H, tgts, step=4)
-    _check(params, got, want)
+def test_batch_stage_tiny(views):
+    _stage(*_tiny(300, 500, 3, 64, 64, views), step=4)
+
+
+def test_batch_stage_of_ten_has_no_first_moment_history():
+    """At BS = 10 beta1 is 0: m after the step is the batch-mean gradient itself."""
+    params, deg, cams, W, H, tgts = _tiny(320, 200, 2, 48, 40, 2)
+    lr, b1, b2, eps = oracle.adam_batch_hparams(1e-3, 0.9, 0.999, 1e-8, 10)
+    assert abs(b1) < 1e-12
+    _stage(params, deg, cams * 5, W, H, tgts * 5, step=3)
+
+
+def test_batch_stage_torus_two_views():
+    _stage(*_torus([0, 5]), step=7)
+
+
+@pytest.mark.parametrize("views", [1, 4])
+def test_batch_e2e_tiny(views):
+    _e2e(*_tiny(300, 500, 3, 64, 64, views), step=4)
+
+
+def test_batch_e2e_torus_two_views():
+    _e2e(*_torus([0, 5]), step=7)
 
 
 def test_batch_ragged_with_dssim():
+    """A ragged 100x70 batch of two views with the L1 + D-SSIM loss through train_batch (the
+    forward, the loss and the backward blend as three calls) against the oracle's batch step on
+    the same views: both sides' gradients from the parameters, a small scene whose decisions sit
+    away from the thresholds (no flipped pixel), so the whole gradient is compared."""
     params, deg, cams, W, H, tgts = _tiny(310, 300, 1, 100, 70, 2)
-    got, want = _run(params, deg, cams, W, H, tgts, step=2, dssim=0.2)
-    _check(params, got, want)
-
-
-def test_batch_of_ten_has_no_first_moment_history():
-    """At BS = 10 beta1 is 0, so m after the step is the batch-mean gradient itself."""
-    params, deg, cams, W, H, tgts = _tiny(320, 200, 2, 48, 40, 2)
-    got, want = _run(params, deg, cams * 5, W, H, tgts * 5, step=3)
-    _check(params, got, want)
-    assert rel_l2(got[2], got[0]) <= 1e-5
-
-
-def test_batch_torus_two_views():
-    params, deg, cams, W, H, tgts = _torus([0, 5])
-    got, want = _run(params, deg, cams, W, H, tgts, step=7)
-    _check(params, got, want)
+    R, n = params.shape
+    m0, v0 = _moments(R, n)
+    po, mo, vo, go = oracle.train_batch_reference(params, deg, [c.flat() for c in cams], W, H, tgts, m0, v0, 2,
+                                                  dssim_lambda=0.2)
+    buf = gsmi.StepBuffers(n, n, deg, W, H, k_capacity=max(4 * n, 1 << 16))
+    p = torch.from_numpy(params).cuda()
+    mt, vt = torch.from_numpy(m0).cuda(), torch.from_numpy(v0).cuda()
+    gsmi.train_batch(buf, p, mt, vt, 2, [gsmi.make_camera(c) for c in cams], [torch.from_numpy(t).cuda() for t in tgts],
+                     torch.empty_like(p), dssim_lambda=0.2)
+    torch.cuda.synchronize()
+    errs = dict(m=rel_l2(mt.cpu().numpy(), mo), v=rel_l2(vt.cpu().numpy(), vo),
+                update=rel_l2(p.cpu().numpy() - params, po - params))
+    say("[batch] ragged D-SSIM batch rel-L2: " + ", ".join(f"{k} {v:.3g}" for k, v in errs.items()))
+    assert max(errs.values()) <= GRAD_REL_L2

@@ -4,17 +4,19 @@ gyroid_4m_2048 (4M Gaussians, SH degree 3, 2048x2048): the oracle runs the whole
 orbit view on the seeded inputs; the GPU runs each stage on the oracle's inputs to it and the
 whole step from the parameters, and every output is compared element by element.
 
-bumps_18m_2048 (18.18M Gaussians): the oracle's preprocess and sort run over every Gaussian and
-the GPU's sort of the oracle's records must match bit for bit; the blends are compared on a
-sample of tiles (the heaviest ones and a seeded random set), both sides given the same lists
-with every other tile emptied.  Set GSMI_FULLSIZE_18M=0 to skip it (its scene takes about a
-minute to draw on the host).
-
 gyroid_4m_1024 and gyroid_4m_2048 with the L1 loss against a seeded target: the fused image pass
 and the preprocess backward from its staged sums -- the launch configuration the bench times --
 on the oracle's records and lists and end to end.
 
-Elsewhere upstream dL/dI is the seeded U(-1, 1) field of the configuration."""
+bumps_18m_2048 (18.18M Gaussians, lists of up to ~1.9M entries): the same launch configuration,
+every stage over every Gaussian and every pixel -- the preprocess, the sort bit-exact, the fused
+image pass on the oracle's records and lists over the whole image, the preprocess backward from
+the staged sums with and without the fused Adam update -- and the whole step from the parameters.
+Set GSMI_FULLSIZE_18M=0 to skip it (its scene takes about a minute to draw on the host).
+
+End to end, decision flips are counted and bounded and the rest is held to the stated bars
+(parity_util.e2e_exclusion).  Elsewhere upstream dL/dI is the seeded U(-1, 1) field of the
+configuration."""
 from __future__ import annotations
 
 import os
@@ -23,23 +25,61 @@ import numpy as np
 import pytest
 
 import oracle
-from gaussian_splatting_differentiable_preprocess_amd import inputs
-from parity_util import (BORDER_FRACTION, FWD_MARGINS, GRAD_REL_L2, IMG_MAX_ABS, GpuStep, oracle_pipeline,
-                         preprocess_borderline, proj_from_splat, records_from_oracle, rel_l2, say)
+from gaussian_splatting_differentiable_preprocess_amd import gsmi, inputs
+from parity_util import (border_bound, FWD_MARGINS, GRAD_REL_L2, IMG_MAX_ABS, PROJ_RTOL, GpuStep, check_e2e,
+                         gpu_e2e, oracle_pipeline, preprocess_borderline, proj_from_splat, records_from_oracle,
+                         rel_l2, say, stage_exclusion)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 BG = (0.0, 0.0, 0.0)
+GROUPS = {"mean": slice(0, 3), "scale": slice(3, 6), "rot": slice(6, 10), "opacity": slice(10, 11),
+          "sh": slice(11, None)}
 
 
 def _compare_forward(g, o, P, label):
     bl = o["borderline"]
     err = np.abs(g["image"] - o["image"]).max(axis=-1)
     say(f"[fullsize] {label} forward: {int(bl.sum())} borderline of {P}; max err non-borderline {err[~bl].max():.3g}")
-    assert bl.sum() <= max(1.0, BORDER_FRACTION * P), bl.sum()
+    assert bl.sum() <= border_bound(o["n_blended"]), bl.sum()
     assert err[~bl].max() <= IMG_MAX_ABS
     np.testing.assert_array_equal(g["last_contrib"][~bl], o["last_contrib"][~bl])
     np.testing.assert_array_equal(g["n_examined"][~bl], o["n_examined"][~bl])
+    assert np.abs(g["T_final"] - o["T_final"])[~bl].max() <= 1e-5
+
+
+def _check_preprocess(params, deg, cam, W, H, o, splat, tiles, label):
+    """The GPU preprocess against the oracle's over every Gaussian: visibility, radii and tile
+    counts exact off the borderline ones, every record field within 1e-5 (the conic relative to
+    its magnitude, colours to their value + 1e-3).  Returns the borderline mask."""
+    gp, gr = proj_from_splat(splat)
+    op = o["proj"]
+    bl = preprocess_borderline(params, deg, cam.flat(), W, H, op[0], op[1], o["radii"])
+    vis_o, vis_g = o["radii"][0] > 0, gr[0] > 0
+    assert ((vis_o != vis_g) & ~bl).sum() == 0
+    same = vis_o & vis_g & ~bl
+    np.testing.assert_array_equal(gr[:, same], o["radii"][:, same])
+    np.testing.assert_array_equal(tiles[same], o["tiles"][same])
+    conic = np.maximum(np.abs(op[4]), np.abs(op[6]))[same]
+    worst = {}
+    for f, name in enumerate(oracle.PROJ_FIELDS):
+        err = np.abs(gp[f, same] - op[f, same])
+        scale = conic if name in ("A", "B", "C") else (np.abs(op[f, same]) + 1e-3 if name in "rgb" else
+                                                       np.abs(op[f, same]))
+        worst[name] = float((err / scale).max())
+        assert worst[name] <= PROJ_RTOL, (name, worst[name])
+    say(f"[fullsize] {label} preprocess: {int(vis_o.sum())} visible, {int(bl.sum())} borderline; worst relative "
+        "error " + ", ".join(f"{k} {v:.2g}" for k, v in worst.items()))
+    assert bl.sum() <= max(2, 1e-3 * bl.size)
+    return bl
+
+
+def _stage_keep(o, fwd, W, H, target=None):
+    """The Gaussians the stage gradient comparisons keep (parity_util.stage_exclusion)."""
+    ex, rep = stage_exclusion(o, fwd, W, H, target)
+    say(f"[fullsize] stage: {rep['pixels']} borderline or sign-flipped px; {rep['excluded']} of {rep['visible']} "
+        "Gaussians composited there left out of the gradient comparison")
+    return ~ex
 
 
 def test_gyroid_4m_2048_full_step():
@@ -56,13 +96,7 @@ def test_gyroid_4m_2048_full_step():
     say(f"[fullsize] K = {K}; GPU preprocess")
     g = GpuStep(params, cfg.sh_degree, cam, W, H, k_capacity=K + 4096)
     splat, tiles, _ = g.preprocess()
-    gp, gr = proj_from_splat(splat)
-    bl = preprocess_borderline(params, cfg.sh_degree, cam.flat(), W, H, o["proj"][0], o["proj"][1], o["radii"])
-    same = (gr[0] > 0) & (o["radii"][0] > 0) & ~bl
-    assert ((gr[0] > 0) != (o["radii"][0] > 0))[~bl].sum() == 0
-    np.testing.assert_array_equal(gr[:, same], o["radii"][:, same])
-    for f in (0, 1, 2, 3):  # u, v, depth, opacity
-        assert (np.abs(gp[f, same] - o["proj"][f, same]) <= 1e-5 * np.abs(o["proj"][f, same])).all(), f
+    bl = _check_preprocess(params, cfg.sh_degree, cam, W, H, o, splat, tiles, "gyroid_4m_2048")
     say("[fullsize] GPU sort of the oracle's records")
     g.load_proj(*records_from_oracle(o["p32"], o["radii"], o["tiles"], W, H))
     Kg, keys, vals, rg = g.bin_and_sort()
@@ -75,27 +109,19 @@ def test_gyroid_4m_2048_full_step():
     _compare_forward(fwd, o["fwd"], W * H, "stage")
     g.set_upstream(o["dl32"])
     g2, grads = g.backward()
-    errs = [rel_l2(g2[r, :n], o["grad2d"][r]) for r in range(9)]
+    keep = _stage_keep(o, fwd, W, H)
+    errs = [rel_l2(g2[r, :n][keep], o["grad2d"][r][keep]) for r in range(9)]
     say("[fullsize] backward blend rel-L2 per row: " + " ".join(f"{e:.2g}" for e in errs))
     assert max(errs) <= GRAD_REL_L2
-    e = rel_l2(grads, o["grads"])
+    e = rel_l2(grads[:, keep], o["grads"][:, keep])
     say(f"[fullsize] preprocess backward (chained) rel-L2 {e:.3g}")
     assert e <= GRAD_REL_L2
     e_iso = rel_l2(g.preprocess_backward(o["grad2d"]), o["grads"])
     assert e_iso <= GRAD_REL_L2
     say("[fullsize] GPU step end to end from the parameters")
-    e2 = GpuStep(params, cfg.sh_degree, cam, W, H, k_capacity=K + 4096)
-    e2.preprocess()
-    e2.bin_and_sort()
-    f2 = e2.forward(BG)
-    err = np.abs(f2["image"] - o["fwd"]["image"]).max(axis=-1)
-    ok = ~o["fwd"]["borderline"]
-    frac_bad = float((err[ok] > IMG_MAX_ABS).mean())
-    e2.set_upstream(up)
-    g2e, grads_e = e2.backward()
-    ee = rel_l2(grads_e, o["grads"])
-    say(f"[fullsize] e2e: image frac > 1e-4 {frac_bad:.3g}, grads rel-L2 {ee:.3g}")
-    assert frac_bad <= 1e-3 and ee <= 1e-2
+    e2 = gpu_e2e(params, cfg.sh_degree, cam, W, H, BG, upstream=up, k_capacity=K + 4096)
+    check_e2e("gyroid_4m_2048 separate passes", o, e2, W, H, BG, e2["grads"], o["grads"], pre_bl=bl,
+              grad2d_g=e2["grad2d"], grad2d_o=o["grad2d"])
 
 
 @pytest.mark.parametrize("name", ["gyroid_4m_1024", "gyroid_4m_2048"])
@@ -122,74 +148,93 @@ def test_gyroid_4m_fused_step_with_l1(name):
     assert r["stall"] == 0
     _compare_forward(r, o["fwd"], W * H, "fused")
     assert r["loss"] == pytest.approx(o["loss"], rel=1e-5)
-    errs = [rel_l2(r["grad2d"][k, :n], o["grad2d"][k]) for k in range(9)]
+    keep = _stage_keep(o, r, W, H, target)
+    errs = [rel_l2(r["grad2d"][k, :n][keep], o["grad2d"][k][keep]) for k in range(9)]
     say("[fullsize] fused backward blend rel-L2 per row: " + " ".join(f"{e:.2g}" for e in errs))
     assert max(errs) <= GRAD_REL_L2
-    e = rel_l2(g.preprocess_backward_staged(), o["grads"])
+    e = rel_l2(g.preprocess_backward_staged()[:, keep], o["grads"][:, keep])
     say(f"[fullsize] preprocess backward from the staged sums rel-L2 {e:.3g}")
     assert e <= GRAD_REL_L2
     say(f"[fullsize] {name}: the whole step from the parameters")
-    e2 = GpuStep(params, cfg.sh_degree, cam, W, H, k_capacity=K + 4096)
-    e2.preprocess()
-    e2.bin_and_sort()
-    r2 = e2.step(BG, target)
-    assert r2["stall"] == 0
-    err = np.abs(r2["image"] - o["fwd"]["image"]).max(axis=-1)
-    frac_bad = float((err[~o["fwd"]["borderline"]] > IMG_MAX_ABS).mean())
-    ee = rel_l2(e2.preprocess_backward_staged(), o["grads"])
-    say(f"[fullsize] e2e fused: image frac > 1e-4 {frac_bad:.3g}, loss {r2['loss']:.7g} vs {o['loss']:.7g}, "
-        f"grads rel-L2 {ee:.3g}")
-    assert frac_bad <= 1e-3 and ee <= 1e-2
-    assert r2["loss"] == pytest.approx(o["loss"], rel=1e-4)
+    bl = preprocess_borderline(params, cfg.sh_degree, cam.flat(), W, H, o["proj"][0], o["proj"][1], o["radii"])
+    e2 = gpu_e2e(params, cfg.sh_degree, cam, W, H, BG, target=target, fused=True, k_capacity=K + 4096)
+    check_e2e(f"{name} fused", o, e2, W, H, BG, e2["grads"], o["grads"], target=target, pre_bl=bl,
+              grad2d_g=e2["grad2d"], grad2d_o=o["grad2d"])
+    assert e2["loss"] == pytest.approx(o["loss"], rel=1e-4)
 
 
+@pytest.mark.timeout(1200)
 @pytest.mark.skipif(os.environ.get("GSMI_FULLSIZE_18M", "1") == "0", reason="GSMI_FULLSIZE_18M=0")
-def test_bumps_18m_2048_sort_and_sampled_tiles():
+def test_bumps_18m_2048_fused_step():
+    """The 18.18M-Gaussian workload (the Miranda-scale row of the isosurface page's Table I) in the
+    bench's launch configuration, every stage in full: the preprocess over all Gaussians, the
+    sort bit-exact, the fused image pass (gs_render_plan + gs_render_step, whose tile walks reach
+    ~1.9M entries here) on the oracle's records and lists over the whole image, the preprocess
+    backward from the staged sums and the same call with the fused Adam update, then the whole
+    step from the parameters under the flip rule."""
+    import torch
+
     cfg = inputs.CONFIGS["bumps_18m_2048"]
     W = H = cfg.res
     say("[fullsize] bumps_18m_2048: drawing the scene")
     params = inputs.gaussian_params(cfg)
     cam = inputs.cameras_for(cfg)[0]
-    up = inputs.upstream_gradient(cfg, W, H)
+    target = np.random.default_rng(cfg.index).uniform(0, 1, (H, W, 3)).astype(np.float32)
     R, n = params.shape
-    c = cam.flat()
-    say("[fullsize] oracle preprocess and sort (all Gaussians)")
-    proj, radii, tiles = oracle.preprocess(params, cfg.sh_degree, c, W, H)
-    from parity_util import proj_f32
-    p32 = proj_f32(proj)
-    okeys, ovals = oracle.bin_sort(p32, radii, W, H)
-    T = oracle.n_tiles(W, H)
-    orng = oracle.ranges(okeys, T).reshape(-1, 2)
-    K = okeys.size
-    say(f"[fullsize] K = {K}; GPU sort of the oracle's records")
+    say("[fullsize] bumps_18m_2048: oracle step with the L1 loss (all Gaussians, all pixels)")
+    o = oracle_pipeline(params, cfg.sh_degree, cam.flat(), W, H, BG, target=target, margins=FWD_MARGINS)
+    K = o["keys"].size
+    lens = o["ranges"][:, 1].astype(np.int64) - o["ranges"][:, 0]
+    say(f"[fullsize] K = {K}, longest list {int(lens.max())}; GPU preprocess")
     g = GpuStep(params, cfg.sh_degree, cam, W, H, k_capacity=K + 4096)
-    g.load_proj(*records_from_oracle(p32, radii, tiles, W, H))
+    splat, tiles, _ = g.preprocess()
+    bl = _check_preprocess(params, cfg.sh_degree, cam, W, H, o, splat, tiles, "bumps_18m_2048")
+    del splat
+    say("[fullsize] GPU sort of the oracle's records")
+    g.load_proj(*records_from_oracle(o["p32"], o["radii"], o["tiles"], W, H))
     Kg, keys, vals, rg = g.bin_and_sort()
     assert Kg == K
-    np.testing.assert_array_equal(keys, okeys)
-    np.testing.assert_array_equal(vals, ovals)
-    np.testing.assert_array_equal(rg.reshape(-1, 2), orng)
-    # sampled tiles: the 8 longest lists and 24 seeded random non-empty ones
-    lens = orng[:, 1].astype(np.int64) - orng[:, 0]
-    nonempty = np.flatnonzero(lens > 0)
-    pick = set(np.argsort(-lens)[:8].tolist())
-    pick |= set(np.random.default_rng(inputs.seed_for(cfg, 4)).choice(nonempty, 24, replace=False).tolist())
-    mask = np.zeros(T, bool)
-    mask[sorted(pick)] = True
-    srng = np.where(mask[:, None], orng, 0).astype(np.uint32)
-    say(f"[fullsize] {mask.sum()} sampled tiles, {int(lens[mask].sum())} list entries; oracle blends")
-    ofwd = oracle.render_forward(p32, ovals, srng, W, H, BG, margins=FWD_MARGINS)
-    dl32 = up.astype(np.float32)
-    og2 = oracle.render_backward(p32, ovals, srng, W, H, dl32.astype(np.float64), BG)
-    g.load_lists(ovals, srng)
-    fwd = g.forward(BG)
-    tile_of_px = ((np.arange(H)[:, None] // 16) * ((W + 15) // 16) + np.arange(W)[None, :] // 16)
-    sel = mask[tile_of_px]
-    sub = {k: fwd[k][sel] for k in ("image", "last_contrib", "n_examined")}
-    osub = {k: ofwd[k][sel] for k in ("image", "last_contrib", "n_examined", "borderline")}
-    _compare_forward(sub, osub, int(sel.sum()), "sampled")
-    g.set_upstream(dl32)
-    g2, _ = g.backward()
-    errs = [rel_l2(g2[r, :n], og2[r]) for r in range(9)]
-    say("[fullsize] sampled backward blend rel-L2 per row: " + " ".join(f"{e:.2g}" for e in errs))
+    np.testing.assert_array_equal(keys, o["keys"])
+    np.testing.assert_array_equal(vals, o["vals"])
+    np.testing.assert_array_equal(rg.reshape(-1, 2), o["ranges"])
+    del keys, vals
+    say("[fullsize] fused image pass on the oracle's records and lists")
+    g.load_lists(o["vals"], o["ranges"])
+    r = g.step(BG, target)
+    assert r["stall"] == 0
+    _compare_forward(r, o["fwd"], W * H, "fused 18.18M")
+    assert r["loss"] == pytest.approx(o["loss"], rel=1e-5)
+    keep = _stage_keep(o, r, W, H, target)
+    errs = [rel_l2(r["grad2d"][k, :n][keep], o["grad2d"][k][keep]) for k in range(9)]
+    say("[fullsize] fused backward blend rel-L2 per row: " + " ".join(f"{e:.2g}" for e in errs))
     assert max(errs) <= GRAD_REL_L2
+    say("[fullsize] preprocess backward from the staged sums, then with the fused Adam update")
+    grads = g.preprocess_backward_staged()
+    e = rel_l2(grads[:, keep], o["grads"][:, keep])
+    eg = {k: rel_l2(grads[sl][:, keep], o["grads"][sl][:, keep]) for k, sl in GROUPS.items()}
+    say(f"[fullsize] preprocess backward rel-L2 {e:.3g} (" + ", ".join(f"{k} {v:.2g}" for k, v in eg.items()) + ")")
+    assert e <= GRAD_REL_L2 and max(eg.values()) <= GRAD_REL_L2
+    # Adam fused into the same pass: against the oracle's Adam on this gradient, on a sample of
+    # columns (every 97th Gaussian), to the float32 rounding of the update
+    rng = np.random.default_rng(77)
+    m0 = (1e-3 * rng.standard_normal((R, n))).astype(np.float32)
+    v0 = (1e-6 * rng.random((R, n))).astype(np.float32)
+    mt, vt = torch.from_numpy(m0).cuda(), torch.from_numpy(v0).cuda()
+    g.preprocess_backward_staged(adam=gsmi.make_adam(mt, vt, 3, 1e-3))
+    sub = np.arange(0, n, 97)
+    p_g = g.params[:, sub].cpu().numpy()
+    m_g, v_g = mt[:, sub].cpu().numpy(), vt[:, sub].cpu().numpy()
+    del mt, vt
+    th, gs, ms, vs = params[:, sub], grads[:, sub], m0[:, sub], v0[:, sub]
+    p_o, m_o, v_o = oracle.adam(th, gs, ms, vs, 3, 1e-3)
+    assert (np.abs(p_g - p_o) <= 1e-6 * np.maximum(np.abs(th), np.abs(p_o)) + 1e-12).all()
+    assert (np.abs(m_g - m_o) <= 1e-6 * np.maximum(np.abs(ms), np.abs(gs)) + 1e-12).all()
+    assert (np.abs(v_g - v_o) <= 1e-6 * v_o + 1e-15).all()
+    say(f"[fullsize] fused Adam on {sub.size} sampled Gaussians: max |dparam| {np.abs(p_g - p_o).max():.3g}")
+    del g, r, grads
+    torch.cuda.empty_cache()
+    say("[fullsize] bumps_18m_2048: the whole step from the parameters")
+    e2 = gpu_e2e(params, cfg.sh_degree, cam, W, H, BG, target=target, fused=True, k_capacity=K + 4096)
+    check_e2e("bumps_18m_2048 fused", o, e2, W, H, BG, e2["grads"], o["grads"], target=target, pre_bl=bl,
+              grad2d_g=e2["grad2d"], grad2d_o=o["grad2d"])
+    assert e2["loss"] == pytest.approx(o["loss"], rel=1e-4)
