@@ -26,6 +26,7 @@ SPLAT_FLOATS = 12  # 48-byte record: u, v, radius_x, radius_y | A, B, C, opacity
 EXPORTS = (
     "gs_version", "gs_last_error", "gs_preprocess", "gs_bin_and_sort_workspace", "gs_bin_and_sort",
     "gs_render_workspace", "gs_render_workspace_capacity", "gs_render_forward", "gs_loss_l1_workspace", "gs_loss_l1",
+    "gs_loss_l1_noalloc",
     "gs_loss_l1_dssim_workspace", "gs_loss_l1_dssim", "gs_render_backward",
     "gs_render_plan", "gs_render_step", "gs_render_init", "gs_render_status", "gs_preprocess_backward", "gs_preprocess_backward_staged", "gs_adam_step",
     "gs_preprocess_backward_accumulate", "gs_adam_batch", "gs_densify_stats", "gs_densify_workspace", "gs_densify",
@@ -99,6 +100,7 @@ def load(path: str = LIB_PATH):
     L.gs_render_forward.argtypes = [CP, i64, P, P, P, i64, ctypes.POINTER(ctypes.c_float), P, P, P, P, P, P, sz, P]
     L.gs_loss_l1_workspace.argtypes = [i64, ctypes.POINTER(sz)]
     L.gs_loss_l1.argtypes = [i64, P, P, P, P, P, sz, P]
+    L.gs_loss_l1_noalloc.argtypes = [i64, P, P, P, P, P]
     L.gs_loss_l1_dssim_workspace.argtypes = [i32, i32, ctypes.POINTER(sz)]
     L.gs_loss_l1_dssim.argtypes = [i32, i32, P, P, ctypes.c_float, P, P, P, sz, P]
     L.gs_render_backward.argtypes = [SP, P, CP, GsProj, P, P, i64, ctypes.POINTER(ctypes.c_float), P, P, P,
@@ -264,6 +266,12 @@ def loss_l1_workspace(count) -> int:
 def loss_l1(count, image, target, loss, dL_dimage, workspace, stream=None):
     _check(load().gs_loss_l1(int(count), _ptr(image), _ptr(target), _ptr(loss), _ptr(dL_dimage),
                              _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def loss_l1_noalloc(count, image, target, loss, dL_dimage, stream=None):
+    """gs_loss_l1 without a workspace (the library's static scratch; see gs_loss_l1_noalloc)."""
+    _check(load().gs_loss_l1_noalloc(int(count), _ptr(image), _ptr(target), _ptr(loss), _ptr(dL_dimage),
+                                     _stream(stream)))
 
 
 def loss_l1_dssim_workspace(width, height) -> int:

@@ -238,6 +238,16 @@ int gs_loss_l1_workspace(int64_t count, size_t* bytes);
 int gs_loss_l1(int64_t count, const float* image, const float* target, float* loss,
                float* dL_dimage, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* The L1 loss without allocation, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): gs_loss_l1 with its
+ * per-workgroup partial sums in a static device array of the library (256 KiB on each GPU it runs
+ * on, held until the process ends) instead of a workspace argument.  Same results as gs_loss_l1,
+ * bit for bit.  count <= 268,435,456 (2^28) elements, else GS_ERR_CAPACITY; GS_ERR_INVALID_ARGUMENT
+ * for count < 0 or a null pointer.  Calls that overlap on one GPU (two streams, two host threads)
+ * share that array and race: serialise them.  Asynchronous. */
+int gs_loss_l1_noalloc(int64_t count, const float* image, const float* target, float* loss,
+                       float* dL_dimage, hipStream_t stream);
+
 /* Bytes of device workspace gs_loss_l1_dssim needs for a width x height image (host-only
  * query): 36 bytes per SSIM window position plus per-workgroup sums, about 36 W H.
  * GS_ERR_INVALID_ARGUMENT if width or height is below 11 or bytes is null. */
