@@ -652,6 +652,82 @@ def test_backward_segments_on_deep_lists():
     torch.cuda.synchronize()
 
 
+def _records_at(u, v, depth, opacity, var, rgb, W, H):
+    """Screen-space records (the oracle's planar layout, float32 values) of isotropic Gaussians
+    of variance `var` px^2 at pixel positions (u, v), with their 3-sigma radii and tile counts."""
+    n = u.size
+    proj = np.zeros((10, n), np.float32)
+    proj[0], proj[1], proj[2], proj[3] = u, v, depth, opacity
+    proj[4], proj[5], proj[6] = 1.0 / var, 0.0, 1.0 / var
+    proj[7:10] = rgb
+    proj = proj.astype(np.float64)
+    r = np.int32(math.ceil(3.0 * math.sqrt(var)))
+    radii = np.full((2, n), r, np.int32)
+    rect = oracle.tile_rects(proj, radii, W, H)
+    tiles = ((rect[1] - rect[0]) * (rect[3] - rect[2])).astype(np.uint32)
+    return proj, radii, tiles
+
+
+def test_one_pixel_alpha_boxes_at_tile_corners_and_edges():
+    """Gaussians so small and faint that only the pixel under the centre reaches alpha 1/255 (an
+    alpha box of one pixel), on every tile's corner and edge pixels, several deep at different
+    depths, over a layer of wider ones: the blends' per-tile and per-quadrant boxes must keep the
+    one-pixel box of a tile's last pixel (15, 15) and drop the empty boxes of the neighbouring
+    tiles the 3-sigma rects reach.  Forward and backward on the oracle's records and lists."""
+    import torch
+    say("[parity] test_one_pixel_alpha_boxes_at_tile_corners_and_edges")
+    W, H = 72, 56  # ragged last tiles
+    rng = np.random.default_rng(44)
+    us, vs = [], []
+    for ty in range((H + 15) // 16):
+        for tx in range((W + 15) // 16):
+            for lx, ly in [(0, 0), (15, 0), (0, 15), (15, 15), (7, 15), (15, 8), (8, 7), (7, 8)]:
+                x, y = 16 * tx + lx, 16 * ty + ly
+                if x < W and y < H:
+                    us.append(x + 0.5)
+                    vs.append(y + 0.5)
+    us, vs = np.repeat(np.array(us), 3), np.repeat(np.array(vs), 3)  # three deep
+    m = us.size
+    var = 0.3  # the screen-space dilation alone: alpha one pixel off the centre is o e^(-1/0.6) ~ 0.19 o
+    # 70% faint (one-pixel boxes), the rest opaque enough for boxes of a few pixels
+    o_small = np.where(rng.uniform(size=m) < 0.7, rng.uniform(0.005, 0.02, m), rng.uniform(0.05, 0.9, m))
+    p1, r1, t1 = _records_at(us, vs, rng.uniform(2.0, 4.0, m), o_small, var,
+                             rng.uniform(0.0, 1.0, (3, m)), W, H)
+    q = 60  # a layer of wider Gaussians behind and in front
+    p2, r2, t2 = _records_at(rng.uniform(0, W, q), rng.uniform(0, H, q), rng.uniform(1.0, 5.0, q),
+                             rng.uniform(0.05, 0.5, q), 9.0, rng.uniform(0.0, 1.0, (3, q)), W, H)
+    proj = np.concatenate([p1, p2], axis=1)
+    radii = np.concatenate([r1, r2], axis=1)
+    tiles = np.concatenate([t1, t2])
+    n = proj.shape[1]
+    # the premise: most of the small ones have a one-pixel alpha box
+    one_px = (o_small >= 1 / 255) & (o_small * math.exp(-1.0 / (2 * var)) < 1 / 255)
+    assert one_px.mean() > 0.5
+    keys, vals = oracle.bin_sort(proj, radii, W, H)
+    rg = oracle.ranges(keys, oracle.n_tiles(W, H))
+    of = oracle.render_forward(proj, vals, rg, W, H, BG, margins=FWD_MARGINS)
+    up = rng.uniform(-1, 1, (H, W, 3)).astype(np.float32)
+    g2o = oracle.render_backward(proj, vals, rg, W, H, up.astype(np.float64), BG)
+    params = np.zeros((14, n), np.float32)
+    params[6] = 1.0
+    g = GpuStep(params, 0, inputs.lookat_camera((3.0, 0.0, 0.0), W, H), W, H)
+    g.load_proj(*records_from_oracle(proj, radii, tiles, W, H))
+    g.load_lists(vals, rg)
+    fwd = g.forward(BG)
+    ok = ~of["borderline"]
+    err = np.abs(fwd["image"] - of["image"]).max(axis=-1)
+    say(f"[parity]   {m} one-pixel-box candidates, K={keys.size}: image max err {err[ok].max():.2e}, "
+        f"{int((~ok).sum())} borderline px")
+    assert err[ok].max() <= IMG_MAX_ABS
+    np.testing.assert_array_equal(fwd["last_contrib"][ok], of["last_contrib"][ok])
+    np.testing.assert_array_equal(fwd["n_examined"][ok], of["n_examined"][ok])
+    g.set_upstream(up)
+    g2, _ = g.backward()
+    for r in range(9):
+        assert rel_l2(g2[r, :n], g2o[r]) <= GRAD_REL_L2, (r, rel_l2(g2[r, :n], g2o[r]))
+    torch.cuda.synchronize()
+
+
 def test_short_render_workspace_is_an_error_not_a_partial_result():
     """A render workspace short of the lists' intersections: with the true K every render call
     refuses on the host (GS_ERR_CAPACITY, nothing enqueued); with an understated K the calls run
@@ -682,7 +758,7 @@ def test_short_render_workspace_is_an_error_not_a_partial_result():
                                                  k=k),
         "backward": lambda k: gsmi.render_backward(g.scene, None, g.cam, g.proj, g.vals, g.ranges, BG, Tf, last, up,
                                                    g2, short, k=k),
-        "plan": lambda k: gsmi.render_plan(g.scene, g.cam, g.proj, g.ranges, short, k=k),
+        "plan": lambda k: gsmi.render_plan(g.scene, g.cam, g.proj, g.vals, g.ranges, short, k=k),
         "step": lambda k: gsmi.render_step(g.scene, g.cam, g.proj, g.vals, g.ranges, BG, tgt, img, Tf, last, loss, dl,
                                            short, k=k),
     }
@@ -701,7 +777,7 @@ def test_short_render_workspace_is_an_error_not_a_partial_result():
     with pytest.raises(gsmi.GsCapacityError):
         gsmi.render_status(short)
     ok = gsmi.new_render_ws(W, H, g.n, K)
-    gsmi.render_plan(g.scene, g.cam, g.proj, g.ranges, ok, k=K)
+    gsmi.render_plan(g.scene, g.cam, g.proj, g.vals, g.ranges, ok, k=K)
     gsmi.render_step(g.scene, g.cam, g.proj, g.vals, g.ranges, BG, tgt, img, Tf, last, loss, dl, ok, k=K)
     assert gsmi.render_status(ok) == (0, 0)
 
