@@ -385,7 +385,7 @@ def main():
         mark()
         g2 = buf.grad2d if args.unfused_adam else None
         if fused:  # forward, L1 and backward blend in one kernel; the sums stay staged
-            gsmi.render_plan(buf.scene, cam, buf.proj, buf.vals, buf.ranges, buf.render_ws, k=K)
+            gsmi.render_plan(buf.scene, cam, buf.proj, buf.ranges, buf.render_ws, k=K)
             mark()
             gsmi.render_step(buf.scene, cam, buf.proj, buf.vals, buf.ranges, bg, targets[view], buf.image,
                              buf.T_final, buf.last, buf.loss, buf.dLdI, buf.render_ws, grad2d=g2, blend_count=blends,

@@ -10,19 +10,20 @@
 // opacity and colour, "Gradients flow back ... to mu, Sigma, c and alpha").
 //
 // Work decomposition.  Each 8x8 quadrant of a tile is one wave64 (one pixel per lane); the
-// four quadrant waves of a tile share a workgroup.  The plan sorts each tile list into four
-// quadrant lists, in list order: the entries whose conservative alpha >= 1/255 box reaches the
-// quadrant, each with that box inside the quadrant (an entry reaches ~1.14 of its tile's four
-// quadrants).  A quadrant wave consumes its list in chunks of 64 entries: sixteen ballots (one per
-// quadrant column and row) turn the chunk's 64 boxes into a 64-bit mask per lane of the entries
-// whose box holds its pixel, and each lane walks only those, in list order, so lanes evaluate
-// different entries at the same time; the per-pixel results are those of the plain walk (an
-// entry outside a pixel's box has alpha < 1/255 there).  The forward's quadrant waves are
+// four quadrant waves of a tile share a workgroup.  A tile's list is consumed in chunks of 64
+// records.  For every record the conservative pixel box of its alpha >= 1/255 ellipse is
+// formed, and sixteen ballots (one per quadrant column and row) give every lane a 64-bit mask
+// of the chunk's records whose box holds its pixel.  Each lane then walks only its own records,
+// in list order, so lanes evaluate different records at the same time: a record costs VALU
+// work only on the pixels it can reach, and the per-pixel results are those of the plain walk
+// (a skipped record has alpha < 1/255 at that pixel).  The forward's quadrant waves are
 // independent (no workgroup barrier).  The forward also leaves, per pixel and chunk, the 64-bit
-// mask of the chunk's entries it composited; the backward walks exactly those entries (per 2x2
-// pixel block of 4 lanes, whose sums are formed with DPP), so no entry is tested twice.  The
-// backward's waves share per-entry gradient sums in LDS.  Bound: VALU issue and lane divergence,
-// not HBM.
+// mask of the chunk's entries it composited; the backward walks exactly those entries (per
+// 2x2 pixel block of 4 lanes, whose sums are formed with DPP), so no record is tested twice.
+// The backward's waves share per-entry gradient sums in LDS.
+// Workgroup b renders tile b: the hardware deals consecutive workgroups to the 8 XCDs in turn,
+// which spreads the (very uneven) per-tile work evenly over them.  Bound: VALU /
+// transcendental and LDS, not HBM.
 #include <algorithm>
 
 #include "gsmi_internal.h"
@@ -76,12 +77,38 @@ __device__ __forceinline__ unsigned long long quad_or(unsigned long long m) {
 }
 
 constexpr int kChunk = 64;  // records staged per chunk (one per lane)
-static_assert(kSeg == kBlock, "the backward gathers one segment's sums, one list position per thread");
+constexpr int kWin = kBlock;  // list entries whose gradient sums a workgroup gathers before adding them to grad2d
 
-// A pixel-index box [x0,x1] x [y0,y1] inside a quadrant (empty when x0 > x1).
+// Conservative pixel-index box [x0,x1] x [y0,y1] (relative to the quadrant origin, clamped to
+// 0..7) of the pixels whose centres can satisfy o e^power >= 1/255.  That region is the ellipse
+// d^T Q d <= tau, tau = 2 ln(255 o), with half-widths sqrt(tau C/det), sqrt(tau A/det); tau and
+// the box are widened so float32 rounding of the per-pixel test can never fall outside.  Empty
+// (x0 > x1) when o < 1/255 or the box misses the quadrant.
 struct Box {
   int x0, x1, y0, y1;
 };
+
+__device__ __forceinline__ Box alpha_box(float u, float v, float A, float B, float C, float o, int xq,
+                                         int yq) {
+  Box b{1, 0, 1, 0};
+  if (!(o >= kAlphaMin)) return b;
+  const float det = A * C - B * B;
+  float hx = 1e30f, hy = 1e30f;
+  if (det > 0.0f && __builtin_isfinite(det)) {
+    const float tau = 2.0f * __logf(255.0f * o) * 1.001f + 1e-3f;
+    hx = sqrtf(tau * C / det) * 1.001f + 0.01f;
+    hy = sqrtf(tau * A / det) * 1.001f + 0.01f;
+  }
+  // pixel index p has its centre at p + 0.5: p in [u - hx - 0.5, u + hx - 0.5]
+  const float fx0 = ceilf(u - hx - 0.5f - (float)xq), fx1 = floorf(u + hx - 0.5f - (float)xq);
+  const float fy0 = ceilf(v - hy - 0.5f - (float)yq), fy1 = floorf(v + hy - 0.5f - (float)yq);
+  if (!(fx0 <= 7.0f && fx1 >= 0.0f && fy0 <= 7.0f && fy1 >= 0.0f)) return b;  // also NaN
+  b.x0 = fx0 < 0.0f ? 0 : (int)fx0;
+  b.x1 = fx1 > 7.0f ? 7 : (int)fx1;
+  b.y0 = fy0 < 0.0f ? 0 : (int)fy0;
+  b.y1 = fy1 > 7.0f ? 7 : (int)fy1;
+  return b;
+}
 
 // Per-lane masks: bit e set iff record e's box contains the lane's pixel (lx, ly).  Lane e
 // holds record e's box; COL[x] / ROW[y] are ballots over the records.
@@ -105,7 +132,6 @@ struct Chunk {
   float4 geo[kChunk];   // u, v, -A/2, -B
   float4 col[kChunk];   // -C/2, o, r, g
   float b[kChunk];
-  uint32_t pos[kChunk];  // the entry's position in its tile list
 };
 
 // The fields of a record that the blend uses (zeros past the end of a list).  Only these are
@@ -230,26 +256,24 @@ __device__ __forceinline__ void drain_memory() {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Segment plan.  A tile list is cut into segments of kSeg = 256 entries:
-//   items(t) = ceil(len / kSeg) segments, the backward's work items (and the quadrant pass's
-//              windows),
-//   slots(t) = items(t) state slots if len > kSeg (one per segment boundary + the final state).
-// The forward's tile order groups the tiles by list-length class (1 + floor(log2 len), 0 for an
-// empty list), longest first.  Three kernels over blocks of 1024 tiles: per-block sums; one
-// workgroup turns them into per-block offsets and the header; then every tile writes bnd_off
-// (exclusive scan of slots), item_off and its place in the order.  Lists that need more
-// intersections than the workspace holds set the capacity flag and the skip word, and every later
-// kernel of the render calls then returns at once (the results are not valid; nothing is written
-// outside the workspace).
+// Segment plan.  For every tile, its list length len decides
+//   items(t) = ceil(len / SEG) backward work items (0 for an empty tile),
+//   slots(t) = ceil(len / SEG) state slots if len > SEG (one per boundary + the final state),
+// SEG = 2^shift is the smallest power of two >= 2^kSegShiftMin whose slots fit the workspace.
+// The forward's tile order groups the tiles by list-length class (1 + floor(log2 len), 0 for
+// an empty list), longest first.  Three kernels over blocks of 1024 tiles: per-block sums for
+// every candidate shift and class counts; one workgroup picks the shift and turns the sums
+// into per-block offsets; then every tile writes bnd_off (exclusive scan of slots), item_off
+// and its place in the order.
 // ---------------------------------------------------------------------------------------------
 constexpr int kPlanThreads = 1024;
 // list-length classes: 0 for an empty list, else 1 + floor(log2 len)
 constexpr int kLenClasses = 33;
 __device__ __forceinline__ int len_class(uint32_t len) { return len ? 32 - __clz((int)len) : 0; }
-__device__ __forceinline__ uint32_t seg_count(uint32_t len) { return (len + (uint32_t)kSeg - 1u) / (uint32_t)kSeg; }
-// per-block partial sums: slots, long tiles, items, class counts, and the largest list end (a
-// maximum, not a sum)
-constexpr int kPartSlots = 0, kPartLong = 1, kPartItems = 2, kPartClass = 3;
+constexpr int kShifts = 32 - kSegShiftMin;  // candidate shifts kSegShiftMin .. 31
+// per-block partial sums: slots(shift), long tiles(shift), non-empty tiles, class counts, and the
+// largest list end (a maximum, not a sum)
+constexpr int kPartSlots = 0, kPartLong = kShifts, kPartNonEmpty = 2 * kShifts, kPartClass = 2 * kShifts + 1;
 constexpr int kPartMaxEnd = kPartClass + kLenClasses;
 constexpr int kPartVals = kPartMaxEnd + 1;
 // per-block offsets: slots, items, then each class's first position in the order
@@ -278,7 +302,7 @@ __device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
 
 __global__ __launch_bounds__(kPlanThreads) void k_plan_count(const uint2* __restrict__ ranges, int T,
                                                              uint32_t* __restrict__ part) {
-  __shared__ uint32_t red[kPlanThreads / 64][3];
+  __shared__ uint32_t red[kPlanThreads / 64][2 * kShifts + 1];
   __shared__ uint32_t cls[kLenClasses];
   __shared__ uint32_t emax[kPlanThreads / 64];
   const int t = (int)(blockIdx.x * kPlanThreads + threadIdx.x), w = threadIdx.x >> 6;
@@ -293,16 +317,20 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_count(const uint2* __rest
   if (threadIdx.x < kLenClasses) cls[threadIdx.x] = 0u;
   __syncthreads();
   if (t < T) atomicAdd(&cls[len_class(len)], 1u);
-  const bool lg = len > (uint32_t)kSeg;
-  const uint32_t sl = wave_sum(lg ? seg_count(len) : 0u), nl = wave_sum(lg ? 1u : 0u), it = wave_sum(seg_count(len));
-  if ((threadIdx.x & 63) == 0) {
-    red[w][kPartSlots] = sl;
-    red[w][kPartLong] = nl;
-    red[w][kPartItems] = it;
+  for (int q = 0; q < kShifts; ++q) {
+    const int sh = kSegShiftMin + q;
+    const bool lg = len > (1u << sh);
+    const uint32_t sl = wave_sum(lg ? ((len - 1u) >> sh) + 1u : 0u), nl = wave_sum(lg ? 1u : 0u);
+    if ((threadIdx.x & 63) == 0) {
+      red[w][kPartSlots + q] = sl;
+      red[w][kPartLong + q] = nl;
+    }
   }
+  const uint32_t ne = wave_sum(len > 0u ? 1u : 0u);
+  if ((threadIdx.x & 63) == 0) red[w][kPartNonEmpty] = ne;
   __syncthreads();
   uint32_t* out = part + (size_t)blockIdx.x * kPartVals;
-  if (threadIdx.x < 3) {
+  if (threadIdx.x < 2 * kShifts + 1) {
     uint32_t v = 0;
     for (int k = 0; k < kPlanThreads / 64; ++k) v += red[k][threadIdx.x];
     out[threadIdx.x] = v;
@@ -315,8 +343,10 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_count(const uint2* __rest
   }
 }
 
-// One workgroup: the header, bnd_off[T] / item_off[T] and the per-block offsets.  The status words
-// are not cleared here: they gather the flags of every call until read.
+// One workgroup: the shift, the header, bnd_off[T] / item_off[T] and the per-block offsets.
+// The lists need room for their largest end: a workspace that holds fewer intersections sets the
+// capacity flag (the kernels then stay inside the workspace and the results are not valid).  The
+// status words are not cleared here: they gather the flags of every call until read.
 __global__ __launch_bounds__(kPlanThreads) void k_plan_scan(const uint32_t* __restrict__ part, int nb, int T,
                                                             uint32_t slots_cap, uint64_t entries_cap,
                                                             uint32_t* __restrict__ off,
@@ -325,6 +355,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_scan(const uint32_t* __re
                                                             uint32_t* __restrict__ item_off) {
   __shared__ uint32_t tot[kPartVals];
   __shared__ uint32_t cbase[kLenClasses];
+  __shared__ int s_q;
   if (threadIdx.x < kPartMaxEnd) {
     uint32_t v = 0;
     for (int b = 0; b < nb; ++b) v += part[(size_t)b * kPartVals + threadIdx.x];
@@ -336,37 +367,40 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_scan(const uint32_t* __re
   }
   __syncthreads();
   if (threadIdx.x == 0) {
+    int q = 0;  // the first shift whose slots fit (the last one if none does)
+    while (q < kShifts - 1 && tot[kPartSlots + q] > slots_cap) ++q;
+    s_q = q;
     uint32_t run = 0;  // classes longest first
     for (int c = kLenClasses - 1; c >= 0; --c) {
       cbase[c] = run;
       run += tot[kPartClass + c];
     }
-    const uint32_t slots = tot[kPartSlots], items = tot[kPartItems];
-    const bool short_ws = (uint64_t)tot[kPartMaxEnd] > entries_cap || slots > slots_cap;
+    const uint32_t slots = tot[kPartSlots + q];
+    const uint32_t items = slots + tot[kPartNonEmpty] - tot[kPartLong + q];
     bnd_off[T] = slots;
     item_off[T] = items;
-    hdr[kHdrShift] = (uint32_t)kSegShift;
+    hdr[kHdrShift] = (uint32_t)(kSegShiftMin + q);
     hdr[kHdrItems] = items;
     hdr[kHdrSlots] = slots;
     hdr[kHdrBwdNext] = 0u;
     hdr[kHdrFwdNext] = 0u;
     hdr[kHdrReady] = 0u;
     hdr[kHdrRole] = 0u;
-    hdr[kHdrSkip] = short_ws ? 1u : 0u;
-    if (short_ws) {
+    if ((uint64_t)tot[kPartMaxEnd] > entries_cap) {
       hdr[kHdrFlags] |= kFlagCapacity;
       hdr[kHdrNeed] = max(hdr[kHdrNeed], tot[kPartMaxEnd]);
     }
   }
   __syncthreads();
+  const int q = s_q;
   if (threadIdx.x == 0) {  // slot and item offsets of the blocks
     uint32_t rs = 0, ri = 0;
     for (int b = 0; b < nb; ++b) {
       const uint32_t* pb = part + (size_t)b * kPartVals;
       off[(size_t)b * kOffVals + 0] = rs;
       off[(size_t)b * kOffVals + 1] = ri;
-      rs += pb[kPartSlots];
-      ri += pb[kPartItems];
+      rs += pb[kPartSlots + q];
+      ri += pb[kPartSlots + q] + pb[kPartNonEmpty] - pb[kPartLong + q];
     }
   } else if (threadIdx.x <= kLenClasses) {  // each class's offsets of the blocks
     const int c = threadIdx.x - 1;
@@ -380,6 +414,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_scan(const uint32_t* __re
 
 __global__ __launch_bounds__(kPlanThreads) void k_plan_write(const uint2* __restrict__ ranges, int T,
                                                              const uint32_t* __restrict__ off,
+                                                             const uint32_t* __restrict__ hdr,
                                                              uint32_t* __restrict__ bnd_off,
                                                              uint32_t* __restrict__ item_off,
                                                              uint32_t* __restrict__ order) {
@@ -393,8 +428,9 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_write(const uint2* __rest
     const uint2 rg = ranges[t];
     len = rg.y - rg.x;
   }
-  const uint32_t k = seg_count(len);
-  const uint32_t sl = len > (uint32_t)kSeg ? k : 0u;
+  const uint32_t shift = hdr[kHdrShift];
+  const uint32_t k = len ? ((len - 1u) >> shift) + 1u : 0u;
+  const uint32_t sl = len > (1u << shift) ? k : 0u;
   const uint32_t pre_s = block_exscan_1024(sl, red32);  // (its barriers also publish cur)
   const uint32_t pre_i = block_exscan_1024(k, red32);
   if (t < T) {
@@ -404,200 +440,15 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_write(const uint2* __rest
   }
 }
 
-// The item list: one wave per tile writes the tile's items (tile, 0), (tile, 1), ... (for the fused
-// step, which publishes them as tiles finish, the marker of a not yet published item instead) and
-// the tile of each of its segments (wtile, read by the quadrant pass).
+// The item list: one wave per tile writes the tile's items (tile, 0), (tile, 1), ...; for the
+// fused step (empty), the marker of a not yet published item instead.
 constexpr uint32_t kNoTile = 0xFFFFFFFFu;
 __global__ __launch_bounds__(kBlock) void k_seg_items(int T, const uint32_t* __restrict__ item_off,
-                                                      uint2* __restrict__ items, uint32_t* __restrict__ wtile,
-                                                      bool empty) {
+                                                      uint2* __restrict__ items, bool empty) {
   const int t = (int)(blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6));
   if (t >= T) return;
   const uint32_t o = item_off[t], k = item_off[t + 1] - o;
-  for (uint32_t j = threadIdx.x & 63; j < k; j += 64) {
-    items[o + j] = make_uint2(empty ? kNoTile : (uint32_t)t, j);
-    wtile[o + j] = (uint32_t)t;
-  }
-}
-
-// ---------------------------------------------------------------------------------------------
-// Quadrant lists.  Each 8x8 quadrant of a tile (one wave64 of the blends) needs only the list
-// entries whose alpha box reaches it: at 4M Gaussians on a 2048x2048 image an entry reaches 1.14 of
-// its tile's four quadrants on average, and 16% reach none.  So the plan sorts each tile list's
-// entries into four quadrant lists, in list order, once; the blends then walk, per quadrant wave,
-// only its own list, with each entry's box inside the quadrant already formed.  Per segment of 256
-// entries (one wave each):
-//   k_quad_count  each entry's alpha box inside its tile (tbox), and per quadrant the number of
-//                 the segment's entries that reach it (qcnt);
-//   k_quad_scan   the exclusive scan of those counts over all segments (one workgroup): the
-//                 entries of segment w for quadrant q start at qcnt[4 w + q] - qcnt[4 w0 + q] in
-//                 the tile's quadrant list (w0 its first segment), which holds
-//                 qcnt[4 w1 + q] - qcnt[4 w0 + q] entries (w1 = w0 + its segments);
-//   k_quad_write  the quadrant lists: each entry's position in the tile list (qent) and its box
-//                 inside the quadrant (qbox).  The list of tile t and quadrant q sits at
-//                 4 start + q len of qent and qbox (start, len: the tile's range), which bounds
-//                 every list by its tile's length without a scan over tiles.
-// ---------------------------------------------------------------------------------------------
-// the alpha box misses the tile (x0 = 1 > x1 = 0: no box that holds a pixel packs to it; 0xFFFF would
-// be the box of the tile's last pixel alone)
-constexpr uint32_t kNoTileBox = 0x0001u;
-constexpr uint32_t kNoQBox = 0x8000u;     // the alpha box misses the quadrant
-
-// Conservative pixel-index box, relative to the tile origin (xt, yt) and clamped to 0..15, of the
-// pixels whose centres can satisfy o e^power >= 1/255, packed x0 | x1 << 4 | y0 << 8 | y1 << 12;
-// kNoTileBox when o < 1/255 or the box holds no pixel of the tile.  That region is the ellipse
-// d^T Q d <= tau, tau = 2 ln(255 o), with half-widths sqrt(tau C/det), sqrt(tau A/det); tau and
-// the half-widths are widened so float32 rounding of the per-pixel test can never fall outside.
-__device__ __forceinline__ uint32_t tile_box(float u, float v, float A, float B, float C, float o, int xt, int yt) {
-  if (!(o >= kAlphaMin)) return kNoTileBox;
-  const float det = A * C - B * B;
-  float hx = 1e30f, hy = 1e30f;
-  if (det > 0.0f && __builtin_isfinite(det)) {
-    const float tau = 2.0f * __logf(255.0f * o) * 1.001f + 1e-3f;
-    hx = sqrtf(tau * C / det) * 1.001f + 0.01f;
-    hy = sqrtf(tau * A / det) * 1.001f + 0.01f;
-  }
-  // pixel index p has its centre at p + 0.5: p in [u - hx - 0.5, u + hx - 0.5]
-  const float fx0 = ceilf(u - hx - 0.5f - (float)xt), fx1 = floorf(u + hx - 0.5f - (float)xt);
-  const float fy0 = ceilf(v - hy - 0.5f - (float)yt), fy1 = floorf(v + hy - 0.5f - (float)yt);
-  if (!(fx0 <= 15.0f && fx1 >= 0.0f && fy0 <= 15.0f && fy1 >= 0.0f && fx0 <= fx1 && fy0 <= fy1))
-    return kNoTileBox;  // misses the tile or holds no pixel centre (also NaN)
-  const uint32_t x0 = fx0 < 0.0f ? 0u : (uint32_t)fx0, x1 = fx1 > 15.0f ? 15u : (uint32_t)fx1;
-  const uint32_t y0 = fy0 < 0.0f ? 0u : (uint32_t)fy0, y1 = fy1 > 15.0f ? 15u : (uint32_t)fy1;
-  return x0 | (x1 << 4) | (y0 << 8) | (y1 << 12);
-}
-
-// Quadrant q's part of a tile box, relative to the quadrant origin, packed x0 | x1 << 3 | y0 << 6 |
-// y1 << 9; kNoQBox when it misses the quadrant.
-__device__ __forceinline__ uint32_t quad_box(uint32_t tb, int q) {
-  if (tb == kNoTileBox) return kNoQBox;
-  const int ox = (q & 1) * 8, oy = (q >> 1) * 8;
-  const int x0 = (int)(tb & 15u) - ox, x1 = (int)((tb >> 4) & 15u) - ox;
-  const int y0 = (int)((tb >> 8) & 15u) - oy, y1 = (int)((tb >> 12) & 15u) - oy;
-  if (x1 < 0 || x0 > 7 || y1 < 0 || y0 > 7) return kNoQBox;
-  return (uint32_t)max(x0, 0) | ((uint32_t)min(x1, 7) << 3) | ((uint32_t)max(y0, 0) << 6) |
-         ((uint32_t)min(y1, 7) << 9);
-}
-
-__device__ __forceinline__ Box decode_qbox(uint32_t b) {
-  Box r{1, 0, 1, 0};
-  if (b & kNoQBox) return r;
-  r.x0 = (int)(b & 7u);
-  r.x1 = (int)((b >> 3) & 7u);
-  r.y0 = (int)((b >> 6) & 7u);
-  r.y1 = (int)((b >> 9) & 7u);
-  return r;
-}
-
-struct QuadArgs {
-  int TX;
-  int64_t n;
-  const float4* splat;
-  const uint32_t* vals;
-  const uint2* ranges;
-  const uint32_t* item_off;
-  const uint32_t* wtile;
-  const uint32_t* hdr;
-  uint16_t* tbox;
-  uint32_t* qcnt;
-  uint32_t* qent;
-  uint16_t* qbox;
-};
-
-__device__ __forceinline__ uint32_t pick4(const uint32_t* v, int i) {
-  return i == 0 ? v[0] : (i == 1 ? v[1] : (i == 2 ? v[2] : v[3]));
-}
-
-// One wave per segment (a grid-stride loop over the segments of every tile).
-__global__ __launch_bounds__(kBlock) void k_quad_count(QuadArgs a) {
-  if (a.hdr[kHdrSkip]) return;
-  const uint32_t nseg = a.hdr[kHdrItems];
-  const int lane = threadIdx.x & 63;
-  for (uint32_t s = blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6); s < nseg; s += gridDim.x * (kBlock / 64)) {
-    const uint32_t t = a.wtile[s];
-    const uint2 rg = a.ranges[t];
-    const uint32_t lo = rg.x + (s - a.item_off[t]) * (uint32_t)kSeg, hi = min(lo + (uint32_t)kSeg, rg.y);
-    const int xt = (int)(t % (uint32_t)a.TX) * kTile, yt = (int)(t / (uint32_t)a.TX) * kTile;
-    uint32_t cnt[4] = {0u, 0u, 0u, 0u};
-    for (int r = 0; r < kSeg / 64; ++r) {
-      const uint32_t p = lo + (uint32_t)(r * 64 + lane);
-      uint32_t tb = kNoTileBox;
-      if (p < hi) {
-        const uint32_t gid = a.vals[p];
-        const float* rec = reinterpret_cast<const float*>(a.splat + 3 * ((int64_t)gid < a.n ? (int64_t)gid : 0));
-        const float2 uv = *reinterpret_cast<const float2*>(rec);
-        const float4 abco = *reinterpret_cast<const float4*>(rec + 4);
-        if ((int64_t)gid < a.n) tb = tile_box(uv.x, uv.y, abco.x, abco.y, abco.z, abco.w, xt, yt);
-        a.tbox[p] = (uint16_t)tb;
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) cnt[q] += (uint32_t)__popcll(__ballot(quad_box(tb, q) != kNoQBox));
-    }
-    if (lane < 4) a.qcnt[4 * (size_t)s + lane] = pick4(cnt, lane);
-  }
-}
-
-// One workgroup: qcnt[4 s + q] <- the exclusive scan over the segments, and the totals after the
-// last segment.
-__global__ __launch_bounds__(kPlanThreads) void k_quad_scan(const uint32_t* __restrict__ hdr, uint32_t* __restrict__ qcnt) {
-  __shared__ uint32_t red32[kPlanThreads / 64];
-  if (hdr[kHdrSkip]) return;
-  const int64_t nseg = hdr[kHdrItems];
-  const int64_t per = (nseg + kPlanThreads - 1) / kPlanThreads;
-  const int64_t lo = std::min<int64_t>(nseg, (int64_t)threadIdx.x * per), hi = std::min<int64_t>(nseg, lo + per);
-  uint4* q4 = reinterpret_cast<uint4*>(qcnt);
-  uint32_t s[4] = {0u, 0u, 0u, 0u};
-  for (int64_t b = lo; b < hi; ++b) {
-    const uint4 x = q4[b];
-    s[0] += x.x;
-    s[1] += x.y;
-    s[2] += x.z;
-    s[3] += x.w;
-  }
-  uint32_t run[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) run[q] = block_exscan_1024(s[q], red32);
-  for (int64_t b = lo; b < hi; ++b) {
-    const uint4 x = q4[b];
-    q4[b] = make_uint4(run[0], run[1], run[2], run[3]);
-    run[0] += x.x;
-    run[1] += x.y;
-    run[2] += x.z;
-    run[3] += x.w;
-  }
-  if (threadIdx.x == kPlanThreads - 1) q4[nseg] = make_uint4(run[0], run[1], run[2], run[3]);  // the totals
-}
-
-__global__ __launch_bounds__(kBlock) void k_quad_write(QuadArgs a) {
-  if (a.hdr[kHdrSkip]) return;
-  const uint32_t nseg = a.hdr[kHdrItems];
-  const int lane = threadIdx.x & 63;
-  const unsigned long long below = (1ull << lane) - 1ull;
-  for (uint32_t s = blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6); s < nseg; s += gridDim.x * (kBlock / 64)) {
-    const uint32_t t = a.wtile[s], s0 = a.item_off[t];
-    const uint2 rg = a.ranges[t];
-    const uint32_t len = rg.y - rg.x;
-    const uint32_t lo = rg.x + (s - s0) * (uint32_t)kSeg, hi = min(lo + (uint32_t)kSeg, rg.y);
-    uint32_t at[4];  // the next index of this segment's entries in each quadrant list
-#pragma unroll
-    for (int q = 0; q < 4; ++q) at[q] = a.qcnt[4 * (size_t)s + q] - a.qcnt[4 * (size_t)s0 + q];
-    for (int r = 0; r < kSeg / 64; ++r) {
-      const uint32_t p = lo + (uint32_t)(r * 64 + lane);
-      const uint32_t tb = p < hi ? (uint32_t)a.tbox[p] : kNoTileBox;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t qb = quad_box(tb, q);
-        const bool hit = qb != kNoQBox;
-        const unsigned long long bal = __ballot(hit);
-        if (hit) {
-          const uint64_t j = 4ull * rg.x + (uint64_t)q * len + at[q] + (uint32_t)__popcll(bal & below);
-          a.qent[j] = p - rg.x;
-          a.qbox[j] = (uint16_t)qb;
-        }
-        at[q] += (uint32_t)__popcll(bal);
-      }
-    }
-  }
+  for (uint32_t j = threadIdx.x & 63; j < k; j += 64) items[o + j] = make_uint2(empty ? kNoTile : (uint32_t)t, j);
 }
 
 // pixel index inside its tile of lane (lx, ly) of quadrant wave w
@@ -605,36 +456,9 @@ __device__ __forceinline__ int tile_pixel(int w, int lx, int ly) {
   return (((w >> 1) << 3) + ly) * kTile + ((w & 1) << 3) + lx;
 }
 
-// A quadrant-list entry as the blends load it: its position in the tile list (kNoPos outside
-// [lo, hi)) and its box inside the quadrant.  Loads are unconditional (an index outside the range
-// is replaced by lo, which must be a valid entry, and the result masked), as for the records.
-constexpr uint32_t kNoPos = 0xFFFFFFFFu;
-struct QEnt {
-  uint32_t pos, box;
-};
-__device__ __forceinline__ QEnt load_qent(const uint32_t* __restrict__ qent, const uint16_t* __restrict__ qbox,
-                                          uint64_t qb, uint32_t i, uint32_t lo, uint32_t hi) {
-  const bool in = i >= lo && i < hi;
-  const uint64_t j = qb + (in ? i : lo);
-  const uint32_t p = qent[j];
-  const uint32_t b = qbox[j];
-  QEnt e;
-  e.pos = in ? p : kNoPos;
-  e.box = in ? b : kNoQBox;
-  return e;
-}
-// The Gaussian at tile-list position pos (0xFFFFFFFF for kNoPos: a record the blends never use).
-// Requires a non-empty list.
-__device__ __forceinline__ uint32_t gid_at(const uint32_t* __restrict__ vals, uint32_t start, uint32_t pos) {
-  const uint32_t v = vals[start + (pos != kNoPos ? pos : 0u)];
-  return pos != kNoPos ? v : 0xFFFFFFFFu;
-}
-
 // ---------------------------------------------------------------------------------------------
-// Forward.  Each quadrant wave walks its tile's quadrant list in chunks of 64 entries.  Besides the
-// image, a tile whose list is longer than one segment leaves each pixel's (T, C) at every segment
-// boundary before its last blended entry, and its final (T, C), in the render workspace; a
-// chunk's composited masks are stored per quadrant-list chunk.
+// Forward.  Besides the image, a tile whose list is longer than one segment leaves each pixel's
+// (T, C) at every segment boundary it reaches and its final (T, C) in the render workspace.
 // ---------------------------------------------------------------------------------------------
 struct FwdArgs {
   int W, H, TX, T;
@@ -653,10 +477,6 @@ struct FwdArgs {
   uint2* masks;
   uint64_t mask_cap;
   const uint32_t* order;
-  const uint32_t* item_off;
-  const uint32_t* qcnt;
-  const uint32_t* qent;
-  const uint16_t* qbox;
   // the fused step only: the L1 loss against the target image, per pixel
   const float* target;
   float* dLdI;
@@ -664,90 +484,68 @@ struct FwdArgs {
   float inv_n;       // 1 / (3 W H)
 };
 
-// The tile-list range of quadrant q of tile t inside qent / qbox, its length and its first mask chunk.
-__device__ __forceinline__ void quad_list(const uint32_t* __restrict__ qcnt, const uint32_t* __restrict__ item_off,
-                                          int tile, int q, uint32_t start, uint32_t len, uint64_t& qb,
-                                          uint32_t& nq, uint64_t& mb) {
-  const uint32_t s0 = item_off[tile], s1 = item_off[tile + 1];
-  nq = qcnt[4 * (size_t)s1 + q] - qcnt[4 * (size_t)s0 + q];
-  qb = 4ull * start + (uint64_t)q * len;
-  mb = qb / kChunk + 4ull * (uint64_t)tile + (uint64_t)q;
-}
-
 // One tile by the workgroup's four quadrant waves (kStep: the fused step, which also takes the
 // pixel's L1 loss and gradient and hands its state to other workgroups at device scope).
 template <bool kStep>
-__device__ void forward_tile(const FwdArgs& a, int tile, Chunk* stg) {
+__device__ void forward_tile(const FwdArgs& a, uint32_t shift, int tile, Chunk* stg) {
   const int W = a.W, H = a.H, TX = a.TX;
   const int64_t n = a.n;
   const float4* __restrict__ splat = a.splat;
   const uint32_t* __restrict__ vals = a.vals;
-  const uint32_t* __restrict__ qent = a.qent;
-  const uint16_t* __restrict__ qbox = a.qbox;
   uint2* __restrict__ masks = a.masks;
   const uint64_t mask_cap = a.mask_cap;
   const int tx = tile % TX, ty = tile / TX;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   Chunk& S = stg[w];
-  const int lx = lane & 7, ly = lane >> 3;  // the quadrant's pixels row-major: lane = ly * 8 + lx
+  const int lx = lane & 7, ly = lane >> 3;
   const int xq = tx * kTile + (w & 1) * 8, yq = ty * kTile + (w >> 1) * 8;  // quadrant origin
   const int px = xq + lx, py = yq + ly;
   const bool inside = px < W && py < H;
   const float pxc = (float)px + 0.5f, pyc = (float)py + 0.5f;
   const uint2 rg = a.ranges[tile];
-  const uint32_t start = rg.x, len = rg.y - rg.x;
-  const bool long_list = len > (uint32_t)kSeg;
+  const uint32_t start = rg.x, end = rg.y, len = end - start;
+  const uint32_t seg_mask = (1u << shift) - 1u;
+  const bool long_list = len > seg_mask + 1u;
   const int pix = tile_pixel(w, lx, ly);
   float4* const st = a.slots + (size_t)(long_list ? a.bnd_off[tile] : 0u) * (kTile * kTile) + pix;
-  uint64_t qb, mb;
-  uint32_t nq;
-  quad_list(a.qcnt, a.item_off, tile, w, start, len, qb, nq, mb);
+  const uint64_t cbase = (uint64_t)(start / kChunk) + (uint64_t)tile;  // the tile's first mask chunk
 
   float Tr = 1.0f, c0 = 0.f, c1 = 0.f, c2 = 0.f;
   uint32_t last = 0, examined = len, blended = 0;
   uint32_t evaluated = 0;  // (pixel, entry) pairs whose alpha is evaluated: the mask bits walked
   bool done = !inside;
-  uint32_t nb = (uint32_t)kSeg;  // the next segment boundary (list position) whose state is owed
 
-  if (nq > 0) {
-    const uint32_t nch = (nq + kChunk - 1) / kChunk;
-    // three loads deep: quadrant entry -> Gaussian -> record.  The first chunk's record has landed
-    // before the loop; each pass has the next chunk's record, the one after's Gaussian and the
-    // third's quadrant entry in flight.  A chunk's composited mask is stored at the start of the
-    // next pass, so that pass's work covers the store's latency.
-    QEnt qc = load_qent(qent, qbox, qb, (uint32_t)lane, 0u, nq);
-    QEnt qn = load_qent(qent, qbox, qb, (uint32_t)(kChunk + lane), 0u, nq);
-    QEnt qnn = load_qent(qent, qbox, qb, (uint32_t)(2 * kChunk + lane), 0u, nq);
-    Raw cur = load_raw(splat, gid_at(vals, start, qc.pos), n);
-    uint32_t gn = gid_at(vals, start, qn.pos);
+  if (len > 0) {
+    uint32_t gnext = load_gid(vals, start + lane, end, start);
+    Raw cur = load_raw(splat, gnext, n);
+    gnext = load_gid(vals, start + kChunk + lane, end, start);
+    // The first chunk has landed before the loop starts; each pass waits for the next chunk's
+    // loads only at its end.  A chunk's composited mask is stored at the start of the next
+    // pass, so that pass's work covers the store's latency.
     settle(cur);
     unsigned long long pend = 0ull;
     uint64_t pend_mc = ~0ull;
-    for (uint32_t c = 0; c < nch; ++c) {
+    for (uint32_t b0 = start; b0 < end; b0 += kChunk) {
       if (__ballot(!done) == 0ull) break;
       if (pend_mc < mask_cap)
-        put_u2<kStep>(masks + pend_mc * kChunk + lane, make_uint2((uint32_t)pend, (uint32_t)(pend >> 32)));
-      const Raw nxt = load_raw(splat, gn, n);  // next chunk in flight
-      const uint32_t gnn = gid_at(vals, start, qnn.pos);
-      const QEnt q3 = load_qent(qent, qbox, qb, (c + 3u) * kChunk + (uint32_t)lane, 0u, nq);
+        put_u2<kStep>(masks + pend_mc * (kTile * kTile) + pix, make_uint2((uint32_t)pend, (uint32_t)(pend >> 32)));
+      const Raw nxt = load_raw(splat, gnext, n);  // next chunk in flight
+      gnext = load_gid(vals, b0 + 2 * kChunk + lane, end, start);
+      const uint32_t rel = b0 - start;
+      if (long_list && rel != 0u && (rel & seg_mask) == 0u)  // state at segment boundary rel
+        put_f4<kStep>(st + (size_t)((rel >> shift) - 1u) * (kTile * kTile), make_float4(Tr, c0, c1, c2));
       put(S, lane, cur);
-      S.pos[lane] = qc.pos;
-      // every lane takes part in the ballots: lane e holds entry e's box
-      unsigned long long m = lane_mask(decode_qbox(qc.box), lx, ly);
+      const Box bx = alpha_box(cur.uv.x, cur.uv.y, cur.abco.x, cur.abco.y, cur.abco.z, opacity_of(cur, n), xq, yq);
+      // every lane takes part in the ballots: lane e holds record e's box
+      unsigned long long m = lane_mask(bx, lx, ly);
       if (done) m = 0ull;
       evaluated += (uint32_t)__popcll(m);
       wave_sync_lds();
-      unsigned long long cm = 0ull;  // the chunk's entries composited at this pixel
-      while (m) {  // this lane's entries, in list order
+      const uint32_t base = rel + 1u;  // 1-based position of slot 0
+      unsigned long long cm = 0ull;    // the chunk's entries composited at this pixel
+      while (m) {  // this lane's records, in list order
         const int e = lowest_bit(m);
         m &= m - 1ull;
-        const uint32_t pe = S.pos[e];
-        if (long_list) {  // the state at each segment boundary passed since the last entry
-          while (pe >= nb) {
-            put_f4<kStep>(st + (size_t)(nb / (uint32_t)kSeg - 1u) * (kTile * kTile), make_float4(Tr, c0, c1, c2));
-            nb += (uint32_t)kSeg;
-          }
-        }
         const float4 g = S.geo[e];
         const float4 cl = S.col[e];
         const float bb = S.b[e];
@@ -756,7 +554,7 @@ __device__ void forward_tile(const FwdArgs& a, int tile, Chunk* stg) {
         const float alpha = fminf(kAlphaMax, eval_oG(cl.y, power));
         if (power <= 0.0f && alpha >= kAlphaMin) {
           const float Tn = Tr * (1.0f - alpha);
-          const uint32_t pos = pe + 1u;  // 1-based list position
+          const uint32_t pos = base + (uint32_t)e;
           if (Tn < kTMin) {
             done = true;
             examined = pos;
@@ -775,19 +573,15 @@ __device__ void forward_tile(const FwdArgs& a, int tile, Chunk* stg) {
         }
       }
       pend = cm;
-      pend_mc = mb + c;
+      pend_mc = cbase + rel / kChunk;
       wave_sync_lds();  // this chunk's reads finish before the next chunk is staged
       cur = nxt;
-      qc = qn;
-      qn = qnn;
-      qnn = q3;
-      gn = gnn;
     }
     if (pend_mc < mask_cap)
-      put_u2<kStep>(masks + pend_mc * kChunk + lane, make_uint2((uint32_t)pend, (uint32_t)(pend >> 32)));
+      put_u2<kStep>(masks + pend_mc * (kTile * kTile) + pix, make_uint2((uint32_t)pend, (uint32_t)(pend >> 32)));
+    if (long_list)  // final state
+      put_f4<kStep>(st + (size_t)((len - 1u) >> shift) * (kTile * kTile), make_float4(Tr, c0, c1, c2));
   }
-  if (long_list)  // final state
-    put_f4<kStep>(st + (size_t)((len - 1u) / (uint32_t)kSeg) * (kTile * kTile), make_float4(Tr, c0, c1, c2));
 
   float l1 = 0.f;  // the pixel's sum of |image - target| (fused step)
   if (inside) {
@@ -841,15 +635,15 @@ __device__ void forward_tile(const FwdArgs& a, int tile, Chunk* stg) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Backward.  Work item = (tile, segment k): list positions [k kSeg, (k+1) kSeg), walked back to
-// front by each quadrant wave over the segment's part of its quadrant list.  A pixel whose last
-// blended entry lies beyond the segment starts from the forward's state at the segment's end: T
-// there, and the colour behind it, (C_final - C_boundary) / T_boundary; otherwise from T_final
-// with nothing behind.  The segments of one tile are independent, so a long list is spread over
-// many CUs.  Persistent workgroups take items from a counter in the workspace until none are left.
+// Backward.  Work item = (tile, segment k): list positions [k SEG, (k+1) SEG), walked back to
+// front by each quadrant wave over its pixels.  A pixel whose last blended entry lies beyond
+// the segment starts from the forward's state at the segment's end: T there, and the colour
+// behind it, (C_final - C_boundary) / T_boundary; otherwise from T_final with nothing behind.
+// The segments of one tile are independent, so a long list is spread over many CUs.
+// Persistent workgroups take items from a counter in the workspace until none are left.
 // Each 2x2 pixel block walks the entries its pixels composited (the forward's masks), back to
-// front; the block's nine gradient sums per entry go into the workgroup's LDS sums over the
-// segment's 256 list positions, whose sums then go to the staging area, one row per (entry, tile).
+// front; the block's nine gradient sums per entry go into the workgroup's LDS sums over a window
+// of 256 entries, whose sums then go to the staging area, one row per (entry, tile).
 // ---------------------------------------------------------------------------------------------
 struct BwdArgs {
   int W, H, TX, TY;
@@ -865,10 +659,6 @@ struct BwdArgs {
   const float4* slots;
   const uint2* masks;
   uint64_t mask_cap;
-  const uint32_t* item_off;
-  const uint32_t* qcnt;
-  const uint32_t* qent;
-  const uint16_t* qbox;
   const uint32_t* goff;
   const uint32_t* goff_blk;
   float* staging;
@@ -877,21 +667,19 @@ struct BwdArgs {
 
 // LDS of a blending workgroup
 struct BlendShared {
-  Chunk stg[4];         // per quadrant wave: its current chunk
-  float acc[9][kSeg];   // the backward's gradient sums over the segment's list positions
+  Chunk stg[4];        // per quadrant wave: its current chunk
+  float acc[9][kWin];  // the backward's gradient sums over a window of entries
   uint32_t mx[4];
 };
 
 // One work item (tile, segment k) by the workgroup's four quadrant waves (kStep: inside the
 // fused step, which reads the tile's state from other workgroups at device scope).
 template <bool kStep>
-__device__ void backward_item(const BwdArgs& a, uint2 it, BlendShared& sh) {
+__device__ void backward_item(const BwdArgs& a, uint32_t shift, uint2 it, BlendShared& sh) {
   const int W = a.W, H = a.H, TX = a.TX, TY = a.TY;
   const int64_t n = a.n;
   const float4* __restrict__ splat = a.splat;
   const uint32_t* __restrict__ vals = a.vals;
-  const uint32_t* __restrict__ qent = a.qent;
-  const uint16_t* __restrict__ qbox = a.qbox;
   const uint2* __restrict__ masks = a.masks;
   const uint64_t mask_cap = a.mask_cap;
   const uint32_t* __restrict__ goff = a.goff;
@@ -900,13 +688,12 @@ __device__ void backward_item(const BwdArgs& a, uint2 it, BlendShared& sh) {
   const uint64_t staging_cap = a.staging_cap;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   Chunk& S = sh.stg[w];
-  float(*acc)[kSeg] = sh.acc;
+  float(*acc)[kWin] = sh.acc;
   uint32_t* s_mx = sh.mx;
   // lanes 4 q .. 4 q + 3 are the 2x2 pixel block q of the quadrant (blocks row-major, pixels
   // row-major inside a block): each block reduces over one DPP quad
   const int lx = ((lane >> 2) & 3) * 2 + (lane & 1), ly = (lane >> 4) * 2 + ((lane >> 1) & 1);
   const int pix = tile_pixel(w, lx, ly);
-  const int pq = ly * 8 + lx;  // the pixel's lane in the forward's masks
   const int tile = (int)it.x;
   const uint32_t k = it.y;
   const int tx = tile % TX, ty = tile / TX;
@@ -915,7 +702,8 @@ __device__ void backward_item(const BwdArgs& a, uint2 it, BlendShared& sh) {
   const bool inside = px < W && py < H;
   const float pxc = (float)px + 0.5f, pyc = (float)py + 0.5f;
   const uint2 rg = a.ranges[tile];
-  const uint32_t start = rg.x, len = rg.y - rg.x;
+  const uint32_t start = rg.x, end = rg.y, len = rg.y - rg.x;
+  const uint64_t cbase = (uint64_t)(start / kChunk) + (uint64_t)tile;  // the tile's first mask chunk
 
   float Tr = 0.f, g0 = 0.f, g1 = 0.f, g2 = 0.f, bgT = 0.f;
   float S0 = 0.f, S1 = 0.f, S2 = 0.f;  // colour accumulated behind the current entry, / T_{k+1}
@@ -934,199 +722,179 @@ __device__ void backward_item(const BwdArgs& a, uint2 it, BlendShared& sh) {
   if (lane == 0) s_mx[w] = mx;
   __syncthreads();
   const uint32_t mxb = max(max(s_mx[0], s_mx[1]), max(s_mx[2], s_mx[3]));
-  const uint32_t seg_lo = k * (uint32_t)kSeg;
-  const uint32_t seg_end = seg_lo + (uint32_t)kSeg;
-  const uint32_t hi_w = min(seg_end, min(mx, len));   // this wave's pixels blend nothing at or above
-  const uint32_t hi_b = min(seg_end, min(mxb, len));  // the workgroup's pixels likewise
+  const uint32_t seg_lo = k << shift;
+  const uint32_t seg_end = seg_lo + (1u << shift);
+  const uint32_t hi_w = min(seg_end, min(mx, len));   // this wave walks [seg_lo, hi_w)
+  const uint32_t hi_b = min(seg_end, min(mxb, len));  // the workgroup walks [seg_lo, hi_b)
   if (seg_lo >= hi_b) return;  // workgroup-uniform: the segment lies behind every pixel's walk
   if (last > seg_end) {  // the pixel's walk starts behind this segment
     const float4* st = a.slots + (size_t)a.bnd_off[tile] * (kTile * kTile) + pix;
     const float4 sb = get_f4<kStep>(st + (size_t)k * (kTile * kTile));
-    const float4 sf = get_f4<kStep>(st + (size_t)((len - 1u) / (uint32_t)kSeg) * (kTile * kTile));
+    const float4 sf = get_f4<kStep>(st + (size_t)((len - 1u) >> shift) * (kTile * kTile));
     const float inv = 1.0f / sb.x;  // T >= 1e-4 at every boundary
     Tr = sb.x;
     S0 = (sf.y - sb.y) * inv;
     S1 = (sf.z - sb.z) * inv;
     S2 = (sf.w - sb.w) * inv;
   }
-  // the segment's entries in this wave's quadrant list: [qa, qz)
-  uint64_t qb, mb;
-  uint32_t nq;
-  quad_list(a.qcnt, a.item_off, tile, w, start, len, qb, nq, mb);
-  const uint32_t s0 = a.item_off[tile];
-  const uint32_t base = a.qcnt[4 * (size_t)s0 + w];
-  const uint32_t qa = a.qcnt[4 * (size_t)(s0 + k) + w] - base, qz = a.qcnt[4 * (size_t)(s0 + k + 1u) + w] - base;
 
+  // windows of kWin entries, top down; the waves walk a window independently, then the
+  // workgroup adds the window's sums to grad2d
+  for (uint32_t wtop = hi_b; wtop > seg_lo;) {
+    const uint32_t wlo = seg_lo + ((wtop - 1u - seg_lo) & ~(uint32_t)(kWin - 1));
 #pragma unroll
-  for (int q = 0; q < 9; ++q) acc[q][tid] = 0.f;
-  __syncthreads();
-  if (hi_w > seg_lo && qz > qa) {  // wave-uniform
-    // chunks of the forward's (64 quadrant entries each, j = jtop .. jlo), cut to [qa, qz), top down
-    const uint32_t jlo = qa / kChunk, jtop = (qz - 1u) / kChunk, nchunks = jtop - jlo + 1u;
-    auto qe_of = [&](uint32_t c) -> QEnt {  // lane's entry of chunk c (none past the last chunk)
-      const bool live = c < nchunks;
-      const uint32_t j = live ? jtop - c : jtop;
-      return load_qent(qent, qbox, qb, j * kChunk + (uint32_t)lane, qa, live ? qz : qa);
-    };
-    auto mask_of = [&](uint32_t c) -> uint2 {
-      const uint64_t mc = mb + (c < nchunks ? jtop - c : jtop);
-      return get_u2<kStep>(masks + (mc < mask_cap ? mc : 0) * kChunk + pq);
-    };
-    QEnt qc = qe_of(0);
-    QEnt qn = qe_of(1);
-    Raw cur = load_raw(splat, gid_at(vals, start, qc.pos), n);
-    uint2 mcur = mask_of(0);
-    uint32_t gn = gid_at(vals, start, qn.pos);
-    QEnt qnn = qe_of(2);
-    for (uint32_t c = 0; c < nchunks; ++c) {
-      const uint32_t j = jtop - c;
-      const Raw nxt = load_raw(splat, gn, n);  // next chunk in flight
-      const uint2 mnxt = mask_of(c + 1);
-      const uint32_t gnn = gid_at(vals, start, qnn.pos);
-      const QEnt q3 = qe_of(c + 3);
-      put(S, lane, cur);
-      S.pos[lane] = qc.pos;
-      wave_sync_lds();
-      // The entries this pixel composited in the chunk (the forward's mask), restricted to the
-      // segment's: exactly those with power <= 0, alpha >= 1/255 in front of the pixel's stop.
-      // Each 2x2 pixel block of the quadrant (4 lanes) takes the entries any of its pixels
-      // composited, back to front, its lanes on the same entry; the block's nine sums are formed in
-      // registers and added to the segment's sums by one lane of the block.
-      // The forward stops walking once every pixel of the wave has stopped, so a chunk's mask was
-      // written only if the walk reached it: exactly when one of its entries lies in front of the
-      // wave's largest last_contrib (a pixel blended that entry or a later one).  Other chunks hold
-      // no composited entry and a stale mask, and take none.
-      const uint32_t jb = j * kChunk;
-      const uint32_t blo = qa > jb ? qa - jb : 0u, bhi = min(qz - jb, (uint32_t)kChunk);
-      const unsigned long long in_seg =
-          (bhi >= 64u ? ~0ull : ((1ull << bhi) - 1ull)) & ~((1ull << blo) - 1ull);
-      const bool walked = __ballot(qc.pos < hi_w) != 0ull;  // kNoPos never is
-      const unsigned long long mine =
-          (walked && mb + j < mask_cap ? ((unsigned long long)mcur.y << 32) | mcur.x : 0ull) & in_seg;
-      unsigned long long rem = quad_or(mine);
-      for (;;) {
-        const bool has = rem != 0ull;
-        if (__ballot(has) == 0ull) break;
-        const int e = has ? highest_bit(rem) : 0;
-        rem &= ~(1ull << e);
-        const float4 g = S.geo[e];  // one address per block: a broadcast within the block
-        const float4 cl = S.col[e];
-        const float cb = S.b[e];
-        const uint32_t pe = S.pos[e];
-        const float dx = pxc - g.x, dy = pyc - g.y;
-        const float power = eval_power(g.z, g.w, cl.x, dx, dy);
-        const float G = __expf(power);
-        const float oG = __fmul_rn(cl.y, G);  // the same operations as eval_oG
-        const float alpha = fminf(kAlphaMax, oG);
-        const bool act = has && ((mine >> e) & 1ull);
-        const float om = 1.0f - alpha;
-        const float rom = __builtin_amdgcn_rcpf(om);  // om >= 0.01
-        const float Tk = Tr * rom;                    // transmittance in front of this entry
-        const float wt = alpha * Tk;
-        const float cr = cl.z, cg = cl.w;
-        const float dL_dalpha = Tk * ((cr - S0) * g0 + (cg - S1) * g1 + (cb - S2) * g2) - bgT * rom;
-        const bool unclamped = act && oG <= kAlphaMax;  // alpha = o G depends on o and power
-        const float dpow = unclamped ? oG * dL_dalpha : 0.0f;
-        // moments of dL/dpower over the pixels; the conic gradients are linear in them
-        float v[9];
-        v[0] = dx * dpow;
-        v[1] = dy * dpow;
-        v[2] = dx * v[0];
-        v[3] = dy * v[0];
-        v[4] = dy * v[1];
-        v[5] = unclamped ? G * dL_dalpha : 0.0f;
-        v[6] = act ? wt * g0 : 0.0f;
-        v[7] = act ? wt * g1 : 0.0f;
-        v[8] = act ? wt * g2 : 0.0f;
-        if (act) {
-          S0 = alpha * cr + om * S0;
-          S1 = alpha * cg + om * S1;
-          S2 = alpha * cb + om * S2;
-          Tr = Tk;
+    for (int q = 0; q < 9; ++q) acc[q][tid] = 0.f;
+    __syncthreads();
+    const uint32_t whi = min(wtop, hi_w);
+    if (whi > wlo) {  // wave-uniform
+      // the window's chunks j (tile-relative entries [64 j, 64 j + 64)), top down
+      const uint32_t jlo = wlo / kChunk, jtop = (whi - 1u) / kChunk, nchunks = jtop - jlo + 1u;
+      // list entry of lane `lane` in chunk c (c >= nchunks: past the end of the list)
+      auto gid_of = [&](uint32_t c) -> uint32_t {
+        return load_gid(vals, c < nchunks ? start + (jtop - c) * kChunk + lane : end, end, start);
+      };
+      auto mask_of = [&](uint32_t c) -> uint2 {
+        const uint64_t mc = cbase + (c < nchunks ? jtop - c : jtop);
+        return get_u2<kStep>(masks + (mc < mask_cap ? mc : 0) * (kTile * kTile) + pix);
+      };
+      uint32_t gnext = gid_of(0);
+      Raw cur = load_raw(splat, gnext, n);
+      uint2 mcur = mask_of(0);
+      gnext = gid_of(1);
+      for (uint32_t c = 0; c < nchunks; ++c) {
+        const uint32_t j = jtop - c;
+        const Raw nxt = load_raw(splat, gnext, n);  // next chunk in flight
+        const uint2 mnxt = mask_of(c + 1);
+        gnext = gid_of(c + 2);
+        put(S, lane, cur);
+        wave_sync_lds();
+        // The entries this pixel composited in the chunk (the forward's mask): exactly those
+        // with power <= 0, alpha >= 1/255 in front of the pixel's stop.  Each 2x2 pixel block
+        // of the quadrant (4 lanes) takes the entries any of its pixels composited, back to
+        // front, its lanes on the same entry; the block's nine sums are formed in registers
+        // and added to the window's sums by one lane of the block.
+        const unsigned long long mine =
+            cbase + j < mask_cap ? ((unsigned long long)mcur.y << 32) | mcur.x : 0ull;
+        unsigned long long rem = quad_or(mine);
+        const uint32_t wbase = j * kChunk - wlo;  // window position of slot 0
+        for (;;) {
+          const bool has = rem != 0ull;
+          if (__ballot(has) == 0ull) break;
+          const int e = has ? highest_bit(rem) : 0;
+          rem &= ~(1ull << e);
+          const float4 g = S.geo[e];  // one address per block: a broadcast within the block
+          const float4 cl = S.col[e];
+          const float cb = S.b[e];
+          const float dx = pxc - g.x, dy = pyc - g.y;
+          const float power = eval_power(g.z, g.w, cl.x, dx, dy);
+          const float G = __expf(power);
+          const float oG = __fmul_rn(cl.y, G);  // the same operations as eval_oG
+          const float alpha = fminf(kAlphaMax, oG);
+          const bool act = has && ((mine >> e) & 1ull);
+          const float om = 1.0f - alpha;
+          const float rom = __builtin_amdgcn_rcpf(om);  // om >= 0.01
+          const float Tk = Tr * rom;                    // transmittance in front of this entry
+          const float wt = alpha * Tk;
+          const float cr = cl.z, cg = cl.w;
+          const float dL_dalpha = Tk * ((cr - S0) * g0 + (cg - S1) * g1 + (cb - S2) * g2) - bgT * rom;
+          const bool unclamped = act && oG <= kAlphaMax;  // alpha = o G depends on o and power
+          const float dpow = unclamped ? oG * dL_dalpha : 0.0f;
+          // moments of dL/dpower over the pixels; the conic gradients are linear in them
+          float v[9];
+          v[0] = dx * dpow;
+          v[1] = dy * dpow;
+          v[2] = dx * v[0];
+          v[3] = dy * v[0];
+          v[4] = dy * v[1];
+          v[5] = unclamped ? G * dL_dalpha : 0.0f;
+          v[6] = act ? wt * g0 : 0.0f;
+          v[7] = act ? wt * g1 : 0.0f;
+          v[8] = act ? wt * g2 : 0.0f;
+          if (act) {
+            S0 = alpha * cr + om * S0;
+            S1 = alpha * cg + om * S1;
+            S2 = alpha * cb + om * S2;
+            Tr = Tk;
+          }
+          quad_sum<9>(v);  // every lane of a pixel block holds the block's sums
+          if ((lane & 3) == 0 && has) {
+            // dL/du = (A m_x + B m_y), dL/dv = (B m_x + C m_y), dL/dA = -m_xx / 2,
+            // dL/dB = -m_xy, dL/dC = -m_yy / 2 with A = -2 nA, B = -nB, C = -2 nC
+            const uint32_t ws = wbase + (uint32_t)e;
+            atomicAdd(&acc[0][ws], -(2.0f * g.z * v[0] + g.w * v[1]));
+            atomicAdd(&acc[1][ws], -(g.w * v[0] + 2.0f * cl.x * v[1]));
+            atomicAdd(&acc[2][ws], -0.5f * v[2]);
+            atomicAdd(&acc[3][ws], -v[3]);
+            atomicAdd(&acc[4][ws], -0.5f * v[4]);
+#pragma unroll
+            for (int q = 5; q < 9; ++q) atomicAdd(&acc[q][ws], v[q]);
+          }
         }
-        quad_sum<9>(v);  // every lane of a pixel block holds the block's sums
-        if ((lane & 3) == 0 && has) {
-          // dL/du = (A m_x + B m_y), dL/dv = (B m_x + C m_y), dL/dA = -m_xx / 2,
-          // dL/dB = -m_xy, dL/dC = -m_yy / 2 with A = -2 nA, B = -nB, C = -2 nC
-          const uint32_t ws = pe - seg_lo;
-          atomicAdd(&acc[0][ws], -(2.0f * g.z * v[0] + g.w * v[1]));
-          atomicAdd(&acc[1][ws], -(g.w * v[0] + 2.0f * cl.x * v[1]));
-          atomicAdd(&acc[2][ws], -0.5f * v[2]);
-          atomicAdd(&acc[3][ws], -v[3]);
-          atomicAdd(&acc[4][ws], -0.5f * v[4]);
-#pragma unroll
-          for (int q = 5; q < 9; ++q) atomicAdd(&acc[q][ws], v[q]);
-        }
-      }
-      wave_sync_lds();  // this chunk's reads finish before the next chunk is staged
-      cur = nxt;
-      mcur = mnxt;
-      qc = qn;
-      qn = qnn;
-      qnn = q3;
-      gn = gnn;
-    }
-  }
-  __syncthreads();
-  // one thread per list position of the segment: the entry's sums go to its Gaussian's staging
-  // slot, the entry's place in the row-major order of the Gaussian's tile rect
-  if (seg_lo + (uint32_t)tid < hi_b) {
-    float x[9];
-    bool any = false;
-#pragma unroll
-    for (int q = 0; q < 9; ++q) {
-      x[q] = acc[q][tid];
-      any = any || x[q] != 0.f;
-    }
-    if (any) {
-      const uint32_t gid = vals[start + seg_lo + tid];
-      const float4 q0 = splat[3 * (int64_t)gid];  // u, v, radius_x, radius_y
-      int x0, y0, x1, y1;
-      tile_rect(q0.x, q0.y, __float_as_int(q0.z), __float_as_int(q0.w), TX, TY, x0, y0, x1, y1);
-      const uint64_t slot = (uint64_t)goff_blk[gid / kGoffBlock] + goff[gid] +
-                            (uint32_t)((ty - y0) * (x1 - x0) + (tx - x0));
-      if (slot < staging_cap) {
-        float* o = staging + 9 * slot;
-#pragma unroll
-        for (int q = 0; q < 9; ++q) o[q] = x[q];
+        wave_sync_lds();  // this chunk's reads finish before the next chunk is staged
+        cur = nxt;
+        mcur = mnxt;
       }
     }
+    __syncthreads();
+    // one thread per entry of the window: the entry's sums go to its Gaussian's staging
+    // slot, the entry's place in the row-major order of the Gaussian's tile rect
+    if (wlo + (uint32_t)tid < wtop) {
+      float x[9];
+      bool any = false;
+#pragma unroll
+      for (int q = 0; q < 9; ++q) {
+        x[q] = acc[q][tid];
+        any = any || x[q] != 0.f;
+      }
+      if (any) {
+        const uint32_t gid = vals[start + wlo + tid];
+        const float4 q0 = splat[3 * (int64_t)gid];  // u, v, radius_x, radius_y
+        int x0, y0, x1, y1;
+        tile_rect(q0.x, q0.y, __float_as_int(q0.z), __float_as_int(q0.w), TX, TY, x0, y0, x1, y1);
+        const uint64_t slot = (uint64_t)goff_blk[gid / kGoffBlock] + goff[gid] +
+                              (uint32_t)((ty - y0) * (x1 - x0) + (tx - x0));
+        if (slot < staging_cap) {
+          float* o = staging + 9 * slot;
+#pragma unroll
+          for (int q = 0; q < 9; ++q) o[q] = x[q];
+        }
+      }
+    }
+    __syncthreads();  // the window's sums are read before the next window clears them
+    wtop = wlo;
   }
-  __syncthreads();  // the segment's sums are read before the workgroup's next item clears them
 }
-
 
 __global__ __launch_bounds__(kBlock) void k_blend_backward(BwdArgs a, uint32_t* __restrict__ ws_hdr,
                                                            const uint2* __restrict__ items) {
   __shared__ BlendShared sh;
   __shared__ uint32_t s_item;
-  if (ws_hdr[kHdrSkip]) return;
-  const uint32_t n_items = ws_hdr[kHdrItems];
+  const uint32_t shift = ws_hdr[kHdrShift], n_items = ws_hdr[kHdrItems];
   for (;;) {
     if (threadIdx.x == 0) s_item = atomicAdd(ws_hdr + kHdrBwdNext, 1u);
     __syncthreads();
     const uint32_t item = s_item;
     __syncthreads();  // every wave has read s_item before it is overwritten
     if (item >= n_items) break;
-    backward_item<false>(a, items[item], sh);
+    backward_item<false>(a, shift, items[item], sh);
   }
 }
 
 // Persistent forward: the workgroups take tiles in the plan's order (list-length classes,
-// longest first) from a counter.  Longest first, a tile's waves walk its lists alone, so the
+// longest first) from a counter.  Longest first, a tile's waves walk its list alone, so the
 // longest walks start at once and the short tiles fill in around them.  A few workgroups per CU
 // suffice: fewer waves share each SIMD with the long walks, which then finish sooner.
 __global__ __launch_bounds__(kBlock) void k_blend_forward(FwdArgs a, uint32_t* __restrict__ hdr) {
   __shared__ Chunk stg[4];
   __shared__ uint32_t s_next;
-  if (hdr[kHdrSkip]) return;
+  const uint32_t shift = hdr[kHdrShift];
   for (;;) {
     if (threadIdx.x == 0) s_next = atomicAdd(hdr + kHdrFwdNext, 1u);
     __syncthreads();
     const uint32_t i = s_next;
     __syncthreads();  // every wave has read s_next before it is overwritten
     if (i >= (uint32_t)a.T) break;
-    forward_tile<false>(a, (int)a.order[i], stg);
+    forward_tile<false>(a, shift, (int)a.order[i], stg);
   }
 }
 
@@ -1140,7 +908,7 @@ __global__ __launch_bounds__(kBlock) void k_blend_forward(FwdArgs a, uint32_t* _
 //     order and waits until its slot has been published.
 // No workgroup waits for anything but a tile that a running workgroup has already taken, and
 // the forward never waits, so every wait ends; a wait is still bounded, and one that gives up
-// flags the stall bit of the status words and leaves its item undone.
+// flags the stall word of the header and leaves its item undone.
 // ---------------------------------------------------------------------------------------------
 constexpr uint32_t kSpinLimit = 1u << 20;  // about a second of polling
 
@@ -1152,8 +920,7 @@ __global__ __launch_bounds__(kBlock) void k_blend_step(FwdArgs fa, BwdArgs ba, u
   __shared__ uint32_t s_next, s_pos;
   __shared__ uint2 s_it;
   const int tid = threadIdx.x;
-  if (hdr[kHdrSkip]) return;
-  const uint32_t n_items = hdr[kHdrItems];
+  const uint32_t shift = hdr[kHdrShift], n_items = hdr[kHdrItems];
   if (tid == 0) s_next = atomicAdd(hdr + kHdrRole, 1u);
   __syncthreads();
   const bool forward_worker = s_next < fwd_workers;
@@ -1167,7 +934,7 @@ __global__ __launch_bounds__(kBlock) void k_blend_step(FwdArgs fa, BwdArgs ba, u
       __syncthreads();
       if (i >= (uint32_t)fa.T) break;
       const int tile = (int)fa.order[i];
-      forward_tile<true>(fa, tile, sh.stg);
+      forward_tile<true>(fa, shift, tile, sh.stg);
       drain_memory();
       __syncthreads();  // the tile's state is visible to every XCD
       const uint32_t o = item_off[tile], k = item_off[tile + 1] - o;
@@ -1201,10 +968,9 @@ __global__ __launch_bounds__(kBlock) void k_blend_step(FwdArgs fa, BwdArgs ba, u
     const uint2 it = s_it;
     __syncthreads();
     if (it.x == kNoTile) break;
-    backward_item<true>(ba, it, sh);
+    backward_item<true>(ba, shift, it, sh);
   }
 }
-
 
 // ---------------------------------------------------------------------------------------------
 // Per-Gaussian staging offsets: exclusive scan of tiles_i in Gaussian order, two levels.
@@ -1268,7 +1034,6 @@ __global__ __launch_bounds__(kPlanThreads) void k_goff_blocks(int64_t nblk, uint
     if ((uint64_t)run > entries_cap) {
       hdr[kHdrFlags] |= kFlagCapacity;
       hdr[kHdrNeed] = max(hdr[kHdrNeed], run);
-      hdr[kHdrSkip] = 1u;
     }
   }
 }
@@ -1318,83 +1083,72 @@ int cu_count() {
 
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 constexpr size_t kSlotBytes = sizeof(float4) * kTile * kTile;
-constexpr size_t kMaskChunkBytes = sizeof(uint2) * kChunk;  // one 64-bit mask per pixel of a quadrant
+constexpr size_t kMaskChunkBytes = sizeof(uint2) * kTile * kTile;  // one 64-bit mask per pixel
+constexpr uint64_t kSegEntries = 1u << kSegShiftMin;
 
 size_t n_goff_blocks(int64_t n) { return (size_t)((n + kGoffBlock - 1) / kGoffBlock); }
 size_t plan_blocks(int T) { return (size_t)((T + kPlanThreads - 1) / kPlanThreads); }
 size_t plan_bytes(int T) { return round256(4 * plan_blocks(T) * kPartVals) + round256(4 * plan_blocks(T) * kOffVals); }
 
-// The regions of the layout for T tiles, n Gaussians and k staged entries (k a multiple of 256),
-// in order; the staging area comes last.
-//   slots     T + k / 256 (a long list of len entries takes ceil(len / 256) <= len / 256 + 1)
-//   items     T + slots (every non-empty tile's segments: slots plus one per short tile)
-//   masks     4 T + 4 k / 64 chunks of 64 pixels: quadrant list (t, q) takes ceil(n_q / 64)
-//             chunks from (4 start + q len) / 64 + 4 t + q on, and n_q <= len
-//   qent, qbox  4 k entries (quadrant list (t, q) at 4 start + q len)
-struct Sizes {
-  size_t slots, items, chunks;
-};
-Sizes sizes_for(int T, uint64_t k) {
-  Sizes z;
-  z.slots = (size_t)T + (size_t)(k / (uint64_t)kSeg);
-  z.items = (size_t)T + z.slots;
-  z.chunks = 4 * (size_t)T + 4 * (size_t)(k / kChunk);
-  return z;
-}
+// bytes of the layout for T tiles, n Gaussians and k staged entries (k a multiple of 256)
+// (tile t's 64-entry chunks start at ranges[t].x / 64 + t, so K entries need at most
+// K / 64 + T mask chunks)
 size_t layout_bytes(int T, int64_t n, uint64_t k) {
-  const Sizes z = sizes_for(T, k);
-  return 256 + 2 * round256(4 * (size_t)(T + 1)) + 2 * round256(4 * (size_t)T) + plan_bytes(T) +
-         round256(4 * (size_t)n) + round256(4 * (n_goff_blocks(n) + 1)) + round256(8 * z.items) +
-         round256(4 * z.items) + round256(16 * (z.items + 1)) + round256(kSlotBytes * z.slots) +
-         round256(kMaskChunkBytes * z.chunks) + round256(2 * (size_t)k) + round256(16 * (size_t)k) +
-         round256(8 * (size_t)k) + round256(36 * (size_t)k + 16);
+  const size_t slots = (size_t)T + (size_t)(k / kSegEntries);
+  const size_t chunks = (size_t)T + (size_t)(k / kChunk);
+  return 256 + 2 * round256(4 * (size_t)(T + 1)) + 2 * round256(4 * (size_t)T) + plan_bytes(T) + round256(4 * (size_t)n) +
+         round256(4 * (n_goff_blocks(n) + 1)) +
+         round256(8 * ((size_t)T + slots)) + round256(kSlotBytes * slots) + kMaskChunkBytes * chunks +
+         round256(36 * (size_t)k + 16);
 }
-// the least the layout grows by per 256 entries of capacity (the small per-item arrays may not
-// grow by a whole 256-byte step)
-constexpr size_t kBytesPerSegMin =
-    kSlotBytes + 4 * (kSeg / kChunk) * kMaskChunkBytes + 2 * kSeg + 16 * kSeg + 8 * kSeg + 36 * kSeg;
+// per 256 entries of capacity
+constexpr size_t kBytesPerSeg = kSlotBytes + 8 + (kSegEntries / kChunk) * kMaskChunkBytes + 36 * kSegEntries;
 
 }  // namespace
 
 size_t render_ws_bytes(int T, int64_t n, int64_t k_capacity) {
   const uint64_t kc = k_capacity > 0 ? (uint64_t)k_capacity : 0;
-  return layout_bytes(T, n, (kc + kSeg - 1) / kSeg * kSeg);
+  return layout_bytes(T, n, (kc + kSegEntries - 1) / kSegEntries * kSegEntries);
 }
 
 bool render_ws_layout(void* ws, size_t bytes, int T, int64_t n, RenderWs* out) {
   const size_t base = layout_bytes(T, n, 0);
   if (!ws || bytes < base || (reinterpret_cast<uintptr_t>(ws) & 255u)) return false;
-  // this start is an upper bound on the capacity; step down to the largest that fits
-  uint64_t k = (bytes - base) / kBytesPerSegMin * kSeg;
-  while (k > 0 && layout_bytes(T, n, k) > bytes) k -= kSeg;
-  const Sizes z = sizes_for(T, k);
-  if (z.items + 1 > 0x7FFFFFFFull) return false;
+  // 256 more entries of capacity cost at least kBytesPerSeg - 8 bytes (the item array may not
+  // grow by a whole 256-byte step), so this start is an upper bound; step down to the largest fit
+  uint64_t k = (bytes - base) / (kBytesPerSeg - 8) * kSegEntries;
+  while (k > 0 && layout_bytes(T, n, k) > bytes) k -= kSegEntries;
+  const size_t slots = (size_t)T + (size_t)(k / kSegEntries);
+  if (slots > 0x7FFFFFFFull) return false;
   char* b = static_cast<char*>(ws);
-  auto take = [&](size_t nbytes) {
-    char* p = b;
-    b += round256(nbytes);
-    return p;
-  };
-  out->hdr = reinterpret_cast<uint32_t*>(take(256));
-  out->bnd_off = reinterpret_cast<uint32_t*>(take(4 * (size_t)(T + 1)));
-  out->item_off = reinterpret_cast<uint32_t*>(take(4 * (size_t)(T + 1)));
-  out->order = reinterpret_cast<uint32_t*>(take(4 * (size_t)T));
-  out->loss_part = reinterpret_cast<float*>(take(4 * (size_t)T));
-  out->plan_part = reinterpret_cast<uint32_t*>(take(4 * plan_blocks(T) * kPartVals));
-  out->plan_off = reinterpret_cast<uint32_t*>(take(4 * plan_blocks(T) * kOffVals));
-  out->goff = reinterpret_cast<uint32_t*>(take(4 * (size_t)n));
-  out->goff_blk = reinterpret_cast<uint32_t*>(take(4 * (n_goff_blocks(n) + 1)));
-  out->items = reinterpret_cast<uint2*>(take(8 * z.items));
-  out->wtile = reinterpret_cast<uint32_t*>(take(4 * z.items));
-  out->qcnt = reinterpret_cast<uint32_t*>(take(16 * (z.items + 1)));
-  out->slots = reinterpret_cast<float4*>(take(kSlotBytes * z.slots));
-  out->masks = reinterpret_cast<uint2*>(take(kMaskChunkBytes * z.chunks));
-  out->tbox = reinterpret_cast<uint16_t*>(take(2 * (size_t)k));
-  out->qent = reinterpret_cast<uint32_t*>(take(16 * (size_t)k));
-  out->qbox = reinterpret_cast<uint16_t*>(take(8 * (size_t)k));
+  out->hdr = reinterpret_cast<uint32_t*>(b);
+  b += 256;
+  out->bnd_off = reinterpret_cast<uint32_t*>(b);
+  b += round256(4 * (size_t)(T + 1));
+  out->item_off = reinterpret_cast<uint32_t*>(b);
+  b += round256(4 * (size_t)(T + 1));
+  out->order = reinterpret_cast<uint32_t*>(b);
+  b += round256(4 * (size_t)T);
+  out->loss_part = reinterpret_cast<float*>(b);
+  b += round256(4 * (size_t)T);
+  out->plan_part = reinterpret_cast<uint32_t*>(b);
+  b += round256(4 * plan_blocks(T) * kPartVals);
+  out->plan_off = reinterpret_cast<uint32_t*>(b);
+  b += round256(4 * plan_blocks(T) * kOffVals);
+  out->goff = reinterpret_cast<uint32_t*>(b);
+  b += round256(4 * (size_t)n);
+  out->goff_blk = reinterpret_cast<uint32_t*>(b);
+  b += round256(4 * (n_goff_blocks(n) + 1));
+  out->items = reinterpret_cast<uint2*>(b);  // T + slots items at most
+  b += round256(8 * ((size_t)T + slots));
+  out->slots = reinterpret_cast<float4*>(b);
+  b += round256(kSlotBytes * slots);
+  const size_t chunks = (size_t)T + (size_t)(k / kChunk);
+  out->masks = reinterpret_cast<uint2*>(b);
+  b += kMaskChunkBytes * chunks;
   out->staging = reinterpret_cast<float*>(b);
-  out->slots_cap = (uint32_t)z.slots;
-  out->mask_cap = z.chunks;
+  out->slots_cap = (uint32_t)slots;
+  out->mask_cap = chunks;
   out->staging_cap = k;
   return true;
 }
@@ -1416,39 +1170,17 @@ int resident_per_cu(const void* kernel, int* cache) {
   return cache[dev];
 }
 
-// the segment plan, the tile order, the item list (empty markers for the fused step) and the
-// quadrant lists
-void launch_plan(const CamK& cam, int64_t n, const gs_splat* splat, const uint32_t* vals, const uint2* rg,
-                 const RenderWs& ws, bool empty_items, hipStream_t s) {
-  const int T = cam.TX * cam.TY;
+// the segment plan, the tile order and the item list (empty markers for the fused step)
+void launch_plan(int T, const uint2* rg, const RenderWs& ws, bool empty_items, hipStream_t s) {
   const int nb = (int)ceil_div(T, kPlanThreads);
   hipLaunchKernelGGL(k_plan_count, dim3((unsigned)nb), dim3(kPlanThreads), 0, s, rg, T, ws.plan_part);
   hipLaunchKernelGGL(k_plan_scan, dim3(1), dim3(kPlanThreads), 0, s, (const uint32_t*)ws.plan_part, nb, T,
                      ws.slots_cap, (uint64_t)ws.staging_cap, ws.plan_off, ws.hdr, ws.bnd_off, ws.item_off);
   hipLaunchKernelGGL(k_plan_write, dim3((unsigned)nb), dim3(kPlanThreads), 0, s, rg, T,
-                     (const uint32_t*)ws.plan_off, ws.bnd_off, ws.item_off, ws.order);
+                     (const uint32_t*)ws.plan_off, (const uint32_t*)ws.hdr, ws.bnd_off, ws.item_off, ws.order);
   hipLaunchKernelGGL(k_seg_items, dim3((unsigned)ceil_div(T, kBlock / 64)), dim3(kBlock), 0, s, T,
-                     (const uint32_t*)ws.item_off, ws.items, ws.wtile, empty_items);
-  if (n <= 0) return;  // no lists
-  QuadArgs q{};
-  q.TX = cam.TX;
-  q.n = n;
-  q.splat = reinterpret_cast<const float4*>(splat);
-  q.vals = vals;
-  q.ranges = rg;
-  q.item_off = ws.item_off;
-  q.wtile = ws.wtile;
-  q.hdr = ws.hdr;
-  q.tbox = ws.tbox;
-  q.qcnt = ws.qcnt;
-  q.qent = ws.qent;
-  q.qbox = ws.qbox;
-  const unsigned grid = (unsigned)std::max(1, cu_count() * 8);
-  hipLaunchKernelGGL(k_quad_count, dim3(grid), dim3(kBlock), 0, s, q);
-  hipLaunchKernelGGL(k_quad_scan, dim3(1), dim3(kPlanThreads), 0, s, (const uint32_t*)ws.hdr, ws.qcnt);
-  hipLaunchKernelGGL(k_quad_write, dim3(grid), dim3(kBlock), 0, s, q);
+                     (const uint32_t*)ws.item_off, ws.items, empty_items);
 }
-
 
 // the per-Gaussian staging offsets and the cleared staging rows
 void launch_staging(int64_t n, const uint32_t* tiles, const RenderWs& ws, hipStream_t s) {
@@ -1486,10 +1218,6 @@ FwdArgs fwd_args(const CamK& cam, int64_t n, const gs_splat* splat, const uint32
   a.masks = ws.masks;
   a.mask_cap = ws.mask_cap;
   a.order = ws.order;
-  a.item_off = ws.item_off;
-  a.qcnt = ws.qcnt;
-  a.qent = ws.qent;
-  a.qbox = ws.qbox;
   return a;
 }
 
@@ -1515,10 +1243,6 @@ BwdArgs bwd_args(const CamK& cam, int64_t n, const gs_splat* splat, const uint32
   a.slots = ws.slots;
   a.masks = ws.masks;
   a.mask_cap = ws.mask_cap;
-  a.item_off = ws.item_off;
-  a.qcnt = ws.qcnt;
-  a.qent = ws.qent;
-  a.qbox = ws.qbox;
   a.goff = ws.goff;
   a.goff_blk = ws.goff_blk;
   a.staging = ws.staging;
@@ -1534,7 +1258,7 @@ hipError_t launch_blend_forward(const CamK& cam, int64_t n, const gs_splat* spla
                                 uint32_t* n_examined, uint64_t* blend_count, const RenderWs& ws,
                                 hipStream_t s) {
   const int T = cam.TX * cam.TY;
-  launch_plan(cam, n, splat, vals, reinterpret_cast<const uint2*>(ranges), ws, false, s);
+  launch_plan(T, reinterpret_cast<const uint2*>(ranges), ws, false, s);
   const FwdArgs a = fwd_args(cam, n, splat, vals, ranges, bg0, bg1, bg2, image, T_final, last_contrib, n_examined,
                              blend_count, ws);
   const unsigned grid = (unsigned)std::max(1, std::min(T, cu_count() * kFwdPerCu));
@@ -1564,9 +1288,9 @@ hipError_t launch_blend_backward(const CamK& cam, int64_t n, const gs_splat* spl
   return hipGetLastError();
 }
 
-hipError_t launch_step_plan(const CamK& cam, int64_t n, const gs_splat* splat, const uint32_t* vals,
-                            const uint32_t* tiles, const uint32_t* ranges, const RenderWs& ws, hipStream_t s) {
-  launch_plan(cam, n, splat, vals, reinterpret_cast<const uint2*>(ranges), ws, true, s);
+hipError_t launch_step_plan(const CamK& cam, int64_t n, const uint32_t* tiles, const uint32_t* ranges,
+                            const RenderWs& ws, hipStream_t s) {
+  launch_plan(cam.TX * cam.TY, reinterpret_cast<const uint2*>(ranges), ws, true, s);
   if (n > 0) launch_staging(n, tiles, ws, s);
   return hipGetLastError();
 }

@@ -485,18 +485,18 @@ int gs_render_backward(const gs_scene* scene, float* params, const gs_camera* ca
                                  "gs_render_backward (preprocess backward)");
 }
 
-int gs_render_plan(const gs_scene* scene, const gs_camera* cam, gs_proj proj, const uint32_t* vals,
-                   const uint32_t* ranges, int64_t k, void* render_ws, size_t render_ws_bytes, hipStream_t stream) {
+int gs_render_plan(const gs_scene* scene, const gs_camera* cam, gs_proj proj, const uint32_t* ranges, int64_t k,
+                   void* render_ws, size_t render_ws_bytes, hipStream_t stream) {
   int st;
-  if ((st = check_scene(scene)) || (st = check_camera(cam)) || (st = check_proj(proj, false, scene->n))) return st;
-  if (!vals || !ranges || !render_ws) return fail(GS_ERR_INVALID_ARGUMENT, "a required pointer is null");
+  if ((st = check_scene(scene)) || (st = check_camera(cam))) return st;
+  if (!ranges || !render_ws) return fail(GS_ERR_INVALID_ARGUMENT, "a required pointer is null");
   if (scene->n > 0 && !proj.tiles) return fail(GS_ERR_INVALID_ARGUMENT, "proj.tiles is null");
   RenderWs ws;
   if (!render_ws_layout(render_ws, render_ws_bytes, (int)n_tiles(*cam), scene->n, &ws))
     return fail(GS_ERR_INVALID_ARGUMENT, "render workspace too small or not 256-byte aligned");
   if ((st = check_render_capacity(*cam, scene->n, k, ws, render_ws_bytes))) return st;
   if (reinterpret_cast<uintptr_t>(ranges) & 7u) return fail(GS_ERR_INVALID_ARGUMENT, "ranges must be 8-byte aligned");
-  const hipError_t e = launch_step_plan(make_cam(*cam), scene->n, proj.splat, vals, proj.tiles, ranges, ws, stream);
+  const hipError_t e = launch_step_plan(make_cam(*cam), scene->n, proj.tiles, ranges, ws, stream);
   return e == hipSuccess ? ok() : hip_fail(e, "gs_render_plan");
 }
 

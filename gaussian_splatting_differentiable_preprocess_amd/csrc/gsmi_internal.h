@@ -97,16 +97,15 @@ hipError_t launch_bin_sort_rest(int64_t n, int64_t K, const BinInfo& info, const
 // blending
 //
 // Render workspace.  The forward leaves in it what the backward needs to walk long tile lists
-// back in parallel segments of 256 entries: a tile list longer than one segment gets one state
-// slot per segment boundary plus one for its final state; a slot holds (T, C_r, C_g, C_b) for the
-// tile's 256 pixels.  The plan sorts each tile list into four quadrant lists (the entries whose
-// alpha box reaches each 8x8 quadrant).  The backward gathers each list entry's nine gradient
-// sums in `staging`, grouped by Gaussian (Gaussian i's entries at goff(i) .. goff(i) + tiles_i, in
-// the row-major order of its tile rect), and then sums each Gaussian's entries into grad2d: no
-// float atomics in memory.
+// back in parallel segments: a tile list longer than one segment (256 entries, or a larger
+// power of two when the workspace is short) gets one state slot per segment boundary plus one
+// for its final state; a slot holds (T, C_r, C_g, C_b) for the tile's 256 pixels.  The
+// backward gathers each list entry's nine gradient sums in `staging`, grouped by Gaussian
+// (Gaussian i's entries at goff(i) .. goff(i) + tiles_i, in the row-major order of its tile
+// rect), and then sums each Gaussian's entries into grad2d: no float atomics in memory.
 //   hdr[64]         header words (kHdr* below)
 //   bnd_off[T + 1]  first slot of each tile
-//   item_off[T + 1] first segment (work item) of each tile
+//   item_off[T + 1] first work item of each tile
 //   order[T]        the forward's tile order: list-length classes (log2), longest first
 //   plan_part[], plan_off[]  the segment plan's per-block partial sums and offsets
 //   goff[n]         exclusive scan of tiles within blocks of kGoffBlock Gaussians; goff(i) =
@@ -114,20 +113,13 @@ hipError_t launch_bin_sort_rest(int64_t n, int64_t K, const BinInfo& info, const
 //   goff_blk[]      exclusive scan of the block totals
 //   items[]         (tile, segment) work items of the backward: tile-major after the forward; in
 //                   the fused step, in the order the tiles' forwards completed
-//   wtile[]         the tile of each segment, in tile-major order
-//   qcnt[][4]       per segment and quadrant, the entries reaching the quadrant, scanned
-//                   exclusively over all segments (one more row for the totals)
 //   slots[][256]    float4 states
-//   masks[][64]     per 64-entry chunk of a quadrant list and pixel of the quadrant: the chunk's
+//   masks[][256]    per 64-entry chunk of a tile list and pixel of the tile: the chunk's
 //                   entries the forward composited at that pixel (64-bit, as uint2 lo, hi);
-//                   quadrant q of tile t has its chunk j at (4 ranges[t].x + q len) / 64 + 4 t + q + j
-//   tbox[]          per list entry: its alpha box inside its tile (4 x 4 bits)
-//   qent[], qbox[]  the quadrant lists: quadrant q of tile t at 4 ranges[t].x + q len, each entry's
-//                   position in the tile list and its box inside the quadrant (4 x 3 bits)
+//                   tile t's chunk j is at (ranges[t].x / 64 + t + j)
 //   loss_part[T]    the fused step's per-tile sums of |image - target|
 //   staging[][9]    per-entry gradient sums
-constexpr int kSegShift = 8;
-constexpr int kSeg = 1 << kSegShift;  // 256 list entries per segment
+constexpr int kSegShiftMin = 8;  // 256 list entries per segment
 // header words of the render workspace
 constexpr int kHdrShift = 0;    // log2 segment length
 constexpr int kHdrItems = 1;    // backward work items
@@ -139,7 +131,6 @@ constexpr int kHdrReady = 6;    // fused step: work items published so far
 constexpr int kHdrRole = 7;     // fused step: workgroups started so far
 constexpr int kHdrFlags = 8;    // status bits (kFlag* below): set by the kernels, kept until read
 constexpr int kHdrNeed = 9;     // the most intersections lists needed (largest list end, or staged entries)
-constexpr int kHdrSkip = 10;    // the last plan's lists exceed the workspace: the render kernels do nothing
 constexpr int kHdrStatusWords = 16;  // header words gs_render_init clears
 constexpr uint32_t kFlagStall = 1u;     // fused step: a workgroup gave up waiting for a work item
 constexpr uint32_t kFlagCapacity = 2u;  // the lists need more intersections than the workspace holds
@@ -154,13 +145,8 @@ struct RenderWs {
   uint32_t* goff;
   uint32_t* goff_blk;
   uint2* items;
-  uint32_t* wtile;   // the tile of each segment (item)
-  uint32_t* qcnt;    // per segment and quadrant: entries reaching it, scanned over all segments
   float4* slots;
   uint2* masks;
-  uint16_t* tbox;    // per list entry: its alpha box inside its tile
-  uint32_t* qent;    // quadrant lists: tile-list positions
-  uint16_t* qbox;    // quadrant lists: boxes inside the quadrant
   float* loss_part;
   float* staging;
   uint32_t slots_cap;
@@ -189,8 +175,8 @@ hipError_t launch_fill_f32(float* p, int64_t count, float value, hipStream_t s);
 size_t loss_workspace_bytes(int64_t count);
 // The fused step's preparation: segment plan, tile order, empty item list, staging offsets and
 // cleared staging rows.
-hipError_t launch_step_plan(const CamK& cam, int64_t n, const gs_splat* splat, const uint32_t* vals,
-                            const uint32_t* tiles, const uint32_t* ranges, const RenderWs& ws, hipStream_t s);
+hipError_t launch_step_plan(const CamK& cam, int64_t n, const uint32_t* tiles, const uint32_t* ranges,
+                            const RenderWs& ws, hipStream_t s);
 // Fused forward, L1 loss and backward blend of one training step (after launch_step_plan);
 // leaves the per-intersection gradient sums staged in ws for the preprocess backward.
 hipError_t launch_blend_step(const CamK& cam, int64_t n, const gs_splat* splat, const uint32_t* tiles,

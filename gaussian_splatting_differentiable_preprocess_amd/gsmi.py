@@ -105,7 +105,7 @@ def load(path: str = LIB_PATH):
     L.gs_loss_l1_dssim.argtypes = [i32, i32, P, P, ctypes.c_float, P, P, P, sz, P]
     L.gs_render_backward.argtypes = [SP, P, CP, GsProj, P, P, i64, ctypes.POINTER(ctypes.c_float), P, P, P,
                                      P, P, AP, P, sz, P]
-    L.gs_render_plan.argtypes = [SP, CP, GsProj, P, P, i64, P, sz, P]
+    L.gs_render_plan.argtypes = [SP, CP, GsProj, P, i64, P, sz, P]
     L.gs_render_step.argtypes = [SP, CP, GsProj, P, P, i64, ctypes.POINTER(ctypes.c_float), P, P, P, P, P, P, P, P, P,
                                  P, sz, P]
     L.gs_render_init.argtypes = [P, sz, P]
@@ -299,11 +299,13 @@ def render_backward(scene: GsScene, params, cam: GsCamera, proj: Proj, vals, ran
                                      _ptr(render_ws), _nbytes(render_ws), _stream(stream)))
 
 
-def render_plan(scene: GsScene, cam: GsCamera, proj: Proj, vals, ranges, render_ws, stream=None, k=None):
-    """Prepares render_ws for render_step over these lists (k intersections; by default the length
-    of the vals buffer, which bounds it)."""
-    _check(load().gs_render_plan(ctypes.byref(scene), ctypes.byref(cam), proj.c(), _ptr(vals), _ptr(ranges),
-                                 _k(k, vals), _ptr(render_ws), _nbytes(render_ws), _stream(stream)))
+def render_plan(scene: GsScene, cam: GsCamera, proj: Proj, ranges, render_ws, stream=None, k=None):
+    """Prepares render_ws for render_step over the lists of these ranges (k intersections; when not
+    given, the largest count the workspace holds is assumed and only the device check applies)."""
+    if k is None:
+        k = render_workspace_capacity(cam.width, cam.height, scene.n, _nbytes(render_ws))
+    _check(load().gs_render_plan(ctypes.byref(scene), ctypes.byref(cam), proj.c(), _ptr(ranges), int(k),
+                                 _ptr(render_ws), _nbytes(render_ws), _stream(stream)))
 
 
 def render_step(scene: GsScene, cam: GsCamera, proj: Proj, vals, ranges, bg, target, image, T_final, last_contrib,
@@ -502,7 +504,7 @@ def train_batch(buf: StepBuffers, params, m, v, step, cams, targets, grads_acc, 
             except GsCapacityError as e:
                 buf.grow(int(e.required * 1.25) + 1024)
         if dssim_lambda is None:
-            render_plan(buf.scene, cam, buf.proj, buf.vals, buf.ranges, buf.render_ws, k=K)
+            render_plan(buf.scene, cam, buf.proj, buf.ranges, buf.render_ws, k=K)
             render_step(buf.scene, cam, buf.proj, buf.vals, buf.ranges, bg, tgt, buf.image, buf.T_final, buf.last,
                         buf.loss, buf.dLdI, buf.render_ws, blend_count=blend_count, k=K)
         else:

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define GSMI_VERSION 9
+#define GSMI_VERSION 8
 #define GS_TILE 16 /* tiles are GS_TILE x GS_TILE pixels */
 
 typedef enum gs_status {
@@ -306,15 +306,13 @@ int gs_render_backward(const gs_scene* scene, float* params, const gs_camera* ca
                        float* grad2d, float* grads, const gs_adam* adam, void* render_ws,
                        size_t render_ws_bytes, hipStream_t stream);
 
-/* Prepares render_ws for gs_render_step over these lists (vals and ranges from gs_bin_and_sort,
- * proj.splat and proj.tiles from gs_preprocess, the same camera): the segment plan and tile order of
- * the forward, an empty list of backward work items, the lists' split by 8x8 quadrant (the entries
- * whose alpha >= 1/255 box reaches each quadrant of their tile, in list order), and each Gaussian's
- * cleared staging rows for the gradient sums.  k is the number of intersections in the lists.
- * Kept apart from gs_render_step so that the fused kernel can be timed alone.  Errors as
- * gs_render_forward. */
-int gs_render_plan(const gs_scene* scene, const gs_camera* cam, gs_proj proj, const uint32_t* vals,
-                   const uint32_t* ranges, int64_t k, void* render_ws, size_t render_ws_bytes, hipStream_t stream);
+/* Prepares render_ws for gs_render_step over these lists (ranges from gs_bin_and_sort, proj.tiles
+ * from gs_preprocess, the same camera): the segment plan and tile order of the forward, an empty
+ * list of backward work items, and each Gaussian's cleared staging rows for the gradient sums.
+ * k is the number of intersections in the lists.  Kept apart from gs_render_step so that the fused
+ * kernel can be timed alone.  Errors as gs_render_forward. */
+int gs_render_plan(const gs_scene* scene, const gs_camera* cam, gs_proj proj, const uint32_t* ranges, int64_t k,
+                   void* render_ws, size_t render_ws_bytes, hipStream_t stream);
 
 /* The image pass of one training step, fused: the forward blend (as gs_render_forward), the L1
  * loss against target (as gs_loss_l1) and the backward blend (as gs_render_backward with

@@ -257,7 +257,7 @@ class GpuStep:
         self.dLdI = torch.empty((H, W, 3), dtype=torch.float32, device="cuda")
         lossv = torch.zeros(1, dtype=torch.float32, device="cuda")
         g2 = torch.empty((max(1, self.ld), 9), dtype=torch.float32, device="cuda")
-        gsmi.render_plan(self.scene, self.cam, self.proj, self.vals, rg, self.render_ws, k=self.K)
+        gsmi.render_plan(self.scene, self.cam, self.proj, rg, self.render_ws, k=self.K)
         gsmi.render_step(self.scene, self.cam, self.proj, self.vals, rg, bg, self.target, self.image, self.T_final,
                          self.last, lossv, self.dLdI, self.render_ws, grad2d=g2, n_examined=self.nex,
                          blend_count=self.bcount, k=self.K)

@@ -22,7 +22,7 @@ def test_library_exports_every_declared_symbol():
     assert len(names) == len(gsmi.EXPORTS) and set(names) == set(gsmi.EXPORTS)
     for name in names:
         assert hasattr(L, name), name
-    assert gsmi.version() == 9
+    assert gsmi.version() == 8
 
 
 def test_invalid_arguments_rejected_before_any_gpu_call():
@@ -84,15 +84,12 @@ def test_workspace_queries():
     with pytest.raises(gsmi.GsError):
         gsmi.bin_and_sort_workspace(-1, 0, 16, 16)
     # render workspace: a fixed part for the tiles and Gaussians plus, per 256 intersections of
-    # capacity, one 4 KiB state slot, one segment (work item, its tile, its four quadrant counts),
-    # room for 16 chunks of composited masks (8 bytes per pixel of a quadrant per 64 entries of a
-    # quadrant list, each entry in up to four lists), each entry's tile box (2 bytes) and its four
-    # quadrant-list slots (position and box, 6 bytes each), and 256 staged 36-byte gradient sums
+    # capacity, one 4 KiB state slot, one work item, four 2 KiB chunks of composited masks (8
+    # bytes per pixel of a tile per 64 entries) and 256 staged 36-byte gradient sums
     r0 = gsmi.render_workspace(2048, 2048, 4_000_000, 0)
     r1 = gsmi.render_workspace(2048, 2048, 4_000_000, 256 * 1000)
-    per_seg = 4096 + (8 + 4 + 16) + 16 * 512 + 256 * (2 + 4 * 6) + 256 * 36
-    assert abs((r1 - r0) - 1000 * per_seg) <= 1024, (r1 - r0) / 1000
-    assert r0 >= 16384 * (4096 + 2 * (8 + 4 + 16) + 4 * 512) + 4 * 4_000_000
+    assert abs((r1 - r0) - 1000 * (4096 + 8 + 4 * 2048 + 256 * 36)) <= 512
+    assert r0 >= 16384 * (4096 + 8 + 2048 + 4) + 4 * 4_000_000
     with pytest.raises(gsmi.GsError):
         gsmi.render_workspace(0, 16, 10, 10)
     # the capacity query inverts the size query: never below the capacity asked for, and no
@@ -294,7 +291,7 @@ def test_render_plan_checks_its_arguments():
     sc = gsmi.make_scene(10, 10, 0)
     proj = gsmi.GsProj(4096, 4096, 4096, 4096)
     call = lambda proj=proj, ranges=p, ws=p, nb=need: L.gs_render_plan(ctypes.byref(sc), ctypes.byref(cam), proj,
-                                                                        p, ranges, 0, ws, nb, None)
+                                                                        ranges, 0, ws, nb, None)
     assert call(ws=None) == gsmi.GS_ERR_INVALID_ARGUMENT and "null" in gsmi.last_error()
     assert call(ranges=None) == gsmi.GS_ERR_INVALID_ARGUMENT and "null" in gsmi.last_error()
     for ws, nb in ((p, 16), (ctypes.c_void_p(4096 + 64), need)):
@@ -327,7 +324,7 @@ def test_render_calls_report_a_workspace_short_of_the_intersections():
     ad = gsmi.GsAdam(4096, 4096, 1, 1e-3, 0.9, 0.999, 1e-8)
     calls = {
         "forward": lambda k: L.gs_render_forward(ctypes.byref(cam), n, p, p, p, k, bg, p, p, p, None, None, p, nb, None),
-        "plan": lambda k: L.gs_render_plan(ctypes.byref(sc), ctypes.byref(cam), proj, p, p, k, p, nb, None),
+        "plan": lambda k: L.gs_render_plan(ctypes.byref(sc), ctypes.byref(cam), proj, p, k, p, nb, None),
         "step": lambda k: L.gs_render_step(ctypes.byref(sc), ctypes.byref(cam), proj, p, p, k, bg, p, p, p, p, None,
                                            None, p, p, None, p, nb, None),
         "backward": lambda k: L.gs_render_backward(ctypes.byref(sc), p, ctypes.byref(cam), proj, p, p, k, bg, p, p,

@@ -147,7 +147,7 @@ def _e2e(params, deg, cams, W, H, tgts, step):
     for j in range(B):
         gsmi.preprocess(buf.scene, p, gcams[j], buf.proj)
         K = gsmi.bin_and_sort(buf.scene, gcams[j], buf.proj, buf.ws, buf.k_capacity, buf.vals, buf.ranges)
-        gsmi.render_plan(buf.scene, gcams[j], buf.proj, buf.vals, buf.ranges, buf.render_ws, k=K)
+        gsmi.render_plan(buf.scene, gcams[j], buf.proj, buf.ranges, buf.render_ws, k=K)
         gsmi.render_step(buf.scene, gcams[j], buf.proj, buf.vals, buf.ranges, BG, gt[j], buf.image, buf.T_final,
                          buf.last, buf.loss, buf.dLdI, buf.render_ws, k=K)
         gsmi.preprocess_backward_accumulate(buf.scene, p, gcams[j], buf.proj, buf.render_ws, acc, j == 0, 1.0 / B)

@@ -100,7 +100,7 @@ def test_densify_stats_after_a_step():
     for _ in range(2):
         gsmi.preprocess(buf.scene, p, c, buf.proj)
         K = gsmi.bin_and_sort(buf.scene, c, buf.proj, buf.ws, buf.k_capacity, buf.vals, buf.ranges)
-        gsmi.render_plan(buf.scene, c, buf.proj, buf.vals, buf.ranges, buf.render_ws, k=K)
+        gsmi.render_plan(buf.scene, c, buf.proj, buf.ranges, buf.render_ws, k=K)
         gsmi.render_step(buf.scene, c, buf.proj, buf.vals, buf.ranges, (0.0, 0.0, 0.0), torch.from_numpy(tgt).cuda(),
                          buf.image, buf.T_final, buf.last, buf.loss, buf.dLdI, buf.render_ws, k=K)
         gsmi.densify_stats(buf.scene, c, buf.proj, buf.render_ws, acc, cnt)

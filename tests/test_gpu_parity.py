@@ -758,7 +758,7 @@ def test_short_render_workspace_is_an_error_not_a_partial_result():
                                                  k=k),
         "backward": lambda k: gsmi.render_backward(g.scene, None, g.cam, g.proj, g.vals, g.ranges, BG, Tf, last, up,
                                                    g2, short, k=k),
-        "plan": lambda k: gsmi.render_plan(g.scene, g.cam, g.proj, g.vals, g.ranges, short, k=k),
+        "plan": lambda k: gsmi.render_plan(g.scene, g.cam, g.proj, g.ranges, short, k=k),
         "step": lambda k: gsmi.render_step(g.scene, g.cam, g.proj, g.vals, g.ranges, BG, tgt, img, Tf, last, loss, dl,
                                            short, k=k),
     }
@@ -777,7 +777,7 @@ def test_short_render_workspace_is_an_error_not_a_partial_result():
     with pytest.raises(gsmi.GsCapacityError):
         gsmi.render_status(short)
     ok = gsmi.new_render_ws(W, H, g.n, K)
-    gsmi.render_plan(g.scene, g.cam, g.proj, g.vals, g.ranges, ok, k=K)
+    gsmi.render_plan(g.scene, g.cam, g.proj, g.ranges, ok, k=K)
     gsmi.render_step(g.scene, g.cam, g.proj, g.vals, g.ranges, BG, tgt, img, Tf, last, loss, dl, ok, k=K)
     assert gsmi.render_status(ok) == (0, 0)
 
