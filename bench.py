@@ -369,7 +369,10 @@ def main():
               ["preprocess", "bin_and_sort", "forward"] + ([] if upstream_mode else ["loss"]) +
               ["backward_blend", "prebwd_adam"])
 
-    def step(t, view, ev=None):
+    ks_dev = torch.zeros(max(1, args.steps), dtype=torch.int64, device="cuda")
+    kc = buf.k_capacity  # the render calls' capacity: the sort leaves K on the device
+
+    def step(t, view, ev=None, kslot=None):
         cam = gcams[view]
         marks = iter(ev or ())
 
@@ -381,22 +384,24 @@ def main():
         mark()
         gsmi.preprocess(buf.scene, p, cam, buf.proj)
         mark()
-        K = gsmi.bin_and_sort(buf.scene, cam, buf.proj, buf.ws, buf.k_capacity, buf.vals, buf.ranges)
+        gsmi.bin_and_sort(buf.scene, cam, buf.proj, buf.ws, buf.k_capacity, buf.vals, buf.ranges, wait=False)
+        if kslot is not None:  # this step's K, from the sort workspace's count (a device copy)
+            ks_dev[kslot].copy_(buf.ws[:8].view(torch.int64)[0])
         mark()
         g2 = buf.grad2d if args.unfused_adam else None
         if fused:  # forward, L1 and backward blend in one kernel; the sums stay staged
-            gsmi.render_plan(buf.scene, cam, buf.proj, buf.ranges, buf.render_ws, k=K)
+            gsmi.render_plan(buf.scene, cam, buf.proj, buf.ranges, buf.render_ws, k=kc)
             mark()
             gsmi.render_step(buf.scene, cam, buf.proj, buf.vals, buf.ranges, bg, targets[view], buf.image,
                              buf.T_final, buf.last, buf.loss, buf.dLdI, buf.render_ws, grad2d=g2, blend_count=blends,
-                             k=K)
+                             k=kc)
             mark()
             if args.densify:
                 gsmi.densify_stats(buf.scene, cam, buf.proj, buf.render_ws, dens_acc, dens_cnt)
                 mark()
         else:
             gsmi.render_forward(cam, N, buf.proj.splat, buf.vals, buf.ranges, bg, buf.image, buf.T_final, buf.last,
-                                buf.render_ws, blend_count=blends, k=K)
+                                buf.render_ws, blend_count=blends, k=kc)
             mark()
             if upstream_mode:
                 dl = up_t
@@ -409,7 +414,7 @@ def main():
                 dl = buf.dLdI
                 mark()
             gsmi.render_backward(buf.scene, None, cam, buf.proj, buf.vals, buf.ranges, bg, buf.T_final, buf.last,
-                                 dl, g2, buf.render_ws, k=K)
+                                 dl, g2, buf.render_ws, k=kc)
             mark()
         if args.batch > 1:  # t counts views; the optimizer steps once per batch
             j = (t - 1) % args.batch
@@ -418,7 +423,7 @@ def main():
             gsmi.preprocess_backward_accumulate(buf.scene, p, cam, buf.proj, buf.render_ws, grads_acc, j == 0,
                                                 1.0 / args.batch, adam)
             mark()
-            return K
+            return
         adam = gsmi.make_adam(m, v, t, 1e-3)
         if args.unfused_adam:
             gsmi.preprocess_backward(buf.scene, p, cam, buf.grad2d, grads)
@@ -426,7 +431,6 @@ def main():
         else:
             gsmi.preprocess_backward_staged(buf.scene, p, cam, buf.proj, buf.render_ws, None, adam)
         mark()
-        return K
 
     log(f"[bench] warmup {args.warmup} steps ...")
     t = 0
@@ -436,15 +440,17 @@ def main():
     torch.cuda.synchronize()
     blends.zero_()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)] for _ in range(args.steps)]
-    ks = []
     log(f"[bench] timing {args.steps} steps ...")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
         t += 1
-        ks.append(step(t, (args.warmup + k) % V, evs[k]))
+        step(t, (args.warmup + k) % V, evs[k], kslot=k)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    ks = [int(x) for x in ks_dev[: args.steps].cpu().tolist()]
+    if max(ks) > buf.k_capacity:  # an overflowed sort renders nothing: the step is not valid
+        raise SystemExit(f"K {max(ks)} exceeded the capacity {buf.k_capacity} in a timed step")
     # the device-side checks of every timed step: a bounded wait that gave up, or lists that
     # outgrew the workspace, would have left results incomplete
     flags, need = gsmi.render_status(buf.render_ws, raise_error=False)

@@ -110,7 +110,7 @@ __global__ __launch_bounds__(kBlock) void k_bin_reduce(int64_t n, const uint32_t
 }
 
 __global__ __launch_bounds__(1024) void k_bin_reduce_final(int64_t nblk, const Partial* __restrict__ part,
-                                                            BinInfo* __restrict__ info) {
+                                                            uint64_t kcap, BinInfo* __restrict__ info) {
   __shared__ unsigned long long ssum[16];
   __shared__ uint32_t smn[16], smx[16];
   unsigned long long s = 0;
@@ -134,26 +134,59 @@ __global__ __launch_bounds__(1024) void k_bin_reduce_final(int64_t nblk, const P
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    BinInfo r{0ull, 0xFFFFFFFFu, 0u};
+    BinInfo r{};
+    r.dmin = 0xFFFFFFFFu;
     for (int k = 0; k < 16; ++k) {
       r.K += ssum[k];
       r.dmin = min(r.dmin, smn[k]);
       r.dmax = max(r.dmax, smx[k]);
     }
+    r.kcap = kcap;
+    r.over = r.K > kcap ? 1u : 0u;
     *info = r;
   }
 }
 
-// ---- radix sort passes --------------------------------------------------------------------
-// Key transform of the first depth pass: clamp(k, lo, hi) - lo.
-__device__ __forceinline__ uint32_t xform_key(uint32_t k, bool xform, uint32_t lo, uint32_t hi) {
-  return xform ? (min(max(k, lo), hi) - lo) : k;
+// ---- what the device knows after the count -------------------------------------------------
+// Every later kernel reads the BinInfo the count wrote, so nothing waits for the host: the sort
+// runs when 0 < K <= capacity, the depth passes that would sort only constant bits return at
+// once, and the tile passes take K from the device.
+__device__ __forceinline__ bool sort_live(const BinInfo& in) { return in.K > 0ull && in.K <= in.kcap; }
+
+// bits of the depth-key span [dmin, dmax] of the visible Gaussians
+__device__ __forceinline__ int depth_bits(const BinInfo& in) {
+  const uint32_t span = in.dmax - in.dmin;  // sort_live implies dmin <= dmax
+  return span == 0u ? 0 : 32 - __clz((int)span);
 }
 
-__global__ __launch_bounds__(kBlock) void k_radix_hist(const uint32_t* __restrict__ keys, int64_t n,
-                                                        int shift, int xform, uint32_t lo, uint32_t hi,
+// depth passes that sort varying bits (at least one: it also writes the first key transform)
+__device__ __forceinline__ int depth_passes(const BinInfo& in) { return max(1, (depth_bits(in) + 7) / 8); }
+
+constexpr int kMaxDepthPasses = 4;
+enum PassKind { kDepthPass = 0, kTilePass = 1 };
+
+// whether pass p of this kind runs, and over how many items
+__device__ __forceinline__ bool pass_runs(const BinInfo& in, int kind, int p) {
+  return sort_live(in) && (kind == kTilePass || p < depth_passes(in));
+}
+__device__ __forceinline__ int64_t pass_items(const BinInfo& in, int kind, int64_t n_gauss) {
+  return kind == kTilePass ? (int64_t)in.K : n_gauss;
+}
+
+// ---- radix sort passes --------------------------------------------------------------------
+// Key transform of the first depth pass: clamp(k, dmin, dmax) - dmin.
+__device__ __forceinline__ uint32_t xform_key(uint32_t k, bool xform, const BinInfo& in) {
+  return xform ? (min(max(k, in.dmin), in.dmax) - in.dmin) : k;
+}
+
+// Per-block digit counts of one pass; a block past the items writes zeros (the scan adds them).
+__global__ __launch_bounds__(kBlock) void k_radix_hist(const uint32_t* __restrict__ keys, const BinInfo* __restrict__ info,
+                                                        int kind, int p, int64_t n_gauss, int shift, int xform,
                                                         uint32_t* __restrict__ counts, int64_t nblk) {
   __shared__ uint32_t hist[4][256];
+  const BinInfo in = *info;
+  if (!pass_runs(in, kind, p)) return;
+  const int64_t n = pass_items(in, kind, n_gauss);
   for (int e = threadIdx.x; e < 4 * 256; e += kBlock) (&hist[0][0])[e] = 0;
   __syncthreads();
   const int64_t base = (int64_t)blockIdx.x * kRadixTile;
@@ -162,7 +195,7 @@ __global__ __launch_bounds__(kBlock) void k_radix_hist(const uint32_t* __restric
   for (int j = 0; j < kItems; ++j) {
     const int64_t idx = base + j * kBlock + threadIdx.x;
     if (idx < n) {
-      const uint32_t k = xform_key(keys[idx], xform != 0, lo, hi);
+      const uint32_t k = xform_key(keys[idx], xform != 0, in);
       atomicAdd(&hist[w][(k >> shift) & 255u], 1u);
     }
   }
@@ -172,9 +205,11 @@ __global__ __launch_bounds__(kBlock) void k_radix_hist(const uint32_t* __restric
 }
 
 // One workgroup per digit: exclusive scan of counts[d][0..nblk) in place; totals[d] = sum.
-__global__ __launch_bounds__(kBlock) void k_radix_scan(uint32_t* __restrict__ counts, int64_t nblk,
+__global__ __launch_bounds__(kBlock) void k_radix_scan(const BinInfo* __restrict__ info, int kind, int p,
+                                                        uint32_t* __restrict__ counts, int64_t nblk,
                                                         uint32_t* __restrict__ totals) {
   __shared__ uint32_t tmp[4];
+  if (!pass_runs(*info, kind, p)) return;
   uint32_t* c = counts + (int64_t)blockIdx.x * nblk;
   const int64_t per = ceil_div(nblk, kBlock);
   const int64_t lo = threadIdx.x * per, hi = min(lo + per, nblk);
@@ -203,8 +238,8 @@ __device__ __forceinline__ void wave_sync_lds() {
 // waves' counts then give each wave its offset inside the block's run of each digit (waves in
 // index order), so the block is sorted stably in LDS and written out in runs of equal digits.
 __global__ __launch_bounds__(kBlock) void k_radix_scatter(
-    const uint32_t* __restrict__ keys_in, const uint32_t* __restrict__ vals_in, int64_t n, int shift,
-    int xform, uint32_t lo, uint32_t hi, const uint32_t* __restrict__ counts,
+    const uint32_t* __restrict__ keys_in, const uint32_t* __restrict__ vals_in, const BinInfo* __restrict__ info,
+    int kind, int p, int64_t n_gauss, int shift, int xform, const uint32_t* __restrict__ counts,
     const uint32_t* __restrict__ totals, int64_t nblk, uint32_t* __restrict__ keys_out,
     uint32_t* __restrict__ vals_out) {
   __shared__ uint32_t s_keys[kRadixTile];
@@ -214,8 +249,12 @@ __global__ __launch_bounds__(kBlock) void k_radix_scatter(
   __shared__ uint32_t lstart[256];
   __shared__ uint32_t tmp[4];
 
+  const BinInfo in = *info;
+  if (!pass_runs(in, kind, p)) return;
+  const int64_t n = pass_items(in, kind, n_gauss);
   const int tid = threadIdx.x, w = wave_id(), lane = tid & 63;
   const int64_t base = (int64_t)blockIdx.x * kRadixTile;
+  if (base >= n) return;  // (block-uniform) no items: the histogram counted none
 
   // global start of each digit's run for this block
   {
@@ -235,7 +274,7 @@ __global__ __launch_bounds__(kBlock) void k_radix_scatter(
     const bool valid = idx < n;
     uint32_t k = 0, v = 0;
     if (valid) {
-      k = xform_key(keys_in[idx], xform != 0, lo, hi);
+      k = xform_key(keys_in[idx], xform != 0, in);
       v = vals_in ? vals_in[idx] : (uint32_t)idx;
     }
     const uint32_t d = (k >> shift) & 255u;
@@ -256,7 +295,6 @@ __global__ __launch_bounds__(kBlock) void k_radix_scatter(
     if (valid && rank == 0) wcnt[w][d] = before + (uint32_t)__popcll(peers);
     wave_sync_lds();
   }
-  (void)lane;
   __syncthreads();
   // per digit: each wave's offset inside the block's run, and the run's start in the block
   {
@@ -297,14 +335,22 @@ __device__ __forceinline__ uint32_t rect_count(uint2 r) {
   return (x1 > x0 && y1 > y0) ? (x1 - x0) * (y1 - y0) : 0u;
 }
 
+// The depth passes leave the order in set A or B by the parity of the passes that ran.
+__device__ __forceinline__ bool result_in_b(const BinInfo& in) { return (depth_passes(in) & 1) != 0; }
+
 // rect_sorted[k] = tile rect of Gaussian order[k] (packed 16-bit x0|y0, x1|y1, from the
 // preprocess); bsum[block] = intersections of the block's items.  The gather reads the dense
 // 8-byte rect array, not the 48-byte records.
-__global__ __launch_bounds__(kBlock) void k_gather_rect(const uint32_t* __restrict__ order, int64_t n,
+__global__ __launch_bounds__(kBlock) void k_gather_rect(const BinInfo* __restrict__ info,
+                                                         const uint32_t* __restrict__ orderA,
+                                                         const uint32_t* __restrict__ orderB, int64_t n,
                                                          const uint2* __restrict__ rect,
                                                          uint2* __restrict__ rect_sorted,
                                                          uint32_t* __restrict__ bsum) {
   __shared__ uint32_t tmp[4];
+  const BinInfo in = *info;
+  if (!sort_live(in)) return;
+  const uint32_t* __restrict__ order = result_in_b(in) ? orderB : orderA;
   // item j of thread t is base + j kBlock + t: every load and store of a round is coalesced
   const int64_t base = (int64_t)blockIdx.x * kGatherTile + threadIdx.x;
   uint32_t s = 0;
@@ -328,8 +374,10 @@ __global__ __launch_bounds__(kBlock) void k_gather_rect(const uint32_t* __restri
 }
 
 // Exclusive scan of bsum[0..nblk) in place by one 1024-thread workgroup.
-__global__ __launch_bounds__(1024) void k_scan_blocks(uint32_t* __restrict__ bsum, int64_t nblk) {
+__global__ __launch_bounds__(1024) void k_scan_blocks(const BinInfo* __restrict__ info, uint32_t* __restrict__ bsum,
+                                                      int64_t nblk) {
   __shared__ uint32_t part[1024];
+  if (!sort_live(*info)) return;
   const int64_t per = ceil_div(nblk, 1024);
   const int64_t lo = threadIdx.x * per, hi = min(lo + per, nblk);
   uint32_t s = 0;
@@ -351,22 +399,26 @@ __global__ __launch_bounds__(1024) void k_scan_blocks(uint32_t* __restrict__ bsu
 }
 
 // Writes the intersections of Gaussians order[k] (in depth order) at their scanned slots:
-// tile id (row-major over the rect) and Gaussian index.  Writes past kcap are dropped.  The
-// block's items go in rounds of kBlock consecutive items, so the loads are coalesced and the
-// threads of a round write neighbouring slots.
-__global__ __launch_bounds__(kBlock) void k_keygen(const uint2* __restrict__ rect_sorted,
-                                                    const uint32_t* __restrict__ order, int64_t n,
+// tile id (row-major over the rect) and Gaussian index.  The block's items go in rounds of
+// kBlock consecutive items, so the loads are coalesced and the threads of a round write
+// neighbouring slots.
+__global__ __launch_bounds__(kBlock) void k_keygen(const BinInfo* __restrict__ info, const uint2* __restrict__ rect,
+                                                    const uint32_t* __restrict__ orderA,
+                                                    const uint32_t* __restrict__ orderB, int64_t n,
                                                     const uint32_t* __restrict__ bsum, int TX,
-                                                    int64_t kcap, uint32_t* __restrict__ tkeys,
-                                                    uint32_t* __restrict__ tvals) {
+                                                    uint32_t* __restrict__ tkeys, uint32_t* __restrict__ tvals) {
   __shared__ uint32_t tmp[4];
+  const BinInfo in = *info;
+  if (!sort_live(in)) return;
+  const uint32_t* __restrict__ order = result_in_b(in) ? orderB : orderA;
+  const int64_t kcap = (int64_t)in.kcap;
   const int64_t base = (int64_t)blockIdx.x * kGatherTile + threadIdx.x;
   uint2 r[kGatherItems];
   uint32_t gi[kGatherItems];
 #pragma unroll
   for (int j = 0; j < kGatherItems; ++j) {
     const int64_t k = base + (int64_t)j * kBlock;
-    r[j] = k < n ? rect_sorted[k] : make_uint2(0u, 0u);
+    r[j] = k < n ? rect[k] : make_uint2(0u, 0u);
     gi[j] = k < n ? order[k] : 0u;
   }
   int64_t run = bsum[blockIdx.x];  // slots of the block's earlier rounds
@@ -380,7 +432,7 @@ __global__ __launch_bounds__(kBlock) void k_keygen(const uint2* __restrict__ rec
     const uint32_t x0 = r[j].x & 0xFFFFu, y0 = r[j].x >> 16, x1 = r[j].y & 0xFFFFu, y1 = r[j].y >> 16;
     for (uint32_t ty = y0; ty < y1; ++ty)
       for (uint32_t tx = x0; tx < x1; ++tx) {
-        if (slot < kcap) {
+        if (slot < kcap) {  // always, with K <= capacity
           tkeys[slot] = ty * (uint32_t)TX + tx;
           tvals[slot] = gi[j];
         }
@@ -389,9 +441,22 @@ __global__ __launch_bounds__(kBlock) void k_keygen(const uint2* __restrict__ rec
   }
 }
 
-// ranges[2t], ranges[2t+1] = first and one-past-last position of tile t (ranges pre-zeroed).
-__global__ __launch_bounds__(kBlock) void k_ranges(const uint32_t* __restrict__ tk, int64_t K,
+// ranges <- all (0, 0), unless the lists overflowed and the caller asked for the ranges to be
+// left untouched then.
+__global__ __launch_bounds__(kBlock) void k_ranges_clear(const BinInfo* __restrict__ info, int64_t T,
+                                                         int keep_on_overflow, uint32_t* __restrict__ ranges) {
+  const BinInfo in = *info;
+  if (in.over && keep_on_overflow) return;
+  for (int64_t j = (int64_t)blockIdx.x * kBlock + threadIdx.x; j < 2 * T; j += (int64_t)gridDim.x * kBlock)
+    ranges[j] = 0u;
+}
+
+// ranges[2t], ranges[2t+1] = first and one-past-last position of tile t.
+__global__ __launch_bounds__(kBlock) void k_ranges(const uint32_t* __restrict__ tk, const BinInfo* __restrict__ info,
                                                     uint32_t T, uint32_t* __restrict__ ranges) {
+  const BinInfo in = *info;
+  if (!sort_live(in)) return;
+  const int64_t K = (int64_t)in.K;
   const int64_t j = (int64_t)blockIdx.x * kBlock + threadIdx.x;
   if (j >= K) return;
   const uint32_t t = tk[j];
@@ -400,31 +465,28 @@ __global__ __launch_bounds__(kBlock) void k_ranges(const uint32_t* __restrict__ 
   if (j == K - 1 || tk[j + 1] != t) ranges[2 * (int64_t)t + 1] = (uint32_t)(j + 1);
 }
 
-__global__ __launch_bounds__(kBlock) void k_iota(uint32_t* __restrict__ out, int64_t n) {
-  const int64_t j = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-  if (j < n) out[j] = (uint32_t)j;
-}
-
-__global__ __launch_bounds__(kBlock) void k_keys64(const uint32_t* __restrict__ tk,
+__global__ __launch_bounds__(kBlock) void k_keys64(const uint32_t* __restrict__ tk, const BinInfo* __restrict__ info,
                                                     const uint32_t* __restrict__ vals,
-                                                    const uint32_t* __restrict__ dkey, int64_t K,
-                                                    int64_t n, uint64_t* __restrict__ keys) {
+                                                    const uint32_t* __restrict__ dkey, int64_t n,
+                                                    uint64_t* __restrict__ keys) {
+  const BinInfo in = *info;
+  if (!sort_live(in)) return;
   const int64_t j = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-  if (j >= K) return;
+  if (j >= (int64_t)in.K) return;
   const uint32_t i = vals[j];
   keys[j] = ((uint64_t)tk[j] << 32) | (uint64_t)((int64_t)i < n ? dkey[i] : 0xFFFFFFFFu);
 }
 
-// One stable radix pass over bits [shift, shift+8) of n items.
-hipError_t radix_pass(const uint32_t* kin, const uint32_t* vin, int64_t n, int shift, bool xform,
-                      uint32_t lo, uint32_t hi, uint32_t* counts, uint32_t* totals, uint32_t* kout,
+// One stable radix pass over bits [shift, shift+8): `nblk` blocks of kRadixTile items cover the
+// most items the pass can have (the Gaussians, or the capacity); the device's count decides.
+hipError_t radix_pass(const BinInfo* info, int kind, int p, int64_t n_gauss, int64_t nblk, int shift, bool xform,
+                      const uint32_t* kin, const uint32_t* vin, uint32_t* counts, uint32_t* totals, uint32_t* kout,
                       uint32_t* vout, hipStream_t s) {
-  const int64_t nblk = ceil_div(n, kRadixTile);
-  hipLaunchKernelGGL(k_radix_hist, dim3((unsigned)nblk), dim3(kBlock), 0, s, kin, n, shift,
-                     (int)xform, lo, hi, counts, nblk);
-  hipLaunchKernelGGL(k_radix_scan, dim3(256), dim3(kBlock), 0, s, counts, nblk, totals);
-  hipLaunchKernelGGL(k_radix_scatter, dim3((unsigned)nblk), dim3(kBlock), 0, s, kin, vin, n, shift,
-                     (int)xform, lo, hi, counts, totals, nblk, kout, vout);
+  hipLaunchKernelGGL(k_radix_hist, dim3((unsigned)nblk), dim3(kBlock), 0, s, kin, info, kind, p, n_gauss, shift,
+                     (int)xform, counts, nblk);
+  hipLaunchKernelGGL(k_radix_scan, dim3(256), dim3(kBlock), 0, s, info, kind, p, counts, nblk, totals);
+  hipLaunchKernelGGL(k_radix_scatter, dim3((unsigned)nblk), dim3(kBlock), 0, s, kin, vin, info, kind, p, n_gauss,
+                     shift, (int)xform, (const uint32_t*)counts, (const uint32_t*)totals, nblk, kout, vout);
   return hipGetLastError();
 }
 
@@ -447,8 +509,8 @@ BinLayout bin_layout(int64_t n, int64_t kcap, int32_t W, int32_t H) {
     off = align_up(off + bytes);
     return o;
   };
+  L.info = take(sizeof(BinInfo));  // first: gs_bin_and_sort_count finds it without the sizes
   L.partials = take(sizeof(Partial) * nr);
-  L.info = take(sizeof(BinInfo));
   L.dkA = take(4 * nn);
   L.dvA = take(4 * nn);
   L.dkB = take(4 * nn);
@@ -465,70 +527,55 @@ BinLayout bin_layout(int64_t n, int64_t kcap, int32_t W, int32_t H) {
   return L;
 }
 
-hipError_t launch_bin_reduce(int64_t n, const uint32_t* tiles, const uint32_t* dkey, char* ws,
-                             const BinLayout& L, hipStream_t s) {
+hipError_t launch_bin_sort(int64_t n, int64_t kcap, const CamK& cam, gs_proj proj, char* ws, const BinLayout& L,
+                           uint32_t* vals, uint32_t* ranges, uint64_t* keys, bool keep_ranges_on_overflow,
+                           hipStream_t s) {
+  const int64_t T = (int64_t)cam.TX * cam.TY;
+  const BinInfo* info = reinterpret_cast<const BinInfo*>(ws + L.info);
+  // 0. K and the depth-key range of the visible Gaussians, and K against the capacity
   const int64_t nr = ceil_div(n > 0 ? n : 1, kReduceTile);
   Partial* part = reinterpret_cast<Partial*>(ws + L.partials);
   if (n > 0)
-    hipLaunchKernelGGL(k_bin_reduce, dim3((unsigned)nr), dim3(kBlock), 0, s, n, tiles, dkey, part);
-  hipLaunchKernelGGL(k_bin_reduce_final, dim3(1), dim3(1024), 0, s, n > 0 ? nr : 0, part,
-                     reinterpret_cast<BinInfo*>(ws + L.info));
-  return hipGetLastError();
-}
-
-hipError_t launch_bin_sort_rest(int64_t n, int64_t K, const BinInfo& info, const CamK& cam,
-                                gs_proj proj, char* ws, const BinLayout& L, uint32_t* vals,
-                                uint32_t* ranges, uint64_t* keys, hipStream_t s) {
-  hipError_t e;
-  const int64_t T = (int64_t)cam.TX * cam.TY;
-  if ((e = launch_fill_u32(ranges, 2 * T, 0u, s)) != hipSuccess) return e;
-  if (K == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_bin_reduce, dim3((unsigned)nr), dim3(kBlock), 0, s, n, proj.tiles, proj.depth_key, part);
+  hipLaunchKernelGGL(k_bin_reduce_final, dim3(1), dim3(1024), 0, s, n > 0 ? nr : 0, (const Partial*)part,
+                     (uint64_t)(kcap > 0 ? kcap : 0), reinterpret_cast<BinInfo*>(ws + L.info));
+  const unsigned clear_grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>(ceil_div(2 * T, kBlock), 1024));
+  hipLaunchKernelGGL(k_ranges_clear, dim3(clear_grid), dim3(kBlock), 0, s, info, T, (int)keep_ranges_on_overflow,
+                     ranges);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || n <= 0 || kcap <= 0) return e;
   uint32_t* counts = reinterpret_cast<uint32_t*>(ws + L.counts);
   uint32_t* totals = reinterpret_cast<uint32_t*>(ws + L.totals);
 
-  // 1. stable depth passes over the N Gaussians (only the bits of dmax - dmin)
-  const uint32_t span = info.dmax - info.dmin;
-  const int dbits = span == 0 ? 0 : 32 - __builtin_clz(span);
-  const int dpasses = (dbits + 7) / 8;
+  // 1. stable depth passes over the N Gaussians: pass p reads set (p odd ? B : A) (pass 0 the
+  //    depth keys and the identity order) and writes the other set
   uint32_t* kA = reinterpret_cast<uint32_t*>(ws + L.dkA);
   uint32_t* vA = reinterpret_cast<uint32_t*>(ws + L.dvA);
   uint32_t* kB = reinterpret_cast<uint32_t*>(ws + L.dkB);
   uint32_t* vB = reinterpret_cast<uint32_t*>(ws + L.dvB);
-  const uint32_t* order = nullptr;  // Gaussian indices in (depth, index) order; null = identity
-  {
-    const uint32_t* kin = proj.depth_key;
-    const uint32_t* vin = nullptr;
-    for (int p = 0; p < dpasses; ++p) {
-      const bool last = p == dpasses - 1;
-      uint32_t* ko = (p & 1) ? kA : kB;
-      uint32_t* vo = (p & 1) ? vA : vB;
-      if ((e = radix_pass(kin, vin, n, 8 * p, p == 0, info.dmin, info.dmax, counts, totals,
-                          last ? nullptr : ko, vo, s)) != hipSuccess)
-        return e;
-      kin = ko;
-      vin = vo;
-    }
-    order = vin;
-  }
-  if (order == nullptr) {
-    // no depth bits vary: (depth, index) order is the index order
-    hipLaunchKernelGGL(k_iota, dim3((unsigned)ceil_div(n, kBlock)), dim3(kBlock), 0, s, vA, n);
-    order = vA;
+  for (int p = 0; p < kMaxDepthPasses; ++p) {
+    const bool first = p == 0, odd = (p & 1) != 0;
+    const uint32_t* kin = first ? proj.depth_key : (odd ? kB : kA);
+    const uint32_t* vin = first ? nullptr : (odd ? vB : vA);
+    uint32_t* kout = p == kMaxDepthPasses - 1 ? nullptr : (odd ? kA : kB);
+    if ((e = radix_pass(info, kDepthPass, p, n, L.nblk_n, 8 * p, first, kin, vin, counts, totals, kout,
+                        odd ? vA : vB, s)) != hipSuccess)
+      return e;
   }
 
   // 2. emission in depth order: rects, block sums, scan, keys
   uint2* rect = reinterpret_cast<uint2*>(ws + L.rect);
   uint32_t* bsum = reinterpret_cast<uint32_t*>(ws + L.bsum);
   const int64_t nb = ceil_div(n, kGatherTile);
-  hipLaunchKernelGGL(k_gather_rect, dim3((unsigned)nb), dim3(kBlock), 0, s, order, n,
-                     reinterpret_cast<const uint2*>(proj.rect), rect, bsum);
-  hipLaunchKernelGGL(k_scan_blocks, dim3(1), dim3(1024), 0, s, bsum, nb);
+  hipLaunchKernelGGL(k_gather_rect, dim3((unsigned)nb), dim3(kBlock), 0, s, info, (const uint32_t*)vA,
+                     (const uint32_t*)vB, n, reinterpret_cast<const uint2*>(proj.rect), rect, bsum);
+  hipLaunchKernelGGL(k_scan_blocks, dim3(1), dim3(1024), 0, s, info, bsum, nb);
   uint32_t* tkA = reinterpret_cast<uint32_t*>(ws + L.tkA);
   uint32_t* tvA = reinterpret_cast<uint32_t*>(ws + L.tvA);
   uint32_t* tkB = reinterpret_cast<uint32_t*>(ws + L.tkB);
   uint32_t* tvB = reinterpret_cast<uint32_t*>(ws + L.tvB);
-  hipLaunchKernelGGL(k_keygen, dim3((unsigned)nb), dim3(kBlock), 0, s, rect, order, n, bsum, cam.TX,
-                     K, tkA, tvA);
+  hipLaunchKernelGGL(k_keygen, dim3((unsigned)nb), dim3(kBlock), 0, s, info, (const uint2*)rect, (const uint32_t*)vA,
+                     (const uint32_t*)vB, n, (const uint32_t*)bsum, cam.TX, tkA, tvA);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
   // 3. stable tile passes over the K intersections; the last pass writes `vals`
@@ -541,7 +588,8 @@ hipError_t launch_bin_sort_rest(int64_t n, int64_t K, const BinInfo& info, const
     const bool last = p == tpasses - 1;
     uint32_t* ko = (p & 1) ? tkA : tkB;
     uint32_t* vo = last ? vals : ((p & 1) ? tvA : tvB);
-    if ((e = radix_pass(kin, vin, K, 8 * p, false, 0u, 0u, counts, totals, ko, vo, s)) != hipSuccess)
+    if ((e = radix_pass(info, kTilePass, p, n, L.nblk_k, 8 * p, false, kin, vin, counts, totals, ko, vo, s)) !=
+        hipSuccess)
       return e;
     kin = ko;
     vin = vo;
@@ -549,10 +597,11 @@ hipError_t launch_bin_sort_rest(int64_t n, int64_t K, const BinInfo& info, const
   const uint32_t* tsorted = kin;
 
   // 4. per-tile ranges and the optional 64-bit keys
-  const unsigned gk = (unsigned)ceil_div(K, kBlock);
-  hipLaunchKernelGGL(k_ranges, dim3(gk), dim3(kBlock), 0, s, tsorted, K, (uint32_t)T, ranges);
+  const unsigned gk = (unsigned)ceil_div(kcap, kBlock);
+  hipLaunchKernelGGL(k_ranges, dim3(gk), dim3(kBlock), 0, s, tsorted, info, (uint32_t)T, ranges);
   if (keys)
-    hipLaunchKernelGGL(k_keys64, dim3(gk), dim3(kBlock), 0, s, tsorted, vals, proj.depth_key, K, n, keys);
+    hipLaunchKernelGGL(k_keys64, dim3(gk), dim3(kBlock), 0, s, tsorted, info, (const uint32_t*)vals,
+                       (const uint32_t*)proj.depth_key, n, keys);
   return hipGetLastError();
 }
 

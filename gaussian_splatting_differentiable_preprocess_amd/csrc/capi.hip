@@ -178,17 +178,17 @@ int gs_bin_and_sort(const gs_scene* scene, const gs_camera* cam, gs_proj proj, v
                     uint64_t* keys, int64_t* k_out, hipStream_t stream) {
   int st;
   if ((st = check_scene(scene)) || (st = check_camera(cam)) || (st = check_proj(proj, true, scene->n))) return st;
-  if (!workspace || !vals || !ranges || !k_out)
-    return fail(GS_ERR_INVALID_ARGUMENT, "workspace / vals / ranges / k_out is null");
+  if (!workspace || !vals || !ranges) return fail(GS_ERR_INVALID_ARGUMENT, "workspace / vals / ranges is null");
   if (k_capacity < 0 || k_capacity > 4294967295LL) return fail(GS_ERR_INVALID_ARGUMENT, "k_capacity out of range");
   const BinLayout L = bin_layout(scene->n, k_capacity, cam->width, cam->height);
   if (workspace_bytes < L.total)
     return fail(GS_ERR_INVALID_ARGUMENT, "workspace has %zu bytes, needs %zu", workspace_bytes, L.total);
   if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(GS_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
   char* ws = static_cast<char*>(workspace);
-  const CamK ck = make_cam(*cam);
-  hipError_t e = launch_bin_reduce(scene->n, proj.tiles, proj.depth_key, ws, L, stream);
-  if (e != hipSuccess) return hip_fail(e, "gs_bin_and_sort (reduce)");
+  hipError_t e = launch_bin_sort(scene->n, k_capacity, make_cam(*cam), proj, ws, L, vals, ranges, keys,
+                                 /*keep_ranges_on_overflow=*/k_out != nullptr, stream);
+  if (e != hipSuccess) return hip_fail(e, "gs_bin_and_sort");
+  if (!k_out) return ok();
   BinInfo info{};
   e = hipMemcpyAsync(&info, ws + L.info, sizeof(BinInfo), hipMemcpyDeviceToHost, stream);
   if (e == hipSuccess) e = hipStreamSynchronize(stream);
@@ -196,8 +196,22 @@ int gs_bin_and_sort(const gs_scene* scene, const gs_camera* cam, gs_proj proj, v
   *k_out = (int64_t)info.K;
   if ((int64_t)info.K > k_capacity)
     return fail(GS_ERR_CAPACITY, "%llu intersections exceed k_capacity %lld", info.K, (long long)k_capacity);
-  e = launch_bin_sort_rest(scene->n, (int64_t)info.K, info, ck, proj, ws, L, vals, ranges, keys, stream);
-  return e == hipSuccess ? ok() : hip_fail(e, "gs_bin_and_sort");
+  return ok();
+}
+
+int gs_bin_and_sort_count(const void* workspace, size_t workspace_bytes, int64_t* k_out, hipStream_t stream) {
+  if (!workspace || !k_out) return fail(GS_ERR_INVALID_ARGUMENT, "workspace / k_out is null");
+  if (workspace_bytes < sizeof(BinInfo)) return fail(GS_ERR_INVALID_ARGUMENT, "workspace too small");
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u) return fail(GS_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  BinInfo info{};
+  hipError_t e = hipMemcpyAsync(&info, workspace, sizeof(BinInfo), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "gs_bin_and_sort_count");
+  *k_out = (int64_t)info.K;
+  if (info.K > info.kcap)
+    return fail(GS_ERR_CAPACITY, "%llu intersections exceeded the capacity %llu of the last gs_bin_and_sort",
+                info.K, info.kcap);
+  return ok();
 }
 
 int gs_render_workspace(int32_t width, int32_t height, int64_t n, int64_t k_capacity, size_t* bytes) {

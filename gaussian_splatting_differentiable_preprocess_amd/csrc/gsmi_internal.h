@@ -79,20 +79,25 @@ hipError_t launch_preprocess_backward(const PrebwdArgs& a, const CamK& cam, hipS
 
 // binning / sorting
 struct BinLayout {
-  size_t partials, info, dkA, dvA, dkB, dvB, counts, totals, rect, bsum, tkA, tvA, tkB, tvB;
+  size_t info, partials, dkA, dvA, dkB, dvB, counts, totals, rect, bsum, tkA, tvA, tkB, tvB;
   size_t total;
   int64_t nblk_n, nblk_k, nblk_rect;
 };
 BinLayout bin_layout(int64_t n, int64_t kcap, int32_t W, int32_t H);
+// What the count leaves at the start of the sort workspace; every later sort kernel reads it.
 struct BinInfo {
-  unsigned long long K;
-  uint32_t dmin, dmax;
+  unsigned long long K;     // intersections
+  unsigned long long kcap;  // the capacity of the call
+  uint32_t dmin, dmax;      // depth-key range of the visible Gaussians
+  uint32_t over;            // K > kcap: nothing is sorted
+  uint32_t pad;
 };
-hipError_t launch_bin_reduce(int64_t n, const uint32_t* tiles, const uint32_t* dkey, char* ws,
-                             const BinLayout& L, hipStream_t s);
-hipError_t launch_bin_sort_rest(int64_t n, int64_t K, const BinInfo& info, const CamK& cam,
-                                gs_proj proj, char* ws, const BinLayout& L, uint32_t* vals,
-                                uint32_t* ranges, uint64_t* keys, hipStream_t s);
+// The whole binning and sort, enqueued without waiting: K and the depth range stay on the device.
+// On overflow (K > kcap) vals and keys are not written, and ranges are cleared to empty unless
+// keep_ranges_on_overflow.
+hipError_t launch_bin_sort(int64_t n, int64_t kcap, const CamK& cam, gs_proj proj, char* ws, const BinLayout& L,
+                           uint32_t* vals, uint32_t* ranges, uint64_t* keys, bool keep_ranges_on_overflow,
+                           hipStream_t s);
 
 // blending
 //

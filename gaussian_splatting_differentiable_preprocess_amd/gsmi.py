@@ -25,6 +25,7 @@ SPLAT_FLOATS = 12  # 48-byte record: u, v, radius_x, radius_y | A, B, C, opacity
 
 EXPORTS = (
     "gs_version", "gs_last_error", "gs_preprocess", "gs_bin_and_sort_workspace", "gs_bin_and_sort",
+    "gs_bin_and_sort_count",
     "gs_render_workspace", "gs_render_workspace_capacity", "gs_render_forward", "gs_loss_l1_workspace", "gs_loss_l1",
     "gs_loss_l1_noalloc",
     "gs_loss_l1_dssim_workspace", "gs_loss_l1_dssim", "gs_render_backward",
@@ -95,6 +96,7 @@ def load(path: str = LIB_PATH):
     L.gs_preprocess.argtypes = [SP, P, CP, GsProj, P]
     L.gs_bin_and_sort_workspace.argtypes = [i64, i64, i32, i32, ctypes.POINTER(sz)]
     L.gs_bin_and_sort.argtypes = [SP, CP, GsProj, P, sz, i64, P, P, P, ctypes.POINTER(i64), P]
+    L.gs_bin_and_sort_count.argtypes = [P, sz, ctypes.POINTER(i64), P]
     L.gs_render_workspace.argtypes = [i32, i32, i64, i64, ctypes.POINTER(sz)]
     L.gs_render_workspace_capacity.argtypes = [i32, i32, i64, sz, ctypes.POINTER(i64)]
     L.gs_render_forward.argtypes = [CP, i64, P, P, P, i64, ctypes.POINTER(ctypes.c_float), P, P, P, P, P, P, sz, P]
@@ -216,12 +218,25 @@ def bin_and_sort_workspace(n, k_capacity, width, height) -> int:
 
 
 def bin_and_sort(scene: GsScene, cam: GsCamera, proj: Proj, workspace, k_capacity, vals, ranges,
-                 keys=None, stream=None) -> int:
-    """Returns K.  Raises GsCapacityError (with .required) if K > k_capacity."""
+                 keys=None, stream=None, wait=True):
+    """Returns K.  Raises GsCapacityError (with .required) if K > k_capacity.  With wait=False
+    the sort is only enqueued (no host synchronisation) and None is returned; bin_and_sort_count
+    reads K (and reports an overflow) later."""
     k = ctypes.c_int64(0)
     rc = load().gs_bin_and_sort(ctypes.byref(scene), ctypes.byref(cam), proj.c(), _ptr(workspace),
                                 workspace.numel() * workspace.element_size(), int(k_capacity),
-                                _ptr(vals), _ptr(ranges), _ptr(keys), ctypes.byref(k), _stream(stream))
+                                _ptr(vals), _ptr(ranges), _ptr(keys), ctypes.byref(k) if wait else None,
+                                _stream(stream))
+    _check(rc, required=k.value)
+    return k.value if wait else None
+
+
+def bin_and_sort_count(workspace, stream=None) -> int:
+    """K of the last bin_and_sort on `workspace` (waits for the stream).  Raises GsCapacityError
+    if that call overflowed its capacity."""
+    k = ctypes.c_int64(0)
+    rc = load().gs_bin_and_sort_count(_ptr(workspace), workspace.numel() * workspace.element_size(),
+                                      ctypes.byref(k), _stream(stream))
     _check(rc, required=k.value)
     return k.value
 

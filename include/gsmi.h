@@ -36,7 +36,8 @@
  *     unless marked "host".  The caller owns every buffer; the library never allocates or
  *     frees device memory.  Host structs are read during the call only.
  *   - Every call enqueues work on `stream` and returns without waiting, except
- *     gs_bin_and_sort and gs_densify, which copy a count to the host and synchronise
+ *     gs_bin_and_sort (with a non-null k_out), gs_bin_and_sort_count and gs_densify, which copy
+ *     a count to the host and synchronise
  *     `stream` once, and gs_render_status, which reads the render workspace's status words
  *     (see there).
  *   - Outputs must not alias inputs, except where a call says it updates in place.
@@ -56,7 +57,7 @@
 extern "C" {
 #endif
 
-#define GSMI_VERSION 8
+#define GSMI_VERSION 9
 #define GS_TILE 16 /* tiles are GS_TILE x GS_TILE pixels */
 
 typedef enum gs_status {
@@ -169,13 +170,24 @@ int gs_bin_and_sort_workspace(int64_t n, int64_t k_capacity, int32_t width, int3
  *                           (0, 0) for an empty tile.  T = ceil(W/16) * ceil(H/16).
  *   keys[k_capacity]   out, nullable: the sorted 64-bit keys
  *   workspace          device scratch of >= gs_bin_and_sort_workspace() bytes
- *   k_out              HOST out: the number of intersections K
- * Synchronisation: this call copies K to the host and waits for `stream` once.  If K >
- * k_capacity it sets *k_out = K and returns GS_ERR_CAPACITY without writing vals, ranges or
- * keys; the caller grows its buffers and calls again. */
+ *   k_out              HOST out, nullable: the number of intersections K
+ * The count, the depth-key range and K stay on the device: every kernel of the sort reads them
+ * there, so the whole sort is enqueued without waiting.  With k_out non-null the call then copies
+ * K to the host and waits for `stream` once, at the end; if K > k_capacity it sets *k_out = K and
+ * returns GS_ERR_CAPACITY, and vals, ranges and keys are left unwritten (the caller grows its
+ * buffers and calls again).  With k_out null the call returns without waiting; if K > k_capacity
+ * then, vals and keys are left unwritten and every tile's range is set empty (nothing renders,
+ * nothing is partial), and gs_bin_and_sort_count reports the overflow. */
 int gs_bin_and_sort(const gs_scene* scene, const gs_camera* cam, gs_proj proj, void* workspace,
                     size_t workspace_bytes, int64_t k_capacity, uint32_t* vals, uint32_t* ranges,
                     uint64_t* keys, int64_t* k_out, hipStream_t stream);
+
+/* K of the last gs_bin_and_sort on `workspace` (after the work enqueued on `stream` so far):
+ * copies it to *k_out (HOST) and waits for `stream`.  GS_ERR_CAPACITY (with *k_out = K) if that
+ * call's lists overflowed its k_capacity; GS_ERR_INVALID_ARGUMENT for a null or misaligned
+ * workspace.  For callers that sort with k_out null and check the count later, e.g. once per
+ * batch of steps instead of once per step. */
+int gs_bin_and_sort_count(const void* workspace, size_t workspace_bytes, int64_t* k_out, hipStream_t stream);
 
 /* Bytes of the render workspace that gs_render_forward fills and gs_render_backward uses, for
  * a width x height image, n Gaussians and lists of up to k_capacity intersections (host-only

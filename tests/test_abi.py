@@ -22,7 +22,21 @@ def test_library_exports_every_declared_symbol():
     assert len(names) == len(gsmi.EXPORTS) and set(names) == set(gsmi.EXPORTS)
     for name in names:
         assert hasattr(L, name), name
-    assert gsmi.version() == 8
+    assert gsmi.version() == 9
+
+
+def test_sort_count_arguments_checked_on_the_host():
+    """gs_bin_and_sort_count rejects a null, short or misaligned workspace and a null k_out
+    before any HIP call."""
+    L = gsmi.load()
+    k = ctypes.c_int64(0)
+    assert L.gs_bin_and_sort_count(None, 4096, ctypes.byref(k), None) == gsmi.GS_ERR_INVALID_ARGUMENT
+    assert "null" in gsmi.last_error()
+    assert L.gs_bin_and_sort_count(ctypes.c_void_p(256), 4096, None, None) == gsmi.GS_ERR_INVALID_ARGUMENT
+    assert L.gs_bin_and_sort_count(ctypes.c_void_p(256), 8, ctypes.byref(k), None) == gsmi.GS_ERR_INVALID_ARGUMENT
+    assert "small" in gsmi.last_error()
+    assert L.gs_bin_and_sort_count(ctypes.c_void_p(260), 4096, ctypes.byref(k), None) == gsmi.GS_ERR_INVALID_ARGUMENT
+    assert "aligned" in gsmi.last_error()
 
 
 def test_invalid_arguments_rejected_before_any_gpu_call():

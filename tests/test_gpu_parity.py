@@ -520,6 +520,40 @@ def test_capacity_error_reports_required_k():
     torch.cuda.synchronize()
 
 
+def test_sort_without_waiting_matches_and_reports_overflow_later():
+    """gs_bin_and_sort with no host count (nothing waits): the same keys, ids and ranges as the
+    waiting call, K read afterwards by gs_bin_and_sort_count; with the capacity one short, every
+    range empty, the ids untouched and the count call reporting GS_ERR_CAPACITY with K."""
+    import torch
+    say("[parity] test_sort_without_waiting")
+    params = inputs.small_scene(13, 3000, 0, logscale_mean=-2.4, logscale_std=0.5)
+    W, H = 160, 120
+    cam = inputs.lookat_camera((3.0, 0.3, 0.2), W, H)
+    g = GpuStep(params, 0, cam, W, H)
+    g.preprocess()
+    K, keys, vals, ranges = g.bin_and_sort()
+    T = gsmi.n_tiles(W, H)
+    scene, ck = g.scene, g.cam
+    for kcap, want_over in ((K + 5000, False), (K, False), (K - 1, True)):
+        ws = torch.empty(gsmi.bin_and_sort_workspace(g.n, kcap, W, H), dtype=torch.uint8, device="cuda")
+        v2 = torch.full((max(kcap, 1),), -7, dtype=torch.int32, device="cuda")
+        k2 = torch.zeros(max(kcap, 1), dtype=torch.int64, device="cuda")
+        r2 = torch.full((T, 2), 5, dtype=torch.int32, device="cuda")
+        assert gsmi.bin_and_sort(scene, ck, g.proj, ws, kcap, v2, r2, k2, wait=False) is None
+        if want_over:
+            with pytest.raises(gsmi.GsCapacityError) as ei:
+                gsmi.bin_and_sort_count(ws)
+            assert ei.value.required == K
+            assert (r2.cpu().numpy() == 0).all()           # nothing renders
+            assert (v2.cpu().numpy() == -7).all()          # nothing partial
+        else:
+            assert gsmi.bin_and_sort_count(ws) == K
+            np.testing.assert_array_equal(v2.cpu().numpy().view(np.uint32)[:K], vals)
+            np.testing.assert_array_equal(k2.cpu().numpy().view(np.uint64)[:K], keys)
+            np.testing.assert_array_equal(r2.cpu().numpy().view(np.uint32), ranges)
+    torch.cuda.synchronize()
+
+
 def test_single_gaussian_closed_form_on_gpu():
     say("[parity] test_single_gaussian")
     W = 64
