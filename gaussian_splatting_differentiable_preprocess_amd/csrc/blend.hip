@@ -705,8 +705,9 @@ __device__ void backward_item(const BwdArgs& a, uint32_t shift, uint2 it, BlendS
   const uint32_t start = rg.x, end = rg.y, len = rg.y - rg.x;
   const uint64_t cbase = (uint64_t)(start / kChunk) + (uint64_t)tile;  // the tile's first mask chunk
 
-  float Tr = 0.f, g0 = 0.f, g1 = 0.f, g2 = 0.f, bgT = 0.f;
-  float S0 = 0.f, S1 = 0.f, S2 = 0.f;  // colour accumulated behind the current entry, / T_{k+1}
+  // Tr: the transmittance behind the current entry; Sg: the colour behind it (normalised by
+  // Tr) dotted with dL/dI -- the gradient needs that colour only through this product
+  float Tr = 0.f, Sg = 0.f, g0 = 0.f, g1 = 0.f, g2 = 0.f, bgT = 0.f;
   uint32_t last = 0;
   if (inside) {
     const int64_t p = (int64_t)py * W + px;
@@ -731,11 +732,8 @@ __device__ void backward_item(const BwdArgs& a, uint32_t shift, uint2 it, BlendS
     const float4* st = a.slots + (size_t)a.bnd_off[tile] * (kTile * kTile) + pix;
     const float4 sb = get_f4<kStep>(st + (size_t)k * (kTile * kTile));
     const float4 sf = get_f4<kStep>(st + (size_t)((len - 1u) >> shift) * (kTile * kTile));
-    const float inv = 1.0f / sb.x;  // T >= 1e-4 at every boundary
-    Tr = sb.x;
-    S0 = (sf.y - sb.y) * inv;
-    S1 = (sf.z - sb.z) * inv;
-    S2 = (sf.w - sb.w) * inv;
+    Tr = sb.x;  // T >= 1e-4 at every boundary
+    Sg = ((sf.y - sb.y) * g0 + (sf.z - sb.z) * g1 + (sf.w - sb.w) * g2) / sb.x;
   }
 
   // windows of kWin entries, top down; the waves walk a window independently, then the
@@ -795,8 +793,8 @@ __device__ void backward_item(const BwdArgs& a, uint32_t shift, uint2 it, BlendS
           const float rom = __builtin_amdgcn_rcpf(om);  // om >= 0.01
           const float Tk = Tr * rom;                    // transmittance in front of this entry
           const float wt = alpha * Tk;
-          const float cr = cl.z, cg = cl.w;
-          const float dL_dalpha = Tk * ((cr - S0) * g0 + (cg - S1) * g1 + (cb - S2) * g2) - bgT * rom;
+          const float cdg = cl.z * g0 + cl.w * g1 + cb * g2;  // c . dL/dI
+          const float dL_dalpha = Tk * (cdg - Sg) - bgT * rom;
           const bool unclamped = act && oG <= kAlphaMax;  // alpha = o G depends on o and power
           const float dpow = unclamped ? oG * dL_dalpha : 0.0f;
           // moments of dL/dpower over the pixels; the conic gradients are linear in them
@@ -811,23 +809,14 @@ __device__ void backward_item(const BwdArgs& a, uint32_t shift, uint2 it, BlendS
           v[7] = act ? wt * g1 : 0.0f;
           v[8] = act ? wt * g2 : 0.0f;
           if (act) {
-            S0 = alpha * cr + om * S0;
-            S1 = alpha * cg + om * S1;
-            S2 = alpha * cb + om * S2;
+            Sg = alpha * cdg + om * Sg;
             Tr = Tk;
           }
           quad_sum<9>(v);  // every lane of a pixel block holds the block's sums
-          if ((lane & 3) == 0 && has) {
-            // dL/du = (A m_x + B m_y), dL/dv = (B m_x + C m_y), dL/dA = -m_xx / 2,
-            // dL/dB = -m_xy, dL/dC = -m_yy / 2 with A = -2 nA, B = -nB, C = -2 nC
+          if ((lane & 3) == 0 && has) {  // the raw moments: the conic enters once per entry
             const uint32_t ws = wbase + (uint32_t)e;
-            atomicAdd(&acc[0][ws], -(2.0f * g.z * v[0] + g.w * v[1]));
-            atomicAdd(&acc[1][ws], -(g.w * v[0] + 2.0f * cl.x * v[1]));
-            atomicAdd(&acc[2][ws], -0.5f * v[2]);
-            atomicAdd(&acc[3][ws], -v[3]);
-            atomicAdd(&acc[4][ws], -0.5f * v[4]);
 #pragma unroll
-            for (int q = 5; q < 9; ++q) atomicAdd(&acc[q][ws], v[q]);
+            for (int q = 0; q < 9; ++q) atomicAdd(&acc[q][ws], v[q]);
           }
         }
         wave_sync_lds();  // this chunk's reads finish before the next chunk is staged
@@ -848,7 +837,16 @@ __device__ void backward_item(const BwdArgs& a, uint32_t shift, uint2 it, BlendS
       }
       if (any) {
         const uint32_t gid = vals[start + wlo + tid];
-        const float4 q0 = splat[3 * (int64_t)gid];  // u, v, radius_x, radius_y
+        const float4 q0 = splat[3 * (int64_t)gid];      // u, v, radius_x, radius_y
+        const float4 q1 = splat[3 * (int64_t)gid + 1];  // conic A, B, C, opacity
+        // from the moments m of dL/dpower (power = -(A dx^2 + C dy^2)/2 - B dx dy):
+        // dL/du = A m_x + B m_y, dL/dv = B m_x + C m_y, dL/dA = -m_xx/2, dL/dB = -m_xy, dL/dC = -m_yy/2
+        const float mx_ = x[0], my_ = x[1];
+        x[0] = q1.x * mx_ + q1.y * my_;
+        x[1] = q1.y * mx_ + q1.z * my_;
+        x[2] = -0.5f * x[2];
+        x[3] = -x[3];
+        x[4] = -0.5f * x[4];
         int x0, y0, x1, y1;
         tile_rect(q0.x, q0.y, __float_as_int(q0.z), __float_as_int(q0.w), TX, TY, x0, y0, x1, y1);
         const uint64_t slot = (uint64_t)goff_blk[gid / kGoffBlock] + goff[gid] +
