@@ -22,7 +22,10 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIBRARY names a prebuilt copy of the library to load instead (the host-sanitizer test
+# builds one with AddressSanitizer and UndefinedBehaviorSanitizer); such a copy is never rebuilt.
+_LIB_OVERRIDE = os.environ.get("ORACLE_LIBRARY")
+_LIB = _LIB_OVERRIDE or os.path.join(_HERE, "liboracle.so")
 
 PROJ_FIELDS = ("u", "v", "depth", "opacity", "A", "B", "C", "r", "g", "b")
 GRAD2D_FIELDS = ("u", "v", "A", "B", "C", "opacity", "r", "g", "b")
@@ -31,6 +34,8 @@ DEC_SKIP, DEC_BLEND, DEC_BLEND_CLAMPED, DEC_STOP, DEC_NONE = 0, 1, 2, 3, 4
 
 def build(force: bool = False) -> str:
     """Compile oracle.c with gcc (no fast-math, no FMA contraction)."""
+    if _LIB_OVERRIDE:
+        return _LIB
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + f".tmp{os.getpid()}"
         subprocess.check_call(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
