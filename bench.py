@@ -487,6 +487,10 @@ def main():
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4)}
     roof.update({"traffic": traffic, "traffic_over_alg_bytes": round(traffic / bytes_alg, 2) if traffic else None,
+                 # the counters' HBM bytes per launch over the launch time, against the 8 TB/s peak:
+                 # the rate the hardware sustains, redundant re-reads included
+                 "traffic_GBps": round(traffic / sec / 1e9, 1) if traffic else None,
+                 "traffic_frac_of_hbm_peak": round(traffic / sec / 1e9 / HBM_PEAK_GBS, 4) if traffic else None,
                  "kernel": kname, "work_per_launch": work, "ms_per_launch": round(ph_ms[dom], 4)})
     per_phase = {}
     for ph in phases:
