@@ -458,6 +458,9 @@ def main():
         raise SystemExit(f"render status flags {flags} (need {need} intersections): timed results not valid")
     total_blends = int(blends[0].item())
     ms_per_step = wall * 1e3 / args.steps
+    # the last step's split tiles (their forward runs in parallel segments) from the header
+    hdr = buf.render_ws[:64].cpu().numpy().view(np.uint32)
+    log(f"[bench] last view: {int(hdr[10])} split tiles, {int(hdr[11])} forward segments")
     ph_ms = {ph: float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)]))
              for i, ph in enumerate(phases)}
     log("[bench] per-phase ms: " + ", ".join(f"{k} {v:.3f}" for k, v in ph_ms.items()))

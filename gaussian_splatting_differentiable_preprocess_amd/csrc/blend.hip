@@ -233,6 +233,18 @@ __device__ __forceinline__ float4 get_f4(const float4* p) {
     return *p;
   }
 }
+template <bool kDev>
+__device__ __forceinline__ void put_u4(uint4* p, uint4 v) {
+  uint2* q = reinterpret_cast<uint2*>(p);
+  put_u2<kDev>(q, make_uint2(v.x, v.y));
+  put_u2<kDev>(q + 1, make_uint2(v.z, v.w));
+}
+template <bool kDev>
+__device__ __forceinline__ uint4 get_u4(const uint4* p) {
+  const uint2* q = reinterpret_cast<const uint2*>(p);
+  const uint2 a = get_u2<kDev>(q), b = get_u2<kDev>(q + 1);
+  return make_uint4(a.x, a.y, b.x, b.y);
+}
 template <bool kDev, typename T>
 __device__ __forceinline__ void put_32(T* p, T v) {
   if constexpr (kDev)
@@ -417,7 +429,8 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_write(const uint2* __rest
                                                              const uint32_t* __restrict__ hdr,
                                                              uint32_t* __restrict__ bnd_off,
                                                              uint32_t* __restrict__ item_off,
-                                                             uint32_t* __restrict__ order) {
+                                                             uint32_t* __restrict__ order,
+                                                             uint32_t* __restrict__ fbase) {
   __shared__ uint32_t red32[kPlanThreads / 64];
   __shared__ uint32_t cur[kLenClasses];
   const int t = (int)(blockIdx.x * kPlanThreads + threadIdx.x);
@@ -437,15 +450,106 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_write(const uint2* __rest
     bnd_off[t] = ob[0] + pre_s;
     item_off[t] = ob[1] + pre_i;
     order[atomicAdd(&cur[len_class(len)], 1u)] = (uint32_t)t;
+    fbase[t] = kNoSplit;  // k_split_plan marks the split tiles
+  }
+}
+
+// One workgroup: the split tiles and their forward segments.  A tile is split when its list
+// holds at least 2^(shift + kSplitLog) entries; its forward segments are F = 2^fshift entries,
+// fshift = max(shift + kFsegLog, round(log2 sqrt(48 len))).  Such tiles lead the order
+// (list-length classes, longest first); whole classes are split or not, so the choice does not
+// depend on the order inside a class: a class is split only if it lies wholly in the first
+// split_cap places of the order and every class up to it fits fseg_cap segments.
+// A split tile's place in the order carries kOrderSplit, so the forward kernels know it from the
+// word they read anyway.
+constexpr uint32_t kOrderSplit = 0x80000000u;
+__device__ void split_plan(const uint2* __restrict__ ranges, int T, uint32_t* __restrict__ order,
+                           uint32_t* __restrict__ hdr, uint32_t* __restrict__ fbase, uint32_t* __restrict__ split_tile,
+                           uint32_t* __restrict__ split_cnt, uint2* __restrict__ fitems, uint32_t fseg_cap,
+                           uint32_t split_cap) {
+  __shared__ uint32_t red[kPlanThreads / 64];
+  __shared__ uint32_t cls[kPlanThreads];
+  __shared__ uint32_t first_seg[kPlanThreads];
+  __shared__ uint32_t cend[kLenClasses];  // segments of the classes up to and including c
+  __shared__ uint32_t s_cut, s_nf;
+  const int i = threadIdx.x;
+  const uint32_t shift = hdr[kHdrShift];
+  const uint64_t min_len = (uint64_t)1 << (shift + kSplitLog);
+  const uint32_t window = min((uint32_t)T, min(split_cap, (uint32_t)kPlanThreads));
+  uint32_t tile = 0, c = 0, nseg = 0, fshift = 0;
+  if ((uint32_t)i < window) {
+    tile = order[i];
+    const uint2 rg = ranges[tile];
+    const uint32_t len = rg.y - rg.x;
+    if (len >= min_len) {
+      c = (uint32_t)len_class(len);
+      fshift = max(shift + (uint32_t)kFsegLog, (c - 1u + 7u) >> 1);  // c - 1 = floor(log2 len)
+      nseg = ((len - 1u) >> fshift) + 1u;
+    }
+  }
+  cls[i] = c;
+  if (i < kLenClasses) cend[i] = 0xFFFFFFFFu;
+  if (i == 0) {  // the class that continues past the window is not split
+    uint32_t cut = 0;
+    if (window < (uint32_t)T) {
+      const uint2 rg = ranges[order[window]];
+      if (rg.y - rg.x >= min_len) cut = (uint32_t)len_class(rg.y - rg.x);
+    }
+    s_cut = cut;
+    s_nf = 0;
+  }
+  const uint32_t excl = block_exscan_1024(nseg, red);  // (its barriers publish cls, cend, s_cut)
+  if (c != 0u && (i + 1 == kPlanThreads || cls[i + 1] != c)) cend[c] = excl + nseg;
+  __syncthreads();
+  const bool take = c != 0u && c > s_cut && cend[c] <= fseg_cap;  // a prefix of the order
+  const uint32_t ns = (uint32_t)__syncthreads_count(take);
+  if (take) {
+    fbase[tile] = excl | (fshift << 27);
+    order[i] = tile | kOrderSplit;
+    split_tile[i] = tile;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) split_cnt[4 * i + q] = 0u;
+    first_seg[i] = excl;
+    atomicMax(&s_nf, excl + nseg);
+  }
+  __syncthreads();
+  const uint32_t nf = s_nf;
+  // fitems[j] = (split tile, segment): the split tile is the last one whose first segment <= j
+  for (uint32_t j = (uint32_t)i; j < nf; j += kPlanThreads) {
+    uint32_t lo = 0, hi = ns - 1u;
+    while (lo < hi) {
+      const uint32_t mid = (lo + hi + 1u) >> 1;
+      if (first_seg[mid] <= j) lo = mid; else hi = mid - 1u;
+    }
+    fitems[j] = make_uint2(lo, j - first_seg[lo]);
+  }
+  if (i == 0) {
+    hdr[kHdrSplit] = ns;
+    hdr[kHdrFsegs] = nf;
+    hdr[kHdrLongNext] = 0u;
   }
 }
 
 // The item list: one wave per tile writes the tile's items (tile, 0), (tile, 1), ...; for the
-// fused step (empty), the marker of a not yet published item instead.
+// fused step (empty), the marker of a not yet published item instead.  Block 0 first plans the
+// split tiles (split_plan).
 constexpr uint32_t kNoTile = 0xFFFFFFFFu;
-__global__ __launch_bounds__(kBlock) void k_seg_items(int T, const uint32_t* __restrict__ item_off,
-                                                      uint2* __restrict__ items, bool empty) {
-  const int t = (int)(blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6));
+struct SplitPlanArgs {
+  const uint2* ranges;
+  uint32_t* order;
+  uint32_t* hdr;
+  uint32_t* fbase;
+  uint32_t* split_tile;
+  uint32_t* split_cnt;
+  uint2* fitems;
+  uint32_t fseg_cap, split_cap;
+};
+__global__ __launch_bounds__(kPlanThreads) void k_seg_items(int T, const uint32_t* __restrict__ item_off,
+                                                            uint2* __restrict__ items, bool empty, SplitPlanArgs sp) {
+  if (blockIdx.x == 0)
+    split_plan(sp.ranges, T, sp.order, sp.hdr, sp.fbase, sp.split_tile, sp.split_cnt, sp.fitems, sp.fseg_cap,
+               sp.split_cap);
+  const int t = (int)(blockIdx.x * (kPlanThreads / 64) + (threadIdx.x >> 6));
   if (t >= T) return;
   const uint32_t o = item_off[t], k = item_off[t + 1] - o;
   for (uint32_t j = threadIdx.x & 63; j < k; j += 64) items[o + j] = make_uint2(empty ? kNoTile : (uint32_t)t, j);
@@ -477,6 +581,7 @@ struct FwdArgs {
   uint2* masks;
   uint64_t mask_cap;
   const uint32_t* order;
+  const uint32_t* fbase;  // kNoSplit, or the split tile's first forward segment
   // the fused step only: the L1 loss against the target image, per pixel
   const float* target;
   float* dLdI;
@@ -484,153 +589,475 @@ struct FwdArgs {
   float inv_n;       // 1 / (3 W H)
 };
 
-// One tile by the workgroup's four quadrant waves (kStep: the fused step, which also takes the
-// pixel's L1 loss and gradient and hands its state to other workgroups at device scope).
-template <bool kStep>
-__device__ void forward_tile(const FwdArgs& a, uint32_t shift, int tile, Chunk* stg) {
-  const int W = a.W, H = a.H, TX = a.TX;
+// A pixel's state along its walk.  Positions are 1-based and relative to the tile's list.
+struct WalkState {
+  float Tr, c0, c1, c2;
+  uint32_t first;     // first composited position (recorded only when asked for)
+  uint32_t last;      // last composited position, 0 if none
+  uint32_t examined;  // the stop's position; unchanged if the walk does not stop
+  uint32_t blended, evaluated;
+  bool done;          // takes no part in the walk
+};
+
+// A quadrant wave's walk over the entries [rs, re) of tile list [start, start + len) (rs a
+// multiple of 64) for the lane's pixel, from the state in s, stopping a pixel when T would fall
+// below 1e-4.  kWrite: each walked chunk's composited mask is stored (at chunk cbase + rel / 64)
+// and, with long_list, the state at every segment boundary rel in [rs, re), rel > 0 (at st +
+// (rel / SEG - 1) slots).  kFirst: records the first composited position.
+template <bool kDev, bool kWrite, bool kFirst>
+__device__ __forceinline__ void walk_entries(const FwdArgs& a, uint32_t shift, uint32_t start, uint32_t rs,
+                                             uint32_t re, bool long_list, float4* st, uint64_t cbase, int pix,
+                                             int xq, int yq, float pxc, float pyc, Chunk& S, WalkState& s) {
   const int64_t n = a.n;
   const float4* __restrict__ splat = a.splat;
   const uint32_t* __restrict__ vals = a.vals;
   uint2* __restrict__ masks = a.masks;
   const uint64_t mask_cap = a.mask_cap;
+  const int lane = threadIdx.x & 63;
+  const int lx = lane & 7, ly = lane >> 3;
+  const uint32_t end = start + re;
+  const uint32_t seg_mask = (1u << shift) - 1u;
+  float Tr = s.Tr, c0 = s.c0, c1 = s.c1, c2 = s.c2;
+  uint32_t first = s.first, last = s.last, examined = s.examined, blended = s.blended, evaluated = s.evaluated;
+  bool done = s.done;
+
+  uint32_t gnext = load_gid(vals, start + rs + lane, end, start);
+  Raw cur = load_raw(splat, gnext, n);
+  gnext = load_gid(vals, start + rs + kChunk + lane, end, start);
+  // The first chunk has landed before the loop starts; each pass waits for the next chunk's
+  // loads only at its end.  A chunk's composited mask is stored at the start of the next
+  // pass, so that pass's work covers the store's latency.
+  settle(cur);
+  unsigned long long pend = 0ull;
+  uint64_t pend_mc = ~0ull;
+  for (uint32_t b0 = start + rs; b0 < end; b0 += kChunk) {
+    if (__ballot(!done) == 0ull) break;
+    if constexpr (kWrite) {
+      if (pend_mc < mask_cap)
+        put_u2<kDev>(masks + pend_mc * (kTile * kTile) + pix, make_uint2((uint32_t)pend, (uint32_t)(pend >> 32)));
+    }
+    const Raw nxt = load_raw(splat, gnext, n);  // next chunk in flight
+    gnext = load_gid(vals, b0 + 2 * kChunk + lane, end, start);
+    const uint32_t rel = b0 - start;
+    if constexpr (kWrite) {
+      if (long_list && rel != 0u && (rel & seg_mask) == 0u)  // state at segment boundary rel
+        put_f4<kDev>(st + (size_t)((rel >> shift) - 1u) * (kTile * kTile), make_float4(Tr, c0, c1, c2));
+    }
+    put(S, lane, cur);
+    const Box bx = alpha_box(cur.uv.x, cur.uv.y, cur.abco.x, cur.abco.y, cur.abco.z, opacity_of(cur, n), xq, yq);
+    // every lane takes part in the ballots: lane e holds record e's box
+    unsigned long long m = lane_mask(bx, lx, ly);
+    if (done) m = 0ull;
+    evaluated += (uint32_t)__popcll(m);
+    wave_sync_lds();
+    const uint32_t base = rel + 1u;  // 1-based position of slot 0
+    unsigned long long cm = 0ull;    // the chunk's entries composited at this pixel
+    while (m) {  // this lane's records, in list order
+      const int e = lowest_bit(m);
+      m &= m - 1ull;
+      const float4 g = S.geo[e];
+      const float4 cl = S.col[e];
+      const float bb = S.b[e];
+      const float dx = pxc - g.x, dy = pyc - g.y;
+      const float power = eval_power(g.z, g.w, cl.x, dx, dy);
+      const float alpha = fminf(kAlphaMax, eval_oG(cl.y, power));
+      if (power <= 0.0f && alpha >= kAlphaMin) {
+        const float Tn = Tr * (1.0f - alpha);
+        const uint32_t pos = base + (uint32_t)e;
+        if (Tn < kTMin) {
+          done = true;
+          examined = pos;
+          evaluated -= (uint32_t)__popcll(m);  // the entries behind the stop are not evaluated
+          m = 0ull;
+        } else {
+          const float wt = alpha * Tr;
+          c0 += cl.z * wt;
+          c1 += cl.w * wt;
+          c2 += bb * wt;
+          Tr = Tn;
+          if constexpr (kFirst) first = first ? first : pos;
+          last = pos;
+          ++blended;
+          cm |= 1ull << e;
+        }
+      }
+    }
+    pend = cm;
+    pend_mc = cbase + rel / kChunk;
+    wave_sync_lds();  // this chunk's reads finish before the next chunk is staged
+    cur = nxt;
+  }
+  if constexpr (kWrite) {
+    if (pend_mc < mask_cap)
+      put_u2<kDev>(masks + pend_mc * (kTile * kTile) + pix, make_uint2((uint32_t)pend, (uint32_t)(pend >> 32)));
+  }
+  s.Tr = Tr;
+  s.c0 = c0;
+  s.c1 = c1;
+  s.c2 = c2;
+  s.first = first;
+  s.last = last;
+  s.examined = examined;
+  s.blended = blended;
+  s.evaluated = evaluated;
+  s.done = done;
+}
+
+// The forward's outputs at pixel p (inside the image); returns the pixel's colour.
+template <bool kDev>
+__device__ __forceinline__ float3 store_pixel(const FwdArgs& a, int64_t p, const WalkState& s) {
+  const float i0 = s.c0 + s.Tr * a.bg0, i1 = s.c1 + s.Tr * a.bg1, i2 = s.c2 + s.Tr * a.bg2;
+  a.image[3 * p + 0] = i0;
+  a.image[3 * p + 1] = i1;
+  a.image[3 * p + 2] = i2;
+  put_32<kDev>(a.T_final + p, s.Tr);
+  put_32<kDev>(a.last_contrib + p, s.last);
+  if (a.n_examined) a.n_examined[p] = s.examined;
+  return make_float3(i0, i1, i2);
+}
+
+// Adds the workgroup's per-pixel counts (examined, walked = last, composited, evaluated) to
+// blend_count; every thread of the workgroup calls it.
+__device__ void add_blend_stats(unsigned long long* bc, uint32_t examined, uint32_t last, uint32_t blended,
+                                uint32_t evaluated) {
+  if (!bc) return;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  unsigned long long ex = examined, lc = last, bl = blended, ev = evaluated;
+  for (int o = 32; o > 0; o >>= 1) {
+    ex += __shfl_xor(ex, o, 64);
+    lc += __shfl_xor(lc, o, 64);
+    bl += __shfl_xor(bl, o, 64);
+    ev += __shfl_xor(ev, o, 64);
+  }
+  // one atomic per counter and workgroup: same-address atomics from every wave of the image
+  // serialise and would cost more than the blending of a light view
+  __shared__ unsigned long long part[4][4];
+  if (lane == 0) {
+    part[0][w] = ex;
+    part[1][w] = lc;
+    part[2][w] = bl;
+    part[3][w] = ev;
+  }
+  __syncthreads();
+  if (tid < 4) {
+    const unsigned long long x = (part[tid][0] + part[tid][1]) + (part[tid][2] + part[tid][3]);
+    if (x != 0ull) atomicAdd(bc + tid, x);
+  }
+  __syncthreads();  // part is read before a later call overwrites it
+}
+
+// L1 loss at pixel p of image colour i: dL/dI = sign(I - target) / (3 W H), sign(0) = 0;
+// returns |I - target| summed over the channels.
+__device__ __forceinline__ float l1_pixel(const FwdArgs& a, int64_t p, float3 i) {
+  const float d0 = i.x - a.target[3 * p + 0], d1 = i.y - a.target[3 * p + 1], d2 = i.z - a.target[3 * p + 2];
+  const float q = a.inv_n;
+  put_32<true>(a.dLdI + 3 * p + 0, d0 > 0.f ? q : (d0 < 0.f ? -q : 0.f));
+  put_32<true>(a.dLdI + 3 * p + 1, d1 > 0.f ? q : (d1 < 0.f ? -q : 0.f));
+  put_32<true>(a.dLdI + 3 * p + 2, d2 > 0.f ? q : (d2 < 0.f ? -q : 0.f));
+  return (fabsf(d0) + fabsf(d1)) + fabsf(d2);
+}
+
+// the tile's loss_part from each thread's pixel sum; every thread calls it
+__device__ void store_loss_part(const FwdArgs& a, int tile, float l1) {
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  for (int o = 32; o > 0; o >>= 1) l1 += __shfl_xor(l1, o, 64);
+  __shared__ float lpart[4];
+  if (lane == 0) lpart[w] = l1;
+  __syncthreads();
+  if (tid == 0) a.loss_part[tile] = (lpart[0] + lpart[1]) + (lpart[2] + lpart[3]);
+}
+
+// One tile by the workgroup's four quadrant waves (kStep: the fused step, which also takes the
+// pixel's L1 loss and gradient and hands its state to other workgroups at device scope).  A
+// split tile's forward ran before (k_long_forward): the fused step takes only its loss.
+template <bool kStep>
+__device__ void forward_tile(const FwdArgs& a, uint32_t shift, int tile, bool split, Chunk* stg) {
+  const int W = a.W, H = a.H, TX = a.TX;
   const int tx = tile % TX, ty = tile / TX;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  Chunk& S = stg[w];
   const int lx = lane & 7, ly = lane >> 3;
   const int xq = tx * kTile + (w & 1) * 8, yq = ty * kTile + (w >> 1) * 8;  // quadrant origin
   const int px = xq + lx, py = yq + ly;
   const bool inside = px < W && py < H;
-  const float pxc = (float)px + 0.5f, pyc = (float)py + 0.5f;
   const uint2 rg = a.ranges[tile];
-  const uint32_t start = rg.x, end = rg.y, len = end - start;
-  const uint32_t seg_mask = (1u << shift) - 1u;
-  const bool long_list = len > seg_mask + 1u;
+  const uint32_t start = rg.x, len = rg.y - rg.x;
+  const bool long_list = len > (1u << shift);
   const int pix = tile_pixel(w, lx, ly);
   float4* const st = a.slots + (size_t)(long_list ? a.bnd_off[tile] : 0u) * (kTile * kTile) + pix;
   const uint64_t cbase = (uint64_t)(start / kChunk) + (uint64_t)tile;  // the tile's first mask chunk
 
-  float Tr = 1.0f, c0 = 0.f, c1 = 0.f, c2 = 0.f;
-  uint32_t last = 0, examined = len, blended = 0;
-  uint32_t evaluated = 0;  // (pixel, entry) pairs whose alpha is evaluated: the mask bits walked
-  bool done = !inside;
-
-  if (len > 0) {
-    uint32_t gnext = load_gid(vals, start + lane, end, start);
-    Raw cur = load_raw(splat, gnext, n);
-    gnext = load_gid(vals, start + kChunk + lane, end, start);
-    // The first chunk has landed before the loop starts; each pass waits for the next chunk's
-    // loads only at its end.  A chunk's composited mask is stored at the start of the next
-    // pass, so that pass's work covers the store's latency.
-    settle(cur);
-    unsigned long long pend = 0ull;
-    uint64_t pend_mc = ~0ull;
-    for (uint32_t b0 = start; b0 < end; b0 += kChunk) {
-      if (__ballot(!done) == 0ull) break;
-      if (pend_mc < mask_cap)
-        put_u2<kStep>(masks + pend_mc * (kTile * kTile) + pix, make_uint2((uint32_t)pend, (uint32_t)(pend >> 32)));
-      const Raw nxt = load_raw(splat, gnext, n);  // next chunk in flight
-      gnext = load_gid(vals, b0 + 2 * kChunk + lane, end, start);
-      const uint32_t rel = b0 - start;
-      if (long_list && rel != 0u && (rel & seg_mask) == 0u)  // state at segment boundary rel
-        put_f4<kStep>(st + (size_t)((rel >> shift) - 1u) * (kTile * kTile), make_float4(Tr, c0, c1, c2));
-      put(S, lane, cur);
-      const Box bx = alpha_box(cur.uv.x, cur.uv.y, cur.abco.x, cur.abco.y, cur.abco.z, opacity_of(cur, n), xq, yq);
-      // every lane takes part in the ballots: lane e holds record e's box
-      unsigned long long m = lane_mask(bx, lx, ly);
-      if (done) m = 0ull;
-      evaluated += (uint32_t)__popcll(m);
-      wave_sync_lds();
-      const uint32_t base = rel + 1u;  // 1-based position of slot 0
-      unsigned long long cm = 0ull;    // the chunk's entries composited at this pixel
-      while (m) {  // this lane's records, in list order
-        const int e = lowest_bit(m);
-        m &= m - 1ull;
-        const float4 g = S.geo[e];
-        const float4 cl = S.col[e];
-        const float bb = S.b[e];
-        const float dx = pxc - g.x, dy = pyc - g.y;
-        const float power = eval_power(g.z, g.w, cl.x, dx, dy);
-        const float alpha = fminf(kAlphaMax, eval_oG(cl.y, power));
-        if (power <= 0.0f && alpha >= kAlphaMin) {
-          const float Tn = Tr * (1.0f - alpha);
-          const uint32_t pos = base + (uint32_t)e;
-          if (Tn < kTMin) {
-            done = true;
-            examined = pos;
-            evaluated -= (uint32_t)__popcll(m);  // the entries behind the stop are not evaluated
-            m = 0ull;
-          } else {
-            const float wt = alpha * Tr;
-            c0 += cl.z * wt;
-            c1 += cl.w * wt;
-            c2 += bb * wt;
-            Tr = Tn;
-            last = pos;
-            ++blended;
-            cm |= 1ull << e;
-          }
-        }
-      }
-      pend = cm;
-      pend_mc = cbase + rel / kChunk;
-      wave_sync_lds();  // this chunk's reads finish before the next chunk is staged
-      cur = nxt;
-    }
-    if (pend_mc < mask_cap)
-      put_u2<kStep>(masks + pend_mc * (kTile * kTile) + pix, make_uint2((uint32_t)pend, (uint32_t)(pend >> 32)));
+  WalkState s{1.0f, 0.f, 0.f, 0.f, 0u, 0u, len, 0u, 0u, !inside};
+  if (len > 0 && !split) {
+    walk_entries<kStep, true, false>(a, shift, start, 0u, len, long_list, st, cbase, pix, xq, yq, (float)px + 0.5f,
+                                     (float)py + 0.5f, stg[w], s);
     if (long_list)  // final state
-      put_f4<kStep>(st + (size_t)((len - 1u) >> shift) * (kTile * kTile), make_float4(Tr, c0, c1, c2));
+      put_f4<kStep>(st + (size_t)((len - 1u) >> shift) * (kTile * kTile), make_float4(s.Tr, s.c0, s.c1, s.c2));
   }
 
   float l1 = 0.f;  // the pixel's sum of |image - target| (fused step)
   if (inside) {
     const int64_t p = (int64_t)py * W + px;
-    const float i0 = c0 + Tr * a.bg0, i1 = c1 + Tr * a.bg1, i2 = c2 + Tr * a.bg2;
-    a.image[3 * p + 0] = i0;
-    a.image[3 * p + 1] = i1;
-    a.image[3 * p + 2] = i2;
-    put_32<kStep>(a.T_final + p, Tr);
-    put_32<kStep>(a.last_contrib + p, last);
-    if (a.n_examined) a.n_examined[p] = examined;
-    if constexpr (kStep) {  // L1: dL/dI = sign(I - target) / (3 W H), sign(0) = 0
-      const float d0 = i0 - a.target[3 * p + 0], d1 = i1 - a.target[3 * p + 1], d2 = i2 - a.target[3 * p + 2];
-      const float q = a.inv_n;
-      put_32<true>(a.dLdI + 3 * p + 0, d0 > 0.f ? q : (d0 < 0.f ? -q : 0.f));
-      put_32<true>(a.dLdI + 3 * p + 1, d1 > 0.f ? q : (d1 < 0.f ? -q : 0.f));
-      put_32<true>(a.dLdI + 3 * p + 2, d2 > 0.f ? q : (d2 < 0.f ? -q : 0.f));
-      l1 = (fabsf(d0) + fabsf(d1)) + fabsf(d2);
+    const float3 i = split ? make_float3(a.image[3 * p + 0], a.image[3 * p + 1], a.image[3 * p + 2])
+                           : store_pixel<kStep>(a, p, s);
+    if constexpr (kStep) l1 = l1_pixel(a, p, i);
+  }
+  if constexpr (kStep) store_loss_part(a, tile, l1);
+  add_blend_stats(a.blend_count, inside && !split ? s.examined : 0u, s.last, s.blended, s.evaluated);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Forward of the split tiles: the longest lists, whose one sequential walk per pixel would
+// outlast the rest of the image while only a few of their pixels are still going after the first
+// thousands of entries.  Four kinds of work items run in one persistent kernel before the other
+// tiles' forward:
+//   first (tile)     the first 2^(shift + kPhase1Log) entries, walked as any list is: a pixel that
+//                    stops there is finished; the others (the survivors) go on in segments.
+//   walk (tile, f)   the survivors walk forward segment f from T = 1, C = 0: their composited
+//                    entries in f do not depend on the T they enter with, so the walk gives the
+//                    segment's product P of (1 - alpha), its colour sum C, and the composited
+//                    masks.  A pixel whose T falls below 1e-4 inside the walk certainly stops
+//                    there or earlier, so the walk stops it (bit 31 of the composited count).
+//   combine (tile)   per survivor, in segment order: (T, C) in front of segment f is (T_in,
+//                    C_in); the pixel stops in f when the walk stopped or T_in P < 1e-4; else
+//                    C_in += T_in C, T_in *= P.  A survivor that never stops is finished here.
+//   redo (tile, f)   the survivors that stop in f walk it again from (T_in, C_in), exactly as
+//                    the sequential walk does, which places the stop.
+// A tile's segments are F = 2^fshift entries, F about sqrt(48 len): a walk costs about F / 64
+// chunk steps and the combine about len / (4 F) dependent loads, so this balances the two.
+// Each item waits only for items of its tile that come before it in the one counter's order
+// (first, walks, combines, redos), i.e. for items that running workgroups already hold and that
+// wait for nothing later.  The waits are bounded all the same (the stall flag).
+// The walks' boundary states are relative to their segment's start: the backward converts
+// them with fin, (T, C) = (T_in T_b, C_in + T_in C_b).  The composited masks past a pixel's
+// stop are not cleared: the backward masks each pixel's bits by its last_contrib.
+// ---------------------------------------------------------------------------------------------
+struct LongArgs {
+  const uint32_t* split_tile;
+  uint32_t* split_cnt;
+  const uint2* fitems;
+  float4* fsum;
+  uint4* fstat;
+  float4* fin;
+  uint4* pstate;
+};
+
+constexpr uint32_t kSpinLimit = 1u << 20;  // about a second of polling
+constexpr uint32_t kPixDone = 0xFFFFFFFFu;   // pstate: finished in the first part
+constexpr uint32_t kPixAlive = 0xFFFFFFFEu;  // pstate: a survivor (until the combine places its stop)
+
+// Waits (thread 0) until *p >= v; gives up after kSpinLimit polls and flags the stall.
+__device__ void wait_for(const uint32_t* p, uint32_t v, uint32_t* hdr) {
+  for (uint32_t spin = 0;; ++spin) {
+    if (get_32<true>(p) >= v) return;
+    if (spin == kSpinLimit) {
+      atomicOr(hdr + kHdrFlags, kFlagStall);
+      return;
+    }
+    __builtin_amdgcn_s_sleep(4);
+  }
+}
+
+// A split tile's geometry and its quadrant wave's pixel.
+struct SplitTile {
+  int tile, xq, yq, px, py, pix;
+  bool inside;
+  uint32_t start, len, fb, fshift, nseg, f0;
+};
+
+__device__ __forceinline__ SplitTile split_tile_of(const FwdArgs& a, const LongArgs& L, uint32_t shift, uint32_t c) {
+  SplitTile t;
+  t.tile = (int)L.split_tile[c];
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int lx = lane & 7, ly = lane >> 3;
+  t.xq = (t.tile % a.TX) * kTile + (w & 1) * 8;
+  t.yq = (t.tile / a.TX) * kTile + (w >> 1) * 8;
+  t.px = t.xq + lx;
+  t.py = t.yq + ly;
+  t.pix = tile_pixel(w, lx, ly);
+  t.inside = t.px < a.W && t.py < a.H;
+  const uint2 rg = a.ranges[t.tile];
+  t.start = rg.x;
+  t.len = rg.y - rg.x;
+  const uint32_t fbv = a.fbase[t.tile];
+  t.fb = fbv & kFbaseMask;
+  t.fshift = fbv >> 27;
+  t.nseg = ((t.len - 1u) >> t.fshift) + 1u;
+  t.f0 = (((1u << (shift + kPhase1Log)) - 1u) >> t.fshift) + 1u;  // segments in the first part
+  return t;
+}
+
+// the forward outputs and the final state slot of a finished pixel of a split tile
+__device__ __forceinline__ void finish_split_pixel(const FwdArgs& a, uint32_t shift, const SplitTile& t,
+                                                   const WalkState& s) {
+  store_pixel<false>(a, (int64_t)t.py * a.W + t.px, s);
+  put_f4<false>(a.slots + ((size_t)a.bnd_off[t.tile] + ((t.len - 1u) >> shift)) * (kTile * kTile) + t.pix,
+                make_float4(s.Tr, s.c0, s.c1, s.c2));
+}
+
+__device__ void long_first(const FwdArgs& a, const LongArgs& L, uint32_t shift, uint32_t c, Chunk* stg) {
+  const SplitTile t = split_tile_of(a, L, shift, c);
+  float4* const st = a.slots + (size_t)a.bnd_off[t.tile] * (kTile * kTile) + t.pix;
+  const uint64_t cbase = (uint64_t)(t.start / kChunk) + (uint64_t)t.tile;
+  WalkState s{1.0f, 0.f, 0.f, 0.f, 0u, 0u, 0u, 0u, 0u, !t.inside};
+  walk_entries<false, true, false>(a, shift, t.start, 0u, t.f0 << t.fshift, true, st, cbase, t.pix, t.xq, t.yq,
+                                   (float)t.px + 0.5f, (float)t.py + 0.5f, stg[threadIdx.x >> 6], s);
+  const bool done = t.inside && s.examined != 0u;
+  if (done) finish_split_pixel(a, shift, t, s);
+  if (t.inside) {
+    put_u4<true>(L.pstate + (size_t)c * (kTile * kTile) + t.pix,
+                 make_uint4(done ? kPixDone : kPixAlive, s.last, s.blended, s.evaluated));
+    if (!done) put_f4<true>(L.fin + ((size_t)t.fb + t.f0) * (kTile * kTile) + t.pix, make_float4(s.Tr, s.c0, s.c1, s.c2));
+  }
+  add_blend_stats(a.blend_count, done ? s.examined : 0u, done ? s.last : 0u, done ? s.blended : 0u,
+                  done ? s.evaluated : 0u);
+  drain_memory();
+  __syncthreads();
+  if (threadIdx.x == 0) put_32<true>(L.split_cnt + 4 * c, 1u);
+  // A barrier between this thread-0 region and the next item's: with the two adjacent, the
+  // compiler merges them into a loop that only thread 0 can leave, and the other lanes take
+  // the same item again for ever.
+  __syncthreads();
+}
+
+__device__ void long_walk(const FwdArgs& a, const LongArgs& L, uint32_t shift, uint2 it, Chunk* stg, uint32_t* hdr) {
+  const uint32_t c = it.x, f = it.y;
+  const SplitTile t = split_tile_of(a, L, shift, c);
+  if (f < t.f0) return;  // (workgroup-uniform) the first part's segments
+  if (threadIdx.x == 0) wait_for(L.split_cnt + 4 * c, 1u, hdr);
+  __syncthreads();
+  const bool alive = t.inside && get_32<true>(&L.pstate[(size_t)c * (kTile * kTile) + t.pix].x) == kPixAlive;
+  if (__ballot(alive) != 0ull) {  // (wave-uniform) a wave without survivors has nothing to walk
+    float4* const st = a.slots + (size_t)a.bnd_off[t.tile] * (kTile * kTile) + t.pix;
+    const uint64_t cbase = (uint64_t)(t.start / kChunk) + (uint64_t)t.tile;
+    const uint32_t fs = f << t.fshift, fe = min(t.len, fs + (1u << t.fshift));
+    WalkState s{1.0f, 0.f, 0.f, 0.f, 0u, 0u, 0u, 0u, 0u, !alive};
+    walk_entries<false, true, true>(a, shift, t.start, fs, fe, true, st, cbase, t.pix, t.xq, t.yq,
+                                    (float)t.px + 0.5f, (float)t.py + 0.5f, stg[threadIdx.x >> 6], s);
+    const size_t o = ((size_t)t.fb + f) * (kTile * kTile) + t.pix;
+    put_f4<true>(L.fsum + o, make_float4(s.Tr, s.c0, s.c1, s.c2));
+    put_u4<true>(L.fstat + o, make_uint4(s.first, s.last, s.blended | (s.examined ? 0x80000000u : 0u), s.evaluated));
+  }
+  drain_memory();
+  __syncthreads();
+  if (threadIdx.x == 0) atomicAdd(L.split_cnt + 4 * c + 1, 1u);
+  __syncthreads();  // (as at the end of long_first)
+}
+
+constexpr uint32_t kCombineBatch = 4;  // forward segments whose sums one pass loads at once
+
+__device__ void long_combine(const FwdArgs& a, const LongArgs& L, uint32_t shift, uint32_t c, uint32_t* hdr) {
+  const SplitTile t = split_tile_of(a, L, shift, c);
+  if (threadIdx.x == 0) wait_for(L.split_cnt + 4 * c + 1, t.nseg - t.f0, hdr);  // the walks past the first part
+  __syncthreads();
+  const uint4 ps = t.inside ? get_u4<true>(L.pstate + (size_t)c * (kTile * kTile) + t.pix) : make_uint4(kPixDone, 0u, 0u, 0u);
+  const bool alive = ps.x == kPixAlive;
+  float4 fi = make_float4(1.f, 0.f, 0.f, 0.f);
+  if (alive) fi = get_f4<true>(L.fin + ((size_t)t.fb + t.f0) * (kTile * kTile) + t.pix);
+  WalkState s{fi.x, fi.y, fi.z, fi.w, 0u, ps.y, t.len, ps.z, ps.w, !alive};
+  uint32_t stop = t.nseg;
+  for (uint32_t f0 = t.f0; __ballot(!s.done) != 0ull; f0 += kCombineBatch) {
+    float4 P[kCombineBatch];
+    uint4 Q[kCombineBatch];
+#pragma unroll
+    for (uint32_t j = 0; j < kCombineBatch; ++j) {  // loads clamped into the list, all in flight at once
+      const size_t o = ((size_t)t.fb + min(f0 + j, t.nseg - 1u)) * (kTile * kTile) + t.pix;
+      P[j] = get_f4<true>(L.fsum + o);
+      Q[j] = get_u4<true>(L.fstat + o);
+    }
+#pragma unroll
+    for (uint32_t j = 0; j < kCombineBatch; ++j) {
+      const uint32_t f = f0 + j;
+      if (!s.done && f >= t.nseg) s.done = true;  // walked the whole list
+      if (s.done) continue;
+      put_f4<true>(L.fin + ((size_t)t.fb + f) * (kTile * kTile) + t.pix, make_float4(s.Tr, s.c0, s.c1, s.c2));
+      if ((Q[j].z >> 31) || s.Tr * P[j].x < kTMin) {  // the stop lies in segment f
+        stop = f;
+        s.done = true;
+        continue;
+      }
+      s.c0 += s.Tr * P[j].y;
+      s.c1 += s.Tr * P[j].z;
+      s.c2 += s.Tr * P[j].w;
+      s.Tr *= P[j].x;
+      s.last = Q[j].y ? Q[j].y : s.last;
+      s.blended += Q[j].z;
+      s.evaluated += Q[j].w;
     }
   }
-  if constexpr (kStep) {
-    for (int o = 32; o > 0; o >>= 1) l1 += __shfl_xor(l1, o, 64);
-    __shared__ float lpart[4];
-    if (lane == 0) lpart[w] = l1;
-    __syncthreads();
-    if (tid == 0) a.loss_part[tile] = (lpart[0] + lpart[1]) + (lpart[2] + lpart[3]);
+  const bool finished = alive && stop == t.nseg;  // never stops: its outputs are complete
+  if (alive) {
+    put_u4<true>(L.pstate + (size_t)c * (kTile * kTile) + t.pix, make_uint4(stop, s.last, s.blended, s.evaluated));
+    if (finished) finish_split_pixel(a, shift, t, s);
   }
-  if (a.blend_count) {
-    unsigned long long ex = inside ? examined : 0u, lc = last, bl = blended, ev = evaluated;
-    for (int o = 32; o > 0; o >>= 1) {
-      ex += __shfl_xor(ex, o, 64);
-      lc += __shfl_xor(lc, o, 64);
-      bl += __shfl_xor(bl, o, 64);
-      ev += __shfl_xor(ev, o, 64);
+  add_blend_stats(a.blend_count, finished ? s.examined : 0u, finished ? s.last : 0u, finished ? s.blended : 0u,
+                  finished ? s.evaluated : 0u);
+  drain_memory();
+  __syncthreads();
+  if (threadIdx.x == 0) put_32<true>(L.split_cnt + 4 * c + 2, 1u);
+  __syncthreads();  // (as at the end of long_first)
+}
+
+__device__ void long_redo(const FwdArgs& a, const LongArgs& L, uint32_t shift, uint2 it, Chunk* stg,
+                          uint32_t* hdr) {
+  const uint32_t c = it.x, f = it.y;
+  const SplitTile t = split_tile_of(a, L, shift, c);
+  if (f < t.f0) return;  // (workgroup-uniform) the first part's stops are exact already
+  if (threadIdx.x == 0) wait_for(L.split_cnt + 4 * c + 2, 1u, hdr);
+  __syncthreads();
+  const bool mine = t.inside && get_32<true>(&L.pstate[(size_t)c * (kTile * kTile) + t.pix].x) == f;  // stops in f
+  if (!__syncthreads_or(mine)) return;
+  const float4 fi = mine ? get_f4<true>(L.fin + ((size_t)t.fb + f) * (kTile * kTile) + t.pix) : make_float4(1.f, 0.f, 0.f, 0.f);
+  WalkState s{fi.x, fi.y, fi.z, fi.w, 0u, 0u, 0u, 0u, 0u, !mine};
+  const uint32_t fs = f << t.fshift, fe = min(t.len, fs + (1u << t.fshift));
+  walk_entries<false, false, false>(a, shift, t.start, fs, fe, true, nullptr, 0, t.pix, t.xq, t.yq,
+                                    (float)t.px + 0.5f, (float)t.py + 0.5f, stg[threadIdx.x >> 6], s);
+  if (mine) {
+    const uint4 ps = get_u4<true>(L.pstate + (size_t)c * (kTile * kTile) + t.pix);  // (reloaded: fewer registers)
+    if (s.examined == 0u) {
+      // No stop inside the segment: the combine's product fell below 1e-4 only by rounding,
+      // and T is now within rounding of 1e-4, so the next composited entry (alpha >= 1/255)
+      // stops the pixel -- the first composited position of a later segment, else none.
+      s.examined = t.len;
+      for (uint32_t g = f + 1u; g < t.nseg; ++g) {
+        const uint32_t q = get_u4<true>(L.fstat + ((size_t)t.fb + g) * (kTile * kTile) + t.pix).x;
+        if (q) {
+          s.examined = q;
+          break;
+        }
+      }
     }
-    // one atomic per counter and non-empty tile: same-address atomics from every wave of
-    // the image serialise and would cost more than the blending of a light view
-    __shared__ unsigned long long part[4][4];
-    if (lane == 0) {
-      part[0][w] = ex;
-      part[1][w] = lc;
-      part[2][w] = bl;
-      part[3][w] = ev;
-    }
+    s.last = s.last ? s.last : ps.y;
+    s.blended += ps.z;
+    s.evaluated += ps.w;
+    finish_split_pixel(a, shift, t, s);
+  }
+  add_blend_stats(a.blend_count, mine ? s.examined : 0u, mine ? s.last : 0u, mine ? s.blended : 0u,
+                  mine ? s.evaluated : 0u);
+}
+
+// Persistent: with S split tiles and F forward segments, items 0 .. S-1 walk the first parts,
+// S .. S+F-1 the segments (in fitems' order), S+F .. 2S+F-1 combine, 2S+F .. 2S+2F-1 redo.
+// (Capped at six waves per SIMD, as the other forward kernels are, it spills; it runs at four.)
+__global__ __launch_bounds__(kBlock) void k_long_forward(FwdArgs a, LongArgs L, uint32_t* __restrict__ hdr) {
+  __shared__ Chunk stg[4];
+  __shared__ uint32_t s_q;
+  const uint32_t shift = hdr[kHdrShift], ns = hdr[kHdrSplit], nf = hdr[kHdrFsegs];
+  if (ns == 0u) return;
+  for (;;) {
+    if (threadIdx.x == 0) s_q = atomicAdd(hdr + kHdrLongNext, 1u);
     __syncthreads();
-    if (tid < 4) {
-      const unsigned long long x = (part[tid][0] + part[tid][1]) + (part[tid][2] + part[tid][3]);
-      if (x != 0ull) atomicAdd(a.blend_count + tid, x);
-    }
+    const uint32_t q = s_q;
+    __syncthreads();  // every wave has read s_q before it is overwritten
+    if (q < ns)
+      long_first(a, L, shift, q, stg);
+    else if (q < ns + nf)
+      long_walk(a, L, shift, L.fitems[q - ns], stg, hdr);
+    else if (q < 2 * ns + nf)
+      long_combine(a, L, shift, q - ns - nf, hdr);
+    else if (q < 2 * ns + 2 * nf)
+      long_redo(a, L, shift, L.fitems[q - 2 * ns - nf], stg, hdr);
+    else
+      break;
   }
 }
 
@@ -663,6 +1090,8 @@ struct BwdArgs {
   const uint32_t* goff_blk;
   float* staging;
   uint64_t staging_cap;
+  const uint32_t* fbase;  // split tiles: their first forward segment (else kNoSplit)
+  const float4* fin;      // split tiles: (T, C) in front of each forward segment, per pixel
 };
 
 // LDS of a blending workgroup
@@ -704,6 +1133,8 @@ __device__ void backward_item(const BwdArgs& a, uint32_t shift, uint2 it, BlendS
   const uint2 rg = a.ranges[tile];
   const uint32_t start = rg.x, end = rg.y, len = rg.y - rg.x;
   const uint64_t cbase = (uint64_t)(start / kChunk) + (uint64_t)tile;  // the tile's first mask chunk
+  const uint32_t fbv = a.fbase[tile];
+  const bool split = fbv != kNoSplit;  // (a split tile's masks go on past each pixel's stop)
 
   // Tr: the transmittance behind the current entry; Sg: the colour behind it (normalised by
   // Tr) dotted with dL/dI -- the gradient needs that colour only through this product
@@ -730,7 +1161,13 @@ __device__ void backward_item(const BwdArgs& a, uint32_t shift, uint2 it, BlendS
   if (seg_lo >= hi_b) return;  // workgroup-uniform: the segment lies behind every pixel's walk
   if (last > seg_end) {  // the pixel's walk starts behind this segment
     const float4* st = a.slots + (size_t)a.bnd_off[tile] * (kTile * kTile) + pix;
-    const float4 sb = get_f4<kStep>(st + (size_t)k * (kTile * kTile));
+    float4 sb = get_f4<kStep>(st + (size_t)k * (kTile * kTile));
+    // a split tile's boundary state past its first part is relative to its forward segment
+    const uint32_t fsh = fbv >> 27;
+    if (split && (seg_end >> fsh) > (((1u << (shift + kPhase1Log)) - 1u) >> fsh)) {
+      const float4 fi = a.fin[((size_t)(fbv & kFbaseMask) + (seg_end >> fsh)) * (kTile * kTile) + pix];
+      sb = make_float4(fi.x * sb.x, fi.y + fi.x * sb.y, fi.z + fi.x * sb.z, fi.w + fi.x * sb.w);
+    }
     const float4 sf = get_f4<kStep>(st + (size_t)((len - 1u) >> shift) * (kTile * kTile));
     Tr = sb.x;  // T >= 1e-4 at every boundary
     Sg = ((sf.y - sb.y) * g0 + (sf.z - sb.z) * g1 + (sf.w - sb.w) * g2) / sb.x;
@@ -771,8 +1208,11 @@ __device__ void backward_item(const BwdArgs& a, uint32_t shift, uint2 it, BlendS
         // of the quadrant (4 lanes) takes the entries any of its pixels composited, back to
         // front, its lanes on the same entry; the block's nine sums are formed in registers
         // and added to the window's sums by one lane of the block.
-        const unsigned long long mine =
-            cbase + j < mask_cap ? ((unsigned long long)mcur.y << 32) | mcur.x : 0ull;
+        unsigned long long mine = cbase + j < mask_cap ? ((unsigned long long)mcur.y << 32) | mcur.x : 0ull;
+        if (split) {  // only entries up to the pixel's last composited one
+          const uint32_t jlo0 = j * kChunk;
+          if (last < jlo0 + kChunk) mine &= last > jlo0 ? (1ull << (last - jlo0)) - 1ull : 0ull;
+        }
         unsigned long long rem = quad_or(mine);
         const uint32_t wbase = j * kChunk - wlo;  // window position of slot 0
         for (;;) {
@@ -895,7 +1335,8 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) voi
     const uint32_t i = s_next;
     __syncthreads();  // every wave has read s_next before it is overwritten
     if (i >= (uint32_t)a.T) break;
-    forward_tile<false>(a, shift, (int)a.order[i], stg);
+    const uint32_t ot = a.order[i];
+    if (!(ot & kOrderSplit)) forward_tile<false>(a, shift, (int)ot, false, stg);  // else done by k_long_forward
   }
 }
 
@@ -911,8 +1352,6 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) voi
 // the forward never waits, so every wait ends; a wait is still bounded, and one that gives up
 // flags the stall word of the header and leaves its item undone.
 // ---------------------------------------------------------------------------------------------
-constexpr uint32_t kSpinLimit = 1u << 20;  // about a second of polling
-
 // Six waves per SIMD, as for the forward: 1.56 instead of 1.61 ms on the 4M-Gaussian 2048x2048 step.
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) void k_blend_step(
     FwdArgs fa, BwdArgs ba, uint32_t* __restrict__ hdr, uint2* __restrict__ items,
@@ -934,8 +1373,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(6))) voi
       const uint32_t i = s_next;
       __syncthreads();
       if (i >= (uint32_t)fa.T) break;
-      const int tile = (int)fa.order[i];
-      forward_tile<true>(fa, shift, tile, sh.stg);
+      const uint32_t ot = fa.order[i];
+      const int tile = (int)(ot & ~kOrderSplit);
+      forward_tile<true>(fa, shift, tile, (ot & kOrderSplit) != 0u, sh.stg);
       drain_memory();
       __syncthreads();  // the tile's state is visible to every XCD
       const uint32_t o = item_off[tile], k = item_off[tile + 1] - o;
@@ -1091,6 +1531,19 @@ size_t n_goff_blocks(int64_t n) { return (size_t)((n + kGoffBlock - 1) / kGoffBl
 size_t plan_blocks(int T) { return (size_t)((T + kPlanThreads - 1) / kPlanThreads); }
 size_t plan_bytes(int T) { return round256(4 * plan_blocks(T) * kPartVals) + round256(4 * plan_blocks(T) * kOffVals); }
 
+// Split tiles and forward segments for k entries: a split list holds len >= kSplitMinLen
+// entries and ceil(len / F) <= len / F + len / kSplitMinLen segments of F >= kFsegMin entries
+// (at the smallest shift; a larger shift only lengthens both).
+constexpr uint64_t kFsegMin = kSegEntries << kFsegLog;
+constexpr uint64_t kSplitMinLen = kSegEntries << kSplitLog;
+size_t split_cap_for(uint64_t k) { return (size_t)std::min<uint64_t>(kMaxSplit, k / kSplitMinLen + 1); }
+size_t fseg_cap_for(uint64_t k) { return (size_t)(k / kFsegMin + k / kSplitMinLen + 2); }
+size_t split_bytes(int T, uint64_t k) {
+  const size_t sc = split_cap_for(k), fc = fseg_cap_for(k);
+  return round256(4 * (size_t)T) + round256(4 * sc) + round256(16 * sc) + round256(8 * fc) + 3 * kSlotBytes * fc +
+         round256(16 * (size_t)(kTile * kTile) * sc);
+}
+
 // bytes of the layout for T tiles, n Gaussians and k staged entries (k a multiple of 256)
 // (tile t's 64-entry chunks start at ranges[t].x / 64 + t, so K entries need at most
 // K / 64 + T mask chunks)
@@ -1100,9 +1553,9 @@ size_t layout_bytes(int T, int64_t n, uint64_t k) {
   return 256 + 2 * round256(4 * (size_t)(T + 1)) + 2 * round256(4 * (size_t)T) + plan_bytes(T) + round256(4 * (size_t)n) +
          round256(4 * (n_goff_blocks(n) + 1)) +
          round256(8 * ((size_t)T + slots)) + round256(kSlotBytes * slots) + kMaskChunkBytes * chunks +
-         round256(36 * (size_t)k + 16);
+         split_bytes(T, k) + round256(36 * (size_t)k + 16);
 }
-// per 256 entries of capacity
+// per 256 entries of capacity, at least (the split tiles' arrays grow in larger steps)
 constexpr size_t kBytesPerSeg = kSlotBytes + 8 + (kSegEntries / kChunk) * kMaskChunkBytes + 36 * kSegEntries;
 
 }  // namespace
@@ -1116,9 +1569,14 @@ bool render_ws_layout(void* ws, size_t bytes, int T, int64_t n, RenderWs* out) {
   const size_t base = layout_bytes(T, n, 0);
   if (!ws || bytes < base || (reinterpret_cast<uintptr_t>(ws) & 255u)) return false;
   // 256 more entries of capacity cost at least kBytesPerSeg - 8 bytes (the item array may not
-  // grow by a whole 256-byte step), so this start is an upper bound; step down to the largest fit
-  uint64_t k = (bytes - base) / (kBytesPerSeg - 8) * kSegEntries;
-  while (k > 0 && layout_bytes(T, n, k) > bytes) k -= kSegEntries;
+  // grow by a whole 256-byte step), so hi is an upper bound; bisect for the largest fit (the
+  // layout grows with k)
+  uint64_t lo = 0, hi = (bytes - base) / (kBytesPerSeg - 8);  // in units of 256 entries
+  while (lo < hi) {
+    const uint64_t mid = lo + (hi - lo + 1) / 2;
+    if (layout_bytes(T, n, mid * kSegEntries) <= bytes) lo = mid; else hi = mid - 1;
+  }
+  const uint64_t k = lo * kSegEntries;
   const size_t slots = (size_t)T + (size_t)(k / kSegEntries);
   if (slots > 0x7FFFFFFFull) return false;
   char* b = static_cast<char*>(ws);
@@ -1147,10 +1605,29 @@ bool render_ws_layout(void* ws, size_t bytes, int T, int64_t n, RenderWs* out) {
   const size_t chunks = (size_t)T + (size_t)(k / kChunk);
   out->masks = reinterpret_cast<uint2*>(b);
   b += kMaskChunkBytes * chunks;
+  const size_t sc = split_cap_for(k), fc = fseg_cap_for(k);
+  out->fbase = reinterpret_cast<uint32_t*>(b);
+  b += round256(4 * (size_t)T);
+  out->split_tile = reinterpret_cast<uint32_t*>(b);
+  b += round256(4 * sc);
+  out->split_cnt = reinterpret_cast<uint32_t*>(b);
+  b += round256(16 * sc);
+  out->fitems = reinterpret_cast<uint2*>(b);
+  b += round256(8 * fc);
+  out->fsum = reinterpret_cast<float4*>(b);
+  b += kSlotBytes * fc;
+  out->fstat = reinterpret_cast<uint4*>(b);
+  b += kSlotBytes * fc;
+  out->fin = reinterpret_cast<float4*>(b);
+  b += kSlotBytes * fc;
+  out->pstate = reinterpret_cast<uint4*>(b);
+  b += round256(16 * (size_t)(kTile * kTile) * sc);
   out->staging = reinterpret_cast<float*>(b);
   out->slots_cap = (uint32_t)slots;
   out->mask_cap = chunks;
   out->staging_cap = k;
+  out->fseg_cap = (uint32_t)fc;
+  out->split_cap = (uint32_t)sc;
   return true;
 }
 
@@ -1178,9 +1655,12 @@ void launch_plan(int T, const uint2* rg, const RenderWs& ws, bool empty_items, h
   hipLaunchKernelGGL(k_plan_scan, dim3(1), dim3(kPlanThreads), 0, s, (const uint32_t*)ws.plan_part, nb, T,
                      ws.slots_cap, (uint64_t)ws.staging_cap, ws.plan_off, ws.hdr, ws.bnd_off, ws.item_off);
   hipLaunchKernelGGL(k_plan_write, dim3((unsigned)nb), dim3(kPlanThreads), 0, s, rg, T,
-                     (const uint32_t*)ws.plan_off, (const uint32_t*)ws.hdr, ws.bnd_off, ws.item_off, ws.order);
-  hipLaunchKernelGGL(k_seg_items, dim3((unsigned)ceil_div(T, kBlock / 64)), dim3(kBlock), 0, s, T,
-                     (const uint32_t*)ws.item_off, ws.items, empty_items);
+                     (const uint32_t*)ws.plan_off, (const uint32_t*)ws.hdr, ws.bnd_off, ws.item_off, ws.order,
+                     ws.fbase);
+  const SplitPlanArgs sp{rg, ws.order, ws.hdr, ws.fbase, ws.split_tile, ws.split_cnt, ws.fitems, ws.fseg_cap,
+                         ws.split_cap};
+  hipLaunchKernelGGL(k_seg_items, dim3((unsigned)std::max(1, (int)ceil_div(T, kPlanThreads / 64))), dim3(kPlanThreads),
+                     0, s, T, (const uint32_t*)ws.item_off, ws.items, empty_items, sp);
 }
 
 // the per-Gaussian staging offsets and the cleared staging rows
@@ -1219,7 +1699,20 @@ FwdArgs fwd_args(const CamK& cam, int64_t n, const gs_splat* splat, const uint32
   a.masks = ws.masks;
   a.mask_cap = ws.mask_cap;
   a.order = ws.order;
+  a.fbase = ws.fbase;
   return a;
+}
+
+LongArgs long_args(const RenderWs& ws) {
+  return LongArgs{ws.split_tile, ws.split_cnt, ws.fitems, ws.fsum, ws.fstat, ws.fin, ws.pstate};
+}
+
+constexpr int kLongPerCu = 4;  // workgroups per CU of the split tiles' forward
+
+// the split tiles' forward (its workgroups return at once when no tile is split)
+void launch_long_forward(const FwdArgs& a, const RenderWs& ws, hipStream_t s) {
+  const unsigned grid = (unsigned)std::max(1, cu_count() * kLongPerCu);
+  hipLaunchKernelGGL(k_long_forward, dim3(grid), dim3(kBlock), 0, s, a, long_args(ws), ws.hdr);
 }
 
 BwdArgs bwd_args(const CamK& cam, int64_t n, const gs_splat* splat, const uint32_t* vals, const uint32_t* ranges,
@@ -1248,6 +1741,8 @@ BwdArgs bwd_args(const CamK& cam, int64_t n, const gs_splat* splat, const uint32
   a.goff_blk = ws.goff_blk;
   a.staging = ws.staging;
   a.staging_cap = ws.staging_cap;
+  a.fbase = ws.fbase;
+  a.fin = ws.fin;
   return a;
 }
 
@@ -1262,6 +1757,7 @@ hipError_t launch_blend_forward(const CamK& cam, int64_t n, const gs_splat* spla
   launch_plan(T, reinterpret_cast<const uint2*>(ranges), ws, false, s);
   const FwdArgs a = fwd_args(cam, n, splat, vals, ranges, bg0, bg1, bg2, image, T_final, last_contrib, n_examined,
                              blend_count, ws);
+  launch_long_forward(a, ws, s);
   const unsigned grid = (unsigned)std::max(1, std::min(T, cu_count() * kFwdPerCu));
   hipLaunchKernelGGL(k_blend_forward, dim3(grid), dim3(kBlock), 0, s, a, ws.hdr);
   return hipGetLastError();
@@ -1315,6 +1811,7 @@ hipError_t launch_blend_step(const CamK& cam, int64_t n, const gs_splat* splat, 
   const int per_cu = resident_per_cu(reinterpret_cast<const void*>(k_blend_step), resident);
   const unsigned grid = (unsigned)std::max(1, cu_count() * per_cu);
   const uint32_t fwd_workers = (uint32_t)std::max(1, std::min(per_cu, kStepFwdPerCu) * cu_count());
+  launch_long_forward(fa, ws, s);
   hipLaunchKernelGGL(k_blend_step, dim3(grid), dim3(kBlock), 0, s, fa, ba, ws.hdr, ws.items,
                      (const uint32_t*)ws.item_off, fwd_workers);
   hipError_t e = hipGetLastError();

@@ -124,7 +124,28 @@ hipError_t launch_bin_sort(int64_t n, int64_t kcap, const CamK& cam, gs_proj pro
 //                   tile t's chunk j is at (ranges[t].x / 64 + t + j)
 //   loss_part[T]    the fused step's per-tile sums of |image - target|
 //   staging[][9]    per-entry gradient sums
+// The forward of the longest lists (at least 2^(shift + kSplitLog) entries) is split: their
+// first 2^(shift + kPhase1Log) entries are walked as any other list, and the pixels still going
+// there walk the rest in forward segments of F = 2^fshift entries in parallel, each from T = 1,
+// combined in list order per pixel:
+//   fbase[T]        a split tile's first forward segment (low 27 bits) and fshift (high 5 bits),
+//                   kNoSplit for the other tiles
+//   split_tile[]    the split tiles (longest list classes first)
+//   split_cnt[][4]  per split tile: first part walked, forward segments walked, combine done
+//   fitems[]        (split tile index, segment) of every forward segment
+//   fsum[][256]     per forward segment and pixel: (P, C_r, C_g, C_b) of the walk from T = 1
+//   fstat[][256]    per forward segment and pixel: first and last composited position, composited
+//                   count (bit 31: the walk stopped), evaluated count
+//   fin[][256]      per forward segment and pixel: (T, C) in front of the segment
+//   pstate[][256]   per split tile and pixel: (stop segment or a marker, last, composited,
+//                   evaluated in front)
 constexpr int kSegShiftMin = 8;  // 256 list entries per segment
+constexpr int kFsegLog = 3;      // the shortest forward segment is 2^kFsegLog backward segments
+constexpr int kSplitLog = 8;     // lists of at least 2^(shift + kSplitLog) entries are split
+constexpr int kPhase1Log = 5;    // ... after a first part of 2^(shift + kPhase1Log) entries walked whole
+constexpr uint32_t kMaxSplit = 1024;  // split tiles at most (one workgroup plans them)
+constexpr uint32_t kNoSplit = 0xFFFFFFFFu;
+constexpr uint32_t kFbaseMask = (1u << 27) - 1u;
 // header words of the render workspace
 constexpr int kHdrShift = 0;    // log2 segment length
 constexpr int kHdrItems = 1;    // backward work items
@@ -136,6 +157,9 @@ constexpr int kHdrReady = 6;    // fused step: work items published so far
 constexpr int kHdrRole = 7;     // fused step: workgroups started so far
 constexpr int kHdrFlags = 8;    // status bits (kFlag* below): set by the kernels, kept until read
 constexpr int kHdrNeed = 9;     // the most intersections lists needed (largest list end, or staged entries)
+constexpr int kHdrSplit = 10;   // split tiles
+constexpr int kHdrFsegs = 11;   // their forward segments
+constexpr int kHdrLongNext = 12;  // next work item of the split tiles' forward (counter)
 constexpr int kHdrStatusWords = 16;  // header words gs_render_init clears
 constexpr uint32_t kFlagStall = 1u;     // fused step: a workgroup gave up waiting for a work item
 constexpr uint32_t kFlagCapacity = 2u;  // the lists need more intersections than the workspace holds
@@ -154,9 +178,19 @@ struct RenderWs {
   uint2* masks;
   float* loss_part;
   float* staging;
+  uint32_t* fbase;
+  uint32_t* split_tile;
+  uint32_t* split_cnt;
+  uint2* fitems;
+  float4* fsum;
+  uint4* fstat;
+  float4* fin;
+  uint4* pstate;
   uint32_t slots_cap;
   uint64_t mask_cap;     // chunks
   uint64_t staging_cap;  // entries
+  uint32_t fseg_cap;     // forward segments
+  uint32_t split_cap;    // split tiles
 };
 size_t render_ws_bytes(int T, int64_t n, int64_t k_capacity);
 // Carves ws (bytes long) into the regions above; only the alignment of ws is read, so a

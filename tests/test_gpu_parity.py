@@ -686,6 +686,93 @@ def test_backward_segments_on_deep_lists():
     torch.cuda.synchronize()
 
 
+def _split_scene():
+    """70,000 Gaussians of low opacity in a blob seen at 64x64: the four centre tiles hold
+    70,000-entry lists (at least 65,536 entries, so their forward runs split: a first part of
+    8192 entries, then 2048-entry forward segments), the others 9,000 to 22,000 (walked whole).
+    Pixels of the split tiles stop in the first part and in many later segments, and most never
+    stop."""
+    n, W = 70000, 64
+    params = inputs.small_scene(37, n, 0, logscale_mean=-1.6, logscale_std=0.2, radius=0.1)
+    params[10] = np.random.default_rng(38).uniform(-6.0, -4.5, n).astype(np.float32)  # opacity 0.0025 .. 0.011
+    cam = inputs.lookat_camera((3.0, 0.0, 0.0), W, W)
+    return params, cam, W
+
+
+def test_split_tiles_forward_in_parallel_segments():
+    """Tiles whose lists hold at least four forward segments run their forward as parallel
+    segment walks from T = 1, an ordered per-pixel combine and an exact walk of each pixel's
+    stop segment.  Forward outputs, the backward blend (which converts the segment walks'
+    boundary states and masks composited entries past each pixel's stop), and the fused step
+    are checked against the oracle on the same records and lists, and the fused step against the
+    separate calls."""
+    import torch
+    say("[parity] test_split_tiles_forward_in_parallel_segments")
+    params, cam, W = _split_scene()
+    n = params.shape[1]
+    up = np.random.default_rng(6).uniform(-1, 1, (W, W, 3)).astype(np.float32)
+    o = oracle_pipeline(params, 0, cam.flat(), W, W, BG, upstream=up, margins=FWD_MARGINS)
+    lens = o["ranges"][:, 1].astype(np.int64) - o["ranges"][:, 0]
+    of = o["fwd"]
+    split = lens >= 65536
+    assert 0 < split.sum() < lens.size, lens
+    tile_of = lambda a: a.reshape(W // 16, 16, W // 16, 16).transpose(0, 2, 1, 3).reshape(-1, 256)
+    ex_t, len_t = tile_of(of["n_examined"]), np.repeat(lens[:, None], 256, 1)
+    stop_seg = (ex_t[split] - 1) // 2048
+    stopped = ex_t[split] < len_t[split]
+    segs = np.unique(stop_seg[stopped])
+    assert segs.min() < 4 and (segs >= 4).sum() >= 10, segs  # stops in the first part and in many segments
+    assert 0.02 < stopped.mean() < 0.5, stopped.mean()
+    g = GpuStep(params, 0, cam, W, W)
+    g.load_proj(*records_from_oracle(o["p32"], o["radii"], o["tiles"], W, W))
+    g.load_lists(o["vals"], o["ranges"])
+    fwd = g.forward(BG)
+    hdr = g.render_ws[:64].cpu().numpy().view(np.uint32)
+    nseg = (lens[split] + 2047) // 2048
+    assert hdr[10] == split.sum() and hdr[11] == nseg.sum(), (hdr[10:12], split.sum(), nseg.sum())
+    ok = ~of["borderline"]
+    say(f"[parity]   split tiles {int(split.sum())} of {lens.size} ({int(nseg.sum())} forward segments); "
+        f"{int((~ok).sum())} borderline px")
+    assert ok.mean() > 0.9
+    assert np.abs(fwd["image"] - of["image"]).max(axis=-1)[ok].max() <= IMG_MAX_ABS
+    assert np.abs(fwd["T_final"] - of["T_final"])[ok].max() <= 1e-5
+    np.testing.assert_array_equal(fwd["last_contrib"][ok], of["last_contrib"][ok])
+    np.testing.assert_array_equal(fwd["n_examined"][ok], of["n_examined"][ok])
+    assert fwd["blend_count"][0] == int(fwd["n_examined"].astype(np.int64).sum())
+    assert fwd["blend_count"][1] == int(fwd["last_contrib"].astype(np.int64).sum())
+    g.set_upstream(o["dl32"])
+    g2, _ = g.backward()
+    errs = [rel_l2(g2[r, :n], o["grad2d"][r]) for r in range(9)]
+    say(f"[parity]   split forward + backward: rel-L2 max {max(errs):.2e}")
+    assert max(errs) <= GRAD_REL_L2, errs
+    # the fused step against a seeded target: the oracle, then the separate calls
+    target = np.random.default_rng(7).uniform(0.0, 1.0, (W, W, 3)).astype(np.float32)
+    ot = oracle_pipeline(params, 0, cam.flat(), W, W, BG, target=target, margins=FWD_MARGINS)
+    r = g.step(BG, target)
+    assert r["stall"] == 0
+    for k in ("image", "T_final", "last_contrib", "n_examined"):
+        np.testing.assert_array_equal(r[k], fwd[k])
+    assert r["blend_count"] == fwd["blend_count"], (r["blend_count"], fwd["blend_count"])
+    di = np.abs(r["image"].astype(np.float64) - ot["img32"].astype(np.float64))
+    assert abs(r["loss"] - ot["loss"]) <= di.mean() + 1e-6 * abs(ot["loss"]) + 1e-9, (r["loss"], ot["loss"])
+    sure = np.abs(ot["img32"].astype(np.float64) - target) > di
+    np.testing.assert_allclose(r["dLdI"][sure], ot["dLdI"][sure], rtol=1e-6, atol=0)
+    # (every Gaussian reaches nearly every pixel here, so one borderline pixel would leave them
+    # all out of a per-Gaussian comparison with the oracle's target step: the fused gradient is
+    # held to the separate calls instead, which are held to the oracle above)
+    f2 = g.forward(BG)
+    for k in ("image", "T_final", "last_contrib", "n_examined"):
+        np.testing.assert_array_equal(f2[k], fwd[k])
+    loss, dLdI = g.loss(target)
+    np.testing.assert_array_equal(dLdI, r["dLdI"])
+    assert abs(loss - r["loss"]) <= 1e-6 * abs(loss)
+    g2s, _ = g.backward()
+    e = rel_l2(r["grad2d"], g2s)
+    say(f"[parity]   split fused step against the separate calls: grad2d rel-L2 {e:.2e}")
+    assert e <= 1e-5
+    torch.cuda.synchronize()
+
+
 def _records_at(u, v, depth, opacity, var, rgb, W, H):
     """Screen-space records (the oracle's planar layout, float32 values) of isotropic Gaussians
     of variance `var` px^2 at pixel positions (u, v), with their 3-sigma radii and tile counts."""
