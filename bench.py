@@ -117,8 +117,8 @@ KERNEL_OF = {"preprocess": ("k_preprocess<3>", "hbm"), "image_pass": ("k_blend_s
 COUNTER_TRAFFIC = {
     "preprocess": {"source": "preprocess.hip", "bytes": 1200081816,
                    "sha256": "bdf2d6b2bfda6bd9c4ee0579c394aa49af9704b4d3f8a784a63a7e38fb911657"},
-    "image_pass": {"source": "blend.hip", "bytes": 6973551326,
-                   "sha256": "6ceeba4e8e7c5307866cd630d9696cf1a5f4ff37e28868639338e8b195b39bff"},
+    "image_pass": {"source": "blend.hip", "bytes": 6962854171,
+                   "sha256": "dd1936f55703a0e7eaca8792e3ceb842ce4dda28f229edd177d0c24a7f4a9420"},
     "prebwd_adam": {"source": "preprocess.hip", "bytes": 5943374354,
                     "sha256": "bdf2d6b2bfda6bd9c4ee0579c394aa49af9704b4d3f8a784a63a7e38fb911657"},
 }

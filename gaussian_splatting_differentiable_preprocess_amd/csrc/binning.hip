@@ -109,8 +109,13 @@ __global__ __launch_bounds__(kBlock) void k_bin_reduce(int64_t n, const uint32_t
   }
 }
 
+// One workgroup: K, the depth-key range and the capacity check into the BinInfo; then ranges
+// <- all (0, 0), unless the lists overflowed and the caller asked for the ranges to be left
+// untouched then.
 __global__ __launch_bounds__(1024) void k_bin_reduce_final(int64_t nblk, const Partial* __restrict__ part,
-                                                            uint64_t kcap, BinInfo* __restrict__ info) {
+                                                            uint64_t kcap, BinInfo* __restrict__ info, int64_t T,
+                                                            int keep_on_overflow, uint32_t* __restrict__ ranges) {
+  __shared__ uint32_t s_over;
   __shared__ unsigned long long ssum[16];
   __shared__ uint32_t smn[16], smx[16];
   unsigned long long s = 0;
@@ -144,7 +149,11 @@ __global__ __launch_bounds__(1024) void k_bin_reduce_final(int64_t nblk, const P
     r.kcap = kcap;
     r.over = r.K > kcap ? 1u : 0u;
     *info = r;
+    s_over = r.over;
   }
+  __syncthreads();
+  if (s_over && keep_on_overflow) return;
+  for (int64_t j = threadIdx.x; j < 2 * T; j += 1024) ranges[j] = 0u;
 }
 
 // ---- what the device knows after the count -------------------------------------------------
@@ -441,16 +450,6 @@ __global__ __launch_bounds__(kBlock) void k_keygen(const BinInfo* __restrict__ i
   }
 }
 
-// ranges <- all (0, 0), unless the lists overflowed and the caller asked for the ranges to be
-// left untouched then.
-__global__ __launch_bounds__(kBlock) void k_ranges_clear(const BinInfo* __restrict__ info, int64_t T,
-                                                         int keep_on_overflow, uint32_t* __restrict__ ranges) {
-  const BinInfo in = *info;
-  if (in.over && keep_on_overflow) return;
-  for (int64_t j = (int64_t)blockIdx.x * kBlock + threadIdx.x; j < 2 * T; j += (int64_t)gridDim.x * kBlock)
-    ranges[j] = 0u;
-}
-
 // ranges[2t], ranges[2t+1] = first and one-past-last position of tile t.
 __global__ __launch_bounds__(kBlock) void k_ranges(const uint32_t* __restrict__ tk, const BinInfo* __restrict__ info,
                                                     uint32_t T, uint32_t* __restrict__ ranges) {
@@ -538,10 +537,8 @@ hipError_t launch_bin_sort(int64_t n, int64_t kcap, const CamK& cam, gs_proj pro
   if (n > 0)
     hipLaunchKernelGGL(k_bin_reduce, dim3((unsigned)nr), dim3(kBlock), 0, s, n, proj.tiles, proj.depth_key, part);
   hipLaunchKernelGGL(k_bin_reduce_final, dim3(1), dim3(1024), 0, s, n > 0 ? nr : 0, (const Partial*)part,
-                     (uint64_t)(kcap > 0 ? kcap : 0), reinterpret_cast<BinInfo*>(ws + L.info));
-  const unsigned clear_grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>(ceil_div(2 * T, kBlock), 1024));
-  hipLaunchKernelGGL(k_ranges_clear, dim3(clear_grid), dim3(kBlock), 0, s, info, T, (int)keep_ranges_on_overflow,
-                     ranges);
+                     (uint64_t)(kcap > 0 ? kcap : 0), reinterpret_cast<BinInfo*>(ws + L.info), T,
+                     (int)keep_ranges_on_overflow, ranges);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n <= 0 || kcap <= 0) return e;
   uint32_t* counts = reinterpret_cast<uint32_t*>(ws + L.counts);

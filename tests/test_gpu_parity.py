@@ -594,6 +594,47 @@ def test_gaussian_covering_many_tiles():
         assert rel_l2(r["grad2d"][row], o["grad2d"][row]) <= GRAD_REL_L2, row
 
 
+@pytest.mark.parametrize("octaves", [0.0, 0.003, 0.2, 2.5, 20.0])
+def test_sort_across_depth_spans(octaves):
+    """The stable (tile, depth) sort, bit-exact against the oracle's, for depth spans whose
+    float32 bits vary over 6, 15, 21, 25 and 28 bits: the depth passes (8-bit digits) cover one
+    to four of the key's digits.  Depths repeat (a tenth of them copy another's), so ties are
+    broken by index, and a share of the Gaussians lie off screen."""
+    import torch
+    say(f"[parity] test_sort_across_depth_spans octaves={octaves}")
+    rng = np.random.default_rng(int(octaves * 10) + 3)
+    W, H, n = 200, 136, 30000
+    u = rng.uniform(-20, W + 20, n).astype(np.float32)
+    v = rng.uniform(-20, H + 20, n).astype(np.float32)
+    if octaves == 0.0:  # a span of ~60 ulps
+        depth = (np.float32(3.0) + np.float32(2.4e-7) * rng.integers(0, 60, n)).astype(np.float32)
+    else:
+        depth = (0.05 * np.exp2(rng.uniform(0, octaves, n))).astype(np.float32)
+    dup = rng.random(n) < 0.1
+    depth[dup] = depth[rng.integers(0, n, int(dup.sum()))]
+    var = rng.uniform(1.0, 60.0, n).astype(np.float32)
+    proj = np.zeros((10, n), np.float32)
+    proj[0], proj[1], proj[2], proj[3] = u, v, depth, 0.5
+    proj[4], proj[6] = 1.0 / var, 1.0 / var
+    proj = proj.astype(np.float64)
+    radii = np.ceil(3.0 * np.sqrt(var)).astype(np.int32)[None].repeat(2, 0)
+    rect = oracle.tile_rects(proj, radii, W, H)
+    tiles = ((rect[1] - rect[0]) * (rect[3] - rect[2])).astype(np.uint32)
+    keys, vals = oracle.bin_sort(proj, radii, W, H)
+    rg = oracle.ranges(keys, oracle.n_tiles(W, H)).reshape(-1, 2)
+    span = int(depth.view(np.uint32).max()) - int(depth.view(np.uint32).min())
+    say(f"[parity]   K={keys.size}, depth-key span {span} ({span.bit_length()} bits)")
+    params = np.zeros((11 + 3, n), np.float32)  # (the preprocess is not run: only n and the degree matter)
+    g = GpuStep(params, 0, inputs.lookat_camera((3.0, 0.0, 0.0), W, H), W, H)
+    g.load_proj(*records_from_oracle(proj, radii, tiles, W, H))
+    K, gk, gv, gr = g.bin_and_sort()
+    assert K == keys.size
+    np.testing.assert_array_equal(gk, keys)
+    np.testing.assert_array_equal(gv, vals)
+    np.testing.assert_array_equal(gr.reshape(-1, 2), rg)
+    torch.cuda.synchronize()
+
+
 def test_repeatable_forward_and_sort():
     say("[parity] test_repeatable")
     params = inputs.small_scene(12, 3000, 3, logscale_mean=-3.0, logscale_std=0.5)
