@@ -15,7 +15,8 @@ Prints ONE JSON line on stdout (progress goes to stderr):
                pass k_blend_step by default) against its roof, from HIP events on the launch
                stream: the method's flops (or bytes) per launch / time against the fp32 vector
                peak (or 8 TB/s), with the HBM bytes the counters measured for it
-               (COUNTER_TRAFFIC)
+               (COUNTER_TRAFFIC) and, for the image pass, the issue rate of all its VALU
+               instructions against the SIMDs' limit (COUNTER_VALU)
   cpu_baseline the CPU oracle on a bounded sample of the same step (see cpu_baseline())
 """
 from __future__ import annotations
@@ -124,11 +125,23 @@ COUNTER_TRAFFIC = {
 }
 
 
+# VALU instructions per launch of the image pass (rocprofv3 SQ_INSTS_VALU, one wave64 instruction
+# each) on the same workload, keyed like COUNTER_TRAFFIC: against what 1024 SIMDs issue in the
+# launch's time (one wave64 VALU instruction per SIMD per 4 cycles at 2.4 GHz), the issue rate
+# that bounds the kernel, box and mask arithmetic included
+COUNTER_VALU = {
+    "image_pass": {"source": "blend.hip", "insts": 610.2e6,
+                   "sha256": "dd1936f55703a0e7eaca8792e3ceb842ce4dda28f229edd177d0c24a7f4a9420"},
+}
+VALU_ISSUE_PER_S = 256 * 4 * 2.4e9 / 4  # wave64 VALU instructions per second, all SIMDs
+
 COUNTER_WORKLOAD = "gyroid_4m_2048"
 
 
-def counter_traffic(phase, workload):
-    rec = COUNTER_TRAFFIC.get(phase)
+def counter_record(table, phase, workload):
+    """The stored counter record of `phase` if it was taken on this workload and the kernel's
+    source is unchanged since, else None."""
+    rec = table.get(phase)
     if rec is None or workload != COUNTER_WORKLOAD:
         return None
     src = os.path.join(ROOT, "gaussian_splatting_differentiable_preprocess_amd", "csrc", rec["source"])
@@ -136,7 +149,12 @@ def counter_traffic(phase, workload):
     with open(src, "rb") as f:
         if hashlib.sha256(f.read()).hexdigest() != rec["sha256"]:
             return None
-    return rec["bytes"]
+    return rec
+
+
+def counter_traffic(phase, workload):
+    rec = counter_record(COUNTER_TRAFFIC, phase, workload)
+    return rec["bytes"] if rec else None
 
 
 def render_targets(gsmi, torch, cfg, cams, tparams_np, targets, log_every=64):
@@ -484,6 +502,9 @@ def main():
         roof = {"bound": "alu", "achieved": round(achieved, 2), "peak": ALU_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / ALU_PEAK_TFLOPS, 4),
                 "frac_of_nonpacked_peak": round(achieved / ALU_PEAK_NONPACKED_TFLOPS, 4)}
+        vrec = counter_record(COUNTER_VALU, dom, cfg.name)
+        # the issue rate of all VALU instructions (the counters'), against the SIMDs' issue limit
+        roof["valu_issue_frac"] = round(vrec["insts"] / sec / VALU_ISSUE_PER_S, 4) if vrec else None
     else:
         work = bytes_alg
         achieved = work / sec / 1e9
