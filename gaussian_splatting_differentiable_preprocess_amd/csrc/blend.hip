@@ -329,10 +329,16 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan_count(const uint2* __rest
   if (threadIdx.x < kLenClasses) cls[threadIdx.x] = 0u;
   __syncthreads();
   if (t < T) atomicAdd(&cls[len_class(len)], 1u);
+  uint32_t mlen = len;  // the wave's longest list: no list is longer than 2^shift past it
+  for (int o = 32; o > 0; o >>= 1) mlen = max(mlen, (uint32_t)__shfl_xor(mlen, o, 64));
   for (int q = 0; q < kShifts; ++q) {
     const int sh = kSegShiftMin + q;
-    const bool lg = len > (1u << sh);
-    const uint32_t sl = wave_sum(lg ? ((len - 1u) >> sh) + 1u : 0u), nl = wave_sum(lg ? 1u : 0u);
+    uint32_t sl = 0, nl = 0;
+    if (mlen > (1u << sh)) {  // (wave-uniform)
+      const bool lg = len > (1u << sh);
+      sl = wave_sum(lg ? ((len - 1u) >> sh) + 1u : 0u);
+      nl = wave_sum(lg ? 1u : 0u);
+    }
     if ((threadIdx.x & 63) == 0) {
       red[w][kPartSlots + q] = sl;
       red[w][kPartLong + q] = nl;
