@@ -19,7 +19,7 @@
 // (a skipped record has alpha < 1/255 at that pixel).  The forward's quadrant waves are
 // independent (no workgroup barrier).  The forward also leaves, per pixel and chunk, the 64-bit
 // mask of the chunk's entries it composited; the backward walks exactly those entries (per
-// 2x2 pixel block of 4 lanes, whose sums are formed with DPP), so no record is tested twice.
+// 4x4 pixel block of 16 lanes, whose sums are formed with DPP), so no record is tested twice.
 // The backward's waves share per-entry gradient sums in LDS.
 // Workgroup b renders tile b: the hardware deals consecutive workgroups to the 8 XCDs in turn,
 // which spreads the (very uneven) per-tile work evenly over them.  Bound: VALU /
@@ -56,24 +56,49 @@ __device__ __forceinline__ uint32_t dpp_or(uint32_t x) {
   return x | (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, true);
 }
 
-// Sums each of N values over each group of 4 consecutive lanes (a DPP quad); every lane gets
-// its group's sums.  Every lane of the wave must be active.
-template <int N>
-__device__ __forceinline__ void quad_sum(float* v) {
-#pragma unroll
-  for (int q = 0; q < N; ++q) v[q] = dpp_add<0xB1>(v[q]);  // quad_perm [1,0,3,2]
-#pragma unroll
-  for (int q = 0; q < N; ++q) v[q] = dpp_add<0x4E>(v[q]);  // quad_perm [2,3,0,1]
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 
-// OR of a 64-bit value over each group of 4 consecutive lanes; every lane must be active.
-__device__ __forceinline__ unsigned long long quad_or(unsigned long long m) {
+// OR of a 64-bit value over each row of 16 lanes: over each quad (quad_perm [1,0,3,2], then
+// [2,3,0,1]), then each quad with its mirror in the row's half (row_half_mirror) and each half
+// with the other (row_mirror).  Every lane must be active; every lane gets its row's OR.
+__device__ __forceinline__ unsigned long long row_or(unsigned long long m) {
   uint32_t lo = (uint32_t)m, hi = (uint32_t)(m >> 32);
   lo = dpp_or<0xB1>(lo);
   hi = dpp_or<0xB1>(hi);
   lo = dpp_or<0x4E>(lo);
   hi = dpp_or<0x4E>(hi);
+  lo = dpp_or<0x141>(lo);
+  hi = dpp_or<0x141>(hi);
+  lo = dpp_or<0x140>(lo);
+  hi = dpp_or<0x140>(hi);
   return ((unsigned long long)hi << 32) | lo;
+}
+
+// Sums of nine values over each row of 16 lanes, spread over the row (a reduce-scatter): lane r
+// of the row ends with the row's sum of v[4 b3 + 2 b2 + b1] (b the bits of r) and *s8 with the
+// row's sum of v[8].  Four exchanges, each pairing lane r with r ^ 15 (row_mirror), r ^ 7
+// (row_half_mirror), r ^ 2 and r ^ 1 (quad_perm): partners differ in bit 3, then bit 2, 1, 0,
+// and agree on the bits already used.  At the first three each lane keeps the half of its values
+// that its bit selects and adds its partner's copy of that half, so the partner's copy of the
+// other half is added there; v[8] and the last step are summed whole.  27 VALU operations
+// against 36 for summing all nine whole.  Every lane must be active.
+__device__ __forceinline__ float row_scatter9(const float* v, int lane, float* s8) {
+  const bool b3 = (lane & 8) != 0, b2 = (lane & 4) != 0, b1 = (lane & 2) != 0;
+  float r[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) r[k] = (b3 ? v[k + 4] : v[k]) + dpp_mov<0x140>(b3 ? v[k] : v[k + 4]);
+  float r8 = dpp_add<0x140>(v[8]);
+  float s[2];
+#pragma unroll
+  for (int k = 0; k < 2; ++k) s[k] = (b2 ? r[k + 2] : r[k]) + dpp_mov<0x141>(b2 ? r[k] : r[k + 2]);
+  r8 = dpp_add<0x141>(r8);
+  const float t = (b1 ? s[1] : s[0]) + dpp_mov<0x4E>(b1 ? s[0] : s[1]);
+  r8 = dpp_add<0x4E>(r8);
+  *s8 = dpp_add<0xB1>(r8);
+  return dpp_add<0xB1>(t);
 }
 
 constexpr int kChunk = 64;  // records staged per chunk (one per lane)
@@ -1074,7 +1099,7 @@ __global__ __launch_bounds__(kBlock) void k_long_forward(FwdArgs a, LongArgs L, 
 // behind it, (C_final - C_boundary) / T_boundary; otherwise from T_final with nothing behind.
 // The segments of one tile are independent, so a long list is spread over many CUs.
 // Persistent workgroups take items from a counter in the workspace until none are left.
-// Each 2x2 pixel block walks the entries its pixels composited (the forward's masks), back to
+// Each 4x4 pixel block walks the entries its pixels composited (the forward's masks), back to
 // front; the block's nine gradient sums per entry go into the workgroup's LDS sums over a window
 // of 256 entries, whose sums then go to the staging area, one row per (entry, tile).
 // ---------------------------------------------------------------------------------------------
@@ -1125,10 +1150,16 @@ __device__ void backward_item(const BwdArgs& a, uint32_t shift, uint2 it, BlendS
   Chunk& S = sh.stg[w];
   float(*acc)[kWin] = sh.acc;
   uint32_t* s_mx = sh.mx;
-  // lanes 4 q .. 4 q + 3 are the 2x2 pixel block q of the quadrant (blocks row-major, pixels
-  // row-major inside a block): each block reduces over one DPP quad
-  const int lx = ((lane >> 2) & 3) * 2 + (lane & 1), ly = (lane >> 4) * 2 + ((lane >> 1) & 1);
+  // the 16 lanes of DPP row q (lanes 16 q .. 16 q + 15) are the 4x4 pixel block q of the
+  // quadrant (blocks row-major): each block reduces over one row
+  const int lx = ((lane >> 4) & 1) * 4 + ((lane >> 2) & 1) * 2 + (lane & 1);
+  const int ly = (lane >> 5) * 4 + ((lane >> 3) & 1) * 2 + ((lane >> 1) & 1);
   const int pix = tile_pixel(w, lx, ly);
+  // the block's sum this lane adds to the window's sums (row_scatter9): lanes 0, 2, .., 14 of
+  // the row hold sums 0..7, lane 1 sum 8
+  const int rl = lane & 15;
+  const bool own = (rl & 1) == 0 || rl == 1;
+  float* const acc_own = acc[rl == 1 ? 8 : ((rl >> 3) & 1) * 4 + ((rl >> 2) & 1) * 2 + ((rl >> 1) & 1)];
   const int tile = (int)it.x;
   const uint32_t k = it.y;
   const int tx = tile % TX, ty = tile / TX;
@@ -1210,16 +1241,16 @@ __device__ void backward_item(const BwdArgs& a, uint32_t shift, uint2 it, BlendS
         put(S, lane, cur);
         wave_sync_lds();
         // The entries this pixel composited in the chunk (the forward's mask): exactly those
-        // with power <= 0, alpha >= 1/255 in front of the pixel's stop.  Each 2x2 pixel block
-        // of the quadrant (4 lanes) takes the entries any of its pixels composited, back to
-        // front, its lanes on the same entry; the block's nine sums are formed in registers
-        // and added to the window's sums by one lane of the block.
+        // with power <= 0, alpha >= 1/255 in front of the pixel's stop.  Each 4x4 pixel block
+        // of the quadrant (16 lanes) takes the entries any of its pixels composited, back to
+        // front, its lanes on the same entry; the block's nine sums are formed in registers,
+        // spread over nine of its lanes, and each of those lanes adds its sum to the window's.
         unsigned long long mine = cbase + j < mask_cap ? ((unsigned long long)mcur.y << 32) | mcur.x : 0ull;
         if (split) {  // only entries up to the pixel's last composited one
           const uint32_t jlo0 = j * kChunk;
           if (last < jlo0 + kChunk) mine &= last > jlo0 ? (1ull << (last - jlo0)) - 1ull : 0ull;
         }
-        unsigned long long rem = quad_or(mine);
+        unsigned long long rem = row_or(mine);
         const uint32_t wbase = j * kChunk - wlo;  // window position of slot 0
         for (;;) {
           const bool has = rem != 0ull;
@@ -1258,12 +1289,10 @@ __device__ void backward_item(const BwdArgs& a, uint32_t shift, uint2 it, BlendS
             Sg = alpha * cdg + om * Sg;
             Tr = Tk;
           }
-          quad_sum<9>(v);  // every lane of a pixel block holds the block's sums
-          if ((lane & 3) == 0 && has) {  // the raw moments: the conic enters once per entry
-            const uint32_t ws = wbase + (uint32_t)e;
-#pragma unroll
-            for (int q = 0; q < 9; ++q) atomicAdd(&acc[q][ws], v[q]);
-          }
+          float s8;
+          const float sq = row_scatter9(v, lane, &s8);
+          if (own && has)  // the raw moments: the conic enters once per entry
+            atomicAdd(acc_own + wbase + (uint32_t)e, rl == 1 ? s8 : sq);
         }
         wave_sync_lds();  // this chunk's reads finish before the next chunk is staged
         cur = nxt;
