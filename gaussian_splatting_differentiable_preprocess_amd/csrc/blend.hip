@@ -120,9 +120,12 @@ __device__ __forceinline__ Box alpha_box(float u, float v, float A, float B, flo
   const float det = A * C - B * B;
   float hx = 1e30f, hy = 1e30f;
   if (det > 0.0f && __builtin_isfinite(det)) {
-    const float tau = 2.0f * __logf(255.0f * o) * 1.001f + 1e-3f;
-    hx = sqrtf(tau * C / det) * 1.001f + 0.01f;
-    hy = sqrtf(tau * A / det) * 1.001f + 0.01f;
+    // the hardware log2, reciprocal and square root (errors of a few ulp, far inside the
+    // widening); 255 o >= 1 here, and a huge or infinite half-width only widens the box
+    const float tau = 1.38629436f * __builtin_amdgcn_logf(255.0f * o) * 1.001f + 1e-3f;  // 2 ln(255 o)
+    const float rdet = __builtin_amdgcn_rcpf(det);
+    hx = __builtin_amdgcn_sqrtf(tau * C * rdet) * 1.001f + 0.01f;
+    hy = __builtin_amdgcn_sqrtf(tau * A * rdet) * 1.001f + 0.01f;
   }
   // pixel index p has its centre at p + 0.5: p in [u - hx - 0.5, u + hx - 0.5]
   const float fx0 = ceilf(u - hx - 0.5f - (float)xq), fx1 = floorf(u + hx - 0.5f - (float)xq);
@@ -136,20 +139,27 @@ __device__ __forceinline__ Box alpha_box(float u, float v, float A, float B, flo
 }
 
 // Per-lane masks: bit e set iff record e's box contains the lane's pixel (lx, ly).  Lane e
-// holds record e's box; COL[x] / ROW[y] are ballots over the records.
-__device__ __forceinline__ unsigned long long lane_mask(const Box& b, int lx, int ly) {
-  unsigned long long col = 0ull, row = 0ull;
+// holds record e's box as 16 coverage bits (columns x0..x1 in bits 0..7, rows y0..y1 in bits
+// 8..15); ballot k over the records is column k's (k < 8) or row k - 8's mask.  The sixteen
+// ballots are kept in lanes 0..15 of two registers (low and high halves), from which each lane
+// fetches its column's and its row's mask (ds_bpermute, no LDS memory).
+__device__ __forceinline__ unsigned long long lane_mask(const Box& b, int lane, int lx, int ly) {
+  const uint32_t cov = b.x0 <= b.x1 ? ((2u << b.x1) - (1u << b.x0)) | (((2u << b.y1) - (1u << b.y0)) << 8) : 0u;
+  int lo = 0, hi = 0;
+  int ln = lane;
 #pragma unroll
-  for (int x = 0; x < 8; ++x) {
-    const unsigned long long c = __ballot(b.x0 <= x && x <= b.x1);
-    col = (lx == x) ? c : col;
+  for (int k = 0; k < 16; ++k) {
+    // (an opaque copy of the lane index: the sixteen lane == k tests are formed here instead
+    // of being held in 32 scalar registers across the walk, which spills)
+    asm volatile("" : "+v"(ln));
+    const unsigned long long m = __builtin_amdgcn_ballot_w64(((cov >> k) & 1u) != 0u);
+    lo = ln == k ? (int)(uint32_t)m : lo;
+    hi = ln == k ? (int)(uint32_t)(m >> 32) : hi;
   }
-#pragma unroll
-  for (int y = 0; y < 8; ++y) {
-    const unsigned long long r = __ballot(b.y0 <= y && y <= b.y1);
-    row = (ly == y) ? r : row;
-  }
-  return col & row;
+  const int ac = lx << 2, ar = (8 + ly) << 2;  // byte addresses of lanes lx and 8 + ly
+  const uint32_t clo = (uint32_t)__builtin_amdgcn_ds_bpermute(ac, lo), chi = (uint32_t)__builtin_amdgcn_ds_bpermute(ac, hi);
+  const uint32_t rlo = (uint32_t)__builtin_amdgcn_ds_bpermute(ar, lo), rhi = (uint32_t)__builtin_amdgcn_ds_bpermute(ar, hi);
+  return ((unsigned long long)(chi & rhi) << 32) | (clo & rlo);
 }
 
 // One chunk of records in LDS, indexed by slot (read per lane).
@@ -677,7 +687,7 @@ __device__ __forceinline__ void walk_entries(const FwdArgs& a, uint32_t shift, u
     put(S, lane, cur);
     const Box bx = alpha_box(cur.uv.x, cur.uv.y, cur.abco.x, cur.abco.y, cur.abco.z, opacity_of(cur, n), xq, yq);
     // every lane takes part in the ballots: lane e holds record e's box
-    unsigned long long m = lane_mask(bx, lx, ly);
+    unsigned long long m = lane_mask(bx, lane, lx, ly);
     if (done) m = 0ull;
     evaluated += (uint32_t)__popcll(m);
     wave_sync_lds();
