@@ -118,8 +118,8 @@ KERNEL_OF = {"preprocess": ("k_preprocess<3>", "hbm"), "image_pass": ("k_blend_s
 COUNTER_TRAFFIC = {
     "preprocess": {"source": "preprocess.hip", "bytes": 1200081816,
                    "sha256": "bdf2d6b2bfda6bd9c4ee0579c394aa49af9704b4d3f8a784a63a7e38fb911657"},
-    "image_pass": {"source": "blend.hip", "bytes": 6962854171,
-                   "sha256": "dd1936f55703a0e7eaca8792e3ceb842ce4dda28f229edd177d0c24a7f4a9420"},
+    "image_pass": {"source": "blend.hip", "bytes": 6899480381,
+                   "sha256": "eb2bea5cd7565a1cf46e13684dc26246875337517aaf555c1157bfdf9fad625c"},
     "prebwd_adam": {"source": "preprocess.hip", "bytes": 5943374354,
                     "sha256": "bdf2d6b2bfda6bd9c4ee0579c394aa49af9704b4d3f8a784a63a7e38fb911657"},
 }
@@ -130,8 +130,8 @@ COUNTER_TRAFFIC = {
 # launch's time (one wave64 VALU instruction per SIMD per 4 cycles at 2.4 GHz), the issue rate
 # that bounds the kernel, box and mask arithmetic included
 COUNTER_VALU = {
-    "image_pass": {"source": "blend.hip", "insts": 610.2e6,
-                   "sha256": "dd1936f55703a0e7eaca8792e3ceb842ce4dda28f229edd177d0c24a7f4a9420"},
+    "image_pass": {"source": "blend.hip", "insts": 649.2e6,
+                   "sha256": "eb2bea5cd7565a1cf46e13684dc26246875337517aaf555c1157bfdf9fad625c"},
 }
 VALU_ISSUE_PER_S = 256 * 4 * 2.4e9 / 4  # wave64 VALU instructions per second, all SIMDs
 
