@@ -5,7 +5,10 @@ A step is one pass of the whole hot path for one orbit view: preprocess -> bin/s
 blend -> L1 loss -> backward blend -> preprocess backward fused with Adam, over the scene's
 Gaussians, with every input already resident in HBM.  Default workload: the 4M-Gaussian gyroid
 isosurface at 2048x2048 over the 448-view orbit (views taken in orbit order; targets rendered
-beforehand from a second seeded Gaussian set, untimed).
+beforehand from a second seeded Gaussian set, untimed).  By default each step's preprocess
+backward also preprocesses the next view from the parameters it has just updated (one read of
+them for both; the first step's view is preprocessed before the loop), so a timed step holds one
+preprocess, as the plain sequence does; --separate-preprocess runs it as a call of its own.
 
 Prints ONE JSON line on stdout (progress goes to stderr):
   value        Gaussian-pixel blends per second over the timed steps (sum of n_examined, the
@@ -58,6 +61,8 @@ def alg_bytes(phase, N, R, K, P, T, n_vis, batch=1):
         if batch > 1:
             return N * ((8 * R + (batch - 2) * 12 * R + 28 * R) / batch + 36)
         return N * (24 * R + 36)
+    if phase == "prebwd_adam_next":    # as prebwd_adam, and the next view's preprocess outputs
+        return alg_bytes("prebwd_adam", N, R, K, P, T, n_vis, batch) + N * 64
     if phase == "image_pass":          # the fused forward + L1 + backward blend
         return sum(alg_bytes(ph, N, R, K, P, T, n_vis) for ph in ("forward", "loss", "backward_blend"))
     return 0
@@ -109,7 +114,8 @@ def alg_flops(phase, examined, walked, composited, evaluated, ssim_values=0):
 # forward and backward phases also run their plan and staging kernels, so their event time is
 # not one kernel's
 KERNEL_OF = {"preprocess": ("k_preprocess<3>", "hbm"), "image_pass": ("k_blend_step", "alu"),
-             "prebwd_adam": ("k_preprocess_backward<3>", "hbm")}
+             "prebwd_adam": ("k_preprocess_backward<3>", "hbm"),
+             "prebwd_adam_next": ("k_preprocess_backward<3, true>", "hbm")}
 
 # HBM bytes per launch from rocprofv3 FETCH_SIZE and WRITE_SIZE passes over the workload named
 # (gyroid_4m_2048), each scaled by the factor the same counter reads for a plain copy of known
@@ -301,6 +307,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=30.0, help="seconds of oracle steps in the CPU baseline")
     ap.add_argument("--unfused-adam", action="store_true", help="separate Adam kernel instead of the fused one")
+    ap.add_argument("--separate-preprocess", action="store_true",
+                    help="preprocess each view in its own call instead of in the previous step's preprocess "
+                         "backward (which reads the updated parameters once for both)")
     ap.add_argument("--separate-passes", action="store_true",
                     help="forward, L1 loss and backward blend as three calls instead of the fused image pass")
     ap.add_argument("--dssim", type=float, default=None, metavar="LAMBDA",
@@ -382,7 +391,12 @@ def main():
     dens_cnt = torch.zeros(N, device="cuda") if args.densify else None
     dssim_ws = (torch.empty(gsmi.loss_l1_dssim_workspace(W, H), dtype=torch.uint8, device="cuda")
                 if args.dssim is not None else None)
-    phases = (["preprocess", "bin_and_sort", "render_plan", "image_pass"] + (["densify_stats"] if args.densify else [])
+    # the next view's preprocess runs in this step's preprocess backward (one read of the updated
+    # parameters for both); the first step's view is preprocessed before the loop
+    tail = fused and not args.unfused_adam and args.batch == 1 and not args.separate_preprocess
+    phases = ((["bin_and_sort", "render_plan", "image_pass"] + (["densify_stats"] if args.densify else [])
+               + ["prebwd_adam_next"]) if tail else
+              ["preprocess", "bin_and_sort", "render_plan", "image_pass"] + (["densify_stats"] if args.densify else [])
               + ["prebwd_adam"] if fused else
               ["preprocess", "bin_and_sort", "forward"] + ([] if upstream_mode else ["loss"]) +
               ["backward_blend", "prebwd_adam"])
@@ -400,8 +414,9 @@ def main():
                 e.record()
 
         mark()
-        gsmi.preprocess(buf.scene, p, cam, buf.proj)
-        mark()
+        if not tail:
+            gsmi.preprocess(buf.scene, p, cam, buf.proj)
+            mark()
         gsmi.bin_and_sort(buf.scene, cam, buf.proj, buf.ws, buf.k_capacity, buf.vals, buf.ranges, wait=False)
         if kslot is not None:  # this step's K, from the sort workspace's count (a device copy)
             ks_dev[kslot].copy_(buf.ws[:8].view(torch.int64)[0])
@@ -446,11 +461,16 @@ def main():
         if args.unfused_adam:
             gsmi.preprocess_backward(buf.scene, p, cam, buf.grad2d, grads)
             gsmi.adam_step(R * N, p, grads, adam)
+        elif tail:
+            gsmi.preprocess_backward_staged_next(buf.scene, p, cam, buf.proj, buf.render_ws, gcams[(view + 1) % V],
+                                                 buf.proj, None, adam)
         else:
             gsmi.preprocess_backward_staged(buf.scene, p, cam, buf.proj, buf.render_ws, None, adam)
         mark()
 
     log(f"[bench] warmup {args.warmup} steps ...")
+    if tail:  # the first step's view; each step then preprocesses the next view
+        gsmi.preprocess(buf.scene, p, gcams[0], buf.proj)
     t = 0
     for w in range(args.warmup):
         t += 1
@@ -581,6 +601,7 @@ def main():
                                         else f"l1+dssim(lambda={args.dssim})"),
                    "adam": "fused" if not args.unfused_adam else "separate", "batch": args.batch,
                    "image_pass": "fused" if fused else "separate",
+                   "preprocess": "in the previous step's preprocess backward" if tail else "separate",
                    "intersections_mean": round(Kmean), "intersections_min": int(min(ks)),
                    "intersections_max": int(max(ks))},
         "roofline": roof,

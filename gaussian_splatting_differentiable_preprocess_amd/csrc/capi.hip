@@ -299,7 +299,8 @@ namespace {
 int run_preprocess_backward(const gs_scene* scene, float* params, const gs_camera* cam, const float* grad2d,
                             const gsmi::RenderWs* ws, const uint32_t* tiles, float* grads, const gs_adam* adam,
                             hipStream_t stream, const char* who, const float* gacc = nullptr,
-                            float gscale = 1.0f) {
+                            float gscale = 1.0f, const gs_camera* next_cam = nullptr,
+                            const gs_proj* next = nullptr) {
   PrebwdArgs a{};
   a.gacc = gacc;
   a.gscale = gscale;
@@ -329,7 +330,15 @@ int run_preprocess_backward(const gs_scene* scene, float* params, const gs_camer
     a.inv_bc1 = c.inv_bc1;
     a.inv_bc2 = c.inv_bc2;
   }
-  const hipError_t e = launch_preprocess_backward(a, make_cam(*cam), stream);
+  hipError_t e;
+  if (next_cam) {
+    const CamK cn = make_cam(*next_cam);
+    const NextOut nx{reinterpret_cast<float4*>(next->splat), next->tiles, next->depth_key,
+                     reinterpret_cast<uint2*>(next->rect)};
+    e = launch_preprocess_backward(a, make_cam(*cam), stream, &cn, &nx);
+  } else {
+    e = launch_preprocess_backward(a, make_cam(*cam), stream);
+  }
   return e == hipSuccess ? ok() : hip_fail(e, who);
 }
 }  // namespace
@@ -361,6 +370,25 @@ int gs_preprocess_backward_staged(const gs_scene* scene, float* params, const gs
     return fail(GS_ERR_INVALID_ARGUMENT, "render workspace too small or not 256-byte aligned");
   return run_preprocess_backward(scene, params, cam, nullptr, &ws, proj.tiles, grads, adam, stream,
                                  "gs_preprocess_backward_staged");
+}
+
+int gs_preprocess_backward_staged_next(const gs_scene* scene, float* params, const gs_camera* cam, gs_proj proj,
+                                       const void* render_ws, size_t render_ws_bytes, float* grads,
+                                       const gs_adam* adam, const gs_camera* next_cam, gs_proj next,
+                                       hipStream_t stream) {
+  int st;
+  if ((st = check_scene(scene)) || (st = check_camera(cam)) || (st = check_adam(adam)) ||
+      (st = check_camera(next_cam)) || (st = check_proj(next, true, scene->n)))
+    return st;
+  if (scene->n > 0 && !params) return fail(GS_ERR_INVALID_ARGUMENT, "params is null");
+  if (scene->n > 0 && !proj.tiles) return fail(GS_ERR_INVALID_ARGUMENT, "proj.tiles is null");
+  if (scene->n > 0 && !grads && !adam)
+    return fail(GS_ERR_INVALID_ARGUMENT, "grads is null and no adam update requested");
+  RenderWs ws;
+  if (!render_ws || !render_ws_layout(const_cast<void*>(render_ws), render_ws_bytes, (int)n_tiles(*cam), scene->n, &ws))
+    return fail(GS_ERR_INVALID_ARGUMENT, "render workspace too small or not 256-byte aligned");
+  return run_preprocess_backward(scene, params, cam, nullptr, &ws, proj.tiles, grads, adam, stream,
+                                 "gs_preprocess_backward_staged_next", nullptr, 1.0f, next_cam, &next);
 }
 
 int gs_preprocess_backward_accumulate(const gs_scene* scene, float* params, const gs_camera* cam, gs_proj proj,

@@ -75,7 +75,16 @@ struct PrebwdArgs {
 struct AdamCoef {
   float lr, b1, omb1, b2, omb2, eps, inv_bc1, inv_bc2;
 };
-hipError_t launch_preprocess_backward(const PrebwdArgs& a, const CamK& cam, hipStream_t s);
+// Outputs of the next view's preprocess when it is fused into the preprocess backward (the
+// arrays of gs_proj, typed).
+struct NextOut {
+  float4* splat;
+  uint32_t* tiles;
+  uint32_t* dkey;
+  uint2* rect;
+};
+hipError_t launch_preprocess_backward(const PrebwdArgs& a, const CamK& cam, hipStream_t s,
+                                      const CamK* next_cam = nullptr, const NextOut* next = nullptr);
 
 // binning / sorting
 struct BinLayout {

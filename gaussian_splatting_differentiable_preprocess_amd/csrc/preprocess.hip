@@ -273,18 +273,51 @@ __global__ __launch_bounds__(kBlock) void k_preprocess(int64_t n, int64_t ld,
 // Backward through the per-Gaussian forward, optionally followed by the Adam update of every
 // parameter row of this Gaussian (m, v non-null).  For batched steps each row's gradient is
 // scaled (the batch mean) and added to the gradient accumulated over the batch's earlier views.
-template <int DEG>
-__global__ __launch_bounds__(kBlock) void k_preprocess_backward(PrebwdArgs A, CamK c) {
+//
+// NEXT: the same pass then preprocesses the next view (camera cn) from the rows' new values, as
+// k_preprocess would from the updated parameters, and writes its outputs (nx).
+template <int DEG, bool NEXT>
+__device__ __forceinline__ void prebwd_gaussian(const PrebwdArgs& A, const CamK& c, const CamK& cn,
+                                                const NextOut& nx, int64_t i, float4& r0, float4& r1,
+                                                float4& r2);
+template <int DEG, bool NEXT>
+__global__ __launch_bounds__(kBlock) void k_preprocess_backward(PrebwdArgs A, CamK c, CamK cn, NextOut nx) {
   constexpr int NB = (DEG + 1) * (DEG + 1);
-  const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-  if (i >= A.n) return;
+  const int64_t i0 = (int64_t)blockIdx.x * kBlock;
+  const int64_t i = i0 + threadIdx.x;
+  if constexpr (NEXT) {
+    // the records are staged per workgroup and written out whole, as k_preprocess does
+    __shared__ float4 stage[kBlock * 3];
+    float4 r0 = make_float4(0.f, 0.f, 0.f, 0.f), r1 = r0, r2 = r0;
+    if (i < A.n) prebwd_gaussian<DEG, true>(A, c, cn, nx, i, r0, r1, r2);
+    stage[3 * threadIdx.x + 0] = r0;
+    stage[3 * threadIdx.x + 1] = r1;
+    stage[3 * threadIdx.x + 2] = r2;
+    __syncthreads();
+    const int64_t cnt = (A.n - i0 < kBlock ? A.n - i0 : kBlock) * 3;
+    float4* dst = nx.splat + i0 * 3;
+    for (int e = threadIdx.x; e < cnt; e += kBlock) dst[e] = stage[e];
+  } else {
+    if (i >= A.n) return;
+    float4 r0, r1, r2;
+    prebwd_gaussian<DEG, false>(A, c, cn, nx, i, r0, r1, r2);
+  }
+}
+
+// One Gaussian of k_preprocess_backward; with NEXT, r0..r2 receive its next-view record.
+template <int DEG, bool NEXT>
+__device__ __forceinline__ void prebwd_gaussian(const PrebwdArgs& A, const CamK& c, const CamK& cn,
+                                                const NextOut& nx, int64_t i, float4& r0, float4& r1,
+                                                float4& r2) {
+  constexpr int NB = (DEG + 1) * (DEG + 1);
   const int64_t ld = A.ld;
   float* __restrict__ prm = A.params;
   const bool adam = A.m != nullptr;
   // Row r's gradient goes to grads and/or through Adam as soon as it is known.  Parameters,
   // moments and the updated parameters stream through once: non-temporal loads and stores
   // (measured 8% faster than cached ones).
-  auto finish_row = [&](int r, float gv, float th) {
+  // (returns the row's new value: the parameter itself when there is no Adam update)
+  auto finish_row = [&](int r, float gv, float th) -> float {
     const int64_t e = (int64_t)r * ld + i;
     float gr_ = A.gscale * gv;
     if (A.gacc) gr_ += A.gacc[e];
@@ -294,11 +327,15 @@ __global__ __launch_bounds__(kBlock) void k_preprocess_backward(PrebwdArgs A, Ca
       const float v = A.b2 * __builtin_nontemporal_load(A.v + e) + A.omb2 * gr_ * gr_;
       __builtin_nontemporal_store(m, A.m + e);
       __builtin_nontemporal_store(v, A.v + e);
-      __builtin_nontemporal_store(th - A.lr * (m * A.inv_bc1) / (sqrtf(v * A.inv_bc2) + A.eps), prm + e);
+      const float nth = th - A.lr * (m * A.inv_bc1) / (sqrtf(v * A.inv_bc2) + A.eps);
+      __builtin_nontemporal_store(nth, prm + e);
+      return nth;
     }
+    return th;
   };
 
   float mu[3], ls[3], q[4];
+  float na = 0.f;  // the new logit
   for (int j = 0; j < 3; ++j) mu[j] = __builtin_nontemporal_load(prm + j * ld + i);
   for (int j = 0; j < 3; ++j) ls[j] = __builtin_nontemporal_load(prm + (3 + j) * ld + i);
   for (int j = 0; j < 4; ++j) q[j] = __builtin_nontemporal_load(prm + (6 + j) * ld + i);
@@ -436,7 +473,14 @@ __global__ __launch_bounds__(kBlock) void k_preprocess_backward(PrebwdArgs A, Ca
       const float qd = w * gq[0] + x * gq[1] + y * gq[2] + z * gq[3];
       for (int j = 0; j < 4; ++j) g[6 + j] = (gq[j] - P.qn[j] * qd) * P.inv_qlen;
     }
-    for (int r = 3; r < 11; ++r) finish_row(r, g[r], r < 6 ? ls[r - 3] : (r < 10 ? q[r - 6] : a));
+    for (int r = 3; r < 11; ++r) {
+      const float nv = finish_row(r, g[r], r < 6 ? ls[r - 3] : (r < 10 ? q[r - 6] : a));
+      if constexpr (NEXT) {  // (the old values are not needed past this point)
+        if (r < 6) ls[r - 3] = nv;
+        else if (r < 10) q[r - 6] = nv;
+      }
+      if (r == 10) na = nv;
+    }
   }
 
   float f[NB][3];  // SH coefficients
@@ -471,11 +515,48 @@ __global__ __launch_bounds__(kBlock) void k_preprocess_backward(PrebwdArgs A, Ca
     g[1] += (gdir[1] - d1 * dd) * idist;
     g[2] += (gdir[2] - d2 * dd) * idist;
   }
-  for (int r = 0; r < 3; ++r) finish_row(r, g[r], mu[r]);
+  if constexpr (!NEXT) {
+    for (int r = 0; r < 3; ++r) finish_row(r, g[r], mu[r]);
 #pragma unroll
-  for (int k = 0; k < NB; ++k)
+    for (int k = 0; k < NB; ++k)
 #pragma unroll
-    for (int ch = 0; ch < 3; ++ch) finish_row(11 + 3 * k + ch, vis ? Y[k] * gc[ch] : 0.f, f[k][ch]);
+      for (int ch = 0; ch < 3; ++ch) finish_row(11 + 3 * k + ch, vis ? Y[k] * gc[ch] : 0.f, f[k][ch]);
+  } else {
+    float nmu[3];
+    for (int r = 0; r < 3; ++r) nmu[r] = finish_row(r, g[r], mu[r]);
+    // the next view's preprocess of the new values: the operations of k_preprocess
+    Proj Pn;
+    project_geometry(cn, nmu, ls, q, na, Pn);
+    float Yn[16];
+    if (Pn.vis) {
+      float d0 = nmu[0] - cn.pos[0], d1 = nmu[1] - cn.pos[1], d2 = nmu[2] - cn.pos[2];
+      const float il = 1.0f / sqrtf(d0 * d0 + d1 * d1 + d2 * d2);
+      d0 *= il; d1 *= il; d2 *= il;
+      sh_eval(DEG, d0, d1, d2, Yn);
+    }
+    float rgb[3] = {0.5f, 0.5f, 0.5f};
+#pragma unroll
+    for (int k = 0; k < NB; ++k)
+#pragma unroll
+      for (int ch = 0; ch < 3; ++ch) {
+        const float nf = finish_row(11 + 3 * k + ch, vis ? Y[k] * gc[ch] : 0.f, f[k][ch]);
+        if (Pn.vis) rgb[ch] += Yn[k] * nf;
+      }
+    uint32_t nt = 0, key = 0xFFFFFFFFu;
+    uint2 rc = make_uint2(0u, 0u);
+    r0 = r1 = r2 = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (Pn.vis) {
+      r0 = make_float4(Pn.u, Pn.v, __int_as_float(Pn.rx), __int_as_float(Pn.ry));
+      r1 = make_float4(Pn.Qa, Pn.Qb, Pn.Qc, Pn.o);
+      r2 = make_float4(fmaxf(rgb[0], 0.f), fmaxf(rgb[1], 0.f), fmaxf(rgb[2], 0.f), Pn.z);
+      nt = (uint32_t)Pn.tiles;
+      key = __float_as_uint(Pn.z);
+      rc = make_uint2(Pn.rect_lo, Pn.rect_hi);
+    }
+    nx.tiles[i] = nt;
+    nx.dkey[i] = key;
+    nx.rect[i] = rc;
+  }
 }
 
 }  // namespace
@@ -495,15 +576,24 @@ hipError_t launch_preprocess(const gs_scene& sc, const float* params, const CamK
   return hipGetLastError();
 }
 
-hipError_t launch_preprocess_backward(const PrebwdArgs& a, const CamK& cam, hipStream_t s) {
+hipError_t launch_preprocess_backward(const PrebwdArgs& a, const CamK& cam, hipStream_t s, const CamK* next_cam,
+                                      const NextOut* next) {
   if (a.n == 0) return hipSuccess;
   const unsigned grid = (unsigned)ceil_div(a.n, kBlock);
+  const CamK cn = next_cam ? *next_cam : cam;
+  const NextOut nx = next ? *next : NextOut{};
+#define GSMI_PREBWD(D)                                                                                  \
+  if (next_cam)                                                                                         \
+    hipLaunchKernelGGL((k_preprocess_backward<D, true>), dim3(grid), dim3(kBlock), 0, s, a, cam, cn, nx); \
+  else                                                                                                  \
+    hipLaunchKernelGGL((k_preprocess_backward<D, false>), dim3(grid), dim3(kBlock), 0, s, a, cam, cn, nx);
   switch (a.deg) {
-    case 0: hipLaunchKernelGGL(k_preprocess_backward<0>, dim3(grid), dim3(kBlock), 0, s, a, cam); break;
-    case 1: hipLaunchKernelGGL(k_preprocess_backward<1>, dim3(grid), dim3(kBlock), 0, s, a, cam); break;
-    case 2: hipLaunchKernelGGL(k_preprocess_backward<2>, dim3(grid), dim3(kBlock), 0, s, a, cam); break;
-    default: hipLaunchKernelGGL(k_preprocess_backward<3>, dim3(grid), dim3(kBlock), 0, s, a, cam); break;
+    case 0: GSMI_PREBWD(0); break;
+    case 1: GSMI_PREBWD(1); break;
+    case 2: GSMI_PREBWD(2); break;
+    default: GSMI_PREBWD(3); break;
   }
+#undef GSMI_PREBWD
   return hipGetLastError();
 }
 

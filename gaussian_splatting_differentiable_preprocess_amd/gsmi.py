@@ -29,7 +29,8 @@ EXPORTS = (
     "gs_render_workspace", "gs_render_workspace_capacity", "gs_render_forward", "gs_loss_l1_workspace", "gs_loss_l1",
     "gs_loss_l1_noalloc",
     "gs_loss_l1_dssim_workspace", "gs_loss_l1_dssim", "gs_render_backward",
-    "gs_render_plan", "gs_render_step", "gs_render_init", "gs_render_status", "gs_preprocess_backward", "gs_preprocess_backward_staged", "gs_adam_step",
+    "gs_render_plan", "gs_render_step", "gs_render_init", "gs_render_status", "gs_preprocess_backward", "gs_preprocess_backward_staged",
+    "gs_preprocess_backward_staged_next", "gs_adam_step",
     "gs_preprocess_backward_accumulate", "gs_adam_batch", "gs_densify_stats", "gs_densify_workspace", "gs_densify",
 )
 
@@ -114,6 +115,7 @@ def load(path: str = LIB_PATH):
     L.gs_render_status.argtypes = [P, sz, ctypes.POINTER(ctypes.c_uint32), ctypes.POINTER(i64), P]
     L.gs_preprocess_backward.argtypes = [SP, P, CP, P, P, AP, P]
     L.gs_preprocess_backward_staged.argtypes = [SP, P, CP, GsProj, P, sz, P, AP, P]
+    L.gs_preprocess_backward_staged_next.argtypes = [SP, P, CP, GsProj, P, sz, P, AP, CP, GsProj, P]
     L.gs_adam_step.argtypes = [i64, P, P, AP, P]
     L.gs_preprocess_backward_accumulate.argtypes = [SP, P, CP, GsProj, P, sz, P, i32, ctypes.c_float, AP, P]
     L.gs_adam_batch.argtypes = [AP, i32, AP]
@@ -377,6 +379,16 @@ def preprocess_backward_staged(scene: GsScene, params, cam: GsCamera, proj: Proj
                                                 _ptr(render_ws), _nbytes(render_ws), _ptr(grads),
                                                 ctypes.byref(adam) if adam is not None else None,
                                                 _stream(stream)))
+
+
+def preprocess_backward_staged_next(scene: GsScene, params, cam: GsCamera, proj: Proj, render_ws, next_cam: GsCamera,
+                                    next_proj: Proj, grads=None, adam: GsAdam | None = None, stream=None):
+    """preprocess_backward_staged, then the preprocess of next_cam on the updated parameters into
+    next_proj (which may be proj), in one pass."""
+    _check(load().gs_preprocess_backward_staged_next(ctypes.byref(scene), _ptr(params), ctypes.byref(cam), proj.c(),
+                                                     _ptr(render_ws), _nbytes(render_ws), _ptr(grads),
+                                                     ctypes.byref(adam) if adam is not None else None,
+                                                     ctypes.byref(next_cam), next_proj.c(), _stream(stream)))
 
 
 def preprocess_backward_accumulate(scene: GsScene, params, cam: GsCamera, proj: Proj, render_ws, grads_acc, first,

@@ -387,6 +387,27 @@ int gs_preprocess_backward_staged(const gs_scene* scene, float* params, const gs
                                   const void* render_ws, size_t render_ws_bytes, float* grads,
                                   const gs_adam* adam, hipStream_t stream);
 
+/* gs_preprocess_backward_staged, then gs_preprocess of the next view on the parameters it leaves,
+ * in one pass over the Gaussians: the training iteration of "Scaling 3D Gaussian Splatting with
+ * Distributed Compute" (its trace section: the optimizer step, then the next iteration's
+ * preprocess of the updated Gaussians) with the parameter rows read once instead of twice.  Each
+ * Gaussian's thread finishes its rows (with the Adam update when adam is set, else the rows keep
+ * their values) and projects the new values with next_cam into next: the records, tile counts,
+ * depth keys and rects gs_preprocess(next_cam) writes for the parameters this call leaves, bit
+ * for bit.  Those parameters, moments and grads are gs_preprocess_backward_staged's up to the
+ * rounding of the fused multiply-adds the compiler forms differently in the two kernels (below
+ * 1e-6 of each row's largest value where measured).
+ *   next_cam  the next view's camera (any camera, the same one included)
+ *   next      out: as gs_preprocess's out.  It may be proj itself (each Gaussian reads its own
+ *             proj entries before it writes them); the lists and render_ws of this view must not
+ *             be used with it afterwards.
+ * GS_ERR_INVALID_ARGUMENT as gs_preprocess_backward_staged and as gs_preprocess for next_cam and
+ * next. */
+int gs_preprocess_backward_staged_next(const gs_scene* scene, float* params, const gs_camera* cam, gs_proj proj,
+                                       const void* render_ws, size_t render_ws_bytes, float* grads,
+                                       const gs_adam* adam, const gs_camera* next_cam, gs_proj next,
+                                       hipStream_t stream);
+
 /* Batched steps ("Scaling 3D Gaussian Splatting with Distributed Compute", the batch-size
  * passage: several camera views per optimizer step; the batch's loss is the mean of its views'
  * losses, so its gradient is the mean of theirs).  The preprocess backward of one view of the

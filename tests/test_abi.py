@@ -266,6 +266,22 @@ def test_render_calls_reject_a_missing_or_short_workspace():
     assert rc == gsmi.GS_ERR_INVALID_ARGUMENT and "tiles" in gsmi.last_error()
     rc = L.gs_preprocess_backward_staged(ctypes.byref(sc), p, ctypes.byref(cam), proj, p, need, None, None, None)
     assert rc == gsmi.GS_ERR_INVALID_ARGUMENT and "grads" in gsmi.last_error()
+    # the same with the next view's preprocess fused in: also the next camera and outputs
+    nxt = gsmi.GsCamera()
+    ctypes.pointer(nxt)[0] = cam
+    rc = L.gs_preprocess_backward_staged_next(ctypes.byref(sc), p, ctypes.byref(cam), proj, p, 16, None,
+                                              ctypes.byref(ad), ctypes.byref(nxt), proj, None)
+    assert rc == gsmi.GS_ERR_INVALID_ARGUMENT and "workspace" in gsmi.last_error()
+    rc = L.gs_preprocess_backward_staged_next(ctypes.byref(sc), p, ctypes.byref(cam), proj, p, need, None,
+                                              ctypes.byref(ad), None, proj, None)
+    assert rc == gsmi.GS_ERR_INVALID_ARGUMENT
+    rc = L.gs_preprocess_backward_staged_next(ctypes.byref(sc), p, ctypes.byref(cam), proj, p, need, None,
+                                              ctypes.byref(ad), ctypes.byref(nxt), gsmi.GsProj(4096, 4096, None, 4096),
+                                              None)
+    assert rc == gsmi.GS_ERR_INVALID_ARGUMENT and "depth_key" in gsmi.last_error()
+    rc = L.gs_preprocess_backward_staged_next(ctypes.byref(sc), p, ctypes.byref(cam), proj, p, need, None,
+                                              None, ctypes.byref(nxt), proj, None)
+    assert rc == gsmi.GS_ERR_INVALID_ARGUMENT and "grads" in gsmi.last_error()
 
 
 def test_fused_step_checks_its_arguments():

@@ -282,6 +282,81 @@ def test_fused_adam_matches_separate_adam(name):
         assert rel_l2(a, b) <= 1e-5
 
 
+def _next_camera(cam, W, H):
+    """The camera 20 degrees further round the z axis from `cam`'s position, looking at the origin."""
+    Rm = np.asarray(cam.viewmat, np.float64)[:, :3]
+    pos = -Rm.T @ np.asarray(cam.viewmat, np.float64)[:, 3]
+    a = np.deg2rad(20.0)
+    rz = np.array([[np.cos(a), -np.sin(a), 0.0], [np.sin(a), np.cos(a), 0.0], [0.0, 0.0, 1.0]])
+    return inputs.lookat_camera(rz @ pos, W, H)
+
+
+def _row_rel(a, b):
+    """Largest difference between two [R][n] arrays, per row relative to that row's largest
+    magnitude (rows of zeros compare absolutely)."""
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    scale = np.maximum(np.abs(a).max(axis=1, keepdims=True), 1e-30)
+    return float((np.abs(a - b) / scale).max()) if a.size else 0.0
+
+
+@pytest.mark.parametrize("name", ["tiny_ragged_d1", "tiny_odd_d2", "tiny_d3", "sphere_16k_256", "torus_262k_512_v0"])
+def test_backward_then_next_preprocess_in_one_pass(name):
+    """gs_preprocess_backward_staged_next: its parameters, moments and gradients are those of
+    gs_preprocess_backward_staged (to the rounding by which the two compiled kernels' fused
+    multiply-adds may differ: 1e-5 of each row's largest value), and the next view's records, tile
+    counts, depth keys and rects are gs_preprocess's of the parameters it leaves, bit for bit,
+    with and without the Adam update, also when they overwrite this view's in place."""
+    import torch
+    d = data(name)
+    say(f"[parity] test_backward_then_next_preprocess {name}")
+    params, deg, cam, W, H = d["params"], d["deg"], d["cam"], d["W"], d["H"]
+    R, n = params.shape
+    ncam = gsmi.make_camera(_next_camera(cam, W, H))
+    for with_adam in (True, False):
+        outs, nexts = [], []
+        for mode in ("separate", "fused", "in_place"):
+            g = GpuStep(params, deg, cam, W, H)
+            g.preprocess()
+            g.bin_and_sort()
+            g.forward(BG)
+            if d["target"] is not None:
+                g.loss(d["target"])
+            else:
+                g.set_upstream(d["upstream"])
+            gsmi.render_backward(g.scene, None, g.cam, g.proj, g.vals, g.ranges, BG, g.T_final, g.last, g.dLdI,
+                                 None, g.render_ws, k=g.K)
+            m = torch.full((R, n), 0.01, dtype=torch.float32, device="cuda")
+            v = torch.full((R, n), 0.02, dtype=torch.float32, device="cuda")
+            adam = gsmi.make_adam(m, v, 3, 1e-3) if with_adam else None
+            grads = None if with_adam else torch.empty((R, n), dtype=torch.float32, device="cuda")
+            if mode == "separate":
+                gsmi.preprocess_backward_staged(g.scene, g.params, g.cam, g.proj, g.render_ws, grads, adam)
+            else:
+                nxt = gsmi.alloc_proj(n) if mode == "fused" else g.proj
+                gsmi.preprocess_backward_staged_next(g.scene, g.params, g.cam, g.proj, g.render_ws, ncam, nxt,
+                                                     grads, adam)
+                ref = gsmi.alloc_proj(n)  # the plain preprocess of the parameters the call left
+                gsmi.preprocess(g.scene, g.params, ncam, ref)
+                torch.cuda.synchronize()
+                nexts.append([(x.cpu().numpy()[:n], y.cpu().numpy()[:n]) for x, y in
+                              ((nxt.splat, ref.splat), (nxt.tiles, ref.tiles), (nxt.depth_key, ref.depth_key),
+                               (nxt.rect, ref.rect))])
+            torch.cuda.synchronize()
+            outs.append([x.cpu().numpy() for x in [g.params, m, v] + ([] if with_adam else [grads])])
+        for o in outs[1:]:
+            u = max(_row_rel(a_, b_) for a_, b_ in zip(outs[0], o))
+            say(f"[parity]   adam={with_adam}: parameters, moments{'' if with_adam else ', gradients'} within {u:.2g} "
+                f"of each row's largest value")
+            assert u <= 1e-5
+        for nx in nexts:
+            vis = int((nx[1][0] != 0).sum())
+            assert vis > 0
+            for k, (a_, b_) in enumerate(nx):
+                assert np.array_equal(np.ascontiguousarray(a_).view(np.uint8), np.ascontiguousarray(b_).view(np.uint8)), k
+        say(f"[parity]   adam={with_adam}: the next view's outputs equal gs_preprocess's, {vis} of {n} visible")
+
+
 @pytest.mark.parametrize("name", ["tiny_odd_d2", "torus_262k_512_v0"])
 def test_staged_sums_match_grad2d(name):
     """The preprocess backward reading the staged per-intersection sums equals the one reading
