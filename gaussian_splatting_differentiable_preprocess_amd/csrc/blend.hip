@@ -1600,7 +1600,7 @@ size_t layout_bytes(int T, int64_t n, uint64_t k) {
          round256(8 * ((size_t)T + slots)) + round256(kSlotBytes * slots) + kMaskChunkBytes * chunks +
          split_bytes(T, k) + round256(36 * (size_t)k + 16);
 }
-// per 256 entries of capacity, at least (the split tiles' arrays grow in larger steps)
+// per segment (512 entries) of capacity, at least (the split tiles' arrays grow in larger steps)
 constexpr size_t kBytesPerSeg = kSlotBytes + 8 + (kSegEntries / kChunk) * kMaskChunkBytes + 36 * kSegEntries;
 
 }  // namespace
@@ -1613,10 +1613,10 @@ size_t render_ws_bytes(int T, int64_t n, int64_t k_capacity) {
 bool render_ws_layout(void* ws, size_t bytes, int T, int64_t n, RenderWs* out) {
   const size_t base = layout_bytes(T, n, 0);
   if (!ws || bytes < base || (reinterpret_cast<uintptr_t>(ws) & 255u)) return false;
-  // 256 more entries of capacity cost at least kBytesPerSeg - 8 bytes (the item array may not
+  // a segment more of capacity costs at least kBytesPerSeg - 8 bytes (the item array may not
   // grow by a whole 256-byte step), so hi is an upper bound; bisect for the largest fit (the
   // layout grows with k)
-  uint64_t lo = 0, hi = (bytes - base) / (kBytesPerSeg - 8);  // in units of 256 entries
+  uint64_t lo = 0, hi = (bytes - base) / (kBytesPerSeg - 8);  // in units of segments
   while (lo < hi) {
     const uint64_t mid = lo + (hi - lo + 1) / 2;
     if (layout_bytes(T, n, mid * kSegEntries) <= bytes) lo = mid; else hi = mid - 1;

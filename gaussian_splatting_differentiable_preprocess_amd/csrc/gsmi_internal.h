@@ -111,7 +111,7 @@ hipError_t launch_bin_sort(int64_t n, int64_t kcap, const CamK& cam, gs_proj pro
 // blending
 //
 // Render workspace.  The forward leaves in it what the backward needs to walk long tile lists
-// back in parallel segments: a tile list longer than one segment (256 entries, or a larger
+// back in parallel segments: a tile list longer than one segment (512 entries, or a larger
 // power of two when the workspace is short) gets one state slot per segment boundary plus one
 // for its final state; a slot holds (T, C_r, C_g, C_b) for the tile's 256 pixels.  The
 // backward gathers each list entry's nine gradient sums in `staging`, grouped by Gaussian
@@ -148,10 +148,10 @@ hipError_t launch_bin_sort(int64_t n, int64_t kcap, const CamK& cam, gs_proj pro
 //   fin[][256]      per forward segment and pixel: (T, C) in front of the segment
 //   pstate[][256]   per split tile and pixel: (stop segment or a marker, last, composited,
 //                   evaluated in front)
-constexpr int kSegShiftMin = 8;  // 256 list entries per segment
-constexpr int kFsegLog = 3;      // the shortest forward segment is 2^kFsegLog backward segments
-constexpr int kSplitLog = 8;     // lists of at least 2^(shift + kSplitLog) entries are split
-constexpr int kPhase1Log = 5;    // ... after a first part of 2^(shift + kPhase1Log) entries walked whole
+constexpr int kSegShiftMin = 9;  // 512 list entries per segment
+constexpr int kFsegLog = 2;      // the shortest forward segment is 2^kFsegLog backward segments
+constexpr int kSplitLog = 7;     // lists of at least 2^(shift + kSplitLog) entries are split
+constexpr int kPhase1Log = 4;    // ... after a first part of 2^(shift + kPhase1Log) entries walked whole
 constexpr uint32_t kMaxSplit = 1024;  // split tiles at most (one workgroup plans them)
 constexpr uint32_t kNoSplit = 0xFFFFFFFFu;
 constexpr uint32_t kFbaseMask = (1u << 27) - 1u;

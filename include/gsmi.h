@@ -191,7 +191,7 @@ int gs_bin_and_sort_count(const void* workspace, size_t workspace_bytes, int64_t
 
 /* Bytes of the render workspace that gs_render_forward fills and gs_render_backward uses, for
  * a width x height image, n Gaussians and lists of up to k_capacity intersections (host-only
- * query).  It holds, for every tile list longer than one segment (256 entries), each pixel's
+ * query).  It holds, for every tile list longer than one segment (512 entries), each pixel's
  * transmittance and colour at every segment boundary and at the end of its walk, plus the
  * backward's work list: the backward walks the segments of a long list in parallel from these
  * states.  For every 64 entries of a tile list and pixel of the tile it holds the 64-bit mask
@@ -202,7 +202,7 @@ int gs_bin_and_sort_count(const void* workspace, size_t workspace_bytes, int64_t
 int gs_render_workspace(int32_t width, int32_t height, int64_t n, int64_t k_capacity, size_t* bytes);
 
 /* The largest intersection count a render workspace of `bytes` serves for this image and n
- * (host-only query; the inverse of gs_render_workspace, rounded to whole 256-entry segments).
+ * (host-only query; the inverse of gs_render_workspace, rounded to whole 512-entry segments).
  * GS_ERR_INVALID_ARGUMENT if `bytes` is below the size for k_capacity 0. */
 int gs_render_workspace_capacity(int32_t width, int32_t height, int64_t n, size_t bytes,
                                  int64_t* k_capacity);

@@ -97,29 +97,29 @@ def test_workspace_queries():
     assert gsmi.loss_l1_workspace(3 * 2048 * 2048) >= 4 * (3 * 2048 * 2048) // 4096
     with pytest.raises(gsmi.GsError):
         gsmi.bin_and_sort_workspace(-1, 0, 16, 16)
-    # render workspace: a fixed part for the tiles and Gaussians plus, per 256 intersections of
-    # capacity, one 4 KiB state slot, one work item, four 2 KiB chunks of composited masks (8
-    # bytes per pixel of a tile per 64 entries) and 256 staged 36-byte gradient sums; and for
+    # render workspace: a fixed part for the tiles and Gaussians plus, per 512 intersections of
+    # capacity, one 4 KiB state slot, one work item, eight 2 KiB chunks of composited masks (8
+    # bytes per pixel of a tile per 64 entries) and 512 staged 36-byte gradient sums; and for
     # the split tiles (lists of at least 65536 entries, in forward segments of at least 2048),
     # per forward segment three 4 KiB per-pixel arrays and an item, and per split tile 4 KiB of
     # pixel state and 20 bytes
     r0 = gsmi.render_workspace(2048, 2048, 4_000_000, 0)
-    k = 256 * 1000
+    k = 512 * 1000
     r1 = gsmi.render_workspace(2048, 2048, 4_000_000, k)
     fsegs = k // 2048 + k // 65536  # (the fixed part holds 2 segments and 1 split tile)
     splits = k // 65536
-    expect = 1000 * (4096 + 8 + 4 * 2048 + 256 * 36) + fsegs * (3 * 4096 + 8) + splits * (16 * 256 + 20)
+    expect = 1000 * (4096 + 8 + 8 * 2048 + 512 * 36) + fsegs * (3 * 4096 + 8) + splits * (16 * 256 + 20)
     assert abs((r1 - r0) - expect) <= 6 * 256, (r1 - r0, expect)
     assert r0 >= 16384 * (4096 + 8 + 2048 + 4) + 4 * 4_000_000
     with pytest.raises(gsmi.GsError):
         gsmi.render_workspace(0, 16, 10, 10)
     # the capacity query inverts the size query: never below the capacity asked for, and no
-    # more than one 256-entry segment above it
+    # more than one 512-entry segment above it
     for W, H in ((17, 33), (64, 64), (1024, 1024), (2048, 2048)):
         for n in (1, 120, 3000, 262144, 4_000_000):
             for k in (0, 1, 255, 256, 257, 12_345, 6_800_000, 10_300_000):
                 got = gsmi.render_workspace_capacity(W, H, n, gsmi.render_workspace(W, H, n, k))
-                assert k <= got < k + 512, (W, H, n, k, got)
+                assert k <= got < k + 1024, (W, H, n, k, got)
     with pytest.raises(gsmi.GsError):
         gsmi.render_workspace_capacity(64, 64, 10, 100)
 

@@ -722,7 +722,7 @@ def test_repeatable_forward_and_sort():
 
 
 def test_long_lists_with_stops_in_many_segments():
-    """Tile lists of 6000 entries (24 segments of 256) with opacities spread so that pixels stop
+    """Tile lists of 6000 entries (12 segments of 512) with opacities spread so that pixels stop
     in many different segments and some never stop: the forward's segment-boundary states and
     composited masks, and the backward's segments started from them, are exercised at every
     depth.  Forward outputs (image, T, last_contrib, n_examined) and the backward blend are
@@ -733,7 +733,7 @@ def test_long_lists_with_stops_in_many_segments():
     params = inputs.small_scene(37, n, 0, logscale_mean=-0.8, logscale_std=0.2, radius=0.1)
     rng = np.random.default_rng(38)
     params[10] = rng.uniform(-6.0, -4.0, n).astype(np.float32)  # opacity 0.0025 .. 0.018
-    # (on these inputs about 16% of the pixels stop, in segments 5 to 23 of 24)
+    # (on these inputs about 16% of the pixels stop, in 256-entry stretches 5 to 23 of 24)
     cam = inputs.lookat_camera((3.0, 0.0, 0.0), W, W)
     up = np.random.default_rng(6).uniform(-1, 1, (W, W, 3)).astype(np.float32)
     o = oracle_pipeline(params, 0, cam.flat(), W, W, BG, upstream=up, margins=FWD_MARGINS)
@@ -748,7 +748,7 @@ def test_long_lists_with_stops_in_many_segments():
     g.load_lists(o["vals"], o["ranges"])
     fwd = g.forward(BG)
     hdr = g.render_ws[:64].cpu().numpy().view(np.uint32)
-    assert hdr[0] == 8, hdr[:4]  # 256-entry segments
+    assert hdr[0] == 9, hdr[:4]  # 512-entry segments
     ok = ~of["borderline"]
     assert ok.mean() > 0.9
     assert np.abs(fwd["image"] - of["image"]).max(axis=-1)[ok].max() <= IMG_MAX_ABS
@@ -765,7 +765,7 @@ def test_long_lists_with_stops_in_many_segments():
 
 
 def test_backward_segments_on_deep_lists():
-    """Tile lists of ~3000 entries with low opacity: pixels walk back across several 256-entry
+    """Tile lists of ~3000 entries with low opacity: pixels walk back across several 512-entry
     segments, which the backward runs in parallel from the forward's boundary states.  The GPU
     forward and backward run on the oracle's records and lists; a second backward from the same
     forward gives the same result."""
@@ -789,7 +789,7 @@ def test_backward_segments_on_deep_lists():
     g.set_upstream(o["dl32"])
     g2_seg, _ = g.backward()
     hdr = g.render_ws[:64].cpu().numpy().view(np.uint32)
-    assert hdr[0] == 8 and hdr[1] > 8, hdr[:4]  # 256-entry segments, several items per long tile
+    assert hdr[0] == 9 and hdr[1] > 8, hdr[:4]  # 512-entry segments, several items per long tile
     assert hdr[4] == K, (hdr[4], K)  # the staged intersections
     for r in range(9):
         assert rel_l2(g2_seg[r, :n], o["grad2d"][r]) <= GRAD_REL_L2, (r, rel_l2(g2_seg[r, :n], o["grad2d"][r]))
