@@ -122,12 +122,12 @@ KERNEL_OF = {"preprocess": ("k_preprocess<3>", "hbm"), "image_pass": ("k_blend_s
 # size; keyed by the SHA-256 of the kernel's source file, so a changed kernel (or another
 # workload) reports null
 COUNTER_TRAFFIC = {
-    "preprocess": {"source": "preprocess.hip", "bytes": 1200081816,
-                   "sha256": "bdf2d6b2bfda6bd9c4ee0579c394aa49af9704b4d3f8a784a63a7e38fb911657"},
-    "image_pass": {"source": "blend.hip", "bytes": 6899480381,
-                   "sha256": "eb2bea5cd7565a1cf46e13684dc26246875337517aaf555c1157bfdf9fad625c"},
-    "prebwd_adam": {"source": "preprocess.hip", "bytes": 5943374354,
-                    "sha256": "bdf2d6b2bfda6bd9c4ee0579c394aa49af9704b4d3f8a784a63a7e38fb911657"},
+    "preprocess": {"source": "preprocess.hip", "bytes": 1200081832,
+                   "sha256": "4e38a63d590fe1fccf49a3783d5f7532613f1d608023e9c1205edd04d4c806a6"},
+    "image_pass": {"source": "blend.hip", "bytes": 6739011144,
+                   "sha256": "68654025237fa93927d67fd1c8f920c01fbb96d229ac13f019d32e98d54f4fb7"},
+    "prebwd_adam_next": {"source": "preprocess.hip", "bytes": 6199430657,
+                         "sha256": "4e38a63d590fe1fccf49a3783d5f7532613f1d608023e9c1205edd04d4c806a6"},
 }
 
 
@@ -136,8 +136,8 @@ COUNTER_TRAFFIC = {
 # launch's time (one wave64 VALU instruction per SIMD per 4 cycles at 2.4 GHz), the issue rate
 # that bounds the kernel, box and mask arithmetic included
 COUNTER_VALU = {
-    "image_pass": {"source": "blend.hip", "insts": 649.2e6,
-                   "sha256": "eb2bea5cd7565a1cf46e13684dc26246875337517aaf555c1157bfdf9fad625c"},
+    "image_pass": {"source": "blend.hip", "insts": 643.7e6,
+                   "sha256": "68654025237fa93927d67fd1c8f920c01fbb96d229ac13f019d32e98d54f4fb7"},
 }
 VALU_ISSUE_PER_S = 256 * 4 * 2.4e9 / 4  # wave64 VALU instructions per second, all SIMDs
 
