@@ -357,6 +357,55 @@ def test_backward_then_next_preprocess_in_one_pass(name):
         say(f"[parity]   adam={with_adam}: the next view's outputs equal gs_preprocess's, {vis} of {n} visible")
 
 
+def test_staged_rows_of_an_earlier_step_do_not_count():
+    """Fused steps on one render workspace, view after view: each view's gradients equal those of
+    the same view on a fresh workspace (to the rounding of the backward's float sums, whose order
+    varies between runs: 1e-5 of each row's largest value).  Rows an earlier view's backward staged
+    and a later one's does not overwrite must not count: read as sums they would be off by whole
+    gradients."""
+    import torch
+    cfg = inputs.CONFIGS["torus_262k_512"]
+    params = inputs.gaussian_params(cfg)
+    cams = inputs.cameras_for(cfg)
+    W = H = 512
+    R, n = params.shape
+    scene = gsmi.make_scene(n, n, 3)
+    p = to_t_f32(params)
+    proj = gsmi.alloc_proj(n)
+    target = to_t_f32(np.random.default_rng(3).uniform(0, 1, (H, W, 3)))
+    kcap = 4 << 20
+    vals = torch.empty(kcap, dtype=torch.int32, device="cuda")
+    ranges = torch.empty((gsmi.n_tiles(W, H), 2), dtype=torch.int32, device="cuda")
+    sws = torch.empty(gsmi.bin_and_sort_workspace(n, kcap, W, H), dtype=torch.uint8, device="cuda")
+    image = torch.empty((H, W, 3), device="cuda")
+    T_final = torch.empty((H, W), device="cuda")
+    last = torch.empty((H, W), dtype=torch.int32, device="cuda")
+    dLdI = torch.empty((H, W, 3), device="cuda")
+    loss = torch.zeros(1, device="cuda")
+
+    def grads_of(view, rws):
+        cam = gsmi.make_camera(cams[view])
+        gsmi.preprocess(scene, p, cam, proj)
+        K = gsmi.bin_and_sort(scene, cam, proj, sws, kcap, vals, ranges)
+        gsmi.render_plan(scene, cam, proj, ranges, rws, k=K)
+        gsmi.render_step(scene, cam, proj, vals, ranges, BG, target, image, T_final, last, loss, dLdI, rws, k=K)
+        grads = torch.empty((R, n), device="cuda")
+        gsmi.preprocess_backward_staged(scene, p, cam, proj, rws, grads)
+        assert gsmi.render_status(rws, raise_error=False)[0] == 0
+        return grads.cpu().numpy(), K
+
+    say("[parity] test_staged_rows_of_an_earlier_step_do_not_count")
+    shared = gsmi.new_render_ws(W, H, n, kcap)
+    views = (0, 3, 1)  # the middle view stages more rows than the last
+    got = [grads_of(v, shared) for v in views]
+    for v, (g, K) in zip(views, got):
+        fresh, K2 = grads_of(v, gsmi.new_render_ws(W, H, n, kcap))
+        assert K == K2
+        d = _row_rel(g, fresh)
+        say(f"[parity]   view {v}: K {K}, gradients within {d:.2g} of a fresh workspace's")
+        assert d <= 1e-5, (v, d)
+
+
 @pytest.mark.parametrize("name", ["tiny_odd_d2", "torus_262k_512_v0"])
 def test_staged_sums_match_grad2d(name):
     """The preprocess backward reading the staged per-intersection sums equals the one reading
