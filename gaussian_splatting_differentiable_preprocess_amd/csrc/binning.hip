@@ -57,6 +57,33 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, uint32_t* tmp, u
   return wpre + incl - x;
 }
 
+// A thread's run c[lo..hi) of block counts, read kRunBatch at a time so that a batch's loads
+// are in flight together: the sum, and the in-place exclusive scan starting at `run`.
+constexpr int kRunBatch = 16;
+__device__ __forceinline__ uint32_t run_sum(const uint32_t* c, int64_t lo, int64_t hi) {
+  uint32_t s = 0;
+  for (int64_t b = lo; b < hi; b += kRunBatch) {
+    uint32_t x[kRunBatch];
+#pragma unroll
+    for (int q = 0; q < kRunBatch; ++q) x[q] = b + q < hi ? c[b + q] : 0u;
+#pragma unroll
+    for (int q = 0; q < kRunBatch; ++q) s += x[q];
+  }
+  return s;
+}
+__device__ __forceinline__ void run_excl_scan(uint32_t* c, int64_t lo, int64_t hi, uint32_t run) {
+  for (int64_t b = lo; b < hi; b += kRunBatch) {
+    uint32_t x[kRunBatch];
+#pragma unroll
+    for (int q = 0; q < kRunBatch; ++q) x[q] = b + q < hi ? c[b + q] : 0u;
+#pragma unroll
+    for (int q = 0; q < kRunBatch; ++q) {
+      if (b + q < hi) c[b + q] = run;
+      run += x[q];
+    }
+  }
+}
+
 // ---- reduction: K and the depth-key range over visible Gaussians -----------------------
 struct Partial {
   unsigned long long sum;
@@ -200,13 +227,16 @@ __global__ __launch_bounds__(kBlock) void k_radix_hist(const uint32_t* __restric
   __syncthreads();
   const int64_t base = (int64_t)blockIdx.x * kRadixTile;
   const int w = wave_id();
-#pragma unroll 4
+  uint32_t kk[kItems];
+#pragma unroll
+  for (int j = 0; j < kItems; ++j) {  // every load in flight before the first atomic
+    const int64_t idx = base + j * kBlock + threadIdx.x;
+    kk[j] = idx < n ? keys[idx] : 0u;
+  }
+#pragma unroll
   for (int j = 0; j < kItems; ++j) {
     const int64_t idx = base + j * kBlock + threadIdx.x;
-    if (idx < n) {
-      const uint32_t k = xform_key(keys[idx], xform != 0, in);
-      atomicAdd(&hist[w][(k >> shift) & 255u], 1u);
-    }
+    if (idx < n) atomicAdd(&hist[w][(xform_key(kk[j], xform != 0, in) >> shift) & 255u], 1u);
   }
   __syncthreads();
   const int d = threadIdx.x;
@@ -222,15 +252,9 @@ __global__ __launch_bounds__(kBlock) void k_radix_scan(const BinInfo* __restrict
   uint32_t* c = counts + (int64_t)blockIdx.x * nblk;
   const int64_t per = ceil_div(nblk, kBlock);
   const int64_t lo = threadIdx.x * per, hi = min(lo + per, nblk);
-  uint32_t s = 0;
-  for (int64_t b = lo; b < hi; ++b) s += c[b];
+  uint32_t s = run_sum(c, lo, hi);
   uint32_t tot;
-  uint32_t run = block_excl_scan(s, tmp, &tot);
-  for (int64_t b = lo; b < hi; ++b) {
-    const uint32_t x = c[b];
-    c[b] = run;
-    run += x;
-  }
+  run_excl_scan(c, lo, hi, block_excl_scan(s, tmp, &tot));
   if (threadIdx.x == 0) totals[blockIdx.x] = tot;
 }
 
@@ -277,15 +301,21 @@ __global__ __launch_bounds__(kBlock) void k_radix_scatter(
   uint32_t mk[kItems], mv[kItems], mr[kItems];
   const unsigned long long lt = __lanemask_lt();
   const int64_t wbase = base + (int64_t)w * (kItems * 64);
+  // every load in flight before the ranking: the ranking's LDS fences would otherwise hold each
+  // round's loads back until the round before had finished
 #pragma unroll
   for (int r = 0; r < kItems; ++r) {
     const int64_t idx = wbase + r * 64 + lane;
     const bool valid = idx < n;
-    uint32_t k = 0, v = 0;
-    if (valid) {
-      k = xform_key(keys_in[idx], xform != 0, in);
-      v = vals_in ? vals_in[idx] : (uint32_t)idx;
-    }
+    mk[r] = valid ? keys_in[idx] : 0u;
+    mv[r] = valid ? (vals_in ? vals_in[idx] : (uint32_t)idx) : 0u;
+  }
+#pragma unroll
+  for (int r = 0; r < kItems; ++r) {
+    const int64_t idx = wbase + r * 64 + lane;
+    const bool valid = idx < n;
+    const uint32_t k = valid ? xform_key(mk[r], xform != 0, in) : 0u;
+    const uint32_t v = mv[r];
     const uint32_t d = (k >> shift) & 255u;
     // lanes of this wave holding the same digit
     unsigned long long peers = __ballot(valid);
@@ -389,8 +419,7 @@ __global__ __launch_bounds__(1024) void k_scan_blocks(const BinInfo* __restrict_
   if (!sort_live(*info)) return;
   const int64_t per = ceil_div(nblk, 1024);
   const int64_t lo = threadIdx.x * per, hi = min(lo + per, nblk);
-  uint32_t s = 0;
-  for (int64_t b = lo; b < hi; ++b) s += bsum[b];
+  const uint32_t s = run_sum(bsum, lo, hi);
   part[threadIdx.x] = s;
   __syncthreads();
   for (int o = 1; o < 1024; o <<= 1) {
@@ -399,12 +428,7 @@ __global__ __launch_bounds__(1024) void k_scan_blocks(const BinInfo* __restrict_
     part[threadIdx.x] += y;
     __syncthreads();
   }
-  uint32_t run = part[threadIdx.x] - s;
-  for (int64_t b = lo; b < hi; ++b) {
-    const uint32_t x = bsum[b];
-    bsum[b] = run;
-    run += x;
-  }
+  run_excl_scan(bsum, lo, hi, part[threadIdx.x] - s);
 }
 
 // Writes the intersections of Gaussians order[k] (in depth order) at their scanned slots:
@@ -450,18 +474,37 @@ __global__ __launch_bounds__(kBlock) void k_keygen(const BinInfo* __restrict__ i
   }
 }
 
-// ranges[2t], ranges[2t+1] = first and one-past-last position of tile t.
+// ranges[2t], ranges[2t+1] = first and one-past-last position of tile t.  Each thread looks at
+// kRangeItems consecutive sorted keys (one 16-byte load) and the key on either side of them.
+constexpr int kRangeItems = 4;
 __global__ __launch_bounds__(kBlock) void k_ranges(const uint32_t* __restrict__ tk, const BinInfo* __restrict__ info,
                                                     uint32_t T, uint32_t* __restrict__ ranges) {
   const BinInfo in = *info;
   if (!sort_live(in)) return;
   const int64_t K = (int64_t)in.K;
-  const int64_t j = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-  if (j >= K) return;
-  const uint32_t t = tk[j];
-  if (t >= T) return;
-  if (j == 0 || tk[j - 1] != t) ranges[2 * (int64_t)t] = (uint32_t)j;
-  if (j == K - 1 || tk[j + 1] != t) ranges[2 * (int64_t)t + 1] = (uint32_t)(j + 1);
+  const int64_t j0 = ((int64_t)blockIdx.x * kBlock + threadIdx.x) * kRangeItems;
+  if (j0 >= K) return;
+  uint32_t t[kRangeItems + 2];  // t[1 + q] = tk[j0 + q]; t[0], t[kRangeItems + 1] the neighbours
+  if (j0 + kRangeItems <= K) {  // tk is 256-byte aligned and j0 a multiple of 4: an aligned uint4
+    const uint4 v = *reinterpret_cast<const uint4*>(tk + j0);
+    t[1] = v.x;
+    t[2] = v.y;
+    t[3] = v.z;
+    t[4] = v.w;
+  } else {
+#pragma unroll
+    for (int q = 0; q < kRangeItems; ++q) t[1 + q] = j0 + q < K ? tk[j0 + q] : 0xFFFFFFFFu;
+  }
+  t[0] = j0 > 0 ? tk[j0 - 1] : 0xFFFFFFFFu;
+  t[kRangeItems + 1] = j0 + kRangeItems < K ? tk[j0 + kRangeItems] : 0xFFFFFFFFu;
+#pragma unroll
+  for (int q = 0; q < kRangeItems; ++q) {
+    const int64_t j = j0 + q;
+    const uint32_t c = t[1 + q];
+    if (j >= K || c >= T) continue;
+    if (j == 0 || t[q] != c) ranges[2 * (int64_t)c] = (uint32_t)j;
+    if (j == K - 1 || t[2 + q] != c) ranges[2 * (int64_t)c + 1] = (uint32_t)(j + 1);
+  }
 }
 
 __global__ __launch_bounds__(kBlock) void k_keys64(const uint32_t* __restrict__ tk, const BinInfo* __restrict__ info,
@@ -595,7 +638,8 @@ hipError_t launch_bin_sort(int64_t n, int64_t kcap, const CamK& cam, gs_proj pro
 
   // 4. per-tile ranges and the optional 64-bit keys
   const unsigned gk = (unsigned)ceil_div(kcap, kBlock);
-  hipLaunchKernelGGL(k_ranges, dim3(gk), dim3(kBlock), 0, s, tsorted, info, (uint32_t)T, ranges);
+  hipLaunchKernelGGL(k_ranges, dim3((unsigned)ceil_div(kcap, (int64_t)kBlock * kRangeItems)), dim3(kBlock), 0, s,
+                     tsorted, info, (uint32_t)T, ranges);
   if (keys)
     hipLaunchKernelGGL(k_keys64, dim3(gk), dim3(kBlock), 0, s, tsorted, info, (const uint32_t*)vals,
                        (const uint32_t*)proj.depth_key, n, keys);

@@ -49,8 +49,16 @@ __global__ __launch_bounds__(kBlock) void k_loss_l1(int64_t count, const float* 
 __global__ __launch_bounds__(1024) void k_loss_final(int64_t nblk, const float* __restrict__ part,
                                                      double inv_n, float* __restrict__ loss) {
   __shared__ double s[16];
+  constexpr int kBatch = 16;  // a batch's loads in flight together; the adds keep the order b, b + 1024, ...
   double acc = 0.0;
-  for (int64_t b = threadIdx.x; b < nblk; b += 1024) acc += (double)part[b];
+  for (int64_t b0 = threadIdx.x; b0 < nblk; b0 += 1024 * kBatch) {
+    float x[kBatch];
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) x[q] = part[std::min<int64_t>(b0 + 1024 * q, nblk - 1)];
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q)
+      if (b0 + 1024 * q < nblk) acc += (double)x[q];
+  }
   for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
   if ((threadIdx.x & 63) == 0) s[threadIdx.x >> 6] = acc;
   __syncthreads();

@@ -315,16 +315,31 @@ __device__ __forceinline__ void prebwd_gaussian(const PrebwdArgs& A, const CamK&
   const bool adam = A.m != nullptr;
   // Row r's gradient goes to grads and/or through Adam as soon as it is known.  Parameters,
   // moments and the updated parameters stream through once: non-temporal loads and stores
-  // (measured 8% faster than cached ones).
-  // (returns the row's new value: the parameter itself when there is no Adam update)
-  auto finish_row = [&](int r, float gv, float th) -> float {
+  // (measured 8% faster than cached ones).  A row's inputs (its moments, and the running sum in
+  // accumulate mode) are loaded by row_in ahead of finish_row, several rows at a time: the
+  // stores of one row would otherwise keep the next row's loads from issuing before them.
+  // (finish_row returns the row's new value: the parameter itself when there is no Adam update)
+  struct RowIn {
+    float m, v, ga;
+  };
+  auto row_in = [&](int r) -> RowIn {
+    const int64_t e = (int64_t)r * ld + i;
+    RowIn o{0.f, 0.f, 0.f};
+    if (A.gacc) o.ga = A.gacc[e];
+    if (adam) {
+      o.m = __builtin_nontemporal_load(A.m + e);
+      o.v = __builtin_nontemporal_load(A.v + e);
+    }
+    return o;
+  };
+  auto finish_row = [&](int r, float gv, float th, const RowIn& in) -> float {
     const int64_t e = (int64_t)r * ld + i;
     float gr_ = A.gscale * gv;
-    if (A.gacc) gr_ += A.gacc[e];
+    if (A.gacc) gr_ += in.ga;
     if (A.grads) A.grads[e] = gr_;
     if (adam) {
-      const float m = A.b1 * __builtin_nontemporal_load(A.m + e) + A.omb1 * gr_;
-      const float v = A.b2 * __builtin_nontemporal_load(A.v + e) + A.omb2 * gr_ * gr_;
+      const float m = A.b1 * in.m + A.omb1 * gr_;
+      const float v = A.b2 * in.v + A.omb2 * gr_ * gr_;
       __builtin_nontemporal_store(m, A.m + e);
       __builtin_nontemporal_store(v, A.v + e);
       const float nth = th - A.lr * (m * A.inv_bc1) / (sqrtf(v * A.inv_bc2) + A.eps);
@@ -473,8 +488,12 @@ __device__ __forceinline__ void prebwd_gaussian(const PrebwdArgs& A, const CamK&
       const float qd = w * gq[0] + x * gq[1] + y * gq[2] + z * gq[3];
       for (int j = 0; j < 4; ++j) g[6 + j] = (gq[j] - P.qn[j] * qd) * P.inv_qlen;
     }
+    RowIn gin[8];  // rows 3..10
+#pragma unroll
+    for (int r = 3; r < 11; ++r) gin[r - 3] = row_in(r);
+#pragma unroll
     for (int r = 3; r < 11; ++r) {
-      const float nv = finish_row(r, g[r], r < 6 ? ls[r - 3] : (r < 10 ? q[r - 6] : a));
+      const float nv = finish_row(r, g[r], r < 6 ? ls[r - 3] : (r < 10 ? q[r - 6] : a), gin[r - 3]);
       if constexpr (NEXT) {  // (the old values are not needed past this point)
         if (r < 6) ls[r - 3] = nv;
         else if (r < 10) q[r - 6] = nv;
@@ -515,15 +534,38 @@ __device__ __forceinline__ void prebwd_gaussian(const PrebwdArgs& A, const CamK&
     g[1] += (gdir[1] - d1 * dd) * idist;
     g[2] += (gdir[2] - d2 * dd) * idist;
   }
+  // the SH rows' inputs, kShGroup coefficients (3 kShGroup rows) at a time
+  constexpr int kShGroup = 2;
+  auto sh_in = [&](int k0, RowIn (&in)[kShGroup][3]) {
+#pragma unroll
+    for (int kk = 0; kk < kShGroup; ++kk)
+      if (k0 + kk < NB)
+#pragma unroll
+        for (int ch = 0; ch < 3; ++ch) in[kk][ch] = row_in(11 + 3 * (k0 + kk) + ch);
+  };
+  RowIn min_in[3];  // the mean rows
+#pragma unroll
+  for (int r = 0; r < 3; ++r) min_in[r] = row_in(r);
   if constexpr (!NEXT) {
-    for (int r = 0; r < 3; ++r) finish_row(r, g[r], mu[r]);
 #pragma unroll
-    for (int k = 0; k < NB; ++k)
+    for (int r = 0; r < 3; ++r) finish_row(r, g[r], mu[r], min_in[r]);
 #pragma unroll
-      for (int ch = 0; ch < 3; ++ch) finish_row(11 + 3 * k + ch, vis ? Y[k] * gc[ch] : 0.f, f[k][ch]);
+    for (int k0 = 0; k0 < NB; k0 += kShGroup) {
+      RowIn in[kShGroup][3];
+      sh_in(k0, in);
+#pragma unroll
+      for (int kk = 0; kk < kShGroup; ++kk)
+        if (k0 + kk < NB)
+#pragma unroll
+          for (int ch = 0; ch < 3; ++ch) {
+            const int k = k0 + kk;
+            finish_row(11 + 3 * k + ch, vis ? Y[k] * gc[ch] : 0.f, f[k][ch], in[kk][ch]);
+          }
+    }
   } else {
     float nmu[3];
-    for (int r = 0; r < 3; ++r) nmu[r] = finish_row(r, g[r], mu[r]);
+#pragma unroll
+    for (int r = 0; r < 3; ++r) nmu[r] = finish_row(r, g[r], mu[r], min_in[r]);
     // the next view's preprocess of the new values: the operations of k_preprocess
     Proj Pn;
     project_geometry(cn, nmu, ls, q, na, Pn);
@@ -536,12 +578,19 @@ __device__ __forceinline__ void prebwd_gaussian(const PrebwdArgs& A, const CamK&
     }
     float rgb[3] = {0.5f, 0.5f, 0.5f};
 #pragma unroll
-    for (int k = 0; k < NB; ++k)
+    for (int k0 = 0; k0 < NB; k0 += kShGroup) {
+      RowIn in[kShGroup][3];
+      sh_in(k0, in);
 #pragma unroll
-      for (int ch = 0; ch < 3; ++ch) {
-        const float nf = finish_row(11 + 3 * k + ch, vis ? Y[k] * gc[ch] : 0.f, f[k][ch]);
-        if (Pn.vis) rgb[ch] += Yn[k] * nf;
-      }
+      for (int kk = 0; kk < kShGroup; ++kk)
+        if (k0 + kk < NB)
+#pragma unroll
+          for (int ch = 0; ch < 3; ++ch) {
+            const int k = k0 + kk;
+            const float nf = finish_row(11 + 3 * k + ch, vis ? Y[k] * gc[ch] : 0.f, f[k][ch], in[kk][ch]);
+            if (Pn.vis) rgb[ch] += Yn[k] * nf;
+          }
+    }
     uint32_t nt = 0, key = 0xFFFFFFFFu;
     uint2 rc = make_uint2(0u, 0u);
     r0 = r1 = r2 = make_float4(0.f, 0.f, 0.f, 0.f);
