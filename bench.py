@@ -122,12 +122,12 @@ KERNEL_OF = {"preprocess": ("k_preprocess<3>", "hbm"), "image_pass": ("k_blend_s
 # size; keyed by the SHA-256 of the kernel's source file, so a changed kernel (or another
 # workload) reports null
 COUNTER_TRAFFIC = {
-    "preprocess": {"source": "preprocess.hip", "bytes": 1200081832,
-                   "sha256": "4e38a63d590fe1fccf49a3783d5f7532613f1d608023e9c1205edd04d4c806a6"},
-    "image_pass": {"source": "blend.hip", "bytes": 6739011144,
+    "preprocess": {"source": "preprocess.hip", "bytes": 1200091687,
+                   "sha256": "2e44421290ff3ba679569f57331f2a8575e2df50829afcd43e503a78ae3ac4bb"},
+    "image_pass": {"source": "blend.hip", "bytes": 6727245517,
                    "sha256": "68654025237fa93927d67fd1c8f920c01fbb96d229ac13f019d32e98d54f4fb7"},
-    "prebwd_adam_next": {"source": "preprocess.hip", "bytes": 6199430657,
-                         "sha256": "4e38a63d590fe1fccf49a3783d5f7532613f1d608023e9c1205edd04d4c806a6"},
+    "prebwd_adam_next": {"source": "preprocess.hip", "bytes": 6199489056,
+                         "sha256": "2e44421290ff3ba679569f57331f2a8575e2df50829afcd43e503a78ae3ac4bb"},
 }
 
 
